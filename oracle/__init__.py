@@ -1,0 +1,28 @@
+"""CPU oracle for shared-prefix tree attention (test infrastructure only).
+
+Plain, slow, float64 NumPy implementation of what the tree-attention path
+computes.  Only the test suite, the smoke check and the benchmark's CPU
+baseline leg may import this package; the product path (the HIP library and
+its Python binding) never does, and shares no code with it.
+
+Parity status of every public function is listed in ``tree_attention``'s
+module docstring; none is "parity unpinned".
+"""
+
+from .tree_attention import (  # noqa: F401
+    ancestors,
+    visible_tokens,
+    visible_mask,
+    position_in_sequence,
+    subtree_end,
+    pairs,
+    forward,
+    backward,
+    forward_rows,
+    backward_rows,
+    backward_keys,
+    masked_dense_forward,
+    masked_dense_backward,
+    as_f64,
+    rel_l2,
+)
