@@ -16,6 +16,7 @@ from .tree_attention import (  # noqa: F401
     position_in_sequence,
     subtree_end,
     pairs,
+    segment_pairs,
     forward,
     backward,
     forward_rows,

@@ -38,6 +38,9 @@ Readings where the pages are silent are listed in the design notes: the child
 sees its whole parent segment, the diagonal is inclusive, the scale is
 1/sqrt(D), query heads map to key/value heads in contiguous groups.
 
+Array arithmetic runs in float64 on the CPU: NumPy for the tiny dense brute
+force, PyTorch CPU ops (matmul, exp, max, sum) for the per-segment forms.
+
 Parity status (pins live in ``tests/test_oracle.py``):
 
 * ``visible_tokens`` / ``visible_mask`` -- pinned: hand-derived golden
@@ -60,6 +63,7 @@ from __future__ import annotations
 import math
 
 import numpy as np
+import torch
 
 # ---------------------------------------------------------------------------
 # topology (definitions only; nothing here is tiled, merged or precomputed)
@@ -131,14 +135,20 @@ def _prefix_len(parent, ln, u):
     return int(sum(ln[a] for a in ancestors(parent, u)))
 
 
-def pairs(topo):
-    """Number of (query, key) pairs on ancestor paths, per head: sum_i |V(i)|."""
+def segment_pairs(topo):
+    """Per segment u: the (query, key) pairs of its queries, per head --
+    each of its n tokens sees every ancestor token plus a causal prefix of u."""
     parent, st, ln = _arrays(topo)
-    total = 0
+    out = []
     for u in range(len(parent)):
         n = int(ln[u])
-        total += n * _prefix_len(parent, ln, u) + n * (n + 1) // 2
-    return total
+        out.append(n * _prefix_len(parent, ln, u) + n * (n + 1) // 2)
+    return out
+
+
+def pairs(topo):
+    """Number of (query, key) pairs on ancestor paths, per head: sum_i |V(i)|."""
+    return int(sum(segment_pairs(topo)))
 
 
 # ---------------------------------------------------------------------------
@@ -166,6 +176,14 @@ def rel_l2(x, ref):
 # per-segment forward / backward (the plain definition, one segment at a time)
 
 
+def _t(x):
+    """Widen an input slice to a float64 CPU tensor.  Inputs may be float32
+    (bf16 values are exact in float32) or float64 NumPy arrays; they are
+    widened slice by slice so full-size tensors never need a float64 copy.
+    All arithmetic is float64 (PyTorch CPU ops: matmul, exp, max, sum)."""
+    return torch.as_tensor(np.asarray(x), dtype=torch.float64)
+
+
 def _default_scale(D, scale):
     return 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
 
@@ -191,11 +209,11 @@ def _segment_scores(Q, Kp, scale, prefix, r0, r1):
     Columns < prefix are ancestor keys (always visible); column c >= prefix
     is own-segment key c - prefix, visible iff c - prefix <= row offset.
     """
-    S = scale * np.einsum("gnd,pd->gnp", Q, Kp, optimize=True)
-    cols = np.arange(Kp.shape[0])
-    rows = np.arange(r0, r1)
-    vis = (cols[None, :] < prefix) | (cols[None, :] - prefix <= rows[:, None])
-    return np.where(vis[None], S, -np.inf)
+    S = scale * (Q @ Kp.T)
+    cols = torch.arange(Kp.shape[0])
+    rows = torch.arange(r0, r1)
+    hidden = (cols[None, :] >= prefix) & (cols[None, :] - prefix > rows[:, None])
+    return S.masked_fill(hidden[None], float("-inf"))
 
 
 def forward(q, k, v, topo, scale=None, heads=None, segments=None):
@@ -205,9 +223,6 @@ def forward(q, k, v, topo, scale=None, heads=None, segments=None):
     segments (other entries stay 0); used for bounded samples.
     """
     parent, st, ln = _arrays(topo)
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
@@ -223,66 +238,64 @@ def forward(q, k, v, topo, scale=None, heads=None, segments=None):
         idx, prefix = _path(parent, st, ln, u)
         s0, n = int(st[u]), int(ln[u])
         for g, hs in by_group.items():
-            Kp, Vp = k[idx, g], v[idx, g]
+            Kp, Vp = _t(k[idx, g]), _t(v[idx, g])
             for r0, r1 in _row_chunks(n, len(idx), len(hs)):
-                Q = q[s0 + r0 : s0 + r1][:, hs].transpose(1, 0, 2)
+                Q = _t(q[s0 + r0 : s0 + r1][:, hs]).transpose(0, 1)
                 S = _segment_scores(Q, Kp, scale, prefix, r0, r1)
-                m = S.max(axis=2, keepdims=True)
-                E = np.exp(S - m)
-                l = E.sum(axis=2, keepdims=True)
-                O = np.einsum("gnp,pd->gnd", E, Vp, optimize=True) / l
-                out[s0 + r0 : s0 + r1, hs] = O.transpose(1, 0, 2)
-                lse[hs, s0 + r0 : s0 + r1] = (m + np.log(l))[..., 0]
+                m = S.amax(dim=2, keepdim=True)
+                E = torch.exp(S - m)
+                l = E.sum(dim=2, keepdim=True)
+                O = (E @ Vp) / l
+                out[s0 + r0 : s0 + r1, hs] = O.transpose(0, 1).numpy()
+                lse[hs, s0 + r0 : s0 + r1] = (m + torch.log(l))[..., 0].numpy()
     return out, lse
 
 
-def backward(q, k, v, dout, topo, scale=None, kv_heads=None):
+def backward(q, k, v, dout, topo, scale=None, kv_heads=None, segments=None):
     """Exact gradients (dq, dk, dv) of L = sum <dout, out>, float64.
 
     Each segment's contribution to its ancestors' dk/dv is added onto the
     shared prefix tokens: branch contributions accumulate there.
     ``kv_heads`` restricts the work to those key/value heads (and their
-    query heads); other entries stay 0.
+    query heads); ``segments`` to the contributions of those query segments
+    (a bounded sample); other entries stay 0.
     """
     parent, st, ln = _arrays(topo)
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    dout = np.asarray(dout, dtype=np.float64)
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
     scale = _default_scale(D, scale)
     kv_heads = range(Hkv) if kv_heads is None else kv_heads
+    segments = range(len(parent)) if segments is None else segments
     heads = [h for g in kv_heads for h in range(g * G, (g + 1) * G)]
-    out, lse = forward(q, k, v, topo, scale, heads=heads)
-    dq = np.zeros_like(q)
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
-    for u in range(len(parent)):
+    out, lse = forward(q, k, v, topo, scale, heads=heads, segments=segments)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for u in segments:
         idx, prefix = _path(parent, st, ln, u)
         s0, n = int(st[u]), int(ln[u])
         for g in kv_heads:
             hs = list(range(g * G, (g + 1) * G))
-            Kp, Vp = k[idx, g], v[idx, g]
-            dKp = np.zeros_like(Kp)
-            dVp = np.zeros_like(Vp)
+            Kp, Vp = _t(k[idx, g]), _t(v[idx, g])
+            dKp = torch.zeros_like(Kp)
+            dVp = torch.zeros_like(Vp)
             for r0, r1 in _row_chunks(n, len(idx), G):
                 sl = slice(s0 + r0, s0 + r1)
-                Q = q[sl][:, hs].transpose(1, 0, 2)
-                dO = dout[sl][:, hs].transpose(1, 0, 2)
-                O = out[sl][:, hs].transpose(1, 0, 2)
-                L = lse[hs, sl][..., None]
+                Q = _t(q[sl][:, hs]).transpose(0, 1)
+                dO = _t(dout[sl][:, hs]).transpose(0, 1)
+                O = _t(out[sl][:, hs]).transpose(0, 1)
+                L = _t(lse[hs, sl])[..., None]
                 S = _segment_scores(Q, Kp, scale, prefix, r0, r1)
-                P = np.exp(S - L)
-                dVp += np.einsum("gnp,gnd->pd", P, dO, optimize=True)
-                dP = np.einsum("gnd,pd->gnp", dO, Vp, optimize=True)
-                delta = (dO * O).sum(axis=2, keepdims=True)
+                P = torch.exp(S - L)
+                dVp += (P.transpose(1, 2) @ dO).sum(dim=0)
+                dP = dO @ Vp.T
+                delta = (dO * O).sum(dim=2, keepdim=True)
                 dS = P * (dP - delta)
-                dq[sl, hs] = (scale * np.einsum("gnp,pd->gnd", dS, Kp, optimize=True)).transpose(1, 0, 2)
-                dKp += scale * np.einsum("gnp,gnd->pd", dS, Q, optimize=True)
-            dk[idx, g] += dKp
-            dv[idx, g] += dVp
+                dq[sl, hs] = (scale * (dS @ Kp)).transpose(0, 1).numpy()
+                dKp += scale * (dS.transpose(1, 2) @ Q).sum(dim=0)
+            dk[idx, g] += dKp.numpy()
+            dv[idx, g] += dVp.numpy()
     return dq, dk, dv
 
 
@@ -304,13 +317,14 @@ def forward_rows(q, k, v, topo, rows, scale=None, heads=None):
     lse = np.zeros((Hq, len(rows)))
     for r, i in enumerate(rows):
         vis = visible_tokens(topo, int(i))
-        for h in heads:
-            g = h // G
-            s = scale * (np.asarray(k[vis, g], np.float64) @ np.asarray(q[i, h], np.float64))
-            m = s.max()
-            e = np.exp(s - m)
-            out[r, h] = e @ np.asarray(v[vis, g], np.float64) / e.sum()
-            lse[h, r] = m + math.log(e.sum())
+        for g in sorted({h // G for h in heads}):
+            K, V = _t(k[vis, g]), _t(v[vis, g])
+            for h in [h for h in heads if h // G == g]:
+                s = scale * (K @ _t(q[i, h]))
+                m = s.max()
+                e = torch.exp(s - m)
+                out[r, h] = (e @ V / e.sum()).numpy()
+                lse[h, r] = float(m + torch.log(e.sum()))
     return out, lse
 
 
@@ -324,14 +338,13 @@ def backward_rows(q, k, v, dout, topo, rows, scale=None):
     dq = np.zeros((len(rows), Hq, D))
     for r, i in enumerate(rows):
         vis = visible_tokens(topo, int(i))
-        for h in range(Hq):
-            g = h // G
-            K = np.asarray(k[vis, g], np.float64)
-            V = np.asarray(v[vis, g], np.float64)
-            do = np.asarray(dout[i, h], np.float64)
-            p = np.exp(scale * (K @ np.asarray(q[i, h], np.float64)) - lse[h, r])
-            ds = p * (V @ do - do @ out[r, h])
-            dq[r, h] = scale * ds @ K
+        for g in range(Hkv):
+            K, V = _t(k[vis, g]), _t(v[vis, g])
+            for h in range(g * G, (g + 1) * G):
+                do = _t(dout[i, h])
+                p = torch.exp(scale * (K @ _t(q[i, h])) - float(lse[h, r]))
+                ds = p * (V @ do - do @ _t(out[r, h]))
+                dq[r, h] = (scale * ds @ K).numpy()
     return dq
 
 
@@ -361,16 +374,16 @@ def backward_keys(q, k, v, dout, topo, keys, kv_head, scale=None):
         qi = np.concatenate(
             [np.arange(j, st[t] + ln[t])] + [np.arange(st[u], st[u] + ln[u]) for u in seers[t] if u != t]
         )
-        kj = np.asarray(k[j, kv_head], np.float64)
-        vj = np.asarray(v[j, kv_head], np.float64)
+        kj = _t(k[j, kv_head])
+        vj = _t(v[j, kv_head])
         for h in hs:
-            Q = np.asarray(q[qi, h], np.float64)
-            dO = np.asarray(dout[qi, h], np.float64)
-            p = np.exp(scale * (Q @ kj) - lse[h, qi])
-            delta = (dO * out[qi, h]).sum(axis=1)
+            Q = _t(q[qi, h])
+            dO = _t(dout[qi, h])
+            p = torch.exp(scale * (Q @ kj) - _t(lse[h, qi]))
+            delta = (dO * _t(out[qi, h])).sum(dim=1)
             ds = p * (dO @ vj - delta)
-            dv[r] += p @ dO
-            dk[r] += scale * ds @ Q
+            dv[r] += (p @ dO).numpy()
+            dk[r] += (scale * ds @ Q).numpy()
     return dk, dv
 
 
