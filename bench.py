@@ -1,0 +1,236 @@
+"""Benchmark: tree-attention ancestor-path TFLOP/s (forward + backward) on one GPU.
+
+One step = one pass of the whole path over one batch: plan (validate the
+segment forest, derive spans and tiles, upload), forward, and the three
+backward stages.  Inputs are generated once and are resident in HBM before
+the timed region.  FLOPs are algorithmic: 4*D*Hq*pairs forward and
+10*D*Hq*pairs backward, with pairs = sum over tokens of the visible-set size
+(from the plan).
+
+Prints one JSON line.  Default workload: the agent-call tree of 65,536 tokens
+(32 query heads, 8 key/value heads, head_dim 128, bf16).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_FP32_MATRIX_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "tree-attention ancestor-path TFLOP/s fwd+bwd and % bf16 MFMA peak, 1 GPU"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, topo, arrs, kv_heads=1, pair_fraction=0.3):
+    """Time the float64 oracle (unchanged) on a bounded sample of the same
+    workload: the first ``kv_heads`` key/value heads (with their query
+    heads) and the query segments, in index order, that hold about
+    ``pair_fraction`` of the pairs.  Credited with the sample's algorithmic
+    FLOPs (14 * D * heads * sampled pairs)."""
+    import oracle
+    from workloads import bf16_to_f32
+
+    G = w.num_q_heads // w.num_kv_heads
+    x = {k: (bf16_to_f32(v) if w.dtype == "bf16" else v) for k, v in arrs.items()}
+    per_seg = oracle.segment_pairs(topo)
+    total = sum(per_seg)
+    segs, got = [], 0
+    for u, p in enumerate(per_seg):
+        if got >= pair_fraction * total:
+            break
+        segs.append(u)
+        got += p
+    t0 = time.perf_counter()
+    oracle.backward(x["q"], x["k"], x["v"], x["dout"], topo, kv_heads=list(range(kv_heads)), segments=segs)
+    dt = time.perf_counter() - t0
+    flops = 14.0 * w.head_dim * G * kv_heads * got
+    try:
+        import torch
+
+        cores = torch.get_num_threads()
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"float64 oracle forward+backward, key/value heads 0..{kv_heads - 1} "
+        f"({kv_heads * G} of {w.num_q_heads} query heads), query segments 0..{len(segs) - 1} "
+        f"of {topo.num_segments} ({got} of {total} pairs): {flops / 1e12:.3f} algorithmic TFLOP "
+        f"in {dt:.2f} s",
+        "seconds": round(dt, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="agent_tree_65536_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-kv-heads", type=int, default=1)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(sharding is described in the design notes); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import shared_prefix_tree_amd as sp
+    from workloads import get_workload
+
+    w = get_workload(args.workload)
+    topo = w.topology()
+    names = ("q", "k", "v", "dout") if w.backward else ("q", "k", "v")
+    log(f"workload {w.name}: generating inputs")
+    arrs = w.tensors(topo, names=names)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def gpu(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    t = {k: gpu(v) for k, v in arrs.items()}
+    T, Hq, D = t["q"].shape
+    Hkv = t["k"].shape[1]
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    if w.backward:
+        dq = torch.empty_like(t["q"])
+        dk = torch.empty_like(t["k"])
+        dv = torch.empty_like(t["v"])
+    probe = sp.Plan.from_topology(topo)
+    info = probe.info()
+    pairs = info["pairs"]
+    ws = torch.empty(max(256, sp.bwd_workspace_bytes(probe, t["q"], t["k"])), dtype=torch.uint8, device=dev)
+    del probe
+
+    stages = ["fwd", "rowstat", "dkdv", "dq"] if w.backward else ["fwd"]
+    plan_host_s = []
+
+    def step(events=None):
+        t0 = time.perf_counter()
+        plan = sp.Plan.from_topology(topo)
+        plan_host_s.append(time.perf_counter() - t0)
+        if events:
+            events[0].record()
+        sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan, out=out, lse=lse)
+        if w.backward:
+            sp.tree_attn_bwd_stages(t["q"], t["k"], t["v"], out, lse, t["dout"], plan, dq, dk, dv, ws,
+                                    events=events[1:] if events else None)
+        elif events:
+            events[1].record()
+        return plan
+
+    log(f"T={T} S={topo.num_segments} Hq={Hq} Hkv={Hkv} D={D} pairs={pairs}; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    plan_host_s.clear()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    keep = []
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        keep.append(step(ev[i]))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    keep.clear()
+    ms_per_step = elapsed / args.steps * 1e3
+    stage_ms = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j, s in enumerate(stages)}
+
+    fwd_flops = 4.0 * D * Hq * pairs
+    bwd_flops = 10.0 * D * Hq * pairs if w.backward else 0.0
+    total = fwd_flops + bwd_flops
+    value = total / (ms_per_step * 1e-3) / 1e12
+    # algorithmic FLOPs credited to each kernel: forward 4D per pair; the
+    # key-major pass does S, dP, dV, dK (8D); the query-major pass adds dQ (2D)
+    credit = {"fwd": fwd_flops, "rowstat": 0.0, "dkdv": 8.0 * D * Hq * pairs, "dq": 2.0 * D * Hq * pairs}
+    kernels = {}
+    for s in stages:
+        tf = credit[s] / (stage_ms[s] * 1e-3) / 1e12
+        kernels[s] = {"ms": round(stage_ms[s], 4), "tflops": round(tf, 2),
+                      "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    dom = max((s for s in stages if s != "rowstat"), key=lambda s: stage_ms[s])
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        try:
+            rec = json.load(open(PROFILE_TRAFFIC)).get(w.name, {}).get(dom)
+            traffic = rec.get("bytes_per_launch") if rec else None
+        except Exception:
+            traffic = None
+    achieved = credit[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MATRIX_TFLOPS
+    fwd_ms = stage_ms["fwd"]
+    bwd_ms = sum(stage_ms[s] for s in stages[1:])
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "tokens": int(T),
+            "segments": int(topo.num_segments),
+            "q_heads": int(Hq),
+            "kv_heads": int(Hkv),
+            "head_dim": int(D),
+            "pairs": int(pairs),
+            "max_path_len": int(info["max_path_len"]),
+            "step": "plan + fwd + bwd" if w.backward else "plan + fwd",
+        },
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2) if w.backward else None,
+        "kernel_tflops_fwd_bwd": round(total / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2),
+        "plan_host_ms": round(1e3 * float(np.mean(plan_host_s)), 4),
+        "kernels": kernels,
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline and w.backward:
+        log("cpu baseline (float64 oracle, bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(w, topo, arrs, args.cpu_kv_heads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

