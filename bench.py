@@ -34,7 +34,7 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, topo, arrs, kv_heads=1, pair_fraction=0.3):
+def cpu_baseline(w, topo, arrs, kv_heads=1, pair_fraction=1.0):
     """Time the float64 oracle (unchanged) on a bounded sample of the same
     workload: the first ``kv_heads`` key/value heads (with their query
     heads) and the query segments, in index order, that hold about
