@@ -27,7 +27,29 @@ PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_FP32_MATRIX_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "tree-attention ancestor-path TFLOP/s fwd+bwd and % bf16 MFMA peak, 1 GPU"
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ("kernel_common.hpp", "fwd.hip", "bwd.hip")
+
+
+def kernel_source_hash():
+    import hashlib
+
+    csrc = os.path.join(ROOT, "shared_prefix_tree_amd", "csrc")
+    blob = b"".join(open(os.path.join(csrc, f), "rb").read() for f in KERNEL_SOURCES)
+    return hashlib.sha256(blob).hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when it was taken on different kernel sources."""
+    try:
+        rec = json.load(open(PROFILE_TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    k = rec.get("workloads", {}).get(workload, {}).get(kernel)
+    return k.get("bytes_per_launch") if k else None
 
 
 def log(msg):
@@ -84,6 +106,8 @@ def main():
     ap.add_argument("--workload", default="agent_tree_65536_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-kv-heads", type=int, default=1)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes, --steps times (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -92,6 +116,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "launches": args.steps}), flush=True)
+        return
 
     import shared_prefix_tree_amd as sp
     from workloads import get_workload
@@ -173,13 +207,7 @@ def main():
         kernels[s] = {"ms": round(stage_ms[s], 4), "tflops": round(tf, 2),
                       "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
     dom = max((s for s in stages if s != "rowstat"), key=lambda s: stage_ms[s])
-    traffic = None
-    if os.path.exists(PROFILE_TRAFFIC):
-        try:
-            rec = json.load(open(PROFILE_TRAFFIC)).get(w.name, {}).get(dom)
-            traffic = rec.get("bytes_per_launch") if rec else None
-        except Exception:
-            traffic = None
+    traffic = measured_traffic(w.name, dom)
     achieved = credit[dom] / (stage_ms[dom] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MATRIX_TFLOPS
     fwd_ms = stage_ms["fwd"]
