@@ -143,13 +143,16 @@ int tree_attn_plan_export(tree_attn_plan_t plan, int32_t which, int32_t* buf, in
  * [T, Hq, D] of the same dtype; lse: device float32 [Hq, T].  Overwrites out
  * and lse.  stream: a hipStream_t (NULL = default).  Asynchronous.
  * Errors: INVALID_ARGUMENT (null pointer, shape mismatch, host-only plan,
- * plan built on another device), UNSUPPORTED (dtype/head_dim), HIP_ERROR.
+ * plan built on another device), UNSUPPORTED (dtype/head_dim, more than
+ * 2^31 elements in a tensor, or a segment whose ancestor path splits into
+ * more than 256 separate token spans), HIP_ERROR.
  */
 int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t plan,
                   const tree_attn_shape* shape, void* out, float* lse, void* stream);
 
 /* Bytes of device workspace tree_attn_bwd needs for this plan and shape
- * (float32 [Hq, T] row statistics, 256-byte aligned); 0 on invalid input. */
+ * (two float32 [Hq, T] row-statistic arrays, 256-byte aligned); 0 on
+ * invalid input. */
 size_t tree_attn_bwd_workspace_bytes(tree_attn_plan_t plan, const tree_attn_shape* shape);
 
 /*
@@ -168,8 +171,9 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* out, 
 /*
  * The three stages tree_attn_bwd runs, in this order, on one stream; each can
  * be called on its own (for example to time it).  They share the workspace:
- *   tree_attn_bwd_rowstat  delta[h,i] = sum_d dout[i,h,d] * out[i,h,d] into the
- *                          workspace (float32 [Hq, T]);
+ *   tree_attn_bwd_rowstat  delta[h,i] = sum_d dout[i,h,d] * out[i,h,d] and
+ *                          lse[h,i] * log2(e) into the workspace (two float32
+ *                          [Hq, T] arrays);
  *   tree_attn_bwd_dkdv     dk, dv: for each key, the contributions of every
  *                          query that sees it, i.e. of every branch below a
  *                          shared prefix (draft "feat(hybrid): add opt-in
@@ -178,8 +182,8 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* out, 
  *   tree_attn_bwd_dq       dq; needs the rowstat workspace.
  * Arguments, checks and errors are those of tree_attn_bwd.
  */
-int tree_attn_bwd_rowstat(const void* out, const void* dout, tree_attn_plan_t plan, const tree_attn_shape* shape,
-                          void* workspace, size_t workspace_bytes, void* stream);
+int tree_attn_bwd_rowstat(const void* out, const float* lse, const void* dout, tree_attn_plan_t plan,
+                          const tree_attn_shape* shape, void* workspace, size_t workspace_bytes, void* stream);
 int tree_attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                        tree_attn_plan_t plan, const tree_attn_shape* shape, void* dk, void* dv, void* workspace,
                        size_t workspace_bytes, void* stream);

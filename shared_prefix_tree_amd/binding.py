@@ -108,7 +108,7 @@ def library():
     lib.tree_attn_bwd_workspace_bytes.argtypes = [vp, ctypes.POINTER(Shape)]
     lib.tree_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.tree_attn_bwd.argtypes = [vp] * 6 + [vp, ctypes.POINTER(Shape)] + [vp] * 4 + [ctypes.c_size_t, vp]
-    lib.tree_attn_bwd_rowstat.argtypes = [vp, vp, vp, ctypes.POINTER(Shape), vp, ctypes.c_size_t, vp]
+    lib.tree_attn_bwd_rowstat.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), vp, ctypes.c_size_t, vp]
     lib.tree_attn_bwd_dkdv.argtypes = [vp] * 6 + [ctypes.POINTER(Shape), vp, vp, vp, ctypes.c_size_t, vp]
     lib.tree_attn_bwd_dq.argtypes = [vp] * 6 + [ctypes.POINTER(Shape), vp, vp, ctypes.c_size_t, vp]
     lib.tree_attn_last_error.restype = ctypes.c_char_p
@@ -304,6 +304,13 @@ def tree_attn_bwd_stages(q, k, v, out, lse, dout, plan: Plan, dq, dk, dv, worksp
 
     lib = library()
     dev = q.device
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    for name, t, shp in (("q", q, (T, Hq, D)), ("k", k, (T, Hkv, D)), ("v", v, (T, Hkv, D)),
+                         ("out", out, (T, Hq, D)), ("dout", dout, (T, Hq, D)), ("dq", dq, (T, Hq, D)),
+                         ("dk", dk, (T, Hkv, D)), ("dv", dv, (T, Hkv, D))):
+        _check_tensor(name, t, q.dtype, shp, dev)
+    _check_tensor("lse", lse, torch.float32, (Hq, T), dev)
     shape = _shape(q, k, softmax_scale)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(s.cuda_stream)
@@ -311,8 +318,8 @@ def tree_attn_bwd_stages(q, k, v, out, lse, dout, plan: Plan, dq, dk, dv, worksp
     with torch.cuda.device(dev):
         if events:
             events[0].record(s)
-        _check(lib.tree_attn_bwd_rowstat(out.data_ptr(), dout.data_ptr(), plan.handle, ctypes.byref(shape),
-                                         workspace.data_ptr(), wsb, sp))
+        _check(lib.tree_attn_bwd_rowstat(out.data_ptr(), lse.data_ptr(), dout.data_ptr(), plan.handle,
+                                         ctypes.byref(shape), workspace.data_ptr(), wsb, sp))
         if events:
             events[1].record(s)
         _check(lib.tree_attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), dout.data_ptr(),

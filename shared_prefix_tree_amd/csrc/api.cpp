@@ -164,8 +164,12 @@ int check_call(const char* fn, tree_attn_plan_t plan, const tree_attn_shape* sha
     return fail(TREE_ATTN_UNSUPPORTED, f + ": dtype must be TREE_ATTN_BF16 or TREE_ATTN_FP32");
   }
   const int64_t rows = int64_t(shape->total_tokens) * shape->num_q_heads;
-  if (rows * shape->head_dim >= (int64_t(1) << 40) || rows >= (int64_t(1) << 31))
-    return fail(TREE_ATTN_UNSUPPORTED, f + ": tensor too large");
+  if (rows * shape->head_dim >= (int64_t(1) << 31))
+    return fail(TREE_ATTN_UNSUPPORTED, f + ": tensors are limited to 2^31 elements");
+  if (plan->host.max_spans > kMaxSpans)
+    return fail(TREE_ATTN_UNSUPPORTED, f + ": a segment's ancestor path has " +
+                                           std::to_string(plan->host.max_spans) + " separate spans (limit " +
+                                           std::to_string(kMaxSpans) + ")");
   const int hg = gcd(shape->num_q_heads / shape->num_kv_heads, 4);
   const int64_t grid_q = int64_t(plan->host.qtiles[qtile_index(32 * (4 / hg))].size()) * (shape->num_q_heads / hg);
   const int64_t grid_k = int64_t(plan->host.ktiles.size()) * shape->num_kv_heads;
@@ -303,7 +307,7 @@ int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t 
 
 size_t tree_attn_bwd_workspace_bytes(tree_attn_plan_t plan, const tree_attn_shape* shape) {
   if (!plan || !shape || shape->total_tokens < 1 || shape->num_q_heads < 1) return 0;
-  const size_t bytes = size_t(shape->num_q_heads) * size_t(shape->total_tokens) * sizeof(float);
+  const size_t bytes = 2 * size_t(shape->num_q_heads) * size_t(shape->total_tokens) * sizeof(float);
   return (bytes + 255) & ~size_t(255);
 }
 
@@ -321,7 +325,7 @@ int prep_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   float scale = 0.f;
   auto need = [&](const void* p, int st) { return (stages & st) && !p; };
   if (need(out, kRowStat) || need(dout, kAll) || need(q, kDkDv | kDq) || need(k, kDkDv | kDq) ||
-      need(v, kDkDv | kDq) || need(lse, kDkDv | kDq) || need(dq, kDq) || need(dk, kDkDv) || need(dv, kDkDv) ||
+      need(v, kDkDv | kDq) || need(lse, kAll) || need(dq, kDq) || need(dk, kDkDv) || need(dv, kDkDv) ||
       !workspace)
     return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": NULL pointer");
   for (const void* p : {q, k, v, out, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
@@ -393,11 +397,11 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* out, 
   return run_bwd("tree_attn_bwd", a, shape, hg, kAll, stream);
 }
 
-int tree_attn_bwd_rowstat(const void* out, const void* dout, tree_attn_plan_t plan, const tree_attn_shape* shape,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+int tree_attn_bwd_rowstat(const void* out, const float* lse, const void* dout, tree_attn_plan_t plan,
+                          const tree_attn_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
   BwdArgs a;
   int hg = 1;
-  if (int rc = prep_bwd("tree_attn_bwd_rowstat", nullptr, nullptr, nullptr, out, nullptr, dout, plan, shape,
+  if (int rc = prep_bwd("tree_attn_bwd_rowstat", nullptr, nullptr, nullptr, out, lse, dout, plan, shape,
                         nullptr, nullptr, nullptr, workspace, workspace_bytes, kRowStat, a, hg))
     return rc;
   return run_bwd("tree_attn_bwd_rowstat", a, shape, hg, kRowStat, stream);

@@ -11,19 +11,28 @@
 //
 // Three launches, no atomics, every output element written once by one
 // workgroup in a fixed order (bitwise reproducible):
-//   1. rowstat: delta[h,i] = sum_d dout[i,h,d] * out[i,h,d];
+//   1. rowstat: delta[h,i] = sum_d dout[i,h,d] * out[i,h,d] and
+//      lse2[h,i] = lse[h,i] * log2(e), into the workspace;
 //   2. dkdv (key-major): a workgroup owns 64 keys of one segment and one
 //      key/value head; in DFS pre-order the queries that see key j are the
 //      contiguous range [j, subtree_end(seg(j))), so it loops over that range
 //      (all G query heads) and accumulates dK, dV in registers:
 //        S = Q K^T, P = exp(S - lse), dV^T += dO^T P,
 //        dP = dO V^T, dS = P (dP - delta), dK^T += Q^T dS;
+//      the 64-query Q / dO tiles and their lse / delta are copied straight
+//      into LDS (two buffers, one barrier per step); Q^T and dO^T fragments
+//      come from the transposing LDS load of the same row-major tiles;
 //   3. dq (query-major): the forward's walk over the ancestor path,
 //        S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - delta),
-//        dQ^T += K^T dS^T.
+//        dQ^T += K^T dS^T   (K^T from the transposing LDS load).
 #include "kernel_common.hpp"
 
 namespace tree_attn {
+
+// 4-byte-per-lane copy global -> LDS: lane l writes (lds_base + 4 l).
+__device__ inline void dma4(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 4, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // 1. row statistics
@@ -31,7 +40,9 @@ namespace tree_attn {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restrict__ out,
                                                                 const T* __restrict__ dout,
-                                                                float* __restrict__ delta, int T_, int Hq) {
+                                                                const float* __restrict__ lse,
+                                                                float* __restrict__ delta,
+                                                                float* __restrict__ lse2, int T_, int Hq) {
   constexpr int E = Chunk<T>::E;
   constexpr int CPR = D / E;
   constexpr int RPB = 256 / CPR;
@@ -50,7 +61,9 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
   for (int off = CPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   if (valid && c == 0) {
     const int i = row / Hq, h = row % Hq;
-    delta[(size_t)h * T_ + i] = acc;
+    const size_t at = (size_t)h * T_ + i;
+    delta[at] = acc;
+    lse2[at] = lse[at] * kLog2e;
   }
 }
 
@@ -58,31 +71,23 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
 // 2. dK / dV, key-major
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void tree_attn_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   using quad = typename M::quad;
-  constexpr int BM = 64;               // queries per step
-  constexpr int E = Chunk<T>::E;
-  constexpr int CPR = D / E;
-  constexpr int KPT = BM * CPR / 256;  // query rows each thread loads per step
+  constexpr int BM = 64;  // queries per step
+  constexpr int E = 16 / int(sizeof(T));
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int KSTR = D + E;
-  constexpr int QSTR = BM + 4;
-  static_assert(KPT == 4, "tile loader assumes 4 rows per thread");
-  constexpr int kTileElems = BM * KSTR;  // sQ, sdO
-  constexpr int kTElems = D * QSTR;      // sQt, sdOt
-  constexpr int kLdsBytes = (2 * kTileElems + 2 * kTElems) * int(sizeof(T));
-  constexpr int kRedBytes = 2 * (2 * DB * 16) * 64 * 4;  // two waves' dK/dV partials
-  static_assert(kRedBytes <= kLdsBytes, "reduction buffer aliases the tiles");
+  constexpr int TILE = BM * kRowBytes / int(sizeof(T));
+  static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
+  static_assert(DB * 16 * 64 * 4 <= TILE * int(sizeof(T)), "one wave's partial fits a tile");
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  __shared__ float slse[BM], sdelta[BM];
-  T* sQ = reinterpret_cast<T*>(lds);
-  T* sdO = sQ + kTileElems;
-  T* sQt = sdO + kTileElems;
-  T* sdOt = sQt + kTElems;
+  __shared__ __attribute__((aligned(16))) T sQ0[TILE];
+  __shared__ __attribute__((aligned(16))) T sO0[TILE];
+  __shared__ __attribute__((aligned(16))) T sQ1[TILE];
+  __shared__ __attribute__((aligned(16))) T sO1[TILE];
+  __shared__ float sL0[BM], sD0[BM], sL1[BM], sD1[BM];
 
   int tile_rank, g;
   decode_item(blockIdx.x, a.Hkv, tile_rank, g);
@@ -98,17 +103,16 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dkdv_kernel(BwdArgs a) {
   const float c = a.scale * kLog2e;
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
-  const T* __restrict__ k = static_cast<const T*>(a.k);
-  const T* __restrict__ v = static_cast<const T*>(a.v);
   const T* __restrict__ dout = static_cast<const T*>(a.dout);
+  const float* lse2 = a.delta + (size_t)a.Hq * a.T;
 
   frag kf[KS], vf[KS];
   {
     const size_t off = ((size_t)ktok * a.Hkv + g) * D + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = load_frag<T>(k + off + ks * 16);
-      vf[ks] = load_frag<T>(v + off + ks * 16);
+      kf[ks] = load_frag<T>(static_cast<const T*>(a.k) + off + ks * 16);
+      vf[ks] = load_frag<T>(static_cast<const T*>(a.v) + off + ks * 16);
     }
   }
   f32x16 dk[DB], dv[DB];
@@ -118,101 +122,94 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dkdv_kernel(BwdArgs a) {
     dv[db] = f32x16{};
   }
 
-  const int dc = tid % CPR, qg = tid / CPR;
-
-  for (int hi = 0; hi < a.G; ++hi) {
-    const int h = g * a.G + hi;
-    for (int i0 = tile.k0; i0 < tile.qend; i0 += BM) {
-      Chunk<T> qc[KPT], oc[KPT];
+  const int nblk = (tile.qend - tile.k0 + BM - 1) / BM;
+  const int n_steps = a.G * nblk;
+  int lrow[4], lchunk[4];
 #pragma unroll
-      for (int r = 0; r < KPT; ++r) {
-        const int qi = i0 + qg * KPT + r;
-        if (qi < tile.qend) {
-          const size_t off = ((size_t)qi * a.Hq + h) * D + dc * E;
-          qc[r] = load_chunk<T>(q + off);
-          oc[r] = load_chunk<T>(dout + off);
-        } else {
-          qc[r] = zero_chunk<T>();
-          oc[r] = zero_chunk<T>();
-        }
-      }
-      float lv = 0.f, dl = 0.f;
-      if (tid < BM) {
-        const int qi = i0 + tid;
-        if (qi < tile.qend) {
-          lv = a.lse[(size_t)h * a.T + qi] * kLog2e;
-          dl = a.delta[(size_t)h * a.T + qi];
-        }
-      }
-      __syncthreads();  // previous step finished with the tiles
+  for (int r = 0; r < 4; ++r) {
+    lrow[r] = (4 * wave + r) * 4 + (lane >> 4);
+    lchunk[r] = (lane & 15) ^ swz(lrow[r]);
+  }
+  // rows past the query range read a valid row and are masked to P = 0
+  auto issue = [&](int step, T* sQ, T* sO, float* sL, float* sD) {
+    const int h = g * a.G + step / nblk;
+    const int i0 = tile.k0 + (step % nblk) * BM;
 #pragma unroll
-      for (int r = 0; r < KPT; ++r) {
-        store_chunk<T>(&sQ[(qg * KPT + r) * KSTR + dc * E], qc[r]);
-        store_chunk<T>(&sdO[(qg * KPT + r) * KSTR + dc * E], oc[r]);
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        quad tq, to;
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-          tq[r] = qc[r].elem(e);
-          to[r] = oc[r].elem(e);
-        }
-        *reinterpret_cast<quad*>(&sQt[(dc * E + e) * QSTR + qg * KPT]) = tq;
-        *reinterpret_cast<quad*>(&sdOt[(dc * E + e) * QSTR + qg * KPT]) = to;
-      }
-      if (tid < BM) {
-        slse[tid] = lv;
-        sdelta[tid] = dl;
-      }
-      __syncthreads();
-
-      // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        M::mma(s, load_frag<T>(&sQ[(qh * 32 + col) * KSTR + ks * 16 + half * 8]), kf[ks]);
-        M::mma(dp, load_frag<T>(&sdO[(qh * 32 + col) * KSTR + ks * 16 + half * 8]), vf[ks]);
-      }
-      const bool need_mask = i0 + qh * 32 < tile.k0 + kb * 32 + 31;
-      frag pf[2], dsf[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qr = qh * 32 + c_row(i, half);
-        float p = __builtin_amdgcn_exp2f(s[i] * c - slse[qr]);
-        if (need_mask && i0 + qr < jkey) p = 0.f;
-        const float ds = p * (dp[i] - sdelta[qr]);
-        pf[i >> 3][i & 7] = to_elem<T>(p);
-        dsf[i >> 3][i & 7] = to_elem<T>(ds);
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int o = (db * 32 + col) * QSTR + qh * 32 + 16 * hh + 4 * half;
-          M::mma(dv[db], load_frag_split<T>(&sdOt[o]), pf[hh]);
-          M::mma(dk[db], load_frag_split<T>(&sQt[o]), dsf[hh]);
-        }
+    for (int r = 0; r < 4; ++r) {
+      const int qi = min(i0 + lrow[r], tile.qend - 1);
+      const size_t off = ((size_t)qi * a.Hq + h) * D + lchunk[r] * E;
+      dma16(q + off, sQ + (4 * wave + r) * 64 * E);
+      dma16(dout + off, sO + (4 * wave + r) * 64 * E);
     }
+    if (wave < 2) {
+      const size_t at = (size_t)h * a.T + min(i0 + lane, tile.qend - 1);
+      dma4(wave == 0 ? lse2 + at : a.delta + at, wave == 0 ? sL : sD);
+    }
+  };
+
+  auto compute = [&](int step, const T* sQ, const T* sO, const float* sL, const float* sD) {
+    const int i0 = tile.k0 + (step % nblk) * BM;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      M::mma(s, tile_row_frag<T>(sQ, qh * 32 + col, ks * 16 + half * 8), kf[ks]);
+      M::mma(dp, tile_row_frag<T>(sO, qh * 32 + col, ks * 16 + half * 8), vf[ks]);
+    }
+    const bool need_mask = i0 + qh * 32 < tile.k0 + kb * 32 + 31 || i0 + qh * 32 + 31 >= tile.qend;
+    frag pf[2], dsf[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int qr = qh * 32 + c_row(i, half);
+      float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -sL[qr]));
+      if (need_mask && (i0 + qr < jkey || i0 + qr >= tile.qend)) p = 0.f;
+      pf[i >> 3][i & 7] = to_elem<T>(p);
+      dsf[i >> 3][i & 7] = to_elem<T>(p * (dp[i] - sD[qr]));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        M::mma(dv[db], tile_tr_frag<T>(sO, qh * 32 + 16 * hh, db * 32, lane), pf[hh]);
+        M::mma(dk[db], tile_tr_frag<T>(sQ, qh * 32 + 16 * hh, db * 32, lane), dsf[hh]);
+      }
+  };
+
+  issue(0, sQ0, sO0, sL0, sD0);
+  wait_dma();
+  __syncthreads();
+  for (int step = 0;;) {
+    const bool more1 = step + 1 < n_steps;
+    if (more1) issue(step + 1, sQ1, sO1, sL1, sD1);
+    compute(step, sQ0, sO0, sL0, sD0);
+    if (!more1) break;
+    wait_dma();
+    __syncthreads();
+    ++step;
+    const bool more0 = step + 1 < n_steps;
+    if (more0) issue(step + 1, sQ0, sO0, sL0, sD0);
+    compute(step, sQ1, sO1, sL1, sD1);
+    if (!more0) break;
+    wait_dma();
+    __syncthreads();
+    ++step;
   }
 
-  // fixed-order reduction of the two query halves, then one store per key
+  // fixed-order reduction of the two query halves, then one store per key:
+  // the qh = 1 waves park their dK (in sQ0 / sO0) and dV (in sQ1 / sO1)
   __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);
-  constexpr int kVals = 2 * DB * 16;
+  float* rk = reinterpret_cast<float*>(kb == 0 ? sQ0 : sO0);
+  float* rv = reinterpret_cast<float*>(kb == 0 ? sQ1 : sO1);
   if (qh == 1) {
-    float* r = red + (size_t)kb * kVals * 64;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        r[(db * 16 + i) * 64 + lane] = dk[db][i];
-        r[((DB + db) * 16 + i) * 64 + lane] = dv[db][i];
+        rk[(db * 16 + i) * 64 + lane] = dk[db][i];
+        rv[(db * 16 + i) * 64 + lane] = dv[db][i];
       }
   }
   __syncthreads();
   if (qh == 0 && key_valid) {
-    const float* r = red + (size_t)kb * kVals * 64;
     T* dkp = static_cast<T*>(a.dk) + ((size_t)jkey * a.Hkv + g) * D;
     T* dvp = static_cast<T*>(a.dv) + ((size_t)jkey * a.Hkv + g) * D;
 #pragma unroll
@@ -223,8 +220,8 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = grp * 4 + e;
-          tk[e] = to_elem<T>((dk[db][i] + r[(db * 16 + i) * 64 + lane]) * a.scale);
-          tv[e] = to_elem<T>(dv[db][i] + r[((DB + db) * 16 + i) * 64 + lane]);
+          tk[e] = to_elem<T>((dk[db][i] + rk[(db * 16 + i) * 64 + lane]) * a.scale);
+          tv[e] = to_elem<T>(dv[db][i] + rv[(db * 16 + i) * 64 + lane]);
         }
         *reinterpret_cast<quad*>(dkp + db * 32 + grp * 8 + half * 4) = tk;
         *reinterpret_cast<quad*>(dvp + db * 32 + grp * 8 + half * 4) = tv;
@@ -241,18 +238,17 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
   using frag = typename M::frag;
   using quad = typename M::quad;
   constexpr int BN = 64;
-  constexpr int E = Chunk<T>::E;
-  constexpr int CPR = D / E;
-  constexpr int KPT = BN * CPR / 256;
+  constexpr int E = 16 / int(sizeof(T));
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int KSTR = D + E;
-  constexpr int VSTR = BN + 4;
-  static_assert(KPT == 4, "tile loader assumes 4 keys per thread");
+  constexpr int TILE = BN * kRowBytes / int(sizeof(T));
+  static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
 
-  __shared__ __attribute__((aligned(16))) T sK[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) T sV[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) T sKt[D * VSTR];
+  __shared__ __attribute__((aligned(16))) T sK0[TILE];
+  __shared__ __attribute__((aligned(16))) T sV0[TILE];
+  __shared__ __attribute__((aligned(16))) T sK1[TILE];
+  __shared__ __attribute__((aligned(16))) T sV1[TILE];
+  __shared__ Span sSpans[kMaxSpans];
 
   int tile_rank, group;
   decode_item(blockIdx.x, a.Hq / HG, tile_rank, group);
@@ -270,70 +266,57 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
   const int kv_len = tile.pos0 + tile.nq;
   const float c = a.scale * kLog2e;
 
-  const T* __restrict__ q = static_cast<const T*>(a.q);
-  const T* __restrict__ k = static_cast<const T*>(a.k);
-  const T* __restrict__ v = static_cast<const T*>(a.v);
-  const T* __restrict__ dout = static_cast<const T*>(a.dout);
+  const T* kg = static_cast<const T*>(a.k) + (size_t)g * D;
+  const T* vg = static_cast<const T*>(a.v) + (size_t)g * D;
+  const size_t row_stride = (size_t)a.Hkv * D;
 
   frag qf[KS], of[KS];
   {
     const size_t off = ((size_t)qtok * a.Hq + h) * D + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qf[ks] = load_frag<T>(q + off + ks * 16);
-      of[ks] = load_frag<T>(dout + off + ks * 16);
+      qf[ks] = load_frag<T>(static_cast<const T*>(a.q) + off + ks * 16);
+      of[ks] = load_frag<T>(static_cast<const T*>(a.dout) + off + ks * 16);
     }
   }
-  const float lse2 = a.lse[(size_t)h * a.T + qtok] * kLog2e;
+  const float lse2 = a.delta[(size_t)a.Hq * a.T + (size_t)h * a.T + qtok];
   const float dlt = a.delta[(size_t)h * a.T + qtok];
 
   f32x16 dq[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
 
-  SpanCursor cur{a.spans + a.span_ptr[tile.seg], 0};
-  const int dc = tid % CPR, kg = tid / CPR;
-  const size_t row_stride = (size_t)a.Hkv * D;
-  const T* kbase = k + (size_t)g * D + dc * E;
-  const T* vbase = v + (size_t)g * D + dc * E;
+  stage_spans(sSpans, a.span_ptr, a.spans, tile.seg);
+  __syncthreads();
+  SpanCursor cur{sSpans, 0};
+  int lrow[4], lchunk[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    lrow[r] = (4 * wave + r) * 4 + (lane >> 4);
+    lchunk[r] = (lane & 15) ^ swz(lrow[r]);
+  }
+  auto issue = [&](int v0, T* sK, T* sV) {
+    size_t off[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int vk = min(v0 + lrow[r], kv_len - 1);
+      off[r] = (size_t)cur.phys(vk) * row_stride + lchunk[r] * E;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dma16(kg + off[r], sK + (4 * wave + r) * 64 * E);
+      dma16(vg + off[r], sV + (4 * wave + r) * 64 * E);
+    }
+  };
 
-  for (int v0 = 0; v0 < kv_len; v0 += BN) {
-    Chunk<T> kc[KPT], vc[KPT];
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int vk = v0 + kg * KPT + r;
-      if (vk < kv_len) {
-        const size_t off = (size_t)cur.phys(vk) * row_stride;
-        kc[r] = load_chunk<T>(kbase + off);
-        vc[r] = load_chunk<T>(vbase + off);
-      } else {
-        kc[r] = zero_chunk<T>();
-        vc[r] = zero_chunk<T>();
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      store_chunk<T>(&sK[(kg * KPT + r) * KSTR + dc * E], kc[r]);
-      store_chunk<T>(&sV[(kg * KPT + r) * KSTR + dc * E], vc[r]);
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      quad t4;
-#pragma unroll
-      for (int r = 0; r < KPT; ++r) t4[r] = kc[r].elem(e);
-      *reinterpret_cast<quad*>(&sKt[(dc * E + e) * VSTR + kg * KPT]) = t4;
-    }
-    __syncthreads();
-
+  auto compute = [&](int v0, const T* sK, const T* sV) {
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int o = (kb * 32 + col) * KSTR + ks * 16 + half * 8;
-        M::mma(s[kb], load_frag<T>(&sK[o]), qf[ks]);
-        M::mma(dp[kb], load_frag<T>(&sV[o]), of[ks]);
+        M::mma(s[kb], tile_row_frag<T>(sK, kb * 32 + col, ks * 16 + half * 8), qf[ks]);
+        M::mma(dp[kb], tile_row_frag<T>(sV, kb * 32 + col, ks * 16 + half * 8), of[ks]);
       }
     const bool need_mask = v0 + BN - 1 > wave_pos0;
     frag dsf[2][2];
@@ -341,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = __builtin_amdgcn_exp2f(s[kb][i] * c - lse2);
+        float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -lse2));
         if (need_mask && v0 + kb * 32 + c_row(i, half) > qpos) p = 0.f;
         dsf[kb][i >> 3][i & 7] = to_elem<T>(p * (dp[kb][i] - dlt));
       }
@@ -351,8 +334,27 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-          M::mma(dq[db], load_frag_split<T>(&sKt[(db * 32 + col) * VSTR + kb * 32 + 16 * hh + 4 * half]),
-                 dsf[kb][hh]);
+          M::mma(dq[db], tile_tr_frag<T>(sK, kb * 32 + 16 * hh, db * 32, lane), dsf[kb][hh]);
+  };
+
+  issue(0, sK0, sV0);
+  wait_dma();
+  __syncthreads();
+  for (int v0 = 0;;) {
+    const bool more1 = v0 + BN < kv_len;
+    if (more1) issue(v0 + BN, sK1, sV1);
+    compute(v0, sK0, sV0);
+    if (!more1) break;
+    wait_dma();
+    __syncthreads();
+    v0 += BN;
+    const bool more0 = v0 + BN < kv_len;
+    if (more0) issue(v0 + BN, sK0, sV0);
+    compute(v0, sK1, sV1);
+    if (!more0) break;
+    wait_dma();
+    __syncthreads();
+    v0 += BN;
   }
 
   if (qrow < tile.nq) {
@@ -378,7 +380,8 @@ hipError_t launch_bwd_rowstat(const BwdArgs& a, hipStream_t stream) {
   constexpr int RPB = 256 / CPR;
   const unsigned rows = (unsigned)a.T * (unsigned)a.Hq;
   hipLaunchKernelGGL((tree_attn_rowstat_kernel<T, D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, stream,
-                     static_cast<const T*>(a.out), static_cast<const T*>(a.dout), a.delta, a.T, a.Hq);
+                     static_cast<const T*>(a.out), static_cast<const T*>(a.dout), a.lse, a.delta,
+                     a.delta + (size_t)a.Hq * a.T, a.T, a.Hq);
   return hipGetLastError();
 }
 

@@ -15,37 +15,44 @@
 //   * wave w holds 32 query rows (token sub-tile w / HG, head w % HG) with Q
 //     in registers;
 //   * the workgroup walks the segment's ancestor path as one virtual key
-//     sequence (the merged spans of the plan), 64 keys per step: K and V are
-//     gathered span by span with 16-byte row-contiguous loads, staged in LDS
-//     (K row-major, V transposed), and every wave computes
-//       S^T = K Q^T -> online softmax per query column -> O^T += V^T P^T
-//     on the matrix cores.  A lane owns one query column, so the row max and
-//     row sum are in-lane reductions plus one exchange with lane l ^ 32.
+//     sequence (the merged spans of the plan), 64 keys per step.  K and V
+//     rows are gathered span by span straight into LDS (global_load_lds,
+//     16 B per lane, row-major, swizzled) into one of two buffers while the
+//     other buffer is being used, so a step costs one barrier;
+//   * every wave computes S^T = K Q^T (K rows read as A fragments), the
+//     online softmax per query column, and O^T += V^T P^T (V read with the
+//     transposing LDS load).  A lane owns one query column, so the row max
+//     and row sum are in-lane reductions plus one exchange with lane l ^ 32;
+//   * the softmax works in base 2 with the scale folded into one FMA per
+//     score; the running max is only moved (and O rescaled) when a row's
+//     maximum grows by more than 2^8, which keeps the result exact (numerator
+//     and denominator share the same reference) and skips most rescales;
 //   * the own-segment causal rule is "virtual key position <= query
 //     position", applied only on the last steps of the walk.
 #include "kernel_common.hpp"
 
 namespace tree_attn {
 
+constexpr float kRescaleSlack = 8.0f;  // log2 units: P values stay <= 256
+
 template <typename T, int D, int HG>
 __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   using quad = typename M::quad;
-  constexpr int BN = 64;                 // keys per step
-  constexpr int NT = 4 / HG;             // 32-token sub-tiles per workgroup
-  constexpr int E = Chunk<T>::E;         // elements per 16-byte chunk
-  constexpr int CPR = D / E;             // chunks per key row
-  constexpr int KPT = BN * CPR / 256;    // keys each thread loads per step
-  constexpr int KS = D / 16;             // 16-deep steps over head_dim
-  constexpr int DB = D / 32;             // 32-row blocks of O^T
-  constexpr int KSTR = D + E;            // K row stride in LDS (16-byte pad)
-  constexpr int VSTR = BN + 4;           // V^T row stride in LDS
-  static_assert(KPT == 4, "tile loader assumes 4 keys per thread");
-  static_assert(NT * HG == 4, "four wavefronts per workgroup");
+  constexpr int BN = 64;  // keys per step
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int E = 16 / int(sizeof(T));
+  constexpr int TILE = BN * kRowBytes / int(sizeof(T));
+  static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
+  static_assert(4 % HG == 0, "four wavefronts per workgroup");
 
-  __shared__ __attribute__((aligned(16))) T sK[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) T sVt[D * VSTR];
+  __shared__ __attribute__((aligned(16))) T sK0[TILE];
+  __shared__ __attribute__((aligned(16))) T sV0[TILE];
+  __shared__ __attribute__((aligned(16))) T sK1[TILE];
+  __shared__ __attribute__((aligned(16))) T sV1[TILE];
+  __shared__ Span sSpans[kMaxSpans];
 
   int tile_rank, group;
   decode_item(blockIdx.x, a.Hq / HG, tile_rank, group);
@@ -64,8 +71,9 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   const float c = a.scale * kLog2e;
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
-  const T* __restrict__ k = static_cast<const T*>(a.k);
-  const T* __restrict__ v = static_cast<const T*>(a.v);
+  const T* kg = static_cast<const T*>(a.k) + (size_t)g * D;
+  const T* vg = static_cast<const T*>(a.v) + (size_t)g * D;
+  const size_t row_stride = (size_t)a.Hkv * D;
 
   frag qf[KS];
   {
@@ -79,85 +87,105 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  SpanCursor cur{a.spans + a.span_ptr[tile.seg], 0};
-  const int dc = tid % CPR, kg = tid / CPR;
-  const size_t row_stride = (size_t)a.Hkv * D;
-  const T* kbase = k + (size_t)g * D + dc * E;
-  const T* vbase = v + (size_t)g * D + dc * E;
-
-  for (int v0 = 0; v0 < kv_len; v0 += BN) {
-    Chunk<T> kc[KPT], vc[KPT];
+  // DMA: wave w, instruction r fills tile chunks [(4w+r)*64, +64): lane l
+  // writes row (4w+r)*4 + l/16, physical chunk l%16 (logical chunk l%16 ^ f(row)).
+  stage_spans(sSpans, a.span_ptr, a.spans, tile.seg);
+  __syncthreads();
+  SpanCursor cur{sSpans, 0};
+  int lrow[4], lchunk[4];
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int vk = v0 + kg * KPT + r;
-      if (vk < kv_len) {
-        const size_t off = (size_t)cur.phys(vk) * row_stride;
-        kc[r] = load_chunk<T>(kbase + off);
-        vc[r] = load_chunk<T>(vbase + off);
-      } else {
-        kc[r] = zero_chunk<T>();
-        vc[r] = zero_chunk<T>();
-      }
+  for (int r = 0; r < 4; ++r) {
+    lrow[r] = (4 * wave + r) * 4 + (lane >> 4);
+    lchunk[r] = (lane & 15) ^ swz(lrow[r]);
+  }
+  auto issue = [&](int v0, T* sK, T* sV) {
+    size_t off[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int vk = min(v0 + lrow[r], kv_len - 1);  // past the path: any valid row, masked
+      off[r] = (size_t)cur.phys(vk) * row_stride + lchunk[r] * E;
     }
-    __syncthreads();  // previous step finished reading sK / sVt
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) store_chunk<T>(&sK[(kg * KPT + r) * KSTR + dc * E], kc[r]);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      quad t4;
-#pragma unroll
-      for (int r = 0; r < KPT; ++r) t4[r] = vc[r].elem(e);
-      *reinterpret_cast<quad*>(&sVt[(dc * E + e) * VSTR + kg * KPT]) = t4;
+    for (int r = 0; r < 4; ++r) {
+      dma16(kg + off[r], sK + (4 * wave + r) * 64 * E);
+      dma16(vg + off[r], sV + (4 * wave + r) * 64 * E);
     }
-    __syncthreads();
+  };
 
-    // S^T = K Q^T for two 32-key blocks
+  auto compute = [&](int v0, const T* sK, const T* sV) {
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        M::mma(s[kb], load_frag<T>(&sK[(kb * 32 + col) * KSTR + ks * 16 + half * 8]), qf[ks]);
+        M::mma(s[kb], tile_row_frag<T>(sK, kb * 32 + col, ks * 16 + half * 8), qf[ks]);
 
-    // online softmax (base 2, scale folded in)
-    const bool need_mask = v0 + BN - 1 > wave_pos0;
+    if (v0 + BN - 1 > wave_pos0) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (v0 + kb * 32 + c_row(i, half) > qpos) s[kb][i] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[kb][i] * c;
-        if (need_mask && v0 + kb * 32 + c_row(i, half) > qpos) x = -INFINITY;
-        s[kb][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    const bool grow = mx > m + kRescaleSlack;
+    const float mnew = grow ? mx : m;
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    if (__any(grow)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    l *= alpha;
     m = mnew;
-    float rs = 0.f;
+
+    // the denominator sums the fp32 probabilities; only the P*V operand is
+    // rounded to the input type
     frag pf[2][2];
+    float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][i] - mnew);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -m));
         rs += p;
         pf[kb][i >> 3][i & 7] = to_elem<T>(p);
       }
-    l = l * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    l += rs;
 
-    // O^T += V^T P^T
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-          M::mma(o[db], load_frag_split<T>(&sVt[(db * 32 + col) * VSTR + kb * 32 + 16 * hh + 4 * half]),
-                 pf[kb][hh]);
+          M::mma(o[db], tile_tr_frag<T>(sV, kb * 32 + 16 * hh, db * 32, lane), pf[kb][hh]);
+  };
+
+  // two statically named buffers, so the compiler can tell the LDS written by
+  // the in-flight DMA from the LDS being read
+  issue(0, sK0, sV0);
+  wait_dma();
+  __syncthreads();
+  for (int v0 = 0;;) {
+    const bool more1 = v0 + BN < kv_len;
+    if (more1) issue(v0 + BN, sK1, sV1);
+    compute(v0, sK0, sV0);
+    if (!more1) break;
+    wait_dma();
+    __syncthreads();
+    v0 += BN;
+    const bool more0 = v0 + BN < kv_len;
+    if (more0) issue(v0 + BN, sK0, sV0);
+    compute(v0, sK1, sV1);
+    if (!more0) break;
+    wait_dma();
+    __syncthreads();
+    v0 += BN;
   }
 
   l += __shfl_xor(l, 32);

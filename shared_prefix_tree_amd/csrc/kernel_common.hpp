@@ -108,6 +108,86 @@ __device__ inline typename Mfma<T>::frag load_frag_split(const T* p) {
   return Mfma<T>::cat(*reinterpret_cast<const quad*>(p), *reinterpret_cast<const quad*>(p + 8));
 }
 
+// ---------------------------------------------------------------------------
+// LDS tiles: ROWS x D elements, one 256-byte row per token, stored row-major
+// with the 16-byte chunks of row r XOR-swizzled by f(r) = ((r&3)<<1)|((r>>2)&1).
+// Both read patterns are then free of bank conflicts (32 banks x 4 B):
+//   * row reads (ds_read_b128): 8 lanes read 8 consecutive rows at one chunk;
+//     f(r) takes 8 distinct values on any 8 consecutive rows;
+//   * transposing reads (ds_read_b64_tr_b16): a 16-lane group reads 4
+//     consecutive rows (starting at a multiple of 4) x 32 bytes; f(r) >> 1
+//     takes 4 distinct values there, so the four 8-bank windows are disjoint.
+// Tiles are filled with global_load_lds_dwordx4: lane l of a wave writes the
+// 16 bytes at (wave base + 16 l), so each lane loads the global chunk that
+// belongs at that swizzled position.
+
+constexpr int kRowBytes = 256;
+constexpr int kChunksPerRow = kRowBytes / 16;
+
+__device__ inline int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// element offset of logical chunk `chunk` of `row` in a tile of element type T
+template <typename T>
+__device__ inline int tile_off(int row, int chunk) {
+  return row * (kRowBytes / int(sizeof(T))) + ((chunk ^ swz(row)) * (16 / int(sizeof(T))));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Asynchronous 16-byte-per-lane copy global -> LDS (wave-uniform LDS base).
+__device__ inline void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+}
+
+__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Fragment of 8 consecutive elements [e0, e0+8) of a tile row (e0 % 8 == 0).
+template <typename T>
+__device__ inline typename Mfma<T>::frag tile_row_frag(const T* tile, int row, int e0) {
+  constexpr int E = 16 / int(sizeof(T));
+  if constexpr (E == 8) {
+    return *reinterpret_cast<const typename Mfma<T>::frag*>(tile + tile_off<T>(row, e0 / E));
+  } else {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + tile_off<T>(row, e0 / E));
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(tile + tile_off<T>(row, e0 / E + 1));
+    return typename Mfma<T>::frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed A fragment: lane l gets column d = d0 + (l % 32) of the tile and
+// the 8 rows {r0 + 4h + 0..3} and {r0 + 8 + 4h + 0..3}, h = l / 32 -- the
+// rows a C-layout B fragment covers (see the header comment).  bf16 uses two
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
+// of the 8-byte pieces read by lanes 4j + i/4 (j = 0..3), so lane 4j+k of
+// group g reads row r0 + 4(g/2) + j at column d0 + 16(g%2) + 4k.  fp32 reads
+// the same elements one by one.
+template <typename T>
+__device__ inline typename Mfma<T>::frag tile_tr_frag(const T* tile, int r0, int d0, int lane) {
+  if constexpr (sizeof(T) == 2) {
+    const int g = lane >> 4, k = lane & 15;
+    const int row = r0 + 4 * (g >> 1) + (k >> 2);
+    const int d = d0 + 16 * (g & 1) + 4 * (k & 3);
+    const T* p0 = tile + tile_off<T>(row, d >> 3) + (d & 7);
+    const T* p1 = tile + tile_off<T>(row + 8, d >> 3) + (d & 7);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p0);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p1);
+    const bf16x4 lo = __builtin_bit_cast(bf16x4, a);
+    const bf16x4 hi = __builtin_bit_cast(bf16x4, b);
+    return Mfma<T>::cat(lo, hi);
+  } else {
+    const int h = lane >> 5, d = d0 + (lane & 31);
+    typename Mfma<T>::frag f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = r0 + 8 * (j >> 2) + 4 * h + (j & 3);
+      f[j] = tile[tile_off<T>(row, d >> 2) + (d & 3)];
+    }
+    return f;
+  }
+}
+
 // Row offset of C-layout value i for lane half `half`.
 __device__ inline constexpr int c_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
 
@@ -132,10 +212,22 @@ __device__ inline void decode_item(int b, int n_groups, int& tile_rank, int& gro
   }
 }
 
+// A segment's merged spans are staged in LDS once per workgroup, so span
+// lookups use the LDS counter and never wait behind in-flight global->LDS
+// copies.  A segment may have at most kMaxSpans spans (checked by the host).
+constexpr int kMaxSpans = 256;
+
+// Copies the spans of segment `seg` to LDS (every thread takes part; the
+// caller synchronises before use).
+__device__ inline void stage_spans(Span* lds_spans, const int32_t* span_ptr, const Span* spans, int seg) {
+  const int first = span_ptr[seg], n = span_ptr[seg + 1] - first;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) lds_spans[i] = spans[first + i];
+}
+
 // Monotone cursor over a segment's merged spans: maps a virtual key position
 // of the reconstructed sequence to its physical token.
 struct SpanCursor {
-  const Span* spans;
+  const Span* spans;  // LDS copy
   int cur;
   __device__ inline int phys(int v) {
     while (v >= spans[cur].virt + spans[cur].len) ++cur;

@@ -112,6 +112,7 @@ bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int3
       virt += seg_len[a];
     }
     p.span_ptr[s + 1] = int32_t(p.spans.size());
+    p.max_spans = std::max(p.max_spans, p.span_ptr[s + 1] - p.span_ptr[s]);
   }
 
   // query tiles per size, longest key range first (stable on ties)

@@ -53,7 +53,7 @@ constexpr int kKTile = 64;
 inline int qtile_index(int tq) { return tq == 32 ? 0 : tq == 64 ? 1 : tq == 128 ? 2 : -1; }
 
 struct HostPlan {
-  int32_t T = 0, S = 0, num_roots = 0, max_depth = 0;
+  int32_t T = 0, S = 0, num_roots = 0, max_depth = 0, max_spans = 0;
   int64_t max_path = 0, pairs = 0;
   std::vector<int32_t> parent, start, len, depth, prefix, end;
   std::vector<int32_t> span_ptr;

@@ -169,3 +169,32 @@ def test_null_arguments_are_rejected_without_a_device():
     assert lib.tree_attn_bwd_workspace_bytes(p.handle, ctypes.byref(shape)) == 256
     rc = lib.tree_attn_bwd(*([one] * 6), p.handle, ctypes.byref(shape), one, one, one, one, 1 << 20, None)
     assert rc == b.INVALID_ARGUMENT
+
+
+def test_backward_stages_reject_null_inputs_before_launch():
+    """Every backward stage checks each pointer it reads (lse included) before
+    any launch; a host-only plan would be rejected later, so a NULL pointer
+    must be what is reported."""
+    import ctypes
+
+    lib = sp.library()
+    p = sp.Plan([-1], [0], [4], device=False)
+    shape = b.Shape(4, 1, 1, 64, b.FP32, 0.0)
+    one = ctypes.c_void_p(256)  # never dereferenced
+    ws = ctypes.c_size_t(1 << 20)
+    assert lib.tree_attn_bwd_rowstat(one, None, one, p.handle, ctypes.byref(shape), one, ws, None) == b.INVALID_ARGUMENT
+    assert "NULL" in lib.tree_attn_last_error().decode()
+    assert lib.tree_attn_bwd_rowstat(None, one, one, p.handle, ctypes.byref(shape), one, ws, None) == b.INVALID_ARGUMENT
+    assert lib.tree_attn_bwd_rowstat(one, one, None, p.handle, ctypes.byref(shape), one, ws, None) == b.INVALID_ARGUMENT
+    args = [one] * 5
+    for i in range(5):  # q, k, v, lse, dout
+        a = list(args)
+        a[i] = None
+        assert lib.tree_attn_bwd_dkdv(*a, p.handle, ctypes.byref(shape), one, one, one, ws, None) == b.INVALID_ARGUMENT
+        assert "NULL" in lib.tree_attn_last_error().decode()
+        assert lib.tree_attn_bwd_dq(*a, p.handle, ctypes.byref(shape), one, one, ws, None) == b.INVALID_ARGUMENT
+    assert lib.tree_attn_bwd_dkdv(*args, p.handle, ctypes.byref(shape), None, one, one, ws, None) == b.INVALID_ARGUMENT
+    assert lib.tree_attn_bwd_dq(*args, p.handle, ctypes.byref(shape), None, one, ws, None) == b.INVALID_ARGUMENT
+    # with every pointer present the host-only plan is what is reported
+    assert lib.tree_attn_bwd_rowstat(one, one, one, p.handle, ctypes.byref(shape), one, ws, None) == b.INVALID_ARGUMENT
+    assert "host-only" in lib.tree_attn_last_error().decode()

@@ -280,3 +280,22 @@ def test_rejected_calls_write_nothing():
     with pytest.raises(sp.TreeAttnError) as e:
         sp.tree_attn_bwd(q, k, k, out2, lse2, q, plan, workspace=small)
     assert e.value.code == b.INVALID_ARGUMENT
+
+
+def test_staged_backward_matches_one_call():
+    """tree_attn_bwd_rowstat / _dkdv / _dq in sequence give bitwise the same
+    gradients as tree_attn_bwd (the staged path the benchmark times)."""
+    sp = lib()
+    rng = np.random.default_rng(41)
+    topo = random_forest(rng, max_tokens=900, max_len=200, max_depth=4)
+    arrs = make_inputs(rng, topo.total_tokens, 8, 2, 128, "bf16")
+    t = {k: to_torch(v, "bf16", "cuda:0") for k, v in arrs.items()}
+    plan = sp.Plan.from_topology(topo)
+    out, lse = sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan)
+    ref = sp.tree_attn_bwd(t["q"], t["k"], t["v"], out, lse, t["dout"], plan)
+    ws = torch.empty(sp.bwd_workspace_bytes(plan, t["q"], t["k"]), dtype=torch.uint8, device="cuda:0")
+    got = sp.tree_attn_bwd_stages(t["q"], t["k"], t["v"], out, lse, t["dout"], plan, torch.empty_like(t["q"]),
+                                  torch.empty_like(t["k"]), torch.empty_like(t["v"]), ws)
+    torch.cuda.synchronize()
+    for a, b_ in zip(ref, got):
+        assert torch.equal(a, b_)
