@@ -16,9 +16,9 @@
 //   2. dkdv (key-major): a workgroup owns 64 keys of one segment and one
 //      key/value head; in DFS pre-order the queries that see key j are the
 //      contiguous range [j, subtree_end(seg(j))), so it loops over that range
-//      (all G query heads) and accumulates dK, dV in registers:
-//        S = Q K^T, P = exp(S - lse), dV^T += dO^T P,
-//        dP = dO V^T, dS = P (dP - delta), dK^T += Q^T dS;
+//      (all G query heads) twice, accumulating in registers
+//        pass 1: S = Q K^T, P = exp(S - lse), dV^T += dO^T P,
+//        pass 2: S, P again, dP = dO V^T, dS = P (dP - delta), dK^T += Q^T dS;
 //      the 64-query Q / dO tiles and their lse / delta are copied straight
 //      into LDS (two buffers, one barrier per step); Q^T and dO^T fragments
 //      come from the transposing LDS load of the same row-major tiles;
@@ -69,9 +69,15 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
 
 // ---------------------------------------------------------------------------
 // 2. dK / dV, key-major
+//
+// The workgroup makes two passes over its query range: the first
+// accumulates dV^T += dO^T P, the second dK^T += Q^T dS.  Recomputing S in
+// the second pass costs 8 of every 40 MFMA steps, but only one fp32
+// accumulator block is live at a time, which keeps two wavefronts per SIMD
+// resident (one fused pass needs ~290 registers and runs one wave per SIMD).
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void tree_attn_dkdv_kernel(BwdArgs a) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   using quad = typename M::quad;
@@ -87,7 +93,10 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) T sO0[TILE];
   __shared__ __attribute__((aligned(16))) T sQ1[TILE];
   __shared__ __attribute__((aligned(16))) T sO1[TILE];
-  __shared__ float sL0[BM], sD0[BM], sL1[BM], sD1[BM];
+  __shared__ __attribute__((aligned(16))) float sL0[BM];
+  __shared__ __attribute__((aligned(16))) float sD0[BM];
+  __shared__ __attribute__((aligned(16))) float sL1[BM];
+  __shared__ __attribute__((aligned(16))) float sD1[BM];
 
   int tile_rank, g;
   decode_item(blockIdx.x, a.Hkv, tile_rank, g);
@@ -105,22 +114,11 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ dout = static_cast<const T*>(a.dout);
   const float* lse2 = a.delta + (size_t)a.Hq * a.T;
+  const size_t kv_off = ((size_t)ktok * a.Hkv + g) * D + half * 8;
 
-  frag kf[KS], vf[KS];
-  {
-    const size_t off = ((size_t)ktok * a.Hkv + g) * D + half * 8;
+  frag kf[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = load_frag<T>(static_cast<const T*>(a.k) + off + ks * 16);
-      vf[ks] = load_frag<T>(static_cast<const T*>(a.v) + off + ks * 16);
-    }
-  }
-  f32x16 dk[DB], dv[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dk[db] = f32x16{};
-    dv[db] = f32x16{};
-  }
+  for (int ks = 0; ks < KS; ++ks) kf[ks] = load_frag<T>(static_cast<const T*>(a.k) + kv_off + ks * 16);
 
   const int nblk = (tile.qend - tile.k0 + BM - 1) / BM;
   const int n_steps = a.G * nblk;
@@ -131,102 +129,155 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     lchunk[r] = (lane & 15) ^ swz(lrow[r]);
   }
   // rows past the query range read a valid row and are masked to P = 0
+  // element offsets fit in 32 bits (tensors are limited to 2^31 elements)
   auto issue = [&](int step, T* sQ, T* sO, float* sL, float* sD) {
     const int h = g * a.G + step / nblk;
     const int i0 = tile.k0 + (step % nblk) * BM;
+    const int last = tile.qend - 1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int qi = min(i0 + lrow[r], tile.qend - 1);
-      const size_t off = ((size_t)qi * a.Hq + h) * D + lchunk[r] * E;
+      const int off = (min(i0 + lrow[r], last) * a.Hq + h) * D + lchunk[r] * E;
       dma16(q + off, sQ + (4 * wave + r) * 64 * E);
       dma16(dout + off, sO + (4 * wave + r) * 64 * E);
     }
     if (wave < 2) {
-      const size_t at = (size_t)h * a.T + min(i0 + lane, tile.qend - 1);
+      const int at = h * a.T + min(i0 + lane, last);
       dma4(wave == 0 ? lse2 + at : a.delta + at, wave == 0 ? sL : sD);
     }
   };
 
-  auto compute = [&](int step, const T* sQ, const T* sO, const float* sL, const float* sD) {
-    const int i0 = tile.k0 + (step % nblk) * BM;
-    f32x16 s = f32x16{}, dp = f32x16{};
+  // lse2 / delta of this lane's 16 C-layout query rows: 4 runs of 4
+  auto row_stats = [&](const float* sX, float (&x)[16]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      M::mma(s, tile_row_frag<T>(sQ, qh * 32 + col, ks * 16 + half * 8), kf[ks]);
-      M::mma(dp, tile_row_frag<T>(sO, qh * 32 + col, ks * 16 + half * 8), vf[ks]);
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 v4 = *reinterpret_cast<const f32x4*>(sX + qh * 32 + 8 * j + 4 * half);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * j + e] = v4[e];
     }
-    const bool need_mask = i0 + qh * 32 < tile.k0 + kb * 32 + 31 || i0 + qh * 32 + 31 >= tile.qend;
-    frag pf[2], dsf[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int qr = qh * 32 + c_row(i, half);
-      float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -sL[qr]));
-      if (need_mask && (i0 + qr < jkey || i0 + qr >= tile.qend)) p = 0.f;
-      pf[i >> 3][i & 7] = to_elem<T>(p);
-      dsf[i >> 3][i & 7] = to_elem<T>(p * (dp[i] - sD[qr]));
-    }
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        M::mma(dv[db], tile_tr_frag<T>(sO, qh * 32 + 16 * hh, db * 32, lane), pf[hh]);
-        M::mma(dk[db], tile_tr_frag<T>(sQ, qh * 32 + 16 * hh, db * 32, lane), dsf[hh]);
-      }
   };
 
-  issue(0, sQ0, sO0, sL0, sD0);
-  wait_dma();
-  __syncthreads();
-  for (int step = 0;;) {
-    const bool more1 = step + 1 < n_steps;
-    if (more1) issue(step + 1, sQ1, sO1, sL1, sD1);
-    compute(step, sQ0, sO0, sL0, sD0);
-    if (!more1) break;
-    wait_dma();
-    __syncthreads();
-    ++step;
-    const bool more0 = step + 1 < n_steps;
-    if (more0) issue(step + 1, sQ0, sO0, sL0, sD0);
-    compute(step, sQ1, sO1, sL1, sD1);
-    if (!more0) break;
-    wait_dma();
-    __syncthreads();
-    ++step;
-  }
-
-  // fixed-order reduction of the two query halves, then one store per key:
-  // the qh = 1 waves park their dK (in sQ0 / sO0) and dV (in sQ1 / sO1)
-  __syncthreads();
-  float* rk = reinterpret_cast<float*>(kb == 0 ? sQ0 : sO0);
-  float* rv = reinterpret_cast<float*>(kb == 0 ? sQ1 : sO1);
-  if (qh == 1) {
+  // P for this wave's 32 queries x 32 keys, rounded to the input type
+  auto probs = [&](int step, const T* sQ, const float* sL, frag (&pf)[2]) {
+    const int i0 = tile.k0 + (step % nblk) * BM;
+    f32x16 s = f32x16{};
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int ks = 0; ks < KS; ++ks) M::mma(s, tile_row_frag<T>(sQ, qh * 32 + col, ks * 16 + half * 8), kf[ks]);
+    sched_pipeline<kLdsAhead, KS, frag_reads<T>(false)>();
+    float lq[16];
+    row_stats(sL, lq);
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lq[i]));
+    // diagonal block (queries before the key) or rows past the range: wave-uniform
+    if (__builtin_amdgcn_readfirstlane(int(i0 + qh * 32 < tile.k0 + kb * 32 + 31 ||
+                                           i0 + qh * 32 + 31 >= tile.qend))) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        rk[(db * 16 + i) * 64 + lane] = dk[db][i];
-        rv[(db * 16 + i) * 64 + lane] = dv[db][i];
+        const int qi = i0 + qh * 32 + c_row(i, half);
+        if (qi < jkey || qi >= tile.qend) p[i] = 0.f;
       }
-  }
-  __syncthreads();
-  if (qh == 0 && key_valid) {
-    T* dkp = static_cast<T*>(a.dk) + ((size_t)jkey * a.Hkv + g) * D;
-    T* dvp = static_cast<T*>(a.dv) + ((size_t)jkey * a.Hkv + g) * D;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = to_elem<T>(p[i]);
+  };
+
+  f32x16 acc[DB];
+  frag vf[KS];
+
+  // dV pass: dV^T += dO^T P
+  auto step_v = [&](int step, const T* sQ, const T* sO, const float* sL, const float*) {
+    frag pf[2];
+    probs(step, sQ, sL, pf);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        quad tk, tv;
+      for (int hh = 0; hh < 2; ++hh)
+        M::mma(acc[db], tile_tr_frag<T>(sO, qh * 32 + 16 * hh, db * 32, lane), pf[hh]);
+    sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
+  };
+  // dK pass: dP = dO V^T, dS = P (dP - delta), dK^T += Q^T dS; dS uses the
+  // same rounded P as the dV pass
+  auto step_k = [&](int step, const T* sQ, const T* sO, const float* sL, const float* sD) {
+    frag pf[2];
+    probs(step, sQ, sL, pf);
+    f32x16 dp = f32x16{};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = grp * 4 + e;
-          tk[e] = to_elem<T>((dk[db][i] + rk[(db * 16 + i) * 64 + lane]) * a.scale);
-          tv[e] = to_elem<T>(dv[db][i] + rv[(db * 16 + i) * 64 + lane]);
+    for (int ks = 0; ks < KS; ++ks) M::mma(dp, tile_row_frag<T>(sO, qh * 32 + col, ks * 16 + half * 8), vf[ks]);
+    sched_pipeline<kLdsAhead, KS, frag_reads<T>(false)>();
+    float dl[16];
+    row_stats(sD, dl);
+    frag dsf[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dsf[i >> 3][i & 7] = to_elem<T>(float(pf[i >> 3][i & 7]) * (dp[i] - dl[i]));
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        M::mma(acc[db], tile_tr_frag<T>(sQ, qh * 32 + 16 * hh, db * 32, lane), dsf[hh]);
+    sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
+  };
+
+  // one pass over all steps: two statically named buffers, one barrier per step
+  auto run = [&](auto&& step_fn) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    issue(0, sQ0, sO0, sL0, sD0);
+    wait_dma();
+    __syncthreads();
+    for (int step = 0;;) {
+      const bool more1 = step + 1 < n_steps;
+      if (more1) issue(step + 1, sQ1, sO1, sL1, sD1);
+      step_fn(step, sQ0, sO0, sL0, sD0);
+      if (!more1) break;
+      wait_dma();
+      __syncthreads();
+      ++step;
+      const bool more0 = step + 1 < n_steps;
+      if (more0) issue(step + 1, sQ0, sO0, sL0, sD0);
+      step_fn(step, sQ1, sO1, sL1, sD1);
+      if (!more0) break;
+      wait_dma();
+      __syncthreads();
+      ++step;
+    }
+    __syncthreads();  // every wave is done with the tiles
+  };
+
+  // fixed-order reduction of the two query halves, then one store per key:
+  // the qh = 1 waves park their partial in sQ0 (kb = 0) / sO0 (kb = 1)
+  auto reduce_store = [&](T* out, float mul) {
+    float* r = reinterpret_cast<float*>(kb == 0 ? sQ0 : sO0);
+    if (qh == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) r[(db * 16 + i) * 64 + lane] = acc[db][i];
+    }
+    __syncthreads();
+    if (qh == 0 && key_valid) {
+      T* op = out + ((size_t)jkey * a.Hkv + g) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          quad t4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = grp * 4 + e;
+            t4[e] = to_elem<T>((acc[db][i] + r[(db * 16 + i) * 64 + lane]) * mul);
+          }
+          *reinterpret_cast<quad*>(op + db * 32 + grp * 8 + half * 4) = t4;
         }
-        *reinterpret_cast<quad*>(dkp + db * 32 + grp * 8 + half * 4) = tk;
-        *reinterpret_cast<quad*>(dvp + db * 32 + grp * 8 + half * 4) = tv;
-      }
-  }
+    }
+    __syncthreads();  // the parking buffer is reused by the next pass
+  };
+
+  run(step_v);
+  reduce_store(static_cast<T*>(a.dv), 1.f);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) vf[ks] = load_frag<T>(static_cast<const T*>(a.v) + kv_off + ks * 16);
+  run(step_k);
+  reduce_store(static_cast<T*>(a.dk), a.scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -268,7 +319,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
 
   const T* kg = static_cast<const T*>(a.k) + (size_t)g * D;
   const T* vg = static_cast<const T*>(a.v) + (size_t)g * D;
-  const size_t row_stride = (size_t)a.Hkv * D;
+  const int row_stride = a.Hkv * D;
 
   frag qf[KS], of[KS];
   {
@@ -295,12 +346,22 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
     lrow[r] = (4 * wave + r) * 4 + (lane >> 4);
     lchunk[r] = (lane & 15) ^ swz(lrow[r]);
   }
+  // Row addresses of the 64 keys [v0, v0 + 64).  Spans are usually much
+  // longer than a step, so when the whole step lies in one span (checked
+  // with a workgroup-uniform cursor) the rows are contiguous from one base;
+  // otherwise every lane looks up its own rows.  Rows past the path read
+  // any valid row and are masked.  Offsets fit in 32 bits.
+  int ucur = 0;
   auto issue = [&](int v0, T* sK, T* sV) {
-    size_t off[4];
+    while (v0 >= sSpans[ucur].virt + sSpans[ucur].len) ++ucur;
+    const int sv = sSpans[ucur].virt, sl = sSpans[ucur].len, spp = sSpans[ucur].phys;
+    int off[4];
+    if (__builtin_amdgcn_readfirstlane(int(v0 + BN <= sv + sl && v0 + BN <= kv_len))) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int vk = min(v0 + lrow[r], kv_len - 1);
-      off[r] = (size_t)cur.phys(vk) * row_stride + lchunk[r] * E;
+      for (int r = 0; r < 4; ++r) off[r] = (spp + (v0 - sv) + lrow[r]) * row_stride + lchunk[r] * E;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) off[r] = cur.phys(min(v0 + lrow[r], kv_len - 1)) * row_stride + lchunk[r] * E;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -318,6 +379,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
         M::mma(s[kb], tile_row_frag<T>(sK, kb * 32 + col, ks * 16 + half * 8), qf[ks]);
         M::mma(dp[kb], tile_row_frag<T>(sV, kb * 32 + col, ks * 16 + half * 8), of[ks]);
       }
+    sched_pipeline<kLdsAhead, 4 * KS, frag_reads<T>(false)>();
     const bool need_mask = v0 + BN - 1 > wave_pos0;
     frag dsf[2][2];
 #pragma unroll
@@ -335,6 +397,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
           M::mma(dq[db], tile_tr_frag<T>(sK, kb * 32 + 16 * hh, db * 32, lane), dsf[kb][hh]);
+    sched_pipeline<kLdsAhead, 4 * DB, frag_reads<T>(true)>();
   };
 
   issue(0, sK0, sV0);

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* kg = static_cast<const T*>(a.k) + (size_t)g * D;
   const T* vg = static_cast<const T*>(a.v) + (size_t)g * D;
-  const size_t row_stride = (size_t)a.Hkv * D;
+  const int row_stride = a.Hkv * D;
 
   frag qf[KS];
   {
@@ -98,12 +98,22 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
     lrow[r] = (4 * wave + r) * 4 + (lane >> 4);
     lchunk[r] = (lane & 15) ^ swz(lrow[r]);
   }
+  // Row addresses of the 64 keys [v0, v0 + 64).  Spans are usually much
+  // longer than a step, so when the whole step lies in one span (checked
+  // with a workgroup-uniform cursor) the rows are contiguous from one base;
+  // otherwise every lane looks up its own rows.  Rows past the path read
+  // any valid row and are masked.  Offsets fit in 32 bits.
+  int ucur = 0;
   auto issue = [&](int v0, T* sK, T* sV) {
-    size_t off[4];
+    while (v0 >= sSpans[ucur].virt + sSpans[ucur].len) ++ucur;
+    const int sv = sSpans[ucur].virt, sl = sSpans[ucur].len, spp = sSpans[ucur].phys;
+    int off[4];
+    if (__builtin_amdgcn_readfirstlane(int(v0 + BN <= sv + sl && v0 + BN <= kv_len))) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int vk = min(v0 + lrow[r], kv_len - 1);  // past the path: any valid row, masked
-      off[r] = (size_t)cur.phys(vk) * row_stride + lchunk[r] * E;
+      for (int r = 0; r < 4; ++r) off[r] = (spp + (v0 - sv) + lrow[r]) * row_stride + lchunk[r] * E;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) off[r] = cur.phys(min(v0 + lrow[r], kv_len - 1)) * row_stride + lchunk[r] * E;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -119,6 +129,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         M::mma(s[kb], tile_row_frag<T>(sK, kb * 32 + col, ks * 16 + half * 8), qf[ks]);
+    sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
 
     if (v0 + BN - 1 > wave_pos0) {
 #pragma unroll
@@ -164,6 +175,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
           M::mma(o[db], tile_tr_frag<T>(sV, kb * 32 + 16 * hh, db * 32, lane), pf[kb][hh]);
+    sched_pipeline<kLdsAhead, 4 * DB, frag_reads<T>(true)>();
   };
 
   // two statically named buffers, so the compiler can tell the LDS written by

@@ -110,13 +110,16 @@ __device__ inline typename Mfma<T>::frag load_frag_split(const T* p) {
 
 // ---------------------------------------------------------------------------
 // LDS tiles: ROWS x D elements, one 256-byte row per token, stored row-major
-// with the 16-byte chunks of row r XOR-swizzled by f(r) = ((r&3)<<1)|((r>>2)&1).
-// Both read patterns are then free of bank conflicts (32 banks x 4 B):
-//   * row reads (ds_read_b128): 8 lanes read 8 consecutive rows at one chunk;
-//     f(r) takes 8 distinct values on any 8 consecutive rows;
-//   * transposing reads (ds_read_b64_tr_b16): a 16-lane group reads 4
-//     consecutive rows (starting at a multiple of 4) x 32 bytes; f(r) >> 1
-//     takes 4 distinct values there, so the four 8-bank windows are disjoint.
+// with the 16 16-byte chunks of row r XOR-swizzled by
+// f(r) = ((r&3)<<2) | ((r>>2)&3).  With 64 banks x 4 B (256 bytes per cycle)
+// both read patterns are free of bank conflicts:
+//   * row reads (ds_read_b128, 16 lanes per cycle): 16 consecutive rows
+//     (aligned) at one logical chunk land on 16 distinct chunks, since f takes
+//     all 16 values there;
+//   * transposing reads (ds_read_b64_tr_b16, 32 lanes per cycle): 4
+//     consecutive rows (aligned) x 4 consecutive chunks (aligned): with
+//     chunk = 4m + x and f = 4y + k the physical chunk is 4(m^y) + (x^k), 16
+//     distinct values.
 // Tiles are filled with global_load_lds_dwordx4: lane l of a wave writes the
 // 16 bytes at (wave base + 16 l), so each lane loads the global chunk that
 // belongs at that swizzled position.
@@ -124,7 +127,7 @@ __device__ inline typename Mfma<T>::frag load_frag_split(const T* p) {
 constexpr int kRowBytes = 256;
 constexpr int kChunksPerRow = kRowBytes / 16;
 
-__device__ inline int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ inline int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 // element offset of logical chunk `chunk` of `row` in a tile of element type T
 template <typename T>
@@ -185,6 +188,36 @@ __device__ inline typename Mfma<T>::frag tile_tr_frag(const T* tile, int r0, int
       f[j] = tile[tile_off<T>(row, d >> 2) + (d & 3)];
     }
     return f;
+  }
+}
+
+// Software pipelining of LDS fragment reads against the products that use
+// them.  After N products, each fed by an A fragment read from LDS, this
+// asks the scheduler for: AHEAD fragments' reads, then (one product, one
+// fragment's reads) repeated, then the last AHEAD products -- so reads run
+// AHEAD fragments in front of the matrix cores instead of each read waiting
+// right before its product.  READS = LDS instructions per fragment (bf16:
+// one ds_read_b128 per row fragment, two ds_read_b64_tr_b16 per transposed
+// one; fp32 needs more and is not pipelined).
+constexpr int kLdsAhead = 3;
+constexpr int kSchedMfma = 0x0008;
+constexpr int kSchedDsRead = 0x0100;
+
+template <typename T>
+constexpr int frag_reads(bool transposed) {
+  return sizeof(T) == 2 ? (transposed ? 2 : 1) : 0;
+}
+
+template <int AHEAD, int N, int READS>
+__device__ inline void sched_pipeline() {
+  if constexpr (READS > 0 && N > AHEAD) {
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AHEAD * READS, 0);
+#pragma unroll
+    for (int i = 0; i < N - AHEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, AHEAD, 0);
   }
 }
 
