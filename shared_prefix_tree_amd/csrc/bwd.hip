@@ -15,24 +15,19 @@
 //      lse2[h,i] = lse[h,i] * log2(e), into the workspace;
 //   2. dkdv (key-major): a workgroup owns 64 keys of one segment and one
 //      key/value head; in DFS pre-order the queries that see key j are the
-//      contiguous range [j, subtree_end(seg(j))), so it loops over that range
-//      (all G query heads) twice, accumulating in registers
-//        pass 1: S = Q K^T, P = exp(S - lse), dV^T += dO^T P,
-//        pass 2: S, P again, dP = dO V^T, dS = P (dP - delta), dK^T += Q^T dS;
-//      the 64-query Q / dO tiles and their lse / delta are copied straight
-//      into LDS (two buffers, one barrier per step); Q^T and dO^T fragments
-//      come from the transposing LDS load of the same row-major tiles;
+//      contiguous range [j, subtree_end(seg(j))), so it walks that range
+//      (all G query heads) once, 64 queries per step; half of its
+//      wavefronts form S = Q K^T, P = exp(S - lse) and dV^T += dO^T P, the
+//      other half, given P through LDS, dP = dO V^T, dS = P (dP - delta) and
+//      dK^T += Q^T dS; the Q / dO tiles and their lse / delta are copied
+//      straight into a ring of LDS buffers; Q^T and dO^T fragments come from
+//      the transposing LDS load of the same row-major tiles;
 //   3. dq (query-major): the forward's walk over the ancestor path,
 //        S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - delta),
 //        dQ^T += K^T dS^T   (K^T from the transposing LDS load).
 #include "kernel_common.hpp"
 
 namespace tree_attn {
-
-// 4-byte-per-lane copy global -> LDS: lane l writes (lds_base + 4 l).
-__device__ inline void dma4(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 4, 0, 0);
-}
 
 // ---------------------------------------------------------------------------
 // 1. row statistics
@@ -70,33 +65,48 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
 // ---------------------------------------------------------------------------
 // 2. dK / dV, key-major
 //
-// The workgroup makes two passes over its query range: the first
-// accumulates dV^T += dO^T P, the second dK^T += Q^T dS.  Recomputing S in
-// the second pass costs 8 of every 40 MFMA steps, but only one fp32
-// accumulator block is live at a time, which keeps two wavefronts per SIMD
-// resident (one fused pass needs ~290 registers and runs one wave per SIMD).
+// One 512-thread workgroup per compute unit owns 64 keys of one key/value
+// head and walks the query range that sees them (all G query heads), 64
+// queries per step, reading the range once.  Its eight wavefronts split by
+// role, one of each role per SIMD; within a role, wave bits (kb, qh) pick 32
+// keys x 32 queries:
+//   * waves 0-3 (dV): S = Q K^T, P = exp2(S c - lse2) rounded to the input
+//     type, dV^T += dO^T P, and P is left in LDS;
+//   * waves 4-7 (dK), one step behind: dP = dO V^T, dS = P (dP - delta)
+//     with the P of the matching dV wave, dK^T += Q^T dS.
+// So S is formed once per step and each SIMD issues the minimum 32 matrix
+// products per step.  Q / dO tiles and their lse2 / delta go through a ring
+// of kRing LDS buffers, copied kRing - 2 steps ahead of the dV waves (the
+// dK waves hold one more); every wave issues the same number of copies per
+// step, so the wait for a step's tiles is a fixed count.  One barrier per
+// step orders copies, P hand-off and buffer reuse.
+
+template <typename T>
+struct DkdvRing {
+  static constexpr int value = sizeof(T) == 2 ? 4 : 3;  // fits P and the ring in LDS
+};
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void tree_attn_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   using quad = typename M::quad;
-  constexpr int BM = 64;  // queries per step
+  constexpr int kRing = DkdvRing<T>::value;
+  constexpr int kAhead = kRing - 2;               // steps copied ahead
+  constexpr int BM = 64;                          // queries per step
   constexpr int E = 16 / int(sizeof(T));
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int TILE = BM * kRowBytes / int(sizeof(T));
+  constexpr int TILE = BM * kRowBytes;            // bytes of one 64-row tile
+  constexpr int BUF = 2 * TILE + 2 * BM * 4;      // Q, dO, lse2, delta
+  constexpr int kCopies = 5;                      // copies per wave per step
+  constexpr int PBLK = 2 * 64;                    // P fragments per wave block
   static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
-  static_assert(DB * 16 * 64 * 4 <= TILE * int(sizeof(T)), "one wave's partial fits a tile");
+  static_assert(4 * DB * 16 * 64 * 4 <= kRing * BUF, "the partials fit the ring");
 
-  __shared__ __attribute__((aligned(16))) T sQ0[TILE];
-  __shared__ __attribute__((aligned(16))) T sO0[TILE];
-  __shared__ __attribute__((aligned(16))) T sQ1[TILE];
-  __shared__ __attribute__((aligned(16))) T sO1[TILE];
-  __shared__ __attribute__((aligned(16))) float sL0[BM];
-  __shared__ __attribute__((aligned(16))) float sD0[BM];
-  __shared__ __attribute__((aligned(16))) float sL1[BM];
-  __shared__ __attribute__((aligned(16))) float sD1[BM];
+  __shared__ __attribute__((aligned(16))) char ring[kRing * BUF];
+  __shared__ __attribute__((aligned(16))) frag pshare[2][4 * PBLK];
+  __shared__ __attribute__((aligned(16))) float junk[64];
 
   int tile_rank, g;
   decode_item(blockIdx.x, a.Hkv, tile_rank, g);
@@ -104,7 +114,9 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
-  const int kb = wave & 1, qh = wave >> 1;
+  const bool dk_role = __builtin_amdgcn_readfirstlane(int(wave >= 4)) != 0;
+  const int wblk = wave & 3;
+  const int kb = wave & 1, qh = (wave >> 1) & 1;
   const int kl = kb * 32 + col;
   const bool key_valid = kl < tile.nk;
   const int ktok = tile.k0 + min(kl, tile.nk - 1);
@@ -114,35 +126,50 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dkdv_kernel(BwdArgs a) {
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ dout = static_cast<const T*>(a.dout);
   const float* lse2 = a.delta + (size_t)a.Hq * a.T;
-  const size_t kv_off = ((size_t)ktok * a.Hkv + g) * D + half * 8;
 
-  frag kf[KS];
+  // the dV waves keep K, the dK waves V (both as B fragments)
+  frag kv[KS];
+  {
+    const T* src = static_cast<const T*>(dk_role ? a.v : a.k) + ((size_t)ktok * a.Hkv + g) * D + half * 8;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kf[ks] = load_frag<T>(static_cast<const T*>(a.k) + kv_off + ks * 16);
+    for (int ks = 0; ks < KS; ++ks) kv[ks] = load_frag<T>(src + ks * 16);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) settle(kv[ks]);
 
   const int nblk = (tile.qend - tile.k0 + BM - 1) / BM;
   const int n_steps = a.G * nblk;
-  int lrow[4], lchunk[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    lrow[r] = (4 * wave + r) * 4 + (lane >> 4);
-    lchunk[r] = (lane & 15) ^ swz(lrow[r]);
-  }
-  // rows past the query range read a valid row and are masked to P = 0
-  // element offsets fit in 32 bits (tensors are limited to 2^31 elements)
-  auto issue = [&](int step, T* sQ, T* sO, float* sL, float* sD) {
+
+  // copy plan: waves 0-3 copy Q rows, waves 4-7 dO rows, 16 rows per wave
+  // (4 instructions of 4 rows); every wave copies one 64-float stat vector
+  // (waves 0 and 1 the real lse2 / delta, the rest a discarded duplicate)
+  const int crow0 = wblk * 16;
+  const T* csrc = dk_role ? dout : q;
+  const int coff = dk_role ? TILE : 0;
+  // Step `step` goes to buffer step % kRing.  Steps past the end copy the
+  // last step's rows into their (idle) buffer, so every wave always issues
+  // kCopies copies.  Rows past the range read a valid row and are masked to
+  // P = 0; element offsets fit in 32 bits (tensors are limited to 2^31
+  // elements).
+  auto issue = [&](int step) {
+    char* buf = ring + (step % kRing) * BUF;
+    step = min(step, n_steps - 1);
     const int h = g * a.G + step / nblk;
     const int i0 = tile.k0 + (step % nblk) * BM;
     const int last = tile.qend - 1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int off = (min(i0 + lrow[r], last) * a.Hq + h) * D + lchunk[r] * E;
-      dma16(q + off, sQ + (4 * wave + r) * 64 * E);
-      dma16(dout + off, sO + (4 * wave + r) * 64 * E);
+      const int row = crow0 + r * 4 + (lane >> 4);
+      const int off = (min(i0 + row, last) * a.Hq + h) * D + ((lane & 15) ^ swz(row)) * E;
+      copy16_async(csrc + off, buf + coff + (crow0 + 4 * r) * kRowBytes);
     }
-    if (wave < 2) {
-      const int at = h * a.T + min(i0 + lane, last);
-      dma4(wave == 0 ? lse2 + at : a.delta + at, wave == 0 ? sL : sD);
+    const int at = h * a.T + min(i0 + lane, last);
+    if (wave == 0) {
+      copy4_async(lse2 + at, buf + 2 * TILE);
+    } else if (wave == 1) {
+      copy4_async(a.delta + at, buf + 2 * TILE + BM * 4);
+    } else {
+      copy4_async(lse2 + at, junk);
     }
   };
 
@@ -156,19 +183,26 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  // P for this wave's 32 queries x 32 keys, rounded to the input type
-  auto probs = [&](int step, const T* sQ, const float* sL, frag (&pf)[2]) {
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  // dV role at `step`: S, P (rows before the key or past the range get
+  // P = 0), P to LDS, dV^T += dO^T P
+  auto step_v = [&](int step, const char* buf, frag* pout) {
+    const T* sQ = reinterpret_cast<const T*>(buf);
+    const T* sO = reinterpret_cast<const T*>(buf + TILE);
+    const float* sL = reinterpret_cast<const float*>(buf + 2 * TILE);
     const int i0 = tile.k0 + (step % nblk) * BM;
     f32x16 s = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) M::mma(s, tile_row_frag<T>(sQ, qh * 32 + col, ks * 16 + half * 8), kf[ks]);
+    for (int ks = 0; ks < KS; ++ks) M::mma(s, tile_row_frag<T>(sQ, qh * 32 + col, ks * 16 + half * 8), kv[ks]);
     sched_pipeline<kLdsAhead, KS, frag_reads<T>(false)>();
     float lq[16];
     row_stats(sL, lq);
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lq[i]));
-    // diagonal block (queries before the key) or rows past the range: wave-uniform
     if (__builtin_amdgcn_readfirstlane(int(i0 + qh * 32 < tile.k0 + kb * 32 + 31 ||
                                            i0 + qh * 32 + 31 >= tile.qend))) {
 #pragma unroll
@@ -177,17 +211,11 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dkdv_kernel(BwdArgs a) {
         if (qi < jkey || qi >= tile.qend) p[i] = 0.f;
       }
     }
+    frag pf[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = to_elem<T>(p[i]);
-  };
-
-  f32x16 acc[DB];
-  frag vf[KS];
-
-  // dV pass: dV^T += dO^T P
-  auto step_v = [&](int step, const T* sQ, const T* sO, const float* sL, const float*) {
-    frag pf[2];
-    probs(step, sQ, sL, pf);
+    pout[lane] = pf[0];
+    pout[64 + lane] = pf[1];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -195,17 +223,19 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dkdv_kernel(BwdArgs a) {
         M::mma(acc[db], tile_tr_frag<T>(sO, qh * 32 + 16 * hh, db * 32, lane), pf[hh]);
     sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
   };
-  // dK pass: dP = dO V^T, dS = P (dP - delta), dK^T += Q^T dS; dS uses the
-  // same rounded P as the dV pass
-  auto step_k = [&](int step, const T* sQ, const T* sO, const float* sL, const float* sD) {
-    frag pf[2];
-    probs(step, sQ, sL, pf);
+  // dK role at `step` (one behind the dV role): dP, dS with the dV wave's
+  // P, dK^T += Q^T dS
+  auto step_k = [&](const char* buf, const frag* pin) {
+    const T* sQ = reinterpret_cast<const T*>(buf);
+    const T* sO = reinterpret_cast<const T*>(buf + TILE);
+    const float* sD = reinterpret_cast<const float*>(buf + 2 * TILE + BM * 4);
     f32x16 dp = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) M::mma(dp, tile_row_frag<T>(sO, qh * 32 + col, ks * 16 + half * 8), vf[ks]);
+    for (int ks = 0; ks < KS; ++ks) M::mma(dp, tile_row_frag<T>(sO, qh * 32 + col, ks * 16 + half * 8), kv[ks]);
     sched_pipeline<kLdsAhead, KS, frag_reads<T>(false)>();
     float dl[16];
     row_stats(sD, dl);
+    const frag pf[2] = {pin[lane], pin[64 + lane]};
     frag dsf[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) dsf[i >> 3][i & 7] = to_elem<T>(float(pf[i >> 3][i & 7]) * (dp[i] - dl[i]));
@@ -217,67 +247,49 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dkdv_kernel(BwdArgs a) {
     sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
   };
 
-  // one pass over all steps: two statically named buffers, one barrier per step
-  auto run = [&](auto&& step_fn) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-    issue(0, sQ0, sO0, sL0, sD0);
-    wait_dma();
-    __syncthreads();
-    for (int step = 0;;) {
-      const bool more1 = step + 1 < n_steps;
-      if (more1) issue(step + 1, sQ1, sO1, sL1, sD1);
-      step_fn(step, sQ0, sO0, sL0, sD0);
-      if (!more1) break;
-      wait_dma();
-      __syncthreads();
-      ++step;
-      const bool more0 = step + 1 < n_steps;
-      if (more0) issue(step + 1, sQ0, sO0, sL0, sD0);
-      step_fn(step, sQ1, sO1, sL1, sD1);
-      if (!more0) break;
-      wait_dma();
-      __syncthreads();
-      ++step;
+  for (int s = 0; s < kAhead; ++s) issue(s);
+  for (int step = 0; step <= n_steps; ++step) {
+    // this wave's copies of `step` are done once only the kAhead - 1 newer
+    // steps' copies may be in flight; after the barrier every wave's are,
+    // the P of step - 1 is in LDS, and nobody reads the buffer refilled next
+    // (last read by the dK waves at step - 2)
+    wait_copies_barrier<(kAhead - 1) * kCopies>();
+    issue(step + kAhead);
+    if (dk_role) {
+      if (step > 0) step_k(ring + ((step - 1) % kRing) * BUF, &pshare[(step - 1) & 1][wblk * PBLK]);
+    } else if (step < n_steps) {
+      step_v(step, ring + (step % kRing) * BUF, &pshare[step & 1][wblk * PBLK]);
     }
-    __syncthreads();  // every wave is done with the tiles
-  };
+  }
+  wait_copies_barrier<0>();  // no copy in flight; the ring is free
 
   // fixed-order reduction of the two query halves, then one store per key:
-  // the qh = 1 waves park their partial in sQ0 (kb = 0) / sO0 (kb = 1)
-  auto reduce_store = [&](T* out, float mul) {
-    float* r = reinterpret_cast<float*>(kb == 0 ? sQ0 : sO0);
-    if (qh == 1) {
+  // the qh = 1 wave of each (role, kb) parks its partial in the ring
+  float* park = reinterpret_cast<float*>(ring) + ((dk_role ? 2 : 0) + kb) * (DB * 16 * 64);
+  if (qh == 1) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) r[(db * 16 + i) * 64 + lane] = acc[db][i];
-    }
-    __syncthreads();
-    if (qh == 0 && key_valid) {
-      T* op = out + ((size_t)jkey * a.Hkv + g) * D;
+      for (int i = 0; i < 16; ++i) park[(db * 16 + i) * 64 + lane] = acc[db][i];
+  }
+  __syncthreads();
+  if (qh == 0 && key_valid) {
+    T* op = static_cast<T*>(dk_role ? a.dk : a.dv) + ((size_t)jkey * a.Hkv + g) * D;
+    const float mul = dk_role ? a.scale : 1.f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          quad t4;
+      for (int grp = 0; grp < 4; ++grp) {
+        quad t4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = grp * 4 + e;
-            t4[e] = to_elem<T>((acc[db][i] + r[(db * 16 + i) * 64 + lane]) * mul);
-          }
-          *reinterpret_cast<quad*>(op + db * 32 + grp * 8 + half * 4) = t4;
+        for (int e = 0; e < 4; ++e) {
+          const int i = grp * 4 + e;
+          t4[e] = to_elem<T>((acc[db][i] + park[(db * 16 + i) * 64 + lane]) * mul);
         }
-    }
-    __syncthreads();  // the parking buffer is reused by the next pass
-  };
-
-  run(step_v);
-  reduce_store(static_cast<T*>(a.dv), 1.f);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) vf[ks] = load_frag<T>(static_cast<const T*>(a.v) + kv_off + ks * 16);
-  run(step_k);
-  reduce_store(static_cast<T*>(a.dk), a.scale);
+        *reinterpret_cast<quad*>(op + db * 32 + grp * 8 + half * 4) = t4;
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -370,34 +382,33 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
     }
   };
 
+  // the two 32-key halves one after the other: only one half's S and dP
+  // are live at a time
   auto compute = [&](int v0, const T* sK, const T* sV) {
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    const bool need_mask = v0 + BN - 1 > wave_pos0;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        M::mma(s[kb], tile_row_frag<T>(sK, kb * 32 + col, ks * 16 + half * 8), qf[ks]);
-        M::mma(dp[kb], tile_row_frag<T>(sV, kb * 32 + col, ks * 16 + half * 8), of[ks]);
+        M::mma(s, tile_row_frag<T>(sK, kb * 32 + col, ks * 16 + half * 8), qf[ks]);
+        M::mma(dp, tile_row_frag<T>(sV, kb * 32 + col, ks * 16 + half * 8), of[ks]);
       }
-    sched_pipeline<kLdsAhead, 4 * KS, frag_reads<T>(false)>();
-    const bool need_mask = v0 + BN - 1 > wave_pos0;
-    frag dsf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
+      frag dsf[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -lse2));
+        float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
         if (need_mask && v0 + kb * 32 + c_row(i, half) > qpos) p = 0.f;
-        dsf[kb][i >> 3][i & 7] = to_elem<T>(p * (dp[kb][i] - dlt));
+        dsf[i >> 3][i & 7] = to_elem<T>(p * (dp[i] - dlt));
       }
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-          M::mma(dq[db], tile_tr_frag<T>(sK, kb * 32 + 16 * hh, db * 32, lane), dsf[kb][hh]);
-    sched_pipeline<kLdsAhead, 4 * DB, frag_reads<T>(true)>();
+          M::mma(dq[db], tile_tr_frag<T>(sK, kb * 32 + 16 * hh, db * 32, lane), dsf[hh]);
+      sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
+    }
   };
 
   issue(0, sK0, sV0);
@@ -450,7 +461,7 @@ hipError_t launch_bwd_rowstat(const BwdArgs& a, hipStream_t stream) {
 
 template <typename T, int D>
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((tree_attn_dkdv_kernel<T, D>), dim3((unsigned)a.n_ktiles * (unsigned)a.Hkv), dim3(256), 0,
+  hipLaunchKernelGGL((tree_attn_dkdv_kernel<T, D>), dim3((unsigned)a.n_ktiles * (unsigned)a.Hkv), dim3(512), 0,
                      stream, a);
   return hipGetLastError();
 }

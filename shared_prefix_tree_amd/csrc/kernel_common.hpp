@@ -144,6 +144,43 @@ __device__ inline void dma16(const void* src, void* lds_base) {
 
 __device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Copies global -> LDS written as inline assembly, for kernels that keep
+// several copies in flight and count them themselves.  The compiler does not
+// see these as LDS writes, so it adds no wait of its own before LDS reads
+// (with the builtin it sometimes waits for every copy in flight); the caller
+// orders them with wait_copies_barrier<N>().  Nothing else in such a kernel
+// may rely on M0 (no dynamic register indexing, no builtin LDS copies).
+__device__ inline void copy16_async(const void* src, void* lds_base) {
+  const unsigned m = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m) : "memory");
+}
+__device__ inline void copy4_async(const void* src, void* lds_base) {
+  const unsigned m = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m) : "memory");
+}
+
+// An empty asm use of `f`: the compiler completes the loads that produce it
+// here, not at its first real use (inside a loop, that wait would also
+// drain the copies in flight).  Wider than 16 bytes it goes element-wise.
+template <typename F>
+__device__ inline void settle(const F& f) {
+  if constexpr (sizeof(F) == 16) {
+    asm volatile("" ::"v"(f));
+  } else {
+#pragma unroll
+    for (int j = 0; j < int(sizeof(F) / 4); ++j) asm volatile("" ::"v"(f[j]));
+  }
+}
+
+// Waits until at most N of this wave's vector-memory operations are in
+// flight and its LDS operations are done, then joins the workgroup barrier.
+// Loads complete in issue order, so with N = the copies issued after a given
+// step's, that step's copies (from every wave) are in LDS after the barrier.
+template <int N>
+__device__ inline void wait_copies_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Fragment of 8 consecutive elements [e0, e0+8) of a tile row (e0 % 8 == 0).
 template <typename T>
 __device__ inline typename Mfma<T>::frag tile_row_frag(const T* tile, int row, int e0) {
