@@ -112,9 +112,10 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   decode_item(blockIdx.x, a.Hkv, tile_rank, g);
   const KTile tile = a.ktiles[tile_rank];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 31, half = lane >> 5;
-  const bool dk_role = __builtin_amdgcn_readfirstlane(int(wave >= 4)) != 0;
+  const bool dk_role = wave >= 4;
   const int wblk = wave & 3;
   const int kb = wave & 1, qh = (wave >> 1) & 1;
   const int kl = kb * 32 + col;
@@ -123,8 +124,6 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   const int jkey = tile.k0 + kl;
   const float c = a.scale * kLog2e;
 
-  const T* __restrict__ q = static_cast<const T*>(a.q);
-  const T* __restrict__ dout = static_cast<const T*>(a.dout);
   const float* lse2 = a.delta + (size_t)a.Hq * a.T;
 
   // the dV waves keep K, the dK waves V (both as B fragments)
@@ -139,38 +138,40 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 
   const int nblk = (tile.qend - tile.k0 + BM - 1) / BM;
   const int n_steps = a.G * nblk;
+  const int last = tile.qend - 1;
 
   // copy plan: waves 0-3 copy Q rows, waves 4-7 dO rows, 16 rows per wave
   // (4 instructions of 4 rows); every wave copies one 64-float stat vector
-  // (waves 0 and 1 the real lse2 / delta, the rest a discarded duplicate)
+  // (waves 0 and 1 the real lse2 / delta, the rest a discarded duplicate).
+  // Per lane: row crow0 + 4 r + lane / 16 and its swizzled 16-byte chunk.
   const int crow0 = wblk * 16;
-  const T* csrc = dk_role ? dout : q;
-  const int coff = dk_role ? TILE : 0;
+  const T* csrc = static_cast<const T*>(dk_role ? a.dout : a.q);
+  const float* ssrc = wave == 1 ? a.delta : lse2;
+  const unsigned ring_lds = lds_addr(ring);
+  const unsigned c_lds = ring_lds + (dk_role ? TILE : 0) + crow0 * kRowBytes;
+  const unsigned s_lds = wave < 2 ? ring_lds + 2 * TILE + wave * BM * 4 : lds_addr(junk);
+  const unsigned s_step = wave < 2 ? BUF : 0;
+  const int crow = crow0 + (lane >> 4);
+  unsigned cchunk[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) cchunk[r] = (((lane & 15) ^ swz(crow + 4 * r)) * 16);
+  const unsigned row_bytes = (unsigned)a.Hq * D * sizeof(T);
   // Step `step` goes to buffer step % kRing.  Steps past the end copy the
   // last step's rows into their (idle) buffer, so every wave always issues
-  // kCopies copies.  Rows past the range read a valid row and are masked to
-  // P = 0; element offsets fit in 32 bits (tensors are limited to 2^31
-  // elements).
+  // kCopies copies.  Rows past the range read the last row (masked to
+  // P = 0).  Each copy reads from a wave-uniform row base plus a small
+  // per-lane offset.
   auto issue = [&](int step) {
-    char* buf = ring + (step % kRing) * BUF;
+    const unsigned bofs = (unsigned)(step % kRing) * BUF;
     step = min(step, n_steps - 1);
     const int h = g * a.G + step / nblk;
     const int i0 = tile.k0 + (step % nblk) * BM;
-    const int last = tile.qend - 1;
+    const T* base = csrc + ((size_t)i0 * a.Hq + h) * D;
+    const int lim = last - i0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = crow0 + r * 4 + (lane >> 4);
-      const int off = (min(i0 + row, last) * a.Hq + h) * D + ((lane & 15) ^ swz(row)) * E;
-      copy16_async(csrc + off, buf + coff + (crow0 + 4 * r) * kRowBytes);
-    }
-    const int at = h * a.T + min(i0 + lane, last);
-    if (wave == 0) {
-      copy4_async(lse2 + at, buf + 2 * TILE);
-    } else if (wave == 1) {
-      copy4_async(a.delta + at, buf + 2 * TILE + BM * 4);
-    } else {
-      copy4_async(lse2 + at, junk);
-    }
+    for (int r = 0; r < 4; ++r)
+      copy16_async(base, (unsigned)min(crow + 4 * r, lim) * row_bytes + cchunk[r], c_lds + bofs + 4 * r * kRowBytes);
+    copy4_async(ssrc + (size_t)h * a.T + i0, (unsigned)min(lane, lim) * 4u, s_lds + (bofs / BUF) * s_step);
   };
 
   // lse2 / delta of this lane's 16 C-layout query rows: 4 runs of 4
@@ -187,63 +188,51 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  // dV role at `step`: S, P (rows before the key or past the range get
-  // P = 0), P to LDS, dV^T += dO^T P
-  auto step_v = [&](int step, const char* buf, frag* pout) {
-    const T* sQ = reinterpret_cast<const T*>(buf);
-    const T* sO = reinterpret_cast<const T*>(buf + TILE);
-    const float* sL = reinterpret_cast<const float*>(buf + 2 * TILE);
-    const int i0 = tile.k0 + (step % nblk) * BM;
-    f32x16 s = f32x16{};
+  // One step of either role, as one instruction stream over role-selected
+  // tiles (so the accumulators never move between registers):
+  //   t   = A B^T   with A = Q (dV role) or dO (dK role), B = K or V;
+  //   x   = P        dV role: exp2(t c - lse2), zero before the key or past
+  //                  the range, rounded to the input type, also left in LDS
+  //       = dS       dK role: P (t - delta) with the dV wave's P;
+  //   acc += C^T x   with C = dO (dV role) or Q (dK role).
+  auto step_fn = [&](int step, const char* buf, frag* pshr) {
+    const T* sA = reinterpret_cast<const T*>(buf + (dk_role ? TILE : 0));
+    const T* sC = reinterpret_cast<const T*>(buf + (dk_role ? 0 : TILE));
+    const float* sX = reinterpret_cast<const float*>(buf + 2 * TILE + (dk_role ? BM * 4 : 0));
+    f32x16 t = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) M::mma(s, tile_row_frag<T>(sQ, qh * 32 + col, ks * 16 + half * 8), kv[ks]);
+    for (int ks = 0; ks < KS; ++ks) M::mma(t, tile_row_frag<T>(sA, qh * 32 + col, ks * 16 + half * 8), kv[ks]);
     sched_pipeline<kLdsAhead, KS, frag_reads<T>(false)>();
-    float lq[16];
-    row_stats(sL, lq);
-    float p[16];
+    float x[16];
+    row_stats(sX, x);
+    frag xf[2];
+    if (!dk_role) {
+      const int i0 = tile.k0 + (step % nblk) * BM;
+      float p[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lq[i]));
-    if (__builtin_amdgcn_readfirstlane(int(i0 + qh * 32 < tile.k0 + kb * 32 + 31 ||
-                                           i0 + qh * 32 + 31 >= tile.qend))) {
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(t[i], c, -x[i]));
+      if (__builtin_amdgcn_readfirstlane(int(i0 + qh * 32 < tile.k0 + kb * 32 + 31 ||
+                                             i0 + qh * 32 + 31 >= tile.qend))) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qi = i0 + qh * 32 + c_row(i, half);
-        if (qi < jkey || qi >= tile.qend) p[i] = 0.f;
+        for (int i = 0; i < 16; ++i) {
+          const int qi = i0 + qh * 32 + c_row(i, half);
+          if (qi < jkey || qi >= tile.qend) p[i] = 0.f;
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xf[i >> 3][i & 7] = to_elem<T>(p[i]);
+      pshr[lane] = xf[0];
+      pshr[64 + lane] = xf[1];
+    } else {
+      const frag pf[2] = {pshr[lane], pshr[64 + lane]};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xf[i >> 3][i & 7] = to_elem<T>(float(pf[i >> 3][i & 7]) * (t[i] - x[i]));
     }
-    frag pf[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = to_elem<T>(p[i]);
-    pout[lane] = pf[0];
-    pout[64 + lane] = pf[1];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        M::mma(acc[db], tile_tr_frag<T>(sO, qh * 32 + 16 * hh, db * 32, lane), pf[hh]);
-    sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
-  };
-  // dK role at `step` (one behind the dV role): dP, dS with the dV wave's
-  // P, dK^T += Q^T dS
-  auto step_k = [&](const char* buf, const frag* pin) {
-    const T* sQ = reinterpret_cast<const T*>(buf);
-    const T* sO = reinterpret_cast<const T*>(buf + TILE);
-    const float* sD = reinterpret_cast<const float*>(buf + 2 * TILE + BM * 4);
-    f32x16 dp = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) M::mma(dp, tile_row_frag<T>(sO, qh * 32 + col, ks * 16 + half * 8), kv[ks]);
-    sched_pipeline<kLdsAhead, KS, frag_reads<T>(false)>();
-    float dl[16];
-    row_stats(sD, dl);
-    const frag pf[2] = {pin[lane], pin[64 + lane]};
-    frag dsf[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dsf[i >> 3][i & 7] = to_elem<T>(float(pf[i >> 3][i & 7]) * (dp[i] - dl[i]));
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        M::mma(acc[db], tile_tr_frag<T>(sQ, qh * 32 + 16 * hh, db * 32, lane), dsf[hh]);
+        M::mma(acc[db], tile_tr_frag<T>(sC, qh * 32 + 16 * hh, db * 32, lane), xf[hh]);
     sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
   };
 
@@ -256,11 +245,8 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     // (last read by the dK waves at step - 2)
     wait_copies_barrier<(kAhead - 1) * kCopies>();
     issue(step + kAhead);
-    if (dk_role) {
-      if (step > 0) step_k(ring + ((step - 1) % kRing) * BUF, &pshare[(step - 1) & 1][wblk * PBLK]);
-    } else if (step < n_steps) {
-      step_v(step, ring + (step % kRing) * BUF, &pshare[step & 1][wblk * PBLK]);
-    }
+    const int my = dk_role ? step - 1 : step;  // the dK waves run one behind
+    if (my >= 0 && my < n_steps) step_fn(my, ring + (my % kRing) * BUF, &pshare[my & 1][wblk * PBLK]);
   }
   wait_copies_barrier<0>();  // no copy in flight; the ring is free
 

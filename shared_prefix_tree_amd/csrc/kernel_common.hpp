@@ -148,16 +148,21 @@ __device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memor
 // several copies in flight and count them themselves.  The compiler does not
 // see these as LDS writes, so it adds no wait of its own before LDS reads
 // (with the builtin it sometimes waits for every copy in flight); the caller
-// orders them with wait_copies_barrier<N>().  Nothing else in such a kernel
-// may rely on M0 (no dynamic register indexing, no builtin LDS copies).
-__device__ inline void copy16_async(const void* src, void* lds_base) {
-  const unsigned m = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void*)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m) : "memory");
+// orders them with wait_copies_barrier<N>().  Lane l reads
+// sbase + voff(l) (sbase wave-uniform) and writes LDS byte address
+// lds + size * l (lds wave-uniform).  Nothing else in such a kernel may
+// rely on M0 (no dynamic register indexing, no builtin LDS copies).
+__device__ inline void copy16_async(const void* sbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory");
 }
-__device__ inline void copy4_async(const void* src, void* lds_base) {
-  const unsigned m = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void*)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m) : "memory");
+__device__ inline void copy4_async(const void* sbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory");
 }
+
+// LDS byte address of a __shared__ object.
+__device__ inline unsigned lds_addr(const void* p) { return (unsigned)(size_t)(const lds_void*)p; }
 
 // An empty asm use of `f`: the compiler completes the loads that produce it
 // here, not at its first real use (inside a loop, that wait would also
