@@ -45,7 +45,7 @@ struct DevicePlan {
   void* block = nullptr;  // one allocation holding every table below
   int32_t* span_ptr = nullptr;
   Span* spans = nullptr;
-  QTile* qtiles[kNumQTileSizes] = {nullptr, nullptr, nullptr};
+  QTile* qtiles[kNumQTileSizes] = {};
   KTile* ktiles = nullptr;
 };
 
@@ -140,6 +140,11 @@ int gcd(int a, int b) {
   return a;
 }
 
+// Query tile of the forward and dQ kernels: 32 query rows per wavefront,
+// HG heads of a key/value group side by side.
+int fwd_query_tile(int hg) { return 32 * (8 / hg); }
+int dq_query_tile(int hg) { return 32 * (4 / hg); }
+
 // Shared argument checks of fwd/bwd.  Returns 0 or an error code.
 int check_call(const char* fn, tree_attn_plan_t plan, const tree_attn_shape* shape, float* scale_out) {
   const std::string f(fn);
@@ -170,8 +175,14 @@ int check_call(const char* fn, tree_attn_plan_t plan, const tree_attn_shape* sha
     return fail(TREE_ATTN_UNSUPPORTED, f + ": a segment's ancestor path has " +
                                            std::to_string(plan->host.max_spans) + " separate spans (limit " +
                                            std::to_string(kMaxSpans) + ")");
+  // the query-major kernels gather K/V rows with 32-bit byte offsets
+  const int64_t elem = shape->dtype == TREE_ATTN_BF16 ? 2 : 4;
+  if (int64_t(shape->total_tokens) * shape->num_kv_heads * shape->head_dim * elem >= (int64_t(1) << 32))
+    return fail(TREE_ATTN_UNSUPPORTED, f + ": k and v are limited to 2^32 bytes");
   const int hg = gcd(shape->num_q_heads / shape->num_kv_heads, 4);
-  const int64_t grid_q = int64_t(plan->host.qtiles[qtile_index(32 * (4 / hg))].size()) * (shape->num_q_heads / hg);
+  int64_t grid_q = 0;
+  for (int tq : {fwd_query_tile(hg), dq_query_tile(hg)})
+    grid_q = std::max(grid_q, int64_t(plan->host.qtiles[qtile_index(tq)].size()) * (shape->num_q_heads / hg));
   const int64_t grid_k = int64_t(plan->host.ktiles.size()) * shape->num_kv_heads;
   if (grid_q >= (int64_t(1) << 31) || grid_k >= (int64_t(1) << 31))
     return fail(TREE_ATTN_UNSUPPORTED, f + ": launch grid too large");
@@ -275,8 +286,7 @@ int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t 
   if (int rc = check_call("tree_attn_fwd", plan, shape, &scale)) return rc;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   const int hg = gcd(G, 4);
-  const int tq = 32 * (4 / hg);
-  const int ti = qtile_index(tq);
+  const int ti = qtile_index(fwd_query_tile(hg));
   FwdArgs a;
   a.q = q;
   a.k = k;
@@ -338,7 +348,7 @@ int prep_bwd(const char* fn, const void* q, const void* k, const void* v, const 
                                                 " bytes < required " + std::to_string(ws));
   const int G = shape->num_q_heads / shape->num_kv_heads;
   hg = gcd(G, 4);
-  const int ti = qtile_index(32 * (4 / hg));
+  const int ti = qtile_index(dq_query_tile(hg));
   a.q = q;
   a.k = k;
   a.v = v;

@@ -9,16 +9,16 @@
 // trajectories", section "Describe the solution you'd like": attention for
 // each query run against only its ancestor path).
 //
-// Work decomposition (one workgroup = 4 wavefronts):
+// Work decomposition (one workgroup = 8 wavefronts, one per compute unit):
 //   * a workgroup owns a query tile of 32*NT tokens (inside one segment) and
-//     HG query heads of one key/value head (NT*HG = 4);
+//     HG query heads of one key/value head (NT*HG = 8);
 //   * wave w holds 32 query rows (token sub-tile w / HG, head w % HG) with Q
 //     in registers;
 //   * the workgroup walks the segment's ancestor path as one virtual key
 //     sequence (the merged spans of the plan), 64 keys per step.  K and V
-//     rows are gathered span by span straight into LDS (global_load_lds,
-//     16 B per lane, row-major, swizzled) into one of two buffers while the
-//     other buffer is being used, so a step costs one barrier;
+//     rows are gathered span by span straight into a ring of four LDS
+//     buffers (global_load_lds, 16 B per lane, row-major, swizzled), three
+//     steps ahead of the compute, with one barrier per step;
 //   * every wave computes S^T = K Q^T (K rows read as A fragments), the
 //     online softmax per query column, and O^T += V^T P^T (V read with the
 //     transposing LDS load).  A lane owns one query column, so the row max
@@ -35,30 +35,31 @@ namespace tree_attn {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P values stay <= 256
 
+constexpr int kFwdRing = 4;
+
 template <typename T, int D, int HG>
-__global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   using quad = typename M::quad;
   constexpr int BN = 64;  // keys per step
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int E = 16 / int(sizeof(T));
-  constexpr int TILE = BN * kRowBytes / int(sizeof(T));
+  constexpr int TILE = BN * kRowBytes;  // bytes of one 64-row tile
+  constexpr int BUF = 2 * TILE;         // K, V
+  constexpr int kAhead = kFwdRing - 1;
   static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
-  static_assert(4 % HG == 0, "four wavefronts per workgroup");
+  static_assert(8 % HG == 0, "eight wavefronts per workgroup");
 
-  __shared__ __attribute__((aligned(16))) T sK0[TILE];
-  __shared__ __attribute__((aligned(16))) T sV0[TILE];
-  __shared__ __attribute__((aligned(16))) T sK1[TILE];
-  __shared__ __attribute__((aligned(16))) T sV1[TILE];
+  __shared__ __attribute__((aligned(16))) char ring[kFwdRing * BUF];
   __shared__ Span sSpans[kMaxSpans];
 
   int tile_rank, group;
   decode_item(blockIdx.x, a.Hq / HG, tile_rank, group);
   const QTile tile = a.tiles[tile_rank];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 31, half = lane >> 5;
   const int ts = wave / HG;
   const int h = group * HG + wave % HG;
@@ -68,58 +69,32 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   const int qpos = tile.pos0 + qrow;
   const int wave_pos0 = tile.pos0 + ts * 32;
   const int kv_len = tile.pos0 + tile.nq;
+  const int n_steps = (kv_len + BN - 1) / BN;
   const float c = a.scale * kLog2e;
-
-  const T* __restrict__ q = static_cast<const T*>(a.q);
-  const T* kg = static_cast<const T*>(a.k) + (size_t)g * D;
-  const T* vg = static_cast<const T*>(a.v) + (size_t)g * D;
-  const int row_stride = a.Hkv * D;
 
   frag qf[KS];
   {
-    const T* p = q + ((size_t)qtok * a.Hq + h) * D + half * 8;
+    const T* p = static_cast<const T*>(a.q) + ((size_t)qtok * a.Hq + h) * D + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = load_frag<T>(p + ks * 16);
   }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
 
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  // DMA: wave w, instruction r fills tile chunks [(4w+r)*64, +64): lane l
-  // writes row (4w+r)*4 + l/16, physical chunk l%16 (logical chunk l%16 ^ f(row)).
   stage_spans(sSpans, a.span_ptr, a.spans, tile.seg);
   __syncthreads();
-  SpanCursor cur{sSpans, 0};
-  int lrow[4], lchunk[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    lrow[r] = (4 * wave + r) * 4 + (lane >> 4);
-    lchunk[r] = (lane & 15) ^ swz(lrow[r]);
-  }
-  // Row addresses of the 64 keys [v0, v0 + 64).  Spans are usually much
-  // longer than a step, so when the whole step lies in one span (checked
-  // with a workgroup-uniform cursor) the rows are contiguous from one base;
-  // otherwise every lane looks up its own rows.  Rows past the path read
-  // any valid row and are masked.  Offsets fit in 32 bits.
-  int ucur = 0;
-  auto issue = [&](int v0, T* sK, T* sV) {
-    while (v0 >= sSpans[ucur].virt + sSpans[ucur].len) ++ucur;
-    const int sv = sSpans[ucur].virt, sl = sSpans[ucur].len, spp = sSpans[ucur].phys;
-    int off[4];
-    if (__builtin_amdgcn_readfirstlane(int(v0 + BN <= sv + sl && v0 + BN <= kv_len))) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) off[r] = (spp + (v0 - sv) + lrow[r]) * row_stride + lchunk[r] * E;
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) off[r] = cur.phys(min(v0 + lrow[r], kv_len - 1)) * row_stride + lchunk[r] * E;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dma16(kg + off[r], sK + (4 * wave + r) * 64 * E);
-      dma16(vg + off[r], sV + (4 * wave + r) * 64 * E);
-    }
+  PathCopier<T> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring), sSpans,
+                       kv_len, wave, lane);
+  // step `step` goes to buffer step % kFwdRing; steps past the end re-copy
+  // the last step into their (idle) buffer so every wave issues the same
+  // number of copies per step
+  auto issue = [&](int step) {
+    copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kFwdRing) * BUF);
   };
 
   auto compute = [&](int v0, const T* sK, const T* sV) {
@@ -178,27 +153,18 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
     sched_pipeline<kLdsAhead, 4 * DB, frag_reads<T>(true)>();
   };
 
-  // two statically named buffers, so the compiler can tell the LDS written by
-  // the in-flight DMA from the LDS being read
-  issue(0, sK0, sV0);
-  wait_dma();
-  __syncthreads();
-  for (int v0 = 0;;) {
-    const bool more1 = v0 + BN < kv_len;
-    if (more1) issue(v0 + BN, sK1, sV1);
-    compute(v0, sK0, sV0);
-    if (!more1) break;
-    wait_dma();
-    __syncthreads();
-    v0 += BN;
-    const bool more0 = v0 + BN < kv_len;
-    if (more0) issue(v0 + BN, sK0, sV0);
-    compute(v0, sK1, sV1);
-    if (!more0) break;
-    wait_dma();
-    __syncthreads();
-    v0 += BN;
+#pragma unroll
+  for (int st = 0; st < kAhead; ++st) issue(st);
+  for (int step = 0; step < n_steps; ++step) {
+    // this wave's copies of `step` are done once only the kAhead - 1 newer
+    // steps' copies may be in flight; after the barrier every wave's are,
+    // and nobody reads the buffer refilled next (last read at step - 1)
+    wait_copies_barrier<(kAhead - 1) * kPathCopies>();
+    issue(step + kAhead);
+    const char* buf = ring + (step % kFwdRing) * BUF;
+    compute(step * BN, reinterpret_cast<const T*>(buf), reinterpret_cast<const T*>(buf + TILE));
   }
+  wait_copies_barrier<0>();  // no copy in flight when the workgroup ends
 
   l += __shfl_xor(l, 32);
   if (qrow < tile.nq) {
@@ -221,7 +187,7 @@ template <typename T, int D, int HG>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const int groups = a.Hq / HG;
   const dim3 grid((unsigned)a.n_tiles * (unsigned)groups);
-  hipLaunchKernelGGL((tree_attn_fwd_kernel<T, D, HG>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((tree_attn_fwd_kernel<T, D, HG>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

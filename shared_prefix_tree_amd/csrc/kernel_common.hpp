@@ -310,6 +310,66 @@ struct SpanCursor {
   }
 };
 
+// Copies of a segment's ancestor path, as one virtual key sequence, into a
+// ring of LDS buffers for the 512-thread query-major kernels.  One buffer
+// holds the K and V rows of 64 consecutive virtual positions (two 64-row
+// tiles, row-major, swizzled); waves 0-3 copy K rows, waves 4-7 V rows, 16
+// rows each in 4 instructions, so every wave issues exactly kPathCopies
+// copies per step.  A step inside one span (the common case: spans are
+// usually much longer than 64) takes its rows from one base; otherwise each
+// lane looks its rows up with a per-lane span cursor.  Positions past the
+// path read the last valid row (the caller masks them).  Byte offsets of
+// rows must fit in 32 bits (checked by the host).
+constexpr int kPathCopies = 4;
+
+template <typename T>
+struct PathCopier {
+  const T* base;       // K (waves 0-3) or V (waves 4-7) of this key/value head
+  unsigned row_bytes;  // bytes between consecutive tokens
+  unsigned lds;        // this wave's first row in buffer 0
+  unsigned chunk[4];   // this lane's swizzled byte offset in its row, per copy
+  int row;             // this lane's row of copy 0 (copy r: row + 4 r)
+  const Span* spans;   // the segment's spans, in LDS
+  int ucur, lcur;      // wave-uniform and per-lane span cursors
+  int kv_len;          // positions on the path
+
+  __device__ PathCopier(const T* k, const T* v, int g, int Hkv, unsigned ring_lds, const Span* sp, int len,
+                        int wave, int lane) {
+    base = (wave < 4 ? k : v) + (size_t)g * kRowBytes / sizeof(T);
+    row_bytes = (unsigned)Hkv * kRowBytes;
+    const int r0 = (wave & 3) * 16;
+    lds = ring_lds + (wave < 4 ? 0u : unsigned(64 * kRowBytes)) + r0 * kRowBytes;
+    row = r0 + (lane >> 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) chunk[r] = unsigned(((lane & 15) ^ swz(row + 4 * r)) * 16);
+    spans = sp;
+    ucur = 0;
+    lcur = 0;
+    kv_len = len;
+  }
+
+  // positions [v0, v0 + 64) into the buffer at byte offset `buf` of the ring
+  __device__ inline void issue(int v0, unsigned buf) {
+    while (v0 >= spans[ucur].virt + spans[ucur].len) ++ucur;
+    const Span sp = spans[ucur];
+    int phys[4];
+    if (v0 + 64 <= sp.virt + sp.len && v0 + 64 <= kv_len) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) phys[r] = sp.phys + (v0 - sp.virt) + row + 4 * r;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = min(v0 + row + 4 * r, kv_len - 1);
+        while (v >= spans[lcur].virt + spans[lcur].len) ++lcur;
+        phys[r] = spans[lcur].phys + (v - spans[lcur].virt);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      copy16_async(base, (unsigned)phys[r] * row_bytes + chunk[r], lds + buf + 4 * r * kRowBytes);
+  }
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
