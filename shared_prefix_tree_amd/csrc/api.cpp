@@ -140,10 +140,10 @@ int gcd(int a, int b) {
   return a;
 }
 
-// Query tile of the forward and dQ kernels: 32 query rows per wavefront,
-// HG heads of a key/value group side by side.
+// Query tile of the forward and dQ kernels (8 wavefronts): 32 query rows
+// per wavefront, HG heads of a key/value group side by side.
 int fwd_query_tile(int hg) { return 32 * (8 / hg); }
-int dq_query_tile(int hg) { return 32 * (4 / hg); }
+int dq_query_tile(int hg) { return 32 * (8 / hg); }
 
 // Shared argument checks of fwd/bwd.  Returns 0 or an error code.
 int check_call(const char* fn, tree_attn_plan_t plan, const tree_attn_shape* shape, float* scale_out) {

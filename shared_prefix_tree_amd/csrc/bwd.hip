@@ -281,29 +281,31 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // 3. dQ, query-major (same walk as the forward kernel)
 
+constexpr int kDqRing = 4;
+
 template <typename T, int D, int HG>
-__global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   using quad = typename M::quad;
   constexpr int BN = 64;
-  constexpr int E = 16 / int(sizeof(T));
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int TILE = BN * kRowBytes / int(sizeof(T));
+  constexpr int TILE = BN * kRowBytes;  // bytes of one 64-row tile
+  constexpr int BUF = 2 * TILE;         // K, V
+  constexpr int kAhead = kDqRing - 1;
   static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
+  static_assert(8 % HG == 0, "eight wavefronts per workgroup");
 
-  __shared__ __attribute__((aligned(16))) T sK0[TILE];
-  __shared__ __attribute__((aligned(16))) T sV0[TILE];
-  __shared__ __attribute__((aligned(16))) T sK1[TILE];
-  __shared__ __attribute__((aligned(16))) T sV1[TILE];
+  __shared__ __attribute__((aligned(16))) char ring[kDqRing * BUF];
   __shared__ Span sSpans[kMaxSpans];
 
   int tile_rank, group;
   decode_item(blockIdx.x, a.Hq / HG, tile_rank, group);
   const QTile tile = a.qtiles[tile_rank];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 31, half = lane >> 5;
   const int ts = wave / HG;
   const int h = group * HG + wave % HG;
@@ -313,11 +315,8 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
   const int qpos = tile.pos0 + qrow;
   const int wave_pos0 = tile.pos0 + ts * 32;
   const int kv_len = tile.pos0 + tile.nq;
+  const int n_steps = (kv_len + BN - 1) / BN;
   const float c = a.scale * kLog2e;
-
-  const T* kg = static_cast<const T*>(a.k) + (size_t)g * D;
-  const T* vg = static_cast<const T*>(a.v) + (size_t)g * D;
-  const int row_stride = a.Hkv * D;
 
   frag qf[KS], of[KS];
   {
@@ -330,6 +329,12 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
   }
   const float lse2 = a.delta[(size_t)a.Hq * a.T + (size_t)h * a.T + qtok];
   const float dlt = a.delta[(size_t)h * a.T + qtok];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    settle(qf[ks]);
+    settle(of[ks]);
+  }
+  asm volatile("" ::"v"(lse2), "v"(dlt));
 
   f32x16 dq[DB];
 #pragma unroll
@@ -337,41 +342,16 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
 
   stage_spans(sSpans, a.span_ptr, a.spans, tile.seg);
   __syncthreads();
-  SpanCursor cur{sSpans, 0};
-  int lrow[4], lchunk[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    lrow[r] = (4 * wave + r) * 4 + (lane >> 4);
-    lchunk[r] = (lane & 15) ^ swz(lrow[r]);
-  }
-  // Row addresses of the 64 keys [v0, v0 + 64).  Spans are usually much
-  // longer than a step, so when the whole step lies in one span (checked
-  // with a workgroup-uniform cursor) the rows are contiguous from one base;
-  // otherwise every lane looks up its own rows.  Rows past the path read
-  // any valid row and are masked.  Offsets fit in 32 bits.
-  int ucur = 0;
-  auto issue = [&](int v0, T* sK, T* sV) {
-    while (v0 >= sSpans[ucur].virt + sSpans[ucur].len) ++ucur;
-    const int sv = sSpans[ucur].virt, sl = sSpans[ucur].len, spp = sSpans[ucur].phys;
-    int off[4];
-    if (__builtin_amdgcn_readfirstlane(int(v0 + BN <= sv + sl && v0 + BN <= kv_len))) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) off[r] = (spp + (v0 - sv) + lrow[r]) * row_stride + lchunk[r] * E;
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) off[r] = cur.phys(min(v0 + lrow[r], kv_len - 1)) * row_stride + lchunk[r] * E;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dma16(kg + off[r], sK + (4 * wave + r) * 64 * E);
-      dma16(vg + off[r], sV + (4 * wave + r) * 64 * E);
-    }
+  PathCopier<T> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring), sSpans,
+                       kv_len, wave, lane);
+  auto issue = [&](int step) {
+    copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kDqRing) * BUF);
   };
 
   // the two 32-key halves one after the other: only one half's S and dP
   // are live at a time
   auto compute = [&](int v0, const T* sK, const T* sV) {
-    const bool need_mask = v0 + BN - 1 > wave_pos0;
+    const bool need_mask = v0 + BN - 1 > wave_pos0;  // wave-uniform
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -381,13 +361,17 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
         M::mma(dp, tile_row_frag<T>(sV, kb * 32 + col, ks * 16 + half * 8), of[ks]);
       }
       sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (v0 + kb * 32 + c_row(i, half) > qpos) p[i] = 0.f;
+      }
       frag dsf[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
-        if (need_mask && v0 + kb * 32 + c_row(i, half) > qpos) p = 0.f;
-        dsf[i >> 3][i & 7] = to_elem<T>(p * (dp[i] - dlt));
-      }
+      for (int i = 0; i < 16; ++i) dsf[i >> 3][i & 7] = to_elem<T>(p[i] * (dp[i] - dlt));
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -397,25 +381,18 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
     }
   };
 
-  issue(0, sK0, sV0);
-  wait_dma();
-  __syncthreads();
-  for (int v0 = 0;;) {
-    const bool more1 = v0 + BN < kv_len;
-    if (more1) issue(v0 + BN, sK1, sV1);
-    compute(v0, sK0, sV0);
-    if (!more1) break;
-    wait_dma();
-    __syncthreads();
-    v0 += BN;
-    const bool more0 = v0 + BN < kv_len;
-    if (more0) issue(v0 + BN, sK0, sV0);
-    compute(v0, sK1, sV1);
-    if (!more0) break;
-    wait_dma();
-    __syncthreads();
-    v0 += BN;
+#pragma unroll
+  for (int st = 0; st < kAhead; ++st) issue(st);
+  for (int step = 0; step < n_steps; ++step) {
+    // this wave's copies of `step` are done once only the kAhead - 1 newer
+    // steps' copies may be in flight; after the barrier every wave's are,
+    // and nobody reads the buffer refilled next (last read at step - 1)
+    wait_copies_barrier<(kAhead - 1) * kPathCopies>();
+    issue(step + kAhead);
+    const char* buf = ring + (step % kDqRing) * BUF;
+    compute(step * BN, reinterpret_cast<const T*>(buf), reinterpret_cast<const T*>(buf + TILE));
   }
+  wait_copies_barrier<0>();  // no copy in flight when the workgroup ends
 
   if (qrow < tile.nq) {
     T* dqp = static_cast<T*>(a.dq) + ((size_t)(tile.q0 + qrow) * a.Hq + h) * D;
@@ -455,7 +432,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
 template <typename T, int D, int HG>
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((tree_attn_dq_kernel<T, D, HG>), dim3((unsigned)a.n_qtiles * (unsigned)(a.Hq / HG)),
-                     dim3(256), 0, stream, a);
+                     dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
