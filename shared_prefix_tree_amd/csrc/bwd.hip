@@ -292,12 +292,11 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = BN * kRowBytes;  // bytes of one 64-row tile
-  constexpr int BUF = 2 * TILE;         // K, V
   constexpr int kAhead = kDqRing - 1;
   static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
   static_assert(8 % HG == 0, "eight wavefronts per workgroup");
 
-  __shared__ __attribute__((aligned(16))) char ring[kDqRing * BUF];
+  __shared__ __attribute__((aligned(16))) char ring[2 * kDqRing * TILE];  // K ring, V ring
   __shared__ Span sSpans[kMaxSpans];
 
   int tile_rank, group;
@@ -342,10 +341,10 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
 
   stage_spans(sSpans, a.span_ptr, a.spans, tile.seg);
   __syncthreads();
-  PathCopier<T> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring), sSpans,
-                       kv_len, wave, lane);
+  PathCopier<T> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring),
+                       lds_addr(ring + kDqRing * TILE), sSpans, kv_len, wave, lane);
   auto issue = [&](int step) {
-    copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kDqRing) * BUF);
+    copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kDqRing) * TILE);
   };
 
   // the two 32-key halves one after the other: only one half's S and dP
@@ -389,8 +388,9 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
     // and nobody reads the buffer refilled next (last read at step - 1)
     wait_copies_barrier<(kAhead - 1) * kPathCopies>();
     issue(step + kAhead);
-    const char* buf = ring + (step % kDqRing) * BUF;
-    compute(step * BN, reinterpret_cast<const T*>(buf), reinterpret_cast<const T*>(buf + TILE));
+    const int slot = step % kDqRing;
+    compute(step * BN, reinterpret_cast<const T*>(ring + slot * TILE),
+            reinterpret_cast<const T*>(ring + (kDqRing + slot) * TILE));
   }
   wait_copies_barrier<0>();  // no copy in flight when the workgroup ends
 

@@ -16,9 +16,11 @@
 //     in registers;
 //   * the workgroup walks the segment's ancestor path as one virtual key
 //     sequence (the merged spans of the plan), 64 keys per step.  K and V
-//     rows are gathered span by span straight into a ring of four LDS
-//     buffers (global_load_lds, 16 B per lane, row-major, swizzled), three
-//     steps ahead of the compute, with one barrier per step;
+//     rows are gathered span by span straight into rings of four LDS tiles
+//     (global_load_lds, 16 B per lane, row-major, swizzled), three steps
+//     ahead of the compute, with one barrier per step; the loop is unrolled
+//     over the ring slots so every LDS read is a per-lane address register
+//     plus an immediate offset;
 //   * every wave computes S^T = K Q^T (K rows read as A fragments), the
 //     online softmax per query column, and O^T += V^T P^T (V read with the
 //     transposing LDS load).  A lane owns one query column, so the row max
@@ -29,13 +31,17 @@
 //     and denominator share the same reference) and skips most rescales;
 //   * the own-segment causal rule is "virtual key position <= query
 //     position", applied only on the last steps of the walk.
+#include <type_traits>
+
 #include "kernel_common.hpp"
 
 namespace tree_attn {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P values stay <= 256
-
 constexpr int kFwdRing = 4;
+
+template <int N>
+using Slot = std::integral_constant<int, N>;
 
 template <typename T, int D, int HG>
 __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
@@ -46,12 +52,13 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = BN * kRowBytes;  // bytes of one 64-row tile
-  constexpr int BUF = 2 * TILE;         // K, V
   constexpr int kAhead = kFwdRing - 1;
   static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
   static_assert(8 % HG == 0, "eight wavefronts per workgroup");
+  static_assert(kFwdRing == 4, "the walk is unrolled over four ring slots");
 
-  __shared__ __attribute__((aligned(16))) char ring[kFwdRing * BUF];
+  // K ring then V ring (each 64 KB, so a slot offset fits an LDS immediate)
+  __shared__ __attribute__((aligned(16))) char ring[2 * kFwdRing * TILE];
   __shared__ Span sSpans[kMaxSpans];
 
   int tile_rank, group;
@@ -88,22 +95,25 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
 
   stage_spans(sSpans, a.span_ptr, a.spans, tile.seg);
   __syncthreads();
-  PathCopier<T> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring), sSpans,
-                       kv_len, wave, lane);
-  // step `step` goes to buffer step % kFwdRing; steps past the end re-copy
-  // the last step into their (idle) buffer so every wave issues the same
+  PathCopier<T> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring),
+                       lds_addr(ring + kFwdRing * TILE), sSpans, kv_len, wave, lane);
+  // step `step` goes to slot step % kFwdRing; steps past the end re-copy
+  // the last step into their (idle) slot so every wave issues the same
   // number of copies per step
   auto issue = [&](int step) {
-    copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kFwdRing) * BUF);
+    copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kFwdRing) * TILE);
   };
+  TileAddr<T, D> ka, va;  // per-lane read addresses in slot 0 of each ring
+  ka.init(lds_addr(ring), lane);
+  va.init(lds_addr(ring + kFwdRing * TILE), lane);
 
-  auto compute = [&](int v0, const T* sK, const T* sV) {
+  auto compute = [&](int v0, auto B) {
+    constexpr int off = decltype(B)::value * TILE;
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        M::mma(s[kb], tile_row_frag<T>(sK, kb * 32 + col, ks * 16 + half * 8), qf[ks]);
+      for (int ks = 0; ks < KS; ++ks) M::mma(s[kb], ka.row(ks, off + kb * 32 * kRowBytes), qf[ks]);
     sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
 
     if (v0 + BN - 1 > wave_pos0) {
@@ -148,21 +158,30 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          M::mma(o[db], tile_tr_frag<T>(sV, kb * 32 + 16 * hh, db * 32, lane), pf[kb][hh]);
+        for (int hh = 0; hh < 2; ++hh) M::mma(o[db], va.tr(db, off + (kb * 32 + 16 * hh) * kRowBytes), pf[kb][hh]);
     sched_pipeline<kLdsAhead, 4 * DB, frag_reads<T>(true)>();
+  };
+  auto body = [&](int step, auto B) {
+    // this wave's copies of `step` are done once only the kAhead - 1 newer
+    // steps' copies may be in flight; after the barrier every wave's are,
+    // and nobody reads the slot refilled next (last read at step - 1)
+    wait_copies_barrier<(kAhead - 1) * kPathCopies>();
+    issue(step + kAhead);
+    compute(step * BN, B);
   };
 
 #pragma unroll
   for (int st = 0; st < kAhead; ++st) issue(st);
-  for (int step = 0; step < n_steps; ++step) {
-    // this wave's copies of `step` are done once only the kAhead - 1 newer
-    // steps' copies may be in flight; after the barrier every wave's are,
-    // and nobody reads the buffer refilled next (last read at step - 1)
-    wait_copies_barrier<(kAhead - 1) * kPathCopies>();
-    issue(step + kAhead);
-    const char* buf = ring + (step % kFwdRing) * BUF;
-    compute(step * BN, reinterpret_cast<const T*>(buf), reinterpret_cast<const T*>(buf + TILE));
+  // unrolled over the ring slots so every LDS offset is a constant
+  for (int step = 0;; step += kFwdRing) {
+    body(step, Slot<0>{});
+    if (step + 1 >= n_steps) break;
+    body(step + 1, Slot<1>{});
+    if (step + 2 >= n_steps) break;
+    body(step + 2, Slot<2>{});
+    if (step + 3 >= n_steps) break;
+    body(step + 3, Slot<3>{});
+    if (step + 4 >= n_steps) break;
   }
   wait_copies_barrier<0>();  // no copy in flight when the workgroup ends
 

@@ -263,6 +263,116 @@ __device__ inline void sched_pipeline() {
   }
 }
 
+// Per-lane LDS byte addresses of the fragments a wavefront reads from a
+// 64-row tile (layout of tile_off), kept in registers for the whole kernel.
+// A read adds a compile-time byte offset (ring slot, tile, row block that is
+// a multiple of 16 rows) which the LDS instruction takes as an immediate;
+// the swizzle repeats every 16 rows, so the per-lane part does not depend
+// on the row block.  The addresses are made opaque to the compiler so it
+// keeps exactly these registers instead of re-deriving one per offset.
+//   row(ks):  the A/B fragment of row (block + lane % 32), elements
+//             [16 ks + 8 half, +8) -- tile_row_frag;
+//   tr(db):   the transposed fragment of rows (block + 0..15) and columns
+//             [32 db, +32) -- tile_tr_frag.
+template <typename T, int D>
+struct TileAddr;
+
+template <int D>
+struct TileAddr<__bf16, D> {
+  static constexpr int KS = D / 16, DB = D / 32;
+  using frag = Mfma<__bf16>::frag;
+  unsigned rowa[KS];
+  unsigned tra[DB][2];
+
+  __device__ void init(unsigned tile, int lane) {
+    const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      rowa[ks] = tile + col * kRowBytes + (((2 * ks + half) ^ swz(col)) * 16);
+      asm volatile("" : "+v"(rowa[ks]));
+    }
+    const int g = lane >> 4, k = lane & 15;
+    const int rr = 4 * (g >> 1) + (k >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = db * 32 + 16 * (g & 1) + 4 * (k & 3);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int row = rr + 8 * p;
+        tra[db][p] = tile + row * kRowBytes + (((d >> 3) ^ swz(row)) * 16) + (d & 7) * 2;
+        asm volatile("" : "+v"(tra[db][p]));
+      }
+    }
+  }
+  __device__ inline frag row(int ks, int off) const {
+    return *reinterpret_cast<const __attribute__((address_space(3))) frag*>((size_t)(rowa[ks] + off));
+  }
+  __device__ inline frag tr(int db, int off) const {
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) s16x4*>((size_t)(tra[db][0] + off)));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) s16x4*>((size_t)(tra[db][1] + off)));
+    return Mfma<__bf16>::cat(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b));
+  }
+};
+
+template <int D>
+struct TileAddr<float, D> {
+  static constexpr int KS = D / 16, DB = D / 32;
+  using frag = Mfma<float>::frag;
+  unsigned rowa[KS][2];
+  unsigned tra[DB][8];
+
+  __device__ void init(unsigned tile, int lane) {
+    const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        rowa[ks][j] = tile + col * kRowBytes + (((4 * ks + 2 * half + j) ^ swz(col)) * 16);
+        asm volatile("" : "+v"(rowa[ks][j]));
+      }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = db * 32 + col;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = 8 * (j >> 2) + 4 * half + (j & 3);
+        tra[db][j] = tile + row * kRowBytes + (((d >> 2) ^ swz(row)) * 16) + (d & 3) * 4;
+        asm volatile("" : "+v"(tra[db][j]));
+      }
+    }
+  }
+  __device__ inline frag row(int ks, int off) const {
+    const f32x4 lo = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>((size_t)(rowa[ks][0] + off));
+    const f32x4 hi = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>((size_t)(rowa[ks][1] + off));
+    return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  __device__ inline frag tr(int db, int off) const {
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      f[j] = *reinterpret_cast<const __attribute__((address_space(3))) float*>((size_t)(tra[db][j] + off));
+    return f;
+  }
+};
+
+// As sched_pipeline, and VALU instructions after every matrix product, so
+// that independent vector work of the same wavefront runs while the matrix
+// core is busy.
+constexpr int kSchedValu = 0x0002;
+
+template <int AHEAD, int N, int READS, int VALU>
+__device__ inline void sched_pipeline_valu() {
+  if constexpr (READS > 0 && N > AHEAD) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AHEAD * READS, 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (READS > 0 && i < N - AHEAD) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU, 0);
+  }
+}
+
 // Row offset of C-layout value i for lane half `half`.
 __device__ inline constexpr int c_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
 
@@ -310,35 +420,36 @@ struct SpanCursor {
   }
 };
 
-// Copies of a segment's ancestor path, as one virtual key sequence, into a
-// ring of LDS buffers for the 512-thread query-major kernels.  One buffer
-// holds the K and V rows of 64 consecutive virtual positions (two 64-row
-// tiles, row-major, swizzled); waves 0-3 copy K rows, waves 4-7 V rows, 16
-// rows each in 4 instructions, so every wave issues exactly kPathCopies
-// copies per step.  A step inside one span (the common case: spans are
-// usually much longer than 64) takes its rows from one base; otherwise each
-// lane looks its rows up with a per-lane span cursor.  Positions past the
-// path read the last valid row (the caller masks them).  Byte offsets of
-// rows must fit in 32 bits (checked by the host).
+// Copies of a segment's ancestor path, as one virtual key sequence, into
+// LDS rings for the 512-thread query-major kernels.  Step `step` covers the
+// 64 virtual positions [64 step, 64 step + 64); its K rows go to a 64-row
+// tile of the K ring and its V rows to the same slot of the V ring
+// (row-major, swizzled).  Waves 0-3 copy K rows, waves 4-7 V rows, 16 rows
+// each in 4 instructions, so every wave issues exactly kPathCopies copies
+// per step.  A step inside one span (the common case: spans are usually
+// much longer than 64) takes its rows from one base; otherwise each lane
+// looks its rows up with a per-lane span cursor.  Positions past the path
+// read the last valid row (the caller masks them).  Byte offsets of rows
+// must fit in 32 bits (checked by the host).
 constexpr int kPathCopies = 4;
 
 template <typename T>
 struct PathCopier {
   const T* base;       // K (waves 0-3) or V (waves 4-7) of this key/value head
   unsigned row_bytes;  // bytes between consecutive tokens
-  unsigned lds;        // this wave's first row in buffer 0
+  unsigned lds;        // this wave's first row in slot 0 of its ring
   unsigned chunk[4];   // this lane's swizzled byte offset in its row, per copy
   int row;             // this lane's row of copy 0 (copy r: row + 4 r)
   const Span* spans;   // the segment's spans, in LDS
   int ucur, lcur;      // wave-uniform and per-lane span cursors
   int kv_len;          // positions on the path
 
-  __device__ PathCopier(const T* k, const T* v, int g, int Hkv, unsigned ring_lds, const Span* sp, int len,
-                        int wave, int lane) {
+  __device__ PathCopier(const T* k, const T* v, int g, int Hkv, unsigned k_ring, unsigned v_ring, const Span* sp,
+                        int len, int wave, int lane) {
     base = (wave < 4 ? k : v) + (size_t)g * kRowBytes / sizeof(T);
     row_bytes = (unsigned)Hkv * kRowBytes;
     const int r0 = (wave & 3) * 16;
-    lds = ring_lds + (wave < 4 ? 0u : unsigned(64 * kRowBytes)) + r0 * kRowBytes;
+    lds = (wave < 4 ? k_ring : v_ring) + r0 * kRowBytes;
     row = r0 + (lane >> 4);
 #pragma unroll
     for (int r = 0; r < 4; ++r) chunk[r] = unsigned(((lane & 15) ^ swz(row + 4 * r)) * 16);
@@ -348,8 +459,8 @@ struct PathCopier {
     kv_len = len;
   }
 
-  // positions [v0, v0 + 64) into the buffer at byte offset `buf` of the ring
-  __device__ inline void issue(int v0, unsigned buf) {
+  // positions [v0, v0 + 64) into the ring slot at byte offset `slot`
+  __device__ inline void issue(int v0, unsigned slot) {
     while (v0 >= spans[ucur].virt + spans[ucur].len) ++ucur;
     const Span sp = spans[ucur];
     int phys[4];
@@ -366,7 +477,7 @@ struct PathCopier {
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      copy16_async(base, (unsigned)phys[r] * row_bytes + chunk[r], lds + buf + 4 * r * kRowBytes);
+      copy16_async(base, (unsigned)phys[r] * row_bytes + chunk[r], lds + slot + 4 * r * kRowBytes);
   }
 };
 
