@@ -25,6 +25,8 @@
 //   3. dq (query-major): the forward's walk over the ancestor path,
 //        S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - delta),
 //        dQ^T += K^T dS^T   (K^T from the transposing LDS load).
+#include <type_traits>
+
 #include "kernel_common.hpp"
 
 namespace tree_attn {
@@ -81,9 +83,12 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
 // step, so the wait for a step's tiles is a fixed count.  One barrier per
 // step orders copies, P hand-off and buffer reuse.
 
+template <int N>
+using Slot = std::integral_constant<int, N>;
+
 template <typename T>
 struct DkdvRing {
-  static constexpr int value = sizeof(T) == 2 ? 4 : 3;  // fits P and the ring in LDS
+  static constexpr int value = sizeof(T) == 2 ? 4 : 3;  // fits P and the rings in LDS
 };
 
 template <typename T, int D>
@@ -94,17 +99,18 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   constexpr int kRing = DkdvRing<T>::value;
   constexpr int kAhead = kRing - 2;               // steps copied ahead
   constexpr int BM = 64;                          // queries per step
-  constexpr int E = 16 / int(sizeof(T));
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = BM * kRowBytes;            // bytes of one 64-row tile
-  constexpr int BUF = 2 * TILE + 2 * BM * 4;      // Q, dO, lse2, delta
+  constexpr int STATS = 2 * BM * 4;               // lse2, delta of one step
   constexpr int kCopies = 5;                      // copies per wave per step
   constexpr int PBLK = 2 * 64;                    // P fragments per wave block
   static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
-  static_assert(4 * DB * 16 * 64 * 4 <= kRing * BUF, "the partials fit the ring");
+  static_assert(4 * DB * 16 * 64 * 4 <= 2 * kRing * TILE, "the partials fit the rings");
 
-  __shared__ __attribute__((aligned(16))) char ring[kRing * BUF];
+  // Q ring, then dO ring (each at most 64 KB, so a slot offset fits an LDS
+  // immediate), then the lse2 / delta ring
+  __shared__ __attribute__((aligned(16))) char ring[2 * kRing * TILE + kRing * STATS];
   __shared__ __attribute__((aligned(16))) frag pshare[2][4 * PBLK];
   __shared__ __attribute__((aligned(16))) float junk[64];
 
@@ -123,7 +129,6 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   const int ktok = tile.k0 + min(kl, tile.nk - 1);
   const int jkey = tile.k0 + kl;
   const float c = a.scale * kLog2e;
-
   const float* lse2 = a.delta + (size_t)a.Hq * a.T;
 
   // the dV waves keep K, the dK waves V (both as B fragments)
@@ -140,6 +145,8 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   const int n_steps = a.G * nblk;
   const int last = tile.qend - 1;
 
+  const unsigned q_ring = lds_addr(ring), o_ring = q_ring + kRing * TILE, s_ring = q_ring + 2 * kRing * TILE;
+
   // copy plan: waves 0-3 copy Q rows, waves 4-7 dO rows, 16 rows per wave
   // (4 instructions of 4 rows); every wave copies one 64-float stat vector
   // (waves 0 and 1 the real lse2 / delta, the rest a discarded duplicate).
@@ -147,22 +154,21 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   const int crow0 = wblk * 16;
   const T* csrc = static_cast<const T*>(dk_role ? a.dout : a.q);
   const float* ssrc = wave == 1 ? a.delta : lse2;
-  const unsigned ring_lds = lds_addr(ring);
-  const unsigned c_lds = ring_lds + (dk_role ? TILE : 0) + crow0 * kRowBytes;
-  const unsigned s_lds = wave < 2 ? ring_lds + 2 * TILE + wave * BM * 4 : lds_addr(junk);
-  const unsigned s_step = wave < 2 ? BUF : 0;
+  const unsigned c_lds = (dk_role ? o_ring : q_ring) + crow0 * kRowBytes;
+  const unsigned s_lds = wave < 2 ? s_ring + wave * BM * 4 : lds_addr(junk);
+  const unsigned s_step = wave < 2 ? STATS : 0;
   const int crow = crow0 + (lane >> 4);
   unsigned cchunk[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) cchunk[r] = (((lane & 15) ^ swz(crow + 4 * r)) * 16);
   const unsigned row_bytes = (unsigned)a.Hq * D * sizeof(T);
-  // Step `step` goes to buffer step % kRing.  Steps past the end copy the
-  // last step's rows into their (idle) buffer, so every wave always issues
+  // Step `step` goes to slot step % kRing.  Steps past the end copy the
+  // last step's rows into their (idle) slot, so every wave always issues
   // kCopies copies.  Rows past the range read the last row (masked to
   // P = 0).  Each copy reads from a wave-uniform row base plus a small
   // per-lane offset.
   auto issue = [&](int step) {
-    const unsigned bofs = (unsigned)(step % kRing) * BUF;
+    const unsigned slot = (unsigned)(step % kRing);
     step = min(step, n_steps - 1);
     const int h = g * a.G + step / nblk;
     const int i0 = tile.k0 + (step % nblk) * BM;
@@ -170,15 +176,24 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     const int lim = last - i0;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      copy16_async(base, (unsigned)min(crow + 4 * r, lim) * row_bytes + cchunk[r], c_lds + bofs + 4 * r * kRowBytes);
-    copy4_async(ssrc + (size_t)h * a.T + i0, (unsigned)min(lane, lim) * 4u, s_lds + (bofs / BUF) * s_step);
+      copy16_async(base, (unsigned)min(crow + 4 * r, lim) * row_bytes + cchunk[r], c_lds + slot * TILE + 4 * r * kRowBytes);
+    copy4_async(ssrc + (size_t)h * a.T + i0, (unsigned)min(lane, lim) * 4u, s_lds + slot * s_step);
   };
 
+  // Per-lane read addresses in slot 0: A rows (Q for the dV role, dO for
+  // the dK role), C transposed (dO, resp. Q), and this lane's stat rows.
+  TileAddr<T, D> ta, tc;
+  ta.init(dk_role ? o_ring : q_ring, lane);
+  tc.init(dk_role ? q_ring : o_ring, lane);
+  unsigned stat_addr = s_ring + (dk_role ? BM * 4 : 0) + (qh * 32 + 4 * half) * 4;
+  asm volatile("" : "+v"(stat_addr));
+
   // lse2 / delta of this lane's 16 C-layout query rows: 4 runs of 4
-  auto row_stats = [&](const float* sX, float (&x)[16]) {
+  auto row_stats = [&](int off, float (&x)[16]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f32x4 v4 = *reinterpret_cast<const f32x4*>(sX + qh * 32 + 8 * j + 4 * half);
+      const f32x4 v4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+          (size_t)(stat_addr + off + 32 * j));
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[4 * j + e] = v4[e];
     }
@@ -188,67 +203,123 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  // One step of either role, as one instruction stream over role-selected
-  // tiles (so the accumulators never move between registers):
-  //   t   = A B^T   with A = Q (dV role) or dO (dK role), B = K or V;
-  //   x   = P        dV role: exp2(t c - lse2), zero before the key or past
-  //                  the range, rounded to the input type, also left in LDS
-  //       = dS       dK role: P (t - delta) with the dV wave's P;
-  //   acc += C^T x   with C = dO (dV role) or Q (dK role).
-  auto step_fn = [&](int step, const char* buf, frag* pshr) {
-    const T* sA = reinterpret_cast<const T*>(buf + (dk_role ? TILE : 0));
-    const T* sC = reinterpret_cast<const T*>(buf + (dk_role ? 0 : TILE));
-    const float* sX = reinterpret_cast<const float*>(buf + 2 * TILE + (dk_role ? BM * 4 : 0));
-    f32x16 t = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) M::mma(t, tile_row_frag<T>(sA, qh * 32 + col, ks * 16 + half * 8), kv[ks]);
-    sched_pipeline<kLdsAhead, KS, frag_reads<T>(false)>();
-    float x[16];
-    row_stats(sX, x);
-    frag xf[2];
-    if (!dk_role) {
-      const int i0 = tile.k0 + (step % nblk) * BM;
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(t[i], c, -x[i]));
-      if (__builtin_amdgcn_readfirstlane(int(i0 + qh * 32 < tile.k0 + kb * 32 + 31 ||
-                                             i0 + qh * 32 + 31 >= tile.qend))) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = i0 + qh * 32 + c_row(i, half);
-          if (qi < jkey || qi >= tile.qend) p[i] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) xf[i >> 3][i & 7] = to_elem<T>(p[i]);
-      pshr[lane] = xf[0];
-      pshr[64 + lane] = xf[1];
-    } else {
-      const frag pf[2] = {pshr[lane], pshr[64 + lane]};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) xf[i >> 3][i & 7] = to_elem<T>(float(pf[i >> 3][i & 7]) * (t[i] - x[i]));
-    }
+  // Both roles run every iteration step = 0 .. n_steps without branches
+  // (the accumulators stay in place):
+  //   dV waves: dV^T += dO^T P of step - 1 (P kept in registers), then
+  //             S = Q K^T and P = exp2(S c - lse2) of `step` (zero before
+  //             the key or past the range, rounded to the input type, also
+  //             left in LDS for the dK waves);
+  //   dK waves: dP = dO V^T of step - 1, dS = P (dP - delta) with the dV
+  //             waves' P, dK^T += Q^T dS.
+  // Each wave thus alternates matrix work with its vector work, and within
+  // a SIMD one role's products cover the other role's exp / dS.  Iteration
+  // 0 reads a zero-filled slot (kRing - 1) and P buffer, so it adds zero;
+  // the S, P of iteration n_steps are never used.
+  frag pprev[2];
+  auto dv_iter = [&](int step, auto J) {
+    constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        M::mma(acc[db], tile_tr_frag<T>(sC, qh * 32 + 16 * hh, db * 32, lane), xf[hh]);
+        M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * kRowBytes), pprev[hh]);
+    f32x16 t = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) M::mma(t, ta.row(ks, j * TILE + qh * 32 * kRowBytes), kv[ks]);
+    sched_pipeline<kLdsAhead, 2 * DB + KS, frag_reads<T>(true)>();
+    float x[16];
+    row_stats(j * STATS, x);
+    const int i0 = tile.k0 + (step % nblk) * BM;
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(t[i], c, -x[i]));
+    if (__builtin_amdgcn_readfirstlane(int(i0 + qh * 32 < tile.k0 + kb * 32 + 31 ||
+                                           i0 + qh * 32 + 31 >= tile.qend))) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qi = i0 + qh * 32 + c_row(i, half);
+        if (qi < jkey || qi >= tile.qend) p[i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pprev[i >> 3][i & 7] = to_elem<T>(p[i]);
+    frag* pshr = &pshare[step & 1][wblk * PBLK];
+    pshr[lane] = pprev[0];
+    pshr[64 + lane] = pprev[1];
+  };
+  auto dk_iter = [&](int step, auto J) {
+    constexpr int jp = (decltype(J)::value + kRing - 1) % kRing;
+    f32x16 t = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) M::mma(t, ta.row(ks, jp * TILE + qh * 32 * kRowBytes), kv[ks]);
+    sched_pipeline<kLdsAhead, KS, frag_reads<T>(false)>();
+    float x[16];
+    row_stats(jp * STATS, x);
+    const frag* pshr = &pshare[(step + 1) & 1][wblk * PBLK];
+    const frag pf[2] = {pshr[lane], pshr[64 + lane]};
+    frag xf[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xf[i >> 3][i & 7] = to_elem<T>(float(pf[i >> 3][i & 7]) * (t[i] - x[i]));
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * kRowBytes), xf[hh]);
     sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
   };
 
-#pragma unroll
-  for (int s = 0; s < kAhead; ++s) issue(s);
-  for (int step = 0; step <= n_steps; ++step) {
+  // iteration `step` in slot J = step % kRing
+  auto body = [&](auto R, int step, auto J) {
     // this wave's copies of `step` are done once only the kAhead - 1 newer
     // steps' copies may be in flight; after the barrier every wave's are,
-    // the P of step - 1 is in LDS, and nobody reads the buffer refilled next
-    // (last read by the dK waves at step - 2)
+    // the P of step - 1 is in LDS, and nobody reads the slot refilled next
+    // (last read at step - 2)
     wait_copies_barrier<(kAhead - 1) * kCopies>();
     issue(step + kAhead);
-    const int my = dk_role ? step - 1 : step;  // the dK waves run one behind
-    if (my >= 0 && my < n_steps) step_fn(my, ring + (my % kRing) * BUF, &pshare[my & 1][wblk * PBLK]);
+    if constexpr (decltype(R)::value)
+      dk_iter(step, J);
+    else
+      dv_iter(step, J);
+  };
+  // unrolled over the ring slots so every LDS offset is a constant; returns
+  // true once iteration n_steps is done
+  auto round = [&](auto self, auto R, int step, auto J) -> bool {
+    constexpr int j = decltype(J)::value;
+    body(R, step + j, J);
+    if (step + j >= n_steps) return true;
+    if constexpr (j + 1 < kRing) {
+      return self(self, R, step, Slot<j + 1>{});
+    } else {
+      return false;
+    }
+  };
+  // each role runs its own copy of the loop (the same barriers in the same
+  // order), so neither role's accumulators are merged with the other's
+  auto walk = [&](auto R) {
+    for (int step = 0;; step += kRing)
+      if (round(round, R, step, Slot<0>{})) break;
+  };
+
+  // zero the slot and P buffer that iteration 0 reads, then start copying
+  {
+    float* z0 = reinterpret_cast<float*>(ring + (kRing - 1) * TILE);              // Q tile
+    float* z1 = reinterpret_cast<float*>(ring + (2 * kRing - 1) * TILE);          // dO tile
+    for (int i = tid; i < TILE / 4; i += 512) z0[i] = z1[i] = 0.f;
+    float* z2 = reinterpret_cast<float*>(ring + 2 * kRing * TILE + (kRing - 1) * STATS);
+    if (tid < STATS / 4) z2[tid] = 0.f;
+    float* z3 = reinterpret_cast<float*>(&pshare[1][0]);
+    for (int i = tid; i < int(sizeof(pshare[1]) / 4); i += 512) z3[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pprev[0][e] = pprev[1][e] = to_elem<T>(0.f);
   }
-  wait_copies_barrier<0>();  // no copy in flight; the ring is free
+  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < kAhead; ++st) issue(st);
+  if (dk_role)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
+  wait_copies_barrier<0>();  // no copy in flight; the rings are free
 
   // fixed-order reduction of the two query halves, then one store per key:
   // the qh = 1 wave of each (role, kb) parks its partial in the ring
@@ -295,8 +366,10 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
   constexpr int kAhead = kDqRing - 1;
   static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
   static_assert(8 % HG == 0, "eight wavefronts per workgroup");
+  static_assert(kDqRing == 4, "the walk is unrolled over four ring slots");
 
-  __shared__ __attribute__((aligned(16))) char ring[2 * kDqRing * TILE];  // K ring, V ring
+  // K ring then V ring (each 64 KB, so a slot offset fits an LDS immediate)
+  __shared__ __attribute__((aligned(16))) char ring[2 * kDqRing * TILE];
   __shared__ Span sSpans[kMaxSpans];
 
   int tile_rank, group;
@@ -347,17 +420,22 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
     copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kDqRing) * TILE);
   };
 
+  TileAddr<T, D> ka, va;  // per-lane read addresses in slot 0 of each ring
+  ka.init(lds_addr(ring), lane);
+  va.init(lds_addr(ring + kDqRing * TILE), lane);
+
   // the two 32-key halves one after the other: only one half's S and dP
   // are live at a time
-  auto compute = [&](int v0, const T* sK, const T* sV) {
+  auto compute = [&](int v0, auto B) {
+    constexpr int off = decltype(B)::value * TILE;
     const bool need_mask = v0 + BN - 1 > wave_pos0;  // wave-uniform
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        M::mma(s, tile_row_frag<T>(sK, kb * 32 + col, ks * 16 + half * 8), qf[ks]);
-        M::mma(dp, tile_row_frag<T>(sV, kb * 32 + col, ks * 16 + half * 8), of[ks]);
+        M::mma(s, ka.row(ks, off + kb * 32 * kRowBytes), qf[ks]);
+        M::mma(dp, va.row(ks, off + kb * 32 * kRowBytes), of[ks]);
       }
       sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
       float p[16];
@@ -375,22 +453,31 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-          M::mma(dq[db], tile_tr_frag<T>(sK, kb * 32 + 16 * hh, db * 32, lane), dsf[hh]);
+          M::mma(dq[db], ka.tr(db, off + (kb * 32 + 16 * hh) * kRowBytes), dsf[hh]);
       sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
     }
+  };
+  auto body = [&](int step, auto B) {
+    // this wave's copies of `step` are done once only the kAhead - 1 newer
+    // steps' copies may be in flight; after the barrier every wave's are,
+    // and nobody reads the slot refilled next (last read at step - 1)
+    wait_copies_barrier<(kAhead - 1) * kPathCopies>();
+    issue(step + kAhead);
+    compute(step * BN, B);
   };
 
 #pragma unroll
   for (int st = 0; st < kAhead; ++st) issue(st);
-  for (int step = 0; step < n_steps; ++step) {
-    // this wave's copies of `step` are done once only the kAhead - 1 newer
-    // steps' copies may be in flight; after the barrier every wave's are,
-    // and nobody reads the buffer refilled next (last read at step - 1)
-    wait_copies_barrier<(kAhead - 1) * kPathCopies>();
-    issue(step + kAhead);
-    const int slot = step % kDqRing;
-    compute(step * BN, reinterpret_cast<const T*>(ring + slot * TILE),
-            reinterpret_cast<const T*>(ring + (kDqRing + slot) * TILE));
+  // unrolled over the ring slots so every LDS offset is a constant
+  for (int step = 0;; step += kDqRing) {
+    body(step, Slot<0>{});
+    if (step + 1 >= n_steps) break;
+    body(step + 1, Slot<1>{});
+    if (step + 2 >= n_steps) break;
+    body(step + 2, Slot<2>{});
+    if (step + 3 >= n_steps) break;
+    body(step + 3, Slot<3>{});
+    if (step + 4 >= n_steps) break;
   }
   wait_copies_barrier<0>();  // no copy in flight when the workgroup ends
 
