@@ -167,17 +167,25 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   // kCopies copies.  Rows past the range read the last row (masked to
   // P = 0).  Each copy reads from a wave-uniform row base plus a small
   // per-lane offset.
-  auto issue = [&](int step) {
-    const unsigned slot = (unsigned)(step % kRing);
-    step = min(step, n_steps - 1);
-    const int h = g * a.G + step / nblk;
-    const int i0 = tile.k0 + (step % nblk) * BM;
-    const T* base = csrc + ((size_t)i0 * a.Hq + h) * D;
-    const int lim = last - i0;
+  // The copy stream advances one step per call: (cp_h, cp_i0) is the head
+  // and first query of the next step to copy, kept incrementally (no
+  // division); once past the end it stays on the last step.
+  int cp_step = 0, cp_h = g * a.G, cp_i0 = tile.k0;
+  auto issue = [&](int slot) {
+    const T* base = csrc + ((size_t)cp_i0 * a.Hq + cp_h) * D;
+    const int lim = last - cp_i0;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      copy16_async(base, (unsigned)min(crow + 4 * r, lim) * row_bytes + cchunk[r], c_lds + slot * TILE + 4 * r * kRowBytes);
-    copy4_async(ssrc + (size_t)h * a.T + i0, (unsigned)min(lane, lim) * 4u, s_lds + slot * s_step);
+      copy16_async(base, (unsigned)min(crow + 4 * r, lim) * row_bytes + cchunk[r],
+                   c_lds + (unsigned)slot * TILE + 4 * r * kRowBytes);
+    copy4_async(ssrc + (size_t)cp_h * a.T + cp_i0, (unsigned)min(lane, lim) * 4u, s_lds + (unsigned)slot * s_step);
+    if (++cp_step < n_steps) {
+      cp_i0 += BM;
+      if (cp_i0 > last) {
+        cp_i0 = tile.k0;
+        ++cp_h;
+      }
+    }
   };
 
   // Per-lane read addresses in slot 0: A rows (Q for the dV role, dO for
@@ -216,6 +224,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   // 0 reads a zero-filled slot (kRing - 1) and P buffer, so it adds zero;
   // the S, P of iteration n_steps are never used.
   frag pprev[2];
+  int dv_i0 = tile.k0;  // first query of the dV waves' current step
   auto dv_iter = [&](int step, auto J) {
     constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
 #pragma unroll
@@ -229,7 +238,8 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     sched_pipeline<kLdsAhead, 2 * DB + KS, frag_reads<T>(true)>();
     float x[16];
     row_stats(j * STATS, x);
-    const int i0 = tile.k0 + (step % nblk) * BM;
+    const int i0 = dv_i0;
+    dv_i0 = dv_i0 + BM > last ? tile.k0 : dv_i0 + BM;
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(t[i], c, -x[i]));
@@ -275,7 +285,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     // the P of step - 1 is in LDS, and nobody reads the slot refilled next
     // (last read at step - 2)
     wait_copies_barrier<(kAhead - 1) * kCopies>();
-    issue(step + kAhead);
+    issue((decltype(J)::value + kAhead) % kRing);
     if constexpr (decltype(R)::value)
       dk_iter(step, J);
     else
