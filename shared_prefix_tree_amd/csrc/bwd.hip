@@ -77,11 +77,11 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
 //   * waves 4-7 (dK), one step behind: dP = dO V^T, dS = P (dP - delta)
 //     with the P of the matching dV wave, dK^T += Q^T dS.
 // So S is formed once per step and each SIMD issues the minimum 32 matrix
-// products per step.  Q / dO tiles and their lse2 / delta go through a ring
-// of kRing LDS buffers, copied kRing - 2 steps ahead of the dV waves (the
-// dK waves hold one more); every wave issues the same number of copies per
-// step, so the wait for a step's tiles is a fixed count.  One barrier per
-// step orders copies, P hand-off and buffer reuse.
+// products per step.  Q / dO tiles and their lse2 / delta go through rings
+// of kRing LDS slots, copied kRing - 2 steps ahead of the dV waves (the dK
+// waves hold one more) by the dK waves alone; each of them issues the same
+// number of copies per step, so the wait for a step's tiles is a fixed
+// count.  One barrier per step orders copies, P hand-off and slot reuse.
 
 template <int N>
 using Slot = std::integral_constant<int, N>;
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   constexpr int DB = D / 32;
   constexpr int TILE = BM * kRowBytes;            // bytes of one 64-row tile
   constexpr int STATS = 2 * BM * 4;               // lse2, delta of one step
-  constexpr int kCopies = 5;                      // copies per wave per step
+  constexpr int kCopiesK = 9;                     // copies per dK wave per step
   constexpr int PBLK = 2 * 64;                    // P fragments per wave block
   static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
   static_assert(4 * DB * 16 * 64 * 4 <= 2 * kRing * TILE, "the partials fit the rings");
@@ -147,37 +147,39 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 
   const unsigned q_ring = lds_addr(ring), o_ring = q_ring + kRing * TILE, s_ring = q_ring + 2 * kRing * TILE;
 
-  // copy plan: waves 0-3 copy Q rows, waves 4-7 dO rows, 16 rows per wave
-  // (4 instructions of 4 rows); every wave copies one 64-float stat vector
-  // (waves 0 and 1 the real lse2 / delta, the rest a discarded duplicate).
-  // Per lane: row crow0 + 4 r + lane / 16 and its swizzled 16-byte chunk.
+  // Copy plan: only the dK waves copy (the dV waves carry the exponentials).
+  // dK wave w copies rows 16 (w - 4) .. +16 of the Q tile and of the dO
+  // tile (4 instructions of 4 rows each) and one 64-float stat vector
+  // (waves 4 and 5 the real lse2 / delta, waves 6 and 7 a discarded
+  // duplicate): kCopiesK copies per step.  Per lane: row crow0 + 4 r +
+  // lane / 16 and its swizzled 16-byte chunk.
   const int crow0 = wblk * 16;
-  const T* csrc = static_cast<const T*>(dk_role ? a.dout : a.q);
-  const float* ssrc = wave == 1 ? a.delta : lse2;
-  const unsigned c_lds = (dk_role ? o_ring : q_ring) + crow0 * kRowBytes;
-  const unsigned s_lds = wave < 2 ? s_ring + wave * BM * 4 : lds_addr(junk);
-  const unsigned s_step = wave < 2 ? STATS : 0;
+  const float* ssrc = wave == 5 ? a.delta : lse2;
+  const unsigned s_lds = wave == 4 || wave == 5 ? s_ring + (wave - 4) * BM * 4 : lds_addr(junk);
+  const unsigned s_step = wave == 4 || wave == 5 ? STATS : 0;
   const int crow = crow0 + (lane >> 4);
   unsigned cchunk[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) cchunk[r] = (((lane & 15) ^ swz(crow + 4 * r)) * 16);
   const unsigned row_bytes = (unsigned)a.Hq * D * sizeof(T);
-  // Step `step` goes to slot step % kRing.  Steps past the end copy the
-  // last step's rows into their (idle) slot, so every wave always issues
-  // kCopies copies.  Rows past the range read the last row (masked to
-  // P = 0).  Each copy reads from a wave-uniform row base plus a small
-  // per-lane offset.
-  // The copy stream advances one step per call: (cp_h, cp_i0) is the head
-  // and first query of the next step to copy, kept incrementally (no
-  // division); once past the end it stays on the last step.
+  // Step `step` goes to slot step % kRing.  The copy stream advances one
+  // step per call: (cp_h, cp_i0) is the head and first query of the next
+  // step to copy, kept incrementally (no division); past the end it stays
+  // on the last step, re-copying its rows into the (idle) slot, so a dK wave
+  // always issues kCopiesK copies.  Rows past the range read the last row
+  // (masked to P = 0).  Each copy reads from a wave-uniform row base plus a
+  // small per-lane offset.
   int cp_step = 0, cp_h = g * a.G, cp_i0 = tile.k0;
   auto issue = [&](int slot) {
-    const T* base = csrc + ((size_t)cp_i0 * a.Hq + cp_h) * D;
     const int lim = last - cp_i0;
+    const size_t row0 = ((size_t)cp_i0 * a.Hq + cp_h) * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      copy16_async(base, (unsigned)min(crow + 4 * r, lim) * row_bytes + cchunk[r],
-                   c_lds + (unsigned)slot * TILE + 4 * r * kRowBytes);
+    for (int r = 0; r < 4; ++r) {
+      const unsigned voff = (unsigned)min(crow + 4 * r, lim) * row_bytes + cchunk[r];
+      const unsigned lofs = crow0 * kRowBytes + (unsigned)slot * TILE + 4 * r * kRowBytes;
+      copy16_async(static_cast<const T*>(a.q) + row0, voff, q_ring + lofs);
+      copy16_async(static_cast<const T*>(a.dout) + row0, voff, o_ring + lofs);
+    }
     copy4_async(ssrc + (size_t)cp_h * a.T + cp_i0, (unsigned)min(lane, lim) * 4u, s_lds + (unsigned)slot * s_step);
     if (++cp_step < n_steps) {
       cp_i0 += BM;
@@ -280,16 +282,18 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 
   // iteration `step` in slot J = step % kRing
   auto body = [&](auto R, int step, auto J) {
-    // this wave's copies of `step` are done once only the kAhead - 1 newer
-    // steps' copies may be in flight; after the barrier every wave's are,
+    // a dK wave's copies of `step` are done once only the kAhead - 1 newer
+    // steps' copies may be in flight; after the barrier every dK wave's are,
     // the P of step - 1 is in LDS, and nobody reads the slot refilled next
     // (last read at step - 2)
-    wait_copies_barrier<(kAhead - 1) * kCopies>();
-    issue((decltype(J)::value + kAhead) % kRing);
-    if constexpr (decltype(R)::value)
+    if constexpr (decltype(R)::value) {
+      wait_copies_barrier<(kAhead - 1) * kCopiesK>();
+      issue((decltype(J)::value + kAhead) % kRing);
       dk_iter(step, J);
-    else
+    } else {
+      wait_copies_barrier<0>();
       dv_iter(step, J);
+    }
   };
   // unrolled over the ring slots so every LDS offset is a constant; returns
   // true once iteration n_steps is done
@@ -323,8 +327,10 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     for (int e = 0; e < 8; ++e) pprev[0][e] = pprev[1][e] = to_elem<T>(0.f);
   }
   __syncthreads();
+  if (dk_role) {
 #pragma unroll
-  for (int st = 0; st < kAhead; ++st) issue(st);
+    for (int st = 0; st < kAhead; ++st) issue(st);
+  }
   if (dk_role)
     walk(std::true_type{});
   else
