@@ -24,7 +24,7 @@
 //   * every wave computes S^T = K Q^T (K rows read as A fragments), the
 //     online softmax per query column, and O^T += V^T P^T (V read with the
 //     transposing LDS load).  A lane owns one query column, so the row max
-//     and row sum are in-lane reductions plus one exchange with lane l ^ 32;
+//     and row sum are in-lane reductions plus one lane swap with lane l ^ 32;
 //   * the softmax works in base 2 with the scale folded into one FMA per
 //     score; the running max is only moved (and O rescaled) when a row's
 //     maximum grows by more than 2^8, which keeps the result exact (numerator
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    mx = max_halves(mx) * c;
     const bool grow = mx > m + kRescaleSlack;
     const float mnew = grow ? mx : m;
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
   }
   wait_copies_barrier<0>();  // no copy in flight when the workgroup ends
 
-  l += __shfl_xor(l, 32);
+  l = sum_halves(l);
   if (qrow < tile.nq) {
     const float inv = 1.f / l;
     T* op = static_cast<T*>(a.out) + ((size_t)(tile.q0 + qrow) * a.Hq + h) * D;

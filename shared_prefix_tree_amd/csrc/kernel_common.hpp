@@ -373,6 +373,18 @@ __device__ inline void sched_pipeline_valu() {
   }
 }
 
+// Combine v over lanes l and l ^ 32 (the two halves of a wavefront) with one
+// VALU lane swap instead of an LDS permute: v_permlane32_swap with both
+// operands v returns v's lanes 0..31 twice and its lanes 32..63 twice.
+__device__ inline float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Row offset of C-layout value i for lane half `half`.
 __device__ inline constexpr int c_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
 
