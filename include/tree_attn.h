@@ -70,7 +70,7 @@ typedef struct {
   int32_t total_tokens; /* T; must equal the plan's token count */
   int32_t num_q_heads;  /* Hq >= 1 */
   int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0 */
-  int32_t head_dim;     /* D: 128 for bf16, 64 for fp32 */
+  int32_t head_dim;     /* D: 64 or 128 for bf16, 64 for fp32 */
   int32_t dtype;        /* TREE_ATTN_BF16 or TREE_ATTN_FP32 */
   float softmax_scale;  /* <= 0: 1/sqrt(D) */
 } tree_attn_shape;

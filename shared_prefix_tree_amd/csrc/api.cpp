@@ -162,7 +162,8 @@ int check_call(const char* fn, tree_attn_plan_t plan, const tree_attn_shape* sha
   if (shape->num_q_heads % shape->num_kv_heads != 0)
     return fail(TREE_ATTN_UNSUPPORTED, f + ": num_q_heads must be a multiple of num_kv_heads");
   if (shape->dtype == TREE_ATTN_BF16) {
-    if (shape->head_dim != 128) return fail(TREE_ATTN_UNSUPPORTED, f + ": bf16 needs head_dim 128");
+    if (shape->head_dim != 128 && shape->head_dim != 64)
+      return fail(TREE_ATTN_UNSUPPORTED, f + ": bf16 needs head_dim 64 or 128");
   } else if (shape->dtype == TREE_ATTN_FP32) {
     if (shape->head_dim != 64) return fail(TREE_ATTN_UNSUPPORTED, f + ": fp32 needs head_dim 64");
   } else {
@@ -304,9 +305,12 @@ int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t 
   a.scale = scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (shape->dtype == TREE_ATTN_BF16) {
+  if (shape->dtype == TREE_ATTN_BF16 && shape->head_dim == 128) {
     e = hg == 4 ? launch_fwd<__bf16, 128, 4>(a, s) : hg == 2 ? launch_fwd<__bf16, 128, 2>(a, s)
                                                            : launch_fwd<__bf16, 128, 1>(a, s);
+  } else if (shape->dtype == TREE_ATTN_BF16) {
+    e = hg == 4 ? launch_fwd<__bf16, 64, 4>(a, s) : hg == 2 ? launch_fwd<__bf16, 64, 2>(a, s)
+                                                          : launch_fwd<__bf16, 64, 1>(a, s);
   } else {
     e = hg == 4 ? launch_fwd<float, 64, 4>(a, s) : hg == 2 ? launch_fwd<float, 64, 2>(a, s)
                                                          : launch_fwd<float, 64, 1>(a, s);
@@ -373,21 +377,25 @@ int prep_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   return TREE_ATTN_OK;
 }
 
+template <typename T, int D>
+hipError_t launch_bwd_stages(const BwdArgs& a, int hg, int stages, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (stages & kRowStat) e = launch_bwd_rowstat<T, D>(a, s);
+  if (e == hipSuccess && (stages & kDkDv)) e = launch_bwd_dkdv<T, D>(a, s);
+  if (e == hipSuccess && (stages & kDq))
+    e = hg == 4 ? launch_bwd_dq<T, D, 4>(a, s) : hg == 2 ? launch_bwd_dq<T, D, 2>(a, s) : launch_bwd_dq<T, D, 1>(a, s);
+  return e;
+}
+
 int run_bwd(const char* fn, const BwdArgs& a, const tree_attn_shape* shape, int hg, int stages, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf16 = shape->dtype == TREE_ATTN_BF16;
-  hipError_t e = hipSuccess;
-  if (stages & kRowStat) e = bf16 ? launch_bwd_rowstat<__bf16, 128>(a, s) : launch_bwd_rowstat<float, 64>(a, s);
-  if (e == hipSuccess && (stages & kDkDv))
-    e = bf16 ? launch_bwd_dkdv<__bf16, 128>(a, s) : launch_bwd_dkdv<float, 64>(a, s);
-  if (e == hipSuccess && (stages & kDq)) {
-    if (bf16)
-      e = hg == 4 ? launch_bwd_dq<__bf16, 128, 4>(a, s) : hg == 2 ? launch_bwd_dq<__bf16, 128, 2>(a, s)
-                                                                : launch_bwd_dq<__bf16, 128, 1>(a, s);
-    else
-      e = hg == 4 ? launch_bwd_dq<float, 64, 4>(a, s) : hg == 2 ? launch_bwd_dq<float, 64, 2>(a, s)
-                                                              : launch_bwd_dq<float, 64, 1>(a, s);
-  }
+  hipError_t e;
+  if (shape->dtype == TREE_ATTN_BF16 && shape->head_dim == 128)
+    e = launch_bwd_stages<__bf16, 128>(a, hg, stages, s);
+  else if (shape->dtype == TREE_ATTN_BF16)
+    e = launch_bwd_stages<__bf16, 64>(a, hg, stages, s);
+  else
+    e = launch_bwd_stages<float, 64>(a, hg, stages, s);
   if (e != hipSuccess) return hip_fail((std::string(fn) + ": launch").c_str(), e);
   return TREE_ATTN_OK;
 }

@@ -101,11 +101,14 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   constexpr int BM = 64;                          // queries per step
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int TILE = BM * kRowBytes;            // bytes of one 64-row tile
+  constexpr int RB = D * int(sizeof(T));          // bytes of one head's row
+  constexpr int TILE = BM * RB;                   // bytes of one 64-row tile
   constexpr int STATS = 2 * BM * 4;               // lse2, delta of one step
-  constexpr int kCopiesK = 9;                     // copies per dK wave per step
+  constexpr int NC = path_copies(RB);             // copies per 16 rows
+  constexpr int RPC = 1024 / RB;                  // rows per copy
+  constexpr int kCopiesK = 2 * NC + 1;            // copies per dK wave per step
   constexpr int PBLK = 2 * 64;                    // P fragments per wave block
-  static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
+  static_assert(RB == 128 || RB == 256, "128- or 256-byte rows");
   static_assert(4 * DB * 16 * 64 * 4 <= 2 * kRing * TILE, "the partials fit the rings");
 
   // Q ring, then dO ring (each at most 64 KB, so a slot offset fits an LDS
@@ -149,19 +152,19 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 
   // Copy plan: only the dK waves copy (the dV waves carry the exponentials).
   // dK wave w copies rows 16 (w - 4) .. +16 of the Q tile and of the dO
-  // tile (4 instructions of 4 rows each) and one 64-float stat vector
+  // tile (NC instructions of 1 KB each) and one 64-float stat vector
   // (waves 4 and 5 the real lse2 / delta, waves 6 and 7 a discarded
-  // duplicate): kCopiesK copies per step.  Per lane: row crow0 + 4 r +
-  // lane / 16 and its swizzled 16-byte chunk.
+  // duplicate): kCopiesK copies per step.  Per lane: row crow0 + RPC r +
+  // lane / (RB / 16) and its swizzled 16-byte chunk.
   const int crow0 = wblk * 16;
   const float* ssrc = wave == 5 ? a.delta : lse2;
   const unsigned s_lds = wave == 4 || wave == 5 ? s_ring + (wave - 4) * BM * 4 : lds_addr(junk);
   const unsigned s_step = wave == 4 || wave == 5 ? STATS : 0;
-  const int crow = crow0 + (lane >> 4);
-  unsigned cchunk[4];
+  const int crow = crow0 + lane / (RB / 16);
+  unsigned cchunk[NC];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) cchunk[r] = (((lane & 15) ^ swz(crow + 4 * r)) * 16);
-  const unsigned row_bytes = (unsigned)a.Hq * D * sizeof(T);
+  for (int r = 0; r < NC; ++r) cchunk[r] = (((lane % (RB / 16)) ^ swz<RB>(crow + RPC * r)) * 16);
+  const unsigned row_bytes = (unsigned)a.Hq * RB;
   // Step `step` goes to slot step % kRing.  The copy stream advances one
   // step per call: (cp_h, cp_i0) is the head and first query of the next
   // step to copy, kept incrementally (no division); past the end it stays
@@ -174,9 +177,9 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     const int lim = last - cp_i0;
     const size_t row0 = ((size_t)cp_i0 * a.Hq + cp_h) * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const unsigned voff = (unsigned)min(crow + 4 * r, lim) * row_bytes + cchunk[r];
-      const unsigned lofs = crow0 * kRowBytes + (unsigned)slot * TILE + 4 * r * kRowBytes;
+    for (int r = 0; r < NC; ++r) {
+      const unsigned voff = (unsigned)min(crow + RPC * r, lim) * row_bytes + cchunk[r];
+      const unsigned lofs = crow0 * RB + (unsigned)slot * TILE + RPC * r * RB;
       copy16_async(static_cast<const T*>(a.q) + row0, voff, q_ring + lofs);
       copy16_async(static_cast<const T*>(a.dout) + row0, voff, o_ring + lofs);
     }
@@ -233,10 +236,10 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * kRowBytes), pprev[hh]);
+        M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * RB), pprev[hh]);
     f32x16 t = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) M::mma(t, ta.row(ks, j * TILE + qh * 32 * kRowBytes), kv[ks]);
+    for (int ks = 0; ks < KS; ++ks) M::mma(t, ta.row(ks, j * TILE + qh * 32 * RB), kv[ks]);
     sched_pipeline<kLdsAhead, 2 * DB + KS, frag_reads<T>(true)>();
     float x[16];
     row_stats(j * STATS, x);
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     constexpr int jp = (decltype(J)::value + kRing - 1) % kRing;
     f32x16 t = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) M::mma(t, ta.row(ks, jp * TILE + qh * 32 * kRowBytes), kv[ks]);
+    for (int ks = 0; ks < KS; ++ks) M::mma(t, ta.row(ks, jp * TILE + qh * 32 * RB), kv[ks]);
     sched_pipeline<kLdsAhead, KS, frag_reads<T>(false)>();
     float x[16];
     row_stats(jp * STATS, x);
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * kRowBytes), xf[hh]);
+        M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * RB), xf[hh]);
     sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
   };
 
@@ -378,9 +381,10 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
   constexpr int BN = 64;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int TILE = BN * kRowBytes;  // bytes of one 64-row tile
+  constexpr int RB = D * int(sizeof(T));  // bytes of one head's row
+  constexpr int TILE = BN * RB;           // bytes of one 64-row tile
   constexpr int kAhead = kDqRing - 1;
-  static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
+  static_assert(RB == 128 || RB == 256, "128- or 256-byte rows");
   static_assert(8 % HG == 0, "eight wavefronts per workgroup");
   static_assert(kDqRing == 4, "the walk is unrolled over four ring slots");
 
@@ -430,7 +434,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
 
   stage_spans(sSpans, a.span_ptr, a.spans, tile.seg);
   __syncthreads();
-  PathCopier<T> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring),
+  PathCopier<T, RB> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring),
                        lds_addr(ring + kDqRing * TILE), sSpans, kv_len, wave, lane);
   auto issue = [&](int step) {
     copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kDqRing) * TILE);
@@ -450,8 +454,8 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        M::mma(s, ka.row(ks, off + kb * 32 * kRowBytes), qf[ks]);
-        M::mma(dp, va.row(ks, off + kb * 32 * kRowBytes), of[ks]);
+        M::mma(s, ka.row(ks, off + kb * 32 * RB), qf[ks]);
+        M::mma(dp, va.row(ks, off + kb * 32 * RB), of[ks]);
       }
       sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
       float p[16];
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-          M::mma(dq[db], ka.tr(db, off + (kb * 32 + 16 * hh) * kRowBytes), dsf[hh]);
+          M::mma(dq[db], ka.tr(db, off + (kb * 32 + 16 * hh) * RB), dsf[hh]);
       sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
     }
   };
@@ -477,7 +481,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
     // this wave's copies of `step` are done once only the kAhead - 1 newer
     // steps' copies may be in flight; after the barrier every wave's are,
     // and nobody reads the slot refilled next (last read at step - 1)
-    wait_copies_barrier<(kAhead - 1) * kPathCopies>();
+    wait_copies_barrier<(kAhead - 1) * path_copies(RB)>();
     issue(step + kAhead);
     compute(step * BN, B);
   };
@@ -540,12 +544,17 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
 }
 
 template hipError_t launch_bwd_rowstat<__bf16, 128>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_rowstat<__bf16, 64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_rowstat<float, 64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_dkdv<__bf16, 128>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_dkdv<__bf16, 64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_dkdv<float, 64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_dq<__bf16, 128, 1>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_dq<__bf16, 128, 2>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_dq<__bf16, 128, 4>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_dq<__bf16, 64, 1>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_dq<__bf16, 64, 2>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd_dq<__bf16, 64, 4>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_dq<float, 64, 1>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_dq<float, 64, 2>(const BwdArgs&, hipStream_t);
 template hipError_t launch_bwd_dq<float, 64, 4>(const BwdArgs&, hipStream_t);

@@ -51,9 +51,10 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
   constexpr int BN = 64;  // keys per step
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int TILE = BN * kRowBytes;  // bytes of one 64-row tile
+  constexpr int RB = D * int(sizeof(T));  // bytes of one head's row
+  constexpr int TILE = BN * RB;           // bytes of one 64-row tile
   constexpr int kAhead = kFwdRing - 1;
-  static_assert(D * int(sizeof(T)) == kRowBytes, "one 256-byte row per token");
+  static_assert(RB == 128 || RB == 256, "128- or 256-byte rows");
   static_assert(8 % HG == 0, "eight wavefronts per workgroup");
   static_assert(kFwdRing == 4, "the walk is unrolled over four ring slots");
 
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
 
   stage_spans(sSpans, a.span_ptr, a.spans, tile.seg);
   __syncthreads();
-  PathCopier<T> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring),
+  PathCopier<T, RB> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring),
                        lds_addr(ring + kFwdRing * TILE), sSpans, kv_len, wave, lane);
   // step `step` goes to slot step % kFwdRing; steps past the end re-copy
   // the last step into their (idle) slot so every wave issues the same
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) M::mma(s[kb], ka.row(ks, off + kb * 32 * kRowBytes), qf[ks]);
+      for (int ks = 0; ks < KS; ++ks) M::mma(s[kb], ka.row(ks, off + kb * 32 * RB), qf[ks]);
     sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
 
     if (v0 + BN - 1 > wave_pos0) {
@@ -158,14 +159,14 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) M::mma(o[db], va.tr(db, off + (kb * 32 + 16 * hh) * kRowBytes), pf[kb][hh]);
+        for (int hh = 0; hh < 2; ++hh) M::mma(o[db], va.tr(db, off + (kb * 32 + 16 * hh) * RB), pf[kb][hh]);
     sched_pipeline<kLdsAhead, 4 * DB, frag_reads<T>(true)>();
   };
   auto body = [&](int step, auto B) {
     // this wave's copies of `step` are done once only the kAhead - 1 newer
     // steps' copies may be in flight; after the barrier every wave's are,
     // and nobody reads the slot refilled next (last read at step - 1)
-    wait_copies_barrier<(kAhead - 1) * kPathCopies>();
+    wait_copies_barrier<(kAhead - 1) * path_copies(RB)>();
     issue(step + kAhead);
     compute(step * BN, B);
   };
@@ -214,6 +215,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
 template hipError_t launch_fwd<__bf16, 128, 1>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd<__bf16, 128, 2>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd<__bf16, 128, 4>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd<__bf16, 64, 1>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd<__bf16, 64, 2>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd<__bf16, 64, 4>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd<float, 64, 1>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd<float, 64, 2>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd<float, 64, 4>(const FwdArgs&, hipStream_t);

@@ -101,48 +101,42 @@ __device__ inline typename Mfma<T>::frag load_frag(const T* p) {
   return *reinterpret_cast<const typename Mfma<T>::frag*>(p);
 }
 
-// Two 4-element runs p[0..3] and p[8..11] as one fragment (transposed tiles).
-template <typename T>
-__device__ inline typename Mfma<T>::frag load_frag_split(const T* p) {
-  using quad = typename Mfma<T>::quad;
-  return Mfma<T>::cat(*reinterpret_cast<const quad*>(p), *reinterpret_cast<const quad*>(p + 8));
-}
-
 // ---------------------------------------------------------------------------
-// LDS tiles: ROWS x D elements, one 256-byte row per token, stored row-major
-// with the 16 16-byte chunks of row r XOR-swizzled by
-// f(r) = ((r&3)<<2) | ((r>>2)&3).  With 64 banks x 4 B (256 bytes per cycle)
-// both read patterns are free of bank conflicts:
-//   * row reads (ds_read_b128, 16 lanes per cycle): 16 consecutive rows
-//     (aligned) at one logical chunk land on 16 distinct chunks, since f takes
-//     all 16 values there;
-//   * transposing reads (ds_read_b64_tr_b16, 32 lanes per cycle): 4
-//     consecutive rows (aligned) x 4 consecutive chunks (aligned): with
-//     chunk = 4m + x and f = 4y + k the physical chunk is 4(m^y) + (x^k), 16
-//     distinct values.
-// Tiles are filled with global_load_lds_dwordx4: lane l of a wave writes the
-// 16 bytes at (wave base + 16 l), so each lane loads the global chunk that
-// belongs at that swizzled position.
+// LDS tiles: 64 rows (tokens) of RB = D * sizeof(T) bytes (one head's row:
+// 256 B for bf16 D = 128 and fp32 D = 64, 128 B for bf16 D = 64), stored
+// row-major with the 16-byte chunks of row r XOR-swizzled by swz<RB>(r).
+// With 64 banks x 4 B (256 bytes per cycle) both read patterns are free of
+// bank conflicts:
+//   * row reads (ds_read_b128, 16 lanes per cycle) touch 16 consecutive rows
+//     (aligned) at one logical chunk;
+//   * transposing reads (ds_read_b64_tr_b16, 32 lanes per cycle) touch 4
+//     consecutive rows (aligned) x 4 consecutive chunks (aligned).
+// RB = 256 (16 chunks, one row per 256-byte bank line): f(r) = ((r&3)<<2) |
+//   ((r>>2)&3) takes all 16 values on 16 aligned rows; on 4 aligned rows x 4
+//   aligned chunks, chunk 4m + x and f = 4y + k give 4(m^y) + (x^k), 16
+//   distinct chunks.
+// RB = 128 (8 chunks, rows r and r+1 share a bank line, in its two halves):
+//   with t = (r>>1) & 7, f(r) = t ^ ((t&1)<<2) is a permutation of 0..7 in t,
+//   so 16 aligned rows hit 2 x 8 distinct half-lines; of 4 aligned rows, the
+//   two of each parity have t of different parity, hence f differing in bit 2,
+//   so their 4-chunk runs land in opposite halves of the 8 chunks.
+// Both swizzles repeat every 16 rows, so a 16-row block offset is a plain
+// byte offset.  Tiles are filled with global_load_lds_dwordx4: lane l of a
+// wave writes the 16 bytes at (wave base + 16 l), so each lane loads the
+// global chunk that belongs at that swizzled position.
 
-constexpr int kRowBytes = 256;
-constexpr int kChunksPerRow = kRowBytes / 16;
-
-__device__ inline int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-
-// element offset of logical chunk `chunk` of `row` in a tile of element type T
-template <typename T>
-__device__ inline int tile_off(int row, int chunk) {
-  return row * (kRowBytes / int(sizeof(T))) + ((chunk ^ swz(row)) * (16 / int(sizeof(T))));
+template <int RB>
+__device__ inline int swz(int row) {
+  static_assert(RB == 128 || RB == 256, "128- or 256-byte rows");
+  if constexpr (RB == 256) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    const int t = (row >> 1) & 7;
+    return t ^ ((t & 1) << 2);
+  }
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
-
-// Asynchronous 16-byte-per-lane copy global -> LDS (wave-uniform LDS base).
-__device__ inline void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
-}
-
-__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Copies global -> LDS written as inline assembly, for kernels that keep
 // several copies in flight and count them themselves.  The compiler does not
@@ -186,52 +180,7 @@ __device__ inline void wait_copies_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Fragment of 8 consecutive elements [e0, e0+8) of a tile row (e0 % 8 == 0).
-template <typename T>
-__device__ inline typename Mfma<T>::frag tile_row_frag(const T* tile, int row, int e0) {
-  constexpr int E = 16 / int(sizeof(T));
-  if constexpr (E == 8) {
-    return *reinterpret_cast<const typename Mfma<T>::frag*>(tile + tile_off<T>(row, e0 / E));
-  } else {
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + tile_off<T>(row, e0 / E));
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(tile + tile_off<T>(row, e0 / E + 1));
-    return typename Mfma<T>::frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-}
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Transposed A fragment: lane l gets column d = d0 + (l % 32) of the tile and
-// the 8 rows {r0 + 4h + 0..3} and {r0 + 8 + 4h + 0..3}, h = l / 32 -- the
-// rows a C-layout B fragment covers (see the header comment).  bf16 uses two
-// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
-// of the 8-byte pieces read by lanes 4j + i/4 (j = 0..3), so lane 4j+k of
-// group g reads row r0 + 4(g/2) + j at column d0 + 16(g%2) + 4k.  fp32 reads
-// the same elements one by one.
-template <typename T>
-__device__ inline typename Mfma<T>::frag tile_tr_frag(const T* tile, int r0, int d0, int lane) {
-  if constexpr (sizeof(T) == 2) {
-    const int g = lane >> 4, k = lane & 15;
-    const int row = r0 + 4 * (g >> 1) + (k >> 2);
-    const int d = d0 + 16 * (g & 1) + 4 * (k & 3);
-    const T* p0 = tile + tile_off<T>(row, d >> 3) + (d & 7);
-    const T* p1 = tile + tile_off<T>(row + 8, d >> 3) + (d & 7);
-    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p0);
-    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p1);
-    const bf16x4 lo = __builtin_bit_cast(bf16x4, a);
-    const bf16x4 hi = __builtin_bit_cast(bf16x4, b);
-    return Mfma<T>::cat(lo, hi);
-  } else {
-    const int h = lane >> 5, d = d0 + (lane & 31);
-    typename Mfma<T>::frag f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = r0 + 8 * (j >> 2) + 4 * h + (j & 3);
-      f[j] = tile[tile_off<T>(row, d >> 2) + (d & 3)];
-    }
-    return f;
-  }
-}
 
 // Software pipelining of LDS fragment reads against the products that use
 // them.  After N products, each fed by an A fragment read from LDS, this
@@ -271,15 +220,22 @@ __device__ inline void sched_pipeline() {
 // on the row block.  The addresses are made opaque to the compiler so it
 // keeps exactly these registers instead of re-deriving one per offset.
 //   row(ks):  the A/B fragment of row (block + lane % 32), elements
-//             [16 ks + 8 half, +8) -- tile_row_frag;
-//   tr(db):   the transposed fragment of rows (block + 0..15) and columns
-//             [32 db, +32) -- tile_tr_frag.
+//             [16 ks + 8 half, +8);
+//   tr(db):   the transposed A fragment of columns [32 db, +32): lane l gets
+//             column 32 db + l % 32 and the 8 rows {block + 4h + 0..3} and
+//             {block + 8 + 4h + 0..3}, h = l / 32 -- the rows a C-layout B
+//             fragment covers (see the header comment).  bf16 uses two
+//             ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+//             element i % 4 of the 8-byte pieces read by lanes 4j + i / 4
+//             (j = 0..3), so lane 4j + k of group g reads row
+//             block + 4 (g / 2) + j at column 32 db + 16 (g % 2) + 4 k.
+//             fp32 reads the same elements one by one.
 template <typename T, int D>
 struct TileAddr;
 
 template <int D>
 struct TileAddr<__bf16, D> {
-  static constexpr int KS = D / 16, DB = D / 32;
+  static constexpr int KS = D / 16, DB = D / 32, RB = 2 * D;
   using frag = Mfma<__bf16>::frag;
   unsigned rowa[KS];
   unsigned tra[DB][2];
@@ -288,7 +244,7 @@ struct TileAddr<__bf16, D> {
     const int col = lane & 31, half = lane >> 5;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      rowa[ks] = tile + col * kRowBytes + (((2 * ks + half) ^ swz(col)) * 16);
+      rowa[ks] = tile + col * RB + (((2 * ks + half) ^ swz<RB>(col)) * 16);
       asm volatile("" : "+v"(rowa[ks]));
     }
     const int g = lane >> 4, k = lane & 15;
@@ -299,7 +255,7 @@ struct TileAddr<__bf16, D> {
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int row = rr + 8 * p;
-        tra[db][p] = tile + row * kRowBytes + (((d >> 3) ^ swz(row)) * 16) + (d & 7) * 2;
+        tra[db][p] = tile + row * RB + (((d >> 3) ^ swz<RB>(row)) * 16) + (d & 7) * 2;
         asm volatile("" : "+v"(tra[db][p]));
       }
     }
@@ -318,7 +274,7 @@ struct TileAddr<__bf16, D> {
 
 template <int D>
 struct TileAddr<float, D> {
-  static constexpr int KS = D / 16, DB = D / 32;
+  static constexpr int KS = D / 16, DB = D / 32, RB = 4 * D;
   using frag = Mfma<float>::frag;
   unsigned rowa[KS][2];
   unsigned tra[DB][8];
@@ -329,7 +285,7 @@ struct TileAddr<float, D> {
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        rowa[ks][j] = tile + col * kRowBytes + (((4 * ks + 2 * half + j) ^ swz(col)) * 16);
+        rowa[ks][j] = tile + col * RB + (((4 * ks + 2 * half + j) ^ swz<RB>(col)) * 16);
         asm volatile("" : "+v"(rowa[ks][j]));
       }
 #pragma unroll
@@ -338,7 +294,7 @@ struct TileAddr<float, D> {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int row = 8 * (j >> 2) + 4 * half + (j & 3);
-        tra[db][j] = tile + row * kRowBytes + (((d >> 2) ^ swz(row)) * 16) + (d & 3) * 4;
+        tra[db][j] = tile + row * RB + (((d >> 2) ^ swz<RB>(row)) * 16) + (d & 3) * 4;
         asm volatile("" : "+v"(tra[db][j]));
       }
     }
@@ -421,50 +377,43 @@ __device__ inline void stage_spans(Span* lds_spans, const int32_t* span_ptr, con
   for (int i = threadIdx.x; i < n; i += blockDim.x) lds_spans[i] = spans[first + i];
 }
 
-// Monotone cursor over a segment's merged spans: maps a virtual key position
-// of the reconstructed sequence to its physical token.
-struct SpanCursor {
-  const Span* spans;  // LDS copy
-  int cur;
-  __device__ inline int phys(int v) {
-    while (v >= spans[cur].virt + spans[cur].len) ++cur;
-    return spans[cur].phys + (v - spans[cur].virt);
-  }
-};
-
 // Copies of a segment's ancestor path, as one virtual key sequence, into
 // LDS rings for the 512-thread query-major kernels.  Step `step` covers the
 // 64 virtual positions [64 step, 64 step + 64); its K rows go to a 64-row
 // tile of the K ring and its V rows to the same slot of the V ring
 // (row-major, swizzled).  Waves 0-3 copy K rows, waves 4-7 V rows, 16 rows
-// each in 4 instructions, so every wave issues exactly kPathCopies copies
-// per step.  A step inside one span (the common case: spans are usually
-// much longer than 64) takes its rows from one base; otherwise each lane
-// looks its rows up with a per-lane span cursor.  Positions past the path
-// read the last valid row (the caller masks them).  Byte offsets of rows
-// must fit in 32 bits (checked by the host).
-constexpr int kPathCopies = 4;
+// each; one copy instruction moves 1 KB = 1024 / RB rows, so every wave
+// issues exactly path_copies(RB) copies per step.  A step inside one span
+// (the common case: spans are usually much longer than 64) takes its rows
+// from one base; otherwise each lane looks its rows up with a per-lane span
+// cursor.  Positions past the path read the last valid row (the caller
+// masks them).  Byte offsets of rows must fit in 32 bits (checked by the
+// host).
+__host__ __device__ constexpr int path_copies(int RB) { return 16 * RB / 1024; }
 
-template <typename T>
+template <typename T, int RB>
 struct PathCopier {
+  static constexpr int NC = path_copies(RB);  // copies per wave per step
+  static constexpr int RPC = 1024 / RB;       // rows per copy
+  static constexpr int LPR = RB / 16;         // lanes per row
   const T* base;       // K (waves 0-3) or V (waves 4-7) of this key/value head
   unsigned row_bytes;  // bytes between consecutive tokens
   unsigned lds;        // this wave's first row in slot 0 of its ring
-  unsigned chunk[4];   // this lane's swizzled byte offset in its row, per copy
-  int row;             // this lane's row of copy 0 (copy r: row + 4 r)
+  unsigned chunk[NC];  // this lane's swizzled byte offset in its row, per copy
+  int row;             // this lane's row of copy 0 (copy r: row + RPC r)
   const Span* spans;   // the segment's spans, in LDS
   int ucur, lcur;      // wave-uniform and per-lane span cursors
   int kv_len;          // positions on the path
 
   __device__ PathCopier(const T* k, const T* v, int g, int Hkv, unsigned k_ring, unsigned v_ring, const Span* sp,
                         int len, int wave, int lane) {
-    base = (wave < 4 ? k : v) + (size_t)g * kRowBytes / sizeof(T);
-    row_bytes = (unsigned)Hkv * kRowBytes;
+    base = (wave < 4 ? k : v) + (size_t)g * RB / sizeof(T);
+    row_bytes = (unsigned)Hkv * RB;
     const int r0 = (wave & 3) * 16;
-    lds = (wave < 4 ? k_ring : v_ring) + r0 * kRowBytes;
-    row = r0 + (lane >> 4);
+    lds = (wave < 4 ? k_ring : v_ring) + r0 * RB;
+    row = r0 + lane / LPR;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) chunk[r] = unsigned(((lane & 15) ^ swz(row + 4 * r)) * 16);
+    for (int r = 0; r < NC; ++r) chunk[r] = unsigned(((lane % LPR) ^ swz<RB>(row + RPC * r)) * 16);
     spans = sp;
     ucur = 0;
     lcur = 0;
@@ -475,21 +424,21 @@ struct PathCopier {
   __device__ inline void issue(int v0, unsigned slot) {
     while (v0 >= spans[ucur].virt + spans[ucur].len) ++ucur;
     const Span sp = spans[ucur];
-    int phys[4];
+    int phys[NC];
     if (v0 + 64 <= sp.virt + sp.len && v0 + 64 <= kv_len) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) phys[r] = sp.phys + (v0 - sp.virt) + row + 4 * r;
+      for (int r = 0; r < NC; ++r) phys[r] = sp.phys + (v0 - sp.virt) + row + RPC * r;
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int v = min(v0 + row + 4 * r, kv_len - 1);
+      for (int r = 0; r < NC; ++r) {
+        const int v = min(v0 + row + RPC * r, kv_len - 1);
         while (v >= spans[lcur].virt + spans[lcur].len) ++lcur;
         phys[r] = spans[lcur].phys + (v - spans[lcur].virt);
       }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      copy16_async(base, (unsigned)phys[r] * row_bytes + chunk[r], lds + slot + 4 * r * kRowBytes);
+    for (int r = 0; r < NC; ++r)
+      copy16_async(base, (unsigned)phys[r] * row_bytes + chunk[r], lds + slot + RPC * r * RB);
   }
 };
 
