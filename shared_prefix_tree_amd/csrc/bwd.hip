@@ -11,8 +11,10 @@
 //
 // Three launches, no atomics, every output element written once by one
 // workgroup in a fixed order (bitwise reproducible):
-//   1. rowstat: delta[h,i] = sum_d dout[i,h,d] * out[i,h,d] and
-//      lse2[h,i] = lse[h,i] * log2(e), into the workspace;
+//   1. rowstat: -delta[h,i] = -sum_d dout[i,h,d] * out[i,h,d] and
+//      -lse2[h,i] = -lse[h,i] * log2(e), into the workspace (negated, so
+//      that they enter the products below as initial accumulators or as
+//      the addend of a fused multiply-add);
 //   2. dkdv (key-major): a workgroup owns 64 keys of one segment and one
 //      key/value head; in DFS pre-order the queries that see key j are the
 //      contiguous range [j, subtree_end(seg(j))), so it walks that range
@@ -38,8 +40,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restrict__ out,
                                                                 const T* __restrict__ dout,
                                                                 const float* __restrict__ lse,
-                                                                float* __restrict__ delta,
-                                                                float* __restrict__ lse2, int T_, int Hq) {
+                                                                float* __restrict__ ndelta,
+                                                                float* __restrict__ nlse2, int T_, int Hq) {
   constexpr int E = Chunk<T>::E;
   constexpr int CPR = D / E;
   constexpr int RPB = 256 / CPR;
@@ -59,8 +61,8 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
   if (valid && c == 0) {
     const int i = row / Hq, h = row % Hq;
     const size_t at = (size_t)h * T_ + i;
-    delta[at] = acc;
-    lse2[at] = lse[at] * kLog2e;
+    ndelta[at] = -acc;
+    nlse2[at] = -(lse[at] * kLog2e);
   }
 }
 
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
 // role, one of each role per SIMD; within a role, wave bits (kb, qh) pick 32
 // keys x 32 queries:
 //   * waves 0-3 (dV): S = Q K^T, P = exp2(S c - lse2) rounded to the input
-//     type, dV^T += dO^T P, and P is left in LDS;
+//     type, dV^T += dO^T P, and P is left in LDS (see PHandoff);
 //   * waves 4-7 (dK), one step behind: dP = dO V^T, dS = P (dP - delta)
 //     with the P of the matching dV wave, dK^T += Q^T dS.
 // So S is formed once per step and each SIMD issues the minimum 32 matrix
@@ -85,6 +87,36 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
 
 template <int N>
 using Slot = std::integral_constant<int, N>;
+
+// How a dV wave hands its probabilities to the dK wave of the same block.
+// bf16 inputs: P (in [0, 1]) travels as fp16, rounded to nearest -- finer
+// than the bf16 operand of dV -- and the dK wave multiplies it into dP -
+// delta with a mixed fp16 x fp32 fused multiply-add, with no separate
+// conversion; fp32 inputs: P itself.
+template <typename T>
+struct PHandoff;
+
+template <>
+struct PHandoff<__bf16> {
+  using frag = Mfma<__bf16>::frag;
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  __device__ static inline frag pack(const frag&, const float* p) {
+    h8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (_Float16)p[e];
+    return __builtin_bit_cast(frag, v);
+  }
+  __device__ static inline float times(const frag& f, int e, float x) {
+    return __builtin_fmaf((float)__builtin_bit_cast(h8, f)[e], x, 0.f);
+  }
+};
+
+template <>
+struct PHandoff<float> {
+  using frag = Mfma<float>::frag;
+  __device__ static inline frag pack(const frag& rounded, const float*) { return rounded; }
+  __device__ static inline float times(const frag& f, int e, float x) { return f[e] * x; }
+};
 
 template <typename T>
 struct DkdvRing {
@@ -197,8 +229,10 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   // Per-lane read addresses in slot 0: A rows (Q for the dV role, dO for
   // the dK role), C transposed (dO, resp. Q), and this lane's stat rows.
   TileAddr<T, D> ta, tc;
-  ta.init(dk_role ? o_ring : q_ring, lane);
-  tc.init(dk_role ? q_ring : o_ring, lane);
+  // (the wave's 32-query half of the tile is part of the base, so every
+  // read below takes a compile-time offset)
+  ta.init((dk_role ? o_ring : q_ring) + qh * 32 * RB, lane);
+  tc.init((dk_role ? q_ring : o_ring) + qh * 32 * RB, lane);
   unsigned stat_addr = s_ring + (dk_role ? BM * 4 : 0) + (qh * 32 + 4 * half) * 4;
   asm volatile("" : "+v"(stat_addr));
 
@@ -237,10 +271,10 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * RB), pprev[hh]);
+        M::mma(acc[db], tc.tr(db, jp * TILE + 16 * hh * RB), pprev[hh]);
     f32x16 t = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) M::mma(t, ta.row(ks, j * TILE + qh * 32 * RB), kv[ks]);
+    for (int ks = 0; ks < KS; ++ks) M::mma(t, ta.row(ks, j * TILE), kv[ks]);
     sched_pipeline<kLdsAhead, 2 * DB + KS, frag_reads<T>(true)>();
     float x[16];
     row_stats(j * STATS, x);
@@ -248,7 +282,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     dv_i0 = dv_i0 + BM > last ? tile.k0 : dv_i0 + BM;
     float p[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(t[i], c, -x[i]));
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(t[i], c, x[i]));
     if (__builtin_amdgcn_readfirstlane(int(i0 + qh * 32 < tile.k0 + kb * 32 + 31 ||
                                            i0 + qh * 32 + 31 >= tile.qend))) {
 #pragma unroll
@@ -260,28 +294,38 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) pprev[i >> 3][i & 7] = to_elem<T>(p[i]);
     frag* pshr = &pshare[step & 1][wblk * PBLK];
-    pshr[lane] = pprev[0];
-    pshr[64 + lane] = pprev[1];
+    pshr[lane] = PHandoff<T>::pack(pprev[0], p);
+    pshr[64 + lane] = PHandoff<T>::pack(pprev[1], p + 8);
   };
-  auto dk_iter = [&](int step, auto J) {
-    constexpr int jp = (decltype(J)::value + kRing - 1) % kRing;
-    f32x16 t = f32x16{};
+  float xd[16];  // -delta of the dK waves' next step (read one iteration early)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) M::mma(t, ta.row(ks, jp * TILE + qh * 32 * RB), kv[ks]);
-    sched_pipeline<kLdsAhead, KS, frag_reads<T>(false)>();
-    float x[16];
-    row_stats(jp * STATS, x);
+  for (int i = 0; i < 16; ++i) xd[i] = 0.f;
+  auto dk_iter = [&](int step, auto J) {
+    constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
     const frag* pshr = &pshare[(step + 1) & 1][wblk * PBLK];
     const frag pf[2] = {pshr[lane], pshr[64 + lane]};
+    // (the P reads go ahead of the software-pipelined fragment reads)
+    __builtin_amdgcn_sched_barrier(0);
+    // dP - delta: the products accumulate onto -delta
+    f32x16 t;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[i] = xd[i];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) M::mma(t, ta.row(ks, jp * TILE), kv[ks]);
+    sched_pipeline<kLdsAhead, KS, frag_reads<T>(false)>();
     frag xf[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) xf[i >> 3][i & 7] = to_elem<T>(float(pf[i >> 3][i & 7]) * (t[i] - x[i]));
+    for (int i = 0; i < 16; ++i) xf[i >> 3][i & 7] = to_elem<T>(PHandoff<T>::times(pf[i >> 3], i & 7, t[i]));
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * RB), xf[hh]);
+        M::mma(acc[db], tc.tr(db, jp * TILE + 16 * hh * RB), xf[hh]);
     sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
+    __builtin_amdgcn_sched_barrier(0);
+    // -delta of `step` (in LDS since this iteration's barrier; its slot is
+    // refilled only kRing - kAhead steps later)
+    row_stats(j * STATS, xd);
   };
 
   // iteration `step` in slot J = step % kRing
@@ -420,14 +464,14 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
       of[ks] = load_frag<T>(static_cast<const T*>(a.dout) + off + ks * 16);
     }
   }
-  const float lse2 = a.delta[(size_t)a.Hq * a.T + (size_t)h * a.T + qtok];
-  const float dlt = a.delta[(size_t)h * a.T + qtok];
+  const float nlse2 = a.delta[(size_t)a.Hq * a.T + (size_t)h * a.T + qtok];
+  const float ndlt = a.delta[(size_t)h * a.T + qtok];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     settle(qf[ks]);
     settle(of[ks]);
   }
-  asm volatile("" ::"v"(lse2), "v"(dlt));
+  asm volatile("" ::"v"(nlse2), "v"(ndlt));
 
   f32x16 dq[DB];
 #pragma unroll
@@ -461,7 +505,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
       sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
       float p[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, nlse2));
       if (need_mask) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
@@ -469,7 +513,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
       }
       frag dsf[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dsf[i >> 3][i & 7] = to_elem<T>(p[i] * (dp[i] - dlt));
+      for (int i = 0; i < 16; ++i) dsf[i >> 3][i & 7] = to_elem<T>(p[i] * (dp[i] + ndlt));
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
