@@ -171,9 +171,9 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* out, 
 /*
  * The three stages tree_attn_bwd runs, in this order, on one stream; each can
  * be called on its own (for example to time it).  They share the workspace:
- *   tree_attn_bwd_rowstat  delta[h,i] = sum_d dout[i,h,d] * out[i,h,d] and
- *                          lse[h,i] * log2(e) into the workspace (two float32
- *                          [Hq, T] arrays);
+ *   tree_attn_bwd_rowstat  -delta[h,i] = -sum_d dout[i,h,d] * out[i,h,d] and
+ *                          -lse[h,i] * log2(e) into the workspace (two float32
+ *                          [Hq, T] arrays, stored negated);
  *   tree_attn_bwd_dkdv     dk, dv: for each key, the contributions of every
  *                          query that sees it, i.e. of every branch below a
  *                          shared prefix (draft "feat(hybrid): add opt-in
