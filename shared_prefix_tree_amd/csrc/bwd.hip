@@ -472,6 +472,9 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
     settle(of[ks]);
   }
   asm volatile("" ::"v"(nlse2), "v"(ndlt));
+  f32x16 ndlt16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndlt16[i] = ndlt;
 
   f32x16 dq[DB];
 #pragma unroll
@@ -496,7 +499,9 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
     const bool need_mask = v0 + BN - 1 > wave_pos0;  // wave-uniform
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // dP - delta: the products accumulate onto -delta (this lane's
+      // query is the same in all 16 entries)
+      f32x16 s = f32x16{}, dp = ndlt16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         M::mma(s, ka.row(ks, off + kb * 32 * RB), qf[ks]);
@@ -513,7 +518,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
       }
       frag dsf[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dsf[i >> 3][i & 7] = to_elem<T>(p[i] * (dp[i] + ndlt));
+      for (int i = 0; i < 16; ++i) dsf[i >> 3][i & 7] = to_elem<T>(p[i] * dp[i]);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
