@@ -403,6 +403,7 @@ struct PathCopier {
   int row;             // this lane's row of copy 0 (copy r: row + RPC r)
   const Span* spans;   // the segment's spans, in LDS
   int ucur, lcur;      // wave-uniform and per-lane span cursors
+  int cphys, clen, cvirt;  // spans[ucur], kept in registers
   int kv_len;          // positions on the path
 
   __device__ PathCopier(const T* k, const T* v, int g, int Hkv, unsigned k_ring, unsigned v_ring, const Span* sp,
@@ -418,16 +419,25 @@ struct PathCopier {
     ucur = 0;
     lcur = 0;
     kv_len = len;
+    cphys = __builtin_amdgcn_readfirstlane(sp[0].phys);
+    clen = __builtin_amdgcn_readfirstlane(sp[0].len);
+    cvirt = __builtin_amdgcn_readfirstlane(sp[0].virt);
   }
 
   // positions [v0, v0 + 64) into the ring slot at byte offset `slot`
   __device__ inline void issue(int v0, unsigned slot) {
-    while (v0 >= spans[ucur].virt + spans[ucur].len) ++ucur;
-    const Span sp = spans[ucur];
+    // the current span stays in registers: a step inside it (the common
+    // case) reads no LDS, so the copies are not held up behind LDS traffic
+    while (v0 >= cvirt + clen) {
+      ++ucur;
+      cphys = __builtin_amdgcn_readfirstlane(spans[ucur].phys);
+      clen = __builtin_amdgcn_readfirstlane(spans[ucur].len);
+      cvirt = __builtin_amdgcn_readfirstlane(spans[ucur].virt);
+    }
     int phys[NC];
-    if (v0 + 64 <= sp.virt + sp.len && v0 + 64 <= kv_len) {
+    if (v0 + 64 <= cvirt + clen && v0 + 64 <= kv_len) {
 #pragma unroll
-      for (int r = 0; r < NC; ++r) phys[r] = sp.phys + (v0 - sp.virt) + row + RPC * r;
+      for (int r = 0; r < NC; ++r) phys[r] = cphys + (v0 - cvirt) + row + RPC * r;
     } else {
 #pragma unroll
       for (int r = 0; r < NC; ++r) {
