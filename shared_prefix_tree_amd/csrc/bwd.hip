@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
 // So S is formed once per step and each SIMD issues the minimum 32 matrix
 // products per step.  Q / dO tiles and their lse2 / delta go through rings
 // of kRing LDS slots, copied kRing - 2 steps ahead of the dV waves (the dK
-// waves hold one more) by the dV waves alone; each of them issues the same
+// waves hold one more) by the dK waves alone; each of them issues the same
 // number of copies per step, so the wait for a step's tiles is a fixed
 // count.  One barrier per step orders copies, P hand-off and slot reuse.
 
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   constexpr int STATS = 2 * BM * 4;               // lse2, delta of one step
   constexpr int NC = path_copies(RB);             // copies per 16 rows
   constexpr int RPC = 1024 / RB;                  // rows per copy
-  constexpr int kCopiesK = 2 * NC + 1;            // copies per dV wave per step
+  constexpr int kCopiesK = 2 * NC + 1;            // copies per dK wave per step
   constexpr int PBLK = 2 * 64;                    // P fragments per wave block
   static_assert(RB == 128 || RB == 256, "128- or 256-byte rows");
   static_assert(4 * DB * 16 * 64 * 4 <= 2 * kRing * TILE, "the partials fit the rings");
@@ -182,17 +182,17 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 
   const unsigned q_ring = lds_addr(ring), o_ring = q_ring + kRing * TILE, s_ring = q_ring + 2 * kRing * TILE;
 
-  // Copy plan: only the dV waves copy (the dK waves carry the longer vector
-  // work, dS and the P conversions, which measured slower with the copies
-  // beside it).  dV wave w copies rows 16 w .. +16 of the Q tile and of the
-  // dO tile (NC instructions of 1 KB each) and one 64-float stat vector
-  // (waves 0 and 1 the real lse2 / delta, waves 2 and 3 a discarded
+  // Copy plan: only the dK waves copy (their vector work, dS with one mixed
+  // fma per element, is the lighter: the dV waves carry the exponentials).
+  // dK wave w copies rows 16 (w - 4) .. +16 of the Q tile and of the dO
+  // tile (NC instructions of 1 KB each) and one 64-float stat vector
+  // (waves 4 and 5 the real lse2 / delta, waves 6 and 7 a discarded
   // duplicate): kCopiesK copies per step.  Per lane: row crow0 + RPC r +
   // lane / (RB / 16) and its swizzled 16-byte chunk.
   const int crow0 = wblk * 16;
-  const float* ssrc = wave == 1 ? a.delta : lse2;
-  const unsigned s_lds = wave == 0 || wave == 1 ? s_ring + wave * BM * 4 : lds_addr(junk);
-  const unsigned s_step = wave == 0 || wave == 1 ? STATS : 0;
+  const float* ssrc = wave == 5 ? a.delta : lse2;
+  const unsigned s_lds = wave == 4 || wave == 5 ? s_ring + (wave - 4) * BM * 4 : lds_addr(junk);
+  const unsigned s_step = wave == 4 || wave == 5 ? STATS : 0;
   const int crow = crow0 + lane / (RB / 16);
   unsigned cchunk[NC];
 #pragma unroll
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   // Step `step` goes to slot step % kRing.  The copy stream advances one
   // step per call: (cp_h, cp_i0) is the head and first query of the next
   // step to copy, kept incrementally (no division); past the end it stays
-  // on the last step, re-copying its rows into the (idle) slot, so a dV wave
+  // on the last step, re-copying its rows into the (idle) slot, so a dK wave
   // always issues kCopiesK copies.  Rows past the range read the last row
   // (masked to P = 0).  Each copy reads from a wave-uniform row base plus a
   // small per-lane offset.
@@ -330,16 +330,16 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 
   // iteration `step` in slot J = step % kRing
   auto body = [&](auto R, int step, auto J) {
-    // a dV wave's copies of `step` are done once only the kAhead - 1 newer
-    // steps' copies may be in flight; after the barrier every dV wave's are,
+    // a dK wave's copies of `step` are done once only the kAhead - 1 newer
+    // steps' copies may be in flight; after the barrier every dK wave's are,
     // the P of step - 1 is in LDS, and nobody reads the slot refilled next
     // (last read at step - 2)
     if constexpr (decltype(R)::value) {
-      wait_copies_barrier<0>();
-      dk_iter(step, J);
-    } else {
       wait_copies_barrier<(kAhead - 1) * kCopiesK>();
       issue((decltype(J)::value + kAhead) % kRing);
+      dk_iter(step, J);
+    } else {
+      wait_copies_barrier<0>();
       dv_iter(step, J);
     }
   };
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     for (int e = 0; e < 8; ++e) pprev[0][e] = pprev[1][e] = to_elem<T>(0.f);
   }
   __syncthreads();
-  if (!dk_role) {
+  if (dk_role) {
 #pragma unroll
     for (int st = 0; st < kAhead; ++st) issue(st);
   }
