@@ -151,8 +151,8 @@ int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t 
                   const tree_attn_shape* shape, void* out, float* lse, void* stream);
 
 /* Bytes of device workspace tree_attn_bwd needs for this plan and shape
- * (two float32 [Hq, T] row-statistic arrays, 256-byte aligned); 0 on
- * invalid input. */
+ * (two float32 [Hq, T] row-statistic arrays, 256-byte aligned, then 128
+ * bytes of work-item counters); 0 on invalid input. */
 size_t tree_attn_bwd_workspace_bytes(tree_attn_plan_t plan, const tree_attn_shape* shape);
 
 /*
@@ -160,7 +160,8 @@ size_t tree_attn_bwd_workspace_bytes(tree_attn_plan_t plan, const tree_attn_shap
  * outputs dq [T, Hq, D], dk, dv [T, Hkv, D] (same dtype as q), overwritten
  * (not accumulated into).  workspace: caller-owned device memory of at least
  * tree_attn_bwd_workspace_bytes().  Every output element is produced by one
- * workgroup in a fixed order with no atomics, so results are bitwise
+ * workgroup in a fixed order, with no atomic accumulation (atomic counters
+ * only decide which workgroup takes which tile), so results are bitwise
  * reproducible run to run.  Asynchronous on `stream`.
  * Errors: as tree_attn_fwd, plus INVALID_ARGUMENT for a small workspace.
  */
@@ -173,7 +174,10 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* out, 
  * be called on its own (for example to time it).  They share the workspace:
  *   tree_attn_bwd_rowstat  -delta[h,i] = -sum_d dout[i,h,d] * out[i,h,d] and
  *                          -lse[h,i] * log2(e) into the workspace (two float32
- *                          [Hq, T] arrays, stored negated);
+ *                          [Hq, T] arrays, stored negated), and zeroes its
+ *                          work-item counters (the other two stages leave
+ *                          them zeroed when they finish, so they may be
+ *                          repeated; a new workspace needs this stage first);
  *   tree_attn_bwd_dkdv     dk, dv: for each key, the contributions of every
  *                          query that sees it, i.e. of every branch below a
  *                          shared prefix (draft "feat(hybrid): add opt-in

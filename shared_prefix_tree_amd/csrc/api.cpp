@@ -47,6 +47,7 @@ struct DevicePlan {
   Span* spans = nullptr;
   QTile* qtiles[kNumQTileSizes] = {};
   KTile* ktiles = nullptr;
+  KTile* ktiles_wide = nullptr;
 };
 
 }  // namespace tree_attn
@@ -81,13 +82,14 @@ hipError_t upload_plan(const HostPlan& h, DevicePlan& d) {
     size_t bytes;
     void** dst;
   };
-  Part parts[3 + kNumQTileSizes] = {
+  Part parts[4 + kNumQTileSizes] = {
       {h.span_ptr.data(), h.span_ptr.size() * sizeof(int32_t), reinterpret_cast<void**>(&d.span_ptr)},
       {h.spans.data(), h.spans.size() * sizeof(Span), reinterpret_cast<void**>(&d.spans)},
       {h.ktiles.data(), h.ktiles.size() * sizeof(KTile), reinterpret_cast<void**>(&d.ktiles)},
+      {h.ktiles_wide.data(), h.ktiles_wide.size() * sizeof(KTile), reinterpret_cast<void**>(&d.ktiles_wide)},
   };
   for (int t = 0; t < kNumQTileSizes; ++t)
-    parts[3 + t] = {h.qtiles[t].data(), h.qtiles[t].size() * sizeof(QTile), reinterpret_cast<void**>(&d.qtiles[t])};
+    parts[4 + t] = {h.qtiles[t].data(), h.qtiles[t].size() * sizeof(QTile), reinterpret_cast<void**>(&d.qtiles[t])};
   size_t total = 0;
   for (const Part& p : parts) total += align16(p.bytes);
   std::vector<unsigned char> stage(total, 0);
@@ -184,7 +186,7 @@ int check_call(const char* fn, tree_attn_plan_t plan, const tree_attn_shape* sha
   int64_t grid_q = 0;
   for (int tq : {fwd_query_tile(hg), dq_query_tile(hg)})
     grid_q = std::max(grid_q, int64_t(plan->host.qtiles[qtile_index(tq)].size()) * (shape->num_q_heads / hg));
-  const int64_t grid_k = int64_t(plan->host.ktiles.size()) * shape->num_kv_heads;
+  const int64_t grid_k = int64_t(plan->host.ktiles.size()) * shape->num_kv_heads;  // >= the wide list's
   if (grid_q >= (int64_t(1) << 31) || grid_k >= (int64_t(1) << 31))
     return fail(TREE_ATTN_UNSUPPORTED, f + ": launch grid too large");
   float s = shape->softmax_scale;
@@ -319,10 +321,16 @@ int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t 
   return TREE_ATTN_OK;
 }
 
-size_t tree_attn_bwd_workspace_bytes(tree_attn_plan_t plan, const tree_attn_shape* shape) {
-  if (!plan || !shape || shape->total_tokens < 1 || shape->num_q_heads < 1) return 0;
+// workspace: -delta and -lse2 ([Hq, T] float32 each), then the work-item
+// counters of the dK/dV and dQ passes
+static size_t stats_bytes(const tree_attn_shape* shape) {
   const size_t bytes = 2 * size_t(shape->num_q_heads) * size_t(shape->total_tokens) * sizeof(float);
   return (bytes + 255) & ~size_t(255);
+}
+
+size_t tree_attn_bwd_workspace_bytes(tree_attn_plan_t plan, const tree_attn_shape* shape) {
+  if (!plan || !shape || shape->total_tokens < 1 || shape->num_q_heads < 1) return 0;
+  return stats_bytes(shape) + 2 * sizeof(ItemCounters);
 }
 
 }  // extern "C"
@@ -363,12 +371,16 @@ int prep_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   a.dk = dk;
   a.dv = dv;
   a.delta = static_cast<float*>(workspace);
+  a.counters = reinterpret_cast<ItemCounters*>(static_cast<char*>(workspace) + stats_bytes(shape));
   a.qtiles = plan->dev.qtiles[ti];
-  a.ktiles = plan->dev.ktiles;
+  // bf16 walks 128-key tiles, fp32 64-key tiles (its P hand-off is twice
+  // as large, so wider tiles would not fit LDS)
+  const bool wide = shape->dtype == TREE_ATTN_BF16;
+  a.ktiles = wide ? plan->dev.ktiles_wide : plan->dev.ktiles;
   a.span_ptr = plan->dev.span_ptr;
   a.spans = plan->dev.spans;
   a.n_qtiles = int32_t(plan->host.qtiles[ti].size());
-  a.n_ktiles = int32_t(plan->host.ktiles.size());
+  a.n_ktiles = int32_t(wide ? plan->host.ktiles_wide.size() : plan->host.ktiles.size());
   a.T = shape->total_tokens;
   a.Hq = shape->num_q_heads;
   a.Hkv = shape->num_kv_heads;

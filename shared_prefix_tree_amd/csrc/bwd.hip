@@ -41,7 +41,13 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
                                                                 const T* __restrict__ dout,
                                                                 const float* __restrict__ lse,
                                                                 float* __restrict__ ndelta,
-                                                                float* __restrict__ nlse2, int T_, int Hq) {
+                                                                float* __restrict__ nlse2,
+                                                                ItemCounters* __restrict__ counters, int T_,
+                                                                int Hq) {
+  // the later stages hand out their work items through these counters
+  if (blockIdx.x == 0 && threadIdx.x < 2 * int(sizeof(ItemCounters) / 4))
+    __hip_atomic_store(reinterpret_cast<unsigned*>(counters) + threadIdx.x, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   constexpr int E = Chunk<T>::E;
   constexpr int CPR = D / E;
   constexpr int RPB = 256 / CPR;
@@ -124,7 +130,7 @@ struct DkdvRing {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_item(const BwdArgs& a, int item) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   using quad = typename M::quad;
@@ -150,10 +156,14 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float junk[64];
 
   int tile_rank, g;
-  decode_item(blockIdx.x, a.Hkv, tile_rank, g);
+  decode_item(item, a.Hkv, tile_rank, g);
   const KTile tile = a.ktiles[tile_rank];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  // (opaque per item, so nothing derived from the thread index is hoisted
+  // out of the item loop to stay live across items)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 31, half = lane >> 5;
   const bool dk_role = wave >= 4;
@@ -413,13 +423,318 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// one workgroup per CU, taking items until none is left
+template <typename T, int D>
+__global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
+  __shared__ int s_item;
+  const int n_items = a.n_ktiles * a.Hkv;
+  for (int item; (item = take_item(&a.counters[0], n_items, &s_item)) >= 0;) dkdv_item<T, D>(a, item);
+  finish_block(&a.counters[0]);
+}
+
+// ---------------------------------------------------------------------------
+// 2b. dK / dV over 128-key tiles (bf16)
+//
+// The 64-key walk above pays a fixed cost per step -- the Q / dO copies, the
+// barrier -- for 32 matrix products per SIMD.  Here a workgroup owns 128
+// keys and every wavefront takes both 32-query halves of a step, so the same
+// 64-query tiles feed twice the products: wavefront w owns keys
+// 32 (w mod 4) .. +32 of the tile in its role (dV: waves 0-3, dK: waves
+// 4-7, the same per-role work as above) and accumulates both halves itself,
+// which also removes the cross-wave reduction at the end.  A step is 64
+// products per SIMD, twice as long, so the rings copy one step ahead in
+// three slots (about the same lead time as two steps of the 64-key walk) and
+// the P hand-off, twice as large, still fits LDS next to them.
+template <typename T, int D>
+__device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, int item) {
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  using quad = typename M::quad;
+  constexpr int kRing = 3;
+  constexpr int kAhead = 1;                       // steps copied ahead
+  constexpr int BM = 64;                          // queries per step
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int RB = D * int(sizeof(T));          // bytes of one head's row
+  constexpr int TILE = BM * RB;                   // bytes of one 64-row tile
+  constexpr int STATS = 2 * BM * 4;               // -lse2, -delta of one step
+  constexpr int NC = path_copies(RB);             // copies per 16 rows
+  constexpr int RPC = 1024 / RB;                  // rows per copy
+  constexpr int kCopiesK = 2 * NC + 1;            // copies per dK wave per step
+  constexpr int PBLK = 2 * 64;                    // P fragments of one 32 x 32 block
+  static_assert(sizeof(T) == 2, "16-bit inputs: the fp32 P hand-off would not fit LDS");
+  static_assert(RB == 128 || RB == 256, "128- or 256-byte rows");
+
+  // Q ring, then dO ring, then the -lse2 / -delta ring
+  __shared__ __attribute__((aligned(16))) char ring[2 * kRing * TILE + kRing * STATS];
+  __shared__ __attribute__((aligned(16))) frag pshare[2][8 * PBLK];
+  __shared__ __attribute__((aligned(16))) float junk[64];
+
+  int tile_rank, g;
+  decode_item(item, a.Hkv, tile_rank, g);
+  const KTile tile = a.ktiles[tile_rank];
+
+  // (opaque per item, so nothing derived from the thread index is hoisted
+  // out of the item loop to stay live across items)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int col = lane & 31, half = lane >> 5;
+  const bool dk_role = wave >= 4;
+  const int kq = wave & 3;
+  const int kl = kq * 32 + col;
+  const bool key_valid = kl < tile.nk;
+  const int ktok = tile.k0 + min(kl, tile.nk - 1);
+  const int jkey = tile.k0 + kl;
+  const float c = a.scale * kLog2e;
+  const float* nlse2 = a.delta + (size_t)a.Hq * a.T;
+
+  // the dV waves keep K, the dK waves V (both as B fragments)
+  frag kv[KS];
+  {
+    const T* src = static_cast<const T*>(dk_role ? a.v : a.k) + ((size_t)ktok * a.Hkv + g) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kv[ks] = load_frag<T>(src + ks * 16);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) settle(kv[ks]);
+
+  const int nblk = (tile.qend - tile.k0 + BM - 1) / BM;
+  const int n_steps = a.G * nblk;
+  const int last = tile.qend - 1;
+
+  const unsigned q_ring = lds_addr(ring), o_ring = q_ring + kRing * TILE, s_ring = q_ring + 2 * kRing * TILE;
+
+  // Copies as in the 64-key walk: dK wave w copies rows 16 (w - 4) .. +16 of
+  // the Q and dO tiles and one 64-float stat vector (waves 4 and 5 the real
+  // -lse2 / -delta, waves 6 and 7 a discarded duplicate).
+  const int crow0 = kq * 16;
+  const float* ssrc = wave == 5 ? a.delta : nlse2;
+  const unsigned s_lds = wave == 4 || wave == 5 ? s_ring + (wave - 4) * BM * 4 : lds_addr(junk);
+  const unsigned s_step = wave == 4 || wave == 5 ? STATS : 0;
+  const int crow = crow0 + lane / (RB / 16);
+  unsigned cchunk[NC];
+#pragma unroll
+  for (int r = 0; r < NC; ++r) cchunk[r] = (((lane % (RB / 16)) ^ swz<RB>(crow + RPC * r)) * 16);
+  const unsigned row_bytes = (unsigned)a.Hq * RB;
+  int cp_step = 0, cp_h = g * a.G, cp_i0 = tile.k0;
+  auto issue = [&](int slot) {
+    const int lim = last - cp_i0;
+    const size_t row0 = ((size_t)cp_i0 * a.Hq + cp_h) * D;
+#pragma unroll
+    for (int r = 0; r < NC; ++r) {
+      const unsigned voff = (unsigned)min(crow + RPC * r, lim) * row_bytes + cchunk[r];
+      const unsigned lofs = crow0 * RB + (unsigned)slot * TILE + RPC * r * RB;
+      copy16_async(static_cast<const T*>(a.q) + row0, voff, q_ring + lofs);
+      copy16_async(static_cast<const T*>(a.dout) + row0, voff, o_ring + lofs);
+    }
+    copy4_async(ssrc + (size_t)cp_h * a.T + cp_i0, (unsigned)min(lane, lim) * 4u, s_lds + (unsigned)slot * s_step);
+    if (++cp_step < n_steps) {
+      cp_i0 += BM;
+      if (cp_i0 > last) {
+        cp_i0 = tile.k0;
+        ++cp_h;
+      }
+    }
+  };
+
+  // per-lane read addresses in slot 0 (the query half is a constant offset)
+  TileAddr<T, D> ta, tc;
+  ta.init(dk_role ? o_ring : q_ring, lane);
+  tc.init(dk_role ? q_ring : o_ring, lane);
+  unsigned stat_addr = s_ring + (dk_role ? BM * 4 : 0) + 4 * half * 4;
+  asm volatile("" : "+v"(stat_addr));
+  auto row_stats = [&](int off, float (&x)[16]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 v4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+          (size_t)(stat_addr + off + 32 * j));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * j + e] = v4[e];
+    }
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  // The per-role work of the 64-key walk, for both query halves qh:
+  //   dV waves: dV^T += dO^T P of step - 1, then S and P of `step`;
+  //   dK waves: dP - delta, dS, dK^T += Q^T dS of step - 1.
+  frag pprev[2][2];
+  int dv_i0 = tile.k0;  // first query of the dV waves' current step
+  auto dv_iter = [&](int step, auto J) {
+    constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * RB), pprev[qh][hh]);
+    f32x16 t[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) M::mma(t[qh], ta.row(ks, j * TILE + qh * 32 * RB), kv[ks]);
+    sched_pipeline<kLdsAhead, 4 * DB + 2 * KS, frag_reads<T>(true)>();
+    const int i0 = dv_i0;
+    dv_i0 = dv_i0 + BM > last ? tile.k0 : dv_i0 + BM;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      float x[16];
+      row_stats(j * STATS + qh * 32 * 4, x);
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(t[qh][i], c, x[i]));
+      if (__builtin_amdgcn_readfirstlane(int(i0 + qh * 32 < tile.k0 + kq * 32 + 31 ||
+                                             i0 + qh * 32 + 31 >= tile.qend))) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qi = i0 + qh * 32 + c_row(i, half);
+          if (qi < jkey || qi >= tile.qend) p[i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pprev[qh][i >> 3][i & 7] = to_elem<T>(p[i]);
+      frag* pshr = &pshare[step & 1][(kq * 2 + qh) * PBLK];
+      pshr[lane] = PHandoff<T>::pack(pprev[qh][0], p);
+      pshr[64 + lane] = PHandoff<T>::pack(pprev[qh][1], p + 8);
+    }
+  };
+  float xd[2][16];  // -delta of the dK waves' next step (read one iteration early)
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xd[qh][i] = 0.f;
+  auto dk_iter = [&](int step, auto J) {
+    constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
+    frag pf[2][2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const frag* pshr = &pshare[(step + 1) & 1][(kq * 2 + qh) * PBLK];
+      pf[qh][0] = pshr[lane];
+      pf[qh][1] = pshr[64 + lane];
+    }
+    // (the P reads go ahead of the software-pipelined fragment reads)
+    __builtin_amdgcn_sched_barrier(0);
+    // dP - delta: the products accumulate onto -delta
+    f32x16 t[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t[qh][i] = xd[qh][i];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) M::mma(t[qh], ta.row(ks, jp * TILE + qh * 32 * RB), kv[ks]);
+    sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
+    frag xf[2][2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        xf[qh][i >> 3][i & 7] = to_elem<T>(PHandoff<T>::times(pf[qh][i >> 3], i & 7, t[qh][i]));
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * RB), xf[qh][hh]);
+    sched_pipeline<kLdsAhead, 4 * DB, frag_reads<T>(true)>();
+    __builtin_amdgcn_sched_barrier(0);
+    // -delta of `step` (in LDS since this iteration's barrier; its slot is
+    // refilled only kRing - kAhead steps later)
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) row_stats(j * STATS + qh * 32 * 4, xd[qh]);
+  };
+
+  // iteration `step` in slot J = step % kRing; at its barrier every dK
+  // wave's copies of `step` are in LDS, the P of step - 1 is in LDS, and
+  // nobody reads the slot refilled next (last read at step - 2)
+  auto body = [&](auto R, int step, auto J) {
+    if constexpr (decltype(R)::value) {
+      wait_copies_barrier<(kAhead - 1) * kCopiesK>();
+      issue((decltype(J)::value + kAhead) % kRing);
+      dk_iter(step, J);
+    } else {
+      wait_copies_barrier<0>();
+      dv_iter(step, J);
+    }
+  };
+  auto round = [&](auto self, auto R, int step, auto J) -> bool {
+    constexpr int j = decltype(J)::value;
+    body(R, step + j, J);
+    if (step + j >= n_steps) return true;
+    if constexpr (j + 1 < kRing) {
+      return self(self, R, step, Slot<j + 1>{});
+    } else {
+      return false;
+    }
+  };
+  auto walk = [&](auto R) {
+    for (int step = 0;; step += kRing)
+      if (round(round, R, step, Slot<0>{})) break;
+  };
+
+  // zero the slot and P buffer that iteration 0 reads, then start copying
+  {
+    float* z0 = reinterpret_cast<float*>(ring + (kRing - 1) * TILE);              // Q tile
+    float* z1 = reinterpret_cast<float*>(ring + (2 * kRing - 1) * TILE);          // dO tile
+    for (int i = tid; i < TILE / 4; i += 512) z0[i] = z1[i] = 0.f;
+    float* z2 = reinterpret_cast<float*>(ring + 2 * kRing * TILE + (kRing - 1) * STATS);
+    if (tid < STATS / 4) z2[tid] = 0.f;
+    float* z3 = reinterpret_cast<float*>(&pshare[1][0]);
+    for (int i = tid; i < int(sizeof(pshare[1]) / 4); i += 512) z3[i] = 0.f;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pprev[qh][0][e] = pprev[qh][1][e] = to_elem<T>(0.f);
+  }
+  __syncthreads();
+  if (dk_role) {
+#pragma unroll
+    for (int st = 0; st < kAhead; ++st) issue(st);
+  }
+  if (dk_role)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
+  wait_copies_barrier<0>();  // no copy in flight when the workgroup ends
+
+  if (key_valid) {
+    T* op = static_cast<T*>(dk_role ? a.dk : a.dv) + ((size_t)jkey * a.Hkv + g) * D;
+    const float mul = dk_role ? a.scale : 1.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        quad t4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t4[e] = to_elem<T>(acc[db][grp * 4 + e] * mul);
+        *reinterpret_cast<quad*>(op + db * 32 + grp * 8 + half * 4) = t4;
+      }
+  }
+}
+
+// one workgroup per CU, taking items until none is left
+template <typename T, int D>
+__global__ __launch_bounds__(512, 1) void tree_attn_dkdv_wide_kernel(BwdArgs a) {
+  __shared__ int s_item;
+  const int n_items = a.n_ktiles * a.Hkv;
+  for (int item; (item = take_item(&a.counters[0], n_items, &s_item)) >= 0;) dkdv_wide_item<T, D>(a, item);
+  finish_block(&a.counters[0]);
+}
+
 // ---------------------------------------------------------------------------
 // 3. dQ, query-major (same walk as the forward kernel)
 
 constexpr int kDqRing = 4;
 
 template <typename T, int D, int HG>
-__global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq_item(const BwdArgs& a, int item) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   using quad = typename M::quad;
@@ -438,10 +753,14 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
   __shared__ Span sSpans[kMaxSpans];
 
   int tile_rank, group;
-  decode_item(blockIdx.x, a.Hq / HG, tile_rank, group);
+  decode_item(item, a.Hq / HG, tile_rank, group);
   const QTile tile = a.qtiles[tile_rank];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  // (opaque per item, so nothing derived from the thread index is hoisted
+  // out of the item loop to stay live across items)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 31, half = lane >> 5;
   const int ts = wave / HG;
@@ -565,8 +884,32 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
   }
 }
 
+// one workgroup per CU, taking items until none is left
+template <typename T, int D, int HG>
+__global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
+  __shared__ int s_item;
+  const int n_items = a.n_qtiles * (a.Hq / HG);
+  for (int item; (item = take_item(&a.counters[1], n_items, &s_item)) >= 0;) dq_item<T, D, HG>(a, item);
+  finish_block(&a.counters[1]);
+}
+
 // ---------------------------------------------------------------------------
 // launchers (one per stage; tree_attn_bwd runs all three in order)
+
+// one 512-thread workgroup fits a CU (LDS), so the item-taking kernels run
+// as many workgroups as the device has CUs (fewer for fewer items)
+static unsigned persistent_grid(unsigned n_items) {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return n_items;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return n_items;
+    cus[dev] = n;
+  }
+  return n_items < unsigned(cus[dev]) ? n_items : unsigned(cus[dev]);
+}
 
 template <typename T, int D>
 hipError_t launch_bwd_rowstat(const BwdArgs& a, hipStream_t stream) {
@@ -575,21 +918,26 @@ hipError_t launch_bwd_rowstat(const BwdArgs& a, hipStream_t stream) {
   const unsigned rows = (unsigned)a.T * (unsigned)a.Hq;
   hipLaunchKernelGGL((tree_attn_rowstat_kernel<T, D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, stream,
                      static_cast<const T*>(a.out), static_cast<const T*>(a.dout), a.lse, a.delta,
-                     a.delta + (size_t)a.Hq * a.T, a.T, a.Hq);
+                     a.delta + (size_t)a.Hq * a.T, a.counters, a.T, a.Hq);
   return hipGetLastError();
 }
 
+// a.ktiles holds 128-key tiles for 16-bit inputs, 64-key tiles for fp32
 template <typename T, int D>
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((tree_attn_dkdv_kernel<T, D>), dim3((unsigned)a.n_ktiles * (unsigned)a.Hkv), dim3(512), 0,
-                     stream, a);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((tree_attn_dkdv_wide_kernel<T, D>), dim3(persistent_grid((unsigned)a.n_ktiles * (unsigned)a.Hkv)),
+                       dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((tree_attn_dkdv_kernel<T, D>), dim3(persistent_grid((unsigned)a.n_ktiles * (unsigned)a.Hkv)),
+                       dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
 template <typename T, int D, int HG>
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((tree_attn_dq_kernel<T, D, HG>), dim3((unsigned)a.n_qtiles * (unsigned)(a.Hq / HG)),
-                     dim3(512), 0, stream, a);
+  hipLaunchKernelGGL((tree_attn_dq_kernel<T, D, HG>),
+                     dim3(persistent_grid((unsigned)a.n_qtiles * (unsigned)(a.Hq / HG))), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -365,6 +365,53 @@ __device__ inline void decode_item(int b, int n_groups, int& tile_rank, int& gro
   }
 }
 
+// Dynamic hand-out of work items across the XCDs.  Under these kernels the
+// eight XCDs of one GPU run at clocks up to ~5 % apart, so a split of the
+// items by block index alone leaves the slowest XCD finishing last.  Here the
+// grid is one workgroup per CU, and each workgroup takes items until none is
+// left: first from the ticket counter of the XCD it runs on -- that XCD's
+// share of the static split (items b with b % 8 == xcd, in order: longest
+// first, with XCD-local head groups) -- and once that list is exhausted,
+// from the other XCDs' lists (their remaining, shortest items).  A pass over
+// the eight lists that finds nothing means every item has been taken (the
+// lists only shrink).  The last workgroup to finish zeroes the counters for
+// the next launch (the first launch on a new workspace relies on the
+// row-statistics stage having zeroed them).
+struct ItemCounters {
+  unsigned next[8];
+  unsigned done;
+  unsigned pad[7];
+};
+
+// the next item for this workgroup, or -1 when none is left (ends with a
+// barrier: the previous item is finished by every wave)
+__device__ inline int take_item(ItemCounters* ctr, int n_items, int* s_item) {
+  if (threadIdx.x == 0) {
+    unsigned xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    int item = -1;
+    for (unsigned k = 0; k < 8; ++k) {
+      const unsigned x = (xcc + k) & 7u;
+      const unsigned t = atomicAdd(&ctr->next[x], 1u);
+      if ((long long)t * 8 + x < n_items) {
+        item = int(t * 8 + x);
+        break;
+      }
+    }
+    *s_item = item;
+  }
+  __syncthreads();
+  return *s_item;
+}
+
+__device__ inline void finish_block(ItemCounters* ctr) {
+  if (threadIdx.x == 0 && atomicAdd(&ctr->done, 1u) == gridDim.x - 1) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) __hip_atomic_store(&ctr->next[x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ctr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // A segment's merged spans are staged in LDS once per workgroup, so span
 // lookups use the LDS counter and never wait behind in-flight global->LDS
 // copies.  A segment may have at most kMaxSpans spans (checked by the host).
@@ -477,6 +524,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;
+  ItemCounters* counters;  // [0]: dK/dV pass, [1]: dQ pass (in the workspace)
   const QTile* qtiles;
   const KTile* ktiles;
   const int32_t* span_ptr;

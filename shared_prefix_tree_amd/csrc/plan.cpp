@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <numeric>
+#include <utility>
 
 namespace tree_attn {
 
@@ -127,13 +128,15 @@ bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int3
       return int64_t(a.pos0) + a.nq > int64_t(b.pos0) + b.nq;
     });
   }
-  // key tiles, most queries first
-  p.ktiles.clear();
-  for (int32_t s = 0; s < S; ++s)
-    for (int32_t o = 0; o < seg_len[s]; o += kKTile)
-      p.ktiles.push_back(KTile{seg_start[s] + o, std::min(kKTile, seg_len[s] - o), s, p.end[s]});
-  std::stable_sort(p.ktiles.begin(), p.ktiles.end(),
-                   [](const KTile& a, const KTile& b) { return a.qend - a.k0 > b.qend - b.k0; });
+  // key tiles per size, most queries first (stable on ties)
+  for (auto [tiles, tk] : {std::pair<std::vector<KTile>*, int>{&p.ktiles, kKTile}, {&p.ktiles_wide, kKTileWide}}) {
+    tiles->clear();
+    for (int32_t s = 0; s < S; ++s)
+      for (int32_t o = 0; o < seg_len[s]; o += tk)
+        tiles->push_back(KTile{seg_start[s] + o, std::min(tk, seg_len[s] - o), s, p.end[s]});
+    std::stable_sort(tiles->begin(), tiles->end(),
+                     [](const KTile& a, const KTile& b) { return a.qend - a.k0 > b.qend - b.k0; });
+  }
   return true;
 }
 

@@ -48,7 +48,8 @@ struct Span {
 
 constexpr int kNumQTileSizes = 4;
 constexpr int kQTileSizes[kNumQTileSizes] = {32, 64, 128, 256};
-constexpr int kKTile = 64;
+constexpr int kKTile = 64;       // key tiles of the fp32 dK/dV pass
+constexpr int kKTileWide = 128;  // key tiles of the bf16 dK/dV pass
 
 inline int qtile_index(int tq) { return tq == 32 ? 0 : tq == 64 ? 1 : tq == 128 ? 2 : tq == 256 ? 3 : -1; }
 
@@ -59,7 +60,8 @@ struct HostPlan {
   std::vector<int32_t> span_ptr;
   std::vector<Span> spans;
   std::vector<QTile> qtiles[kNumQTileSizes];
-  std::vector<KTile> ktiles;
+  std::vector<KTile> ktiles;       // kKTile keys
+  std::vector<KTile> ktiles_wide;  // kKTileWide keys
 };
 
 // Validates the topology and fills `plan`; on failure returns false and

@@ -166,7 +166,8 @@ def test_null_arguments_are_rejected_without_a_device():
     one = ctypes.c_void_p(256)  # never dereferenced: rejected before any launch
     rc = lib.tree_attn_fwd(one, one, one, p.handle, ctypes.byref(shape), one, one, None)
     assert rc == b.INVALID_ARGUMENT and "host-only" in lib.tree_attn_last_error().decode()
-    assert lib.tree_attn_bwd_workspace_bytes(p.handle, ctypes.byref(shape)) == 256
+    # two [Hq, T] float32 arrays rounded up to 256 bytes, then two 64-byte counter blocks
+    assert lib.tree_attn_bwd_workspace_bytes(p.handle, ctypes.byref(shape)) == 256 + 128
     rc = lib.tree_attn_bwd(*([one] * 6), p.handle, ctypes.byref(shape), one, one, one, one, 1 << 20, None)
     assert rc == b.INVALID_ARGUMENT
 
