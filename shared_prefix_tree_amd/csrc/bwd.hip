@@ -130,7 +130,7 @@ struct DkdvRing {
 };
 
 template <typename T, int D>
-__device__ __forceinline__ void dkdv_item(const BwdArgs& a, int item) {
+__device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, int g, char* lds) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   using quad = typename M::quad;
@@ -151,13 +151,10 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, int item) {
 
   // Q ring, then dO ring (each at most 64 KB, so a slot offset fits an LDS
   // immediate), then the lse2 / delta ring
-  __shared__ __attribute__((aligned(16))) char ring[2 * kRing * TILE + kRing * STATS];
-  __shared__ __attribute__((aligned(16))) frag pshare[2][4 * PBLK];
-  __shared__ __attribute__((aligned(16))) float junk[64];
+  char* const ring = lds;
+  frag (*const pshare)[4 * PBLK] = reinterpret_cast<frag (*)[4 * PBLK]>(lds + 2 * kRing * TILE + kRing * STATS);
+  float* const junk = reinterpret_cast<float*>(lds + 2 * kRing * TILE + kRing * STATS + 2 * 4 * PBLK * sizeof(frag));
 
-  int tile_rank, g;
-  decode_item(item, a.Hkv, tile_rank, g);
-  const KTile tile = a.ktiles[tile_rank];
 
   // (opaque per item, so nothing derived from the thread index is hoisted
   // out of the item loop to stay live across items)
@@ -423,13 +420,11 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, int item) {
   }
 }
 
-// one workgroup per CU, taking items until none is left
+// LDS of the 64-key walk
 template <typename T, int D>
-__global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
-  __shared__ int s_item;
-  const int n_items = a.n_ktiles * a.Hkv;
-  for (int item; (item = take_item(&a.counters[0], n_items, &s_item)) >= 0;) dkdv_item<T, D>(a, item);
-  finish_block(&a.counters[0]);
+constexpr int dkdv_lds_bytes() {
+  constexpr int kRing = DkdvRing<T>::value, TILE = 64 * D * int(sizeof(T));
+  return 2 * kRing * TILE + kRing * 2 * 64 * 4 + 2 * 4 * 128 * int(sizeof(typename Mfma<T>::frag)) + 64 * 4;
 }
 
 // ---------------------------------------------------------------------------
@@ -446,7 +441,7 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 // three slots (about the same lead time as two steps of the 64-key walk) and
 // the P hand-off, twice as large, still fits LDS next to them.
 template <typename T, int D>
-__device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, int item) {
+__device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& tile, int g, char* lds) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   using quad = typename M::quad;
@@ -466,13 +461,10 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, int item) {
   static_assert(RB == 128 || RB == 256, "128- or 256-byte rows");
 
   // Q ring, then dO ring, then the -lse2 / -delta ring
-  __shared__ __attribute__((aligned(16))) char ring[2 * kRing * TILE + kRing * STATS];
-  __shared__ __attribute__((aligned(16))) frag pshare[2][8 * PBLK];
-  __shared__ __attribute__((aligned(16))) float junk[64];
+  char* const ring = lds;
+  frag (*const pshare)[8 * PBLK] = reinterpret_cast<frag (*)[8 * PBLK]>(lds + 2 * kRing * TILE + kRing * STATS);
+  float* const junk = reinterpret_cast<float*>(lds + 2 * kRing * TILE + kRing * STATS + 2 * 8 * PBLK * sizeof(frag));
 
-  int tile_rank, g;
-  decode_item(item, a.Hkv, tile_rank, g);
-  const KTile tile = a.ktiles[tile_rank];
 
   // (opaque per item, so nothing derived from the thread index is hoisted
   // out of the item loop to stay live across items)
@@ -719,12 +711,37 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, int item) {
   }
 }
 
-// one workgroup per CU, taking items until none is left
+// LDS of the 128-key walk
 template <typename T, int D>
-__global__ __launch_bounds__(512, 1) void tree_attn_dkdv_wide_kernel(BwdArgs a) {
+constexpr int dkdv_wide_lds_bytes() {
+  constexpr int TILE = 64 * D * int(sizeof(T));
+  return 2 * 3 * TILE + 3 * 2 * 64 * 4 + 2 * 8 * 128 * int(sizeof(typename Mfma<T>::frag)) + 64 * 4;
+}
+
+// One workgroup per CU, taking key tiles until none is left.  16-bit inputs
+// walk 128-key tiles and the 64-key remainders of segments (the plan's wide
+// list); fp32 walks 64-key tiles.  Both walks share one LDS buffer.
+template <typename T, int D>
+__global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
+  constexpr int kLds = sizeof(T) == 2 && dkdv_wide_lds_bytes<T, D>() > dkdv_lds_bytes<T, D>()
+                           ? dkdv_wide_lds_bytes<T, D>()
+                           : dkdv_lds_bytes<T, D>();
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
   __shared__ int s_item;
   const int n_items = a.n_ktiles * a.Hkv;
-  for (int item; (item = take_item(&a.counters[0], n_items, &s_item)) >= 0;) dkdv_wide_item<T, D>(a, item);
+  for (int item; (item = take_item(&a.counters[0], n_items, &s_item)) >= 0;) {
+    int tile_rank, g;
+    decode_item(item, a.Hkv, tile_rank, g);
+    const KTile tile = a.ktiles[tile_rank];
+    if constexpr (sizeof(T) == 2) {
+      if (tile.nk > 64)
+        dkdv_wide_item<T, D>(a, tile, g, lds);
+      else
+        dkdv_item<T, D>(a, tile, g, lds);
+    } else {
+      dkdv_item<T, D>(a, tile, g, lds);
+    }
+  }
   finish_block(&a.counters[0]);
 }
 
@@ -922,15 +939,10 @@ hipError_t launch_bwd_rowstat(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// a.ktiles holds 128-key tiles for 16-bit inputs, 64-key tiles for fp32
 template <typename T, int D>
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((tree_attn_dkdv_wide_kernel<T, D>), dim3(persistent_grid((unsigned)a.n_ktiles * (unsigned)a.Hkv)),
-                       dim3(512), 0, stream, a);
-  else
-    hipLaunchKernelGGL((tree_attn_dkdv_kernel<T, D>), dim3(persistent_grid((unsigned)a.n_ktiles * (unsigned)a.Hkv)),
-                       dim3(512), 0, stream, a);
+  hipLaunchKernelGGL((tree_attn_dkdv_kernel<T, D>), dim3(persistent_grid((unsigned)a.n_ktiles * (unsigned)a.Hkv)),
+                     dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -128,15 +128,25 @@ bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int3
       return int64_t(a.pos0) + a.nq > int64_t(b.pos0) + b.nq;
     });
   }
-  // key tiles per size, most queries first (stable on ties)
-  for (auto [tiles, tk] : {std::pair<std::vector<KTile>*, int>{&p.ktiles, kKTile}, {&p.ktiles_wide, kKTileWide}}) {
-    tiles->clear();
-    for (int32_t s = 0; s < S; ++s)
-      for (int32_t o = 0; o < seg_len[s]; o += tk)
-        tiles->push_back(KTile{seg_start[s] + o, std::min(tk, seg_len[s] - o), s, p.end[s]});
-    std::stable_sort(tiles->begin(), tiles->end(),
-                     [](const KTile& a, const KTile& b) { return a.qend - a.k0 > b.qend - b.k0; });
-  }
+  // 64-key tiles, most queries first (stable on ties)
+  p.ktiles.clear();
+  for (int32_t s = 0; s < S; ++s)
+    for (int32_t o = 0; o < seg_len[s]; o += kKTile)
+      p.ktiles.push_back(KTile{seg_start[s] + o, std::min(kKTile, seg_len[s] - o), s, p.end[s]});
+  std::stable_sort(p.ktiles.begin(), p.ktiles.end(),
+                   [](const KTile& a, const KTile& b) { return a.qend - a.k0 > b.qend - b.k0; });
+  // 128-key tiles; a segment's remainder of at most 64 keys is a 64-key tile
+  // (walked at half the cost per step), so no tile is more than half empty.
+  // Longest estimated walk first: query steps times 15 (128-key) or 8.
+  p.ktiles_wide.clear();
+  for (int32_t s = 0; s < S; ++s)
+    for (int32_t o = 0; o < seg_len[s]; o += kKTileWide)
+      p.ktiles_wide.push_back(KTile{seg_start[s] + o, std::min(kKTileWide, seg_len[s] - o), s, p.end[s]});
+  auto cost = [](const KTile& t) {
+    return int64_t((t.qend - t.k0 + kKTile - 1) / kKTile) * (t.nk > kKTile ? 15 : 8);
+  };
+  std::stable_sort(p.ktiles_wide.begin(), p.ktiles_wide.end(),
+                   [&](const KTile& a, const KTile& b) { return cost(a) > cost(b); });
   return true;
 }
 
