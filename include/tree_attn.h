@@ -87,6 +87,8 @@ typedef struct {
   int32_t num_q_tiles;   /* query tiles of 32 tokens */
   int32_t num_kv_tiles;  /* key tiles of 64 tokens */
   int32_t on_device;     /* 1 if device tables were uploaded */
+  int32_t q_begin;       /* the plan's query run [q_begin, q_end): 0 and T */
+  int32_t q_end;         /* unless built by tree_attn_plan_query_run */
 } tree_attn_plan_info_t;
 
 /*
@@ -107,6 +109,30 @@ typedef struct {
  */
 int tree_attn_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
                    int32_t num_segments, tree_attn_plan_t* out);
+
+/*
+ * A plan for one query run: the queries are the tokens [q_begin, q_end)
+ * (0 <= q_begin < q_end <= T), the keys and values still every token.  This
+ * is one context-parallel rank's share when the run is the rank's local
+ * tokens and K/V were gathered from the group (issue "Shared-prefix training
+ * with context parallelism for exact agent trajectories", section "Describe
+ * the solution you'd like": queries stay local, K/V is gathered).
+ *   tree_attn_fwd writes out and lse for the run's rows only and reads q of
+ *     those rows only; other rows are untouched;
+ *   tree_attn_bwd writes dq for the run's rows (others untouched) and all of
+ *     dk and dv: the gradient of the run's part of the loss,
+ *     sum over i in the run of <dout[i], out[i]>, i.e. this rank's share,
+ *     to be summed over the ranks (keys no run query sees get zeros); it
+ *     reads out, dout and lse of the run's rows only.
+ * So over a partition of [0, T) into runs, out, lse and dq of every row are
+ * bitwise those of the whole-token plan, and dk, dv are sums of the shares.
+ * Validation and errors as tree_attn_plan, plus INVALID_ARGUMENT for an
+ * empty or out-of-range run. */
+int tree_attn_plan_query_run(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                             int32_t num_segments, int32_t q_begin, int32_t q_end, tree_attn_plan_t* out);
+/* The same, host only (see tree_attn_plan_host). */
+int tree_attn_plan_query_run_host(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                                  int32_t num_segments, int32_t q_begin, int32_t q_end, tree_attn_plan_t* out);
 
 /* Same validation and derivation without touching any device: the plan can
  * be inspected (info, export) but not executed. */

@@ -34,6 +34,8 @@ EXPORT_SEG_END = 6
 # every symbol include/tree_attn.h declares
 SYMBOLS = (
     "tree_attn_plan",
+    "tree_attn_plan_query_run",
+    "tree_attn_plan_query_run_host",
     "tree_attn_plan_host",
     "tree_attn_plan_destroy",
     "tree_attn_plan_info",
@@ -77,6 +79,8 @@ class PlanInfo(ctypes.Structure):
         ("num_q_tiles", ctypes.c_int32),
         ("num_kv_tiles", ctypes.c_int32),
         ("on_device", ctypes.c_int32),
+        ("q_begin", ctypes.c_int32),
+        ("q_end", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -100,6 +104,9 @@ def library():
     i32p = ctypes.POINTER(ctypes.c_int32)
     vp = ctypes.c_void_p
     lib.tree_attn_plan.argtypes = [i32p, i32p, i32p, ctypes.c_int32, ctypes.POINTER(vp)]
+    for name in ("tree_attn_plan_query_run", "tree_attn_plan_query_run_host"):
+        getattr(lib, name).argtypes = [i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.POINTER(vp)]
     lib.tree_attn_plan_host.argtypes = [i32p, i32p, i32p, ctypes.c_int32, ctypes.POINTER(vp)]
     lib.tree_attn_plan_destroy.argtypes = [vp]
     lib.tree_attn_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
@@ -112,7 +119,9 @@ def library():
     lib.tree_attn_bwd_dkdv.argtypes = [vp] * 6 + [ctypes.POINTER(Shape), vp, vp, vp, ctypes.c_size_t, vp]
     lib.tree_attn_bwd_dq.argtypes = [vp] * 6 + [ctypes.POINTER(Shape), vp, vp, ctypes.c_size_t, vp]
     lib.tree_attn_last_error.restype = ctypes.c_char_p
-    for name in ("tree_attn_plan", "tree_attn_plan_host", "tree_attn_plan_destroy", "tree_attn_plan_info",
+    for name in ("tree_attn_plan", "tree_attn_plan_query_run", "tree_attn_plan_query_run_host",
+                 "tree_attn_plan_host", "tree_attn_plan_destroy",
+                 "tree_attn_plan_info",
                  "tree_attn_plan_export", "tree_attn_fwd", "tree_attn_bwd", "tree_attn_bwd_rowstat",
                  "tree_attn_bwd_dkdv", "tree_attn_bwd_dq"):
         getattr(lib, name).restype = ctypes.c_int
@@ -135,10 +144,11 @@ class Plan:
 
     ``device=True`` uploads the tables to the current HIP device (call under
     ``torch.cuda.device(...)`` to choose it); ``device=False`` builds a
-    host-only plan for inspection.
+    host-only plan for inspection.  ``query_run=(q_begin, q_end)`` restricts
+    the queries to those tokens (``tree_attn_plan_query_run[_host]``).
     """
 
-    def __init__(self, parent, seg_start, seg_len, device=True):
+    def __init__(self, parent, seg_start, seg_len, device=True, query_run=None):
         lib = library()
         self._handle = None
         p, pp = _i32(parent)
@@ -147,8 +157,13 @@ class Plan:
         if not (len(p) == len(s) == len(n)):
             raise ValueError("parent, seg_start and seg_len must have the same length")
         h = ctypes.c_void_p()
-        fn = lib.tree_attn_plan if device else lib.tree_attn_plan_host
-        _check(fn(pp, sp, np_, ctypes.c_int32(len(p)), ctypes.byref(h)))
+        if query_run is not None:
+            qb, qe = (int(x) for x in query_run)
+            fn = lib.tree_attn_plan_query_run if device else lib.tree_attn_plan_query_run_host
+            _check(fn(pp, sp, np_, ctypes.c_int32(len(p)), ctypes.c_int32(qb), ctypes.c_int32(qe), ctypes.byref(h)))
+        else:
+            fn = lib.tree_attn_plan if device else lib.tree_attn_plan_host
+            _check(fn(pp, sp, np_, ctypes.c_int32(len(p)), ctypes.byref(h)))
         self._handle = h
         self.device_index = None
         if device:
@@ -157,8 +172,8 @@ class Plan:
             self.device_index = torch.cuda.current_device()
 
     @classmethod
-    def from_topology(cls, topo, device=True):
-        return cls(topo.parent, topo.seg_start, topo.seg_len, device=device)
+    def from_topology(cls, topo, device=True, query_run=None):
+        return cls(topo.parent, topo.seg_start, topo.seg_len, device=device, query_run=query_run)
 
     @property
     def handle(self):

@@ -110,12 +110,12 @@ hipError_t upload_plan(const HostPlan& h, DevicePlan& d) {
 }
 
 int make_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len, int32_t num_segments,
-              tree_attn_plan_t* out, bool device) {
+              int32_t q_begin, int32_t q_end, tree_attn_plan_t* out, bool device) {
   if (!out) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan: out is NULL");
   *out = nullptr;
   auto* p = new tree_attn_plan_s();
   std::string err;
-  if (!build_host_plan(parent, seg_start, seg_len, num_segments, p->host, err)) {
+  if (!build_host_plan(parent, seg_start, seg_len, num_segments, q_begin, q_end, p->host, err)) {
     delete p;
     return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan: " + err);
   }
@@ -204,12 +204,22 @@ extern "C" {
 
 int tree_attn_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len, int32_t num_segments,
                    tree_attn_plan_t* out) {
-  return make_plan(parent, seg_start, seg_len, num_segments, out, true);
+  return make_plan(parent, seg_start, seg_len, num_segments, 0, -1, out, true);
+}
+
+int tree_attn_plan_query_run(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                             int32_t num_segments, int32_t q_begin, int32_t q_end, tree_attn_plan_t* out) {
+  return make_plan(parent, seg_start, seg_len, num_segments, q_begin, q_end, out, true);
+}
+
+int tree_attn_plan_query_run_host(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                                  int32_t num_segments, int32_t q_begin, int32_t q_end, tree_attn_plan_t* out) {
+  return make_plan(parent, seg_start, seg_len, num_segments, q_begin, q_end, out, false);
 }
 
 int tree_attn_plan_host(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
                         int32_t num_segments, tree_attn_plan_t* out) {
-  return make_plan(parent, seg_start, seg_len, num_segments, out, false);
+  return make_plan(parent, seg_start, seg_len, num_segments, 0, -1, out, false);
 }
 
 int tree_attn_plan_destroy(tree_attn_plan_t plan) {
@@ -232,6 +242,8 @@ int tree_attn_plan_info(tree_attn_plan_t plan, tree_attn_plan_info_t* info) {
   info->num_q_tiles = int32_t(h.qtiles[0].size());
   info->num_kv_tiles = int32_t(h.ktiles.size());
   info->on_device = plan->on_device ? 1 : 0;
+  info->q_begin = h.q_begin;
+  info->q_end = h.q_end;
   return TREE_ATTN_OK;
 }
 
@@ -382,6 +394,8 @@ int prep_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   a.n_qtiles = int32_t(plan->host.qtiles[ti].size());
   a.n_ktiles = int32_t(wide ? plan->host.ktiles_wide.size() : plan->host.ktiles.size());
   a.T = shape->total_tokens;
+  a.q_begin = plan->host.q_begin;
+  a.q_end = plan->host.q_end;
   a.Hq = shape->num_q_heads;
   a.Hkv = shape->num_kv_heads;
   a.G = G;

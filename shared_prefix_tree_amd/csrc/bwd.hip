@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
                                                                 float* __restrict__ ndelta,
                                                                 float* __restrict__ nlse2,
                                                                 ItemCounters* __restrict__ counters, int T_,
-                                                                int Hq) {
+                                                                int Hq, int row0, int row_end) {
   // the later stages hand out their work items through these counters
   if (blockIdx.x == 0 && threadIdx.x < 2 * int(sizeof(ItemCounters) / 4))
     __hip_atomic_store(reinterpret_cast<unsigned*>(counters) + threadIdx.x, 0u, __ATOMIC_RELAXED,
@@ -52,9 +52,9 @@ __global__ __launch_bounds__(256) void tree_attn_rowstat_kernel(const T* __restr
   constexpr int CPR = D / E;
   constexpr int RPB = 256 / CPR;
   static_assert(CPR <= 64 && 64 % CPR == 0, "row chunks must tile a wavefront");
-  const int row = blockIdx.x * RPB + threadIdx.x / CPR;  // row = i * Hq + h
+  const int row = row0 + blockIdx.x * RPB + threadIdx.x / CPR;  // row = i * Hq + h
   const int c = threadIdx.x % CPR;
-  const bool valid = row < T_ * Hq;
+  const bool valid = row < row_end;
   float acc = 0.f;
   if (valid) {
     const Chunk<T> o = load_chunk<T>(out + (size_t)row * D + c * E);
@@ -183,9 +183,21 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) settle(kv[ks]);
 
-  const int nblk = (tile.qend - tile.k0 + BM - 1) / BM;
+  // the queries walked: those of the run that see the tile
+  const int qbeg = max(tile.k0, a.q_begin), qend = min(tile.qend, a.q_end);
+  const int nblk = qend > qbeg ? (qend - qbeg + BM - 1) / BM : 0;
   const int n_steps = a.G * nblk;
-  const int last = tile.qend - 1;
+  const int last = qend - 1;
+  if (n_steps == 0) {  // no query of the run sees the tile: zero gradients
+    if (qh == 0 && key_valid) {
+      T* op = static_cast<T*>(dk_role ? a.dk : a.dv) + ((size_t)jkey * a.Hkv + g) * D;
+#pragma unroll
+      for (int d = 0; d < D; d += 32)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) *reinterpret_cast<quad*>(op + d + grp * 8 + half * 4) = quad{};
+    }
+    return;
+  }
 
   const unsigned q_ring = lds_addr(ring), o_ring = q_ring + kRing * TILE, s_ring = q_ring + 2 * kRing * TILE;
 
@@ -212,7 +224,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
   // always issues kCopiesK copies.  Rows past the range read the last row
   // (masked to P = 0).  Each copy reads from a wave-uniform row base plus a
   // small per-lane offset.
-  int cp_step = 0, cp_h = g * a.G, cp_i0 = tile.k0;
+  int cp_step = 0, cp_h = g * a.G, cp_i0 = qbeg;
   auto issue = [&](int slot) {
     const int lim = last - cp_i0;
     const size_t row0 = ((size_t)cp_i0 * a.Hq + cp_h) * D;
@@ -227,7 +239,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
     if (++cp_step < n_steps) {
       cp_i0 += BM;
       if (cp_i0 > last) {
-        cp_i0 = tile.k0;
+        cp_i0 = qbeg;
         ++cp_h;
       }
     }
@@ -271,7 +283,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
   // 0 reads a zero-filled slot (kRing - 1) and P buffer, so it adds zero;
   // the S, P of iteration n_steps are never used.
   frag pprev[2];
-  int dv_i0 = tile.k0;  // first query of the dV waves' current step
+  int dv_i0 = qbeg;  // first query of the dV waves' current step
   auto dv_iter = [&](int step, auto J) {
     constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
 #pragma unroll
@@ -286,16 +298,16 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
     float x[16];
     row_stats(j * STATS, x);
     const int i0 = dv_i0;
-    dv_i0 = dv_i0 + BM > last ? tile.k0 : dv_i0 + BM;
+    dv_i0 = dv_i0 + BM > last ? qbeg : dv_i0 + BM;
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(t[i], c, x[i]));
     if (__builtin_amdgcn_readfirstlane(int(i0 + qh * 32 < tile.k0 + kb * 32 + 31 ||
-                                           i0 + qh * 32 + 31 >= tile.qend))) {
+                                           i0 + qh * 32 + 31 >= qend))) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int qi = i0 + qh * 32 + c_row(i, half);
-        if (qi < jkey || qi >= tile.qend) p[i] = 0.f;
+        if (qi < jkey || qi >= qend) p[i] = 0.f;
       }
     }
 #pragma unroll
@@ -492,9 +504,21 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) settle(kv[ks]);
 
-  const int nblk = (tile.qend - tile.k0 + BM - 1) / BM;
+  // the queries walked: those of the run that see the tile
+  const int qbeg = max(tile.k0, a.q_begin), qend = min(tile.qend, a.q_end);
+  const int nblk = qend > qbeg ? (qend - qbeg + BM - 1) / BM : 0;
   const int n_steps = a.G * nblk;
-  const int last = tile.qend - 1;
+  const int last = qend - 1;
+  if (n_steps == 0) {  // no query of the run sees the tile: zero gradients
+    if (key_valid) {
+      T* op = static_cast<T*>(dk_role ? a.dk : a.dv) + ((size_t)jkey * a.Hkv + g) * D;
+#pragma unroll
+      for (int d = 0; d < D; d += 32)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) *reinterpret_cast<quad*>(op + d + grp * 8 + half * 4) = quad{};
+    }
+    return;
+  }
 
   const unsigned q_ring = lds_addr(ring), o_ring = q_ring + kRing * TILE, s_ring = q_ring + 2 * kRing * TILE;
 
@@ -510,7 +534,7 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
 #pragma unroll
   for (int r = 0; r < NC; ++r) cchunk[r] = (((lane % (RB / 16)) ^ swz<RB>(crow + RPC * r)) * 16);
   const unsigned row_bytes = (unsigned)a.Hq * RB;
-  int cp_step = 0, cp_h = g * a.G, cp_i0 = tile.k0;
+  int cp_step = 0, cp_h = g * a.G, cp_i0 = qbeg;
   auto issue = [&](int slot) {
     const int lim = last - cp_i0;
     const size_t row0 = ((size_t)cp_i0 * a.Hq + cp_h) * D;
@@ -525,7 +549,7 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
     if (++cp_step < n_steps) {
       cp_i0 += BM;
       if (cp_i0 > last) {
-        cp_i0 = tile.k0;
+        cp_i0 = qbeg;
         ++cp_h;
       }
     }
@@ -555,7 +579,7 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
   //   dV waves: dV^T += dO^T P of step - 1, then S and P of `step`;
   //   dK waves: dP - delta, dS, dK^T += Q^T dS of step - 1.
   frag pprev[2][2];
-  int dv_i0 = tile.k0;  // first query of the dV waves' current step
+  int dv_i0 = qbeg;  // first query of the dV waves' current step
   auto dv_iter = [&](int step, auto J) {
     constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
 #pragma unroll
@@ -572,7 +596,7 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
       for (int ks = 0; ks < KS; ++ks) M::mma(t[qh], ta.row(ks, j * TILE + qh * 32 * RB), kv[ks]);
     sched_pipeline<kLdsAhead, 4 * DB + 2 * KS, frag_reads<T>(true)>();
     const int i0 = dv_i0;
-    dv_i0 = dv_i0 + BM > last ? tile.k0 : dv_i0 + BM;
+    dv_i0 = dv_i0 + BM > last ? qbeg : dv_i0 + BM;
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
       float x[16];
@@ -581,11 +605,11 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
 #pragma unroll
       for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(t[qh][i], c, x[i]));
       if (__builtin_amdgcn_readfirstlane(int(i0 + qh * 32 < tile.k0 + kq * 32 + 31 ||
-                                             i0 + qh * 32 + 31 >= tile.qend))) {
+                                             i0 + qh * 32 + 31 >= qend))) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qi = i0 + qh * 32 + c_row(i, half);
-          if (qi < jkey || qi >= tile.qend) p[i] = 0.f;
+          if (qi < jkey || qi >= qend) p[i] = 0.f;
         }
       }
 #pragma unroll
@@ -932,10 +956,11 @@ template <typename T, int D>
 hipError_t launch_bwd_rowstat(const BwdArgs& a, hipStream_t stream) {
   constexpr int CPR = D / Chunk<T>::E;
   constexpr int RPB = 256 / CPR;
-  const unsigned rows = (unsigned)a.T * (unsigned)a.Hq;
+  // the query run's rows only
+  const unsigned rows = (unsigned)(a.q_end - a.q_begin) * (unsigned)a.Hq;
   hipLaunchKernelGGL((tree_attn_rowstat_kernel<T, D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, stream,
                      static_cast<const T*>(a.out), static_cast<const T*>(a.dout), a.lse, a.delta,
-                     a.delta + (size_t)a.Hq * a.T, a.counters, a.T, a.Hq);
+                     a.delta + (size_t)a.Hq * a.T, a.counters, a.T, a.Hq, a.q_begin * a.Hq, a.q_end * a.Hq);
   return hipGetLastError();
 }
 

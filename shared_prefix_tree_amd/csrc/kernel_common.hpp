@@ -531,6 +531,7 @@ struct BwdArgs {
   const Span* spans;
   int32_t n_qtiles, n_ktiles;
   int32_t T, Hq, Hkv, G;
+  int32_t q_begin, q_end;  // the plan's query run
   float scale;
 };
 

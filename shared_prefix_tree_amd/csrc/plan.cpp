@@ -20,7 +20,7 @@ std::string fmt(const char* f, long long a, long long b = 0, long long c = 0) {
 }  // namespace
 
 bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
-                     int32_t S, HostPlan& p, std::string& err) {
+                     int32_t S, int32_t q_begin, int32_t q_end, HostPlan& p, std::string& err) {
   if (!parent || !seg_start || !seg_len) {
     err = "null topology pointer";
     return false;
@@ -68,8 +68,15 @@ bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int3
     path.push_back(s);
   }
   for (int32_t s : path) p.end[s] = int32_t(T);
+  if (q_end < 0) q_end = int32_t(T);
+  if (q_begin < 0 || q_begin >= q_end || q_end > T) {
+    err = fmt("query run [%lld, %lld) must be a non-empty range inside [0, %lld)", q_begin, q_end, T);
+    return false;
+  }
 
   p.T = int32_t(T);
+  p.q_begin = q_begin;
+  p.q_end = q_end;
   p.S = S;
   p.parent.assign(parent, parent + S);
   p.start.assign(seg_start, seg_start + S);
@@ -91,7 +98,9 @@ bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int3
     p.max_depth = std::max(p.max_depth, p.depth[s]);
     const int64_t n = seg_len[s];
     p.max_path = std::max<int64_t>(p.max_path, int64_t(p.prefix[s]) + n);
-    p.pairs += n * int64_t(p.prefix[s]) + n * (n + 1) / 2;
+    // pairs of the run's queries in this segment: offsets [o0, o1)
+    const int64_t o0 = std::max<int64_t>(0, q_begin - seg_start[s]), o1 = std::min<int64_t>(n, q_end - seg_start[s]);
+    if (o1 > o0) p.pairs += (o1 - o0) * int64_t(p.prefix[s]) + (o1 * (o1 + 1) - o0 * (o0 + 1)) / 2;
   }
 
   // merged ancestor spans per segment: root ... parent, then the segment
@@ -121,20 +130,28 @@ bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int3
     const int tq = kQTileSizes[t];
     auto& tiles = p.qtiles[t];
     tiles.clear();
-    for (int32_t s = 0; s < S; ++s)
-      for (int32_t o = 0; o < seg_len[s]; o += tq)
-        tiles.push_back(QTile{seg_start[s] + o, std::min(tq, seg_len[s] - o), s, p.prefix[s] + o});
+    for (int32_t s = 0; s < S; ++s) {
+      // the run's tokens of this segment, [o0, o1) from its start
+      const int32_t o0 = std::max(0, q_begin - seg_start[s]), o1 = std::min(seg_len[s], q_end - seg_start[s]);
+      for (int32_t o = o0; o < o1; o += tq)
+        tiles.push_back(QTile{seg_start[s] + o, std::min(tq, o1 - o), s, p.prefix[s] + o});
+    }
     std::stable_sort(tiles.begin(), tiles.end(), [](const QTile& a, const QTile& b) {
       return int64_t(a.pos0) + a.nq > int64_t(b.pos0) + b.nq;
     });
   }
-  // 64-key tiles, most queries first (stable on ties)
+  // 64-key tiles over every key, most run queries first (stable on ties).
+  // The queries that see key tile [k0, k0 + nk) are [k0, qend); the kernels
+  // walk their intersection with the run (empty: the tile's keys get zero
+  // gradients).
+  auto walk = [&](const KTile& t) {
+    return int64_t(std::max(0, std::min(t.qend, q_end) - std::max(t.k0, q_begin)));
+  };
   p.ktiles.clear();
   for (int32_t s = 0; s < S; ++s)
     for (int32_t o = 0; o < seg_len[s]; o += kKTile)
       p.ktiles.push_back(KTile{seg_start[s] + o, std::min(kKTile, seg_len[s] - o), s, p.end[s]});
-  std::stable_sort(p.ktiles.begin(), p.ktiles.end(),
-                   [](const KTile& a, const KTile& b) { return a.qend - a.k0 > b.qend - b.k0; });
+  std::stable_sort(p.ktiles.begin(), p.ktiles.end(), [&](const KTile& a, const KTile& b) { return walk(a) > walk(b); });
   // 128-key tiles; a segment's remainder of at most 64 keys is a 64-key tile
   // (walked at half the cost per step), so no tile is more than half empty.
   // Longest estimated walk first: query steps times 15 (128-key) or 8.
@@ -142,9 +159,7 @@ bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int3
   for (int32_t s = 0; s < S; ++s)
     for (int32_t o = 0; o < seg_len[s]; o += kKTileWide)
       p.ktiles_wide.push_back(KTile{seg_start[s] + o, std::min(kKTileWide, seg_len[s] - o), s, p.end[s]});
-  auto cost = [](const KTile& t) {
-    return int64_t((t.qend - t.k0 + kKTile - 1) / kKTile) * (t.nk > kKTile ? 15 : 8);
-  };
+  auto cost = [&](const KTile& t) { return (walk(t) + kKTile - 1) / kKTile * (t.nk > kKTile ? 15 : 8); };
   std::stable_sort(p.ktiles_wide.begin(), p.ktiles_wide.end(),
                    [&](const KTile& a, const KTile& b) { return cost(a) > cost(b); });
   return true;

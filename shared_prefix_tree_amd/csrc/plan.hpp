@@ -55,6 +55,7 @@ inline int qtile_index(int tq) { return tq == 32 ? 0 : tq == 64 ? 1 : tq == 128 
 
 struct HostPlan {
   int32_t T = 0, S = 0, num_roots = 0, max_depth = 0, max_spans = 0;
+  int32_t q_begin = 0, q_end = 0;  // the query run: tokens whose attention is computed
   int64_t max_path = 0, pairs = 0;
   std::vector<int32_t> parent, start, len, depth, prefix, end;
   std::vector<int32_t> span_ptr;
@@ -66,7 +67,9 @@ struct HostPlan {
 
 // Validates the topology and fills `plan`; on failure returns false and
 // sets `err`.
+// A query run [q_begin, q_end) restricts the queries (q_end < 0: to the
+// last token); the keys are always every token.
 bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
-                     int32_t num_segments, HostPlan& plan, std::string& err);
+                     int32_t num_segments, int32_t q_begin, int32_t q_end, HostPlan& plan, std::string& err);
 
 }  // namespace tree_attn
