@@ -98,6 +98,90 @@ def cpu_baseline(w, topo, arrs, kv_heads=1, pair_fraction=1.0):
     }
 
 
+def balanced_runs(topo, R):
+    """R contiguous query runs of (nearly) equal pair counts: token i sees
+    A(s) + (offset in s) + 1 keys."""
+    import numpy as np
+
+    parent, st, ln = (np.asarray(x, np.int64) for x in (topo.parent, topo.seg_start, topo.seg_len))
+    prefix = np.zeros(len(ln), np.int64)
+    for s in range(len(ln)):
+        if parent[s] >= 0:
+            prefix[s] = prefix[parent[s]] + ln[parent[s]]
+    per_token = np.concatenate([prefix[s] + np.arange(1, ln[s] + 1) for s in range(len(ln))])
+    cum = np.cumsum(per_token)
+    cuts = [int(np.searchsorted(cum, cum[-1] * r / R)) + 1 for r in range(1, R)]
+    edges = [0, *cuts, int(cum.size)]
+    return list(zip(edges[:-1], edges[1:]))
+
+
+def query_run_shares(args, sp, w, topo, t, out, lse, dq, dk, dv, ws, pairs):
+    """Times each rank's share (forward + backward of one query run against
+    every key) and checks that out / dq rows equal the whole plan's and that
+    the dK / dV shares sum to its gradient.  One JSON line."""
+    import numpy as np
+    import torch
+
+    R = args.query_runs
+    runs = balanced_runs(topo, R)
+    whole = sp.Plan.from_topology(topo)
+    sp.tree_attn_fwd(t["q"], t["k"], t["v"], whole, out=out, lse=lse)
+    sp.tree_attn_bwd(t["q"], t["k"], t["v"], out, lse, t["dout"], whole, dq=dq, dk=dk, dv=dv, workspace=ws)
+    out_r, lse_r, dq_r = torch.empty_like(out), torch.empty_like(lse), torch.empty_like(dq)
+    dk_r, dv_r = torch.empty_like(dk), torch.empty_like(dv)
+    sum_dk = torch.zeros(dk.shape, dtype=torch.float64, device=dk.device)
+    sum_dv = torch.zeros_like(sum_dk)
+    T, Hq, D = t["q"].shape
+    ranks = []
+    exact = True
+    for qb, qe in runs:
+        plan = sp.Plan.from_topology(topo, query_run=(qb, qe))
+        rp = plan.info()["pairs"]
+
+        def share(events=None):
+            if events:
+                events[0].record()
+            sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan, out=out_r, lse=lse_r)
+            if events:
+                events[1].record()
+            sp.tree_attn_bwd(t["q"], t["k"], t["v"], out_r, lse_r, t["dout"], plan, dq=dq_r, dk=dk_r, dv=dv_r,
+                             workspace=ws)
+            if events:
+                events[2].record()
+
+        for _ in range(args.warmup):
+            share()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            share(ev[i])
+        torch.cuda.synchronize()
+        f_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+        b_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+        exact &= bool(torch.equal(out_r[qb:qe], out[qb:qe]) and torch.equal(dq_r[qb:qe], dq[qb:qe])
+                      and torch.equal(lse_r[:, qb:qe], lse[:, qb:qe]))
+        sum_dk += dk_r.double()
+        sum_dv += dv_r.double()
+        flops = 14.0 * D * Hq * rp
+        ranks.append({"run": [int(qb), int(qe)], "pairs": int(rp), "fwd_ms": round(f_ms, 4),
+                      "bwd_ms": round(b_ms, 4), "tflops": round(flops / ((f_ms + b_ms) * 1e-3) / 1e12, 2)})
+        log(f"rank run [{qb}, {qe}): pairs {rp}, fwd {f_ms:.3f} ms, bwd {b_ms:.3f} ms")
+
+    def rel(a, b):
+        return float(torch.linalg.vector_norm(a - b.double()) / torch.linalg.vector_norm(b.double()))
+
+    slowest = max(r["fwd_ms"] + r["bwd_ms"] for r in ranks)
+    print(json.dumps({
+        "metric": "query-run shares (one context-parallel rank each), fwd+bwd",
+        "workload": w.name, "ranks": R, "pairs": int(pairs), "dtype": w.dtype,
+        "per_rank": ranks,
+        "slowest_rank_ms": round(slowest, 4),
+        "sum_of_ranks_ms": round(sum(r["fwd_ms"] + r["bwd_ms"] for r in ranks), 4),
+        "out_lse_dq_rows_bitwise_equal_whole": exact,
+        "dk_sum_rel_l2_vs_whole": rel(sum_dk, dk),
+        "dv_sum_rel_l2_vs_whole": rel(sum_dv, dv),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +192,9 @@ def main():
     ap.add_argument("--cpu-kv-heads", type=int, default=1)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes, --steps times (scales HBM counters)")
+    ap.add_argument("--query-runs", type=int, default=0, metavar="R",
+                    help="only time the shares of R context-parallel ranks: query runs of equal pairs, "
+                         "each against every key (prints its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -160,6 +247,9 @@ def main():
 
     stages = ["fwd", "rowstat", "dkdv", "dq"] if w.backward else ["fwd"]
     plan_host_s = []
+    if args.query_runs:
+        query_run_shares(args, sp, w, topo, t, out, lse, dq, dk, dv, ws, pairs)
+        return
 
     def step(events=None):
         t0 = time.perf_counter()
