@@ -98,6 +98,36 @@ def cpu_baseline(w, topo, arrs, kv_heads=1, pair_fraction=1.0):
     }
 
 
+def fragment_planner(args):
+    """Host timing and token counts of bounded fragment planning (the pages
+    report their tree before and after fragmentation in tokens)."""
+    import numpy as np
+
+    import shared_prefix_tree_amd as sp
+    from workloads import agent_tree, get_workload
+
+    B = args.fragment_bound
+    forests = [(args.workload, get_workload(args.workload).topology())]
+    forests.append(("agent_trees_4194304", agent_tree(np.random.default_rng([7, 0]), total=1 << 22)))
+    rows = []
+    for name, topo in forests:
+        times = []
+        for _ in range(max(3, args.steps // 4)):
+            t0 = time.perf_counter()
+            frags, info = sp.fragment(topo.parent, topo.seg_start, topo.seg_len, B)
+            times.append(time.perf_counter() - t0)
+        ms = 1e3 * float(np.median(times))
+        T, F = info["source_tokens"], info["fragment_tokens"]
+        rows.append({"forest": name, "tokens": int(T), "segments": int(topo.num_segments),
+                     "fragments": int(info["num_fragments"]), "fragment_tokens": int(F),
+                     "repeated_pct": round(100.0 * (F - T) / T, 3), "host_ms": round(ms, 3),
+                     "mtokens_per_s": round(T / (ms * 1e-3) / 1e6, 2)})
+        log(f"{name}: {T} tokens -> {F} in {info['num_fragments']} fragments of <= {B} "
+            f"(+{100.0 * (F - T) / T:.2f} %), {ms:.2f} ms")
+    print(json.dumps({"metric": "bounded fragment planning (host)", "max_tokens": B,
+                      "binding_includes_table_export": True, "forests": rows}), flush=True)
+
+
 def balanced_runs(topo, R):
     """R contiguous query runs of (nearly) equal pair counts: token i sees
     A(s) + (offset in s) + 1 keys."""
@@ -192,6 +222,9 @@ def main():
     ap.add_argument("--cpu-kv-heads", type=int, default=1)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes, --steps times (scales HBM counters)")
+    ap.add_argument("--fragment-bound", type=int, default=0, metavar="B",
+                    help="only time the host fragment planner on the workload's forest and on a stream of "
+                         "agent-call trees, fragments of at most B tokens (prints its own JSON line)")
     ap.add_argument("--query-runs", type=int, default=0, metavar="R",
                     help="only time the shares of R context-parallel ranks: query runs of equal pairs, "
                          "each against every key (prints its own JSON line)")
@@ -202,6 +235,11 @@ def main():
         sys.exit(2)
 
     import numpy as np
+
+    if args.fragment_bound:
+        fragment_planner(args)
+        return
+
     import torch
 
     if args.copy_calibration:

@@ -146,6 +146,51 @@ int tree_attn_plan_destroy(tree_attn_plan_t plan);
 /* Topology statistics of a plan (FLOP accounting uses `pairs`). */
 int tree_attn_plan_info(tree_attn_plan_t plan, tree_attn_plan_info_t* info);
 
+/*
+ * Bounded fragment planning with ancestor repetition (host only; issue
+ * "Shared-prefix training with context parallelism for exact agent
+ * trajectories": the trainer bounds fragments and may repeat ancestors
+ * across fragments to honour the memory bound).  Splits a DFS segment forest
+ * (as for tree_attn_plan) into fragments of at most max_tokens tokens, each
+ * a DFS forest of its own (segments contiguous from token 0) in which every
+ * token sees exactly the tokens it sees in the source forest: a fragment
+ * that starts inside a tree first repeats the ancestor chain of its first
+ * segment, root first, and a segment split at a fragment boundary restarts
+ * in the next fragment with a repeated copy of its already placed part (one
+ * segment).  Every source token is owned -- carries its loss -- in exactly
+ * one fragment; repeated tokens are not owned (give them zero dout, and sum
+ * dk/dv over a token's copies).  Fragments are filled in DFS order.
+ * Errors: INVALID_ARGUMENT for a malformed forest, max_tokens < 1, or a
+ * root-to-leaf path longer than max_tokens.  The result is library-owned.
+ */
+typedef struct tree_attn_fragments_s* tree_attn_fragments_t;
+typedef struct {
+  int32_t num_fragments;
+  int32_t num_segments;     /* over all fragments */
+  int32_t max_tokens;
+  int64_t source_tokens;    /* T of the source forest */
+  int64_t fragment_tokens;  /* tokens over all fragments: T plus the repeated ones */
+} tree_attn_fragments_info_t;
+int tree_attn_fragment(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len, int32_t num_segments,
+                       int32_t max_tokens, tree_attn_fragments_t* out);
+int tree_attn_fragments_destroy(tree_attn_fragments_t fragments);
+int tree_attn_fragments_info(tree_attn_fragments_t fragments, tree_attn_fragments_info_t* info);
+/* Tables (int32), like tree_attn_plan_export (buf NULL: query *count):
+ *   FRAG_SEG_PTR      [F+1]  fragment f's segments are [ptr[f], ptr[f+1])
+ *   FRAG_TOKEN_PTR    [F+1]  fragment f's tokens are [ptr[f], ptr[f+1])
+ *   FRAG_SEG_PARENT   per segment: parent within its fragment, -1 for a root
+ *   FRAG_SEG_LEN      per segment (a fragment's segments start at its token 0)
+ *   FRAG_TOKEN_SOURCE per fragment token: its source token
+ *   FRAG_TOKEN_OWNER  per fragment token: 1 owned, 0 repeated */
+#define TREE_ATTN_FRAG_SEG_PTR 0
+#define TREE_ATTN_FRAG_TOKEN_PTR 1
+#define TREE_ATTN_FRAG_SEG_PARENT 2
+#define TREE_ATTN_FRAG_SEG_LEN 3
+#define TREE_ATTN_FRAG_TOKEN_SOURCE 4
+#define TREE_ATTN_FRAG_TOKEN_OWNER 5
+int tree_attn_fragments_export(tree_attn_fragments_t fragments, int32_t which, int32_t* buf, int64_t cap,
+                               int64_t* count);
+
 /* Copy one of the plan's host tables (int32 records) for inspection.
  *   which = TREE_ATTN_EXPORT_*; buf may be NULL to query *count;
  *   cap = capacity of buf in int32 elements; *count = elements available.

@@ -27,3 +27,4 @@ from .tree_attention import (  # noqa: F401
     as_f64,
     rel_l2,
 )
+from .fragments import fragment  # noqa: F401

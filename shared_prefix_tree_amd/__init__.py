@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     Plan,
     TreeAttnError,
     bwd_workspace_bytes,
+    fragment,
     library,
     tree_attn_bwd,
     tree_attn_bwd_stages,

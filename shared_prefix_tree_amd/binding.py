@@ -47,7 +47,18 @@ SYMBOLS = (
     "tree_attn_bwd_dkdv",
     "tree_attn_bwd_dq",
     "tree_attn_last_error",
+    "tree_attn_fragment",
+    "tree_attn_fragments_destroy",
+    "tree_attn_fragments_info",
+    "tree_attn_fragments_export",
 )
+
+FRAG_SEG_PTR = 0
+FRAG_TOKEN_PTR = 1
+FRAG_SEG_PARENT = 2
+FRAG_SEG_LEN = 3
+FRAG_TOKEN_SOURCE = 4
+FRAG_TOKEN_OWNER = 5
 
 
 class TreeAttnError(RuntimeError):
@@ -87,6 +98,19 @@ class PlanInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class FragmentsInfo(ctypes.Structure):
+    _fields_ = [
+        ("num_fragments", ctypes.c_int32),
+        ("num_segments", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int32),
+        ("source_tokens", ctypes.c_int64),
+        ("fragment_tokens", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
 _lib = None
 
 
@@ -119,6 +143,14 @@ def library():
     lib.tree_attn_bwd_dkdv.argtypes = [vp] * 6 + [ctypes.POINTER(Shape), vp, vp, vp, ctypes.c_size_t, vp]
     lib.tree_attn_bwd_dq.argtypes = [vp] * 6 + [ctypes.POINTER(Shape), vp, vp, ctypes.c_size_t, vp]
     lib.tree_attn_last_error.restype = ctypes.c_char_p
+    lib.tree_attn_fragment.argtypes = [i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(vp)]
+    lib.tree_attn_fragments_destroy.argtypes = [vp]
+    lib.tree_attn_fragments_info.argtypes = [vp, ctypes.POINTER(FragmentsInfo)]
+    lib.tree_attn_fragments_export.argtypes = [vp, ctypes.c_int32, i32p, ctypes.c_int64,
+                                               ctypes.POINTER(ctypes.c_int64)]
+    for name in ("tree_attn_fragment", "tree_attn_fragments_destroy", "tree_attn_fragments_info",
+                 "tree_attn_fragments_export"):
+        getattr(lib, name).restype = ctypes.c_int
     for name in ("tree_attn_plan", "tree_attn_plan_query_run", "tree_attn_plan_query_run_host",
                  "tree_attn_plan_host", "tree_attn_plan_destroy",
                  "tree_attn_plan_info",
@@ -209,6 +241,46 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def fragment(parent, seg_start, seg_len, max_tokens):
+    """Bounded fragment planning (``tree_attn_fragment``).  Returns a list of
+    fragments, each a dict: ``parent``, ``seg_start``, ``seg_len`` (a DFS
+    forest starting at token 0), ``source`` (source token of each token) and
+    ``owner`` (1 owned, 0 repeated), plus the info record."""
+    lib = library()
+    p, pp = _i32(parent)
+    s, sp = _i32(seg_start)
+    n, np_ = _i32(seg_len)
+    h = ctypes.c_void_p()
+    _check(lib.tree_attn_fragment(pp, sp, np_, ctypes.c_int32(len(p)), ctypes.c_int32(int(max_tokens)),
+                                  ctypes.byref(h)))
+    try:
+        inf = FragmentsInfo()
+        _check(lib.tree_attn_fragments_info(h, ctypes.byref(inf)))
+        tables = {}
+        for which in (FRAG_SEG_PTR, FRAG_TOKEN_PTR, FRAG_SEG_PARENT, FRAG_SEG_LEN, FRAG_TOKEN_SOURCE,
+                      FRAG_TOKEN_OWNER):
+            cnt = ctypes.c_int64()
+            _check(lib.tree_attn_fragments_export(h, which, None, 0, ctypes.byref(cnt)))
+            buf = np.zeros(max(1, cnt.value), dtype=np.int32)
+            _check(lib.tree_attn_fragments_export(h, which, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                                  cnt.value, ctypes.byref(cnt)))
+            tables[which] = buf[: cnt.value]
+    finally:
+        lib.tree_attn_fragments_destroy(h)
+    sptr, tptr = tables[FRAG_SEG_PTR], tables[FRAG_TOKEN_PTR]
+    frags = []
+    for f in range(inf.num_fragments):
+        ln = tables[FRAG_SEG_LEN][sptr[f]:sptr[f + 1]]
+        frags.append({
+            "parent": tables[FRAG_SEG_PARENT][sptr[f]:sptr[f + 1]],
+            "seg_start": np.concatenate([[0], np.cumsum(ln)[:-1]]).astype(np.int32),
+            "seg_len": ln,
+            "source": tables[FRAG_TOKEN_SOURCE][tptr[f]:tptr[f + 1]],
+            "owner": tables[FRAG_TOKEN_OWNER][tptr[f]:tptr[f + 1]],
+        })
+    return frags, inf.as_dict()
 
 
 def _shape(q, k, softmax_scale):

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "lib", "libtree_attn.so")
-SOURCES = ["plan.cpp", "api.cpp", "fwd.hip", "bwd.hip"]
+SOURCES = ["plan.cpp", "fragments.cpp", "api.cpp", "fwd.hip", "bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

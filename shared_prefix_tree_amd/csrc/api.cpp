@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/tree_attn.h"
+#include "fragments.hpp"
 #include "kernel_common.hpp"
 #include "plan.hpp"
 
@@ -51,6 +52,10 @@ struct DevicePlan {
 };
 
 }  // namespace tree_attn
+
+struct tree_attn_fragments_s {
+  tree_attn::Fragments f;
+};
 
 struct tree_attn_plan_s {
   tree_attn::HostPlan host;
@@ -220,6 +225,56 @@ int tree_attn_plan_query_run_host(const int32_t* parent, const int32_t* seg_star
 int tree_attn_plan_host(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
                         int32_t num_segments, tree_attn_plan_t* out) {
   return make_plan(parent, seg_start, seg_len, num_segments, 0, -1, out, false);
+}
+
+int tree_attn_fragment(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len, int32_t num_segments,
+                       int32_t max_tokens, tree_attn_fragments_t* out) {
+  if (!out) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fragment: out is NULL");
+  *out = nullptr;
+  auto* r = new tree_attn_fragments_s();
+  std::string err;
+  if (!build_fragments(parent, seg_start, seg_len, num_segments, max_tokens, r->f, err)) {
+    delete r;
+    return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fragment: " + err);
+  }
+  *out = r;
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_fragments_destroy(tree_attn_fragments_t fr) {
+  delete fr;
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_fragments_info(tree_attn_fragments_t fr, tree_attn_fragments_info_t* info) {
+  if (!fr || !info) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fragments_info: NULL argument");
+  const Fragments& f = fr->f;
+  info->num_fragments = int32_t(f.frag_seg_ptr.size()) - 1;
+  info->num_segments = int32_t(f.seg_len.size());
+  info->max_tokens = f.max_tokens;
+  info->source_tokens = f.source_tokens;
+  info->fragment_tokens = int64_t(f.token_source.size());
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_fragments_export(tree_attn_fragments_t fr, int32_t which, int32_t* buf, int64_t cap, int64_t* count) {
+  if (!fr || !count) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fragments_export: NULL argument");
+  const Fragments& f = fr->f;
+  const std::vector<int32_t>* src = nullptr;
+  switch (which) {
+    case TREE_ATTN_FRAG_SEG_PTR: src = &f.frag_seg_ptr; break;
+    case TREE_ATTN_FRAG_TOKEN_PTR: src = &f.frag_token_ptr; break;
+    case TREE_ATTN_FRAG_SEG_PARENT: src = &f.seg_parent; break;
+    case TREE_ATTN_FRAG_SEG_LEN: src = &f.seg_len; break;
+    case TREE_ATTN_FRAG_TOKEN_SOURCE: src = &f.token_source; break;
+    case TREE_ATTN_FRAG_TOKEN_OWNER: src = &f.token_owner; break;
+    default: return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fragments_export: unknown table");
+  }
+  *count = int64_t(src->size());
+  if (!buf) return TREE_ATTN_OK;
+  if (cap < *count) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fragments_export: buffer too small");
+  std::memcpy(buf, src->data(), src->size() * sizeof(int32_t));
+  return TREE_ATTN_OK;
 }
 
 int tree_attn_plan_destroy(tree_attn_plan_t plan) {
