@@ -212,6 +212,72 @@ def query_run_shares(args, sp, w, topo, t, out, lse, dq, dk, dv, ws, pairs):
     }), flush=True)
 
 
+def edge_loss(args):
+    """Times the sampled-edge projection and loss: the workload's forest,
+    every segment sampled with probability 1/4 (each sampled token is an
+    edge from the token before it), a 4096-wide hidden state and a
+    131,072-word bf16 vocabulary head.  Algorithmic work: 2 E d V flops
+    forward (the logits GEMM), 6 E d V backward (logits again, dh, dW).
+    One JSON line."""
+    import numpy as np
+    import torch
+
+    import shared_prefix_tree_amd as sp
+    from workloads import get_workload, make_tensor, sampled_edges
+
+    d, V = 4096, 131072
+    w = get_workload(args.workload)
+    topo = w.topology()
+    T = topo.total_tokens
+    src, tgt = sampled_edges(topo, np.random.default_rng([w.seed, 5]), V, 0.25)
+    E = int(src.size)
+    log(f"edge loss: T={T} E={E} d={d} V={V}: generating inputs")
+    dev = "cuda:0"
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    h = dev_bf16(make_tensor("hidden", w.seed, T, 1, d)[:, 0])
+    W = dev_bf16(make_tensor("weight", w.seed, V, 1, d, std=0.02)[:, 0])
+    dloss = torch.full((E,), 1.0 / E, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        edges = sp.EdgePlan(src, tgt, T, V)
+    ws = torch.empty(edges.workspace_bytes(d), dtype=torch.uint8, device=dev)
+    loss, lse = sp.edge_loss_fwd(h, W, edges, workspace=ws)
+    for _ in range(args.warmup):
+        loss, lse = sp.edge_loss_fwd(h, W, edges, workspace=ws)
+        sp.edge_loss_bwd(h, W, edges, lse, dloss, workspace=ws)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        loss, lse = sp.edge_loss_fwd(h, W, edges, workspace=ws)
+        ev[i][1].record()
+        dh, dW = sp.edge_loss_bwd(h, W, edges, lse, dloss, workspace=ws)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps * 1e3
+    f_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    b_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    fwd_f, bwd_f = 2.0 * E * d * V, 6.0 * E * d * V
+    tf = (fwd_f + bwd_f) / ((f_ms + b_ms) * 1e-3) / 1e12
+    mean_loss = float(loss.double().mean())
+    log(f"edge loss: fwd {f_ms:.3f} ms, bwd {b_ms:.3f} ms, {tf:.1f} TFLOP/s, mean loss {mean_loss:.4f} "
+        f"(log V = {np.log(V):.4f})")
+    print(json.dumps({
+        "metric": "sampled-edge projection + loss, fwd+bwd", "value": round(tf, 2), "unit": "TFLOP/s",
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall, 4), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name} edges", "tokens": T, "edges": E, "hidden": d, "vocab": V},
+        "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+        "fwd_tflops": round(fwd_f / (f_ms * 1e-3) / 1e12, 2), "bwd_tflops": round(bwd_f / (b_ms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tf / 2500.0, 4), "traffic": None},
+        "mean_loss": round(mean_loss, 5),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,9 +294,12 @@ def main():
     ap.add_argument("--query-runs", type=int, default=0, metavar="R",
                     help="only time the shares of R context-parallel ranks: query runs of equal pairs, "
                          "each against every key (prints its own JSON line)")
+    ap.add_argument("--edge-loss", action="store_true",
+                    help="only time the sampled-edge projection and loss on the workload's forest "
+                         "(prints its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(sharding is described in the design notes); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
@@ -250,6 +319,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n * 4, "launches": args.steps}), flush=True)
+        return
+
+    if args.edge_loss:
+        edge_loss(args)
         return
 
     import shared_prefix_tree_amd as sp

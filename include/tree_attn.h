@@ -191,6 +191,43 @@ int tree_attn_fragments_info(tree_attn_fragments_t fragments, tree_attn_fragment
 int tree_attn_fragments_export(tree_attn_fragments_t fragments, int32_t which, int32_t* buf, int64_t cap,
                                int64_t* count);
 
+/*
+ * Sampled-edge projection and loss (draft "feat(hybrid): add opt-in
+ * shared-prefix attention and Mamba execution", section "Summary": select
+ * edge-source hidden states before the vocabulary projection, one loss owner
+ * per sampled action).  An edge e is a sampled token tgt[e] (a vocabulary
+ * index) predicted from the hidden state of token src[e]; only those states
+ * go through the vocabulary head W [V, d]:
+ *   logits[e] = W h[src[e]],  lse[e] = log sum_v exp(logits[e, v]),
+ *   loss[e]   = lse[e] - logits[e, tgt[e]].
+ * Backward, given dloss [E]: G[e] = (softmax(logits[e]) - onehot(tgt[e]))
+ * dloss[e]; dh[t] = sum over edges with src = t of G[e] W (rows of tokens
+ * that are no edge's source: 0); dW = sum_e G[e]^T h[src[e]].  A token may
+ * be the source of several edges (a branch point).  h, W, dh, dW are bf16
+ * row-major, 16-byte aligned, d a multiple of 8; loss, lse, dloss float32.
+ * Deterministic (no atomics; library GEMMs with atomics disabled).
+ *
+ * tree_attn_edges validates the host arrays (0 <= src < num_tokens,
+ * 0 <= tgt < vocab), groups the edges by source and uploads them to the
+ * current device; the object is library-owned and immutable.
+ * Errors: INVALID_ARGUMENT (NULL, out of range, small workspace, other
+ * device), UNSUPPORTED (d not a multiple of 8, > 262,143 edges), HIP_ERROR.
+ */
+typedef struct tree_attn_edges_s* tree_attn_edges_t;
+int tree_attn_edges(const int32_t* edge_src, const int32_t* edge_tgt, int32_t num_edges, int32_t num_tokens,
+                    int32_t vocab, tree_attn_edges_t* out);
+int tree_attn_edges_destroy(tree_attn_edges_t edges);
+/* Device workspace bytes of the forward and backward for hidden size d. */
+size_t tree_attn_edge_loss_workspace_bytes(tree_attn_edges_t edges, int32_t hidden);
+/* loss, lse: [E] float32 outputs.  h: [num_tokens, d]; W: [vocab, d]. */
+int tree_attn_edge_loss_fwd(const void* hidden, const void* weight, int32_t hidden_dim, tree_attn_edges_t edges,
+                            float* loss, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+/* lse from the forward; dloss [E]; dhidden [num_tokens, d] and dweight
+ * [vocab, d] are overwritten. */
+int tree_attn_edge_loss_bwd(const void* hidden, const void* weight, int32_t hidden_dim, tree_attn_edges_t edges,
+                            const float* lse, const float* dloss, void* dhidden, void* dweight, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Copy one of the plan's host tables (int32 records) for inspection.
  *   which = TREE_ATTN_EXPORT_*; buf may be NULL to query *count;
  *   cap = capacity of buf in int32 elements; *count = elements available.

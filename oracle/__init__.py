@@ -28,3 +28,4 @@ from .tree_attention import (  # noqa: F401
     rel_l2,
 )
 from .fragments import fragment  # noqa: F401
+from .edge_loss import edge_logits, edge_loss_forward, edge_loss_backward  # noqa: F401

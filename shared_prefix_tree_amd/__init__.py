@@ -9,9 +9,12 @@ ABI in ``include/tree_attn.h``.  This package is the thin Python binding.
 from .binding import (  # noqa: F401
     BF16,
     FP32,
+    EdgePlan,
     Plan,
     TreeAttnError,
     bwd_workspace_bytes,
+    edge_loss_bwd,
+    edge_loss_fwd,
     fragment,
     library,
     tree_attn_bwd,

@@ -51,6 +51,11 @@ SYMBOLS = (
     "tree_attn_fragments_destroy",
     "tree_attn_fragments_info",
     "tree_attn_fragments_export",
+    "tree_attn_edges",
+    "tree_attn_edges_destroy",
+    "tree_attn_edge_loss_workspace_bytes",
+    "tree_attn_edge_loss_fwd",
+    "tree_attn_edge_loss_bwd",
 )
 
 FRAG_SEG_PTR = 0
@@ -150,6 +155,14 @@ def library():
                                                ctypes.POINTER(ctypes.c_int64)]
     for name in ("tree_attn_fragment", "tree_attn_fragments_destroy", "tree_attn_fragments_info",
                  "tree_attn_fragments_export"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.tree_attn_edges.argtypes = [i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(vp)]
+    lib.tree_attn_edges_destroy.argtypes = [vp]
+    lib.tree_attn_edge_loss_workspace_bytes.argtypes = [vp, ctypes.c_int32]
+    lib.tree_attn_edge_loss_workspace_bytes.restype = ctypes.c_size_t
+    lib.tree_attn_edge_loss_fwd.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.tree_attn_edge_loss_bwd.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    for name in ("tree_attn_edges", "tree_attn_edges_destroy", "tree_attn_edge_loss_fwd", "tree_attn_edge_loss_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     for name in ("tree_attn_plan", "tree_attn_plan_query_run", "tree_attn_plan_query_run_host",
                  "tree_attn_plan_host", "tree_attn_plan_destroy",
@@ -281,6 +294,96 @@ def fragment(parent, seg_start, seg_len, max_tokens):
             "owner": tables[FRAG_TOKEN_OWNER][tptr[f]:tptr[f + 1]],
         })
     return frags, inf.as_dict()
+
+
+class EdgePlan:
+    """Sampled edges (source token, sampled vocabulary index), grouped by
+    source and uploaded to the current device (``tree_attn_edges``)."""
+
+    def __init__(self, edge_src, edge_tgt, num_tokens, vocab):
+        lib = library()
+        self._handle = None
+        s, sp = _i32(edge_src)
+        t, tp = _i32(edge_tgt)
+        if len(s) != len(t):
+            raise ValueError("edge_src and edge_tgt must have the same length")
+        h = ctypes.c_void_p()
+        _check(lib.tree_attn_edges(sp, tp, ctypes.c_int32(len(s)), ctypes.c_int32(int(num_tokens)),
+                                   ctypes.c_int32(int(vocab)), ctypes.byref(h)))
+        self._handle = h
+        self.num_edges, self.num_tokens, self.vocab = len(s), int(num_tokens), int(vocab)
+
+    @property
+    def handle(self):
+        return self._handle
+
+    def workspace_bytes(self, hidden):
+        return int(library().tree_attn_edge_loss_workspace_bytes(self._handle, int(hidden)))
+
+    def close(self):
+        if self._handle is not None and _lib is not None:
+            _lib.tree_attn_edges_destroy(self._handle)
+        self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _edge_check(hidden, weight, edges):
+    import torch
+
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    T, d = hidden.shape
+    if T != edges.num_tokens or tuple(weight.shape) != (edges.vocab, d):
+        raise ValueError(f"expected hidden [{edges.num_tokens}, d] and weight [{edges.vocab}, d]")
+    for name, t in (("hidden", hidden), ("weight", weight)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    return d
+
+
+def edge_loss_fwd(hidden, weight, edges: EdgePlan, workspace=None, stream=None):
+    """Per-edge loss and log-sum-exp (``tree_attn_edge_loss_fwd``)."""
+    import torch
+
+    d = _edge_check(hidden, weight, edges)
+    dev = hidden.device
+    loss = torch.empty(edges.num_edges, dtype=torch.float32, device=dev)
+    lse = torch.empty_like(loss)
+    if workspace is None:
+        workspace = torch.empty(max(256, edges.workspace_bytes(d)), dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        _check(library().tree_attn_edge_loss_fwd(hidden.data_ptr(), weight.data_ptr(), d, edges.handle,
+                                                 loss.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                                                 workspace.numel(), ctypes.c_void_p(s.cuda_stream)))
+    return loss, lse
+
+
+def edge_loss_bwd(hidden, weight, edges: EdgePlan, lse, dloss, workspace=None, stream=None):
+    """Gradients (dhidden, dweight) of sum_e dloss[e] * loss[e]."""
+    import torch
+
+    d = _edge_check(hidden, weight, edges)
+    dev = hidden.device
+    for name, t in (("lse", lse), ("dloss", dloss)):
+        if t.dtype != torch.float32 or t.numel() != edges.num_edges or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of {edges.num_edges} elements")
+    dh = torch.empty_like(hidden)
+    dw = torch.empty_like(weight)
+    if workspace is None:
+        workspace = torch.empty(max(256, edges.workspace_bytes(d)), dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        _check(library().tree_attn_edge_loss_bwd(hidden.data_ptr(), weight.data_ptr(), d, edges.handle,
+                                                 lse.data_ptr(), dloss.data_ptr(), dh.data_ptr(), dw.data_ptr(),
+                                                 workspace.data_ptr(), workspace.numel(),
+                                                 ctypes.c_void_p(s.cuda_stream)))
+    return dh, dw
 
 
 def _shape(q, k, softmax_scale):

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "lib", "libtree_attn.so")
-SOURCES = ["plan.cpp", "fragments.cpp", "api.cpp", "fwd.hip", "bwd.hip"]
+SOURCES = ["plan.cpp", "fragments.cpp", "api.cpp", "fwd.hip", "bwd.hip", "edge_loss.hip"]
+LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -62,7 +63,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *LIBS], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -41,6 +41,9 @@ int hip_fail(const char* what, hipError_t e) {
 
 }  // namespace
 
+// the message store of tree_attn_last_error, for the other translation units
+int report_error(int code, const std::string& msg) { return fail(code, msg); }
+
 struct DevicePlan {
   int device = -1;
   void* block = nullptr;  // one allocation holding every table below

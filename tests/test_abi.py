@@ -199,3 +199,14 @@ def test_backward_stages_reject_null_inputs_before_launch():
     # with every pointer present the host-only plan is what is reported
     assert lib.tree_attn_bwd_rowstat(one, one, one, p.handle, ctypes.byref(shape), one, ws, None) == b.INVALID_ARGUMENT
     assert "host-only" in lib.tree_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("src,tgt,T,V,frag", [
+    ([0, 5], [1, 2], 5, 10, "edge 1 has source 5"),
+    ([0, 1], [1, 10], 5, 10, "edge 1 has source 1 / sampled token 10"),
+    ([0, -1], [1, 2], 5, 10, "edge 1"),
+    ([], [], 5, 10, "need >= 1 edge"),
+])
+def test_edge_plan_rejects_bad_edges_without_a_device(src, tgt, T, V, frag):
+    with pytest.raises(b.TreeAttnError, match=frag):
+        sp.EdgePlan(np.array(src, np.int32), np.array(tgt, np.int32), T, V)

@@ -301,3 +301,41 @@ def test_staged_backward_matches_one_call():
     torch.cuda.synchronize()
     for a, b_ in zip(ref, got):
         assert torch.equal(a, b_)
+
+
+def test_repeated_stages_reuse_their_work_counters():
+    """The dK/dV and dQ stages hand out work through counters in the
+    workspace and leave them zeroed: calling each stage again (without the
+    row-statistics stage that first zeroes them) gives bitwise the same
+    gradients."""
+    import ctypes
+
+    import shared_prefix_tree_amd.binding as b
+
+    sp = lib()
+    rng = np.random.default_rng(42)
+    topo = random_forest(rng, max_tokens=900, max_len=200, max_depth=4)
+    arrs = make_inputs(rng, topo.total_tokens, 8, 2, 128, "bf16")
+    t = {k: to_torch(v, "bf16", "cuda:0") for k, v in arrs.items()}
+    plan = sp.Plan.from_topology(topo)
+    out, lse = sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan)
+    ws = torch.empty(sp.bwd_workspace_bytes(plan, t["q"], t["k"]), dtype=torch.uint8, device="cuda:0")
+    dq, dk, dv = (torch.empty_like(t[n]) for n in ("q", "k", "v"))
+    sp.tree_attn_bwd_stages(t["q"], t["k"], t["v"], out, lse, t["dout"], plan, dq, dk, dv, ws)
+    ref = [x.clone() for x in (dq, dk, dv)]
+    lib_ = b.library()
+    shape = b._shape(t["q"], t["k"], 0.0)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    wsb = ctypes.c_size_t(ws.numel())
+    for _ in range(3):
+        for x in (dq, dk, dv):
+            x.fill_(7.0)
+        assert lib_.tree_attn_bwd_dkdv(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), lse.data_ptr(),
+                                       t["dout"].data_ptr(), plan.handle, ctypes.byref(shape), dk.data_ptr(),
+                                       dv.data_ptr(), ws.data_ptr(), wsb, stream) == b.OK
+        assert lib_.tree_attn_bwd_dq(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), lse.data_ptr(),
+                                     t["dout"].data_ptr(), plan.handle, ctypes.byref(shape), dq.data_ptr(),
+                                     ws.data_ptr(), wsb, stream) == b.OK
+        torch.cuda.synchronize()
+        for a, b_ in zip(ref, (dq, dk, dv)):
+            assert torch.equal(a, b_)

@@ -45,10 +45,11 @@ __all__ = [
     "bf16_to_f32",
     "f32_to_bf16",
     "CHUNK_TOKENS",
+    "sampled_edges",
 ]
 
 CHUNK_TOKENS = 256
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "dout": 3}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "dout": 3, "hidden": 4, "weight": 5}
 
 
 @dataclass
@@ -286,6 +287,31 @@ def random_forest(rng, max_tokens=64, max_len=9, max_depth=4, p_new_root=0.15) -
     if not nodes:
         nodes = [(-1, 1)]
     return _from_dfs_list(nodes)
+
+
+def sampled_edges(topo: Topology, rng, vocab, p_sampled=0.5):
+    """Sampled edges of a forest: (source token, sampled vocabulary id).
+
+    Each segment is a sampled (model-generated) part with probability
+    ``p_sampled``, else a prompt part.  Every token of a sampled segment is
+    a sampled action, predicted from the token before it in its sequence:
+    the previous token of the segment, or for the segment's first token the
+    last token of its parent (a root's first token has no source and is not
+    an edge).  A parent with several sampled children is thus the source of
+    several edges.  Sampled ids are uniform over the vocabulary.  Returns
+    int32 arrays (src, tgt), edges in token order."""
+    src = []
+    for s in range(topo.num_segments):
+        if rng.random() >= p_sampled:
+            continue
+        a, n = int(topo.seg_start[s]), int(topo.seg_len[s])
+        par = int(topo.parent[s])
+        if par >= 0:
+            src.append(int(topo.seg_start[par] + topo.seg_len[par] - 1))
+        src.extend(range(a, a + n - 1))
+    src = np.asarray(src, dtype=np.int32)
+    tgt = rng.integers(0, vocab, size=src.size, dtype=np.int64).astype(np.int32)
+    return src, tgt
 
 
 # ---------------------------------------------------------------------------
