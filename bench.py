@@ -217,8 +217,8 @@ def edge_loss(args):
     every segment sampled with probability 1/4 (each sampled token is an
     edge from the token before it), a 4096-wide hidden state and a
     131,072-word bf16 vocabulary head.  Algorithmic work: 2 E d V flops
-    forward (the logits GEMM), 6 E d V backward (logits again, dh, dW).
-    One JSON line."""
+    forward (the logits), 4 E d V backward (dh and dW); the backward's
+    recomputation of the logits is not counted.  One JSON line."""
     import numpy as np
     import torch
 
@@ -260,7 +260,7 @@ def edge_loss(args):
     wall = (time.perf_counter() - t0) / args.steps * 1e3
     f_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
     b_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
-    fwd_f, bwd_f = 2.0 * E * d * V, 6.0 * E * d * V
+    fwd_f, bwd_f = 2.0 * E * d * V, 4.0 * E * d * V
     tf = (fwd_f + bwd_f) / ((f_ms + b_ms) * 1e-3) / 1e12
     mean_loss = float(loss.double().mean())
     log(f"edge loss: fwd {f_ms:.3f} ms, bwd {b_ms:.3f} ms, {tf:.1f} TFLOP/s, mean loss {mean_loss:.4f} "

@@ -72,35 +72,68 @@ __global__ void gather_rows_kernel(const uint4* __restrict__ h, const int32_t* _
   hg[i] = h[(long long)src[e] * pieces + p];
 }
 
-// Running row statistics over one chunk: columns [c0, c0 + n) of the
-// vocabulary, logits[e, j] at L[e * ld + j].  One 256-thread block per edge;
-// a fixed reduction tree, so the result does not depend on scheduling.
-__device__ inline float block_reduce(float v, float* red, bool is_max) {
-  const int t = threadIdx.x;
-  red[t] = v;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) red[t] = is_max ? fmaxf(red[t], red[t + s]) : red[t] + red[t + s];
-    __syncthreads();
+// One 256-thread block per edge row of a chunk.  Thread t holds columns
+// 4 (t + 256 k) .. + 3 for k < kPer in registers, so a row is read from HBM
+// once; columns past n read as -inf.  Rows are 16-byte aligned when the
+// leading dimension is a multiple of 4 (every chunk but a vocabulary of
+// fewer than kVocabChunk rows that is not), else the loads are scalar.
+constexpr int kRowThreads = 256;
+constexpr int kPer = kVocabChunk / (4 * kRowThreads);
+
+__device__ inline void load_row(const float* __restrict__ row, int n, bool vec, float (&v)[kPer][4]) {
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int j = 4 * (threadIdx.x + kRowThreads * k);
+    if (vec && j + 3 < n) {
+      const float4 x = *reinterpret_cast<const float4*>(row + j);
+      v[k][0] = x.x, v[k][1] = x.y, v[k][2] = x.z, v[k][3] = x.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[k][c] = j + c < n ? row[j + c] : -INFINITY;
+    }
   }
-  const float r = red[0];
+}
+
+// fixed-order block reduction (shuffle tree inside a wave, then the four
+// wave results in order), so the result does not depend on scheduling
+__device__ inline float block_reduce(float v, float* red, bool is_max) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float u = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, u) : v + u;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))
+                         : (red[0] + red[1]) + (red[2] + red[3]);
   __syncthreads();
   return r;
 }
 
-__global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restrict__ L, int ld, int n, int c0,
-                                                          const int32_t* __restrict__ tgt, float* __restrict__ m,
-                                                          float* __restrict__ s, float* __restrict__ tl, int first) {
-  __shared__ float red[256];
+// Running row statistics over one chunk: columns [c0, c0 + n) of the
+// vocabulary, logits[e, j] at L[e * ld + j]
+__global__ __launch_bounds__(kRowThreads) void chunk_stats_kernel(const float* __restrict__ L, int ld, int n, int c0,
+                                                                  const int32_t* __restrict__ tgt,
+                                                                  float* __restrict__ m, float* __restrict__ s,
+                                                                  float* __restrict__ tl, int first) {
+  __shared__ float red[kRowThreads / 64];
   const int e = blockIdx.x;
   const float* row = L + (long long)e * ld;
+  float v[kPer][4];
+  load_row(row, n, (ld & 3) == 0, v);
   float mx = -INFINITY;
-  for (int j = threadIdx.x; j < n; j += 256) mx = fmaxf(mx, row[j]);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mx = fmaxf(mx, v[k][c]);
   mx = block_reduce(mx, red, true);
   const float m_old = first ? -INFINITY : m[e];
   const float m_new = fmaxf(m_old, mx);
   float acc = 0.f;
-  for (int j = threadIdx.x; j < n; j += 256) acc += __expf(row[j] - m_new);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc += __expf(v[k][c] - m_new);
   acc = block_reduce(acc, red, false);
   if (threadIdx.x == 0) {
     const float s_old = first ? 0.f : s[e] * __expf(m_old - m_new);
@@ -121,28 +154,61 @@ __global__ void finalize_kernel(const float* __restrict__ m, const float* __rest
   loss[e] = l - tl[e];
 }
 
-// G[e, j] = (exp(L[e, j] - lse[e]) - [c0 + j == tgt[e]]) dloss[e], bf16
-__global__ void chunk_grad_kernel(const float* __restrict__ L, int ld, int n, int c0, int E,
-                                  const int32_t* __restrict__ tgt, const float* __restrict__ lse,
-                                  const float* __restrict__ dloss, unsigned short* __restrict__ G) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)E * n) return;
-  const int e = int(i / n), j = int(i % n);
-  const float p = __expf(L[(long long)e * ld + j] - lse[e]);
-  const float g = (p - (c0 + j == tgt[e] ? 1.f : 0.f)) * dloss[e];
-  G[(long long)e * ld + j] = f32_to_bf16(g);
+// G[e, j] = (exp(L[e, j] - lse[e]) - [c0 + j == tgt[e]]) dloss[e], bf16; one
+// block per edge row, four columns per thread and step
+__global__ __launch_bounds__(kRowThreads) void chunk_grad_kernel(const float* __restrict__ L, int ld, int n, int c0,
+                                                                 const int32_t* __restrict__ tgt,
+                                                                 const float* __restrict__ lse,
+                                                                 const float* __restrict__ dloss,
+                                                                 unsigned short* __restrict__ G) {
+  const int e = blockIdx.x;
+  const float* row = L + (long long)e * ld;
+  unsigned short* grow = G + (long long)e * ld;
+  const float le = lse[e], dl = dloss[e];
+  const int t = tgt[e] - c0;
+  const bool vec = (ld & 3) == 0;
+  for (int j = 4 * threadIdx.x; j < n; j += 4 * kRowThreads) {
+    float x[4];
+    if (vec && j + 3 < n) {
+      const float4 q = *reinterpret_cast<const float4*>(row + j);
+      x[0] = q.x, x[1] = q.y, x[2] = q.z, x[3] = q.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = j + c < n ? row[j + c] : 0.f;
+    }
+    unsigned short g[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) g[c] = f32_to_bf16((__expf(x[c] - le) - (j + c == t ? 1.f : 0.f)) * dl);
+    if (vec && j + 3 < n) {
+      *reinterpret_cast<uint2*>(grow + j) =
+          make_uint2(unsigned(g[0]) | (unsigned(g[1]) << 16), unsigned(g[2]) | (unsigned(g[3]) << 16));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (j + c < n) grow[j + c] = g[c];
+    }
+  }
 }
 
-// dh[t] = sum of dhg over t's edges, in edge order; 0 for tokens without one
+// dh[t] = sum of dhg over t's edges, in edge order; 0 for tokens without
+// one.  One thread per 8 columns of a token row (d is a multiple of 8).
 __global__ void scatter_rows_kernel(const float* __restrict__ dhg, const int32_t* __restrict__ row_ptr,
-                                    const int32_t* __restrict__ ids, int T, int d,
-                                    unsigned short* __restrict__ dh) {
+                                    const int32_t* __restrict__ ids, int T, int d, uint4* __restrict__ dh) {
+  const int pieces = d / 8;
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)T * d) return;
-  const int t = int(i / d), c = int(i % d);
-  float acc = 0.f;
-  for (int k = row_ptr[t]; k < row_ptr[t + 1]; ++k) acc += dhg[(long long)ids[k] * d + c];
-  dh[i] = f32_to_bf16(acc);
+  if (i >= (long long)T * pieces) return;
+  const int t = int(i / pieces), c = int(i % pieces) * 8;
+  float acc[8] = {};
+  for (int k = row_ptr[t]; k < row_ptr[t + 1]; ++k) {
+    const float4* p = reinterpret_cast<const float4*>(dhg + (long long)ids[k] * d + c);
+    const float4 x = p[0], y = p[1];
+    acc[0] += x.x, acc[1] += x.y, acc[2] += x.z, acc[3] += x.w;
+    acc[4] += y.x, acc[5] += y.y, acc[6] += y.z, acc[7] += y.w;
+  }
+  unsigned u[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) u[q] = unsigned(f32_to_bf16(acc[2 * q])) | (unsigned(f32_to_bf16(acc[2 * q + 1])) << 16);
+  dh[i] = make_uint4(u[0], u[1], u[2], u[3]);
 }
 
 struct Handle {
@@ -336,7 +402,7 @@ int tree_attn_edge_loss_fwd(const void* hidden, const void* weight, int32_t d, t
     const int n = std::min(chunk, V - c0);
     if (rocblas_status st = chunk_logits(h, w, weight, E, d, c0, n, chunk); st != rocblas_status_success)
       return blas_error(fn, st);
-    hipLaunchKernelGGL(chunk_stats_kernel, dim3(E), dim3(256), 0, s, w.L, chunk, n, c0, edges->tgt, w.m, w.s,
+    hipLaunchKernelGGL(chunk_stats_kernel, dim3(E), dim3(kRowThreads), 0, s, w.L, chunk, n, c0, edges->tgt, w.m, w.s,
                        w.tl, c0 == 0 ? 1 : 0);
   }
   hipLaunchKernelGGL(finalize_kernel, dim3((E + 255) / 256), dim3(256), 0, s, w.m, w.s, w.tl, E, loss, lse);
@@ -367,8 +433,8 @@ int tree_attn_edge_loss_bwd(const void* hidden, const void* weight, int32_t d, t
     const int n = std::min(chunk, V - c0);
     if (rocblas_status st = chunk_logits(h, w, weight, E, d, c0, n, chunk); st != rocblas_status_success)
       return blas_error(fn, st);
-    hipLaunchKernelGGL(chunk_grad_kernel, dim3(unsigned((int64_t(E) * n + 255) / 256)), dim3(256), 0, s, w.L,
-                       chunk, n, c0, E, edges->tgt, lse, dloss, w.G);
+    hipLaunchKernelGGL(chunk_grad_kernel, dim3(E), dim3(kRowThreads), 0, s, w.L, chunk, n, c0, edges->tgt, lse,
+                       dloss, w.G);
     // dhg^T [d, E] (+)= W_c^T [d, n] G_c^T [n, E]   (column-major views)
     rocblas_status st = gemm(h, rocblas_operation_none, rocblas_operation_none, d, E, n,
                              static_cast<const unsigned short*>(weight) + size_t(c0) * d, d, w.G, chunk,
@@ -379,8 +445,8 @@ int tree_attn_edge_loss_bwd(const void* hidden, const void* weight, int32_t d, t
               static_cast<unsigned short*>(dweight) + size_t(c0) * d, rocblas_datatype_bf16_r, d);
     if (st != rocblas_status_success) return blas_error(fn, st);
   }
-  hipLaunchKernelGGL(scatter_rows_kernel, dim3(unsigned((int64_t(T) * d + 255) / 256)), dim3(256), 0, s, w.dhg,
-                     edges->row_ptr, edges->ids, T, d, static_cast<unsigned short*>(dhidden));
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3(unsigned((int64_t(T) * pieces + 255) / 256)), dim3(256), 0, s, w.dhg,
+                     edges->row_ptr, edges->ids, T, d, static_cast<uint4*>(dhidden));
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_error(fn, e);
   return TREE_ATTN_OK;
 }
