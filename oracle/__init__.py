@@ -29,3 +29,11 @@ from .tree_attention import (  # noqa: F401
 )
 from .fragments import fragment  # noqa: F401
 from .edge_loss import edge_logits, edge_loss_forward, edge_loss_backward  # noqa: F401
+from .mamba_tree import (  # noqa: F401
+    previous_token,
+    conv_forward,
+    conv_backward,
+    ssm_states,
+    ssm_forward,
+    ssm_backward,
+)
