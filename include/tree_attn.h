@@ -228,6 +228,79 @@ int tree_attn_edge_loss_bwd(const void* hidden, const void* weight, int32_t hidd
                             const float* lse, const float* dloss, void* dhidden, void* dweight, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/*
+ * Mamba state forking on the same forests (draft "feat(hybrid): add opt-in
+ * shared-prefix attention and Mamba execution", intro: the prompt head is
+ * shared, recurrent state forks into each branch, the convolution halo is
+ * handled per branch and backward accumulates the branches into the shared
+ * prefix; issue "Shared-prefix training with context parallelism for exact
+ * agent trajectories", section "Describe the solution you'd like": the
+ * convolution and recurrent state at branch points stay differentiable).
+ * prev(i) is the token before i on its root-to-leaf path: the previous token
+ * of its segment, or the parent segment's last token for a segment's first
+ * token, -1 at a root.  Two ops run along it (all tensors float32,
+ * row-major, on the plan's device):
+ *
+ * Depthwise causal convolution, x, y, dy, dx: [T, channels], weight
+ * [channels, width], bias [channels]:
+ *   y[i, c] = bias[c] + sum_{j < width} weight[c, j] x[prev^(width-1-j)(i), c]
+ * (terms past a root are zero).  channels a multiple of 4, width 1..4;
+ * x, y, dy, dx, bias 16-byte aligned.
+ *
+ * Selective state-space recurrence with a scalar decay per head (Mamba-2
+ * form), x, y: [T, H, 64]; dt: [T, H] (positive step sizes, after any
+ * softplus); A, D: [H]; B, C: [T, G, N]; head h reads group h / (H / G):
+ *   S_i = exp(dt[i,h] A[h]) S_prev(i) + dt[i,h] x[i,h,:] outer B[i,g,:],  S_-1 = 0
+ *   y[i,h,:] = S_i C[i,g,:] + D[h] x[i,h,:]
+ * N = state_dim is 64 or 128; B, C 16-byte aligned.
+ *
+ * tree_attn_mamba_plan validates the forest (same rules as tree_attn_plan),
+ * derives prev, the convolution halo and successor tables and the scan
+ * units (segments cut into units of at most unit_tokens tokens), and
+ * uploads them to the current device; _host builds the tables only (for
+ * inspection).  The plan is library-owned and immutable.
+ * Determinism: no atomics; results are bitwise reproducible.
+ * Errors: INVALID_ARGUMENT (NULL, malformed forest, small buffers, other
+ * device, host-only plan), UNSUPPORTED (shapes outside the above), HIP_ERROR.
+ */
+typedef struct tree_attn_mamba_plan_s* tree_attn_mamba_plan_t;
+typedef struct {
+  int32_t num_tokens, num_segments, num_units, unit_tokens, max_depth, max_conv_width;
+} tree_attn_mamba_plan_info_t;
+typedef struct {
+  int32_t num_heads, head_dim, num_groups, state_dim;
+} tree_attn_ssm_shape;
+int tree_attn_mamba_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                         int32_t num_segments, tree_attn_mamba_plan_t* out);
+int tree_attn_mamba_plan_host(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                              int32_t num_segments, tree_attn_mamba_plan_t* out);
+int tree_attn_mamba_plan_destroy(tree_attn_mamba_plan_t plan);
+int tree_attn_mamba_plan_info(tree_attn_mamba_plan_t plan, tree_attn_mamba_plan_info_t* info);
+/* Host tables, int32: PREV [T]; UNIT_START, UNIT_LEN, UNIT_PRED [num_units]
+ * (predecessor unit, -1 at a root).  buf NULL queries *count. */
+#define TREE_ATTN_MAMBA_PREV 0
+#define TREE_ATTN_MAMBA_UNIT_START 1
+#define TREE_ATTN_MAMBA_UNIT_LEN 2
+#define TREE_ATTN_MAMBA_UNIT_PRED 3
+int tree_attn_mamba_plan_export(tree_attn_mamba_plan_t plan, int32_t which, int32_t* buf, int64_t cap,
+                                int64_t* count);
+/* Convolution forward: writes y. */
+int tree_attn_conv_fwd(const float* x, const float* weight, const float* bias, int32_t channels, int32_t width,
+                       tree_attn_mamba_plan_t plan, float* y, void* stream);
+size_t tree_attn_conv_bwd_workspace_bytes(tree_attn_mamba_plan_t plan, int32_t channels, int32_t width);
+/* Convolution backward of sum <dy, y>: overwrites dx, dweight, dbias. */
+int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int32_t channels, int32_t width,
+                       tree_attn_mamba_plan_t plan, float* dx, float* dweight, float* dbias, void* workspace,
+                       size_t workspace_bytes, void* stream);
+/* Bytes of the saved states (the state before every unit, written by the
+ * forward for the backward) and of the forward's workspace. */
+size_t tree_attn_ssm_states_bytes(tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape);
+size_t tree_attn_ssm_workspace_bytes(tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape);
+/* Recurrence forward: writes y and the saved states. */
+int tree_attn_ssm_fwd(const float* x, const float* dt, const float* A, const float* B, const float* C,
+                      const float* D, tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape, float* y,
+                      float* states, size_t states_bytes, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Copy one of the plan's host tables (int32 records) for inspection.
  *   which = TREE_ATTN_EXPORT_*; buf may be NULL to query *count;
  *   cap = capacity of buf in int32 elements; *count = elements available.

@@ -10,13 +10,18 @@ from .binding import (  # noqa: F401
     BF16,
     FP32,
     EdgePlan,
+    MambaPlan,
     Plan,
     TreeAttnError,
     bwd_workspace_bytes,
+    conv_bwd,
+    conv_fwd,
     edge_loss_bwd,
     edge_loss_fwd,
     fragment,
     library,
+    ssm_fwd,
+    ssm_states_bytes,
     tree_attn_bwd,
     tree_attn_bwd_stages,
     tree_attn_fwd,

@@ -56,6 +56,17 @@ SYMBOLS = (
     "tree_attn_edge_loss_workspace_bytes",
     "tree_attn_edge_loss_fwd",
     "tree_attn_edge_loss_bwd",
+    "tree_attn_mamba_plan",
+    "tree_attn_mamba_plan_host",
+    "tree_attn_mamba_plan_destroy",
+    "tree_attn_mamba_plan_info",
+    "tree_attn_mamba_plan_export",
+    "tree_attn_conv_fwd",
+    "tree_attn_conv_bwd_workspace_bytes",
+    "tree_attn_conv_bwd",
+    "tree_attn_ssm_states_bytes",
+    "tree_attn_ssm_workspace_bytes",
+    "tree_attn_ssm_fwd",
 )
 
 FRAG_SEG_PTR = 0
@@ -116,6 +127,31 @@ class FragmentsInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class MambaPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("num_segments", ctypes.c_int32),
+        ("num_units", ctypes.c_int32),
+        ("unit_tokens", ctypes.c_int32),
+        ("max_depth", ctypes.c_int32),
+        ("max_conv_width", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class SsmShape(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("num_groups", ctypes.c_int32),
+        ("state_dim", ctypes.c_int32),
+    ]
+
+
+MAMBA_EXPORT = {"prev": 0, "unit_start": 1, "unit_len": 2, "unit_pred": 3}
+
 _lib = None
 
 
@@ -163,6 +199,26 @@ def library():
     lib.tree_attn_edge_loss_fwd.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.tree_attn_edge_loss_bwd.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     for name in ("tree_attn_edges", "tree_attn_edges_destroy", "tree_attn_edge_loss_fwd", "tree_attn_edge_loss_bwd"):
+        getattr(lib, name).restype = ctypes.c_int
+    for name in ("tree_attn_mamba_plan", "tree_attn_mamba_plan_host"):
+        getattr(lib, name).argtypes = [i32p, i32p, i32p, ctypes.c_int32, ctypes.POINTER(vp)]
+    lib.tree_attn_mamba_plan_destroy.argtypes = [vp]
+    lib.tree_attn_mamba_plan_info.argtypes = [vp, ctypes.POINTER(MambaPlanInfo)]
+    lib.tree_attn_mamba_plan_export.argtypes = [vp, ctypes.c_int32, i32p, ctypes.c_int64,
+                                                ctypes.POINTER(ctypes.c_int64)]
+    lib.tree_attn_conv_fwd.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+    lib.tree_attn_conv_bwd_workspace_bytes.argtypes = [vp, ctypes.c_int32, ctypes.c_int32]
+    lib.tree_attn_conv_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.tree_attn_conv_bwd.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp,
+                                       ctypes.c_size_t, vp]
+    for name in ("tree_attn_ssm_states_bytes", "tree_attn_ssm_workspace_bytes"):
+        getattr(lib, name).argtypes = [vp, ctypes.POINTER(SsmShape)]
+        getattr(lib, name).restype = ctypes.c_size_t
+    lib.tree_attn_ssm_fwd.argtypes = [vp] * 7 + [ctypes.POINTER(SsmShape), vp, vp, ctypes.c_size_t, vp,
+                                                 ctypes.c_size_t, vp]
+    for name in ("tree_attn_mamba_plan", "tree_attn_mamba_plan_host", "tree_attn_mamba_plan_destroy",
+                 "tree_attn_mamba_plan_info", "tree_attn_mamba_plan_export", "tree_attn_conv_fwd",
+                 "tree_attn_conv_bwd", "tree_attn_ssm_fwd"):
         getattr(lib, name).restype = ctypes.c_int
     for name in ("tree_attn_plan", "tree_attn_plan_query_run", "tree_attn_plan_query_run_host",
                  "tree_attn_plan_host", "tree_attn_plan_destroy",
@@ -384,6 +440,152 @@ def edge_loss_bwd(hidden, weight, edges: EdgePlan, lse, dloss, workspace=None, s
                                                  workspace.data_ptr(), workspace.numel(),
                                                  ctypes.c_void_p(s.cuda_stream)))
     return dh, dw
+
+
+class MambaPlan:
+    """Tables of the Mamba path for one forest (``tree_attn_mamba_plan``):
+    each token's predecessor, the convolution halo and the scan units.
+    ``device=False`` builds a host-only plan for inspection."""
+
+    def __init__(self, parent, seg_start, seg_len, device=True):
+        lib = library()
+        self._handle = None
+        p, pp = _i32(parent)
+        s, sp = _i32(seg_start)
+        n, np_ = _i32(seg_len)
+        if not (len(p) == len(s) == len(n)):
+            raise ValueError("parent, seg_start and seg_len must have the same length")
+        h = ctypes.c_void_p()
+        fn = lib.tree_attn_mamba_plan if device else lib.tree_attn_mamba_plan_host
+        _check(fn(pp, sp, np_, ctypes.c_int32(len(p)), ctypes.byref(h)))
+        self._handle = h
+        self.device = device
+
+    @classmethod
+    def from_topology(cls, topo, device=True):
+        return cls(topo.parent, topo.seg_start, topo.seg_len, device=device)
+
+    @property
+    def handle(self):
+        return self._handle
+
+    def info(self) -> dict:
+        info = MambaPlanInfo()
+        _check(library().tree_attn_mamba_plan_info(self._handle, ctypes.byref(info)))
+        return info.as_dict()
+
+    def export(self, which):
+        lib = library()
+        code = MAMBA_EXPORT[which]
+        count = ctypes.c_int64()
+        _check(lib.tree_attn_mamba_plan_export(self._handle, code, None, 0, ctypes.byref(count)))
+        buf = np.zeros(count.value, dtype=np.int32)
+        _check(lib.tree_attn_mamba_plan_export(self._handle, code, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                               count.value, ctypes.byref(count)))
+        return buf
+
+    def close(self):
+        if self._handle is not None and _lib is not None:
+            _lib.tree_attn_mamba_plan_destroy(self._handle)
+        self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _f32(name, t, shape=None):
+    import torch
+
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 CUDA tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _stream_of(t, stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def conv_fwd(x, weight, bias, plan: MambaPlan, out=None, stream=None):
+    """Tree-causal depthwise convolution (``tree_attn_conv_fwd``):
+    x [T, C], weight [C, W], bias [C] -> y [T, C]."""
+    import torch
+
+    T, C = x.shape
+    W = weight.shape[1]
+    _f32("x", x), _f32("weight", weight, (C, W)), _f32("bias", bias, (C,))
+    y = out if out is not None else torch.empty_like(x)
+    _f32("out", y, (T, C))
+    with torch.cuda.device(x.device):
+        _check(library().tree_attn_conv_fwd(x.data_ptr(), weight.data_ptr(), bias.data_ptr(), C, W, plan.handle,
+                                            y.data_ptr(), _stream_of(x, stream)))
+    return y
+
+
+def conv_bwd(x, weight, dy, plan: MambaPlan, workspace=None, stream=None):
+    """(dx, dweight, dbias) of sum <dy, y> (``tree_attn_conv_bwd``)."""
+    import torch
+
+    T, C = x.shape
+    W = weight.shape[1]
+    _f32("x", x), _f32("weight", weight, (C, W)), _f32("dy", dy, (T, C))
+    dx, dw, db = torch.empty_like(x), torch.empty_like(weight), torch.empty(C, dtype=torch.float32, device=x.device)
+    lib = library()
+    if workspace is None:
+        workspace = torch.empty(max(256, lib.tree_attn_conv_bwd_workspace_bytes(plan.handle, C, W)),
+                                dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib.tree_attn_conv_bwd(x.data_ptr(), weight.data_ptr(), dy.data_ptr(), C, W, plan.handle,
+                                      dx.data_ptr(), dw.data_ptr(), db.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel(), _stream_of(x, stream)))
+    return dx, dw, db
+
+
+def _ssm_shape(x, B):
+    T, H, P = x.shape
+    _, G, N = B.shape
+    return SsmShape(H, P, G, N)
+
+
+def ssm_states_bytes(plan: MambaPlan, num_heads, head_dim, num_groups, state_dim):
+    sh = SsmShape(num_heads, head_dim, num_groups, state_dim)
+    return int(library().tree_attn_ssm_states_bytes(plan.handle, ctypes.byref(sh)))
+
+
+def ssm_fwd(x, dt, A, B, C, D, plan: MambaPlan, out=None, states=None, workspace=None, stream=None):
+    """State-space recurrence along the forest (``tree_attn_ssm_fwd``):
+    returns y [T, H, P] and the saved states (uint8 device buffer) that the
+    backward reads."""
+    import torch
+
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    for name, t, shp in (("x", x, None), ("dt", dt, (T, H)), ("A", A, (H,)), ("B", B, (T, G, N)),
+                         ("C", C, (T, G, N)), ("D", D, (H,))):
+        _f32(name, t, shp)
+    sh = _ssm_shape(x, B)
+    lib = library()
+    y = out if out is not None else torch.empty_like(x)
+    _f32("out", y, (T, H, P))
+    nst = lib.tree_attn_ssm_states_bytes(plan.handle, ctypes.byref(sh))
+    if states is None:
+        states = torch.empty(max(256, nst), dtype=torch.uint8, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(256, lib.tree_attn_ssm_workspace_bytes(plan.handle, ctypes.byref(sh))),
+                                dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib.tree_attn_ssm_fwd(x.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(),
+                                     D.data_ptr(), plan.handle, ctypes.byref(sh), y.data_ptr(), states.data_ptr(),
+                                     states.numel(), workspace.data_ptr(), workspace.numel(),
+                                     _stream_of(x, stream)))
+    return y, states
 
 
 def _shape(q, k, softmax_scale):

@@ -1,0 +1,580 @@
+// Mamba state forking on a shared-prefix forest: the tree-causal depthwise
+// convolution and the scalar-decay state-space recurrence of a Mamba-2
+// mixer, run along each token's ancestor path.
+//
+// The draft "feat(hybrid): add opt-in shared-prefix attention and Mamba
+// execution" (intro) shares the prompt once, forks the recurrent state into
+// each branch, runs the convolution halo per branch and accumulates the
+// branches' gradients into the shared prefix; the issue "Shared-prefix
+// training with context parallelism for exact agent trajectories" (section
+// "Describe the solution you'd like") keeps convolution and recurrent state
+// at branch points differentiable.  With prev(i) the token before i on its
+// root-to-leaf path (the previous token of its segment, or the parent
+// segment's last token for a segment's first token, none at a root):
+//
+//   conv:  y[i, c] = bias[c] + sum_{j < W} w[c, j] x[prev^(W-1-j)(i), c]
+//   scan:  S_i = exp(dt[i,h] A[h]) S_prev(i) + dt[i,h] x[i,h,:] outer B[i,g,:]
+//          y[i,h,:] = S_i C[i,g,:] + D[h] x[i,h,:]          (g = h / (H / G))
+//
+// Scan decomposition.  The plan cuts every segment into units of at most
+// kUnit tokens; a unit's predecessor is the previous unit of its segment or
+// the parent segment's last unit, so the units form a tree in DFS order.
+// The state after a unit is linear in the state before it:
+//   end(u) = decay(u) start(u) + local(u),  decay(u) = exp(A sum_{i in u} dt_i)
+// 1. local:     per (unit, head), scan the unit from a zero state -> local(u),
+//               decay(u)   (all units in parallel);
+// 2. propagate: per (head, quarter of the state), walk the units in DFS
+//               order: start(u) = end(pred(u)); a fork reads its parent's
+//               start and local back (each thread reads what it wrote);
+// 3. output:    per (unit, head), scan again from start(u) and write y.
+// start(u) is kept for the backward pass.  The state of one head (64 x N
+// floats) is spread over a 256-thread block: thread (p, q) holds row p,
+// columns [q N/4, (q+1) N/4); y's sum over the state dimension is a
+// four-lane reduction.  Everything is fp32 with no atomics: results are
+// bitwise reproducible.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/tree_attn.h"
+#include "plan.hpp"
+
+namespace tree_attn {
+int report_error(int code, const std::string& msg);
+}
+
+using tree_attn::report_error;
+
+namespace {
+
+constexpr int kUnit = 128;         // tokens per scan unit
+constexpr int kConvMaxWidth = 4;   // convolution widths 1..4
+constexpr int kHalo = kConvMaxWidth - 1;
+constexpr int kHeadDim = 64;       // P
+
+}  // namespace
+
+struct tree_attn_mamba_plan_s {
+  int device = -1;  // -1: host-only plan
+  int32_t T = 0, S = 0, U = 0, max_depth = 0;
+  std::vector<int32_t> prev;                    // [T]
+  std::vector<int32_t> halo;                    // [T][kHalo]: prev^1 .. prev^kHalo (-1: none)
+  std::vector<int32_t> csucc_ptr, csucc;        // token j -> entries 4 i + k with prev^k(i) = j, k = 1..kHalo
+  std::vector<int32_t> unit_start, unit_len, unit_pred;  // [U]
+  std::vector<int32_t> usucc_ptr, usucc;        // unit u -> units v with pred(v) = u, ascending
+  void* block = nullptr;
+  const int32_t *d_halo = nullptr, *d_csucc_ptr = nullptr, *d_csucc = nullptr;
+  const int32_t *d_unit_start = nullptr, *d_unit_len = nullptr, *d_unit_pred = nullptr;
+  const int32_t *d_usucc_ptr = nullptr, *d_usucc = nullptr;
+};
+
+namespace {
+
+bool build_mamba_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len, int32_t S,
+                      tree_attn_mamba_plan_s& m, std::string& err) {
+  tree_attn::HostPlan hp;  // validation of the DFS forest (same rules as the attention plan)
+  if (!tree_attn::build_host_plan(parent, seg_start, seg_len, S, 0, -1, hp, err)) return false;
+  const int32_t T = hp.T;
+  m.T = T;
+  m.S = S;
+  m.max_depth = hp.max_depth;
+  m.prev.resize(T);
+  for (int32_t i = 0; i < T; ++i) m.prev[i] = i - 1;
+  for (int32_t s = 0; s < S; ++s)
+    m.prev[seg_start[s]] = parent[s] < 0 ? -1 : seg_start[parent[s]] + seg_len[parent[s]] - 1;
+  m.halo.assign(size_t(T) * kHalo, -1);
+  std::vector<int32_t> count(size_t(T) + 1, 0);
+  for (int32_t i = 0; i < T; ++i) {
+    int32_t j = i;
+    for (int k = 1; k <= kHalo; ++k) {
+      j = j < 0 ? -1 : m.prev[j];
+      m.halo[size_t(i) * kHalo + k - 1] = j;
+      if (j >= 0) ++count[size_t(j) + 1];
+    }
+  }
+  for (int32_t t = 0; t < T; ++t) count[t + 1] += count[t];
+  m.csucc_ptr = count;
+  m.csucc.resize(count[T]);
+  std::vector<int32_t> fill(count.begin(), count.end() - 1);
+  // entries of a token in (k, i) order: for each k, successors ascending
+  for (int k = 1; k <= kHalo; ++k)
+    for (int32_t i = 0; i < T; ++i) {
+      const int32_t j = m.halo[size_t(i) * kHalo + k - 1];
+      if (j >= 0) m.csucc[fill[j]++] = 4 * i + k;
+    }
+  // units
+  std::vector<int32_t> last_unit(S, -1);
+  for (int32_t s = 0; s < S; ++s) {
+    for (int32_t off = 0; off < seg_len[s]; off += kUnit) {
+      const int32_t u = int32_t(m.unit_start.size());
+      m.unit_start.push_back(seg_start[s] + off);
+      m.unit_len.push_back(std::min(kUnit, seg_len[s] - off));
+      m.unit_pred.push_back(off > 0 ? u - 1 : parent[s] < 0 ? -1 : last_unit[parent[s]]);
+      last_unit[s] = u;
+    }
+  }
+  m.U = int32_t(m.unit_start.size());
+  m.usucc_ptr.assign(size_t(m.U) + 1, 0);
+  for (int32_t u = 0; u < m.U; ++u)
+    if (m.unit_pred[u] >= 0) ++m.usucc_ptr[size_t(m.unit_pred[u]) + 1];
+  for (int32_t u = 0; u < m.U; ++u) m.usucc_ptr[u + 1] += m.usucc_ptr[u];
+  m.usucc.resize(m.usucc_ptr[m.U]);
+  std::vector<int32_t> uf(m.usucc_ptr.begin(), m.usucc_ptr.end() - 1);
+  for (int32_t u = 0; u < m.U; ++u)
+    if (m.unit_pred[u] >= 0) m.usucc[uf[m.unit_pred[u]]++] = u;
+  return true;
+}
+
+hipError_t upload_mamba_plan(tree_attn_mamba_plan_s& m) {
+  const std::vector<int32_t>* parts[] = {&m.halo,     &m.csucc_ptr, &m.csucc,     &m.unit_start,
+                                         &m.unit_len, &m.unit_pred, &m.usucc_ptr, &m.usucc};
+  size_t off[8], total = 0;
+  for (int k = 0; k < 8; ++k) {
+    off[k] = total;
+    total += (parts[k]->size() * 4 + 255) & ~size_t(255);
+  }
+  std::vector<char> stage(std::max<size_t>(total, 256), 0);
+  for (int k = 0; k < 8; ++k)
+    if (!parts[k]->empty()) std::memcpy(stage.data() + off[k], parts[k]->data(), parts[k]->size() * 4);
+  hipError_t e = hipGetDevice(&m.device);
+  if (e == hipSuccess) e = hipMalloc(&m.block, stage.size());
+  if (e == hipSuccess) e = hipMemcpy(m.block, stage.data(), stage.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return e;
+  const int32_t** dst[] = {&m.d_halo,     &m.d_csucc_ptr, &m.d_csucc,     &m.d_unit_start,
+                           &m.d_unit_len, &m.d_unit_pred, &m.d_usucc_ptr, &m.d_usucc};
+  for (int k = 0; k < 8; ++k) *dst[k] = reinterpret_cast<const int32_t*>(static_cast<char*>(m.block) + off[k]);
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// convolution
+
+// one thread per (token, 4 channels)
+__global__ void conv_fwd_kernel(const float4* __restrict__ x, const float* __restrict__ w,
+                                const float4* __restrict__ bias, const int32_t* __restrict__ halo, int T, int C4,
+                                int W, float4* __restrict__ y) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)T * C4) return;
+  const int i = int(idx / C4), c4 = int(idx % C4), c = 4 * c4;
+  float4 acc = bias[c4];
+  for (int k = 0; k < W; ++k) {  // k steps back along the path
+    const int src = k == 0 ? i : halo[(long long)i * kHalo + k - 1];
+    if (src < 0) break;
+    const float4 v = x[(long long)src * C4 + c4];
+    const int j = W - 1 - k;
+    acc.x = fmaf(w[(c + 0) * W + j], v.x, acc.x);
+    acc.y = fmaf(w[(c + 1) * W + j], v.y, acc.y);
+    acc.z = fmaf(w[(c + 2) * W + j], v.z, acc.z);
+    acc.w = fmaf(w[(c + 3) * W + j], v.w, acc.w);
+  }
+  y[idx] = acc;
+}
+
+// dx[j] = w[:, W-1] dy[j] + sum over tokens i with prev^k(i) = j, 1 <= k < W,
+// of w[:, W-1-k] dy[i]; every branch's halo lands on the shared prefix
+__global__ void conv_bwd_dx_kernel(const float4* __restrict__ dy, const float* __restrict__ w,
+                                   const int32_t* __restrict__ csucc_ptr, const int32_t* __restrict__ csucc, int T,
+                                   int C4, int W, float4* __restrict__ dx) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)T * C4) return;
+  const int j = int(idx / C4), c4 = int(idx % C4), c = 4 * c4;
+  const float4 g = dy[idx];
+  float4 acc = make_float4(w[(c + 0) * W + W - 1] * g.x, w[(c + 1) * W + W - 1] * g.y, w[(c + 2) * W + W - 1] * g.z,
+                           w[(c + 3) * W + W - 1] * g.w);
+  for (int e = csucc_ptr[j]; e < csucc_ptr[j + 1]; ++e) {
+    const int ent = csucc[e], i = ent >> 2, k = ent & 3;
+    if (k >= W) continue;
+    const float4 v = dy[(long long)i * C4 + c4];
+    const int wj = W - 1 - k;
+    acc.x = fmaf(w[(c + 0) * W + wj], v.x, acc.x);
+    acc.y = fmaf(w[(c + 1) * W + wj], v.y, acc.y);
+    acc.z = fmaf(w[(c + 2) * W + wj], v.z, acc.z);
+    acc.w = fmaf(w[(c + 3) * W + wj], v.w, acc.w);
+  }
+  dx[idx] = acc;
+}
+
+constexpr int kConvRows = 256;  // tokens per partial of the weight gradient
+
+// partial[b][c][0..W-1] = sum over tokens of block b of dy[i, c] x[prev^(W-1-j)(i), c],
+// partial[b][c][W] = sum of dy[i, c]; one thread per channel
+__global__ void conv_bwd_dw_partial_kernel(const float* __restrict__ x, const float* __restrict__ dy,
+                                           const int32_t* __restrict__ halo, int T, int C, int W,
+                                           float* __restrict__ partial) {
+  const int c = blockIdx.y * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  const int i0 = blockIdx.x * kConvRows, i1 = min(T, i0 + kConvRows);
+  float acc[kConvMaxWidth + 1] = {};
+  for (int i = i0; i < i1; ++i) {
+    const float g = dy[(long long)i * C + c];
+    acc[kConvMaxWidth] += g;
+#pragma unroll
+    for (int k = 0; k < kConvMaxWidth; ++k) {
+      if (k >= W) break;
+      const int src = k == 0 ? i : halo[(long long)i * kHalo + k - 1];
+      if (src < 0) break;
+      acc[k] = fmaf(g, x[(long long)src * C + c], acc[k]);
+    }
+  }
+  float* out = partial + ((long long)blockIdx.x * C + c) * (kConvMaxWidth + 1);
+#pragma unroll
+  for (int k = 0; k <= kConvMaxWidth; ++k) out[k] = acc[k];
+}
+
+// dw[c][W-1-k] and dbias[c]: the partials summed in block order
+__global__ void conv_bwd_dw_reduce_kernel(const float* __restrict__ partial, int nblk, int C, int W,
+                                          float* __restrict__ dw, float* __restrict__ dbias) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  float acc[kConvMaxWidth + 1] = {};
+  for (int b = 0; b < nblk; ++b) {
+    const float* p = partial + ((long long)b * C + c) * (kConvMaxWidth + 1);
+#pragma unroll
+    for (int k = 0; k <= kConvMaxWidth; ++k) acc[k] += p[k];
+  }
+  for (int k = 0; k < W; ++k) dw[c * W + (W - 1 - k)] = acc[k];
+  dbias[c] = acc[kConvMaxWidth];
+}
+
+// ---------------------------------------------------------------------------
+// state-space scan
+
+struct ScanArgs {
+  const float *x, *dt, *A, *B, *C, *D;
+  const int32_t *unit_start, *unit_len, *unit_pred;
+  int H, G, U;
+  float* y;
+  float* states;  // [U][H][P][N] state before each unit
+  float* local;   // [U][H][P][N] unit scanned from a zero state
+  float* decay;   // [U][H]
+};
+
+template <int N>
+__device__ inline void load_row(const float* __restrict__ p, float (&v)[N / 4]) {
+#pragma unroll
+  for (int k = 0; k < N / 16; ++k) {
+    const float4 t = reinterpret_cast<const float4*>(p)[k];
+    v[4 * k] = t.x, v[4 * k + 1] = t.y, v[4 * k + 2] = t.z, v[4 * k + 3] = t.w;
+  }
+}
+
+template <int N>
+__device__ inline void store_row(float* __restrict__ p, const float (&v)[N / 4]) {
+#pragma unroll
+  for (int k = 0; k < N / 16; ++k)
+    reinterpret_cast<float4*>(p)[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+}
+
+// one block per (unit, head); thread (p, q) holds S[p][q N/4 .. (q+1) N/4)
+template <int N, bool kOutput>
+__global__ __launch_bounds__(256) void ssm_scan_kernel(ScanArgs a) {
+  constexpr int NE = N / 4;
+  const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int g = h / (a.H / a.G);
+  const int p = threadIdx.x >> 2, q = threadIdx.x & 3;
+  const int t0 = a.unit_start[u], n = a.unit_len[u];
+  const size_t srow = ((size_t(u) * a.H + h) * kHeadDim + p) * N + q * NE;
+  float S[NE];
+  if (kOutput) {
+    load_row<N>(a.states + srow, S);
+  } else {
+#pragma unroll
+    for (int k = 0; k < NE; ++k) S[k] = 0.f;
+  }
+  const float Ah = a.A[h], Dh = a.D[h];
+  float dsum = 0.f;
+  for (int t = t0; t < t0 + n; ++t) {
+    const float d = a.dt[(size_t)t * a.H + h];
+    const float xp = a.x[((size_t)t * a.H + h) * kHeadDim + p];
+    float b[NE];
+    load_row<N>(a.B + ((size_t)t * a.G + g) * N + q * NE, b);
+    const float decay = __expf(d * Ah), ux = d * xp;
+#pragma unroll
+    for (int k = 0; k < NE; ++k) S[k] = fmaf(ux, b[k], decay * S[k]);
+    dsum += d;
+    if (kOutput) {
+      float c[NE];
+      load_row<N>(a.C + ((size_t)t * a.G + g) * N + q * NE, c);
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < NE; ++k) acc = fmaf(S[k], c[k], acc);
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      if (q == 0) a.y[((size_t)t * a.H + h) * kHeadDim + p] = fmaf(Dh, xp, acc);
+    }
+  }
+  if (!kOutput) {
+    store_row<N>(a.local + srow, S);
+    if (threadIdx.x == 0) a.decay[(size_t)u * a.H + h] = __expf(Ah * dsum);
+  }
+}
+
+// one block per (head, quarter of the rows); thread holds row p, columns
+// [c NE2, (c+1) NE2); walks the units in DFS order
+template <int N>
+__global__ __launch_bounds__(256) void ssm_propagate_kernel(ScanArgs a) {
+  constexpr int NE2 = N / 16;
+  const int h = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  const int p = quarter * 16 + (threadIdx.x >> 4), c = threadIdx.x & 15;
+  const size_t col = size_t(p) * N + c * NE2;
+  const size_t ustride = size_t(a.H) * kHeadDim * N;
+  const size_t hoff = size_t(h) * kHeadDim * N + col;
+  float end[NE2];
+#pragma unroll
+  for (int k = 0; k < NE2; ++k) end[k] = 0.f;
+  for (int u = 0; u < a.U; ++u) {
+    const int pred = a.unit_pred[u];
+    float start[NE2];
+    if (pred < 0) {
+#pragma unroll
+      for (int k = 0; k < NE2; ++k) start[k] = 0.f;
+    } else if (pred == u - 1) {
+#pragma unroll
+      for (int k = 0; k < NE2; ++k) start[k] = end[k];
+    } else {  // a fork: the parent's end, from what this thread stored
+      const float dp = a.decay[(size_t)pred * a.H + h];
+      const float* sp = a.states + pred * ustride + hoff;
+      const float* lp = a.local + pred * ustride + hoff;
+#pragma unroll
+      for (int k = 0; k < NE2; ++k) start[k] = fmaf(dp, sp[k], lp[k]);
+    }
+    float* out = a.states + u * ustride + hoff;
+#pragma unroll
+    for (int k = 0; k < NE2; ++k) out[k] = start[k];
+    const float du = a.decay[(size_t)u * a.H + h];
+    const float* lu = a.local + u * ustride + hoff;
+#pragma unroll
+    for (int k = 0; k < NE2; ++k) end[k] = fmaf(du, start[k], lu[k]);
+  }
+}
+
+template <int N>
+hipError_t launch_ssm_fwd(const ScanArgs& a, hipStream_t s) {
+  const dim3 grid(unsigned(a.U) * unsigned(a.H));
+  hipLaunchKernelGGL((ssm_scan_kernel<N, false>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((ssm_propagate_kernel<N>), dim3(unsigned(a.H) * 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((ssm_scan_kernel<N, true>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_plan(const char* fn, tree_attn_mamba_plan_t plan) {
+  if (!plan) return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": plan is NULL");
+  if (plan->device < 0)
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": plan was built host-only");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": plan was built on another device");
+  return TREE_ATTN_OK;
+}
+
+int check_ssm_shape(const char* fn, const tree_attn_ssm_shape* sh) {
+  const std::string f(fn);
+  if (!sh) return report_error(TREE_ATTN_INVALID_ARGUMENT, f + ": shape is NULL");
+  if (sh->num_heads < 1 || sh->num_groups < 1 || sh->num_heads % sh->num_groups != 0)
+    return report_error(TREE_ATTN_UNSUPPORTED, f + ": num_heads must be a positive multiple of num_groups");
+  if (sh->head_dim != kHeadDim)
+    return report_error(TREE_ATTN_UNSUPPORTED, f + ": head_dim must be 64");
+  if (sh->state_dim != 64 && sh->state_dim != 128)
+    return report_error(TREE_ATTN_UNSUPPORTED, f + ": state_dim must be 64 or 128");
+  return TREE_ATTN_OK;
+}
+
+size_t state_floats(const tree_attn_mamba_plan_s* p, const tree_attn_ssm_shape* sh) {
+  return size_t(p->U) * sh->num_heads * sh->head_dim * sh->state_dim;
+}
+
+int hip_error(const char* fn, hipError_t e) {
+  return report_error(TREE_ATTN_HIP_ERROR, std::string(fn) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+static int mamba_plan_impl(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                           int32_t num_segments, bool upload, tree_attn_mamba_plan_t* out, const char* fn) {
+  if (!out) return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": out is NULL");
+  *out = nullptr;
+  if (!parent || !seg_start || !seg_len)
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL topology array");
+  auto* m = new tree_attn_mamba_plan_s();
+  std::string err;
+  if (!build_mamba_plan(parent, seg_start, seg_len, num_segments, *m, err)) {
+    delete m;
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": " + err);
+  }
+  if (upload) {
+    if (hipError_t e = upload_mamba_plan(*m); e != hipSuccess) {
+      if (m->block) (void)hipFree(m->block);
+      delete m;
+      return hip_error(fn, e);
+    }
+  }
+  *out = m;
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_mamba_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                         int32_t num_segments, tree_attn_mamba_plan_t* out) {
+  return mamba_plan_impl(parent, seg_start, seg_len, num_segments, true, out, "tree_attn_mamba_plan");
+}
+
+int tree_attn_mamba_plan_host(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                              int32_t num_segments, tree_attn_mamba_plan_t* out) {
+  return mamba_plan_impl(parent, seg_start, seg_len, num_segments, false, out, "tree_attn_mamba_plan_host");
+}
+
+int tree_attn_mamba_plan_destroy(tree_attn_mamba_plan_t plan) {
+  if (!plan) return TREE_ATTN_OK;
+  if (plan->block) {
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(plan->device);
+    (void)hipFree(plan->block);
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+  delete plan;
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_mamba_plan_info(tree_attn_mamba_plan_t plan, tree_attn_mamba_plan_info_t* info) {
+  if (!plan || !info) return report_error(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_mamba_plan_info: NULL argument");
+  info->num_tokens = plan->T;
+  info->num_segments = plan->S;
+  info->num_units = plan->U;
+  info->unit_tokens = kUnit;
+  info->max_depth = plan->max_depth;
+  info->max_conv_width = kConvMaxWidth;
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_mamba_plan_export(tree_attn_mamba_plan_t plan, int32_t which, int32_t* buf, int64_t cap,
+                                int64_t* count) {
+  if (!plan || !count)
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_mamba_plan_export: NULL argument");
+  const std::vector<int32_t>* v = nullptr;
+  switch (which) {
+    case TREE_ATTN_MAMBA_PREV: v = &plan->prev; break;
+    case TREE_ATTN_MAMBA_UNIT_START: v = &plan->unit_start; break;
+    case TREE_ATTN_MAMBA_UNIT_LEN: v = &plan->unit_len; break;
+    case TREE_ATTN_MAMBA_UNIT_PRED: v = &plan->unit_pred; break;
+    default: return report_error(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_mamba_plan_export: unknown table");
+  }
+  *count = int64_t(v->size());
+  if (buf) {
+    if (cap < *count) return report_error(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_mamba_plan_export: buffer too small");
+    std::memcpy(buf, v->data(), v->size() * 4);
+  }
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_conv_fwd(const float* x, const float* weight, const float* bias, int32_t channels, int32_t width,
+                       tree_attn_mamba_plan_t plan, float* y, void* stream) {
+  const char* fn = "tree_attn_conv_fwd";
+  if (int rc = check_plan(fn, plan)) return rc;
+  if (!x || !weight || !bias || !y) return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL pointer");
+  if (channels < 4 || channels % 4 != 0)
+    return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": channels must be a positive multiple of 4");
+  if (width < 1 || width > kConvMaxWidth)
+    return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": width must be 1..4");
+  if (!aligned16(x) || !aligned16(bias) || !aligned16(y))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": x, bias and y must be 16-byte aligned");
+  const int C4 = channels / 4;
+  const long long n = (long long)plan->T * C4;
+  hipLaunchKernelGGL(conv_fwd_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), reinterpret_cast<const float4*>(x), weight,
+                     reinterpret_cast<const float4*>(bias), plan->d_halo, plan->T, C4, width,
+                     reinterpret_cast<float4*>(y));
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_error(fn, e);
+  return TREE_ATTN_OK;
+}
+
+size_t tree_attn_conv_bwd_workspace_bytes(tree_attn_mamba_plan_t plan, int32_t channels, int32_t width) {
+  (void)width;
+  if (!plan || channels < 1) return 0;
+  const size_t nblk = (size_t(plan->T) + kConvRows - 1) / kConvRows;
+  return align256(nblk * size_t(channels) * (kConvMaxWidth + 1) * 4);
+}
+
+int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int32_t channels, int32_t width,
+                       tree_attn_mamba_plan_t plan, float* dx, float* dweight, float* dbias, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  const char* fn = "tree_attn_conv_bwd";
+  if (int rc = check_plan(fn, plan)) return rc;
+  if (!x || !weight || !dy || !dx || !dweight || !dbias || !workspace)
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL pointer");
+  if (channels < 4 || channels % 4 != 0)
+    return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": channels must be a positive multiple of 4");
+  if (width < 1 || width > kConvMaxWidth)
+    return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": width must be 1..4");
+  if (!aligned16(dy) || !aligned16(dx))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": dy and dx must be 16-byte aligned");
+  const size_t need = tree_attn_conv_bwd_workspace_bytes(plan, channels, width);
+  if (workspace_bytes < need)
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": workspace " +
+                                                        std::to_string(workspace_bytes) + " bytes < required " +
+                                                        std::to_string(need));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int C4 = channels / 4, T = plan->T;
+  const long long n = (long long)T * C4;
+  hipLaunchKernelGGL(conv_bwd_dx_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(dy), weight, plan->d_csucc_ptr, plan->d_csucc, T, C4, width,
+                     reinterpret_cast<float4*>(dx));
+  const int nblk = (T + kConvRows - 1) / kConvRows;
+  float* partial = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(conv_bwd_dw_partial_kernel, dim3(unsigned(nblk), unsigned((channels + 63) / 64)), dim3(64), 0,
+                     s, x, dy, plan->d_halo, T, channels, width, partial);
+  hipLaunchKernelGGL(conv_bwd_dw_reduce_kernel, dim3(unsigned((channels + 255) / 256)), dim3(256), 0, s, partial,
+                     nblk, channels, width, dweight, dbias);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_error(fn, e);
+  return TREE_ATTN_OK;
+}
+
+size_t tree_attn_ssm_states_bytes(tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape) {
+  if (!plan || !shape || shape->num_heads < 1 || shape->head_dim < 1 || shape->state_dim < 1) return 0;
+  return align256(state_floats(plan, shape) * 4);
+}
+
+size_t tree_attn_ssm_workspace_bytes(tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape) {
+  if (!plan || !shape || shape->num_heads < 1 || shape->head_dim < 1 || shape->state_dim < 1) return 0;
+  return align256(state_floats(plan, shape) * 4) + align256(size_t(plan->U) * shape->num_heads * 4);
+}
+
+int tree_attn_ssm_fwd(const float* x, const float* dt, const float* A, const float* B, const float* C,
+                      const float* D, tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape, float* y,
+                      float* states, size_t states_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "tree_attn_ssm_fwd";
+  if (int rc = check_plan(fn, plan)) return rc;
+  if (int rc = check_ssm_shape(fn, shape)) return rc;
+  if (!x || !dt || !A || !B || !C || !D || !y || !states || !workspace)
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL pointer");
+  if (!aligned16(B) || !aligned16(C) || !aligned16(states) || !aligned16(workspace))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": B, C, states and workspace must be 16-byte aligned");
+  if (states_bytes < tree_attn_ssm_states_bytes(plan, shape))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": states buffer too small");
+  if (workspace_bytes < tree_attn_ssm_workspace_bytes(plan, shape))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": workspace too small");
+  if ((long long)plan->U * shape->num_heads >= (1LL << 31))
+    return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": too many units x heads");
+  ScanArgs a{};
+  a.x = x, a.dt = dt, a.A = A, a.B = B, a.C = C, a.D = D;
+  a.unit_start = plan->d_unit_start, a.unit_len = plan->d_unit_len, a.unit_pred = plan->d_unit_pred;
+  a.H = shape->num_heads, a.G = shape->num_groups, a.U = plan->U;
+  a.y = y;
+  a.states = states;
+  a.local = static_cast<float*>(workspace);
+  a.decay = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(state_floats(plan, shape) * 4));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = shape->state_dim == 128 ? launch_ssm_fwd<128>(a, s) : launch_ssm_fwd<64>(a, s);
+  if (e != hipSuccess) return hip_error(fn, e);
+  return TREE_ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+"""GPU: Mamba state forking (tree-causal convolution and state-space
+recurrence) against the float64 oracle.
+
+Draft "feat(hybrid): add opt-in shared-prefix attention and Mamba
+execution" (intro): the recurrent state forks into each branch, the
+convolution halo runs per branch, and backward accumulates the branches into
+the shared prefix.  Everything is float32; the bound is the float32 one of
+the attention path (rel-L2 1e-5; the pages' own float32 tree comparisons of
+the Mamba path were within about 1.2e-5).  Two runs are bitwise equal.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity_util import log, rel_l2
+from workloads import mamba_tensors, random_forest, tiny_tree
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def dev_tensors(d, dev):
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in d.items()}
+
+
+def forests():
+    rng = np.random.default_rng(61)
+    return {
+        "tiny_tree": tiny_tree(),
+        "forest_long_segments": random_forest(rng, max_tokens=900, max_len=300, max_depth=4, p_new_root=0.1),
+        "forest_short_segments": random_forest(rng, max_tokens=500, max_len=20, max_depth=6, p_new_root=0.1),
+    }
+
+
+@pytest.mark.parametrize("name", ["tiny_tree", "forest_long_segments", "forest_short_segments"])
+@pytest.mark.parametrize("width", [4, 3, 1])
+def test_conv_matches_oracle(name, width):
+    import shared_prefix_tree_amd as sp
+
+    topo = forests()[name]
+    T = topo.total_tokens
+    d = mamba_tensors(70 + width, T, channels=96, width=width)
+    rng = np.random.default_rng(width)
+    dy = rng.standard_normal((T, 96)).astype(np.float32)
+    dev = "cuda:0"
+    t = dev_tensors({"x": d["conv_x"], "w": d["conv_w"], "b": d["conv_b"], "dy": dy}, dev)
+    with torch.cuda.device(dev):
+        plan = sp.MambaPlan.from_topology(topo)
+    y = sp.conv_fwd(t["x"], t["w"], t["b"], plan)
+    dx, dw, db = sp.conv_bwd(t["x"], t["w"], t["dy"], plan)
+    torch.cuda.synchronize()
+    y_ref = oracle.conv_forward(d["conv_x"], d["conv_w"], d["conv_b"], topo)
+    dx_ref, dw_ref, db_ref = oracle.conv_backward(dy, d["conv_x"], d["conv_w"], topo)
+    errs = {k: rel_l2(g.cpu().numpy(), r) for k, g, r in
+            (("y", y, y_ref), ("dx", dx, dx_ref), ("dw", dw, dw_ref), ("db", db, db_ref))}
+    log(f"conv {name} T={T} width={width}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL for v in errs.values()), errs
+    y2 = sp.conv_fwd(t["x"], t["w"], t["b"], plan)
+    g2 = sp.conv_bwd(t["x"], t["w"], t["dy"], plan)
+    assert torch.equal(y, y2) and all(torch.equal(a, b) for a, b in zip((dx, dw, db), g2))
+
+
+@pytest.mark.parametrize("name", ["tiny_tree", "forest_long_segments", "forest_short_segments"])
+@pytest.mark.parametrize("N,H,G", [(128, 4, 2), (64, 6, 3)])
+def test_ssm_forward_matches_oracle(name, N, H, G):
+    import shared_prefix_tree_amd as sp
+
+    topo = forests()[name]
+    T = topo.total_tokens
+    d = mamba_tensors(80 + N, T, heads=H, groups=G, state_dim=N)
+    dev = "cuda:0"
+    keys = ("x", "dt", "A", "B", "C", "D")
+    t = dev_tensors({k: d[k] for k in keys}, dev)
+    with torch.cuda.device(dev):
+        plan = sp.MambaPlan.from_topology(topo)
+    log(f"ssm fwd {name}: T={T} units={plan.info()['num_units']} H={H} G={G} N={N}")
+    y, states = sp.ssm_fwd(*(t[k] for k in keys), plan)
+    torch.cuda.synchronize()
+    y_ref = oracle.ssm_forward(*(d[k] for k in keys), topo)
+    e = rel_l2(y.cpu().numpy(), y_ref)
+    # the saved state before each unit is the oracle's state after the unit's predecessor token
+    S_ref = oracle.ssm_states(d["x"], d["dt"], d["A"], d["B"], topo)
+    st = plan.export("unit_start")
+    prev = oracle.previous_token(topo)
+    saved = states[: st.size * H * 64 * N * 4].view(torch.float32).view(st.size, H, 64, N).cpu().numpy()
+    ref = np.stack([S_ref[prev[s]] if prev[s] >= 0 else np.zeros_like(S_ref[0]) for s in st])
+    e_s = rel_l2(saved, ref) if np.any(ref) else float(np.abs(saved).max())
+    log(f"  y rel-L2 {e:.2e}, saved states rel-L2 {e_s:.2e}")
+    assert e <= TOL and e_s <= TOL
+    y2, _ = sp.ssm_fwd(*(t[k] for k in keys), plan)
+    assert torch.equal(y, y2)
+
+
+def test_ssm_rejects_unsupported_shapes():
+    import shared_prefix_tree_amd as sp
+
+    dev = "cuda:0"
+    topo = tiny_tree()
+    T = topo.total_tokens
+    with torch.cuda.device(dev):
+        plan = sp.MambaPlan.from_topology(topo)
+    z = lambda *s: torch.zeros(*s, dtype=torch.float32, device=dev)  # noqa: E731
+    with pytest.raises(sp.TreeAttnError, match="head_dim must be 64"):
+        sp.ssm_fwd(z(T, 2, 32), z(T, 2), z(2), z(T, 1, 64), z(T, 1, 64), z(2), plan)
+    with pytest.raises(sp.TreeAttnError, match="state_dim"):
+        sp.ssm_fwd(z(T, 2, 64), z(T, 2), z(2), z(T, 1, 32), z(T, 1, 32), z(2), plan)
+    with pytest.raises(sp.TreeAttnError, match="multiple of 4"):
+        sp.conv_fwd(z(T, 6), z(6, 4), z(6), plan)

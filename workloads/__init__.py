@@ -46,6 +46,7 @@ __all__ = [
     "f32_to_bf16",
     "CHUNK_TOKENS",
     "sampled_edges",
+    "mamba_tensors",
 ]
 
 CHUNK_TOKENS = 256
@@ -312,6 +313,28 @@ def sampled_edges(topo: Topology, rng, vocab, p_sampled=0.5):
     src = np.asarray(src, dtype=np.int32)
     tgt = rng.integers(0, vocab, size=src.size, dtype=np.int64).astype(np.int32)
     return src, tgt
+
+
+def mamba_tensors(seed, tokens, heads=4, groups=2, head_dim=64, state_dim=128, channels=64, width=4):
+    """float32 inputs of the Mamba path, drawn from one generator seeded with
+    ``seed``, following a Mamba-2 mixer's initialisation ranges: x, B, C,
+    conv input standard normal; dt log-uniform in [1e-3, 1e-1]; A = -U(1, 16);
+    D standard normal; conv weight U(-1/sqrt(width), 1/sqrt(width)), bias
+    U(-0.1, 0.1)."""
+    rng = np.random.default_rng([seed, 7])
+    f = np.float32
+    out = {
+        "x": rng.standard_normal((tokens, heads, head_dim), dtype=f),
+        "dt": np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), (tokens, heads))).astype(f),
+        "A": (-rng.uniform(1.0, 16.0, heads)).astype(f),
+        "B": rng.standard_normal((tokens, groups, state_dim), dtype=f),
+        "C": rng.standard_normal((tokens, groups, state_dim), dtype=f),
+        "D": rng.standard_normal(heads, dtype=f),
+        "conv_x": rng.standard_normal((tokens, channels), dtype=f),
+        "conv_w": rng.uniform(-1.0, 1.0, (channels, width)).astype(f) / f(np.sqrt(width)),
+        "conv_b": rng.uniform(-0.1, 0.1, channels).astype(f),
+    }
+    return out
 
 
 # ---------------------------------------------------------------------------
