@@ -300,6 +300,15 @@ size_t tree_attn_ssm_workspace_bytes(tree_attn_mamba_plan_t plan, const tree_att
 int tree_attn_ssm_fwd(const float* x, const float* dt, const float* A, const float* B, const float* C,
                       const float* D, tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape, float* y,
                       float* states, size_t states_bytes, void* workspace, size_t workspace_bytes, void* stream);
+size_t tree_attn_ssm_bwd_workspace_bytes(tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape);
+/* Recurrence backward of sum <dy, y> (every token counted once; the
+ * gradient reaching a branch point's state is the sum over its branches):
+ * overwrites dx [T, H, 64], ddt [T, H], dA [H], dB, dC [T, G, N], dD [H].
+ * states: the forward's saved states for the same inputs. */
+int tree_attn_ssm_bwd(const float* x, const float* dt, const float* A, const float* B, const float* C,
+                      const float* D, const float* dy, tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape,
+                      const float* states, size_t states_bytes, float* dx, float* ddt, float* dA, float* dB,
+                      float* dC, float* dD, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Copy one of the plan's host tables (int32 records) for inspection.
  *   which = TREE_ATTN_EXPORT_*; buf may be NULL to query *count;

@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     edge_loss_fwd,
     fragment,
     library,
+    ssm_bwd,
     ssm_fwd,
     ssm_states_bytes,
     tree_attn_bwd,

@@ -67,6 +67,8 @@ SYMBOLS = (
     "tree_attn_ssm_states_bytes",
     "tree_attn_ssm_workspace_bytes",
     "tree_attn_ssm_fwd",
+    "tree_attn_ssm_bwd_workspace_bytes",
+    "tree_attn_ssm_bwd",
 )
 
 FRAG_SEG_PTR = 0
@@ -216,9 +218,13 @@ def library():
         getattr(lib, name).restype = ctypes.c_size_t
     lib.tree_attn_ssm_fwd.argtypes = [vp] * 7 + [ctypes.POINTER(SsmShape), vp, vp, ctypes.c_size_t, vp,
                                                  ctypes.c_size_t, vp]
+    lib.tree_attn_ssm_bwd_workspace_bytes.argtypes = [vp, ctypes.POINTER(SsmShape)]
+    lib.tree_attn_ssm_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.tree_attn_ssm_bwd.argtypes = [vp] * 8 + [ctypes.POINTER(SsmShape), vp, ctypes.c_size_t] + [vp] * 7 + \
+        [ctypes.c_size_t, vp]
     for name in ("tree_attn_mamba_plan", "tree_attn_mamba_plan_host", "tree_attn_mamba_plan_destroy",
                  "tree_attn_mamba_plan_info", "tree_attn_mamba_plan_export", "tree_attn_conv_fwd",
-                 "tree_attn_conv_bwd", "tree_attn_ssm_fwd"):
+                 "tree_attn_conv_bwd", "tree_attn_ssm_fwd", "tree_attn_ssm_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     for name in ("tree_attn_plan", "tree_attn_plan_query_run", "tree_attn_plan_query_run_host",
                  "tree_attn_plan_host", "tree_attn_plan_destroy",
@@ -586,6 +592,32 @@ def ssm_fwd(x, dt, A, B, C, D, plan: MambaPlan, out=None, states=None, workspace
                                      states.numel(), workspace.data_ptr(), workspace.numel(),
                                      _stream_of(x, stream)))
     return y, states
+
+
+def ssm_bwd(x, dt, A, B, C, D, dy, plan: MambaPlan, states, workspace=None, stream=None):
+    """Gradients (dx, ddt, dA, dB, dC, dD) of sum <dy, y> (``tree_attn_ssm_bwd``);
+    ``states`` is what ``ssm_fwd`` returned for the same inputs."""
+    import torch
+
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    for name, t, shp in (("x", x, None), ("dt", dt, (T, H)), ("A", A, (H,)), ("B", B, (T, G, N)),
+                         ("C", C, (T, G, N)), ("D", D, (H,)), ("dy", dy, (T, H, P))):
+        _f32(name, t, shp)
+    sh = _ssm_shape(x, B)
+    lib = library()
+    if workspace is None:
+        workspace = torch.empty(max(256, lib.tree_attn_ssm_bwd_workspace_bytes(plan.handle, ctypes.byref(sh))),
+                                dtype=torch.uint8, device=x.device)
+    dx, ddt, dA = torch.empty_like(x), torch.empty_like(dt), torch.empty_like(A)
+    dB, dC, dD = torch.empty_like(B), torch.empty_like(C), torch.empty_like(D)
+    with torch.cuda.device(x.device):
+        _check(lib.tree_attn_ssm_bwd(x.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(),
+                                     D.data_ptr(), dy.data_ptr(), plan.handle, ctypes.byref(sh), states.data_ptr(),
+                                     states.numel(), dx.data_ptr(), ddt.data_ptr(), dA.data_ptr(), dB.data_ptr(),
+                                     dC.data_ptr(), dD.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                     _stream_of(x, stream)))
+    return dx, ddt, dA, dB, dC, dD
 
 
 def _shape(q, k, softmax_scale):

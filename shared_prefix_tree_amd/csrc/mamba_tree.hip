@@ -360,6 +360,394 @@ hipError_t launch_ssm_fwd(const ScanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// state-space backward
+//
+// dS_i, the gradient of the loss with respect to S_i, obeys
+//   dS_i = dy_i outer C_i + sum over successors k of i of a_k dS_k,
+// so at a branch point the branches' gradients add up.  Per unit the
+// gradient reaching the state before it is linear in the gradient leaving
+// its last token:  in(u) = local_in(u) + decay(u) out(u),
+//   local_in(u) = sum_{k in u} exp(l_k) dy_k outer C_k   (l_k: A times the
+//   sum of dt over the unit's tokens up to and including k),
+//   out(u)      = sum over successor units v of in(v).
+// 4. local_in:   per (unit, head), local_in(u) and decay(u);
+// 5. propagate:  per (head, quarter), walk the units in reverse DFS order;
+// 6. gradients:  per (unit, head), the unit in chunks of 32 tokens, last
+//    chunk first, in the chunk (dual) form of the recurrence: with S0 the
+//    state before the chunk and G the gradient leaving its last token,
+//      S_i  = exp(l_i) S0 + sum_{j<=i} exp(l_i - l_j) dt_j x_j outer B_j
+//      dS_i = sum_{k>=i} exp(l_k - l_i) dy_k outer C_k + exp(l_e - l_i) G
+//    (l now cumulative over the chunk, l_e its last value), which gives
+//      dx_i = D dy_i + dt_i [sum_{k>=i} e^(l_k-l_i) (C_k.B_i) dy_k + e^(l_e-l_i) G B_i]
+//      dB_i = dt_i [sum_{k>=i} e^(l_k-l_i) (x_i.dy_k) C_k + e^(l_e-l_i) G^T x_i]
+//      dC_k = e^(l_k) S0^T dy_k + sum_{j<=k} e^(l_k-l_j) dt_j (x_j.dy_k) B_j
+//      a_i <dS_i, S_{i-1}> = sum_{k>=i} e^(l_k) (S0^T dy_k).C_k
+//          + sum_{k>=i} sum_{j<i} e^(l_k-l_j) dt_j (x_j.dy_k)(C_k.B_j)
+//          + e^(l_e) <G, S0> + sum_{j<i} e^(l_e-l_j) dt_j x_j.(G B_j)
+//      ddt_i = x_i.(dS_i B_i) + A a_i <dS_i, S_{i-1}>,  dA = sum_i dt_i a_i <dS_i, S_{i-1}>
+//    Every exponent is <= 0.  The chunk's start states come from one
+//    forward sweep over the unit from the saved start(u); G from out(u),
+//    moved back one chunk at a time.  dB and dC are summed over the heads
+//    of a group, and dA, dD over units, by separate fixed-order passes.
+
+struct ScanBwdArgs {
+  const float *x, *dt, *A, *B, *C, *D, *dy, *states;
+  const int32_t *unit_start, *unit_len, *unit_pred, *usucc_ptr, *usucc;
+  int H, G, U, T;
+  float* in;      // [U][H][P][N]: local_in, then in(u)
+  float* gout;    // [U][H][P][N]: out(u)
+  float* decay;   // [U][H]
+  float* dB_part; // [T][H][N]
+  float* dC_part; // [T][H][N]
+  float* dA_part; // [U][H]
+  float* dD_part; // [U][H]
+  float *dx, *ddt, *dA, *dB, *dC, *dD;
+};
+
+template <int N>
+__global__ __launch_bounds__(256) void ssm_bwd_local_kernel(ScanBwdArgs a) {
+  constexpr int NE = N / 4;
+  const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int g = h / (a.H / a.G);
+  const int p = threadIdx.x >> 2, q = threadIdx.x & 3;
+  const int t0 = a.unit_start[u], n = a.unit_len[u];
+  const float Ah = a.A[h];
+  float L[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) L[k] = 0.f;
+  float e = 1.f;
+  for (int t = t0; t < t0 + n; ++t) {
+    e *= __expf(a.dt[(size_t)t * a.H + h] * Ah);
+    const float w = e * a.dy[((size_t)t * a.H + h) * kHeadDim + p];
+    float c[NE];
+    load_row<N>(a.C + ((size_t)t * a.G + g) * N + q * NE, c);
+#pragma unroll
+    for (int k = 0; k < NE; ++k) L[k] = fmaf(w, c[k], L[k]);
+  }
+  store_row<N>(a.in + ((size_t(u) * a.H + h) * kHeadDim + p) * N + q * NE, L);
+  if (threadIdx.x == 0) a.decay[(size_t)u * a.H + h] = e;
+}
+
+template <int N>
+__global__ __launch_bounds__(256) void ssm_bwd_propagate_kernel(ScanBwdArgs a) {
+  constexpr int NE2 = N / 16;
+  const int h = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  const int p = quarter * 16 + (threadIdx.x >> 4), c = threadIdx.x & 15;
+  const size_t ustride = size_t(a.H) * kHeadDim * N;
+  const size_t hoff = size_t(h) * kHeadDim * N + size_t(p) * N + c * NE2;
+  float next_in[NE2];  // in(u + 1)
+#pragma unroll
+  for (int k = 0; k < NE2; ++k) next_in[k] = 0.f;
+  for (int u = a.U - 1; u >= 0; --u) {
+    const int s0 = a.usucc_ptr[u], s1 = a.usucc_ptr[u + 1];
+    float G[NE2];
+#pragma unroll
+    for (int k = 0; k < NE2; ++k) G[k] = 0.f;
+    if (s1 - s0 == 1 && a.usucc[s0] == u + 1) {
+#pragma unroll
+      for (int k = 0; k < NE2; ++k) G[k] = next_in[k];
+    } else {  // a branch point (or a leaf): the successors' in(v), ascending
+      for (int e = s0; e < s1; ++e) {
+        const float* iv = a.in + size_t(a.usucc[e]) * ustride + hoff;
+#pragma unroll
+        for (int k = 0; k < NE2; ++k) G[k] += iv[k];
+      }
+    }
+    float* go = a.gout + size_t(u) * ustride + hoff;
+    float* iu = a.in + size_t(u) * ustride + hoff;
+    const float du = a.decay[(size_t)u * a.H + h];
+#pragma unroll
+    for (int k = 0; k < NE2; ++k) {
+      go[k] = G[k];
+      next_in[k] = fmaf(du, G[k], iu[k]);
+      iu[k] = next_in[k];
+    }
+  }
+}
+
+constexpr int kChunk = 32;                 // tokens per chunk of the gradient kernel
+constexpr int kBwdThreads = 512;
+
+template <int N>
+struct BwdSmem {
+  float x[kChunk * kHeadDim], dy[kChunk * kHeadDim];
+  float B[kChunk * N], C[kChunk * N];
+  float S0[kHeadDim * N], G[kHeadDim * N];
+  float CB[kChunk * kChunk], XD[kChunk * kChunk];  // [k][j]: C_k.B_j, x_j.dy_k
+  float GB[kChunk * kHeadDim];                      // [j][p]: (G B_j)[p]
+  float dt[kChunk], l[kChunk], q[kChunk], r[kChunk], s[kChunk];
+  float red[kBwdThreads / 64];
+};
+
+__device__ inline float reduce16(float v) {  // sum over 16 consecutive lanes
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+
+// fixed-order sum over the block (all threads get the result)
+__device__ inline float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int w = 0; w < kBwdThreads / 64; ++w) r += red[w];
+  return r;
+}
+
+template <int N>
+__global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a) {
+  constexpr int NE3 = N / 8;   // state elements per thread (row p, columns c8 NE3 ..)
+  constexpr int NN = N / 16;   // columns per thread in the (token, column) phase
+  __shared__ __attribute__((aligned(16))) BwdSmem<N> sm;
+  const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int g = h / (a.H / a.G);
+  const int tid = threadIdx.x;
+  const int t0 = a.unit_start[u], len = a.unit_len[u];
+  const int nch = (len + kChunk - 1) / kChunk;
+  const float Ah = a.A[h], Dh = a.D[h];
+  const size_t urow = (size_t(u) * a.H + h) * kHeadDim * N;
+
+  // state layout: row p, columns [c8 NE3, (c8 + 1) NE3)
+  const int sp = tid >> 3, sc = (tid & 7) * NE3;
+  float Gr[NE3];
+#pragma unroll
+  for (int k = 0; k < NE3; ++k) Gr[k] = a.gout[urow + size_t(sp) * N + sc + k];
+  float dA_acc = 0.f, dD_acc = 0.f;
+
+  for (int c = nch - 1; c >= 0; --c) {
+    // the state before chunk c: a forward sweep from the unit's saved start
+    float S0r[NE3];
+#pragma unroll
+    for (int k = 0; k < NE3; ++k) S0r[k] = a.states[urow + size_t(sp) * N + sc + k];
+    for (int t = t0; t < t0 + c * kChunk; ++t) {
+      const float d = a.dt[(size_t)t * a.H + h];
+      const float ux = d * a.x[((size_t)t * a.H + h) * kHeadDim + sp];
+      const float dec = __expf(d * Ah);
+      float b[NE3];
+#pragma unroll
+      for (int k = 0; k < NE3 / 4; ++k) {
+        const float4 v = reinterpret_cast<const float4*>(a.B + ((size_t)t * a.G + g) * N + sc)[k];
+        b[4 * k] = v.x, b[4 * k + 1] = v.y, b[4 * k + 2] = v.z, b[4 * k + 3] = v.w;
+      }
+#pragma unroll
+      for (int k = 0; k < NE3; ++k) S0r[k] = fmaf(ux, b[k], dec * S0r[k]);
+    }
+    const int c0 = t0 + c * kChunk, clen = min(kChunk, len - c * kChunk);
+    // stage the chunk (padding: zeros, so padded tokens contribute nothing)
+    for (int e = tid; e < kChunk * kHeadDim; e += kBwdThreads) {
+      const int k = e / kHeadDim, p = e % kHeadDim;
+      const size_t off = ((size_t)(c0 + k) * a.H + h) * kHeadDim + p;
+      sm.x[e] = k < clen ? a.x[off] : 0.f;
+      sm.dy[e] = k < clen ? a.dy[off] : 0.f;
+    }
+    for (int e = tid; e < kChunk * N; e += kBwdThreads) {
+      const int k = e / N, n = e % N;
+      const size_t off = ((size_t)(c0 + k) * a.G + g) * N + n;
+      sm.B[e] = k < clen ? a.B[off] : 0.f;
+      sm.C[e] = k < clen ? a.C[off] : 0.f;
+    }
+    if (tid < kChunk) sm.dt[tid] = tid < clen ? a.dt[(size_t)(c0 + tid) * a.H + h] : 0.f;
+#pragma unroll
+    for (int k = 0; k < NE3; ++k) {
+      sm.S0[sp * N + sc + k] = S0r[k];
+      sm.G[sp * N + sc + k] = Gr[k];
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float l = 0.f;
+      for (int k = 0; k < kChunk; ++k) {
+        l = fmaf(sm.dt[k], Ah, l);
+        sm.l[k] = l;
+      }
+    }
+    // <G, S0>
+    float gs = 0.f;
+#pragma unroll
+    for (int k = 0; k < NE3; ++k) gs = fmaf(Gr[k], S0r[k], gs);
+    gs = block_sum(gs, sm.red);  // (its barriers also publish l)
+    // CB, XD and G B
+    for (int e = tid; e < kChunk * kChunk; e += kBwdThreads) {
+      const int k = e / kChunk, j = e % kChunk;
+      float cb = 0.f, xd = 0.f;
+      for (int n = 0; n < N; ++n) cb = fmaf(sm.C[k * N + n], sm.B[j * N + n], cb);
+      for (int p = 0; p < kHeadDim; ++p) xd = fmaf(sm.x[j * kHeadDim + p], sm.dy[k * kHeadDim + p], xd);
+      sm.CB[e] = cb;
+      sm.XD[e] = xd;
+    }
+    for (int e = tid; e < kChunk * kHeadDim; e += kBwdThreads) {
+      const int j = e / kHeadDim, p = e % kHeadDim;
+      float acc = 0.f;
+      for (int n = 0; n < N; ++n) acc = fmaf(sm.G[p * N + n], sm.B[j * N + n], acc);
+      sm.GB[e] = acc;
+    }
+    __syncthreads();
+    const float le = sm.l[kChunk - 1];
+    const float ele = __expf(le);
+    // (token k, columns) phase: dC_k, dB_k, q_k
+    {
+      const int k = tid >> 4, n0 = (tid & 15) * NN;
+      const float lk = sm.l[k];
+      float s0dy[NN], gx[NN];
+#pragma unroll
+      for (int m = 0; m < NN; ++m) s0dy[m] = gx[m] = 0.f;
+      for (int p = 0; p < kHeadDim; ++p) {
+        const float dyp = sm.dy[k * kHeadDim + p], xp = sm.x[k * kHeadDim + p];
+#pragma unroll
+        for (int m = 0; m < NN; ++m) {
+          s0dy[m] = fmaf(sm.S0[p * N + n0 + m], dyp, s0dy[m]);
+          gx[m] = fmaf(sm.G[p * N + n0 + m], xp, gx[m]);
+        }
+      }
+      const float ek = __expf(lk);
+      float dC[NN], dB[NN], qp = 0.f;
+#pragma unroll
+      for (int m = 0; m < NN; ++m) {
+        qp = fmaf(s0dy[m], sm.C[k * N + n0 + m], qp);
+        dC[m] = ek * s0dy[m];
+        dB[m] = __expf(le - lk) * gx[m];
+      }
+      for (int j = 0; j <= k; ++j) {
+        const float w = __expf(lk - sm.l[j]) * sm.dt[j] * sm.XD[k * kChunk + j];
+#pragma unroll
+        for (int m = 0; m < NN; ++m) dC[m] = fmaf(w, sm.B[j * N + n0 + m], dC[m]);
+      }
+      for (int m2 = k; m2 < kChunk; ++m2) {
+        const float w = __expf(sm.l[m2] - lk) * sm.XD[m2 * kChunk + k];
+#pragma unroll
+        for (int m = 0; m < NN; ++m) dB[m] = fmaf(w, sm.C[m2 * N + n0 + m], dB[m]);
+      }
+      qp = reduce16(qp);
+      if ((tid & 15) == 0) sm.q[k] = ek * qp;
+      if (k < clen) {
+        const float dtk = sm.dt[k];
+        float* pc = a.dC_part + ((size_t)(c0 + k) * a.H + h) * N + n0;
+        float* pb = a.dB_part + ((size_t)(c0 + k) * a.H + h) * N + n0;
+#pragma unroll
+        for (int m = 0; m < NN; ++m) {
+          pc[m] = dC[m];
+          pb[m] = dtk * dB[m];
+        }
+      }
+    }
+    // (token j, rows) phase: dx_j, x_j.(dS_j B_j), r'_j, dD
+    {
+      const int j = tid >> 4, p0 = (tid & 15) * 4;
+      const float lj = sm.l[j], dtj = sm.dt[j];
+      float br[4];
+      const float eg = __expf(le - lj);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) br[m] = eg * sm.GB[j * kHeadDim + p0 + m];
+      for (int k = j; k < kChunk; ++k) {
+        const float w = __expf(sm.l[k] - lj) * sm.CB[k * kChunk + j];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) br[m] = fmaf(w, sm.dy[k * kHeadDim + p0 + m], br[m]);
+      }
+      float sp_ = 0.f, rp = 0.f, dd = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float xv = sm.x[j * kHeadDim + p0 + m], dyv = sm.dy[j * kHeadDim + p0 + m];
+        sp_ = fmaf(xv, br[m], sp_);
+        rp = fmaf(xv, sm.GB[j * kHeadDim + p0 + m], rp);
+        dd = fmaf(dyv, xv, dd);
+        if (j < clen) a.dx[((size_t)(c0 + j) * a.H + h) * kHeadDim + p0 + m] = fmaf(Dh, dyv, dtj * br[m]);
+      }
+      sp_ = reduce16(sp_);
+      rp = reduce16(rp);
+      dd = reduce16(dd);
+      if ((tid & 15) == 0) {
+        sm.s[j] = sp_;
+        sm.r[j] = eg * dtj * rp;
+        dD_acc += dd;
+      }
+    }
+    __syncthreads();
+    // a_i <dS_i, S_{i-1}>: ddt_i and dA
+    {
+      const int i = tid >> 4, sub = tid & 15;
+      float R = 0.f;
+      for (int k = i + sub; k < kChunk; k += 16) {
+        const float lk = sm.l[k];
+        for (int j = 0; j < i; ++j)
+          R = fmaf(__expf(lk - sm.l[j]) * sm.dt[j], sm.XD[k * kChunk + j] * sm.CB[k * kChunk + j], R);
+      }
+      R = reduce16(R);
+      if (sub == 0) {
+        float W = R + ele * gs;
+        for (int k = i; k < kChunk; ++k) W += sm.q[k];
+        for (int j = 0; j < i; ++j) W += sm.r[j];
+        if (i < clen) a.ddt[(size_t)(c0 + i) * a.H + h] = fmaf(Ah, W, sm.s[i]);
+        dA_acc = fmaf(sm.dt[i], W, dA_acc);
+      }
+    }
+    // gradient leaving the previous chunk's last token
+#pragma unroll
+    for (int k = 0; k < NE3; ++k) Gr[k] *= ele;
+    for (int k = 0; k < kChunk; ++k) {
+      const float w = __expf(sm.l[k]) * sm.dy[k * kHeadDim + sp];
+#pragma unroll
+      for (int m = 0; m < NE3; ++m) Gr[m] = fmaf(w, sm.C[k * N + sc + m], Gr[m]);
+    }
+    __syncthreads();
+  }
+  dA_acc = block_sum(dA_acc, sm.red);
+  dD_acc = block_sum(dD_acc, sm.red);
+  if (tid == 0) {
+    a.dA_part[(size_t)u * a.H + h] = dA_acc;
+    a.dD_part[(size_t)u * a.H + h] = dD_acc;
+  }
+}
+
+// dB, dC: the heads of each group summed in head order; one thread per (token, group, column)
+__global__ void ssm_bwd_group_sum_kernel(ScanBwdArgs a, int N) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)a.T * a.G * N) return;
+  const int n = int(idx % N);
+  const long long tg = idx / N;
+  const int g = int(tg % a.G);
+  const long long t = tg / a.G;
+  const int hpg = a.H / a.G;
+  float sb = 0.f, sc = 0.f;
+  for (int hh = 0; hh < hpg; ++hh) {
+    const size_t off = ((size_t)t * a.H + g * hpg + hh) * N + n;
+    sb += a.dB_part[off];
+    sc += a.dC_part[off];
+  }
+  a.dB[idx] = sb;
+  a.dC[idx] = sc;
+}
+
+// dA, dD: the units summed in unit order; one thread per head
+__global__ void ssm_bwd_unit_sum_kernel(ScanBwdArgs a) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= a.H) return;
+  float sa = 0.f, sd = 0.f;
+  for (int u = 0; u < a.U; ++u) {
+    sa += a.dA_part[(size_t)u * a.H + h];
+    sd += a.dD_part[(size_t)u * a.H + h];
+  }
+  a.dA[h] = sa;
+  a.dD[h] = sd;
+}
+
+template <int N>
+hipError_t launch_ssm_bwd(const ScanBwdArgs& a, hipStream_t s) {
+  const dim3 grid(unsigned(a.U) * unsigned(a.H));
+  hipLaunchKernelGGL((ssm_bwd_local_kernel<N>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((ssm_bwd_propagate_kernel<N>), dim3(unsigned(a.H) * 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((ssm_bwd_grad_kernel<N>), grid, dim3(kBwdThreads), 0, s, a);
+  const long long n = (long long)a.T * a.G * N;
+  hipLaunchKernelGGL(ssm_bwd_group_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, a, N);
+  hipLaunchKernelGGL(ssm_bwd_unit_sum_kernel, dim3(unsigned((a.H + 63) / 64)), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -545,6 +933,55 @@ size_t tree_attn_ssm_states_bytes(tree_attn_mamba_plan_t plan, const tree_attn_s
 size_t tree_attn_ssm_workspace_bytes(tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape) {
   if (!plan || !shape || shape->num_heads < 1 || shape->head_dim < 1 || shape->state_dim < 1) return 0;
   return align256(state_floats(plan, shape) * 4) + align256(size_t(plan->U) * shape->num_heads * 4);
+}
+
+size_t tree_attn_ssm_bwd_workspace_bytes(tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape) {
+  if (!plan || !shape || shape->num_heads < 1 || shape->head_dim < 1 || shape->state_dim < 1) return 0;
+  const size_t st = align256(state_floats(plan, shape) * 4);
+  const size_t part = align256(size_t(plan->T) * shape->num_heads * shape->state_dim * 4);
+  const size_t uh = align256(size_t(plan->U) * shape->num_heads * 4);
+  return 2 * st + 2 * part + 3 * uh;
+}
+
+int tree_attn_ssm_bwd(const float* x, const float* dt, const float* A, const float* B, const float* C,
+                      const float* D, const float* dy, tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape,
+                      const float* states, size_t states_bytes, float* dx, float* ddt, float* dA, float* dB,
+                      float* dC, float* dD, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "tree_attn_ssm_bwd";
+  if (int rc = check_plan(fn, plan)) return rc;
+  if (int rc = check_ssm_shape(fn, shape)) return rc;
+  if (!x || !dt || !A || !B || !C || !D || !dy || !states || !dx || !ddt || !dA || !dB || !dC || !dD || !workspace)
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL pointer");
+  if (!aligned16(C) || !aligned16(states) || !aligned16(workspace))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": C, states and workspace must be 16-byte aligned");
+  if (states_bytes < tree_attn_ssm_states_bytes(plan, shape))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": states buffer too small");
+  if (workspace_bytes < tree_attn_ssm_bwd_workspace_bytes(plan, shape))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": workspace too small");
+  if ((long long)plan->U * shape->num_heads >= (1LL << 31) ||
+      (long long)plan->T * shape->num_groups * shape->state_dim >= (1LL << 40))
+    return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": too many units x heads");
+  ScanBwdArgs a{};
+  a.x = x, a.dt = dt, a.A = A, a.B = B, a.C = C, a.D = D, a.dy = dy, a.states = states;
+  a.unit_start = plan->d_unit_start, a.unit_len = plan->d_unit_len, a.unit_pred = plan->d_unit_pred;
+  a.usucc_ptr = plan->d_usucc_ptr, a.usucc = plan->d_usucc;
+  a.H = shape->num_heads, a.G = shape->num_groups, a.U = plan->U, a.T = plan->T;
+  char* w = static_cast<char*>(workspace);
+  const size_t st = align256(state_floats(plan, shape) * 4);
+  const size_t part = align256(size_t(plan->T) * shape->num_heads * shape->state_dim * 4);
+  const size_t uh = align256(size_t(plan->U) * shape->num_heads * 4);
+  a.in = reinterpret_cast<float*>(w);
+  a.gout = reinterpret_cast<float*>(w + st);
+  a.dB_part = reinterpret_cast<float*>(w + 2 * st);
+  a.dC_part = reinterpret_cast<float*>(w + 2 * st + part);
+  a.decay = reinterpret_cast<float*>(w + 2 * st + 2 * part);
+  a.dA_part = reinterpret_cast<float*>(w + 2 * st + 2 * part + uh);
+  a.dD_part = reinterpret_cast<float*>(w + 2 * st + 2 * part + 2 * uh);
+  a.dx = dx, a.ddt = ddt, a.dA = dA, a.dB = dB, a.dC = dC, a.dD = dD;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = shape->state_dim == 128 ? launch_ssm_bwd<128>(a, s) : launch_ssm_bwd<64>(a, s);
+  if (e != hipSuccess) return hip_error(fn, e);
+  return TREE_ATTN_OK;
 }
 
 int tree_attn_ssm_fwd(const float* x, const float* dt, const float* A, const float* B, const float* C,

@@ -94,6 +94,37 @@ def test_ssm_forward_matches_oracle(name, N, H, G):
     assert torch.equal(y, y2)
 
 
+@pytest.mark.parametrize("name", ["tiny_tree", "forest_long_segments", "forest_short_segments"])
+@pytest.mark.parametrize("N,H,G", [(128, 4, 2), (64, 6, 3)])
+def test_ssm_backward_matches_oracle(name, N, H, G):
+    """Every gradient against the oracle; a branch point's state gets the sum
+    of its branches (the forests have forks inside and at the end of units)."""
+    import shared_prefix_tree_amd as sp
+
+    topo = forests()[name]
+    T = topo.total_tokens
+    d = mamba_tensors(90 + N, T, heads=H, groups=G, state_dim=N)
+    dy = np.random.default_rng(N + H).standard_normal((T, H, 64)).astype(np.float32)
+    dev = "cuda:0"
+    keys = ("x", "dt", "A", "B", "C", "D")
+    t = dev_tensors({k: d[k] for k in keys}, dev)
+    dyt = torch.from_numpy(dy).to(dev)
+    with torch.cuda.device(dev):
+        plan = sp.MambaPlan.from_topology(topo)
+    log(f"ssm bwd {name}: T={T} units={plan.info()['num_units']} H={H} G={G} N={N}")
+    _, states = sp.ssm_fwd(*(t[k] for k in keys), plan)
+    got = sp.ssm_bwd(*(t[k] for k in keys), dyt, plan, states)
+    torch.cuda.synchronize()
+    ref = oracle.ssm_backward(dy, *(d[k] for k in keys), topo)
+    errs = {}
+    for k, g, r in zip(("dx", "ddt", "dA", "dB", "dC", "dD"), got, ref):
+        errs[k] = rel_l2(g.cpu().numpy(), r)
+    log("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL for v in errs.values()), errs
+    again = sp.ssm_bwd(*(t[k] for k in keys), dyt, plan, states)
+    assert all(torch.equal(a, b) for a, b in zip(got, again))
+
+
 def test_ssm_rejects_unsupported_shapes():
     import shared_prefix_tree_amd as sp
 
