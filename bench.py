@@ -278,6 +278,89 @@ def edge_loss(args):
     }), flush=True)
 
 
+def mamba(args):
+    """Times Mamba state forking on the workload's forest: a Mamba-2 mixer of
+    a 4096-wide model (128 heads of 64, 8 groups, state 128; convolution of
+    width 4 over the 10,240 x/B/C channels), all float32.  Algorithmic work
+    per token and head: 5 P N flops forward (state update 3, output 2),
+    11 P N backward (gradient update 3, dx, dB, dC and the decay term 2
+    each); the convolution is counted by bytes (one read of every input,
+    one write of every output).  One JSON line."""
+    import numpy as np
+    import torch
+
+    import shared_prefix_tree_amd as sp
+    from workloads import get_workload
+
+    H, G, P, N, W = 128, 8, 64, 128, 4
+    CH = H * P + 2 * G * N
+    w = get_workload(args.workload)
+    topo = w.topology()
+    T = topo.total_tokens
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+
+    def normal(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32)
+
+    def uniform(lo, hi, *shape):
+        return lo + (hi - lo) * torch.rand(*shape, generator=gen, device=dev, dtype=torch.float32)
+
+    x, B, C, dy = normal(T, H, P), normal(T, G, N), normal(T, G, N), normal(T, H, P)
+    dt = torch.exp(uniform(float(np.log(1e-3)), float(np.log(1e-1)), T, H))
+    A, D = -uniform(1.0, 16.0, H), normal(H)
+    cx, cdy = normal(T, CH), normal(T, CH)
+    cw, cb = uniform(-0.5, 0.5, CH, W), uniform(-0.1, 0.1, CH)
+    with torch.cuda.device(dev):
+        plan = sp.MambaPlan.from_topology(topo)
+    info = plan.info()
+    log(f"mamba: T={T} units={info['num_units']} H={H} G={G} P={P} N={N} conv channels={CH}")
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        rec(0)
+        sp.conv_fwd(cx, cw, cb, plan)
+        rec(1)
+        _, states = sp.ssm_fwd(x, dt, A, B, C, D, plan)
+        rec(2)
+        sp.conv_bwd(cx, cw, cdy, plan)
+        rec(3)
+        sp.ssm_bwd(x, dt, A, B, C, D, dy, plan, states)
+        rec(4)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps * 1e3
+    ms = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(4)]
+    cf, sf, cbw, sbw = ms
+    unit = T * H * P * N
+    f_fwd, f_bwd = 5.0 * unit, 11.0 * unit
+    scan_tf = (f_fwd + f_bwd) / ((sf + sbw) * 1e-3) / 1e12
+    conv_gbs = (8.0 * T * CH) / (cf * 1e-3) / 1e9, (12.0 * T * CH) / (cbw * 1e-3) / 1e9
+    log(f"mamba: conv fwd {cf:.3f} ms ({conv_gbs[0]:.0f} GB/s), scan fwd {sf:.3f} ms, conv bwd {cbw:.3f} ms "
+        f"({conv_gbs[1]:.0f} GB/s), scan bwd {sbw:.3f} ms; scan {scan_tf:.2f} TFLOP/s")
+    print(json.dumps({
+        "metric": "Mamba state forking (tree convolution + state-space scan), fwd+bwd, scan TFLOP/s",
+        "value": round(scan_tf, 3), "unit": "TFLOP/s", "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall, 4), "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name} forest, Mamba-2 mixer", "tokens": T, "units": info["num_units"],
+                   "heads": H, "groups": G, "head_dim": P, "state_dim": N, "conv_channels": CH, "conv_width": W},
+        "conv_fwd_ms": round(cf, 4), "ssm_fwd_ms": round(sf, 4), "conv_bwd_ms": round(cbw, 4),
+        "ssm_bwd_ms": round(sbw, 4),
+        "ssm_fwd_tflops": round(f_fwd / (sf * 1e-3) / 1e12, 3), "ssm_bwd_tflops": round(f_bwd / (sbw * 1e-3) / 1e12, 3),
+        "conv_fwd_gbs": round(conv_gbs[0], 1), "conv_bwd_gbs": round(conv_gbs[1], 1),
+        "roofline": {"bound": "alu", "achieved": round(scan_tf, 3), "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": round(scan_tf / 157.3, 4), "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,6 +380,9 @@ def main():
     ap.add_argument("--edge-loss", action="store_true",
                     help="only time the sampled-edge projection and loss on the workload's forest "
                          "(prints its own JSON line)")
+    ap.add_argument("--mamba", action="store_true",
+                    help="only time Mamba state forking (tree convolution and state-space scan, forward and "
+                         "backward) on the workload's forest (prints its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -323,6 +409,9 @@ def main():
 
     if args.edge_loss:
         edge_loss(args)
+        return
+    if args.mamba:
+        mamba(args)
         return
 
     import shared_prefix_tree_amd as sp

@@ -252,7 +252,7 @@ int tree_attn_edge_loss_bwd(const void* hidden, const void* weight, int32_t hidd
  * softplus); A, D: [H]; B, C: [T, G, N]; head h reads group h / (H / G):
  *   S_i = exp(dt[i,h] A[h]) S_prev(i) + dt[i,h] x[i,h,:] outer B[i,g,:],  S_-1 = 0
  *   y[i,h,:] = S_i C[i,g,:] + D[h] x[i,h,:]
- * N = state_dim is 64 or 128; B, C 16-byte aligned.
+ * N = state_dim is 64 or 128; x, y, dy, dx, B, C 16-byte aligned.
  *
  * tree_attn_mamba_plan validates the forest (same rules as tree_attn_plan),
  * derives prev, the convolution halo and successor tables and the scan
@@ -292,8 +292,9 @@ size_t tree_attn_conv_bwd_workspace_bytes(tree_attn_mamba_plan_t plan, int32_t c
 int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int32_t channels, int32_t width,
                        tree_attn_mamba_plan_t plan, float* dx, float* dweight, float* dbias, void* workspace,
                        size_t workspace_bytes, void* stream);
-/* Bytes of the saved states (the state before every unit, written by the
- * forward for the backward) and of the forward's workspace. */
+/* Bytes of the saved states (the state before every 32-token chunk of every
+ * scan unit, written by the forward for the backward) and of the forward's
+ * workspace. */
 size_t tree_attn_ssm_states_bytes(tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape);
 size_t tree_attn_ssm_workspace_bytes(tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape);
 /* Recurrence forward: writes y and the saved states. */

@@ -242,73 +242,178 @@ __global__ void conv_bwd_dw_reduce_kernel(const float* __restrict__ partial, int
 // ---------------------------------------------------------------------------
 // state-space scan
 
+constexpr int kChunk = 32;                        // tokens staged in LDS at a time
+constexpr int kChunksPerUnit = kUnit / kChunk;  // saved states per unit and head
+
 struct ScanArgs {
   const float *x, *dt, *A, *B, *C, *D;
   const int32_t *unit_start, *unit_len, *unit_pred;
   int H, G, U;
   float* y;
-  float* states;  // [U][H][P][N] state before each unit
+  float* states;  // [U][kChunksPerUnit][H][P][N]: state before each chunk of each unit
   float* local;   // [U][H][P][N] unit scanned from a zero state
   float* decay;   // [U][H]
 };
 
-template <int N>
-__device__ inline void load_row(const float* __restrict__ p, float (&v)[N / 4]) {
-#pragma unroll
-  for (int k = 0; k < N / 16; ++k) {
-    const float4 t = reinterpret_cast<const float4*>(p)[k];
-    v[4 * k] = t.x, v[4 * k + 1] = t.y, v[4 * k + 2] = t.z, v[4 * k + 3] = t.w;
-  }
+__host__ __device__ inline size_t state_index(int u, int chunk, int H, int h, int N) {
+  return ((size_t(u) * kChunksPerUnit + chunk) * H + h) * size_t(kHeadDim) * N;
 }
 
+// local pass: one block per (unit, head); thread (row group, column quad)
+// holds rows [pg PR, (pg+1) PR) x columns [4 nq, 4 nq + 4); the chunk's B
+// rows, x rows and step sizes are staged in LDS
 template <int N>
-__device__ inline void store_row(float* __restrict__ p, const float (&v)[N / 4]) {
-#pragma unroll
-  for (int k = 0; k < N / 16; ++k)
-    reinterpret_cast<float4*>(p)[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
-}
-
-// one block per (unit, head); thread (p, q) holds S[p][q N/4 .. (q+1) N/4)
-template <int N, bool kOutput>
-__global__ __launch_bounds__(256) void ssm_scan_kernel(ScanArgs a) {
-  constexpr int NE = N / 4;
+__global__ __launch_bounds__(256) void ssm_local_kernel(ScanArgs a) {
+  constexpr int NQ = N / 4, PG = 256 / NQ, PR = kHeadDim / PG;
+  __shared__ float4 sB[kChunk][NQ];
+  __shared__ __attribute__((aligned(16))) float sX[kChunk][kHeadDim];
+  __shared__ float sDT[kChunk], sDec[kChunk];
   const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int g = h / (a.H / a.G);
-  const int p = threadIdx.x >> 2, q = threadIdx.x & 3;
-  const int t0 = a.unit_start[u], n = a.unit_len[u];
-  const size_t srow = ((size_t(u) * a.H + h) * kHeadDim + p) * N + q * NE;
-  float S[NE];
-  if (kOutput) {
-    load_row<N>(a.states + srow, S);
-  } else {
+  const int tid = threadIdx.x, nq = tid % NQ, pg = tid / NQ;
+  const int t0 = a.unit_start[u], len = a.unit_len[u];
+  const float Ah = a.A[h];
+  float S[PR][4];
 #pragma unroll
-    for (int k = 0; k < NE; ++k) S[k] = 0.f;
-  }
-  const float Ah = a.A[h], Dh = a.D[h];
+  for (int r = 0; r < PR; ++r)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) S[r][k] = 0.f;
   float dsum = 0.f;
-  for (int t = t0; t < t0 + n; ++t) {
-    const float d = a.dt[(size_t)t * a.H + h];
-    const float xp = a.x[((size_t)t * a.H + h) * kHeadDim + p];
-    float b[NE];
-    load_row<N>(a.B + ((size_t)t * a.G + g) * N + q * NE, b);
-    const float decay = __expf(d * Ah), ux = d * xp;
+  for (int c0 = t0; c0 < t0 + len; c0 += kChunk) {
+    const int clen = min(kChunk, t0 + len - c0);
+    __syncthreads();
+    for (int e = tid; e < kChunk * NQ; e += 256) {
+      const int k = e / NQ, q = e % NQ;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < clen) v = reinterpret_cast<const float4*>(a.B + ((size_t)(c0 + k) * a.G + g) * N)[q];
+      sB[k][q] = v;
+    }
+    for (int e = tid; e < kChunk * (kHeadDim / 4); e += 256) {
+      const int k = e / (kHeadDim / 4), q = e % (kHeadDim / 4);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < clen) v = reinterpret_cast<const float4*>(a.x + ((size_t)(c0 + k) * a.H + h) * kHeadDim)[q];
+      reinterpret_cast<float4*>(sX[k])[q] = v;
+    }
+    if (tid < kChunk) {
+      const float d = tid < clen ? a.dt[(size_t)(c0 + tid) * a.H + h] : 0.f;
+      sDT[tid] = d;
+      sDec[tid] = __expf(d * Ah);
+    }
+    __syncthreads();
+    for (int k = 0; k < clen; ++k) {
+      const float4 b = sB[k][nq];
+      const float d = sDT[k], dec = sDec[k];
+      dsum += d;
 #pragma unroll
-    for (int k = 0; k < NE; ++k) S[k] = fmaf(ux, b[k], decay * S[k]);
-    dsum += d;
-    if (kOutput) {
-      float c[NE];
-      load_row<N>(a.C + ((size_t)t * a.G + g) * N + q * NE, c);
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < NE; ++k) acc = fmaf(S[k], c[k], acc);
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      if (q == 0) a.y[((size_t)t * a.H + h) * kHeadDim + p] = fmaf(Dh, xp, acc);
+      for (int r = 0; r < PR; ++r) {
+        const float ux = d * sX[k][pg * PR + r];
+        S[r][0] = fmaf(ux, b.x, dec * S[r][0]);
+        S[r][1] = fmaf(ux, b.y, dec * S[r][1]);
+        S[r][2] = fmaf(ux, b.z, dec * S[r][2]);
+        S[r][3] = fmaf(ux, b.w, dec * S[r][3]);
+      }
     }
   }
-  if (!kOutput) {
-    store_row<N>(a.local + srow, S);
-    if (threadIdx.x == 0) a.decay[(size_t)u * a.H + h] = __expf(Ah * dsum);
+  const size_t base = (size_t(u) * a.H + h) * kHeadDim * N;
+#pragma unroll
+  for (int r = 0; r < PR; ++r)
+    reinterpret_cast<float4*>(a.local + base + size_t(pg * PR + r) * N)[nq] =
+        make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
+  if (tid == 0) a.decay[(size_t)u * a.H + h] = __expf(Ah * dsum);
+}
+
+// output pass: one block per (unit, head) from the unit's start state;
+// thread (row pair pr, column group ng) holds rows 2 pr, 2 pr + 1 x columns
+// [ng NC, (ng+1) NC); y's sum over columns is an eight-lane reduction.  The
+// state before every chunk after the first is saved for the backward pass.
+template <int N>
+__global__ __launch_bounds__(256) void ssm_output_kernel(ScanArgs a) {
+  constexpr int NG = 8, NC = N / NG;
+  __shared__ __attribute__((aligned(16))) float sB[kChunk][N];
+  __shared__ __attribute__((aligned(16))) float sC[kChunk][N];
+  __shared__ __attribute__((aligned(16))) float sX[kChunk][kHeadDim];
+  __shared__ float sDT[kChunk], sDec[kChunk];
+  const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int g = h / (a.H / a.G);
+  const int tid = threadIdx.x, ng = tid & (NG - 1), pr = tid / NG;
+  const int t0 = a.unit_start[u], len = a.unit_len[u];
+  const float Ah = a.A[h], Dh = a.D[h];
+  float S[2][NC];
+  {
+    const float* s0 = a.states + state_index(u, 0, a.H, h, N) + size_t(2 * pr) * N + ng * NC;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int m = 0; m < NC / 4; ++m) {
+        const float4 v = reinterpret_cast<const float4*>(s0 + r * N)[m];
+        S[r][4 * m] = v.x, S[r][4 * m + 1] = v.y, S[r][4 * m + 2] = v.z, S[r][4 * m + 3] = v.w;
+      }
+  }
+  for (int ci = 0; ci * kChunk < len; ++ci) {
+    const int c0 = t0 + ci * kChunk, clen = min(kChunk, len - ci * kChunk);
+    if (ci > 0) {
+      float* sv = a.states + state_index(u, ci, a.H, h, N) + size_t(2 * pr) * N + ng * NC;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int m = 0; m < NC / 4; ++m)
+          reinterpret_cast<float4*>(sv + r * N)[m] =
+              make_float4(S[r][4 * m], S[r][4 * m + 1], S[r][4 * m + 2], S[r][4 * m + 3]);
+    }
+    __syncthreads();
+    for (int e = tid; e < kChunk * (N / 4); e += 256) {
+      const int k = e / (N / 4), q = e % (N / 4);
+      const size_t off = ((size_t)(c0 + k) * a.G + g) * N;
+      float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
+      if (k < clen) {
+        vb = reinterpret_cast<const float4*>(a.B + off)[q];
+        vc = reinterpret_cast<const float4*>(a.C + off)[q];
+      }
+      reinterpret_cast<float4*>(sB[k])[q] = vb;
+      reinterpret_cast<float4*>(sC[k])[q] = vc;
+    }
+    for (int e = tid; e < kChunk * (kHeadDim / 4); e += 256) {
+      const int k = e / (kHeadDim / 4), q = e % (kHeadDim / 4);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < clen) v = reinterpret_cast<const float4*>(a.x + ((size_t)(c0 + k) * a.H + h) * kHeadDim)[q];
+      reinterpret_cast<float4*>(sX[k])[q] = v;
+    }
+    if (tid < kChunk) {
+      const float d = tid < clen ? a.dt[(size_t)(c0 + tid) * a.H + h] : 0.f;
+      sDT[tid] = d;
+      sDec[tid] = __expf(d * Ah);
+    }
+    __syncthreads();
+    for (int k = 0; k < clen; ++k) {
+      const float d = sDT[k], dec = sDec[k];
+      const float x0 = sX[k][2 * pr], x1 = sX[k][2 * pr + 1];
+      const float u0 = d * x0, u1 = d * x1;
+      float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+      for (int m = 0; m < NC / 4; ++m) {
+        const float4 b = reinterpret_cast<const float4*>(&sB[k][ng * NC])[m];
+        const float4 c = reinterpret_cast<const float4*>(&sC[k][ng * NC])[m];
+#define TREE_SSM_STEP(J, BJ, CJ)                                   \
+  S[0][4 * m + J] = fmaf(u0, BJ, dec * S[0][4 * m + J]);           \
+  S[1][4 * m + J] = fmaf(u1, BJ, dec * S[1][4 * m + J]);           \
+  y0 = fmaf(S[0][4 * m + J], CJ, y0);                              \
+  y1 = fmaf(S[1][4 * m + J], CJ, y1);
+        TREE_SSM_STEP(0, b.x, c.x)
+        TREE_SSM_STEP(1, b.y, c.y)
+        TREE_SSM_STEP(2, b.z, c.z)
+        TREE_SSM_STEP(3, b.w, c.w)
+#undef TREE_SSM_STEP
+      }
+      y0 += __shfl_xor(y0, 1);
+      y1 += __shfl_xor(y1, 1);
+      y0 += __shfl_xor(y0, 2);
+      y1 += __shfl_xor(y1, 2);
+      y0 += __shfl_xor(y0, 4);
+      y1 += __shfl_xor(y1, 4);
+      if (ng == 0)
+        *reinterpret_cast<float2*>(a.y + ((size_t)(c0 + k) * a.H + h) * kHeadDim + 2 * pr) =
+            make_float2(fmaf(Dh, x0, y0), fmaf(Dh, x1, y1));
+    }
   }
 }
 
@@ -320,8 +425,8 @@ __global__ __launch_bounds__(256) void ssm_propagate_kernel(ScanArgs a) {
   const int h = blockIdx.x >> 2, quarter = blockIdx.x & 3;
   const int p = quarter * 16 + (threadIdx.x >> 4), c = threadIdx.x & 15;
   const size_t col = size_t(p) * N + c * NE2;
-  const size_t ustride = size_t(a.H) * kHeadDim * N;
-  const size_t hoff = size_t(h) * kHeadDim * N + col;
+  const size_t lstride = size_t(a.H) * kHeadDim * N;
+  const size_t loff = size_t(h) * kHeadDim * N + col;
   float end[NE2];
 #pragma unroll
   for (int k = 0; k < NE2; ++k) end[k] = 0.f;
@@ -336,16 +441,16 @@ __global__ __launch_bounds__(256) void ssm_propagate_kernel(ScanArgs a) {
       for (int k = 0; k < NE2; ++k) start[k] = end[k];
     } else {  // a fork: the parent's end, from what this thread stored
       const float dp = a.decay[(size_t)pred * a.H + h];
-      const float* sp = a.states + pred * ustride + hoff;
-      const float* lp = a.local + pred * ustride + hoff;
+      const float* sp = a.states + state_index(pred, 0, a.H, h, N) + col;
+      const float* lp = a.local + pred * lstride + loff;
 #pragma unroll
       for (int k = 0; k < NE2; ++k) start[k] = fmaf(dp, sp[k], lp[k]);
     }
-    float* out = a.states + u * ustride + hoff;
+    float* out = a.states + state_index(u, 0, a.H, h, N) + col;
 #pragma unroll
     for (int k = 0; k < NE2; ++k) out[k] = start[k];
     const float du = a.decay[(size_t)u * a.H + h];
-    const float* lu = a.local + u * ustride + hoff;
+    const float* lu = a.local + u * lstride + loff;
 #pragma unroll
     for (int k = 0; k < NE2; ++k) end[k] = fmaf(du, start[k], lu[k]);
   }
@@ -354,9 +459,9 @@ __global__ __launch_bounds__(256) void ssm_propagate_kernel(ScanArgs a) {
 template <int N>
 hipError_t launch_ssm_fwd(const ScanArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.U) * unsigned(a.H));
-  hipLaunchKernelGGL((ssm_scan_kernel<N, false>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((ssm_local_kernel<N>), grid, dim3(256), 0, s, a);
   hipLaunchKernelGGL((ssm_propagate_kernel<N>), dim3(unsigned(a.H) * 4), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((ssm_scan_kernel<N, true>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((ssm_output_kernel<N>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -405,28 +510,70 @@ struct ScanBwdArgs {
   float *dx, *ddt, *dA, *dB, *dC, *dD;
 };
 
+// local_in(u) = sum_k exp(l_k) dy_k outer C_k; same thread layout and
+// staging as the forward local pass
 template <int N>
 __global__ __launch_bounds__(256) void ssm_bwd_local_kernel(ScanBwdArgs a) {
-  constexpr int NE = N / 4;
+  constexpr int NQ = N / 4, PG = 256 / NQ, PR = kHeadDim / PG;
+  __shared__ float4 sC[kChunk][NQ];
+  __shared__ __attribute__((aligned(16))) float sY[kChunk][kHeadDim];
+  __shared__ float sE[kChunk];
+  __shared__ float sL;  // l at the end of the previous chunk
   const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int g = h / (a.H / a.G);
-  const int p = threadIdx.x >> 2, q = threadIdx.x & 3;
-  const int t0 = a.unit_start[u], n = a.unit_len[u];
+  const int tid = threadIdx.x, nq = tid % NQ, pg = tid / NQ;
+  const int t0 = a.unit_start[u], len = a.unit_len[u];
   const float Ah = a.A[h];
-  float L[NE];
+  float L[PR][4];
 #pragma unroll
-  for (int k = 0; k < NE; ++k) L[k] = 0.f;
-  float e = 1.f;
-  for (int t = t0; t < t0 + n; ++t) {
-    e *= __expf(a.dt[(size_t)t * a.H + h] * Ah);
-    const float w = e * a.dy[((size_t)t * a.H + h) * kHeadDim + p];
-    float c[NE];
-    load_row<N>(a.C + ((size_t)t * a.G + g) * N + q * NE, c);
+  for (int r = 0; r < PR; ++r)
 #pragma unroll
-    for (int k = 0; k < NE; ++k) L[k] = fmaf(w, c[k], L[k]);
+    for (int k = 0; k < 4; ++k) L[r][k] = 0.f;
+  if (tid == 0) sL = 0.f;
+  for (int c0 = t0; c0 < t0 + len; c0 += kChunk) {
+    const int clen = min(kChunk, t0 + len - c0);
+    __syncthreads();
+    for (int e = tid; e < kChunk * NQ; e += 256) {
+      const int k = e / NQ, q = e % NQ;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < clen) v = reinterpret_cast<const float4*>(a.C + ((size_t)(c0 + k) * a.G + g) * N)[q];
+      sC[k][q] = v;
+    }
+    for (int e = tid; e < kChunk * (kHeadDim / 4); e += 256) {
+      const int k = e / (kHeadDim / 4), q = e % (kHeadDim / 4);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < clen) v = reinterpret_cast<const float4*>(a.dy + ((size_t)(c0 + k) * a.H + h) * kHeadDim)[q];
+      reinterpret_cast<float4*>(sY[k])[q] = v;
+    }
+    if (tid == 0) {
+      float l = sL;
+      for (int k = 0; k < clen; ++k) {
+        l = fmaf(a.dt[(size_t)(c0 + k) * a.H + h], Ah, l);
+        sE[k] = __expf(l);
+      }
+      sL = l;
+    }
+    __syncthreads();
+    for (int k = 0; k < clen; ++k) {
+      const float4 c = sC[k][nq];
+      const float ek = sE[k];
+#pragma unroll
+      for (int r = 0; r < PR; ++r) {
+        const float w = ek * sY[k][pg * PR + r];
+        L[r][0] = fmaf(w, c.x, L[r][0]);
+        L[r][1] = fmaf(w, c.y, L[r][1]);
+        L[r][2] = fmaf(w, c.z, L[r][2]);
+        L[r][3] = fmaf(w, c.w, L[r][3]);
+      }
+    }
   }
-  store_row<N>(a.in + ((size_t(u) * a.H + h) * kHeadDim + p) * N + q * NE, L);
-  if (threadIdx.x == 0) a.decay[(size_t)u * a.H + h] = e;
+  const size_t base = (size_t(u) * a.H + h) * kHeadDim * N;
+#pragma unroll
+  for (int r = 0; r < PR; ++r)
+    reinterpret_cast<float4*>(a.in + base + size_t(pg * PR + r) * N)[nq] =
+        make_float4(L[r][0], L[r][1], L[r][2], L[r][3]);
+  __syncthreads();
+  if (tid == 0) a.decay[(size_t)u * a.H + h] = __expf(sL);
 }
 
 template <int N>
@@ -466,16 +613,21 @@ __global__ __launch_bounds__(256) void ssm_bwd_propagate_kernel(ScanBwdArgs a) {
   }
 }
 
-constexpr int kChunk = 32;                 // tokens per chunk of the gradient kernel
 constexpr int kBwdThreads = 512;
+
+// LDS rows are padded by one float so that lanes walking down a column
+// (different rows, same column) hit different banks
+constexpr int kPX = kHeadDim + 1;  // x, dy rows and (G B_j) rows
+constexpr int kPCB = kChunk + 1;   // C_k.B_j and x_j.dy_k rows
 
 template <int N>
 struct BwdSmem {
-  float x[kChunk * kHeadDim], dy[kChunk * kHeadDim];
-  float B[kChunk * N], C[kChunk * N];
-  float S0[kHeadDim * N], G[kHeadDim * N];
-  float CB[kChunk * kChunk], XD[kChunk * kChunk];  // [k][j]: C_k.B_j, x_j.dy_k
-  float GB[kChunk * kHeadDim];                      // [j][p]: (G B_j)[p]
+  static constexpr int PB = N + 1;  // B, C, S0, G rows
+  float x[kChunk * kPX], dy[kChunk * kPX];
+  float B[kChunk * PB], C[kChunk * PB];
+  float S0[kHeadDim * PB], G[kHeadDim * PB];
+  float CB[kChunk * kPCB], XD[kChunk * kPCB];  // [k][j]: C_k.B_j, x_j.dy_k
+  float GB[kChunk * kPX];                      // [j][p]: (G B_j)[p]
   float dt[kChunk], l[kChunk], q[kChunk], r[kChunk], s[kChunk];
   float red[kBwdThreads / 64];
 };
@@ -505,6 +657,7 @@ template <int N>
 __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a) {
   constexpr int NE3 = N / 8;   // state elements per thread (row p, columns c8 NE3 ..)
   constexpr int NN = N / 16;   // columns per thread in the (token, column) phase
+  constexpr int PB = BwdSmem<N>::PB;
   __shared__ __attribute__((aligned(16))) BwdSmem<N> sm;
   const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int g = h / (a.H / a.G);
@@ -512,52 +665,44 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
   const int t0 = a.unit_start[u], len = a.unit_len[u];
   const int nch = (len + kChunk - 1) / kChunk;
   const float Ah = a.A[h], Dh = a.D[h];
-  const size_t urow = (size_t(u) * a.H + h) * kHeadDim * N;
 
   // state layout: row p, columns [c8 NE3, (c8 + 1) NE3)
   const int sp = tid >> 3, sc = (tid & 7) * NE3;
   float Gr[NE3];
+  {
+    const float* go = a.gout + (size_t(u) * a.H + h) * kHeadDim * N + size_t(sp) * N + sc;
 #pragma unroll
-  for (int k = 0; k < NE3; ++k) Gr[k] = a.gout[urow + size_t(sp) * N + sc + k];
+    for (int k = 0; k < NE3; ++k) Gr[k] = go[k];
+  }
   float dA_acc = 0.f, dD_acc = 0.f;
 
   for (int c = nch - 1; c >= 0; --c) {
-    // the state before chunk c: a forward sweep from the unit's saved start
+    // the state before chunk c, saved by the forward pass
     float S0r[NE3];
+    {
+      const float* s0 = a.states + state_index(u, c, a.H, h, N) + size_t(sp) * N + sc;
 #pragma unroll
-    for (int k = 0; k < NE3; ++k) S0r[k] = a.states[urow + size_t(sp) * N + sc + k];
-    for (int t = t0; t < t0 + c * kChunk; ++t) {
-      const float d = a.dt[(size_t)t * a.H + h];
-      const float ux = d * a.x[((size_t)t * a.H + h) * kHeadDim + sp];
-      const float dec = __expf(d * Ah);
-      float b[NE3];
-#pragma unroll
-      for (int k = 0; k < NE3 / 4; ++k) {
-        const float4 v = reinterpret_cast<const float4*>(a.B + ((size_t)t * a.G + g) * N + sc)[k];
-        b[4 * k] = v.x, b[4 * k + 1] = v.y, b[4 * k + 2] = v.z, b[4 * k + 3] = v.w;
-      }
-#pragma unroll
-      for (int k = 0; k < NE3; ++k) S0r[k] = fmaf(ux, b[k], dec * S0r[k]);
+      for (int k = 0; k < NE3; ++k) S0r[k] = s0[k];
     }
     const int c0 = t0 + c * kChunk, clen = min(kChunk, len - c * kChunk);
     // stage the chunk (padding: zeros, so padded tokens contribute nothing)
     for (int e = tid; e < kChunk * kHeadDim; e += kBwdThreads) {
       const int k = e / kHeadDim, p = e % kHeadDim;
       const size_t off = ((size_t)(c0 + k) * a.H + h) * kHeadDim + p;
-      sm.x[e] = k < clen ? a.x[off] : 0.f;
-      sm.dy[e] = k < clen ? a.dy[off] : 0.f;
+      sm.x[k * kPX + p] = k < clen ? a.x[off] : 0.f;
+      sm.dy[k * kPX + p] = k < clen ? a.dy[off] : 0.f;
     }
     for (int e = tid; e < kChunk * N; e += kBwdThreads) {
       const int k = e / N, n = e % N;
       const size_t off = ((size_t)(c0 + k) * a.G + g) * N + n;
-      sm.B[e] = k < clen ? a.B[off] : 0.f;
-      sm.C[e] = k < clen ? a.C[off] : 0.f;
+      sm.B[k * PB + n] = k < clen ? a.B[off] : 0.f;
+      sm.C[k * PB + n] = k < clen ? a.C[off] : 0.f;
     }
     if (tid < kChunk) sm.dt[tid] = tid < clen ? a.dt[(size_t)(c0 + tid) * a.H + h] : 0.f;
 #pragma unroll
     for (int k = 0; k < NE3; ++k) {
-      sm.S0[sp * N + sc + k] = S0r[k];
-      sm.G[sp * N + sc + k] = Gr[k];
+      sm.S0[sp * PB + sc + k] = S0r[k];
+      sm.G[sp * PB + sc + k] = Gr[k];
     }
     __syncthreads();
     if (tid == 0) {
@@ -576,16 +721,16 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
     for (int e = tid; e < kChunk * kChunk; e += kBwdThreads) {
       const int k = e / kChunk, j = e % kChunk;
       float cb = 0.f, xd = 0.f;
-      for (int n = 0; n < N; ++n) cb = fmaf(sm.C[k * N + n], sm.B[j * N + n], cb);
-      for (int p = 0; p < kHeadDim; ++p) xd = fmaf(sm.x[j * kHeadDim + p], sm.dy[k * kHeadDim + p], xd);
-      sm.CB[e] = cb;
-      sm.XD[e] = xd;
+      for (int n = 0; n < N; ++n) cb = fmaf(sm.C[k * PB + n], sm.B[j * PB + n], cb);
+      for (int p = 0; p < kHeadDim; ++p) xd = fmaf(sm.x[j * kPX + p], sm.dy[k * kPX + p], xd);
+      sm.CB[k * kPCB + j] = cb;
+      sm.XD[k * kPCB + j] = xd;
     }
     for (int e = tid; e < kChunk * kHeadDim; e += kBwdThreads) {
       const int j = e / kHeadDim, p = e % kHeadDim;
       float acc = 0.f;
-      for (int n = 0; n < N; ++n) acc = fmaf(sm.G[p * N + n], sm.B[j * N + n], acc);
-      sm.GB[e] = acc;
+      for (int n = 0; n < N; ++n) acc = fmaf(sm.G[p * PB + n], sm.B[j * PB + n], acc);
+      sm.GB[j * kPX + p] = acc;
     }
     __syncthreads();
     const float le = sm.l[kChunk - 1];
@@ -598,30 +743,30 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
 #pragma unroll
       for (int m = 0; m < NN; ++m) s0dy[m] = gx[m] = 0.f;
       for (int p = 0; p < kHeadDim; ++p) {
-        const float dyp = sm.dy[k * kHeadDim + p], xp = sm.x[k * kHeadDim + p];
+        const float dyp = sm.dy[k * kPX + p], xp = sm.x[k * kPX + p];
 #pragma unroll
         for (int m = 0; m < NN; ++m) {
-          s0dy[m] = fmaf(sm.S0[p * N + n0 + m], dyp, s0dy[m]);
-          gx[m] = fmaf(sm.G[p * N + n0 + m], xp, gx[m]);
+          s0dy[m] = fmaf(sm.S0[p * PB + n0 + m], dyp, s0dy[m]);
+          gx[m] = fmaf(sm.G[p * PB + n0 + m], xp, gx[m]);
         }
       }
       const float ek = __expf(lk);
       float dC[NN], dB[NN], qp = 0.f;
 #pragma unroll
       for (int m = 0; m < NN; ++m) {
-        qp = fmaf(s0dy[m], sm.C[k * N + n0 + m], qp);
+        qp = fmaf(s0dy[m], sm.C[k * PB + n0 + m], qp);
         dC[m] = ek * s0dy[m];
         dB[m] = __expf(le - lk) * gx[m];
       }
       for (int j = 0; j <= k; ++j) {
-        const float w = __expf(lk - sm.l[j]) * sm.dt[j] * sm.XD[k * kChunk + j];
+        const float w = __expf(lk - sm.l[j]) * sm.dt[j] * sm.XD[k * kPCB + j];
 #pragma unroll
-        for (int m = 0; m < NN; ++m) dC[m] = fmaf(w, sm.B[j * N + n0 + m], dC[m]);
+        for (int m = 0; m < NN; ++m) dC[m] = fmaf(w, sm.B[j * PB + n0 + m], dC[m]);
       }
       for (int m2 = k; m2 < kChunk; ++m2) {
-        const float w = __expf(sm.l[m2] - lk) * sm.XD[m2 * kChunk + k];
+        const float w = __expf(sm.l[m2] - lk) * sm.XD[m2 * kPCB + k];
 #pragma unroll
-        for (int m = 0; m < NN; ++m) dB[m] = fmaf(w, sm.C[m2 * N + n0 + m], dB[m]);
+        for (int m = 0; m < NN; ++m) dB[m] = fmaf(w, sm.C[m2 * PB + n0 + m], dB[m]);
       }
       qp = reduce16(qp);
       if ((tid & 15) == 0) sm.q[k] = ek * qp;
@@ -643,21 +788,25 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
       float br[4];
       const float eg = __expf(le - lj);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) br[m] = eg * sm.GB[j * kHeadDim + p0 + m];
+      for (int m = 0; m < 4; ++m) br[m] = eg * sm.GB[j * kPX + p0 + m];
       for (int k = j; k < kChunk; ++k) {
-        const float w = __expf(sm.l[k] - lj) * sm.CB[k * kChunk + j];
+        const float w = __expf(sm.l[k] - lj) * sm.CB[k * kPCB + j];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) br[m] = fmaf(w, sm.dy[k * kHeadDim + p0 + m], br[m]);
+        for (int m = 0; m < 4; ++m) br[m] = fmaf(w, sm.dy[k * kPX + p0 + m], br[m]);
       }
       float sp_ = 0.f, rp = 0.f, dd = 0.f;
+      float dxv[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const float xv = sm.x[j * kHeadDim + p0 + m], dyv = sm.dy[j * kHeadDim + p0 + m];
+        const float xv = sm.x[j * kPX + p0 + m], dyv = sm.dy[j * kPX + p0 + m];
         sp_ = fmaf(xv, br[m], sp_);
-        rp = fmaf(xv, sm.GB[j * kHeadDim + p0 + m], rp);
+        rp = fmaf(xv, sm.GB[j * kPX + p0 + m], rp);
         dd = fmaf(dyv, xv, dd);
-        if (j < clen) a.dx[((size_t)(c0 + j) * a.H + h) * kHeadDim + p0 + m] = fmaf(Dh, dyv, dtj * br[m]);
+        dxv[m] = fmaf(Dh, dyv, dtj * br[m]);
       }
+      if (j < clen)
+        *reinterpret_cast<float4*>(a.dx + ((size_t)(c0 + j) * a.H + h) * kHeadDim + p0) =
+            make_float4(dxv[0], dxv[1], dxv[2], dxv[3]);
       sp_ = reduce16(sp_);
       rp = reduce16(rp);
       dd = reduce16(dd);
@@ -675,7 +824,7 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
       for (int k = i + sub; k < kChunk; k += 16) {
         const float lk = sm.l[k];
         for (int j = 0; j < i; ++j)
-          R = fmaf(__expf(lk - sm.l[j]) * sm.dt[j], sm.XD[k * kChunk + j] * sm.CB[k * kChunk + j], R);
+          R = fmaf(__expf(lk - sm.l[j]) * sm.dt[j], sm.XD[k * kPCB + j] * sm.CB[k * kPCB + j], R);
       }
       R = reduce16(R);
       if (sub == 0) {
@@ -690,9 +839,9 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
 #pragma unroll
     for (int k = 0; k < NE3; ++k) Gr[k] *= ele;
     for (int k = 0; k < kChunk; ++k) {
-      const float w = __expf(sm.l[k]) * sm.dy[k * kHeadDim + sp];
+      const float w = __expf(sm.l[k]) * sm.dy[k * kPX + sp];
 #pragma unroll
-      for (int m = 0; m < NE3; ++m) Gr[m] = fmaf(w, sm.C[k * N + sc + m], Gr[m]);
+      for (int m = 0; m < NE3; ++m) Gr[m] = fmaf(w, sm.C[k * PB + sc + m], Gr[m]);
     }
     __syncthreads();
   }
@@ -776,6 +925,10 @@ int check_ssm_shape(const char* fn, const tree_attn_ssm_shape* sh) {
 
 size_t state_floats(const tree_attn_mamba_plan_s* p, const tree_attn_ssm_shape* sh) {
   return size_t(p->U) * sh->num_heads * sh->head_dim * sh->state_dim;
+}
+
+size_t saved_state_floats(const tree_attn_mamba_plan_s* p, const tree_attn_ssm_shape* sh) {
+  return state_floats(p, sh) * kChunksPerUnit;
 }
 
 int hip_error(const char* fn, hipError_t e) {
@@ -927,7 +1080,7 @@ int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int
 
 size_t tree_attn_ssm_states_bytes(tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape) {
   if (!plan || !shape || shape->num_heads < 1 || shape->head_dim < 1 || shape->state_dim < 1) return 0;
-  return align256(state_floats(plan, shape) * 4);
+  return align256(saved_state_floats(plan, shape) * 4);
 }
 
 size_t tree_attn_ssm_workspace_bytes(tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape) {
@@ -952,8 +1105,10 @@ int tree_attn_ssm_bwd(const float* x, const float* dt, const float* A, const flo
   if (int rc = check_ssm_shape(fn, shape)) return rc;
   if (!x || !dt || !A || !B || !C || !D || !dy || !states || !dx || !ddt || !dA || !dB || !dC || !dD || !workspace)
     return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL pointer");
-  if (!aligned16(C) || !aligned16(states) || !aligned16(workspace))
-    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": C, states and workspace must be 16-byte aligned");
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(B) || !aligned16(C) || !aligned16(states) ||
+      !aligned16(workspace))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT,
+                        std::string(fn) + ": x, dy, dx, B, C, states and workspace must be 16-byte aligned");
   if (states_bytes < tree_attn_ssm_states_bytes(plan, shape))
     return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": states buffer too small");
   if (workspace_bytes < tree_attn_ssm_bwd_workspace_bytes(plan, shape))
@@ -992,8 +1147,10 @@ int tree_attn_ssm_fwd(const float* x, const float* dt, const float* A, const flo
   if (int rc = check_ssm_shape(fn, shape)) return rc;
   if (!x || !dt || !A || !B || !C || !D || !y || !states || !workspace)
     return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL pointer");
-  if (!aligned16(B) || !aligned16(C) || !aligned16(states) || !aligned16(workspace))
-    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": B, C, states and workspace must be 16-byte aligned");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(B) || !aligned16(C) || !aligned16(states) ||
+      !aligned16(workspace))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT,
+                        std::string(fn) + ": x, y, B, C, states and workspace must be 16-byte aligned");
   if (states_bytes < tree_attn_ssm_states_bytes(plan, shape))
     return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": states buffer too small");
   if (workspace_bytes < tree_attn_ssm_workspace_bytes(plan, shape))

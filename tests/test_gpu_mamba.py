@@ -81,13 +81,21 @@ def test_ssm_forward_matches_oracle(name, N, H, G):
     torch.cuda.synchronize()
     y_ref = oracle.ssm_forward(*(d[k] for k in keys), topo)
     e = rel_l2(y.cpu().numpy(), y_ref)
-    # the saved state before each unit is the oracle's state after the unit's predecessor token
+    # the saved state before each 32-token chunk of a unit is the oracle's
+    # state after the chunk's predecessor token
     S_ref = oracle.ssm_states(d["x"], d["dt"], d["A"], d["B"], topo)
-    st = plan.export("unit_start")
+    st, ln = plan.export("unit_start"), plan.export("unit_len")
     prev = oracle.previous_token(topo)
-    saved = states[: st.size * H * 64 * N * 4].view(torch.float32).view(st.size, H, 64, N).cpu().numpy()
-    ref = np.stack([S_ref[prev[s]] if prev[s] >= 0 else np.zeros_like(S_ref[0]) for s in st])
-    e_s = rel_l2(saved, ref) if np.any(ref) else float(np.abs(saved).max())
+    cpu = plan.info()["unit_tokens"] // 32
+    saved = states[: st.size * cpu * H * 64 * N * 4].view(torch.float32).view(st.size, cpu, H, 64, N).cpu().numpy()
+    got, ref = [], []
+    for u in range(st.size):
+        for c in range(-(-int(ln[u]) // 32)):
+            first = int(st[u]) + 32 * c
+            got.append(saved[u, c])
+            ref.append(S_ref[prev[first]] if prev[first] >= 0 else np.zeros_like(S_ref[0]))
+    got, ref = np.stack(got), np.stack(ref)
+    e_s = rel_l2(got, ref) if np.any(ref) else float(np.abs(got).max())
     log(f"  y rel-L2 {e:.2e}, saved states rel-L2 {e_s:.2e}")
     assert e <= TOL and e_s <= TOL
     y2, _ = sp.ssm_fwd(*(t[k] for k in keys), plan)
