@@ -615,22 +615,30 @@ __global__ __launch_bounds__(256) void ssm_bwd_propagate_kernel(ScanBwdArgs a) {
 
 constexpr int kBwdThreads = 512;
 
-// LDS rows are padded by one float so that lanes walking down a column
-// (different rows, same column) hit different banks
-constexpr int kPX = kHeadDim + 1;  // x, dy rows and (G B_j) rows
-constexpr int kPCB = kChunk + 1;   // C_k.B_j and x_j.dy_k rows
+// LDS rows are padded by four floats: rows stay 16-byte aligned for b128
+// reads, and lanes reading the same column of consecutive rows hit
+// different banks
+constexpr int kPX = kHeadDim + 4;  // x, dy rows and (G B_j) rows
+constexpr int kPZ = kChunk + 1;    // C_k.B_j, x_j.dy_k and Z rows (scalar reads)
 
 template <int N>
 struct BwdSmem {
-  static constexpr int PB = N + 1;  // B, C, S0, G rows
+  static constexpr int PB = N + 4;  // B, C, S0, G rows
   float x[kChunk * kPX], dy[kChunk * kPX];
   float B[kChunk * PB], C[kChunk * PB];
   float S0[kHeadDim * PB], G[kHeadDim * PB];
-  float CB[kChunk * kPCB], XD[kChunk * kPCB];  // [k][j]: C_k.B_j, x_j.dy_k
-  float GB[kChunk * kPX];                      // [j][p]: (G B_j)[p]
+  float CB[kChunk * kPZ], XD[kChunk * kPZ];  // [k][j]: C_k.B_j, x_j.dy_k
+  float Z[kChunk * kPZ];                     // [k][j], j < k: e^(l_k-l_j) dt_j (x_j.dy_k)(C_k.B_j)
+  float GB[kChunk * kPX];                    // [j][p]: (G B_j)[p]
   float dt[kChunk], l[kChunk], q[kChunk], r[kChunk], s[kChunk];
   float red[kBwdThreads / 64];
 };
+
+__device__ inline float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+__device__ inline float dot4(float4 a, float4 b, float acc) {
+  return fmaf(a.w, b.w, fmaf(a.z, b.z, fmaf(a.y, b.y, fmaf(a.x, b.x, acc))));
+}
 
 __device__ inline float reduce16(float v) {  // sum over 16 consecutive lanes
   v += __shfl_xor(v, 1);
@@ -686,17 +694,27 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
     }
     const int c0 = t0 + c * kChunk, clen = min(kChunk, len - c * kChunk);
     // stage the chunk (padding: zeros, so padded tokens contribute nothing)
-    for (int e = tid; e < kChunk * kHeadDim; e += kBwdThreads) {
-      const int k = e / kHeadDim, p = e % kHeadDim;
-      const size_t off = ((size_t)(c0 + k) * a.H + h) * kHeadDim + p;
-      sm.x[k * kPX + p] = k < clen ? a.x[off] : 0.f;
-      sm.dy[k * kPX + p] = k < clen ? a.dy[off] : 0.f;
+    for (int e = tid; e < kChunk * (kHeadDim / 4); e += kBwdThreads) {
+      const int k = e / (kHeadDim / 4), q = e % (kHeadDim / 4);
+      float4 vx = make_float4(0.f, 0.f, 0.f, 0.f), vy = vx;
+      if (k < clen) {
+        const size_t off = ((size_t)(c0 + k) * a.H + h) * kHeadDim;
+        vx = reinterpret_cast<const float4*>(a.x + off)[q];
+        vy = reinterpret_cast<const float4*>(a.dy + off)[q];
+      }
+      *reinterpret_cast<float4*>(&sm.x[k * kPX + 4 * q]) = vx;
+      *reinterpret_cast<float4*>(&sm.dy[k * kPX + 4 * q]) = vy;
     }
-    for (int e = tid; e < kChunk * N; e += kBwdThreads) {
-      const int k = e / N, n = e % N;
-      const size_t off = ((size_t)(c0 + k) * a.G + g) * N + n;
-      sm.B[k * PB + n] = k < clen ? a.B[off] : 0.f;
-      sm.C[k * PB + n] = k < clen ? a.C[off] : 0.f;
+    for (int e = tid; e < kChunk * (N / 4); e += kBwdThreads) {
+      const int k = e / (N / 4), q = e % (N / 4);
+      float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
+      if (k < clen) {
+        const size_t off = ((size_t)(c0 + k) * a.G + g) * N;
+        vb = reinterpret_cast<const float4*>(a.B + off)[q];
+        vc = reinterpret_cast<const float4*>(a.C + off)[q];
+      }
+      *reinterpret_cast<float4*>(&sm.B[k * PB + 4 * q]) = vb;
+      *reinterpret_cast<float4*>(&sm.C[k * PB + 4 * q]) = vc;
     }
     if (tid < kChunk) sm.dt[tid] = tid < clen ? a.dt[(size_t)(c0 + tid) * a.H + h] : 0.f;
 #pragma unroll
@@ -717,20 +735,42 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
 #pragma unroll
     for (int k = 0; k < NE3; ++k) gs = fmaf(Gr[k], S0r[k], gs);
     gs = block_sum(gs, sm.red);  // (its barriers also publish l)
-    // CB, XD and G B
-    for (int e = tid; e < kChunk * kChunk; e += kBwdThreads) {
-      const int k = e / kChunk, j = e % kChunk;
-      float cb = 0.f, xd = 0.f;
-      for (int n = 0; n < N; ++n) cb = fmaf(sm.C[k * PB + n], sm.B[j * PB + n], cb);
-      for (int p = 0; p < kHeadDim; ++p) xd = fmaf(sm.x[j * kPX + p], sm.dy[k * kPX + p], xd);
-      sm.CB[k * kPCB + j] = cb;
-      sm.XD[k * kPCB + j] = xd;
+    // CB, XD and Z: thread (k, jq) computes columns jq and jq + 16 of row k
+    {
+      const int k = tid >> 4, jq = tid & 15;
+      float cb0 = 0.f, cb1 = 0.f, xd0 = 0.f, xd1 = 0.f;
+#pragma unroll 8
+      for (int n = 0; n < N; n += 4) {
+        const float4 c = lds4(&sm.C[k * PB + n]);
+        cb0 = dot4(c, lds4(&sm.B[jq * PB + n]), cb0);
+        cb1 = dot4(c, lds4(&sm.B[(jq + 16) * PB + n]), cb1);
+      }
+#pragma unroll 8
+      for (int p = 0; p < kHeadDim; p += 4) {
+        const float4 d = lds4(&sm.dy[k * kPX + p]);
+        xd0 = dot4(d, lds4(&sm.x[jq * kPX + p]), xd0);
+        xd1 = dot4(d, lds4(&sm.x[(jq + 16) * kPX + p]), xd1);
+      }
+      sm.CB[k * kPZ + jq] = cb0;
+      sm.CB[k * kPZ + jq + 16] = cb1;
+      sm.XD[k * kPZ + jq] = xd0;
+      sm.XD[k * kPZ + jq + 16] = xd1;
+      const float lk = sm.l[k];
+      sm.Z[k * kPZ + jq] = jq < k ? __expf(lk - sm.l[jq]) * sm.dt[jq] * xd0 * cb0 : 0.f;
+      sm.Z[k * kPZ + jq + 16] = jq + 16 < k ? __expf(lk - sm.l[jq + 16]) * sm.dt[jq + 16] * xd1 * cb1 : 0.f;
     }
-    for (int e = tid; e < kChunk * kHeadDim; e += kBwdThreads) {
-      const int j = e / kHeadDim, p = e % kHeadDim;
-      float acc = 0.f;
-      for (int n = 0; n < N; ++n) acc = fmaf(sm.G[p * PB + n], sm.B[j * PB + n], acc);
-      sm.GB[j * kPX + p] = acc;
+    // G B: thread (j, pq) computes rows pq, pq + 16, pq + 32, pq + 48
+    {
+      const int j = tid >> 4, pq = tid & 15;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int n = 0; n < N; n += 4) {
+        const float4 b = lds4(&sm.B[j * PB + n]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = dot4(b, lds4(&sm.G[(pq + 16 * r) * PB + n]), acc[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.GB[j * kPX + pq + 16 * r] = acc[r];
     }
     __syncthreads();
     const float le = sm.l[kChunk - 1];
@@ -745,9 +785,16 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
       for (int p = 0; p < kHeadDim; ++p) {
         const float dyp = sm.dy[k * kPX + p], xp = sm.x[k * kPX + p];
 #pragma unroll
-        for (int m = 0; m < NN; ++m) {
-          s0dy[m] = fmaf(sm.S0[p * PB + n0 + m], dyp, s0dy[m]);
-          gx[m] = fmaf(sm.G[p * PB + n0 + m], xp, gx[m]);
+        for (int m = 0; m < NN; m += 4) {
+          const float4 sv = lds4(&sm.S0[p * PB + n0 + m]), gv = lds4(&sm.G[p * PB + n0 + m]);
+          s0dy[m] = fmaf(sv.x, dyp, s0dy[m]);
+          s0dy[m + 1] = fmaf(sv.y, dyp, s0dy[m + 1]);
+          s0dy[m + 2] = fmaf(sv.z, dyp, s0dy[m + 2]);
+          s0dy[m + 3] = fmaf(sv.w, dyp, s0dy[m + 3]);
+          gx[m] = fmaf(gv.x, xp, gx[m]);
+          gx[m + 1] = fmaf(gv.y, xp, gx[m + 1]);
+          gx[m + 2] = fmaf(gv.z, xp, gx[m + 2]);
+          gx[m + 3] = fmaf(gv.w, xp, gx[m + 3]);
         }
       }
       const float ek = __expf(lk);
@@ -759,14 +806,26 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
         dB[m] = __expf(le - lk) * gx[m];
       }
       for (int j = 0; j <= k; ++j) {
-        const float w = __expf(lk - sm.l[j]) * sm.dt[j] * sm.XD[k * kPCB + j];
+        const float w = __expf(lk - sm.l[j]) * sm.dt[j] * sm.XD[k * kPZ + j];
 #pragma unroll
-        for (int m = 0; m < NN; ++m) dC[m] = fmaf(w, sm.B[j * PB + n0 + m], dC[m]);
+        for (int m = 0; m < NN; m += 4) {
+          const float4 bv = lds4(&sm.B[j * PB + n0 + m]);
+          dC[m] = fmaf(w, bv.x, dC[m]);
+          dC[m + 1] = fmaf(w, bv.y, dC[m + 1]);
+          dC[m + 2] = fmaf(w, bv.z, dC[m + 2]);
+          dC[m + 3] = fmaf(w, bv.w, dC[m + 3]);
+        }
       }
       for (int m2 = k; m2 < kChunk; ++m2) {
-        const float w = __expf(sm.l[m2] - lk) * sm.XD[m2 * kPCB + k];
+        const float w = __expf(sm.l[m2] - lk) * sm.XD[m2 * kPZ + k];
 #pragma unroll
-        for (int m = 0; m < NN; ++m) dB[m] = fmaf(w, sm.C[m2 * PB + n0 + m], dB[m]);
+        for (int m = 0; m < NN; m += 4) {
+          const float4 cv = lds4(&sm.C[m2 * PB + n0 + m]);
+          dB[m] = fmaf(w, cv.x, dB[m]);
+          dB[m + 1] = fmaf(w, cv.y, dB[m + 1]);
+          dB[m + 2] = fmaf(w, cv.z, dB[m + 2]);
+          dB[m + 3] = fmaf(w, cv.w, dB[m + 3]);
+        }
       }
       qp = reduce16(qp);
       if ((tid & 15) == 0) sm.q[k] = ek * qp;
@@ -790,9 +849,12 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
 #pragma unroll
       for (int m = 0; m < 4; ++m) br[m] = eg * sm.GB[j * kPX + p0 + m];
       for (int k = j; k < kChunk; ++k) {
-        const float w = __expf(sm.l[k] - lj) * sm.CB[k * kPCB + j];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) br[m] = fmaf(w, sm.dy[k * kPX + p0 + m], br[m]);
+        const float w = __expf(sm.l[k] - lj) * sm.CB[k * kPZ + j];
+        const float4 dv = lds4(&sm.dy[k * kPX + p0]);
+        br[0] = fmaf(w, dv.x, br[0]);
+        br[1] = fmaf(w, dv.y, br[1]);
+        br[2] = fmaf(w, dv.z, br[2]);
+        br[3] = fmaf(w, dv.w, br[3]);
       }
       float sp_ = 0.f, rp = 0.f, dd = 0.f;
       float dxv[4];
@@ -821,11 +883,8 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
     {
       const int i = tid >> 4, sub = tid & 15;
       float R = 0.f;
-      for (int k = i + sub; k < kChunk; k += 16) {
-        const float lk = sm.l[k];
-        for (int j = 0; j < i; ++j)
-          R = fmaf(__expf(lk - sm.l[j]) * sm.dt[j], sm.XD[k * kPCB + j] * sm.CB[k * kPCB + j], R);
-      }
+      for (int k = i + sub; k < kChunk; k += 16)
+        for (int j = 0; j < i; ++j) R += sm.Z[k * kPZ + j];
       R = reduce16(R);
       if (sub == 0) {
         float W = R + ele * gs;
@@ -841,7 +900,13 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
     for (int k = 0; k < kChunk; ++k) {
       const float w = __expf(sm.l[k]) * sm.dy[k * kPX + sp];
 #pragma unroll
-      for (int m = 0; m < NE3; ++m) Gr[m] = fmaf(w, sm.C[k * PB + sc + m], Gr[m]);
+      for (int m = 0; m < NE3; m += 4) {
+        const float4 cv = lds4(&sm.C[k * PB + sc + m]);
+        Gr[m] = fmaf(w, cv.x, Gr[m]);
+        Gr[m + 1] = fmaf(w, cv.y, Gr[m + 1]);
+        Gr[m + 2] = fmaf(w, cv.z, Gr[m + 2]);
+        Gr[m + 3] = fmaf(w, cv.w, Gr[m + 3]);
+      }
     }
     __syncthreads();
   }
