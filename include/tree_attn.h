@@ -245,7 +245,7 @@ int tree_attn_edge_loss_bwd(const void* hidden, const void* weight, int32_t hidd
  * [channels, width], bias [channels]:
  *   y[i, c] = bias[c] + sum_{j < width} weight[c, j] x[prev^(width-1-j)(i), c]
  * (terms past a root are zero).  channels a multiple of 4, width 1..4;
- * x, y, dy, dx, bias 16-byte aligned.
+ * x, y, dy, dx, weight, bias 16-byte aligned.
  *
  * Selective state-space recurrence with a scalar decay per head (Mamba-2
  * form), x, y: [T, H, 64]; dt: [T, H] (positive step sizes, after any

@@ -152,49 +152,81 @@ hipError_t upload_mamba_plan(tree_attn_mamba_plan_s& m) {
 // ---------------------------------------------------------------------------
 // convolution
 
-// one thread per (token, 4 channels)
-__global__ void conv_fwd_kernel(const float4* __restrict__ x, const float* __restrict__ w,
-                                const float4* __restrict__ bias, const int32_t* __restrict__ halo, int T, int C4,
-                                int W, float4* __restrict__ y) {
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long long)T * C4) return;
-  const int i = int(idx / C4), c4 = int(idx % C4), c = 4 * c4;
-  float4 acc = bias[c4];
-  for (int k = 0; k < W; ++k) {  // k steps back along the path
-    const int src = k == 0 ? i : halo[(long long)i * kHalo + k - 1];
-    if (src < 0) break;
-    const float4 v = x[(long long)src * C4 + c4];
-    const int j = W - 1 - k;
-    acc.x = fmaf(w[(c + 0) * W + j], v.x, acc.x);
-    acc.y = fmaf(w[(c + 1) * W + j], v.y, acc.y);
-    acc.z = fmaf(w[(c + 2) * W + j], v.z, acc.z);
-    acc.w = fmaf(w[(c + 3) * W + j], v.w, acc.w);
+// weights of channels c .. c+3 at tap j (w is [C][W])
+template <int W>
+__device__ inline void load_taps(const float* __restrict__ w, int c, float4 (&t)[W]) {
+  if constexpr (W == 4) {
+    const float4 r0 = reinterpret_cast<const float4*>(w + (c + 0) * 4)[0];
+    const float4 r1 = reinterpret_cast<const float4*>(w + (c + 1) * 4)[0];
+    const float4 r2 = reinterpret_cast<const float4*>(w + (c + 2) * 4)[0];
+    const float4 r3 = reinterpret_cast<const float4*>(w + (c + 3) * 4)[0];
+    t[0] = make_float4(r0.x, r1.x, r2.x, r3.x);
+    t[1] = make_float4(r0.y, r1.y, r2.y, r3.y);
+    t[2] = make_float4(r0.z, r1.z, r2.z, r3.z);
+    t[3] = make_float4(r0.w, r1.w, r2.w, r3.w);
+  } else {
+#pragma unroll
+    for (int j = 0; j < W; ++j) t[j] = make_float4(w[c * W + j], w[(c + 1) * W + j], w[(c + 2) * W + j], w[(c + 3) * W + j]);
   }
-  y[idx] = acc;
+}
+
+__device__ inline float4 fma4(float4 a, float4 b, float4 c) {
+  return make_float4(fmaf(a.x, b.x, c.x), fmaf(a.y, b.y, c.y), fmaf(a.z, b.z, c.z), fmaf(a.w, b.w, c.w));
+}
+
+constexpr int kConvTokens = 16;  // tokens per block: the taps loaded once serve all of them
+
+// one block per (16 tokens, 256 channel quads): a thread loads its taps once
+// and walks the tokens; halo indices are block-uniform
+template <int W>
+__global__ __launch_bounds__(256) void conv_fwd_kernel(const float4* __restrict__ x, const float* __restrict__ w,
+                                                       const float4* __restrict__ bias,
+                                                       const int32_t* __restrict__ halo, int T, int C4,
+                                                       float4* __restrict__ y) {
+  const int c4 = blockIdx.y * blockDim.x + threadIdx.x;
+  if (c4 >= C4) return;
+  float4 t[W];
+  load_taps<W>(w, 4 * c4, t);
+  const float4 b = bias[c4];
+  const int i0 = blockIdx.x * kConvTokens, i1 = min(T, i0 + kConvTokens);
+  for (int i = i0; i < i1; ++i) {
+    float4 acc = fma4(t[W - 1], x[(size_t)i * C4 + c4], b);
+#pragma unroll
+    for (int k = 1; k < W; ++k) {  // k steps back along the path: tap W-1-k
+      const int src = halo[(size_t)i * kHalo + k - 1];
+      if (src < 0) break;
+      acc = fma4(t[W - 1 - k], x[(size_t)src * C4 + c4], acc);
+    }
+    y[(size_t)i * C4 + c4] = acc;
+  }
 }
 
 // dx[j] = w[:, W-1] dy[j] + sum over tokens i with prev^k(i) = j, 1 <= k < W,
 // of w[:, W-1-k] dy[i]; every branch's halo lands on the shared prefix
-__global__ void conv_bwd_dx_kernel(const float4* __restrict__ dy, const float* __restrict__ w,
-                                   const int32_t* __restrict__ csucc_ptr, const int32_t* __restrict__ csucc, int T,
-                                   int C4, int W, float4* __restrict__ dx) {
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long long)T * C4) return;
-  const int j = int(idx / C4), c4 = int(idx % C4), c = 4 * c4;
-  const float4 g = dy[idx];
-  float4 acc = make_float4(w[(c + 0) * W + W - 1] * g.x, w[(c + 1) * W + W - 1] * g.y, w[(c + 2) * W + W - 1] * g.z,
-                           w[(c + 3) * W + W - 1] * g.w);
-  for (int e = csucc_ptr[j]; e < csucc_ptr[j + 1]; ++e) {
-    const int ent = csucc[e], i = ent >> 2, k = ent & 3;
-    if (k >= W) continue;
-    const float4 v = dy[(long long)i * C4 + c4];
-    const int wj = W - 1 - k;
-    acc.x = fmaf(w[(c + 0) * W + wj], v.x, acc.x);
-    acc.y = fmaf(w[(c + 1) * W + wj], v.y, acc.y);
-    acc.z = fmaf(w[(c + 2) * W + wj], v.z, acc.z);
-    acc.w = fmaf(w[(c + 3) * W + wj], v.w, acc.w);
+template <int W>
+__global__ __launch_bounds__(256) void conv_bwd_dx_kernel(const float4* __restrict__ dy, const float* __restrict__ w,
+                                                          const int32_t* __restrict__ csucc_ptr,
+                                                          const int32_t* __restrict__ csucc, int T, int C4,
+                                                          float4* __restrict__ dx) {
+  const int c4 = blockIdx.y * blockDim.x + threadIdx.x;
+  if (c4 >= C4) return;
+  float4 t[W];
+  load_taps<W>(w, 4 * c4, t);
+  const int j0 = blockIdx.x * kConvTokens, j1 = min(T, j0 + kConvTokens);
+  for (int j = j0; j < j1; ++j) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    acc = fma4(t[W - 1], dy[(size_t)j * C4 + c4], acc);
+    for (int e = csucc_ptr[j]; e < csucc_ptr[j + 1]; ++e) {
+      const int ent = csucc[e], i = ent >> 2, k = ent & 3;
+      if (k >= W) continue;
+      float4 tk = t[0];
+#pragma unroll
+      for (int q = 1; q < W; ++q)
+        if (W - 1 - k == q) tk = t[q];
+      acc = fma4(tk, dy[(size_t)i * C4 + c4], acc);
+    }
+    dx[(size_t)j * C4 + c4] = acc;
   }
-  dx[idx] = acc;
 }
 
 constexpr int kConvRows = 256;  // tokens per partial of the weight gradient
@@ -1090,14 +1122,23 @@ int tree_attn_conv_fwd(const float* x, const float* weight, const float* bias, i
     return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": channels must be a positive multiple of 4");
   if (width < 1 || width > kConvMaxWidth)
     return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": width must be 1..4");
-  if (!aligned16(x) || !aligned16(bias) || !aligned16(y))
-    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": x, bias and y must be 16-byte aligned");
+  if (!aligned16(x) || !aligned16(bias) || !aligned16(y) || !aligned16(weight))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT,
+                        std::string(fn) + ": x, weight, bias and y must be 16-byte aligned");
   const int C4 = channels / 4;
-  const long long n = (long long)plan->T * C4;
-  hipLaunchKernelGGL(conv_fwd_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), reinterpret_cast<const float4*>(x), weight,
-                     reinterpret_cast<const float4*>(bias), plan->d_halo, plan->T, C4, width,
-                     reinterpret_cast<float4*>(y));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>((plan->T + kConvTokens - 1) / kConvTokens),
+                  static_cast<unsigned>((C4 + 255) / 256)),
+      block(256);
+  const float4* x4 = reinterpret_cast<const float4*>(x);
+  const float4* b4 = reinterpret_cast<const float4*>(bias);
+  float4* y4 = reinterpret_cast<float4*>(y);
+  switch (width) {
+    case 1: hipLaunchKernelGGL(conv_fwd_kernel<1>, grid, block, 0, s, x4, weight, b4, plan->d_halo, plan->T, C4, y4); break;
+    case 2: hipLaunchKernelGGL(conv_fwd_kernel<2>, grid, block, 0, s, x4, weight, b4, plan->d_halo, plan->T, C4, y4); break;
+    case 3: hipLaunchKernelGGL(conv_fwd_kernel<3>, grid, block, 0, s, x4, weight, b4, plan->d_halo, plan->T, C4, y4); break;
+    default: hipLaunchKernelGGL(conv_fwd_kernel<4>, grid, block, 0, s, x4, weight, b4, plan->d_halo, plan->T, C4, y4); break;
+  }
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_error(fn, e);
   return TREE_ATTN_OK;
 }
@@ -1120,8 +1161,8 @@ int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int
     return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": channels must be a positive multiple of 4");
   if (width < 1 || width > kConvMaxWidth)
     return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": width must be 1..4");
-  if (!aligned16(dy) || !aligned16(dx))
-    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": dy and dx must be 16-byte aligned");
+  if (!aligned16(dy) || !aligned16(dx) || !aligned16(weight))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": dy, dx and weight must be 16-byte aligned");
   const size_t need = tree_attn_conv_bwd_workspace_bytes(plan, channels, width);
   if (workspace_bytes < need)
     return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": workspace " +
@@ -1129,10 +1170,19 @@ int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int
                                                         std::to_string(need));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int C4 = channels / 4, T = plan->T;
-  const long long n = (long long)T * C4;
-  hipLaunchKernelGGL(conv_bwd_dx_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
-                     reinterpret_cast<const float4*>(dy), weight, plan->d_csucc_ptr, plan->d_csucc, T, C4, width,
-                     reinterpret_cast<float4*>(dx));
+  {
+    const dim3 grid(static_cast<unsigned>((T + kConvTokens - 1) / kConvTokens), static_cast<unsigned>((C4 + 255) / 256)),
+        block(256);
+    const float4* g4 = reinterpret_cast<const float4*>(dy);
+    float4* d4 = reinterpret_cast<float4*>(dx);
+    const int32_t *cp = plan->d_csucc_ptr, *cs = plan->d_csucc;
+    switch (width) {
+      case 1: hipLaunchKernelGGL(conv_bwd_dx_kernel<1>, grid, block, 0, s, g4, weight, cp, cs, T, C4, d4); break;
+      case 2: hipLaunchKernelGGL(conv_bwd_dx_kernel<2>, grid, block, 0, s, g4, weight, cp, cs, T, C4, d4); break;
+      case 3: hipLaunchKernelGGL(conv_bwd_dx_kernel<3>, grid, block, 0, s, g4, weight, cp, cs, T, C4, d4); break;
+      default: hipLaunchKernelGGL(conv_bwd_dx_kernel<4>, grid, block, 0, s, g4, weight, cp, cs, T, C4, d4); break;
+    }
+  }
   const int nblk = (T + kConvRows - 1) / kConvRows;
   float* partial = static_cast<float*>(workspace);
   hipLaunchKernelGGL(conv_bwd_dw_partial_kernel, dim3(unsigned(nblk), unsigned((channels + 63) / 64)), dim3(64), 0,
