@@ -807,68 +807,101 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
     __syncthreads();
     const float le = sm.l[kChunk - 1];
     const float ele = __expf(le);
-    // (token k, columns) phase: dC_k, dB_k, q_k
+    // (token k, columns) phase: dC_k, dB_k, q_k for tokens kp and kp + 16,
+    // columns [n0, n0 + NN2): each LDS read serves both tokens
     {
-      const int k = tid >> 4, n0 = (tid & 15) * NN;
-      const float lk = sm.l[k];
-      float s0dy[NN], gx[NN];
+      constexpr int NN2 = N / 32;
+      const int kp = tid >> 5, n0 = (tid & 31) * NN2;
+      const int ka = kp, kb = kp + 16;
+      const float la = sm.l[ka], lb = sm.l[kb];
+      float s0a[NN2], s0b[NN2], gxa[NN2], gxb[NN2];
 #pragma unroll
-      for (int m = 0; m < NN; ++m) s0dy[m] = gx[m] = 0.f;
+      for (int m = 0; m < NN2; ++m) s0a[m] = s0b[m] = gxa[m] = gxb[m] = 0.f;
+      auto row = [&](const float* base, float (&v)[NN2]) {
+        if constexpr (NN2 == 4) {
+          const float4 t = lds4(base);
+          v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
+        } else {
+#pragma unroll
+          for (int m = 0; m < NN2; ++m) v[m] = base[m];
+        }
+      };
       for (int p = 0; p < kHeadDim; ++p) {
-        const float dyp = sm.dy[k * kPX + p], xp = sm.x[k * kPX + p];
+        const float dya = sm.dy[ka * kPX + p], dyb = sm.dy[kb * kPX + p];
+        const float xa = sm.x[ka * kPX + p], xb = sm.x[kb * kPX + p];
+        float sv[NN2], gv[NN2];
+        row(&sm.S0[p * PB + n0], sv);
+        row(&sm.G[p * PB + n0], gv);
 #pragma unroll
-        for (int m = 0; m < NN; m += 4) {
-          const float4 sv = lds4(&sm.S0[p * PB + n0 + m]), gv = lds4(&sm.G[p * PB + n0 + m]);
-          s0dy[m] = fmaf(sv.x, dyp, s0dy[m]);
-          s0dy[m + 1] = fmaf(sv.y, dyp, s0dy[m + 1]);
-          s0dy[m + 2] = fmaf(sv.z, dyp, s0dy[m + 2]);
-          s0dy[m + 3] = fmaf(sv.w, dyp, s0dy[m + 3]);
-          gx[m] = fmaf(gv.x, xp, gx[m]);
-          gx[m + 1] = fmaf(gv.y, xp, gx[m + 1]);
-          gx[m + 2] = fmaf(gv.z, xp, gx[m + 2]);
-          gx[m + 3] = fmaf(gv.w, xp, gx[m + 3]);
+        for (int m = 0; m < NN2; ++m) {
+          s0a[m] = fmaf(sv[m], dya, s0a[m]);
+          s0b[m] = fmaf(sv[m], dyb, s0b[m]);
+          gxa[m] = fmaf(gv[m], xa, gxa[m]);
+          gxb[m] = fmaf(gv[m], xb, gxb[m]);
         }
       }
-      const float ek = __expf(lk);
-      float dC[NN], dB[NN], qp = 0.f;
+      const float ea = __expf(la), eb = __expf(lb);
+      float dCa[NN2], dCb[NN2], dBa[NN2], dBb[NN2], qa = 0.f, qb = 0.f;
+      {
+        float ca[NN2], cb[NN2];
+        row(&sm.C[ka * PB + n0], ca);
+        row(&sm.C[kb * PB + n0], cb);
+        const float fa = __expf(le - la), fb = __expf(le - lb);
 #pragma unroll
-      for (int m = 0; m < NN; ++m) {
-        qp = fmaf(s0dy[m], sm.C[k * PB + n0 + m], qp);
-        dC[m] = ek * s0dy[m];
-        dB[m] = __expf(le - lk) * gx[m];
-      }
-      for (int j = 0; j <= k; ++j) {
-        const float w = __expf(lk - sm.l[j]) * sm.dt[j] * sm.XD[k * kPZ + j];
-#pragma unroll
-        for (int m = 0; m < NN; m += 4) {
-          const float4 bv = lds4(&sm.B[j * PB + n0 + m]);
-          dC[m] = fmaf(w, bv.x, dC[m]);
-          dC[m + 1] = fmaf(w, bv.y, dC[m + 1]);
-          dC[m + 2] = fmaf(w, bv.z, dC[m + 2]);
-          dC[m + 3] = fmaf(w, bv.w, dC[m + 3]);
+        for (int m = 0; m < NN2; ++m) {
+          qa = fmaf(s0a[m], ca[m], qa);
+          qb = fmaf(s0b[m], cb[m], qb);
+          dCa[m] = ea * s0a[m];
+          dCb[m] = eb * s0b[m];
+          dBa[m] = fa * gxa[m];
+          dBb[m] = fb * gxb[m];
         }
       }
-      for (int m2 = k; m2 < kChunk; ++m2) {
-        const float w = __expf(sm.l[m2] - lk) * sm.XD[m2 * kPZ + k];
+      for (int j = 0; j <= kb; ++j) {  // dC: sources j <= k
+        const float lj = sm.l[j], dtj = sm.dt[j];
+        const float wa = j <= ka ? __expf(la - lj) * dtj * sm.XD[ka * kPZ + j] : 0.f;
+        const float wb = __expf(lb - lj) * dtj * sm.XD[kb * kPZ + j];
+        float bv[NN2];
+        row(&sm.B[j * PB + n0], bv);
 #pragma unroll
-        for (int m = 0; m < NN; m += 4) {
-          const float4 cv = lds4(&sm.C[m2 * PB + n0 + m]);
-          dB[m] = fmaf(w, cv.x, dB[m]);
-          dB[m + 1] = fmaf(w, cv.y, dB[m + 1]);
-          dB[m + 2] = fmaf(w, cv.z, dB[m + 2]);
-          dB[m + 3] = fmaf(w, cv.w, dB[m + 3]);
+        for (int m = 0; m < NN2; ++m) {
+          dCa[m] = fmaf(wa, bv[m], dCa[m]);
+          dCb[m] = fmaf(wb, bv[m], dCb[m]);
         }
       }
-      qp = reduce16(qp);
-      if ((tid & 15) == 0) sm.q[k] = ek * qp;
-      if (k < clen) {
-        const float dtk = sm.dt[k];
-        float* pc = a.dC_part + ((size_t)(c0 + k) * a.H + h) * N + n0;
-        float* pb = a.dB_part + ((size_t)(c0 + k) * a.H + h) * N + n0;
+      for (int m2 = ka; m2 < kChunk; ++m2) {  // dB: readers m2 >= k
+        const float lm = sm.l[m2];
+        const float wa = __expf(lm - la) * sm.XD[m2 * kPZ + ka];
+        const float wb = m2 >= kb ? __expf(lm - lb) * sm.XD[m2 * kPZ + kb] : 0.f;
+        float cv[NN2];
+        row(&sm.C[m2 * PB + n0], cv);
 #pragma unroll
-        for (int m = 0; m < NN; ++m) {
-          pc[m] = dC[m];
-          pb[m] = dtk * dB[m];
+        for (int m = 0; m < NN2; ++m) {
+          dBa[m] = fmaf(wa, cv[m], dBa[m]);
+          dBb[m] = fmaf(wb, cv[m], dBb[m]);
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) {
+        qa += __shfl_xor(qa, o);
+        qb += __shfl_xor(qb, o);
+      }
+      if ((tid & 31) == 0) {
+        sm.q[ka] = ea * qa;
+        sm.q[kb] = eb * qb;
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int k = half ? kb : ka;
+        if (k < clen) {
+          const float dtk = sm.dt[k];
+          float* pc = a.dC_part + ((size_t)(c0 + k) * a.H + h) * N + n0;
+          float* pb = a.dB_part + ((size_t)(c0 + k) * a.H + h) * N + n0;
+#pragma unroll
+          for (int m = 0; m < NN2; ++m) {
+            pc[m] = half ? dCb[m] : dCa[m];
+            pb[m] = dtk * (half ? dBb[m] : dBa[m]);
+          }
         }
       }
     }
