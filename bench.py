@@ -243,18 +243,19 @@ def edge_loss(args):
     with torch.cuda.device(dev):
         edges = sp.EdgePlan(src, tgt, T, V)
     ws = torch.empty(edges.workspace_bytes(d), dtype=torch.uint8, device=dev)
-    loss, lse = sp.edge_loss_fwd(h, W, edges, workspace=ws)
+    saved = torch.empty(edges.saved_bytes(), dtype=torch.uint8, device=dev)  # fp16 logits, forward -> backward
+    loss, lse = sp.edge_loss_fwd(h, W, edges, workspace=ws, saved=saved)
     for _ in range(args.warmup):
-        loss, lse = sp.edge_loss_fwd(h, W, edges, workspace=ws)
-        sp.edge_loss_bwd(h, W, edges, lse, dloss, workspace=ws)
+        loss, lse = sp.edge_loss_fwd(h, W, edges, workspace=ws, saved=saved)
+        sp.edge_loss_bwd(h, W, edges, lse, dloss, workspace=ws, saved=saved)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record()
-        loss, lse = sp.edge_loss_fwd(h, W, edges, workspace=ws)
+        loss, lse = sp.edge_loss_fwd(h, W, edges, workspace=ws, saved=saved)
         ev[i][1].record()
-        dh, dW = sp.edge_loss_bwd(h, W, edges, lse, dloss, workspace=ws)
+        dh, dW = sp.edge_loss_bwd(h, W, edges, lse, dloss, workspace=ws, saved=saved)
         ev[i][2].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps * 1e3
@@ -269,7 +270,8 @@ def edge_loss(args):
         "metric": "sampled-edge projection + loss, fwd+bwd", "value": round(tf, 2), "unit": "TFLOP/s",
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall, 4), "higher_is_better": True,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{w.name} edges", "tokens": T, "edges": E, "hidden": d, "vocab": V},
+        "config": {"workload": f"{w.name} edges", "tokens": T, "edges": E, "hidden": d, "vocab": V,
+                   "saved_logits_gb": round(edges.saved_bytes() / 1e9, 3)},
         "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
         "fwd_tflops": round(fwd_f / (f_ms * 1e-3) / 1e12, 2), "bwd_tflops": round(bwd_f / (b_ms * 1e-3) / 1e12, 2),
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": 2500.0, "unit": "TFLOP/s",

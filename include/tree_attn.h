@@ -219,14 +219,21 @@ int tree_attn_edges(const int32_t* edge_src, const int32_t* edge_tgt, int32_t nu
 int tree_attn_edges_destroy(tree_attn_edges_t edges);
 /* Device workspace bytes of the forward and backward for hidden size d. */
 size_t tree_attn_edge_loss_workspace_bytes(tree_attn_edges_t edges, int32_t hidden);
-/* loss, lse: [E] float32 outputs.  h: [num_tokens, d]; W: [vocab, d]. */
+/* Bytes of the optional saved logits: every logit as fp16, relative to its
+ * vocabulary chunk's row maximum (about 2 E V bytes; caller-owned). */
+size_t tree_attn_edge_loss_saved_bytes(tree_attn_edges_t edges);
+/* loss, lse: [E] float32 outputs.  h: [num_tokens, d]; W: [vocab, d].
+ * saved: NULL, or a buffer of tree_attn_edge_loss_saved_bytes the forward
+ * fills so that the backward need not recompute the logits. */
 int tree_attn_edge_loss_fwd(const void* hidden, const void* weight, int32_t hidden_dim, tree_attn_edges_t edges,
-                            float* loss, float* lse, void* workspace, size_t workspace_bytes, void* stream);
-/* lse from the forward; dloss [E]; dhidden [num_tokens, d] and dweight
- * [vocab, d] are overwritten. */
-int tree_attn_edge_loss_bwd(const void* hidden, const void* weight, int32_t hidden_dim, tree_attn_edges_t edges,
-                            const float* lse, const float* dloss, void* dhidden, void* dweight, void* workspace,
+                            float* loss, float* lse, void* saved, size_t saved_bytes, void* workspace,
                             size_t workspace_bytes, void* stream);
+/* lse from the forward; saved: the forward's saved logits for the same
+ * inputs, or NULL (the logits are recomputed); dloss [E]; dhidden
+ * [num_tokens, d] and dweight [vocab, d] are overwritten. */
+int tree_attn_edge_loss_bwd(const void* hidden, const void* weight, int32_t hidden_dim, tree_attn_edges_t edges,
+                            const float* lse, const void* saved, size_t saved_bytes, const float* dloss,
+                            void* dhidden, void* dweight, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Mamba state forking on the same forests (draft "feat(hybrid): add opt-in

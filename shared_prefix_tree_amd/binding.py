@@ -54,6 +54,7 @@ SYMBOLS = (
     "tree_attn_edges",
     "tree_attn_edges_destroy",
     "tree_attn_edge_loss_workspace_bytes",
+    "tree_attn_edge_loss_saved_bytes",
     "tree_attn_edge_loss_fwd",
     "tree_attn_edge_loss_bwd",
     "tree_attn_mamba_plan",
@@ -198,8 +199,12 @@ def library():
     lib.tree_attn_edges_destroy.argtypes = [vp]
     lib.tree_attn_edge_loss_workspace_bytes.argtypes = [vp, ctypes.c_int32]
     lib.tree_attn_edge_loss_workspace_bytes.restype = ctypes.c_size_t
-    lib.tree_attn_edge_loss_fwd.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
-    lib.tree_attn_edge_loss_bwd.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.tree_attn_edge_loss_saved_bytes.argtypes = [vp]
+    lib.tree_attn_edge_loss_saved_bytes.restype = ctypes.c_size_t
+    lib.tree_attn_edge_loss_fwd.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp,
+                                            ctypes.c_size_t, vp]
+    lib.tree_attn_edge_loss_bwd.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, ctypes.c_size_t, vp, vp, vp, vp,
+                                            ctypes.c_size_t, vp]
     for name in ("tree_attn_edges", "tree_attn_edges_destroy", "tree_attn_edge_loss_fwd", "tree_attn_edge_loss_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     for name in ("tree_attn_mamba_plan", "tree_attn_mamba_plan_host"):
@@ -382,6 +387,9 @@ class EdgePlan:
     def workspace_bytes(self, hidden):
         return int(library().tree_attn_edge_loss_workspace_bytes(self._handle, int(hidden)))
 
+    def saved_bytes(self):
+        return int(library().tree_attn_edge_loss_saved_bytes(self._handle))
+
     def close(self):
         if self._handle is not None and _lib is not None:
             _lib.tree_attn_edges_destroy(self._handle)
@@ -408,8 +416,10 @@ def _edge_check(hidden, weight, edges):
     return d
 
 
-def edge_loss_fwd(hidden, weight, edges: EdgePlan, workspace=None, stream=None):
-    """Per-edge loss and log-sum-exp (``tree_attn_edge_loss_fwd``)."""
+def edge_loss_fwd(hidden, weight, edges: EdgePlan, workspace=None, stream=None, saved=None):
+    """Per-edge loss and log-sum-exp (``tree_attn_edge_loss_fwd``).  ``saved``:
+    None, or a uint8 device buffer of ``edges.saved_bytes()`` that the
+    forward fills with the logits for the backward."""
     import torch
 
     d = _edge_check(hidden, weight, edges)
@@ -421,13 +431,16 @@ def edge_loss_fwd(hidden, weight, edges: EdgePlan, workspace=None, stream=None):
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
         _check(library().tree_attn_edge_loss_fwd(hidden.data_ptr(), weight.data_ptr(), d, edges.handle,
-                                                 loss.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                                                 loss.data_ptr(), lse.data_ptr(),
+                                                 saved.data_ptr() if saved is not None else None,
+                                                 saved.numel() if saved is not None else 0, workspace.data_ptr(),
                                                  workspace.numel(), ctypes.c_void_p(s.cuda_stream)))
     return loss, lse
 
 
-def edge_loss_bwd(hidden, weight, edges: EdgePlan, lse, dloss, workspace=None, stream=None):
-    """Gradients (dhidden, dweight) of sum_e dloss[e] * loss[e]."""
+def edge_loss_bwd(hidden, weight, edges: EdgePlan, lse, dloss, workspace=None, stream=None, saved=None):
+    """Gradients (dhidden, dweight) of sum_e dloss[e] * loss[e]; ``saved``:
+    the forward's saved logits, or None to recompute them."""
     import torch
 
     d = _edge_check(hidden, weight, edges)
@@ -442,9 +455,10 @@ def edge_loss_bwd(hidden, weight, edges: EdgePlan, lse, dloss, workspace=None, s
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
         _check(library().tree_attn_edge_loss_bwd(hidden.data_ptr(), weight.data_ptr(), d, edges.handle,
-                                                 lse.data_ptr(), dloss.data_ptr(), dh.data_ptr(), dw.data_ptr(),
-                                                 workspace.data_ptr(), workspace.numel(),
-                                                 ctypes.c_void_p(s.cuda_stream)))
+                                                 lse.data_ptr(), saved.data_ptr() if saved is not None else None,
+                                                 saved.numel() if saved is not None else 0, dloss.data_ptr(),
+                                                 dh.data_ptr(), dw.data_ptr(), workspace.data_ptr(),
+                                                 workspace.numel(), ctypes.c_void_p(s.cuda_stream)))
     return dh, dw
 
 

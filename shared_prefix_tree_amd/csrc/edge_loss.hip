@@ -24,6 +24,7 @@
 // chunk's rows of dW.  dh is scattered back to the tokens by a per-token sum
 // over that token's edges in edge order.  No atomics anywhere (the GEMMs run
 // with rocBLAS atomics disabled), so results are bitwise reproducible.
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 
@@ -112,10 +113,20 @@ __device__ inline float block_reduce(float v, float* red, bool is_max) {
 
 // Running row statistics over one chunk: columns [c0, c0 + n) of the
 // vocabulary, logits[e, j] at L[e * ld + j]
+// Saved logits (optional): row e of chunk ci is kept as fp16 values of
+// logit - cmax[e][ci], where cmax is the chunk's row maximum, so every kept
+// value is <= 0 and the large probabilities keep fp16's relative precision.
+struct Saved {
+  __half* z;      // [E][V]
+  float* cmax;    // [E][nchunks]
+  int V, nchunks;
+};
+
 __global__ __launch_bounds__(kRowThreads) void chunk_stats_kernel(const float* __restrict__ L, int ld, int n, int c0,
                                                                   const int32_t* __restrict__ tgt,
                                                                   float* __restrict__ m, float* __restrict__ s,
-                                                                  float* __restrict__ tl, int first) {
+                                                                  float* __restrict__ tl, int first, Saved sv,
+                                                                  int ci) {
   __shared__ float red[kRowThreads / 64];
   const int e = blockIdx.x;
   const float* row = L + (long long)e * ld;
@@ -135,6 +146,27 @@ __global__ __launch_bounds__(kRowThreads) void chunk_stats_kernel(const float* _
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc += __expf(v[k][c] - m_new);
   acc = block_reduce(acc, red, false);
+  if (sv.z) {
+    __half* zr = sv.z + (long long)e * sv.V + c0;
+    const bool vec = ((sv.V & 3) == 0);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = 4 * (threadIdx.x + kRowThreads * k);
+      if (vec && j + 3 < n) {
+        const __half2 lo = __floats2half2_rn(v[k][0] - mx, v[k][1] - mx);
+        const __half2 hi = __floats2half2_rn(v[k][2] - mx, v[k][3] - mx);
+        uint2 pk;
+        pk.x = *reinterpret_cast<const unsigned*>(&lo);
+        pk.y = *reinterpret_cast<const unsigned*>(&hi);
+        *reinterpret_cast<uint2*>(zr + j) = pk;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (j + c < n) zr[j + c] = __float2half_rn(v[k][c] - mx);
+      }
+    }
+    if (threadIdx.x == 0) sv.cmax[(long long)e * sv.nchunks + ci] = mx;
+  }
   if (threadIdx.x == 0) {
     const float s_old = first ? 0.f : s[e] * __expf(m_old - m_new);
     m[e] = m_new;
@@ -179,6 +211,43 @@ __global__ __launch_bounds__(kRowThreads) void chunk_grad_kernel(const float* __
     unsigned short g[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) g[c] = f32_to_bf16((__expf(x[c] - le) - (j + c == t ? 1.f : 0.f)) * dl);
+    if (vec && j + 3 < n) {
+      *reinterpret_cast<uint2*>(grow + j) =
+          make_uint2(unsigned(g[0]) | (unsigned(g[1]) << 16), unsigned(g[2]) | (unsigned(g[3]) << 16));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (j + c < n) grow[j + c] = g[c];
+    }
+  }
+}
+
+// G from the saved logits: p = exp(z + cmax - lse)
+__global__ __launch_bounds__(kRowThreads) void chunk_grad_saved_kernel(Saved sv, int ci, int ld, int n, int c0,
+                                                                       const int32_t* __restrict__ tgt,
+                                                                       const float* __restrict__ lse,
+                                                                       const float* __restrict__ dloss,
+                                                                       unsigned short* __restrict__ G) {
+  const int e = blockIdx.x;
+  const __half* zr = sv.z + (long long)e * sv.V + c0;
+  unsigned short* grow = G + (long long)e * ld;
+  const float off = sv.cmax[(long long)e * sv.nchunks + ci] - lse[e], dl = dloss[e];
+  const int t = tgt[e] - c0;
+  const bool vec = ((sv.V & 3) == 0) && ((ld & 3) == 0);
+  for (int j = 4 * threadIdx.x; j < n; j += 4 * kRowThreads) {
+    float x[4];
+    if (vec && j + 3 < n) {
+      const uint2 pk = *reinterpret_cast<const uint2*>(zr + j);
+      const float2 lo = __half22float2(*reinterpret_cast<const __half2*>(&pk.x));
+      const float2 hi = __half22float2(*reinterpret_cast<const __half2*>(&pk.y));
+      x[0] = lo.x, x[1] = lo.y, x[2] = hi.x, x[3] = hi.y;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = j + c < n ? __half2float(zr[j + c]) : 0.f;
+    }
+    unsigned short g[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) g[c] = f32_to_bf16((__expf(x[c] + off) - (j + c == t ? 1.f : 0.f)) * dl);
     if (vec && j + 3 < n) {
       *reinterpret_cast<uint2*>(grow + j) =
           make_uint2(unsigned(g[0]) | (unsigned(g[1]) << 16), unsigned(g[2]) | (unsigned(g[3]) << 16));
@@ -382,11 +451,40 @@ size_t tree_attn_edge_loss_workspace_bytes(tree_attn_edges_t edges, int32_t hidd
   return workspace_layout(edges->E, hidden, edges->V, nullptr, nullptr);
 }
 
+size_t tree_attn_edge_loss_saved_bytes(tree_attn_edges_t edges) {
+  if (!edges) return 0;
+  const int nch = (edges->V + kVocabChunk - 1) / kVocabChunk;
+  return align256(size_t(edges->E) * edges->V * 2) + align256(size_t(edges->E) * nch * 4);
+}
+
+}  // extern "C"
+
+namespace {
+
+int saved_view(const char* fn, tree_attn_edges_t edges, void* saved, size_t saved_bytes, Saved* sv) {
+  *sv = Saved{nullptr, nullptr, edges->V, (edges->V + kVocabChunk - 1) / kVocabChunk};
+  if (!saved) return TREE_ATTN_OK;
+  if (!aligned16(saved))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": saved must be 16-byte aligned");
+  if (saved_bytes < tree_attn_edge_loss_saved_bytes(edges))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": saved buffer too small");
+  sv->z = static_cast<__half*>(saved);
+  sv->cmax = reinterpret_cast<float*>(static_cast<char*>(saved) + align256(size_t(edges->E) * edges->V * 2));
+  return TREE_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int tree_attn_edge_loss_fwd(const void* hidden, const void* weight, int32_t d, tree_attn_edges_t edges, float* loss,
-                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                            float* lse, void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   const char* fn = "tree_attn_edge_loss_fwd";
   if (int rc = check_call(fn, edges, d, hidden, weight, loss, workspace, workspace_bytes)) return rc;
   if (!lse) return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL pointer");
+  Saved sv;
+  if (int rc = saved_view(fn, edges, saved, saved_bytes, &sv)) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int E = edges->E, V = edges->V, chunk = std::min(V, kVocabChunk);
   Workspace w;
@@ -403,7 +501,7 @@ int tree_attn_edge_loss_fwd(const void* hidden, const void* weight, int32_t d, t
     if (rocblas_status st = chunk_logits(h, w, weight, E, d, c0, n, chunk); st != rocblas_status_success)
       return blas_error(fn, st);
     hipLaunchKernelGGL(chunk_stats_kernel, dim3(E), dim3(kRowThreads), 0, s, w.L, chunk, n, c0, edges->tgt, w.m, w.s,
-                       w.tl, c0 == 0 ? 1 : 0);
+                       w.tl, c0 == 0 ? 1 : 0, sv, c0 / kVocabChunk);
   }
   hipLaunchKernelGGL(finalize_kernel, dim3((E + 255) / 256), dim3(256), 0, s, w.m, w.s, w.tl, E, loss, lse);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_error(fn, e);
@@ -411,11 +509,13 @@ int tree_attn_edge_loss_fwd(const void* hidden, const void* weight, int32_t d, t
 }
 
 int tree_attn_edge_loss_bwd(const void* hidden, const void* weight, int32_t d, tree_attn_edges_t edges,
-                            const float* lse, const float* dloss, void* dhidden, void* dweight, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            const float* lse, const void* saved, size_t saved_bytes, const float* dloss,
+                            void* dhidden, void* dweight, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "tree_attn_edge_loss_bwd";
   if (int rc = check_call(fn, edges, d, hidden, weight, dhidden, workspace, workspace_bytes)) return rc;
   if (!lse || !dloss || !dweight) return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL pointer");
+  Saved sv;
+  if (int rc = saved_view(fn, edges, const_cast<void*>(saved), saved_bytes, &sv)) return rc;
   if (!aligned16(dhidden) || !aligned16(dweight))
     return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": pointers must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -431,10 +531,15 @@ int tree_attn_edge_loss_bwd(const void* hidden, const void* weight, int32_t d, t
                      static_cast<const uint4*>(hidden), edges->src, E, pieces, reinterpret_cast<uint4*>(w.hg));
   for (int c0 = 0; c0 < V; c0 += chunk) {
     const int n = std::min(chunk, V - c0);
-    if (rocblas_status st = chunk_logits(h, w, weight, E, d, c0, n, chunk); st != rocblas_status_success)
-      return blas_error(fn, st);
-    hipLaunchKernelGGL(chunk_grad_kernel, dim3(E), dim3(kRowThreads), 0, s, w.L, chunk, n, c0, edges->tgt, lse,
-                       dloss, w.G);
+    if (sv.z) {  // the forward kept this chunk's logits
+      hipLaunchKernelGGL(chunk_grad_saved_kernel, dim3(E), dim3(kRowThreads), 0, s, sv, c0 / kVocabChunk, chunk, n,
+                         c0, edges->tgt, lse, dloss, w.G);
+    } else {
+      if (rocblas_status st = chunk_logits(h, w, weight, E, d, c0, n, chunk); st != rocblas_status_success)
+        return blas_error(fn, st);
+      hipLaunchKernelGGL(chunk_grad_kernel, dim3(E), dim3(kRowThreads), 0, s, w.L, chunk, n, c0, edges->tgt, lse,
+                         dloss, w.G);
+    }
     // dhg^T [d, E] (+)= W_c^T [d, n] G_c^T [n, E]   (column-major views)
     rocblas_status st = gemm(h, rocblas_operation_none, rocblas_operation_none, d, E, n,
                              static_cast<const unsigned short*>(weight) + size_t(c0) * d, d, w.G, chunk,

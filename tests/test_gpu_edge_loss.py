@@ -44,12 +44,13 @@ def make_case(seed, T_max, d, V, p_sampled, w_std):
     return T, src, tgt, h, w, dloss
 
 
-def run(sp, T, src, tgt, h, w, dloss, d, V, dev):
+def run(sp, T, src, tgt, h, w, dloss, d, V, dev, keep_logits=False):
     with torch.cuda.device(dev):
         edges = sp.EdgePlan(src, tgt, T, V)
     ht, wt = bf16_tensor(h, dev), bf16_tensor(w, dev)
-    loss, lse = sp.edge_loss_fwd(ht, wt, edges)
-    dh, dw = sp.edge_loss_bwd(ht, wt, edges, lse, torch.from_numpy(dloss).to(dev))
+    saved = torch.empty(edges.saved_bytes(), dtype=torch.uint8, device=dev) if keep_logits else None
+    loss, lse = sp.edge_loss_fwd(ht, wt, edges, saved=saved)
+    dh, dw = sp.edge_loss_bwd(ht, wt, edges, lse, torch.from_numpy(dloss).to(dev), saved=saved)
     torch.cuda.synchronize()
     return loss, lse, dh, dw
 
@@ -63,14 +64,17 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("keep", [False, True], ids=["recompute", "saved_logits"])
 @pytest.mark.parametrize("label,seed,Tm,d,V,p,ws", CASES, ids=[c[0] for c in CASES])
-def test_edge_loss_matches_oracle(label, seed, Tm, d, V, p, ws):
+def test_edge_loss_matches_oracle(label, seed, Tm, d, V, p, ws, keep):
+    """Both backward paths: logits recomputed per chunk, or kept by the
+    forward as fp16 relative to each chunk's row maximum."""
     import shared_prefix_tree_amd as sp
 
     T, src, tgt, h, w, dloss = make_case(seed, Tm, d, V, p, ws)
-    log(f"edge loss {label}: T={T} E={src.size} d={d} V={V}")
+    log(f"edge loss {label}: T={T} E={src.size} d={d} V={V} saved logits={keep}")
     dev = "cuda:0"
-    loss, lse, dh, dw = run(sp, T, src, tgt, h, w, dloss, d, V, dev)
+    loss, lse, dh, dw = run(sp, T, src, tgt, h, w, dloss, d, V, dev, keep)
     hf, wf = bf16_to_f32(h), bf16_to_f32(w)
     loss_ref, lse_ref = oracle.edge_loss_forward(hf, wf, src, tgt)
     dh_ref, dw_ref = oracle.edge_loss_backward(hf, wf, src, tgt, dloss)
@@ -83,14 +87,15 @@ def test_edge_loss_matches_oracle(label, seed, Tm, d, V, p, ws):
     others = np.setdiff1d(np.arange(T), src)
     assert np.all(to_host(dh)[others] == 0.0)
     # bitwise reproducible
-    loss2, lse2, dh2, dw2 = run(sp, T, src, tgt, h, w, dloss, d, V, dev)
+    loss2, lse2, dh2, dw2 = run(sp, T, src, tgt, h, w, dloss, d, V, dev, keep)
     for a, b in ((loss, loss2), (lse, lse2), (dh, dh2), (dw, dw2)):
         assert torch.equal(a, b)
 
 
 def test_edge_loss_full_vocabulary_and_width():
     """A 4096-wide hidden state and a 131,072-word vocabulary (16 chunks):
-    every output against the oracle, on 48 edges of a small tree."""
+    every output against the oracle, on 48 edges of a small tree (saved
+    logits, as the benchmark runs)."""
     import shared_prefix_tree_amd as sp
 
     d, V = 4096, 131072
@@ -103,7 +108,7 @@ def test_edge_loss_full_vocabulary_and_width():
     w = make_tensor("weight", 45, V, 1, d, std=0.02)[:, 0]
     dloss = np.full(src.size, 1.0 / src.size, np.float32)
     log(f"edge loss full vocabulary: T={T} E={src.size} d={d} V={V}")
-    loss, lse, dh, dw = run(sp, T, src, tgt, h, w, dloss, d, V, "cuda:0")
+    loss, lse, dh, dw = run(sp, T, src, tgt, h, w, dloss, d, V, "cuda:0", keep_logits=True)
     hf, wf = bf16_to_f32(h), bf16_to_f32(w)
     loss_ref, lse_ref = oracle.edge_loss_forward(hf, wf, src, tgt)
     dh_ref, dw_ref = oracle.edge_loss_backward(hf, wf, src, tgt, dloss)
