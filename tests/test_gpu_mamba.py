@@ -148,3 +148,41 @@ def test_ssm_rejects_unsupported_shapes():
         sp.ssm_fwd(z(T, 2, 64), z(T, 2), z(2), z(T, 1, 32), z(T, 1, 32), z(2), plan)
     with pytest.raises(sp.TreeAttnError, match="multiple of 4"):
         sp.conv_fwd(z(T, 6), z(6, 4), z(6), plan)
+
+
+def test_ssm_at_the_benchmark_shape_on_two_groups():
+    """The benchmark's mixer shape (128 heads x 64, 8 groups, state 128) on a
+    ~1,000-token forest.  A group's heads read only that group's B and C, so
+    the oracle run on the 16 heads of one group alone gives exactly those
+    heads' outputs and the group's dB / dC; groups 0 and 7 are checked."""
+    import shared_prefix_tree_amd as sp
+
+    H, G, N = 128, 8, 128
+    rng = np.random.default_rng(97)
+    topo = random_forest(rng, max_tokens=1100, max_len=260, max_depth=5, p_new_root=0.05)
+    T = topo.total_tokens
+    d = mamba_tensors(97, T, heads=H, groups=G, state_dim=N)
+    dy = rng.standard_normal((T, H, 64)).astype(np.float32)
+    dev = "cuda:0"
+    keys = ("x", "dt", "A", "B", "C", "D")
+    t = dev_tensors({k: d[k] for k in keys}, dev)
+    with torch.cuda.device(dev):
+        plan = sp.MambaPlan.from_topology(topo)
+    log(f"ssm benchmark shape: T={T} units={plan.info()['num_units']}")
+    y, states = sp.ssm_fwd(*(t[k] for k in keys), plan)
+    grads = sp.ssm_bwd(*(t[k] for k in keys), torch.from_numpy(dy).to(dev), plan, states)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    dx, ddt, dA, dB, dC, dD = (g.cpu().numpy() for g in grads)
+    hpg = H // G
+    for g in (0, G - 1):
+        hs = slice(g * hpg, (g + 1) * hpg)
+        sub = {"x": d["x"][:, hs], "dt": d["dt"][:, hs], "A": d["A"][hs], "B": d["B"][:, g:g + 1],
+               "C": d["C"][:, g:g + 1], "D": d["D"][hs]}
+        y_ref = oracle.ssm_forward(*(sub[k] for k in keys), topo)
+        ref = oracle.ssm_backward(dy[:, hs], *(sub[k] for k in keys), topo)
+        got = (dx[:, hs], ddt[:, hs], dA[hs], dB[:, g:g + 1], dC[:, g:g + 1], dD[hs])
+        errs = {"y": rel_l2(y[:, hs], y_ref)}
+        errs.update({k: rel_l2(a, r) for k, a, r in zip(("dx", "ddt", "dA", "dB", "dC", "dD"), got, ref)})
+        log(f"  group {g}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+        assert all(v <= TOL for v in errs.values()), (g, errs)
