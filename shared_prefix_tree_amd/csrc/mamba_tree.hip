@@ -647,114 +647,178 @@ __global__ __launch_bounds__(256) void ssm_bwd_propagate_kernel(ScanBwdArgs a) {
 
 constexpr int kBwdThreads = 512;
 
-// LDS rows are padded by four floats: rows stay 16-byte aligned for b128
-// reads, and lanes reading the same column of consecutive rows hit
-// different banks
-constexpr int kPX = kHeadDim + 4;  // x, dy rows and (G B_j) rows
-constexpr int kPZ = kChunk + 1;    // C_k.B_j, x_j.dy_k and Z rows (scalar reads)
+// Chunk gradients on the fp32 matrix cores.  Every contraction of the chunk
+// form is a product of 32 x 32 tiles (v_mfma_f32_32x32x2f32: lane l feeds
+// A[l % 32][k0 + l / 32] and B[k0 + l / 32][l % 32]; accumulator r of lane l
+// is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]).  Operands are read from LDS
+// with a per-lane address; the eight waves share out the tiles by a fixed
+// table.  The gradient G leaving the chunk lives in accumulator layout, one
+// 32 x 32 tile of the 64 x N state per wave.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPX = kHeadDim + 4;  // x, dy, (G B_j) and bracket rows (16-byte aligned rows)
+constexpr int kPZ = kChunk + 1;    // 32 x 32 matrices
 
 template <int N>
 struct BwdSmem {
   static constexpr int PB = N + 4;  // B, C, S0, G rows
   float x[kChunk * kPX], dy[kChunk * kPX];
   float B[kChunk * PB], C[kChunk * PB];
-  float S0[kHeadDim * PB], G[kHeadDim * PB];
-  float CB[kChunk * kPZ], XD[kChunk * kPZ];  // [k][j]: C_k.B_j, x_j.dy_k
-  float Z[kChunk * kPZ];                     // [k][j], j < k: e^(l_k-l_j) dt_j (x_j.dy_k)(C_k.B_j)
-  float GB[kChunk * kPX];                    // [j][p]: (G B_j)[p]
+  float S0[kHeadDim * PB], G[kHeadDim * PB];  // reused as S0^T dy and G^T x ([k][n]) after the first products
+  float CB[kChunk * kPZ], XD[kChunk * kPZ];   // [k][j]: C_k.B_j, x_j.dy_k
+  float Z[kChunk * kPZ];                      // [k][j], j < k: e^(l_k-l_j) dt_j XD CB
+  float W1[kChunk * kPZ], W2[kChunk * kPZ], W3[kChunk * kPZ];
+  float GB[kChunk * kPX];                     // [j][p]: (G B_j)[p], then the dx bracket
   float dt[kChunk], l[kChunk], q[kChunk], r[kChunk], s[kChunk];
   float red[kBwdThreads / 64];
 };
 
-__device__ inline float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-
-__device__ inline float dot4(float4 a, float4 b, float acc) {
-  return fmaf(a.w, b.w, fmaf(a.z, b.z, fmaf(a.y, b.y, fmaf(a.x, b.x, acc))));
+// c += A B over K (a multiple of 2): A(i, k) = a[i ai + k ak], B(k, j) = b[k bk + j bj]
+template <int K>
+__device__ inline void mma_tile(f32x16& c, const float* a, int ai, int ak, const float* b, int bk, int bj, int ln) {
+  const int i = ln & 31, hk = ln >> 5;
+#pragma unroll 4
+  for (int k0 = 0; k0 < K; k0 += 2) {
+    const float av = a[i * ai + (k0 + hk) * ak];
+    const float bv = b[(k0 + hk) * bk + i * bj];
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, c, 0, 0, 0);
+  }
 }
 
-__device__ inline float reduce16(float v) {  // sum over 16 consecutive lanes
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+// ln: the lane index, passed in so that a loop can make it opaque (address
+// arithmetic is then redone per iteration instead of held in registers)
+__device__ inline int tile_row(int r, int ln) { return 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3); }
+__device__ inline int tile_col(int ln) { return ln & 31; }
+
+__device__ inline float reduce32(float v) {  // sum over 32 consecutive lanes
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o);
   return v;
 }
+
+// barrier for LDS hand-offs only: global loads issued ahead stay in flight
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // fixed-order sum over the block (all threads get the result)
 __device__ inline float block_sum(float v, float* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  __syncthreads();
+  lds_barrier();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
+  lds_barrier();
   float r = 0.f;
 #pragma unroll
   for (int w = 0; w < kBwdThreads / 64; ++w) r += red[w];
   return r;
 }
 
+// first products of a chunk, shared out over the waves:
+//   0: C B^T, 1: X D, 2..: G B (per 32 rows of G), then S0^T dy and G^T x (per 32 columns)
+template <int N>
+struct FirstJobs {
+  static constexpr int NT = N / 32;
+  // job ids per wave (-1: none); N = 128: CB | GB0 | GB1 | XD, S0dy0 | S0dy1, S0dy2 | S0dy3, Gx0 | Gx1, Gx2 | Gx3
+  static __device__ inline int job(int w, int slot) {
+    if constexpr (N == 128) {
+      if (slot == 0) return w == 0 ? 0 : w == 1 ? 2 : w == 2 ? 3 : w == 3 ? 1 : 2 * w - 3;
+      return w == 3 ? 4 : (w >= 4 && w <= 6) ? 2 * w - 2 : -1;
+    } else {
+      if (slot == 1) return -1;
+      return w == 0 ? 0 : w == 1 ? 2 : w == 2 ? 3 : w == 3 ? 1 : w;
+    }
+  }
+};
+
 template <int N>
 __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a) {
-  constexpr int NE3 = N / 8;   // state elements per thread (row p, columns c8 NE3 ..)
-  constexpr int NN = N / 16;   // columns per thread in the (token, column) phase
   constexpr int PB = BwdSmem<N>::PB;
+  constexpr int NT = N / 32;            // 32-column tiles of the state
+  constexpr int GT = 2 * NT;            // 32 x 32 tiles of the 64 x N state
   __shared__ __attribute__((aligned(16))) BwdSmem<N> sm;
   const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int g = h / (a.H / a.G);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = a.unit_start[u], len = a.unit_len[u];
   const int nch = (len + kChunk - 1) / kChunk;
   const float Ah = a.A[h], Dh = a.D[h];
+  const size_t hrow = (size_t(u) * a.H + h) * kHeadDim * N;
 
-  // state layout: row p, columns [c8 NE3, (c8 + 1) NE3)
-  const int sp = tid >> 3, sc = (tid & 7) * NE3;
-  float Gr[NE3];
-  {
-    const float* go = a.gout + (size_t(u) * a.H + h) * kHeadDim * N + size_t(sp) * N + sc;
+  // this wave's tile of G (and of S0): rows 32 gp .., columns 32 gn ..
+  const bool gown = wave < GT;
+  const int gp = wave / NT, gn = wave % NT;
+  f32x16 Gt;
 #pragma unroll
-    for (int k = 0; k < NE3; ++k) Gr[k] = go[k];
-  }
+  for (int r = 0; r < 16; ++r)
+    Gt[r] = gown ? a.gout[hrow + size_t(32 * gp + tile_row(r, tid & 63)) * N + 32 * gn + tile_col(tid & 63)] : 0.f;
   float dA_acc = 0.f, dD_acc = 0.f;
 
-  for (int c = nch - 1; c >= 0; --c) {
-    // the state before chunk c, saved by the forward pass
-    float S0r[NE3];
-    {
-      const float* s0 = a.states + state_index(u, c, a.H, h, N) + size_t(sp) * N + sc;
-#pragma unroll
-      for (int k = 0; k < NE3; ++k) S0r[k] = s0[k];
-    }
+  // the next chunk's inputs are loaded into registers while this one is
+  // processed (x, dy: one float4 per thread; B, C: N / 64 each)
+  constexpr int NBC = N / 64;
+  float4 pfx, pfy, pfb[NBC], pfc[NBC];
+  float pfdt = 0.f, pfs[16];
+  auto fetch = [&](int c) {
     const int c0 = t0 + c * kChunk, clen = min(kChunk, len - c * kChunk);
-    // stage the chunk (padding: zeros, so padded tokens contribute nothing)
-    for (int e = tid; e < kChunk * (kHeadDim / 4); e += kBwdThreads) {
-      const int k = e / (kHeadDim / 4), q = e % (kHeadDim / 4);
-      float4 vx = make_float4(0.f, 0.f, 0.f, 0.f), vy = vx;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    {
+      const int k = tid / (kHeadDim / 4), q = tid % (kHeadDim / 4);
+      pfx = pfy = z;
       if (k < clen) {
         const size_t off = ((size_t)(c0 + k) * a.H + h) * kHeadDim;
-        vx = reinterpret_cast<const float4*>(a.x + off)[q];
-        vy = reinterpret_cast<const float4*>(a.dy + off)[q];
+        pfx = reinterpret_cast<const float4*>(a.x + off)[q];
+        pfy = reinterpret_cast<const float4*>(a.dy + off)[q];
       }
-      *reinterpret_cast<float4*>(&sm.x[k * kPX + 4 * q]) = vx;
-      *reinterpret_cast<float4*>(&sm.dy[k * kPX + 4 * q]) = vy;
     }
-    for (int e = tid; e < kChunk * (N / 4); e += kBwdThreads) {
-      const int k = e / (N / 4), q = e % (N / 4);
-      float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
+#pragma unroll
+    for (int m = 0; m < NBC; ++m) {
+      const int e = tid + m * kBwdThreads, k = e / (N / 4), q = e % (N / 4);
+      pfb[m] = pfc[m] = z;
       if (k < clen) {
         const size_t off = ((size_t)(c0 + k) * a.G + g) * N;
-        vb = reinterpret_cast<const float4*>(a.B + off)[q];
-        vc = reinterpret_cast<const float4*>(a.C + off)[q];
+        pfb[m] = reinterpret_cast<const float4*>(a.B + off)[q];
+        pfc[m] = reinterpret_cast<const float4*>(a.C + off)[q];
       }
-      *reinterpret_cast<float4*>(&sm.B[k * PB + 4 * q]) = vb;
-      *reinterpret_cast<float4*>(&sm.C[k * PB + 4 * q]) = vc;
     }
-    if (tid < kChunk) sm.dt[tid] = tid < clen ? a.dt[(size_t)(c0 + tid) * a.H + h] : 0.f;
+    pfdt = tid < clen ? a.dt[(size_t)(c0 + tid) * a.H + h] : 0.f;
+    if (gown) {
+      const float* s0 = a.states + state_index(u, c, a.H, h, N);
 #pragma unroll
-    for (int k = 0; k < NE3; ++k) {
-      sm.S0[sp * PB + sc + k] = S0r[k];
-      sm.G[sp * PB + sc + k] = Gr[k];
+      for (int r = 0; r < 16; ++r)
+        pfs[r] = s0[size_t(32 * gp + tile_row(r, tid & 63)) * N + 32 * gn + tile_col(tid & 63)];
     }
-    __syncthreads();
+  };
+  fetch(nch - 1);
+
+  for (int c = nch - 1; c >= 0; --c) {
+    const int c0 = t0 + c * kChunk, clen = min(kChunk, len - c * kChunk);
+    int ln = tid & 63;
+    asm volatile("" : "+v"(ln));
+    // stage the chunk (padding: zeros, so padded tokens contribute nothing)
+    {
+      const int k = tid / (kHeadDim / 4), q = tid % (kHeadDim / 4);
+      *reinterpret_cast<float4*>(&sm.x[k * kPX + 4 * q]) = pfx;
+      *reinterpret_cast<float4*>(&sm.dy[k * kPX + 4 * q]) = pfy;
+    }
+#pragma unroll
+    for (int m = 0; m < NBC; ++m) {
+      const int e = tid + m * kBwdThreads, k = e / (N / 4), q = e % (N / 4);
+      *reinterpret_cast<float4*>(&sm.B[k * PB + 4 * q]) = pfb[m];
+      *reinterpret_cast<float4*>(&sm.C[k * PB + 4 * q]) = pfc[m];
+    }
+    if (tid < kChunk) sm.dt[tid] = pfdt;
+    // the state before the chunk (saved by the forward) and G, into LDS; <G, S0>
+    float gs = 0.f;
+    if (gown) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * gp + tile_row(r, ln), col = 32 * gn + tile_col(ln);
+        sm.S0[row * PB + col] = pfs[r];
+        sm.G[row * PB + col] = Gt[r];
+        gs = fmaf(Gt[r], pfs[r], gs);
+      }
+    }
+    if (c > 0) fetch(c - 1);  // in flight during this chunk
+    lds_barrier();
     if (tid == 0) {
       float l = 0.f;
       for (int k = 0; k < kChunk; ++k) {
@@ -762,218 +826,159 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
         sm.l[k] = l;
       }
     }
-    // <G, S0>
-    float gs = 0.f;
-#pragma unroll
-    for (int k = 0; k < NE3; ++k) gs = fmaf(Gr[k], S0r[k], gs);
     gs = block_sum(gs, sm.red);  // (its barriers also publish l)
-    // CB, XD and Z: thread (k, jq) computes columns jq and jq + 16 of row k
-    {
-      const int k = tid >> 4, jq = tid & 15;
-      float cb0 = 0.f, cb1 = 0.f, xd0 = 0.f, xd1 = 0.f;
-#pragma unroll 8
-      for (int n = 0; n < N; n += 4) {
-        const float4 c = lds4(&sm.C[k * PB + n]);
-        cb0 = dot4(c, lds4(&sm.B[jq * PB + n]), cb0);
-        cb1 = dot4(c, lds4(&sm.B[(jq + 16) * PB + n]), cb1);
-      }
-#pragma unroll 8
-      for (int p = 0; p < kHeadDim; p += 4) {
-        const float4 d = lds4(&sm.dy[k * kPX + p]);
-        xd0 = dot4(d, lds4(&sm.x[jq * kPX + p]), xd0);
-        xd1 = dot4(d, lds4(&sm.x[(jq + 16) * kPX + p]), xd1);
-      }
-      sm.CB[k * kPZ + jq] = cb0;
-      sm.CB[k * kPZ + jq + 16] = cb1;
-      sm.XD[k * kPZ + jq] = xd0;
-      sm.XD[k * kPZ + jq + 16] = xd1;
-      const float lk = sm.l[k];
-      sm.Z[k * kPZ + jq] = jq < k ? __expf(lk - sm.l[jq]) * sm.dt[jq] * xd0 * cb0 : 0.f;
-      sm.Z[k * kPZ + jq + 16] = jq + 16 < k ? __expf(lk - sm.l[jq + 16]) * sm.dt[jq + 16] * xd1 * cb1 : 0.f;
-    }
-    // G B: thread (j, pq) computes rows pq, pq + 16, pq + 32, pq + 48
-    {
-      const int j = tid >> 4, pq = tid & 15;
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int n = 0; n < N; n += 4) {
-        const float4 b = lds4(&sm.B[j * PB + n]);
+
+    // first products
+    f32x16 acc[2];
+    int jobs[2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = dot4(b, lds4(&sm.G[(pq + 16 * r) * PB + n]), acc[r]);
+    for (int sl = 0; sl < 2; ++sl) {
+      jobs[sl] = FirstJobs<N>::job(wave, sl);
+      acc[sl] = f32x16{};
+      const int j = jobs[sl];
+      if (j == 0) {
+        mma_tile<N>(acc[sl], sm.C, PB, 1, sm.B, 1, PB, ln);  // CB(k, j) = C_k . B_j
+      } else if (j == 1) {
+        mma_tile<kHeadDim>(acc[sl], sm.dy, kPX, 1, sm.x, 1, kPX, ln);  // XD(k, j) = dy_k . x_j
+      } else if (j >= 2 && j < 4) {
+        const int pt = j - 2;  // GB(j, p) = B_j . G_p, rows p in 32 pt ..
+        mma_tile<N>(acc[sl], sm.B, PB, 1, sm.G + 32 * pt * PB, 1, PB, ln);
+      } else if (j >= 4 && j < 4 + NT) {
+        const int nt = j - 4;  // S0^T dy: (k, n) = sum_p dy[k][p] S0[p][n]
+        mma_tile<kHeadDim>(acc[sl], sm.dy, kPX, 1, sm.S0 + 32 * nt, PB, 1, ln);
+      } else if (j >= 4 + NT) {
+        const int nt = j - 4 - NT;  // G^T x: (k, n) = sum_p x[k][p] G[p][n]
+        mma_tile<kHeadDim>(acc[sl], sm.x, kPX, 1, sm.G + 32 * nt, PB, 1, ln);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.GB[j * kPX + pq + 16 * r] = acc[r];
     }
-    __syncthreads();
+    lds_barrier();  // S0 and G are overwritten below
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int j = jobs[sl];
+      if (j < 0) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = tile_row(r, ln), col = tile_col(ln);
+        if (j == 0) sm.CB[row * kPZ + col] = acc[sl][r];
+        else if (j == 1) sm.XD[row * kPZ + col] = acc[sl][r];
+        else if (j < 4) sm.GB[row * kPX + 32 * (j - 2) + col] = acc[sl][r];
+        else if (j < 4 + NT) sm.S0[row * PB + 32 * (j - 4) + col] = acc[sl][r];
+        else sm.G[row * PB + 32 * (j - 4 - NT) + col] = acc[sl][r];
+      }
+    }
+    lds_barrier();
     const float le = sm.l[kChunk - 1];
     const float ele = __expf(le);
-    // (token k, columns) phase: dC_k, dB_k, q_k for tokens kp and kp + 16,
-    // columns [n0, n0 + NN2): each LDS read serves both tokens
-    {
-      constexpr int NN2 = N / 32;
-      const int kp = tid >> 5, n0 = (tid & 31) * NN2;
-      const int ka = kp, kb = kp + 16;
-      const float la = sm.l[ka], lb = sm.l[kb];
-      float s0a[NN2], s0b[NN2], gxa[NN2], gxb[NN2];
-#pragma unroll
-      for (int m = 0; m < NN2; ++m) s0a[m] = s0b[m] = gxa[m] = gxb[m] = 0.f;
-      auto row = [&](const float* base, float (&v)[NN2]) {
-        if constexpr (NN2 == 4) {
-          const float4 t = lds4(base);
-          v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
-        } else {
-#pragma unroll
-          for (int m = 0; m < NN2; ++m) v[m] = base[m];
-        }
-      };
-      for (int p = 0; p < kHeadDim; ++p) {
-        const float dya = sm.dy[ka * kPX + p], dyb = sm.dy[kb * kPX + p];
-        const float xa = sm.x[ka * kPX + p], xb = sm.x[kb * kPX + p];
-        float sv[NN2], gv[NN2];
-        row(&sm.S0[p * PB + n0], sv);
-        row(&sm.G[p * PB + n0], gv);
-#pragma unroll
-        for (int m = 0; m < NN2; ++m) {
-          s0a[m] = fmaf(sv[m], dya, s0a[m]);
-          s0b[m] = fmaf(sv[m], dyb, s0b[m]);
-          gxa[m] = fmaf(gv[m], xa, gxa[m]);
-          gxb[m] = fmaf(gv[m], xb, gxb[m]);
-        }
-      }
-      const float ea = __expf(la), eb = __expf(lb);
-      float dCa[NN2], dCb[NN2], dBa[NN2], dBb[NN2], qa = 0.f, qb = 0.f;
-      {
-        float ca[NN2], cb[NN2];
-        row(&sm.C[ka * PB + n0], ca);
-        row(&sm.C[kb * PB + n0], cb);
-        const float fa = __expf(le - la), fb = __expf(le - lb);
-#pragma unroll
-        for (int m = 0; m < NN2; ++m) {
-          qa = fmaf(s0a[m], ca[m], qa);
-          qb = fmaf(s0b[m], cb[m], qb);
-          dCa[m] = ea * s0a[m];
-          dCb[m] = eb * s0b[m];
-          dBa[m] = fa * gxa[m];
-          dBb[m] = fb * gxb[m];
-        }
-      }
-      for (int j = 0; j <= kb; ++j) {  // dC: sources j <= k
-        const float lj = sm.l[j], dtj = sm.dt[j];
-        const float wa = j <= ka ? __expf(la - lj) * dtj * sm.XD[ka * kPZ + j] : 0.f;
-        const float wb = __expf(lb - lj) * dtj * sm.XD[kb * kPZ + j];
-        float bv[NN2];
-        row(&sm.B[j * PB + n0], bv);
-#pragma unroll
-        for (int m = 0; m < NN2; ++m) {
-          dCa[m] = fmaf(wa, bv[m], dCa[m]);
-          dCb[m] = fmaf(wb, bv[m], dCb[m]);
-        }
-      }
-      for (int m2 = ka; m2 < kChunk; ++m2) {  // dB: readers m2 >= k
-        const float lm = sm.l[m2];
-        const float wa = __expf(lm - la) * sm.XD[m2 * kPZ + ka];
-        const float wb = m2 >= kb ? __expf(lm - lb) * sm.XD[m2 * kPZ + kb] : 0.f;
-        float cv[NN2];
-        row(&sm.C[m2 * PB + n0], cv);
-#pragma unroll
-        for (int m = 0; m < NN2; ++m) {
-          dBa[m] = fmaf(wa, cv[m], dBa[m]);
-          dBb[m] = fmaf(wb, cv[m], dBb[m]);
-        }
-      }
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) {
-        qa += __shfl_xor(qa, o);
-        qb += __shfl_xor(qb, o);
-      }
-      if ((tid & 31) == 0) {
-        sm.q[ka] = ea * qa;
-        sm.q[kb] = eb * qb;
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int k = half ? kb : ka;
-        if (k < clen) {
-          const float dtk = sm.dt[k];
-          float* pc = a.dC_part + ((size_t)(c0 + k) * a.H + h) * N + n0;
-          float* pb = a.dB_part + ((size_t)(c0 + k) * a.H + h) * N + n0;
-#pragma unroll
-          for (int m = 0; m < NN2; ++m) {
-            pc[m] = half ? dCb[m] : dCa[m];
-            pb[m] = dtk * (half ? dBb[m] : dBa[m]);
-          }
-        }
-      }
+    // decay-weighted 32 x 32 matrices
+    for (int e = tid; e < kChunk * kChunk; e += kBwdThreads) {
+      const int k = e / kChunk, j = e % kChunk;
+      const float lk = sm.l[k], lj = sm.l[j];
+      const float xd = sm.XD[k * kPZ + j];
+      sm.W1[k * kPZ + j] = j <= k ? __expf(lk - lj) * sm.dt[j] * xd : 0.f;              // dC: sources j <= k
+      sm.W2[k * kPZ + j] = j >= k ? __expf(lj - lk) * sm.XD[j * kPZ + k] : 0.f;         // dB: readers j >= k
+      sm.W3[k * kPZ + j] = j >= k ? __expf(lj - lk) * sm.CB[j * kPZ + k] : 0.f;         // dx: readers j >= k
+      sm.Z[k * kPZ + j] = j < k ? __expf(lk - lj) * sm.dt[j] * xd * sm.CB[k * kPZ + j] : 0.f;
     }
-    // (token j, rows) phase: dx_j, x_j.(dS_j B_j), r'_j, dD
+    // per-token sums: q_k = e^(l_k) (S0^T dy_k).C_k, r'_j = e^(l_e-l_j) dt_j x_j.(G B_j), dD
     {
-      const int j = tid >> 4, p0 = (tid & 15) * 4;
-      const float lj = sm.l[j], dtj = sm.dt[j];
-      float br[4];
-      const float eg = __expf(le - lj);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) br[m] = eg * sm.GB[j * kPX + p0 + m];
-      for (int k = j; k < kChunk; ++k) {
-        const float w = __expf(sm.l[k] - lj) * sm.CB[k * kPZ + j];
-        const float4 dv = lds4(&sm.dy[k * kPX + p0]);
-        br[0] = fmaf(w, dv.x, br[0]);
-        br[1] = fmaf(w, dv.y, br[1]);
-        br[2] = fmaf(w, dv.z, br[2]);
-        br[3] = fmaf(w, dv.w, br[3]);
+      const int k = tid >> 4, sub = tid & 15;  // 16 lanes per token
+      float qv = 0.f, rv = 0.f, dd = 0.f;
+      for (int n = sub; n < N; n += 16) qv = fmaf(sm.S0[k * PB + n], sm.C[k * PB + n], qv);
+      for (int p = sub; p < kHeadDim; p += 16) {
+        rv = fmaf(sm.x[k * kPX + p], sm.GB[k * kPX + p], rv);
+        dd = fmaf(sm.x[k * kPX + p], sm.dy[k * kPX + p], dd);
       }
-      float sp_ = 0.f, rp = 0.f, dd = 0.f;
-      float dxv[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float xv = sm.x[j * kPX + p0 + m], dyv = sm.dy[j * kPX + p0 + m];
-        sp_ = fmaf(xv, br[m], sp_);
-        rp = fmaf(xv, sm.GB[j * kPX + p0 + m], rp);
-        dd = fmaf(dyv, xv, dd);
-        dxv[m] = fmaf(Dh, dyv, dtj * br[m]);
+      for (int o = 1; o < 16; o <<= 1) {
+        qv += __shfl_xor(qv, o);
+        rv += __shfl_xor(rv, o);
+        dd += __shfl_xor(dd, o);
       }
-      if (j < clen)
-        *reinterpret_cast<float4*>(a.dx + ((size_t)(c0 + j) * a.H + h) * kHeadDim + p0) =
-            make_float4(dxv[0], dxv[1], dxv[2], dxv[3]);
-      sp_ = reduce16(sp_);
-      rp = reduce16(rp);
-      dd = reduce16(dd);
-      if ((tid & 15) == 0) {
-        sm.s[j] = sp_;
-        sm.r[j] = eg * dtj * rp;
+      if (sub == 0) {
+        const float lk = sm.l[k];
+        sm.q[k] = __expf(lk) * qv;
+        sm.r[k] = __expf(le - lk) * sm.dt[k] * rv;
         dD_acc += dd;
       }
     }
-    __syncthreads();
-    // a_i <dS_i, S_{i-1}>: ddt_i and dA
+    lds_barrier();
+    // second products: dC, dB per 32 columns; the dx bracket per 32 rows
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      // jobs: 0..NT-1 dC, NT..2NT-1 dB, 2NT, 2NT+1 bracket
+      const int j = sl == 0 ? (wave < NT ? wave : (wave < NT + 2 ? 2 * NT + (wave - NT) : -1))
+                            : (wave < NT ? NT + wave : -1);
+      if (j < 0) continue;
+      f32x16 cc;
+      if (j < NT) {  // dC(k, n) = e^(l_k) S0^T dy + sum_j W1[k][j] B[j][n]
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cc[r] = __expf(sm.l[tile_row(r, ln)]) * sm.S0[tile_row(r, ln) * PB + 32 * j + tile_col(ln)];
+        mma_tile<kChunk>(cc, sm.W1, kPZ, 1, sm.B + 32 * j, PB, 1, ln);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int k = tile_row(r, ln);
+          if (k < clen) a.dC_part[((size_t)(c0 + k) * a.H + h) * N + 32 * j + tile_col(ln)] = cc[r];
+        }
+      } else if (j < 2 * NT) {  // dB(k, n) = dt_k [e^(l_e-l_k) G^T x + sum_m W2[k][m] C[m][n]]
+        const int nt = j - NT;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          cc[r] = __expf(le - sm.l[tile_row(r, ln)]) * sm.G[tile_row(r, ln) * PB + 32 * nt + tile_col(ln)];
+        mma_tile<kChunk>(cc, sm.W2, kPZ, 1, sm.C + 32 * nt, PB, 1, ln);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int k = tile_row(r, ln);
+          if (k < clen) a.dB_part[((size_t)(c0 + k) * a.H + h) * N + 32 * nt + tile_col(ln)] = sm.dt[k] * cc[r];
+        }
+      } else {  // bracket(j, p) = e^(l_e-l_j) (G B_j)[p] + sum_k W3[j][k] dy[k][p]; dx = D dy + dt_j bracket
+        const int pt = j - 2 * NT;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          cc[r] = __expf(le - sm.l[tile_row(r, ln)]) * sm.GB[tile_row(r, ln) * kPX + 32 * pt + tile_col(ln)];
+        mma_tile<kChunk>(cc, sm.W3, kPZ, 1, sm.dy + 32 * pt, kPX, 1, ln);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jj = tile_row(r, ln), p = 32 * pt + tile_col(ln);
+          sm.GB[jj * kPX + p] = cc[r];  // this wave's own entries: read above, overwritten here
+          if (jj < clen)
+            a.dx[((size_t)(c0 + jj) * a.H + h) * kHeadDim + p] = fmaf(Dh, sm.dy[jj * kPX + p], sm.dt[jj] * cc[r]);
+        }
+      }
+    }
+    lds_barrier();
+    // s_j = x_j . bracket_j; then a_i <dS_i, S_{i-1}> -> ddt_i, dA
     {
-      const int i = tid >> 4, sub = tid & 15;
+      const int k = tid >> 4, sub = tid & 15;
+      float sv = 0.f;
+      for (int p = sub; p < kHeadDim; p += 16) sv = fmaf(sm.x[k * kPX + p], sm.GB[k * kPX + p], sv);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) sv += __shfl_xor(sv, o);
       float R = 0.f;
-      for (int k = i + sub; k < kChunk; k += 16)
-        for (int j = 0; j < i; ++j) R += sm.Z[k * kPZ + j];
-      R = reduce16(R);
+      for (int kk = k + sub; kk < kChunk; kk += 16)
+        for (int j = 0; j < k; ++j) R += sm.Z[kk * kPZ + j];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) R += __shfl_xor(R, o);
       if (sub == 0) {
         float W = R + ele * gs;
-        for (int k = i; k < kChunk; ++k) W += sm.q[k];
-        for (int j = 0; j < i; ++j) W += sm.r[j];
-        if (i < clen) a.ddt[(size_t)(c0 + i) * a.H + h] = fmaf(Ah, W, sm.s[i]);
-        dA_acc = fmaf(sm.dt[i], W, dA_acc);
+        for (int kk = k; kk < kChunk; ++kk) W += sm.q[kk];
+        for (int j = 0; j < k; ++j) W += sm.r[j];
+        if (k < clen) a.ddt[(size_t)(c0 + k) * a.H + h] = fmaf(Ah, W, sv);
+        dA_acc = fmaf(sm.dt[k], W, dA_acc);
       }
     }
-    // gradient leaving the previous chunk's last token
-#pragma unroll
-    for (int k = 0; k < NE3; ++k) Gr[k] *= ele;
-    for (int k = 0; k < kChunk; ++k) {
-      const float w = __expf(sm.l[k]) * sm.dy[k * kPX + sp];
-#pragma unroll
-      for (int m = 0; m < NE3; m += 4) {
-        const float4 cv = lds4(&sm.C[k * PB + sc + m]);
-        Gr[m] = fmaf(w, cv.x, Gr[m]);
-        Gr[m + 1] = fmaf(w, cv.y, Gr[m + 1]);
-        Gr[m + 2] = fmaf(w, cv.z, Gr[m + 2]);
-        Gr[m + 3] = fmaf(w, cv.w, Gr[m + 3]);
-      }
+    // dy rows scaled by e^(l_k) for the update of G
+    for (int e = tid; e < kChunk * kHeadDim; e += kBwdThreads) {
+      const int k = e / kHeadDim, p = e % kHeadDim;
+      sm.dy[k * kPX + p] *= __expf(sm.l[k]);
     }
-    __syncthreads();
+    lds_barrier();
+    // gradient leaving the previous chunk: G <- e^(l_e) G + sum_k e^(l_k) dy_k outer C_k
+    if (gown) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Gt[r] *= ele;
+      mma_tile<kChunk>(Gt, sm.dy + 32 * gp, 1, kPX, sm.C + 32 * gn, PB, 1, ln);
+    }
+    lds_barrier();
   }
   dA_acc = block_sum(dA_acc, sm.red);
   dD_acc = block_sum(dD_acc, sm.red);
