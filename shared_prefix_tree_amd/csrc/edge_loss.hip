@@ -394,8 +394,8 @@ int tree_attn_edges(const int32_t* edge_src, const int32_t* edge_tgt, int32_t nu
                               " outside [0, " + std::to_string(num_tokens) + ") / [0, " + std::to_string(vocab) +
                               ")");
   }
-  if (int64_t(num_edges) * kVocabChunk >= (int64_t(1) << 31) || int64_t(num_tokens) * 65536 >= (int64_t(1) << 40))
-    return report_error(TREE_ATTN_UNSUPPORTED, "tree_attn_edges: too many edges");
+  if (int64_t(num_edges) * kVocabChunk >= (int64_t(1) << 31))
+    return report_error(TREE_ATTN_UNSUPPORTED, "tree_attn_edges: more than 262,143 edges");
   // CSR by source token, edges ascending within a token
   std::vector<int32_t> row_ptr(size_t(num_tokens) + 1, 0), ids(num_edges);
   for (int32_t e = 0; e < num_edges; ++e) ++row_ptr[size_t(edge_src[e]) + 1];

@@ -65,10 +65,11 @@ struct tree_attn_mamba_plan_s {
   std::vector<int32_t> csucc_ptr, csucc;        // token j -> entries 4 i + k with prev^k(i) = j, k = 1..kHalo
   std::vector<int32_t> unit_start, unit_len, unit_pred;  // [U]
   std::vector<int32_t> usucc_ptr, usucc;        // unit u -> units v with pred(v) = u, ascending
+  std::vector<int32_t> uchain;                  // 1: u's only successor is u + 1
   void* block = nullptr;
   const int32_t *d_halo = nullptr, *d_csucc_ptr = nullptr, *d_csucc = nullptr;
   const int32_t *d_unit_start = nullptr, *d_unit_len = nullptr, *d_unit_pred = nullptr;
-  const int32_t *d_usucc_ptr = nullptr, *d_usucc = nullptr;
+  const int32_t *d_usucc_ptr = nullptr, *d_usucc = nullptr, *d_uchain = nullptr;
 };
 
 namespace {
@@ -125,27 +126,32 @@ bool build_mamba_plan(const int32_t* parent, const int32_t* seg_start, const int
   std::vector<int32_t> uf(m.usucc_ptr.begin(), m.usucc_ptr.end() - 1);
   for (int32_t u = 0; u < m.U; ++u)
     if (m.unit_pred[u] >= 0) m.usucc[uf[m.unit_pred[u]]++] = u;
+  m.uchain.assign(m.U, 0);
+  for (int32_t u = 0; u < m.U; ++u)
+    m.uchain[u] = (m.usucc_ptr[u + 1] - m.usucc_ptr[u] == 1 && m.usucc[m.usucc_ptr[u]] == u + 1) ? 1 : 0;
   return true;
 }
 
 hipError_t upload_mamba_plan(tree_attn_mamba_plan_s& m) {
-  const std::vector<int32_t>* parts[] = {&m.halo,     &m.csucc_ptr, &m.csucc,     &m.unit_start,
-                                         &m.unit_len, &m.unit_pred, &m.usucc_ptr, &m.usucc};
-  size_t off[8], total = 0;
-  for (int k = 0; k < 8; ++k) {
+  const std::vector<int32_t>* parts[] = {&m.halo,     &m.csucc_ptr, &m.csucc,     &m.unit_start, &m.unit_len,
+                                         &m.unit_pred, &m.usucc_ptr, &m.usucc,     &m.uchain};
+  constexpr int kParts = 9;
+  size_t off[kParts], total = 0;
+  for (int k = 0; k < kParts; ++k) {
     off[k] = total;
     total += (parts[k]->size() * 4 + 255) & ~size_t(255);
   }
   std::vector<char> stage(std::max<size_t>(total, 256), 0);
-  for (int k = 0; k < 8; ++k)
+  for (int k = 0; k < kParts; ++k)
     if (!parts[k]->empty()) std::memcpy(stage.data() + off[k], parts[k]->data(), parts[k]->size() * 4);
   hipError_t e = hipGetDevice(&m.device);
   if (e == hipSuccess) e = hipMalloc(&m.block, stage.size());
   if (e == hipSuccess) e = hipMemcpy(m.block, stage.data(), stage.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) return e;
-  const int32_t** dst[] = {&m.d_halo,     &m.d_csucc_ptr, &m.d_csucc,     &m.d_unit_start,
-                           &m.d_unit_len, &m.d_unit_pred, &m.d_usucc_ptr, &m.d_usucc};
-  for (int k = 0; k < 8; ++k) *dst[k] = reinterpret_cast<const int32_t*>(static_cast<char*>(m.block) + off[k]);
+  const int32_t** dst[] = {&m.d_halo,     &m.d_csucc_ptr, &m.d_csucc,      &m.d_unit_start, &m.d_unit_len,
+                           &m.d_unit_pred, &m.d_usucc_ptr, &m.d_usucc, &m.d_uchain};
+  for (int k = 0; k < kParts; ++k)
+    *dst[k] = reinterpret_cast<const int32_t*>(static_cast<char*>(m.block) + off[k]);
   return hipSuccess;
 }
 
@@ -449,42 +455,92 @@ __global__ __launch_bounds__(256) void ssm_output_kernel(ScanArgs a) {
   }
 }
 
+constexpr int kWalkAhead = 8;   // units whose state rows are in flight ahead of the walk
+constexpr int kWalkTile = 256;  // walk steps whose unit tables are staged in LDS at a time
+
+__device__ inline void load8(const float* p, float (&v)[8], int o) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[o] = a.x, v[o + 1] = a.y, v[o + 2] = a.z, v[o + 3] = a.w;
+  v[o + 4] = b.x, v[o + 5] = b.y, v[o + 6] = b.z, v[o + 7] = b.w;
+}
+
+template <int NE>
+__device__ inline void load_row_part(const float* p, float (&v)[NE]) {
+  static_assert(NE % 4 == 0, "whole float4 pieces");
+#pragma unroll
+  for (int m = 0; m < NE / 4; ++m) {
+    const float4 t = reinterpret_cast<const float4*>(p)[m];
+    v[4 * m] = t.x, v[4 * m + 1] = t.y, v[4 * m + 2] = t.z, v[4 * m + 3] = t.w;
+  }
+}
+
+template <int NE>
+__device__ inline void store_row_part(float* p, const float (&v)[NE]) {
+#pragma unroll
+  for (int m = 0; m < NE / 4; ++m)
+    reinterpret_cast<float4*>(p)[m] = make_float4(v[4 * m], v[4 * m + 1], v[4 * m + 2], v[4 * m + 3]);
+}
+
 // one block per (head, quarter of the rows); thread holds row p, columns
-// [c NE2, (c+1) NE2); walks the units in DFS order
+// [c NE2, (c+1) NE2); walks the units in DFS order.  The walk's unit tables
+// (predecessor, decay) are staged in LDS a tile at a time, and each unit's
+// local row, which does not depend on the walk, is loaded kWalkAhead units
+// ahead into a register ring; the loop is unrolled over the ring so every
+// slot index is a constant.
 template <int N>
 __global__ __launch_bounds__(256) void ssm_propagate_kernel(ScanArgs a) {
-  constexpr int NE2 = N / 16;
+  constexpr int NE2 = N / 16, R = kWalkAhead;
+  __shared__ int sPred[kWalkTile];
+  __shared__ float sDec[kWalkTile];
   const int h = blockIdx.x >> 2, quarter = blockIdx.x & 3;
   const int p = quarter * 16 + (threadIdx.x >> 4), c = threadIdx.x & 15;
   const size_t col = size_t(p) * N + c * NE2;
   const size_t lstride = size_t(a.H) * kHeadDim * N;
   const size_t loff = size_t(h) * kHeadDim * N + col;
+  float rloc[R][NE2];
+  auto load = [&](int u, int slot) {
+    if (u < a.U) load_row_part<NE2>(a.local + u * lstride + loff, rloc[slot]);
+  };
+#pragma unroll
+  for (int j = 0; j < R; ++j) load(j, j);
   float end[NE2];
 #pragma unroll
   for (int k = 0; k < NE2; ++k) end[k] = 0.f;
-  for (int u = 0; u < a.U; ++u) {
-    const int pred = a.unit_pred[u];
-    float start[NE2];
-    if (pred < 0) {
-#pragma unroll
-      for (int k = 0; k < NE2; ++k) start[k] = 0.f;
-    } else if (pred == u - 1) {
-#pragma unroll
-      for (int k = 0; k < NE2; ++k) start[k] = end[k];
-    } else {  // a fork: the parent's end, from what this thread stored
-      const float dp = a.decay[(size_t)pred * a.H + h];
-      const float* sp = a.states + state_index(pred, 0, a.H, h, N) + col;
-      const float* lp = a.local + pred * lstride + loff;
-#pragma unroll
-      for (int k = 0; k < NE2; ++k) start[k] = fmaf(dp, sp[k], lp[k]);
+  for (int base = 0; base < a.U; base += R) {
+    if (base % kWalkTile == 0) {
+      __syncthreads();
+      for (int t = threadIdx.x; t < kWalkTile && base + t < a.U; t += blockDim.x) {
+        sPred[t] = a.unit_pred[base + t];
+        sDec[t] = a.decay[(size_t)(base + t) * a.H + h];
+      }
+      __syncthreads();
     }
-    float* out = a.states + state_index(u, 0, a.H, h, N) + col;
 #pragma unroll
-    for (int k = 0; k < NE2; ++k) out[k] = start[k];
-    const float du = a.decay[(size_t)u * a.H + h];
-    const float* lu = a.local + u * lstride + loff;
+    for (int j = 0; j < R; ++j) {
+      const int u = base + j;
+      if (u >= a.U) break;
+      const int pred = sPred[u % kWalkTile];
+      float start[NE2];
+      if (pred < 0) {
 #pragma unroll
-    for (int k = 0; k < NE2; ++k) end[k] = fmaf(du, start[k], lu[k]);
+        for (int k = 0; k < NE2; ++k) start[k] = 0.f;
+      } else if (pred == u - 1) {
+#pragma unroll
+        for (int k = 0; k < NE2; ++k) start[k] = end[k];
+      } else {  // a fork: the parent's end, from what this thread stored
+        const float dp = a.decay[(size_t)pred * a.H + h];
+        float sp[NE2], lp[NE2];
+        load_row_part<NE2>(a.states + state_index(pred, 0, a.H, h, N) + col, sp);
+        load_row_part<NE2>(a.local + pred * lstride + loff, lp);
+#pragma unroll
+        for (int k = 0; k < NE2; ++k) start[k] = fmaf(dp, sp[k], lp[k]);
+      }
+      store_row_part<NE2>(a.states + state_index(u, 0, a.H, h, N) + col, start);
+      const float du = sDec[u % kWalkTile];
+#pragma unroll
+      for (int k = 0; k < NE2; ++k) end[k] = fmaf(du, start[k], rloc[j][k]);
+      load(u + R, j);
+    }
   }
 }
 
@@ -530,7 +586,7 @@ hipError_t launch_ssm_fwd(const ScanArgs& a, hipStream_t s) {
 
 struct ScanBwdArgs {
   const float *x, *dt, *A, *B, *C, *D, *dy, *states;
-  const int32_t *unit_start, *unit_len, *unit_pred, *usucc_ptr, *usucc;
+  const int32_t *unit_start, *unit_len, *unit_pred, *usucc_ptr, *usucc, *uchain;
   int H, G, U, T;
   float* in;      // [U][H][P][N]: local_in, then in(u)
   float* gout;    // [U][H][P][N]: out(u)
@@ -608,39 +664,61 @@ __global__ __launch_bounds__(256) void ssm_bwd_local_kernel(ScanBwdArgs a) {
   if (tid == 0) a.decay[(size_t)u * a.H + h] = __expf(sL);
 }
 
+// reverse DFS walk, staged like the forward walk
 template <int N>
 __global__ __launch_bounds__(256) void ssm_bwd_propagate_kernel(ScanBwdArgs a) {
-  constexpr int NE2 = N / 16;
+  constexpr int NE2 = N / 16, R = kWalkAhead;
+  __shared__ int sChain[kWalkTile];
+  __shared__ float sDec[kWalkTile];
   const int h = blockIdx.x >> 2, quarter = blockIdx.x & 3;
   const int p = quarter * 16 + (threadIdx.x >> 4), c = threadIdx.x & 15;
   const size_t ustride = size_t(a.H) * kHeadDim * N;
   const size_t hoff = size_t(h) * kHeadDim * N + size_t(p) * N + c * NE2;
+  float rin[R][NE2];
+  // walk step t visits unit U - 1 - t
+  auto load = [&](int t, int slot) {
+    if (t < a.U) load_row_part<NE2>(a.in + size_t(a.U - 1 - t) * ustride + hoff, rin[slot]);
+  };
+#pragma unroll
+  for (int j = 0; j < R; ++j) load(j, j);
   float next_in[NE2];  // in(u + 1)
 #pragma unroll
   for (int k = 0; k < NE2; ++k) next_in[k] = 0.f;
-  for (int u = a.U - 1; u >= 0; --u) {
-    const int s0 = a.usucc_ptr[u], s1 = a.usucc_ptr[u + 1];
-    float G[NE2];
-#pragma unroll
-    for (int k = 0; k < NE2; ++k) G[k] = 0.f;
-    if (s1 - s0 == 1 && a.usucc[s0] == u + 1) {
-#pragma unroll
-      for (int k = 0; k < NE2; ++k) G[k] = next_in[k];
-    } else {  // a branch point (or a leaf): the successors' in(v), ascending
-      for (int e = s0; e < s1; ++e) {
-        const float* iv = a.in + size_t(a.usucc[e]) * ustride + hoff;
-#pragma unroll
-        for (int k = 0; k < NE2; ++k) G[k] += iv[k];
+  for (int base = 0; base < a.U; base += R) {
+    if (base % kWalkTile == 0) {
+      __syncthreads();
+      for (int t = threadIdx.x; t < kWalkTile && base + t < a.U; t += blockDim.x) {
+        const int u = a.U - 1 - (base + t);
+        sChain[t] = a.uchain[u];
+        sDec[t] = a.decay[(size_t)u * a.H + h];
       }
+      __syncthreads();
     }
-    float* go = a.gout + size_t(u) * ustride + hoff;
-    float* iu = a.in + size_t(u) * ustride + hoff;
-    const float du = a.decay[(size_t)u * a.H + h];
 #pragma unroll
-    for (int k = 0; k < NE2; ++k) {
-      go[k] = G[k];
-      next_in[k] = fmaf(du, G[k], iu[k]);
-      iu[k] = next_in[k];
+    for (int j = 0; j < R; ++j) {
+      const int t = base + j;
+      if (t >= a.U) break;
+      const int u = a.U - 1 - t;
+      float G[NE2];
+      if (sChain[t % kWalkTile]) {
+#pragma unroll
+        for (int k = 0; k < NE2; ++k) G[k] = next_in[k];
+      } else {  // a branch point (or a leaf): the successors' in(v), ascending
+#pragma unroll
+        for (int k = 0; k < NE2; ++k) G[k] = 0.f;
+        for (int e = a.usucc_ptr[u]; e < a.usucc_ptr[u + 1]; ++e) {
+          float iv[NE2];
+          load_row_part<NE2>(a.in + size_t(a.usucc[e]) * ustride + hoff, iv);
+#pragma unroll
+          for (int k = 0; k < NE2; ++k) G[k] += iv[k];
+        }
+      }
+      const float du = sDec[t % kWalkTile];
+#pragma unroll
+      for (int k = 0; k < NE2; ++k) next_in[k] = fmaf(du, G[k], rin[j][k]);
+      store_row_part<NE2>(a.gout + size_t(u) * ustride + hoff, G);
+      store_row_part<NE2>(a.in + size_t(u) * ustride + hoff, next_in);
+      load(t + R, j);
     }
   }
 }
@@ -1272,7 +1350,7 @@ int tree_attn_ssm_bwd(const float* x, const float* dt, const float* A, const flo
   ScanBwdArgs a{};
   a.x = x, a.dt = dt, a.A = A, a.B = B, a.C = C, a.D = D, a.dy = dy, a.states = states;
   a.unit_start = plan->d_unit_start, a.unit_len = plan->d_unit_len, a.unit_pred = plan->d_unit_pred;
-  a.usucc_ptr = plan->d_usucc_ptr, a.usucc = plan->d_usucc;
+  a.usucc_ptr = plan->d_usucc_ptr, a.usucc = plan->d_usucc, a.uchain = plan->d_uchain;
   a.H = shape->num_heads, a.G = shape->num_groups, a.U = plan->U, a.T = plan->T;
   char* w = static_cast<char*>(workspace);
   const size_t st = align256(state_floats(plan, shape) * 4);
