@@ -21,17 +21,18 @@
 // the parent segment's last unit, so the units form a tree in DFS order.
 // The state after a unit is linear in the state before it:
 //   end(u) = decay(u) start(u) + local(u),  decay(u) = exp(A sum_{i in u} dt_i)
-// 1. local:     per (unit, head), scan the unit from a zero state -> local(u),
-//               decay(u)   (all units in parallel);
+// 1. local:     per (unit, head), the unit from a zero state -> local(u),
+//               decay(u)   (all units in parallel; 32 tokens at a time as one
+//               rank-32 update of the state on the fp32 matrix cores);
 // 2. propagate: per (head, quarter of the state), walk the units in DFS
 //               order: start(u) = end(pred(u)); a fork reads its parent's
 //               start and local back (each thread reads what it wrote);
 // 3. output:    per (unit, head), scan again from start(u) and write y.
-// start(u) is kept for the backward pass.  The state of one head (64 x N
-// floats) is spread over a 256-thread block: thread (p, q) holds row p,
-// columns [q N/4, (q+1) N/4); y's sum over the state dimension is a
-// four-lane reduction.  Everything is fp32 with no atomics: results are
-// bitwise reproducible.
+// The state before every 32-token chunk is kept for the backward pass.  In
+// the output pass the state of one head (64 x N floats) is spread over a
+// 256-thread block, two rows and N/8 columns per thread; y's sum over the
+// state dimension is an eight-lane reduction.  Everything is fp32 with no
+// atomics: results are bitwise reproducible.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -297,67 +298,140 @@ __host__ __device__ inline size_t state_index(int u, int chunk, int H, int h, in
   return ((size_t(u) * kChunksPerUnit + chunk) * H + h) * size_t(kHeadDim) * N;
 }
 
-// local pass: one block per (unit, head); thread (row group, column quad)
-// holds rows [pg PR, (pg+1) PR) x columns [4 nq, 4 nq + 4); the chunk's B
-// rows, x rows and step sizes are staged in LDS
+// ---------------------------------------------------------------------------
+// fp32 matrix-core tiles
+//
+// In the chunk form of the recurrence every contraction over a chunk of 32
+// tokens is a product of 32 x 32 tiles, run on the fp32 matrix cores
+// (v_mfma_f32_32x32x2f32: lane l feeds A[l % 32][k0 + l / 32] and
+// B[k0 + l / 32][l % 32]; accumulator r of lane l is
+// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]).  Operands are read from LDS
+// with a per-lane address; the waves of a block share out the tiles by a
+// fixed table, and a 64 x N state (or its gradient) stays in accumulator
+// layout, one 32 x 32 tile per wave.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// c += A B over K (a multiple of 2): A(i, k) = a[i ai + k ak], B(k, j) = b[k bk + j bj]
+template <int K>
+__device__ inline void mma_tile(f32x16& c, const float* a, int ai, int ak, const float* b, int bk, int bj, int ln) {
+  const int i = ln & 31, hk = ln >> 5;
+#pragma unroll 4
+  for (int k0 = 0; k0 < K; k0 += 2) {
+    const float av = a[i * ai + (k0 + hk) * ak];
+    const float bv = b[(k0 + hk) * bk + i * bj];
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, c, 0, 0, 0);
+  }
+}
+
+// ln: the lane index, passed in so that a loop can make it opaque (address
+// arithmetic is then redone per iteration instead of held in registers)
+__device__ inline int tile_row(int r, int ln) { return 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3); }
+__device__ inline int tile_col(int ln) { return ln & 31; }
+
+__device__ inline float reduce32(float v) {  // sum over 32 consecutive lanes
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// barrier for LDS hand-offs only: global loads issued ahead stay in flight
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// fixed-order sum over the block (all threads get the result)
+__device__ inline float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  lds_barrier();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  lds_barrier();
+  float r = 0.f;
+  for (int w = 0; w < int(blockDim.x) / 64; ++w) r += red[w];
+  return r;
+}
+
+constexpr int kFwdThreads = 512;
+constexpr int kFX = kHeadDim + 4;  // x rows in LDS (16-byte aligned, banks staggered)
+
 template <int N>
-__global__ __launch_bounds__(256) void ssm_local_kernel(ScanArgs a) {
-  constexpr int NQ = N / 4, PG = 256 / NQ, PR = kHeadDim / PG;
-  __shared__ float4 sB[kChunk][NQ];
-  __shared__ __attribute__((aligned(16))) float sX[kChunk][kHeadDim];
-  __shared__ float sDT[kChunk], sDec[kChunk];
+struct FwdSmem {
+  static constexpr int PB = N + 4;
+  float x[kChunk * kFX], xw[kChunk * kFX];  // x rows; x_j scaled by w_j
+  float B[kChunk * PB];
+  float dt[kChunk], l[kChunk], w[kChunk];   // w_j = e^(l_e - l_j) dt_j
+};
+
+// Local pass in chunk form: one block of eight waves per (unit, head), from
+// a zero state; wave w owns 32 x 32 tile w of the 64 x N state.  Per chunk
+// of 32 tokens, with l_i = A times the sum of dt up to and including token i,
+//   S <- e^(l_e) S + sum_j (e^(l_e - l_j) dt_j x_j) outer B_j
+// (one rank-32 tile product on the fp32 matrix cores).  Writes local(u) and
+// decay(u) = e^(A sum dt).
+template <int N>
+__global__ __launch_bounds__(kFwdThreads) void ssm_local_kernel(ScanArgs a) {
+  constexpr int PB = FwdSmem<N>::PB, NT = N / 32, GT = 2 * NT;
+  __shared__ __attribute__((aligned(16))) FwdSmem<N> sm;
   const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int g = h / (a.H / a.G);
-  const int tid = threadIdx.x, nq = tid % NQ, pg = tid / NQ;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = a.unit_start[u], len = a.unit_len[u];
   const float Ah = a.A[h];
-  float S[PR][4];
-#pragma unroll
-  for (int r = 0; r < PR; ++r)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) S[r][k] = 0.f;
-  float dsum = 0.f;
-  for (int c0 = t0; c0 < t0 + len; c0 += kChunk) {
-    const int clen = min(kChunk, t0 + len - c0);
-    __syncthreads();
-    for (int e = tid; e < kChunk * NQ; e += 256) {
-      const int k = e / NQ, q = e % NQ;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (k < clen) v = reinterpret_cast<const float4*>(a.B + ((size_t)(c0 + k) * a.G + g) * N)[q];
-      sB[k][q] = v;
-    }
-    for (int e = tid; e < kChunk * (kHeadDim / 4); e += 256) {
+  const bool sown = wave < GT;
+  const int sp = wave / NT, sn = wave % NT;  // state tile: rows 32 sp .., columns 32 sn ..
+  f32x16 S = f32x16{};
+  float lsum = 0.f;
+  for (int ci = 0; ci * kChunk < len; ++ci) {
+    const int c0 = t0 + ci * kChunk, clen = min(kChunk, len - ci * kChunk);
+    int ln = tid & 63;
+    asm volatile("" : "+v"(ln));
+    // stage the chunk (padding: zeros)
+    for (int e = tid; e < kChunk * (kHeadDim / 4); e += kFwdThreads) {
       const int k = e / (kHeadDim / 4), q = e % (kHeadDim / 4);
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (k < clen) v = reinterpret_cast<const float4*>(a.x + ((size_t)(c0 + k) * a.H + h) * kHeadDim)[q];
-      reinterpret_cast<float4*>(sX[k])[q] = v;
+      *reinterpret_cast<float4*>(&sm.x[k * kFX + 4 * q]) = v;
     }
-    if (tid < kChunk) {
-      const float d = tid < clen ? a.dt[(size_t)(c0 + tid) * a.H + h] : 0.f;
-      sDT[tid] = d;
-      sDec[tid] = __expf(d * Ah);
+    for (int e = tid; e < kChunk * (N / 4); e += kFwdThreads) {
+      const int k = e / (N / 4), q = e % (N / 4);
+      float4 vb = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < clen) vb = reinterpret_cast<const float4*>(a.B + ((size_t)(c0 + k) * a.G + g) * N)[q];
+      *reinterpret_cast<float4*>(&sm.B[k * PB + 4 * q]) = vb;
     }
-    __syncthreads();
-    for (int k = 0; k < clen; ++k) {
-      const float4 b = sB[k][nq];
-      const float d = sDT[k], dec = sDec[k];
-      dsum += d;
-#pragma unroll
-      for (int r = 0; r < PR; ++r) {
-        const float ux = d * sX[k][pg * PR + r];
-        S[r][0] = fmaf(ux, b.x, dec * S[r][0]);
-        S[r][1] = fmaf(ux, b.y, dec * S[r][1]);
-        S[r][2] = fmaf(ux, b.z, dec * S[r][2]);
-        S[r][3] = fmaf(ux, b.w, dec * S[r][3]);
+    if (tid < kChunk) sm.dt[tid] = tid < clen ? a.dt[(size_t)(c0 + tid) * a.H + h] : 0.f;
+    lds_barrier();
+    if (tid == 0) {
+      float l = 0.f;
+      for (int k = 0; k < kChunk; ++k) {
+        l = fmaf(sm.dt[k], Ah, l);
+        sm.l[k] = l;
       }
+      for (int k = 0; k < kChunk; ++k) sm.w[k] = __expf(l - sm.l[k]) * sm.dt[k];
     }
-  }
-  const size_t base = (size_t(u) * a.H + h) * kHeadDim * N;
+    lds_barrier();
+    const float le = sm.l[kChunk - 1];
+    lsum += le;
+    for (int e = tid; e < kChunk * (kHeadDim / 4); e += kFwdThreads) {
+      const int j = e / (kHeadDim / 4), q = e % (kHeadDim / 4);
+      const float wj = sm.w[j];
+      float4 v = *reinterpret_cast<const float4*>(&sm.x[j * kFX + 4 * q]);
+      v.x *= wj, v.y *= wj, v.z *= wj, v.w *= wj;
+      *reinterpret_cast<float4*>(&sm.xw[j * kFX + 4 * q]) = v;
+    }
+    lds_barrier();
+    if (sown) {  // S <- e^(l_e) S + xw^T B
+      const float ele = __expf(le);
 #pragma unroll
-  for (int r = 0; r < PR; ++r)
-    reinterpret_cast<float4*>(a.local + base + size_t(pg * PR + r) * N)[nq] =
-        make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
-  if (tid == 0) a.decay[(size_t)u * a.H + h] = __expf(Ah * dsum);
+      for (int r = 0; r < 16; ++r) S[r] *= ele;
+      mma_tile<kChunk>(S, sm.xw + 32 * sp, 1, kFX, sm.B + 32 * sn, PB, 1, ln);
+    }
+    lds_barrier();
+  }
+  if (sown) {
+    const size_t base = (size_t(u) * a.H + h) * kHeadDim * N;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      a.local[base + size_t(32 * sp + tile_row(r, tid & 63)) * N + 32 * sn + tile_col(tid & 63)] = S[r];
+  }
+  if (tid == 0) a.decay[(size_t)u * a.H + h] = __expf(lsum);
 }
 
 // output pass: one block per (unit, head) from the unit's start state;
@@ -547,7 +621,7 @@ __global__ __launch_bounds__(256) void ssm_propagate_kernel(ScanArgs a) {
 template <int N>
 hipError_t launch_ssm_fwd(const ScanArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.U) * unsigned(a.H));
-  hipLaunchKernelGGL((ssm_local_kernel<N>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((ssm_local_kernel<N>), grid, dim3(kFwdThreads), 0, s, a);
   hipLaunchKernelGGL((ssm_propagate_kernel<N>), dim3(unsigned(a.H) * 4), dim3(256), 0, s, a);
   hipLaunchKernelGGL((ssm_output_kernel<N>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
@@ -725,15 +799,6 @@ __global__ __launch_bounds__(256) void ssm_bwd_propagate_kernel(ScanBwdArgs a) {
 
 constexpr int kBwdThreads = 512;
 
-// Chunk gradients on the fp32 matrix cores.  Every contraction of the chunk
-// form is a product of 32 x 32 tiles (v_mfma_f32_32x32x2f32: lane l feeds
-// A[l % 32][k0 + l / 32] and B[k0 + l / 32][l % 32]; accumulator r of lane l
-// is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]).  Operands are read from LDS
-// with a per-lane address; the eight waves share out the tiles by a fixed
-// table.  The gradient G leaving the chunk lives in accumulator layout, one
-// 32 x 32 tile of the 64 x N state per wave.
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 constexpr int kPX = kHeadDim + 4;  // x, dy, (G B_j) and bracket rows (16-byte aligned rows)
 constexpr int kPZ = kChunk + 1;    // 32 x 32 matrices
 
@@ -750,45 +815,6 @@ struct BwdSmem {
   float dt[kChunk], l[kChunk], q[kChunk], r[kChunk], s[kChunk];
   float red[kBwdThreads / 64];
 };
-
-// c += A B over K (a multiple of 2): A(i, k) = a[i ai + k ak], B(k, j) = b[k bk + j bj]
-template <int K>
-__device__ inline void mma_tile(f32x16& c, const float* a, int ai, int ak, const float* b, int bk, int bj, int ln) {
-  const int i = ln & 31, hk = ln >> 5;
-#pragma unroll 4
-  for (int k0 = 0; k0 < K; k0 += 2) {
-    const float av = a[i * ai + (k0 + hk) * ak];
-    const float bv = b[(k0 + hk) * bk + i * bj];
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, c, 0, 0, 0);
-  }
-}
-
-// ln: the lane index, passed in so that a loop can make it opaque (address
-// arithmetic is then redone per iteration instead of held in registers)
-__device__ inline int tile_row(int r, int ln) { return 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3); }
-__device__ inline int tile_col(int ln) { return ln & 31; }
-
-__device__ inline float reduce32(float v) {  // sum over 32 consecutive lanes
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// barrier for LDS hand-offs only: global loads issued ahead stay in flight
-__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// fixed-order sum over the block (all threads get the result)
-__device__ inline float block_sum(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  lds_barrier();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  lds_barrier();
-  float r = 0.f;
-#pragma unroll
-  for (int w = 0; w < kBwdThreads / 64; ++w) r += red[w];
-  return r;
-}
 
 // first products of a chunk, shared out over the waves:
 //   0: C B^T, 1: X D, 2..: G B (per 32 rows of G), then S0^T dy and G^T x (per 32 columns)
