@@ -61,6 +61,7 @@ CASES = [
     ("three_chunks_ragged", 42, 500, 256, 20000, 0.5, 0.06),
     ("hidden_200", 43, 300, 200, 9000, 0.8, 0.08),
     ("one_edge", 44, 40, 64, 8192, 0.0, 0.1),
+    ("odd_vocab_8201", 46, 300, 8, 8201, 0.5, 0.3),  # vocabulary not a multiple of 4: scalar row paths
 ]
 
 

@@ -186,3 +186,57 @@ def test_ssm_at_the_benchmark_shape_on_two_groups():
         errs.update({k: rel_l2(a, r) for k, a, r in zip(("dx", "ddt", "dA", "dB", "dC", "dD"), got, ref)})
         log(f"  group {g}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
         assert all(v <= TOL for v in errs.values()), (g, errs)
+
+
+def edge_forests():
+    from workloads import Topology
+
+    def dfs(nodes):
+        parent = np.array([p for p, _ in nodes])
+        ln = np.array([n for _, n in nodes])
+        st = np.concatenate([[0], np.cumsum(ln)[:-1]])
+        return Topology(parent, st, ln)
+
+    return {
+        "one_token": dfs([(-1, 1)]),
+        "one_unit": dfs([(-1, 128)]),
+        "unit_plus_one": dfs([(-1, 129)]),
+        "fork_at_unit_end": dfs([(-1, 128), (0, 1), (0, 33), (0, 128)]),
+        "chain_of_single_tokens": dfs([(-1, 1), (0, 1), (1, 1), (2, 1), (3, 1), (4, 1), (4, 2)]),
+        "two_roots": dfs([(-1, 40), (0, 3), (-1, 200), (2, 64)]),
+    }
+
+
+@pytest.mark.parametrize("name", list(edge_forests()))
+def test_mamba_edge_topologies(name):
+    """Degenerate forests: one token, exactly one unit and one past it, a
+    fork right at a unit end, chains of one-token segments, several roots."""
+    import shared_prefix_tree_amd as sp
+
+    topo = edge_forests()[name]
+    T = topo.total_tokens
+    H, G, N = 4, 2, 64
+    d = mamba_tensors(131, T, heads=H, groups=G, state_dim=N, channels=8, width=4)
+    rng = np.random.default_rng(132)
+    dy = rng.standard_normal((T, H, 64)).astype(np.float32)
+    dcy = rng.standard_normal((T, 8)).astype(np.float32)
+    dev = "cuda:0"
+    keys = ("x", "dt", "A", "B", "C", "D")
+    t = dev_tensors({k: d[k] for k in keys}, dev)
+    with torch.cuda.device(dev):
+        plan = sp.MambaPlan.from_topology(topo)
+    y, states = sp.ssm_fwd(*(t[k] for k in keys), plan)
+    got = sp.ssm_bwd(*(t[k] for k in keys), torch.from_numpy(dy).to(dev), plan, states)
+    c = dev_tensors({"x": d["conv_x"], "w": d["conv_w"], "b": d["conv_b"], "dy": dcy}, dev)
+    cy = sp.conv_fwd(c["x"], c["w"], c["b"], plan)
+    cg = sp.conv_bwd(c["x"], c["w"], c["dy"], plan)
+    torch.cuda.synchronize()
+    ref = {"y": oracle.ssm_forward(*(d[k] for k in keys), topo)}
+    ref.update(zip(("dx", "ddt", "dA", "dB", "dC", "dD"), oracle.ssm_backward(dy, *(d[k] for k in keys), topo)))
+    ref["cy"] = oracle.conv_forward(d["conv_x"], d["conv_w"], d["conv_b"], topo)
+    ref.update(zip(("cdx", "cdw", "cdb"), oracle.conv_backward(dcy, d["conv_x"], d["conv_w"], topo)))
+    gots = {"y": y, **dict(zip(("dx", "ddt", "dA", "dB", "dC", "dD"), got)), "cy": cy,
+            **dict(zip(("cdx", "cdw", "cdb"), cg))}
+    errs = {k: rel_l2(gots[k].cpu().numpy(), ref[k]) for k in ref}
+    log(f"mamba edge {name} T={T}: " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+    assert all(v <= TOL for v in errs.values()), errs
