@@ -314,12 +314,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // c += A B over K (a multiple of 2): A(i, k) = a[i ai + k ak], B(k, j) = b[k bk + j bj]
 template <int K>
 __device__ inline void mma_tile(f32x16& c, const float* a, int ai, int ak, const float* b, int bk, int bj, int ln) {
+  static_assert(K % 8 == 0, "K in steps of 8");
   const int i = ln & 31, hk = ln >> 5;
-#pragma unroll 4
-  for (int k0 = 0; k0 < K; k0 += 2) {
-    const float av = a[i * ai + (k0 + hk) * ak];
-    const float bv = b[(k0 + hk) * bk + i * bj];
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, c, 0, 0, 0);
+  for (int k0 = 0; k0 < K; k0 += 8) {  // four products per step, operands read ahead
+#pragma unroll
+    for (int kk = 0; kk < 8; kk += 2) {
+      const float av = a[i * ai + (k0 + kk + hk) * ak];
+      const float bv = b[(k0 + kk + hk) * bk + i * bj];
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, c, 0, 0, 0);
+    }
   }
 }
 
@@ -327,12 +330,6 @@ __device__ inline void mma_tile(f32x16& c, const float* a, int ai, int ak, const
 // arithmetic is then redone per iteration instead of held in registers)
 __device__ inline int tile_row(int r, int ln) { return 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3); }
 __device__ inline int tile_col(int ln) { return ln & 31; }
-
-__device__ inline float reduce32(float v) {  // sum over 32 consecutive lanes
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 // barrier for LDS hand-offs only: global loads issued ahead stay in flight
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -531,12 +528,6 @@ __global__ __launch_bounds__(256) void ssm_output_kernel(ScanArgs a) {
 
 constexpr int kWalkAhead = 8;   // units whose state rows are in flight ahead of the walk
 constexpr int kWalkTile = 256;  // walk steps whose unit tables are staged in LDS at a time
-
-__device__ inline void load8(const float* p, float (&v)[8], int o) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-  v[o] = a.x, v[o + 1] = a.y, v[o + 2] = a.z, v[o + 3] = a.w;
-  v[o + 4] = b.x, v[o + 5] = b.y, v[o + 6] = b.z, v[o + 7] = b.w;
-}
 
 template <int NE>
 __device__ inline void load_row_part(const float* p, float (&v)[NE]) {
