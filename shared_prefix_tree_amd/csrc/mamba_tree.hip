@@ -183,6 +183,38 @@ __device__ inline float4 fma4(float4 a, float4 b, float4 c) {
 
 constexpr int kConvTokens = 16;  // tokens per block: the taps loaded once serve all of them
 
+// The last few rows a thread touched, keyed by token (the keys are the same
+// in every lane, so hits and misses do not diverge).  Inside a segment a
+// token's predecessors, or its successors, are the neighbouring tokens the
+// thread has just loaded, so most rows are read from memory once.
+template <typename V, int R>
+struct RowCache {
+  int id[R];
+  V v[R];
+  __device__ inline RowCache() {
+#pragma unroll
+    for (int q = 0; q < R; ++q) id[q] = -1;
+  }
+  template <typename Load>
+  __device__ inline V get(int key, Load load) {
+    V r{};
+    bool hit = false;
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+      if (id[q] == key) r = v[q], hit = true;
+    if (!hit) {
+      r = load(key);
+      put(key, r);
+    }
+    return r;
+  }
+  __device__ inline void put(int key, V val) {
+#pragma unroll
+    for (int q = R - 1; q > 0; --q) id[q] = id[q - 1], v[q] = v[q - 1];
+    id[0] = key, v[0] = val;
+  }
+};
+
 // one block per (16 tokens, 256 channel quads): a thread loads its taps once
 // and walks the tokens; halo indices are block-uniform
 template <int W>
@@ -196,15 +228,19 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const float4* __restrict_
   load_taps<W>(w, 4 * c4, t);
   const float4 b = bias[c4];
   const int i0 = blockIdx.x * kConvTokens, i1 = min(T, i0 + kConvTokens);
+  RowCache<float4, kHalo> cache;
+  auto load = [&](int tok) { return x[(size_t)tok * C4 + c4]; };
   for (int i = i0; i < i1; ++i) {
-    float4 acc = fma4(t[W - 1], x[(size_t)i * C4 + c4], b);
+    const float4 xi = load(i);
+    float4 acc = fma4(t[W - 1], xi, b);
 #pragma unroll
     for (int k = 1; k < W; ++k) {  // k steps back along the path: tap W-1-k
       const int src = halo[(size_t)i * kHalo + k - 1];
       if (src < 0) break;
-      acc = fma4(t[W - 1 - k], x[(size_t)src * C4 + c4], acc);
+      acc = fma4(t[W - 1 - k], cache.get(src, load), acc);
     }
     y[(size_t)i * C4 + c4] = acc;
+    cache.put(i, xi);
   }
 }
 
@@ -220,9 +256,11 @@ __global__ __launch_bounds__(256) void conv_bwd_dx_kernel(const float4* __restri
   float4 t[W];
   load_taps<W>(w, 4 * c4, t);
   const int j0 = blockIdx.x * kConvTokens, j1 = min(T, j0 + kConvTokens);
+  RowCache<float4, kHalo + 1> cache;
+  auto load = [&](int tok) { return dy[(size_t)tok * C4 + c4]; };
   for (int j = j0; j < j1; ++j) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    acc = fma4(t[W - 1], dy[(size_t)j * C4 + c4], acc);
+    acc = fma4(t[W - 1], cache.get(j, load), acc);
     for (int e = csucc_ptr[j]; e < csucc_ptr[j + 1]; ++e) {
       const int ent = csucc[e], i = ent >> 2, k = ent & 3;
       if (k >= W) continue;
@@ -230,7 +268,7 @@ __global__ __launch_bounds__(256) void conv_bwd_dx_kernel(const float4* __restri
 #pragma unroll
       for (int q = 1; q < W; ++q)
         if (W - 1 - k == q) tk = t[q];
-      acc = fma4(tk, dy[(size_t)i * C4 + c4], acc);
+      acc = fma4(tk, cache.get(i, load), acc);
     }
     dx[(size_t)j * C4 + c4] = acc;
   }
@@ -238,29 +276,38 @@ __global__ __launch_bounds__(256) void conv_bwd_dx_kernel(const float4* __restri
 
 constexpr int kConvRows = 256;  // tokens per partial of the weight gradient
 
-// partial[b][c][0..W-1] = sum over tokens of block b of dy[i, c] x[prev^(W-1-j)(i), c],
-// partial[b][c][W] = sum of dy[i, c]; one thread per channel
-__global__ void conv_bwd_dw_partial_kernel(const float* __restrict__ x, const float* __restrict__ dy,
-                                           const int32_t* __restrict__ halo, int T, int C, int W,
+// partial[b][c][k] = sum over tokens i of block b of dy[i, c] x[prev^k(i), c]
+// for k < W, partial[b][c][kConvMaxWidth] = sum of dy[i, c]; one thread per
+// four channels
+__global__ void conv_bwd_dw_partial_kernel(const float4* __restrict__ x, const float4* __restrict__ dy,
+                                           const int32_t* __restrict__ halo, int T, int C4, int W,
                                            float* __restrict__ partial) {
-  const int c = blockIdx.y * blockDim.x + threadIdx.x;
-  if (c >= C) return;
+  const int c4 = blockIdx.y * blockDim.x + threadIdx.x;
+  if (c4 >= C4) return;
   const int i0 = blockIdx.x * kConvRows, i1 = min(T, i0 + kConvRows);
-  float acc[kConvMaxWidth + 1] = {};
+  float4 acc[kConvMaxWidth + 1];
+#pragma unroll
+  for (int k = 0; k <= kConvMaxWidth; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int i = i0; i < i1; ++i) {
-    const float g = dy[(long long)i * C + c];
-    acc[kConvMaxWidth] += g;
+    const float4 g = dy[(size_t)i * C4 + c4];
+    acc[kConvMaxWidth].x += g.x, acc[kConvMaxWidth].y += g.y, acc[kConvMaxWidth].z += g.z,
+        acc[kConvMaxWidth].w += g.w;
 #pragma unroll
     for (int k = 0; k < kConvMaxWidth; ++k) {
       if (k >= W) break;
-      const int src = k == 0 ? i : halo[(long long)i * kHalo + k - 1];
+      const int src = k == 0 ? i : halo[(size_t)i * kHalo + k - 1];
       if (src < 0) break;
-      acc[k] = fmaf(g, x[(long long)src * C + c], acc[k]);
+      acc[k] = fma4(g, x[(size_t)src * C4 + c4], acc[k]);
     }
   }
-  float* out = partial + ((long long)blockIdx.x * C + c) * (kConvMaxWidth + 1);
+  float* out = partial + ((size_t)blockIdx.x * C4 * 4 + 4 * c4) * (kConvMaxWidth + 1);
 #pragma unroll
-  for (int k = 0; k <= kConvMaxWidth; ++k) out[k] = acc[k];
+  for (int k = 0; k <= kConvMaxWidth; ++k) {
+    out[0 * (kConvMaxWidth + 1) + k] = acc[k].x;
+    out[1 * (kConvMaxWidth + 1) + k] = acc[k].y;
+    out[2 * (kConvMaxWidth + 1) + k] = acc[k].z;
+    out[3 * (kConvMaxWidth + 1) + k] = acc[k].w;
+  }
 }
 
 // dw[c][W-1-k] and dbias[c]: the partials summed in block order
@@ -1294,8 +1341,9 @@ int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int
     return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": channels must be a positive multiple of 4");
   if (width < 1 || width > kConvMaxWidth)
     return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": width must be 1..4");
-  if (!aligned16(dy) || !aligned16(dx) || !aligned16(weight))
-    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": dy, dx and weight must be 16-byte aligned");
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(weight))
+    return report_error(TREE_ATTN_INVALID_ARGUMENT,
+                        std::string(fn) + ": x, dy, dx and weight must be 16-byte aligned");
   const size_t need = tree_attn_conv_bwd_workspace_bytes(plan, channels, width);
   if (workspace_bytes < need)
     return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": workspace " +
@@ -1318,8 +1366,9 @@ int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int
   }
   const int nblk = (T + kConvRows - 1) / kConvRows;
   float* partial = static_cast<float*>(workspace);
-  hipLaunchKernelGGL(conv_bwd_dw_partial_kernel, dim3(unsigned(nblk), unsigned((channels + 63) / 64)), dim3(64), 0,
-                     s, x, dy, plan->d_halo, T, channels, width, partial);
+  hipLaunchKernelGGL(conv_bwd_dw_partial_kernel, dim3(unsigned(nblk), unsigned((C4 + 63) / 64)), dim3(64), 0, s,
+                     reinterpret_cast<const float4*>(x), reinterpret_cast<const float4*>(dy), plan->d_halo, T, C4,
+                     width, partial);
   hipLaunchKernelGGL(conv_bwd_dw_reduce_kernel, dim3(unsigned((channels + 255) / 256)), dim3(256), 0, s, partial,
                      nblk, channels, width, dweight, dbias);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_error(fn, e);
