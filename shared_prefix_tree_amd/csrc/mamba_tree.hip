@@ -404,14 +404,26 @@ struct FwdSmem {
   float dt[kChunk], l[kChunk], w[kChunk];   // w_j = e^(l_e - l_j) dt_j
 };
 
-// Local pass in chunk form: one block of eight waves per (unit, head), from
-// a zero state; wave w owns 32 x 32 tile w of the 64 x N state.  Per chunk
-// of 32 tokens, with l_i = A times the sum of dt up to and including token i,
-//   S <- e^(l_e) S + sum_j (e^(l_e - l_j) dt_j x_j) outer B_j
-// (one rank-32 tile product on the fp32 matrix cores).  Writes local(u) and
-// decay(u) = e^(A sum dt).
-template <int N>
-__global__ __launch_bounds__(kFwdThreads) void ssm_local_kernel(ScanArgs a) {
+// Unit-local passes in chunk form: one block of eight waves per (unit,
+// head); wave w owns 32 x 32 tile w of a 64 x N accumulator.  Per chunk of
+// 32 tokens, with l_i = A times the sum of dt over the chunk up to and
+// including token i, and l_b that sum over the unit's earlier chunks:
+//   forward (kGrad = false): S <- e^(l_e) S + sum_j (e^(l_e - l_j) dt_j x_j) outer B_j
+//       from a zero state: S = local(u);
+//   backward (kGrad = true): L <- L + sum_k (e^(l_b + l_k) dy_k) outer C_k
+//       = local_in(u), the gradient reaching the unit's start from inside.
+// Both are one rank-32 tile product per chunk on the fp32 matrix cores.
+// decay(u) = e^(A sum dt) either way.
+struct LocalArgs {
+  const float *v, *w, *dt, *A;  // v: x or dy [T][H][64]; w: B or C [T][G][N]
+  const int32_t *unit_start, *unit_len;
+  int H, G;
+  float* out;    // [U][H][64][N]
+  float* decay;  // [U][H]
+};
+
+template <int N, bool kGrad>
+__global__ __launch_bounds__(kFwdThreads) void ssm_unit_local_kernel(LocalArgs a) {
   constexpr int PB = FwdSmem<N>::PB, NT = N / 32, GT = 2 * NT;
   __shared__ __attribute__((aligned(16))) FwdSmem<N> sm;
   const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
@@ -420,7 +432,7 @@ __global__ __launch_bounds__(kFwdThreads) void ssm_local_kernel(ScanArgs a) {
   const int t0 = a.unit_start[u], len = a.unit_len[u];
   const float Ah = a.A[h];
   const bool sown = wave < GT;
-  const int sp = wave / NT, sn = wave % NT;  // state tile: rows 32 sp .., columns 32 sn ..
+  const int sp = wave / NT, sn = wave % NT;  // tile: rows 32 sp .., columns 32 sn ..
   f32x16 S = f32x16{};
   float lsum = 0.f;
   for (int ci = 0; ci * kChunk < len; ++ci) {
@@ -431,13 +443,13 @@ __global__ __launch_bounds__(kFwdThreads) void ssm_local_kernel(ScanArgs a) {
     for (int e = tid; e < kChunk * (kHeadDim / 4); e += kFwdThreads) {
       const int k = e / (kHeadDim / 4), q = e % (kHeadDim / 4);
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (k < clen) v = reinterpret_cast<const float4*>(a.x + ((size_t)(c0 + k) * a.H + h) * kHeadDim)[q];
+      if (k < clen) v = reinterpret_cast<const float4*>(a.v + ((size_t)(c0 + k) * a.H + h) * kHeadDim)[q];
       *reinterpret_cast<float4*>(&sm.x[k * kFX + 4 * q]) = v;
     }
     for (int e = tid; e < kChunk * (N / 4); e += kFwdThreads) {
       const int k = e / (N / 4), q = e % (N / 4);
       float4 vb = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (k < clen) vb = reinterpret_cast<const float4*>(a.B + ((size_t)(c0 + k) * a.G + g) * N)[q];
+      if (k < clen) vb = reinterpret_cast<const float4*>(a.w + ((size_t)(c0 + k) * a.G + g) * N)[q];
       *reinterpret_cast<float4*>(&sm.B[k * PB + 4 * q]) = vb;
     }
     if (tid < kChunk) sm.dt[tid] = tid < clen ? a.dt[(size_t)(c0 + tid) * a.H + h] : 0.f;
@@ -448,7 +460,8 @@ __global__ __launch_bounds__(kFwdThreads) void ssm_local_kernel(ScanArgs a) {
         l = fmaf(sm.dt[k], Ah, l);
         sm.l[k] = l;
       }
-      for (int k = 0; k < kChunk; ++k) sm.w[k] = __expf(l - sm.l[k]) * sm.dt[k];
+      for (int k = 0; k < kChunk; ++k)
+        sm.w[k] = kGrad ? __expf(lsum + sm.l[k]) : __expf(l - sm.l[k]) * sm.dt[k];
     }
     lds_barrier();
     const float le = sm.l[kChunk - 1];
@@ -461,10 +474,12 @@ __global__ __launch_bounds__(kFwdThreads) void ssm_local_kernel(ScanArgs a) {
       *reinterpret_cast<float4*>(&sm.xw[j * kFX + 4 * q]) = v;
     }
     lds_barrier();
-    if (sown) {  // S <- e^(l_e) S + xw^T B
-      const float ele = __expf(le);
+    if (sown) {
+      if (!kGrad) {
+        const float ele = __expf(le);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] *= ele;
+        for (int r = 0; r < 16; ++r) S[r] *= ele;
+      }
       mma_tile<kChunk>(S, sm.xw + 32 * sp, 1, kFX, sm.B + 32 * sn, PB, 1, ln);
     }
     lds_barrier();
@@ -473,7 +488,7 @@ __global__ __launch_bounds__(kFwdThreads) void ssm_local_kernel(ScanArgs a) {
     const size_t base = (size_t(u) * a.H + h) * kHeadDim * N;
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      a.local[base + size_t(32 * sp + tile_row(r, tid & 63)) * N + 32 * sn + tile_col(tid & 63)] = S[r];
+      a.out[base + size_t(32 * sp + tile_row(r, tid & 63)) * N + 32 * sn + tile_col(tid & 63)] = S[r];
   }
   if (tid == 0) a.decay[(size_t)u * a.H + h] = __expf(lsum);
 }
@@ -659,7 +674,8 @@ __global__ __launch_bounds__(256) void ssm_propagate_kernel(ScanArgs a) {
 template <int N>
 hipError_t launch_ssm_fwd(const ScanArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.U) * unsigned(a.H));
-  hipLaunchKernelGGL((ssm_local_kernel<N>), grid, dim3(kFwdThreads), 0, s, a);
+  const LocalArgs la{a.x, a.B, a.dt, a.A, a.unit_start, a.unit_len, a.H, a.G, a.local, a.decay};
+  hipLaunchKernelGGL((ssm_unit_local_kernel<N, false>), grid, dim3(kFwdThreads), 0, s, la);
   hipLaunchKernelGGL((ssm_propagate_kernel<N>), dim3(unsigned(a.H) * 4), dim3(256), 0, s, a);
   hipLaunchKernelGGL((ssm_output_kernel<N>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
@@ -709,72 +725,6 @@ struct ScanBwdArgs {
   float* dD_part; // [U][H]
   float *dx, *ddt, *dA, *dB, *dC, *dD;
 };
-
-// local_in(u) = sum_k exp(l_k) dy_k outer C_k; same thread layout and
-// staging as the forward local pass
-template <int N>
-__global__ __launch_bounds__(256) void ssm_bwd_local_kernel(ScanBwdArgs a) {
-  constexpr int NQ = N / 4, PG = 256 / NQ, PR = kHeadDim / PG;
-  __shared__ float4 sC[kChunk][NQ];
-  __shared__ __attribute__((aligned(16))) float sY[kChunk][kHeadDim];
-  __shared__ float sE[kChunk];
-  __shared__ float sL;  // l at the end of the previous chunk
-  const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const int g = h / (a.H / a.G);
-  const int tid = threadIdx.x, nq = tid % NQ, pg = tid / NQ;
-  const int t0 = a.unit_start[u], len = a.unit_len[u];
-  const float Ah = a.A[h];
-  float L[PR][4];
-#pragma unroll
-  for (int r = 0; r < PR; ++r)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) L[r][k] = 0.f;
-  if (tid == 0) sL = 0.f;
-  for (int c0 = t0; c0 < t0 + len; c0 += kChunk) {
-    const int clen = min(kChunk, t0 + len - c0);
-    __syncthreads();
-    for (int e = tid; e < kChunk * NQ; e += 256) {
-      const int k = e / NQ, q = e % NQ;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (k < clen) v = reinterpret_cast<const float4*>(a.C + ((size_t)(c0 + k) * a.G + g) * N)[q];
-      sC[k][q] = v;
-    }
-    for (int e = tid; e < kChunk * (kHeadDim / 4); e += 256) {
-      const int k = e / (kHeadDim / 4), q = e % (kHeadDim / 4);
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (k < clen) v = reinterpret_cast<const float4*>(a.dy + ((size_t)(c0 + k) * a.H + h) * kHeadDim)[q];
-      reinterpret_cast<float4*>(sY[k])[q] = v;
-    }
-    if (tid == 0) {
-      float l = sL;
-      for (int k = 0; k < clen; ++k) {
-        l = fmaf(a.dt[(size_t)(c0 + k) * a.H + h], Ah, l);
-        sE[k] = __expf(l);
-      }
-      sL = l;
-    }
-    __syncthreads();
-    for (int k = 0; k < clen; ++k) {
-      const float4 c = sC[k][nq];
-      const float ek = sE[k];
-#pragma unroll
-      for (int r = 0; r < PR; ++r) {
-        const float w = ek * sY[k][pg * PR + r];
-        L[r][0] = fmaf(w, c.x, L[r][0]);
-        L[r][1] = fmaf(w, c.y, L[r][1]);
-        L[r][2] = fmaf(w, c.z, L[r][2]);
-        L[r][3] = fmaf(w, c.w, L[r][3]);
-      }
-    }
-  }
-  const size_t base = (size_t(u) * a.H + h) * kHeadDim * N;
-#pragma unroll
-  for (int r = 0; r < PR; ++r)
-    reinterpret_cast<float4*>(a.in + base + size_t(pg * PR + r) * N)[nq] =
-        make_float4(L[r][0], L[r][1], L[r][2], L[r][3]);
-  __syncthreads();
-  if (tid == 0) a.decay[(size_t)u * a.H + h] = __expf(sL);
-}
 
 // reverse DFS walk, staged like the forward walk
 template <int N>
@@ -1165,7 +1115,8 @@ __global__ void ssm_bwd_unit_sum_kernel(ScanBwdArgs a) {
 template <int N>
 hipError_t launch_ssm_bwd(const ScanBwdArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.U) * unsigned(a.H));
-  hipLaunchKernelGGL((ssm_bwd_local_kernel<N>), grid, dim3(256), 0, s, a);
+  const LocalArgs la{a.dy, a.C, a.dt, a.A, a.unit_start, a.unit_len, a.H, a.G, a.in, a.decay};
+  hipLaunchKernelGGL((ssm_unit_local_kernel<N, true>), grid, dim3(kFwdThreads), 0, s, la);
   hipLaunchKernelGGL((ssm_bwd_propagate_kernel<N>), dim3(unsigned(a.H) * 4), dim3(256), 0, s, a);
   hipLaunchKernelGGL((ssm_bwd_grad_kernel<N>), grid, dim3(kBwdThreads), 0, s, a);
   const long long n = (long long)a.T * a.G * N;
