@@ -58,7 +58,7 @@ extern "C" {
 #define TREE_ATTN_OK 0
 #define TREE_ATTN_INVALID_ARGUMENT (-1) /* null pointer, malformed topology, size mismatch, small workspace */
 #define TREE_ATTN_UNSUPPORTED (-2)      /* dtype / head_dim / head grouping not implemented */
-#define TREE_ATTN_HIP_ERROR (-3)        /* a HIP runtime call or launch failed */
+#define TREE_ATTN_HIP_ERROR (-3)        /* a HIP runtime call or launch failed, or host memory ran out */
 
 /* element types */
 #define TREE_ATTN_BF16 0

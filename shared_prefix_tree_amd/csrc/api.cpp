@@ -7,6 +7,9 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <memory>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -43,6 +46,20 @@ int hip_fail(const char* what, hipError_t e) {
 
 // the message store of tree_attn_last_error, for the other translation units
 int report_error(int code, const std::string& msg) { return fail(code, msg); }
+
+// Runs a host-side body so that no C++ exception crosses the C ABI: a failed
+// host allocation (or any other exception) becomes TREE_ATTN_HIP_ERROR.
+int guard_host(const char* fn, const std::function<int()>& body) noexcept {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return fail(TREE_ATTN_HIP_ERROR, std::string(fn) + ": out of host memory");
+  } catch (const std::exception& e) {
+    return fail(TREE_ATTN_HIP_ERROR, std::string(fn) + ": " + e.what());
+  } catch (...) {
+    return fail(TREE_ATTN_HIP_ERROR, std::string(fn) + ": unexpected host error");
+  }
+}
 
 struct DevicePlan {
   int device = -1;
@@ -121,24 +138,23 @@ int make_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* se
               int32_t q_begin, int32_t q_end, tree_attn_plan_t* out, bool device) {
   if (!out) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan: out is NULL");
   *out = nullptr;
-  auto* p = new tree_attn_plan_s();
-  std::string err;
-  if (!build_host_plan(parent, seg_start, seg_len, num_segments, q_begin, q_end, p->host, err)) {
-    delete p;
-    return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan: " + err);
-  }
-  if (device) {
-    hipError_t e = hipGetDevice(&p->dev.device);
-    if (e == hipSuccess) e = upload_plan(p->host, p->dev);
-    if (e != hipSuccess) {
-      free_device(p->dev);
-      delete p;
-      return hip_fail("tree_attn_plan: device upload", e);
+  return guard_host("tree_attn_plan", [&]() -> int {
+    auto p = std::make_unique<tree_attn_plan_s>();
+    std::string err;
+    if (!build_host_plan(parent, seg_start, seg_len, num_segments, q_begin, q_end, p->host, err))
+      return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan: " + err);
+    if (device) {
+      hipError_t e = hipGetDevice(&p->dev.device);
+      if (e == hipSuccess) e = upload_plan(p->host, p->dev);
+      if (e != hipSuccess) {
+        free_device(p->dev);
+        return hip_fail("tree_attn_plan: device upload", e);
+      }
+      p->on_device = true;
     }
-    p->on_device = true;
-  }
-  *out = p;
-  return TREE_ATTN_OK;
+    *out = p.release();
+    return TREE_ATTN_OK;
+  });
 }
 
 int gcd(int a, int b) {
@@ -234,14 +250,14 @@ int tree_attn_fragment(const int32_t* parent, const int32_t* seg_start, const in
                        int32_t max_tokens, tree_attn_fragments_t* out) {
   if (!out) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fragment: out is NULL");
   *out = nullptr;
-  auto* r = new tree_attn_fragments_s();
-  std::string err;
-  if (!build_fragments(parent, seg_start, seg_len, num_segments, max_tokens, r->f, err)) {
-    delete r;
-    return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fragment: " + err);
-  }
-  *out = r;
-  return TREE_ATTN_OK;
+  return guard_host("tree_attn_fragment", [&]() -> int {
+    auto r = std::make_unique<tree_attn_fragments_s>();
+    std::string err;
+    if (!build_fragments(parent, seg_start, seg_len, num_segments, max_tokens, r->f, err))
+      return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fragment: " + err);
+    *out = r.release();
+    return TREE_ATTN_OK;
+  });
 }
 
 int tree_attn_fragments_destroy(tree_attn_fragments_t fr) {

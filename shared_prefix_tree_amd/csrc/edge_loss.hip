@@ -31,6 +31,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <functional>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -39,6 +41,7 @@
 
 namespace tree_attn {
 int report_error(int code, const std::string& msg);
+int guard_host(const char* fn, const std::function<int()>& body) noexcept;
 }
 
 using tree_attn::report_error;
@@ -396,43 +399,42 @@ int tree_attn_edges(const int32_t* edge_src, const int32_t* edge_tgt, int32_t nu
   }
   if (int64_t(num_edges) * kVocabChunk >= (int64_t(1) << 31))
     return report_error(TREE_ATTN_UNSUPPORTED, "tree_attn_edges: more than 262,143 edges");
-  // CSR by source token, edges ascending within a token
-  std::vector<int32_t> row_ptr(size_t(num_tokens) + 1, 0), ids(num_edges);
-  for (int32_t e = 0; e < num_edges; ++e) ++row_ptr[size_t(edge_src[e]) + 1];
-  for (int32_t t = 0; t < num_tokens; ++t) row_ptr[t + 1] += row_ptr[t];
-  std::vector<int32_t> fill(row_ptr.begin(), row_ptr.end() - 1);
-  for (int32_t e = 0; e < num_edges; ++e) ids[fill[edge_src[e]]++] = e;
+  return tree_attn::guard_host("tree_attn_edges", [&]() -> int {
+    // CSR by source token, edges ascending within a token
+    std::vector<int32_t> row_ptr(size_t(num_tokens) + 1, 0), ids(num_edges);
+    for (int32_t e = 0; e < num_edges; ++e) ++row_ptr[size_t(edge_src[e]) + 1];
+    for (int32_t t = 0; t < num_tokens; ++t) row_ptr[t + 1] += row_ptr[t];
+    std::vector<int32_t> fill(row_ptr.begin(), row_ptr.end() - 1);
+    for (int32_t e = 0; e < num_edges; ++e) ids[fill[edge_src[e]]++] = e;
 
-  auto* r = new tree_attn_edges_s();
-  r->E = num_edges;
-  r->T = num_tokens;
-  r->V = vocab;
-  const size_t n_src = align256(size_t(num_edges) * 4), n_ptr = align256((size_t(num_tokens) + 1) * 4);
-  const size_t total = 3 * n_src + n_ptr;
-  hipError_t e = hipGetDevice(&r->device);
-  if (e == hipSuccess) e = hipMalloc(&r->block, total);
-  if (e != hipSuccess) {
-    delete r;
-    return report_error(TREE_ATTN_HIP_ERROR, std::string("tree_attn_edges: ") + hipGetErrorString(e));
-  }
-  char* b = static_cast<char*>(r->block);
-  r->src = reinterpret_cast<int32_t*>(b);
-  r->tgt = reinterpret_cast<int32_t*>(b + n_src);
-  r->ids = reinterpret_cast<int32_t*>(b + 2 * n_src);
-  r->row_ptr = reinterpret_cast<int32_t*>(b + 3 * n_src);
-  std::vector<char> stage(total, 0);
-  std::memcpy(stage.data(), edge_src, size_t(num_edges) * 4);
-  std::memcpy(stage.data() + n_src, edge_tgt, size_t(num_edges) * 4);
-  std::memcpy(stage.data() + 2 * n_src, ids.data(), size_t(num_edges) * 4);
-  std::memcpy(stage.data() + 3 * n_src, row_ptr.data(), row_ptr.size() * 4);
-  e = hipMemcpy(r->block, stage.data(), total, hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    (void)hipFree(r->block);
-    delete r;
-    return report_error(TREE_ATTN_HIP_ERROR, std::string("tree_attn_edges: upload: ") + hipGetErrorString(e));
-  }
-  *out = r;
-  return TREE_ATTN_OK;
+    auto r = std::make_unique<tree_attn_edges_s>();
+    r->E = num_edges;
+    r->T = num_tokens;
+    r->V = vocab;
+    const size_t n_src = align256(size_t(num_edges) * 4), n_ptr = align256((size_t(num_tokens) + 1) * 4);
+    const size_t total = 3 * n_src + n_ptr;
+    std::vector<char> stage(total, 0);  // (host allocations before the device one: nothing leaks on a throw)
+    std::memcpy(stage.data(), edge_src, size_t(num_edges) * 4);
+    std::memcpy(stage.data() + n_src, edge_tgt, size_t(num_edges) * 4);
+    std::memcpy(stage.data() + 2 * n_src, ids.data(), size_t(num_edges) * 4);
+    std::memcpy(stage.data() + 3 * n_src, row_ptr.data(), row_ptr.size() * 4);
+    hipError_t e = hipGetDevice(&r->device);
+    if (e == hipSuccess) e = hipMalloc(&r->block, total);
+    if (e != hipSuccess)
+      return report_error(TREE_ATTN_HIP_ERROR, std::string("tree_attn_edges: ") + hipGetErrorString(e));
+    char* b = static_cast<char*>(r->block);
+    r->src = reinterpret_cast<int32_t*>(b);
+    r->tgt = reinterpret_cast<int32_t*>(b + n_src);
+    r->ids = reinterpret_cast<int32_t*>(b + 2 * n_src);
+    r->row_ptr = reinterpret_cast<int32_t*>(b + 3 * n_src);
+    e = hipMemcpy(r->block, stage.data(), total, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(r->block);
+      return report_error(TREE_ATTN_HIP_ERROR, std::string("tree_attn_edges: upload: ") + hipGetErrorString(e));
+    }
+    *out = r.release();
+    return TREE_ATTN_OK;
+  });
 }
 
 int tree_attn_edges_destroy(tree_attn_edges_t edges) {

@@ -37,6 +37,8 @@
 
 #include <algorithm>
 #include <cstring>
+#include <functional>
+#include <memory>
 #include <string>
 #include <vector>
 
@@ -45,6 +47,7 @@
 
 namespace tree_attn {
 int report_error(int code, const std::string& msg);
+int guard_host(const char* fn, const std::function<int()>& body) noexcept;
 }
 
 using tree_attn::report_error;
@@ -1173,21 +1176,20 @@ static int mamba_plan_impl(const int32_t* parent, const int32_t* seg_start, cons
   *out = nullptr;
   if (!parent || !seg_start || !seg_len)
     return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL topology array");
-  auto* m = new tree_attn_mamba_plan_s();
-  std::string err;
-  if (!build_mamba_plan(parent, seg_start, seg_len, num_segments, *m, err)) {
-    delete m;
-    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": " + err);
-  }
-  if (upload) {
-    if (hipError_t e = upload_mamba_plan(*m); e != hipSuccess) {
-      if (m->block) (void)hipFree(m->block);
-      delete m;
-      return hip_error(fn, e);
+  return tree_attn::guard_host(fn, [&]() -> int {
+    auto m = std::make_unique<tree_attn_mamba_plan_s>();
+    std::string err;
+    if (!build_mamba_plan(parent, seg_start, seg_len, num_segments, *m, err))
+      return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": " + err);
+    if (upload) {
+      if (hipError_t e = upload_mamba_plan(*m); e != hipSuccess) {
+        if (m->block) (void)hipFree(m->block);
+        return hip_error(fn, e);
+      }
     }
-  }
-  *out = m;
-  return TREE_ATTN_OK;
+    *out = m.release();
+    return TREE_ATTN_OK;
+  });
 }
 
 int tree_attn_mamba_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
