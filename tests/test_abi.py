@@ -210,3 +210,32 @@ def test_backward_stages_reject_null_inputs_before_launch():
 def test_edge_plan_rejects_bad_edges_without_a_device(src, tgt, T, V, frag):
     with pytest.raises(b.TreeAttnError, match=frag):
         sp.EdgePlan(np.array(src, np.int32), np.array(tgt, np.int32), T, V)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """There is no CPU fallback: without the built library every entry point
+    raises instead of computing something else."""
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(b, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        b.library()
+    with pytest.raises(RuntimeError, match="no fallback"):
+        sp.Plan([-1], [0], [4], device=False)
+
+
+def test_product_package_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "shared_prefix_tree_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), f
+                assert "oracle/" not in src, f
+
+
+def test_mamba_calls_reject_a_host_only_plan_without_a_device():
+    plan = sp.MambaPlan([-1, 0], [0, 4], [4, 4], device=False)
+    lib = sp.library()
+    rc = lib.tree_attn_conv_fwd(None, None, None, 4, 4, plan.handle, None, None)
+    assert rc == b.INVALID_ARGUMENT
+    assert "host-only" in lib.tree_attn_last_error().decode()
