@@ -361,18 +361,41 @@ __host__ __device__ inline size_t state_index(int u, int chunk, int H, int h, in
 // layout, one 32 x 32 tile per wave.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// c += A B over K (a multiple of 2): A(i, k) = a[i ai + k ak], B(k, j) = b[k bk + j bj]
-template <int K>
-__device__ inline void mma_tile(f32x16& c, const float* a, int ai, int ak, const float* b, int bk, int bj, int ln) {
+// c += A B over K: A(i, k) = a[i AI + k AK], B(k, j) = b[k BK + j BJ].
+// The contraction may run over k in any order, so the two halves of the
+// wave take the two halves of k: consecutive products of a lane then read
+// consecutive k, an operand that is contiguous in k (stride 1, 16-byte
+// aligned rows) is read four products at a time with one 16-byte LDS read,
+// and the next four products' operands are read while the current four run.
+template <int S>
+__device__ inline float4 read4(const float* p) {
+  if constexpr (S == 1) {
+    return *reinterpret_cast<const float4*>(p);
+  } else {
+    return make_float4(p[0], p[S], p[2 * S], p[3 * S]);
+  }
+}
+template <int K, int AI, int AK, int BK, int BJ>
+__device__ inline void mma_tile(f32x16& c, const float* a, const float* b, int ln) {
   static_assert(K % 8 == 0, "K in steps of 8");
+  constexpr int KH = K / 2, NG = KH / 4;
   const int i = ln & 31, hk = ln >> 5;
-  for (int k0 = 0; k0 < K; k0 += 8) {  // four products per step, operands read ahead
+  const float* pa = a + i * AI + hk * KH * AK;
+  const float* pb = b + i * BJ + hk * KH * BK;
+  float4 va = read4<AK>(pa), vb = read4<BK>(pb);
 #pragma unroll
-    for (int kk = 0; kk < 8; kk += 2) {
-      const float av = a[i * ai + (k0 + kk + hk) * ak];
-      const float bv = b[(k0 + kk + hk) * bk + i * bj];
-      c = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, c, 0, 0, 0);
+  for (int g = 0; g < NG; ++g) {
+    float4 na = va, nb = vb;
+    if (g + 1 < NG) {
+      na = read4<AK>(pa + 4 * (g + 1) * AK);
+      nb = read4<BK>(pb + 4 * (g + 1) * BK);
     }
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(va.x, vb.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(va.y, vb.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(va.z, vb.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(va.w, vb.w, c, 0, 0, 0);
+    va = na;
+    vb = nb;
   }
 }
 
@@ -483,7 +506,7 @@ __global__ __launch_bounds__(kFwdThreads) void ssm_unit_local_kernel(LocalArgs a
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[r] *= ele;
       }
-      mma_tile<kChunk>(S, sm.xw + 32 * sp, 1, kFX, sm.B + 32 * sn, PB, 1, ln);
+      mma_tile<kChunk, 1, kFX, PB, 1>(S, sm.xw + 32 * sp, sm.B + 32 * sn, ln);
     }
     lds_barrier();
   }
@@ -791,7 +814,8 @@ __global__ __launch_bounds__(256) void ssm_bwd_propagate_kernel(ScanBwdArgs a) {
 constexpr int kBwdThreads = 512;
 
 constexpr int kPX = kHeadDim + 4;  // x, dy, (G B_j) and bracket rows (16-byte aligned rows)
-constexpr int kPZ = kChunk + 1;    // 32 x 32 matrices
+constexpr int kPZ = kChunk + 1;    // 32 x 32 matrices read along rows and columns
+constexpr int kPW = kChunk + 4;    // 32 x 32 matrices read as matrix-core operands (16-byte rows)
 
 template <int N>
 struct BwdSmem {
@@ -801,7 +825,7 @@ struct BwdSmem {
   float S0[kHeadDim * PB], G[kHeadDim * PB];  // reused as S0^T dy and G^T x ([k][n]) after the first products
   float CB[kChunk * kPZ], XD[kChunk * kPZ];   // [k][j]: C_k.B_j, x_j.dy_k
   float Z[kChunk * kPZ];                      // [k][j], j < k: e^(l_k-l_j) dt_j XD CB
-  float W1[kChunk * kPZ], W2[kChunk * kPZ], W3[kChunk * kPZ];
+  float W1[kChunk * kPW], W2[kChunk * kPW], W3[kChunk * kPW];
   float GB[kChunk * kPX];                     // [j][p]: (G B_j)[p], then the dx bracket
   float dt[kChunk], l[kChunk], q[kChunk], r[kChunk], s[kChunk];
   float red[kBwdThreads / 64];
@@ -932,18 +956,18 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
       acc[sl] = f32x16{};
       const int j = jobs[sl];
       if (j == 0) {
-        mma_tile<N>(acc[sl], sm.C, PB, 1, sm.B, 1, PB, ln);  // CB(k, j) = C_k . B_j
+        mma_tile<N, PB, 1, 1, PB>(acc[sl], sm.C, sm.B, ln);  // CB(k, j) = C_k . B_j
       } else if (j == 1) {
-        mma_tile<kHeadDim>(acc[sl], sm.dy, kPX, 1, sm.x, 1, kPX, ln);  // XD(k, j) = dy_k . x_j
+        mma_tile<kHeadDim, kPX, 1, 1, kPX>(acc[sl], sm.dy, sm.x, ln);  // XD(k, j) = dy_k . x_j
       } else if (j >= 2 && j < 4) {
         const int pt = j - 2;  // GB(j, p) = B_j . G_p, rows p in 32 pt ..
-        mma_tile<N>(acc[sl], sm.B, PB, 1, sm.G + 32 * pt * PB, 1, PB, ln);
+        mma_tile<N, PB, 1, 1, PB>(acc[sl], sm.B, sm.G + 32 * pt * PB, ln);
       } else if (j >= 4 && j < 4 + NT) {
         const int nt = j - 4;  // S0^T dy: (k, n) = sum_p dy[k][p] S0[p][n]
-        mma_tile<kHeadDim>(acc[sl], sm.dy, kPX, 1, sm.S0 + 32 * nt, PB, 1, ln);
+        mma_tile<kHeadDim, kPX, 1, PB, 1>(acc[sl], sm.dy, sm.S0 + 32 * nt, ln);
       } else if (j >= 4 + NT) {
         const int nt = j - 4 - NT;  // G^T x: (k, n) = sum_p x[k][p] G[p][n]
-        mma_tile<kHeadDim>(acc[sl], sm.x, kPX, 1, sm.G + 32 * nt, PB, 1, ln);
+        mma_tile<kHeadDim, kPX, 1, PB, 1>(acc[sl], sm.x, sm.G + 32 * nt, ln);
       }
     }
     lds_barrier();  // S0 and G are overwritten below
@@ -969,9 +993,9 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
       const int k = e / kChunk, j = e % kChunk;
       const float lk = sm.l[k], lj = sm.l[j];
       const float xd = sm.XD[k * kPZ + j];
-      sm.W1[k * kPZ + j] = j <= k ? __expf(lk - lj) * sm.dt[j] * xd : 0.f;              // dC: sources j <= k
-      sm.W2[k * kPZ + j] = j >= k ? __expf(lj - lk) * sm.XD[j * kPZ + k] : 0.f;         // dB: readers j >= k
-      sm.W3[k * kPZ + j] = j >= k ? __expf(lj - lk) * sm.CB[j * kPZ + k] : 0.f;         // dx: readers j >= k
+      sm.W1[k * kPW + j] = j <= k ? __expf(lk - lj) * sm.dt[j] * xd : 0.f;              // dC: sources j <= k
+      sm.W2[k * kPW + j] = j >= k ? __expf(lj - lk) * sm.XD[j * kPZ + k] : 0.f;         // dB: readers j >= k
+      sm.W3[k * kPW + j] = j >= k ? __expf(lj - lk) * sm.CB[j * kPZ + k] : 0.f;         // dx: readers j >= k
       sm.Z[k * kPZ + j] = j < k ? __expf(lk - lj) * sm.dt[j] * xd * sm.CB[k * kPZ + j] : 0.f;
     }
     // per-token sums: q_k = e^(l_k) (S0^T dy_k).C_k, r'_j = e^(l_e-l_j) dt_j x_j.(G B_j), dD
@@ -1008,7 +1032,7 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
       if (j < NT) {  // dC(k, n) = e^(l_k) S0^T dy + sum_j W1[k][j] B[j][n]
 #pragma unroll
         for (int r = 0; r < 16; ++r) cc[r] = __expf(sm.l[tile_row(r, ln)]) * sm.S0[tile_row(r, ln) * PB + 32 * j + tile_col(ln)];
-        mma_tile<kChunk>(cc, sm.W1, kPZ, 1, sm.B + 32 * j, PB, 1, ln);
+        mma_tile<kChunk, kPW, 1, PB, 1>(cc, sm.W1, sm.B + 32 * j, ln);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int k = tile_row(r, ln);
@@ -1019,7 +1043,7 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           cc[r] = __expf(le - sm.l[tile_row(r, ln)]) * sm.G[tile_row(r, ln) * PB + 32 * nt + tile_col(ln)];
-        mma_tile<kChunk>(cc, sm.W2, kPZ, 1, sm.C + 32 * nt, PB, 1, ln);
+        mma_tile<kChunk, kPW, 1, PB, 1>(cc, sm.W2, sm.C + 32 * nt, ln);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int k = tile_row(r, ln);
@@ -1030,7 +1054,7 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           cc[r] = __expf(le - sm.l[tile_row(r, ln)]) * sm.GB[tile_row(r, ln) * kPX + 32 * pt + tile_col(ln)];
-        mma_tile<kChunk>(cc, sm.W3, kPZ, 1, sm.dy + 32 * pt, kPX, 1, ln);
+        mma_tile<kChunk, kPW, 1, kPX, 1>(cc, sm.W3, sm.dy + 32 * pt, ln);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int jj = tile_row(r, ln), p = 32 * pt + tile_col(ln);
@@ -1071,7 +1095,7 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
     if (gown) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) Gt[r] *= ele;
-      mma_tile<kChunk>(Gt, sm.dy + 32 * gp, 1, kPX, sm.C + 32 * gn, PB, 1, ln);
+      mma_tile<kChunk, 1, kPX, PB, 1>(Gt, sm.dy + 32 * gp, sm.C + 32 * gn, ln);
     }
     lds_barrier();
   }
