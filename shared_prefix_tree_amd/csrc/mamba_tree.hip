@@ -404,6 +404,17 @@ __device__ inline void mma_tile(f32x16& c, const float* a, const float* b, int l
 __device__ inline int tile_row(int r, int ln) { return 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3); }
 __device__ inline int tile_col(int ln) { return ln & 31; }
 
+// l_k = sum_{j <= k} v_j over the 32 tokens of a chunk, v_j = dt_j A held by
+// lane k of a 32-lane group (inclusive scan by lane shuffles)
+__device__ inline float chunk_log_decay(float v, int k) {
+#pragma unroll
+  for (int o = 1; o < kChunk; o <<= 1) {
+    const float t = __shfl_up(v, o, kChunk);
+    if (k >= o) v += t;
+  }
+  return v;
+}
+
 // barrier for LDS hand-offs only: global loads issued ahead stay in flight
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
@@ -480,14 +491,14 @@ __global__ __launch_bounds__(kFwdThreads) void ssm_unit_local_kernel(LocalArgs a
     }
     if (tid < kChunk) sm.dt[tid] = tid < clen ? a.dt[(size_t)(c0 + tid) * a.H + h] : 0.f;
     lds_barrier();
-    if (tid == 0) {
-      float l = 0.f;
-      for (int k = 0; k < kChunk; ++k) {
-        l = fmaf(sm.dt[k], Ah, l);
+    if (tid < 64) {  // l_k = sum_{j <= k} dt_j A: a scan over the 32 lanes of a half-wave
+      const int k = tid & (kChunk - 1);
+      const float l = chunk_log_decay(sm.dt[k] * Ah, k);
+      const float le = __shfl(l, kChunk - 1, kChunk);
+      if (tid < kChunk) {
         sm.l[k] = l;
+        sm.w[k] = kGrad ? __expf(lsum + l) : __expf(le - l) * sm.dt[k];
       }
-      for (int k = 0; k < kChunk; ++k)
-        sm.w[k] = kGrad ? __expf(lsum + sm.l[k]) : __expf(l - sm.l[k]) * sm.dt[k];
     }
     lds_barrier();
     const float le = sm.l[kChunk - 1];
@@ -824,7 +835,7 @@ struct BwdSmem {
   float B[kChunk * PB], C[kChunk * PB];
   float S0[kHeadDim * PB], G[kHeadDim * PB];  // reused as S0^T dy and G^T x ([k][n]) after the first products
   float CB[kChunk * kPZ], XD[kChunk * kPZ];   // [k][j]: C_k.B_j, x_j.dy_k
-  float Z[kChunk * kPZ];                      // [k][j], j < k: e^(l_k-l_j) dt_j XD CB
+  float Z[kChunk * kPZ];                      // [k][i]: sum over j < min(i, k) of e^(l_k-l_j) dt_j XD CB
   float W1[kChunk * kPW], W2[kChunk * kPW], W3[kChunk * kPW];
   float GB[kChunk * kPX];                     // [j][p]: (G B_j)[p], then the dx bracket
   float dt[kChunk], l[kChunk], q[kChunk], r[kChunk], s[kChunk];
@@ -938,12 +949,10 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
     }
     if (c > 0) fetch(c - 1);  // in flight during this chunk
     lds_barrier();
-    if (tid == 0) {
-      float l = 0.f;
-      for (int k = 0; k < kChunk; ++k) {
-        l = fmaf(sm.dt[k], Ah, l);
-        sm.l[k] = l;
-      }
+    if (tid < 64) {  // the scan runs on a whole wave (lanes 32.. repeat it)
+      const int k = tid & (kChunk - 1);
+      const float l = chunk_log_decay(sm.dt[k] * Ah, k);
+      if (tid < kChunk) sm.l[k] = l;
     }
     gs = block_sum(gs, sm.red);  // (its barriers also publish l)
 
@@ -996,7 +1005,16 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
       sm.W1[k * kPW + j] = j <= k ? __expf(lk - lj) * sm.dt[j] * xd : 0.f;              // dC: sources j <= k
       sm.W2[k * kPW + j] = j >= k ? __expf(lj - lk) * sm.XD[j * kPZ + k] : 0.f;         // dB: readers j >= k
       sm.W3[k * kPW + j] = j >= k ? __expf(lj - lk) * sm.CB[j * kPZ + k] : 0.f;         // dx: readers j >= k
-      sm.Z[k * kPZ + j] = j < k ? __expf(lk - lj) * sm.dt[j] * xd * sm.CB[k * kPZ + j] : 0.f;
+      // Z(k, i) = sum_{j < i} e^(l_k-l_j) dt_j XD CB over j < k: an exclusive scan along the row,
+      // whose 32 entries are the 32 lanes of a half-wave (every lane takes part: 1024 = 2 x 512)
+      float z = j < k ? __expf(lk - lj) * sm.dt[j] * xd * sm.CB[k * kPZ + j] : 0.f;
+#pragma unroll
+      for (int o = 1; o < kChunk; o <<= 1) {
+        const float t = __shfl_up(z, o, kChunk);
+        if (j >= o) z += t;
+      }
+      const float zx = __shfl_up(z, 1, kChunk);
+      sm.Z[k * kPZ + j] = j > 0 ? zx : 0.f;
     }
     // per-token sums: q_k = e^(l_k) (S0^T dy_k).C_k, r'_j = e^(l_e-l_j) dt_j x_j.(G B_j), dD
     {
@@ -1072,15 +1090,14 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
       for (int p = sub; p < kHeadDim; p += 16) sv = fmaf(sm.x[k * kPX + p], sm.GB[k * kPX + p], sv);
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) sv += __shfl_xor(sv, o);
-      float R = 0.f;
-      for (int kk = k + sub; kk < kChunk; kk += 16)
-        for (int j = 0; j < k; ++j) R += sm.Z[kk * kPZ + j];
+      // W_k - e^(l_e) <G, S0> = sum_{kk >= k} (Z(kk, k) + q_kk) + sum_{j < k} r'_j
+      float wv = 0.f;
+      for (int kk = k + sub; kk < kChunk; kk += 16) wv += sm.Z[kk * kPZ + k] + sm.q[kk];
+      for (int j = sub; j < k; j += 16) wv += sm.r[j];
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) R += __shfl_xor(R, o);
+      for (int o = 1; o < 16; o <<= 1) wv += __shfl_xor(wv, o);
       if (sub == 0) {
-        float W = R + ele * gs;
-        for (int kk = k; kk < kChunk; ++kk) W += sm.q[kk];
-        for (int j = 0; j < k; ++j) W += sm.r[j];
+        const float W = wv + ele * gs;
         if (k < clen) a.ddt[(size_t)(c0 + k) * a.H + h] = fmaf(Ah, W, sv);
         dA_acc = fmaf(sm.dt[k], W, dA_acc);
       }
