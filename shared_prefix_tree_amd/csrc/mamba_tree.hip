@@ -404,15 +404,47 @@ __device__ inline void mma_tile(f32x16& c, const float* a, const float* b, int l
 __device__ inline int tile_row(int r, int ln) { return 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3); }
 __device__ inline int tile_col(int ln) { return ln & 31; }
 
-// l_k = sum_{j <= k} v_j over the 32 tokens of a chunk, v_j = dt_j A held by
-// lane k of a 32-lane group (inclusive scan by lane shuffles)
-__device__ inline float chunk_log_decay(float v, int k) {
-#pragma unroll
-  for (int o = 1; o < kChunk; o <<= 1) {
-    const float t = __shfl_up(v, o, kChunk);
-    if (k >= o) v += t;
-  }
+// Cross-lane sums and scans with DPP lane moves, which stay in the vector
+// unit (a shuffle goes through LDS and waits for it).  All lanes of the wave
+// must be active.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ inline float dpp(float v) {  // lanes whose source is invalid or masked get 0
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, false));
+}
+// sum over an aligned group of 8 lanes: pairs (quad_perm [1,0,3,2]), quads
+// (quad_perm [2,3,0,1]), the other quad of the half-row (row_half_mirror);
+// every lane of the group gets the same value
+__device__ inline float sum8_dpp(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
   return v;
+}
+// sum over an aligned group of 16 lanes (a DPP row): then the other half-row (row_mirror)
+__device__ inline float sum16_dpp(float v) {
+  v = sum8_dpp(v);
+  v += dpp<0x140>(v);
+  return v;
+}
+// inclusive scan over each aligned group of 32 lanes: within each 16-lane
+// row by shifts of 1, 2, 4, 8 (row_shr), then the last lane of rows 0 and 2
+// into every lane of rows 1 and 3 (row_bcast15 with row mask 0b1010)
+__device__ inline float scan32_dpp(float v) {
+  v += dpp<0x111>(v);
+  v += dpp<0x112>(v);
+  v += dpp<0x114>(v);
+  v += dpp<0x118>(v);
+  v += dpp<0x142, 0xA>(v);
+  return v;
+}
+// the value of the lane below (wave_shr 1; lane 0 gets 0)
+__device__ inline float lane_below_dpp(float v) { return dpp<0x138>(v); }
+
+// l_k = sum_{j <= k} v_j over the 32 tokens of a chunk, v_j = dt_j A held by
+// lane k of an aligned 32-lane group (an inclusive scan); all 64 lanes active
+__device__ inline float chunk_log_decay(float v) {
+  static_assert(kChunk == 32, "one chunk is one 32-lane scan");
+  return scan32_dpp(v);
 }
 
 // barrier for LDS hand-offs only: global loads issued ahead stay in flight
@@ -493,7 +525,7 @@ __global__ __launch_bounds__(kFwdThreads) void ssm_unit_local_kernel(LocalArgs a
     lds_barrier();
     if (tid < 64) {  // l_k = sum_{j <= k} dt_j A: a scan over the 32 lanes of a half-wave
       const int k = tid & (kChunk - 1);
-      const float l = chunk_log_decay(sm.dt[k] * Ah, k);
+      const float l = chunk_log_decay(sm.dt[k] * Ah);
       const float le = __shfl(l, kChunk - 1, kChunk);
       if (tid < kChunk) {
         sm.l[k] = l;
@@ -530,6 +562,8 @@ __global__ __launch_bounds__(kFwdThreads) void ssm_unit_local_kernel(LocalArgs a
   if (tid == 0) a.decay[(size_t)u * a.H + h] = __expf(lsum);
 }
 
+constexpr float kRefStep = 32.f;  // log-space step of the output pass's state reference
+
 // output pass: one block per (unit, head) from the unit's start state;
 // thread (row pair pr, column group ng) holds rows 2 pr, 2 pr + 1 x columns
 // [ng NC, (ng+1) NC); y's sum over columns is an eight-lane reduction.  The
@@ -540,7 +574,7 @@ __global__ __launch_bounds__(256) void ssm_output_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) float sB[kChunk][N];
   __shared__ __attribute__((aligned(16))) float sC[kChunk][N];
   __shared__ __attribute__((aligned(16))) float sX[kChunk][kHeadDim];
-  __shared__ float sDT[kChunk], sDec[kChunk];
+  __shared__ float sDF[kChunk], sG[kChunk], sRho[kChunk];
   const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int g = h / (a.H / a.G);
   const int tid = threadIdx.x, ng = tid & (NG - 1), pr = tid / NG;
@@ -586,24 +620,44 @@ __global__ __launch_bounds__(256) void ssm_output_kernel(ScanArgs a) {
       if (k < clen) v = reinterpret_cast<const float4*>(a.x + ((size_t)(c0 + k) * a.H + h) * kHeadDim)[q];
       reinterpret_cast<float4*>(sX[k])[q] = v;
     }
-    if (tid < kChunk) {
-      const float d = tid < clen ? a.dt[(size_t)(c0 + tid) * a.H + h] : 0.f;
-      sDT[tid] = d;
-      sDec[tid] = __expf(d * Ah);
+    // The state is kept as S~ = e^(R - l_k) S against a reference R that is
+    // a multiple of kRefStep in log space (R_k = kRefStep ceil(l_k / kRefStep),
+    // so 1 <= e^(R - l_k) < e^kRefStep): a token's update is then one fma per
+    // element, S~ += e^(R - l_k) dt_k x_k B_k, and y_k = e^(l_k - R) S~ C_k.
+    // When R moves, S~ is rescaled by e^(R_new - R_old).  Per token: sDF =
+    // dt e^(R - l), sG = e^(l - R), sRho = the rescale (1: none).
+    if (tid < 64) {
+      const int k = tid & (kChunk - 1);
+      const float d = k < clen ? a.dt[(size_t)(c0 + k) * a.H + h] : 0.f;
+      const float l = chunk_log_decay(d * Ah);
+      const float ref = kRefStep * ceilf(l * (1.f / kRefStep));
+      float prev = __shfl_up(ref, 1, kChunk);
+      if (k == 0) prev = 0.f;
+      if (tid < kChunk) {
+        sDF[k] = d * expf(ref - l);
+        sG[k] = expf(l - ref);
+        sRho[k] = ref == prev ? 1.f : expf(ref - prev);
+      }
     }
     __syncthreads();
     for (int k = 0; k < clen; ++k) {
-      const float d = sDT[k], dec = sDec[k];
+      const float df = sDF[k], gk = sG[k], rho = sRho[k];
+      if (rho != 1.f) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int m = 0; m < NC; ++m) S[r][m] *= rho;
+      }
       const float x0 = sX[k][2 * pr], x1 = sX[k][2 * pr + 1];
-      const float u0 = d * x0, u1 = d * x1;
+      const float u0 = df * x0, u1 = df * x1;
       float y0 = 0.f, y1 = 0.f;
 #pragma unroll
       for (int m = 0; m < NC / 4; ++m) {
         const float4 b = reinterpret_cast<const float4*>(&sB[k][ng * NC])[m];
         const float4 c = reinterpret_cast<const float4*>(&sC[k][ng * NC])[m];
 #define TREE_SSM_STEP(J, BJ, CJ)                                   \
-  S[0][4 * m + J] = fmaf(u0, BJ, dec * S[0][4 * m + J]);           \
-  S[1][4 * m + J] = fmaf(u1, BJ, dec * S[1][4 * m + J]);           \
+  S[0][4 * m + J] = fmaf(u0, BJ, S[0][4 * m + J]);                 \
+  S[1][4 * m + J] = fmaf(u1, BJ, S[1][4 * m + J]);                 \
   y0 = fmaf(S[0][4 * m + J], CJ, y0);                              \
   y1 = fmaf(S[1][4 * m + J], CJ, y1);
         TREE_SSM_STEP(0, b.x, c.x)
@@ -612,15 +666,18 @@ __global__ __launch_bounds__(256) void ssm_output_kernel(ScanArgs a) {
         TREE_SSM_STEP(3, b.w, c.w)
 #undef TREE_SSM_STEP
       }
-      y0 += __shfl_xor(y0, 1);
-      y1 += __shfl_xor(y1, 1);
-      y0 += __shfl_xor(y0, 2);
-      y1 += __shfl_xor(y1, 2);
-      y0 += __shfl_xor(y0, 4);
-      y1 += __shfl_xor(y1, 4);
+      y0 = sum8_dpp(y0);
+      y1 = sum8_dpp(y1);
       if (ng == 0)
         *reinterpret_cast<float2*>(a.y + ((size_t)(c0 + k) * a.H + h) * kHeadDim + 2 * pr) =
-            make_float2(fmaf(Dh, x0, y0), fmaf(Dh, x1, y1));
+            make_float2(fmaf(Dh, x0, gk * y0), fmaf(Dh, x1, gk * y1));
+    }
+    {  // back to the state itself at the chunk's end
+      const float ge = sG[clen - 1];
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int m = 0; m < NC; ++m) S[r][m] *= ge;
     }
   }
 }
@@ -951,7 +1008,7 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
     lds_barrier();
     if (tid < 64) {  // the scan runs on a whole wave (lanes 32.. repeat it)
       const int k = tid & (kChunk - 1);
-      const float l = chunk_log_decay(sm.dt[k] * Ah, k);
+      const float l = chunk_log_decay(sm.dt[k] * Ah);
       if (tid < kChunk) sm.l[k] = l;
     }
     gs = block_sum(gs, sm.red);  // (its barriers also publish l)
@@ -1007,14 +1064,10 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
       sm.W3[k * kPW + j] = j >= k ? __expf(lj - lk) * sm.CB[j * kPZ + k] : 0.f;         // dx: readers j >= k
       // Z(k, i) = sum_{j < i} e^(l_k-l_j) dt_j XD CB over j < k: an exclusive scan along the row,
       // whose 32 entries are the 32 lanes of a half-wave (every lane takes part: 1024 = 2 x 512)
-      float z = j < k ? __expf(lk - lj) * sm.dt[j] * xd * sm.CB[k * kPZ + j] : 0.f;
-#pragma unroll
-      for (int o = 1; o < kChunk; o <<= 1) {
-        const float t = __shfl_up(z, o, kChunk);
-        if (j >= o) z += t;
-      }
-      const float zx = __shfl_up(z, 1, kChunk);
-      sm.Z[k * kPZ + j] = j > 0 ? zx : 0.f;
+      const float z = j < k ? __expf(lk - lj) * sm.dt[j] * xd * sm.CB[k * kPZ + j] : 0.f;
+      const float zx = scan32_dpp(z);  // inclusive; the exclusive value is the lane below's
+      const float zb = lane_below_dpp(zx);
+      sm.Z[k * kPZ + j] = j > 0 ? zb : 0.f;
     }
     // per-token sums: q_k = e^(l_k) (S0^T dy_k).C_k, r'_j = e^(l_e-l_j) dt_j x_j.(G B_j), dD
     {
@@ -1025,12 +1078,9 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
         rv = fmaf(sm.x[k * kPX + p], sm.GB[k * kPX + p], rv);
         dd = fmaf(sm.x[k * kPX + p], sm.dy[k * kPX + p], dd);
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        qv += __shfl_xor(qv, o);
-        rv += __shfl_xor(rv, o);
-        dd += __shfl_xor(dd, o);
-      }
+      qv = sum16_dpp(qv);
+      rv = sum16_dpp(rv);
+      dd = sum16_dpp(dd);
       if (sub == 0) {
         const float lk = sm.l[k];
         sm.q[k] = __expf(lk) * qv;
@@ -1088,14 +1138,12 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
       const int k = tid >> 4, sub = tid & 15;
       float sv = 0.f;
       for (int p = sub; p < kHeadDim; p += 16) sv = fmaf(sm.x[k * kPX + p], sm.GB[k * kPX + p], sv);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) sv += __shfl_xor(sv, o);
+      sv = sum16_dpp(sv);
       // W_k - e^(l_e) <G, S0> = sum_{kk >= k} (Z(kk, k) + q_kk) + sum_{j < k} r'_j
       float wv = 0.f;
       for (int kk = k + sub; kk < kChunk; kk += 16) wv += sm.Z[kk * kPZ + k] + sm.q[kk];
       for (int j = sub; j < k; j += 16) wv += sm.r[j];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) wv += __shfl_xor(wv, o);
+      wv = sum16_dpp(wv);
       if (sub == 0) {
         const float W = wv + ele * gs;
         if (k < clen) a.ddt[(size_t)(c0 + k) * a.H + h] = fmaf(Ah, W, sv);
