@@ -66,7 +66,7 @@ struct tree_attn_mamba_plan_s {
   int32_t T = 0, S = 0, U = 0, max_depth = 0;
   std::vector<int32_t> prev;                    // [T]
   std::vector<int32_t> halo;                    // [T][kHalo]: prev^1 .. prev^kHalo (-1: none)
-  std::vector<int32_t> csucc_ptr, csucc;        // token j -> entries 4 i + k with prev^k(i) = j, k = 1..kHalo
+  std::vector<int32_t> csucc_ptr, csucc;        // token j -> entries 4 i + k with prev^k(i) = j, i != j + k, k = 1..kHalo
   std::vector<int32_t> unit_start, unit_len, unit_pred;  // [U]
   std::vector<int32_t> usucc_ptr, usucc;        // unit u -> units v with pred(v) = u, ascending
   std::vector<int32_t> uchain;                  // 1: u's only successor is u + 1
@@ -97,7 +97,7 @@ bool build_mamba_plan(const int32_t* parent, const int32_t* seg_start, const int
     for (int k = 1; k <= kHalo; ++k) {
       j = j < 0 ? -1 : m.prev[j];
       m.halo[size_t(i) * kHalo + k - 1] = j;
-      if (j >= 0) ++count[size_t(j) + 1];
+      if (j >= 0 && j != i - k) ++count[size_t(j) + 1];  // (successors k tokens ahead are read from the halo)
     }
   }
   for (int32_t t = 0; t < T; ++t) count[t + 1] += count[t];
@@ -108,7 +108,7 @@ bool build_mamba_plan(const int32_t* parent, const int32_t* seg_start, const int
   for (int k = 1; k <= kHalo; ++k)
     for (int32_t i = 0; i < T; ++i) {
       const int32_t j = m.halo[size_t(i) * kHalo + k - 1];
-      if (j >= 0) m.csucc[fill[j]++] = 4 * i + k;
+      if (j >= 0 && j != i - k) m.csucc[fill[j]++] = 4 * i + k;
     }
   // units
   std::vector<int32_t> last_unit(S, -1);
@@ -186,40 +186,12 @@ __device__ inline float4 fma4(float4 a, float4 b, float4 c) {
 
 constexpr int kConvTokens = 16;  // tokens per block: the taps loaded once serve all of them
 
-// The last few rows a thread touched, keyed by token (the keys are the same
-// in every lane, so hits and misses do not diverge).  Inside a segment a
-// token's predecessors, or its successors, are the neighbouring tokens the
-// thread has just loaded, so most rows are read from memory once.
-template <typename V, int R>
-struct RowCache {
-  int id[R];
-  V v[R];
-  __device__ inline RowCache() {
-#pragma unroll
-    for (int q = 0; q < R; ++q) id[q] = -1;
-  }
-  template <typename Load>
-  __device__ inline V get(int key, Load load) {
-    V r{};
-    bool hit = false;
-#pragma unroll
-    for (int q = 0; q < R; ++q)
-      if (id[q] == key) r = v[q], hit = true;
-    if (!hit) {
-      r = load(key);
-      put(key, r);
-    }
-    return r;
-  }
-  __device__ inline void put(int key, V val) {
-#pragma unroll
-    for (int q = R - 1; q > 0; --q) id[q] = id[q - 1], v[q] = v[q - 1];
-    id[0] = key, v[0] = val;
-  }
-};
-
-// one block per (16 tokens, 256 channel quads): a thread loads its taps once
-// and walks the tokens; halo indices are block-uniform
+// one block per (16 tokens, 256 channel quads): a thread loads its taps once,
+// issues the loads of all its 16 token rows together (the walk would otherwise
+// have one row in flight at a time), and reads a tap k tokens back from those
+// registers when it lies in the block's own rows on the same path (src = i - k);
+// other sources (a segment's first tokens) are loaded when needed.  Halo
+// indices are block-uniform.
 template <int W>
 __global__ __launch_bounds__(256) void conv_fwd_kernel(const float4* __restrict__ x, const float* __restrict__ w,
                                                        const float4* __restrict__ bias,
@@ -230,27 +202,47 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const float4* __restrict_
   float4 t[W];
   load_taps<W>(w, 4 * c4, t);
   const float4 b = bias[c4];
-  const int i0 = blockIdx.x * kConvTokens, i1 = min(T, i0 + kConvTokens);
-  RowCache<float4, kHalo> cache;
-  auto load = [&](int tok) { return x[(size_t)tok * C4 + c4]; };
-  for (int i = i0; i < i1; ++i) {
-    const float4 xi = load(i);
-    float4 acc = fma4(t[W - 1], xi, b);
+  const int i0 = blockIdx.x * kConvTokens, n = min(T - i0, kConvTokens);
+  float4 rows[kConvTokens];
 #pragma unroll
-    for (int k = 1; k < W; ++k) {  // k steps back along the path: tap W-1-k
-      const int src = halo[(size_t)i * kHalo + k - 1];
-      if (src < 0) break;
-      acc = fma4(t[W - 1 - k], cache.get(src, load), acc);
+  for (int q = 0; q < kConvTokens; ++q)
+    rows[q] = q < n ? x[(size_t)(i0 + q) * C4 + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  // back[k - 1]: the row k tokens before the current one in the block (k <= kHalo)
+  float4 back[kHalo];
+#pragma unroll
+  for (int k = 0; k < kHalo; ++k) back[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int q = 0; q < kConvTokens; ++q) {
+    if (q < n) {
+      const int i = i0 + q;
+      float4 acc = fma4(t[W - 1], rows[q], b);
+#pragma unroll
+      for (int k = 1; k < W; ++k) {  // k steps back along the path: tap W-1-k (-1: the path is shorter)
+        const int src = halo[(size_t)i * kHalo + k - 1];
+        if (src >= 0) {
+          float4 xs = back[k - 1];
+          if (!(q >= k && src == i - k)) xs = x[(size_t)src * C4 + c4];
+          acc = fma4(t[W - 1 - k], xs, acc);
+        }
+      }
+      y[(size_t)i * C4 + c4] = acc;
     }
-    y[(size_t)i * C4 + c4] = acc;
-    cache.put(i, xi);
+#pragma unroll
+    for (int k = kHalo - 1; k > 0; --k) back[k] = back[k - 1];
+    back[0] = rows[q];
   }
 }
 
 // dx[j] = w[:, W-1] dy[j] + sum over tokens i with prev^k(i) = j, 1 <= k < W,
-// of w[:, W-1-k] dy[i]; every branch's halo lands on the shared prefix
+// of w[:, W-1-k] dy[i]; every branch's halo lands on the shared prefix.  As in
+// the forward, a thread issues the loads of its block's 16 dy rows together.
+// A successor k tokens ahead on the same path (i = j + k, found in the halo
+// table) is read from them when it lies in the block; the other successors (a
+// branch point's children, listed in the successor table) and the rows past
+// the block are loaded when needed.
 template <int W>
 __global__ __launch_bounds__(256) void conv_bwd_dx_kernel(const float4* __restrict__ dy, const float* __restrict__ w,
+                                                          const int32_t* __restrict__ halo,
                                                           const int32_t* __restrict__ csucc_ptr,
                                                           const int32_t* __restrict__ csucc, int T, int C4,
                                                           float4* __restrict__ dx) {
@@ -258,22 +250,48 @@ __global__ __launch_bounds__(256) void conv_bwd_dx_kernel(const float4* __restri
   if (c4 >= C4) return;
   float4 t[W];
   load_taps<W>(w, 4 * c4, t);
-  const int j0 = blockIdx.x * kConvTokens, j1 = min(T, j0 + kConvTokens);
-  RowCache<float4, kHalo + 1> cache;
-  auto load = [&](int tok) { return dy[(size_t)tok * C4 + c4]; };
-  for (int j = j0; j < j1; ++j) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    acc = fma4(t[W - 1], cache.get(j, load), acc);
+  const int j0 = blockIdx.x * kConvTokens, n = min(T - j0, kConvTokens);
+  float4 rows[kConvTokens];
+#pragma unroll
+  for (int q = 0; q < kConvTokens; ++q)
+    rows[q] = q < n ? dy[(size_t)(j0 + q) * C4 + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  // the other successors (a branch point's children), then the store
+  auto dx_far = [&](int j, float4 acc) {
     for (int e = csucc_ptr[j]; e < csucc_ptr[j + 1]; ++e) {
       const int ent = csucc[e], i = ent >> 2, k = ent & 3;
       if (k >= W) continue;
       float4 tk = t[0];
 #pragma unroll
-      for (int q = 1; q < W; ++q)
-        if (W - 1 - k == q) tk = t[q];
-      acc = fma4(tk, cache.get(i, load), acc);
+      for (int r = 1; r < W; ++r)
+        if (W - 1 - k == r) tk = t[r];
+      acc = fma4(tk, dy[(size_t)i * C4 + c4], acc);
     }
     dx[(size_t)j * C4 + c4] = acc;
+  };
+  // the block's tokens in reverse, so that ahead[k - 1] holds the row k tokens ahead
+  float4 ahead[kHalo];
+#pragma unroll
+  for (int k = 0; k < kHalo; ++k) ahead[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int q = kConvTokens - 1; q >= 0; --q) {
+    if (q < n) {
+      const int j = j0 + q;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      acc = fma4(t[W - 1], rows[q], acc);
+#pragma unroll
+      for (int k = 1; k < W; ++k) {  // the successor k tokens ahead, if j is its k-th predecessor
+        const int i = j + k;
+        if (i < T && halo[(size_t)i * kHalo + k - 1] == j) {
+          float4 v = ahead[k - 1];
+          if (q + k >= n) v = dy[(size_t)i * C4 + c4];  // past the block's rows
+          acc = fma4(t[W - 1 - k], v, acc);
+        }
+      }
+      dx_far(j, acc);
+    }
+#pragma unroll
+    for (int k = kHalo - 1; k > 0; --k) ahead[k] = ahead[k - 1];
+    ahead[0] = rows[q];
   }
 }
 
@@ -281,26 +299,54 @@ constexpr int kConvRows = 256;  // tokens per partial of the weight gradient
 
 // partial[b][c][k] = sum over tokens i of block b of dy[i, c] x[prev^k(i), c]
 // for k < W, partial[b][c][kConvMaxWidth] = sum of dy[i, c]; one thread per
-// four channels
+// four channels.  The thread walks its tokens in batches whose dy and x rows
+// are loaded together, and keeps the x rows of the last kHalo tokens for the
+// taps that reach back along the same path (prev^k(i) = i - k); other
+// sources are loaded when needed.
+constexpr int kDwBatch = 8;
 __global__ void conv_bwd_dw_partial_kernel(const float4* __restrict__ x, const float4* __restrict__ dy,
                                            const int32_t* __restrict__ halo, int T, int C4, int W,
                                            float* __restrict__ partial) {
   const int c4 = blockIdx.y * blockDim.x + threadIdx.x;
   if (c4 >= C4) return;
   const int i0 = blockIdx.x * kConvRows, i1 = min(T, i0 + kConvRows);
+  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 acc[kConvMaxWidth + 1];
 #pragma unroll
-  for (int k = 0; k <= kConvMaxWidth; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i = i0; i < i1; ++i) {
-    const float4 g = dy[(size_t)i * C4 + c4];
-    acc[kConvMaxWidth].x += g.x, acc[kConvMaxWidth].y += g.y, acc[kConvMaxWidth].z += g.z,
-        acc[kConvMaxWidth].w += g.w;
+  for (int k = 0; k <= kConvMaxWidth; ++k) acc[k] = zero;
+  float4 back[kHalo];  // back[k - 1]: the x row of the token k before the current one (in this walk)
 #pragma unroll
-    for (int k = 0; k < kConvMaxWidth; ++k) {
-      if (k >= W) break;
-      const int src = k == 0 ? i : halo[(size_t)i * kHalo + k - 1];
-      if (src < 0) break;
-      acc[k] = fma4(g, x[(size_t)src * C4 + c4], acc[k]);
+  for (int k = 0; k < kHalo; ++k) back[k] = zero;
+  for (int ib = i0; ib < i1; ib += kDwBatch) {
+    float4 g[kDwBatch], xr[kDwBatch];
+#pragma unroll
+    for (int q = 0; q < kDwBatch; ++q) {
+      const bool in = ib + q < i1;
+      g[q] = in ? dy[(size_t)(ib + q) * C4 + c4] : zero;
+      xr[q] = in ? x[(size_t)(ib + q) * C4 + c4] : zero;
+    }
+#pragma unroll
+    for (int q = 0; q < kDwBatch; ++q) {
+      const int i = ib + q;
+      if (i < i1) {
+        acc[kConvMaxWidth].x += g[q].x, acc[kConvMaxWidth].y += g[q].y, acc[kConvMaxWidth].z += g[q].z,
+            acc[kConvMaxWidth].w += g[q].w;
+        acc[0] = fma4(g[q], xr[q], acc[0]);
+#pragma unroll
+        for (int k = 1; k < kConvMaxWidth; ++k) {
+          if (k < W) {
+            const int src = halo[(size_t)i * kHalo + k - 1];
+            if (src >= 0) {
+              float4 xs = back[k - 1];
+              if (!(src == i - k && i - k >= i0)) xs = x[(size_t)src * C4 + c4];
+              acc[k] = fma4(g[q], xs, acc[k]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int k = kHalo - 1; k > 0; --k) back[k] = back[k - 1];
+      back[0] = xr[q];
     }
   }
   float* out = partial + ((size_t)blockIdx.x * C4 * 4 + 4 * c4) * (kConvMaxWidth + 1);
@@ -1400,10 +1446,10 @@ int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int
     float4* d4 = reinterpret_cast<float4*>(dx);
     const int32_t *cp = plan->d_csucc_ptr, *cs = plan->d_csucc;
     switch (width) {
-      case 1: hipLaunchKernelGGL(conv_bwd_dx_kernel<1>, grid, block, 0, s, g4, weight, cp, cs, T, C4, d4); break;
-      case 2: hipLaunchKernelGGL(conv_bwd_dx_kernel<2>, grid, block, 0, s, g4, weight, cp, cs, T, C4, d4); break;
-      case 3: hipLaunchKernelGGL(conv_bwd_dx_kernel<3>, grid, block, 0, s, g4, weight, cp, cs, T, C4, d4); break;
-      default: hipLaunchKernelGGL(conv_bwd_dx_kernel<4>, grid, block, 0, s, g4, weight, cp, cs, T, C4, d4); break;
+      case 1: hipLaunchKernelGGL(conv_bwd_dx_kernel<1>, grid, block, 0, s, g4, weight, plan->d_halo, cp, cs, T, C4, d4); break;
+      case 2: hipLaunchKernelGGL(conv_bwd_dx_kernel<2>, grid, block, 0, s, g4, weight, plan->d_halo, cp, cs, T, C4, d4); break;
+      case 3: hipLaunchKernelGGL(conv_bwd_dx_kernel<3>, grid, block, 0, s, g4, weight, plan->d_halo, cp, cs, T, C4, d4); break;
+      default: hipLaunchKernelGGL(conv_bwd_dx_kernel<4>, grid, block, 0, s, g4, weight, plan->d_halo, cp, cs, T, C4, d4); break;
     }
   }
   const int nblk = (T + kConvRows - 1) / kConvRows;
