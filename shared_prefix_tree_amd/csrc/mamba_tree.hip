@@ -859,8 +859,9 @@ struct ScanBwdArgs {
   float* in;      // [U][H][P][N]: local_in, then in(u)
   float* gout;    // [U][H][P][N]: out(u)
   float* decay;   // [U][H]
-  float* dB_part; // [T][H][N]
-  float* dC_part; // [T][H][N]
+  int hpb;        // heads per block of the gradient pass (they share a group)
+  float* dB_part; // [T][H / hpb][N]: per block of heads
+  float* dC_part; // [T][H / hpb][N]
   float* dA_part; // [U][H]
   float* dD_part; // [U][H]
   float *dx, *ddt, *dA, *dB, *dC, *dD;
@@ -963,12 +964,12 @@ struct FirstJobs {
 };
 
 template <int N>
-__global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a) {
+__device__ __forceinline__ void ssm_bwd_grad_head(const ScanBwdArgs& a, BwdSmem<N>& sm, int u, int h, int hp,
+                                                  int hh) {
   constexpr int PB = BwdSmem<N>::PB;
   constexpr int NT = N / 32;            // 32-column tiles of the state
   constexpr int GT = 2 * NT;            // 32 x 32 tiles of the 64 x N state
-  __shared__ __attribute__((aligned(16))) BwdSmem<N> sm;
-  const int u = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int HP = a.H / a.hpb;           // blocks of heads
   const int g = h / (a.H / a.G);
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = a.unit_start[u], len = a.unit_len[u];
@@ -1048,6 +1049,19 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
         sm.S0[row * PB + col] = pfs[r];
         sm.G[row * PB + col] = Gt[r];
         gs = fmaf(Gt[r], pfs[r], gs);
+      }
+    }
+    // this lane's dB / dC entries of the chunk from the block's earlier heads,
+    // read before the next chunk's inputs (loads complete in order, so using
+    // them then does not wait for those)
+    float prevC[16], prevB[16];
+    if (hh > 0 && wave < NT) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int k = tile_row(r, ln);
+        const size_t e = ((size_t)(c0 + min(k, clen - 1)) * HP + hp) * N + 32 * wave + tile_col(ln);
+        prevC[r] = a.dC_part[e];
+        prevB[r] = a.dB_part[e];
       }
     }
     if (c > 0) fetch(c - 1);  // in flight during this chunk
@@ -1150,7 +1164,8 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int k = tile_row(r, ln);
-          if (k < clen) a.dC_part[((size_t)(c0 + k) * a.H + h) * N + 32 * j + tile_col(ln)] = cc[r];
+          if (k < clen)  // the block's heads added in order
+            a.dC_part[((size_t)(c0 + k) * HP + hp) * N + 32 * j + tile_col(ln)] = hh == 0 ? cc[r] : prevC[r] + cc[r];
         }
       } else if (j < 2 * NT) {  // dB(k, n) = dt_k [e^(l_e-l_k) G^T x + sum_m W2[k][m] C[m][n]]
         const int nt = j - NT;
@@ -1161,7 +1176,9 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int k = tile_row(r, ln);
-          if (k < clen) a.dB_part[((size_t)(c0 + k) * a.H + h) * N + 32 * nt + tile_col(ln)] = sm.dt[k] * cc[r];
+          if (k < clen)
+            a.dB_part[((size_t)(c0 + k) * HP + hp) * N + 32 * nt + tile_col(ln)] =
+                hh == 0 ? sm.dt[k] * cc[r] : fmaf(sm.dt[k], cc[r], prevB[r]);
         }
       } else {  // bracket(j, p) = e^(l_e-l_j) (G B_j)[p] + sum_k W3[j][k] dy[k][p]; dx = D dy + dt_j bracket
         const int pt = j - 2 * NT;
@@ -1218,7 +1235,21 @@ __global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a
   }
 }
 
-// dB, dC: the heads of each group summed in head order; one thread per (token, group, column)
+// one block per (unit, block of hpb heads of one group), the heads in order:
+// each adds its dB, dC terms onto the previous head's (every lane writes the
+// same entries for every head), so the group sum reads H / hpb partials
+template <int N>
+__global__ __launch_bounds__(kBwdThreads) void ssm_bwd_grad_kernel(ScanBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) BwdSmem<N> sm;
+  const int HP = a.H / a.hpb;
+  const int u = blockIdx.x / HP, hp = blockIdx.x % HP;
+  for (int hh = 0; hh < a.hpb; ++hh) {
+    ssm_bwd_grad_head<N>(a, sm, u, hp * a.hpb + hh, hp, hh);
+    __syncthreads();  // the next head reuses LDS
+  }
+}
+
+// dB, dC: the partials of each group summed in head order; one thread per (token, group, column)
 __global__ void ssm_bwd_group_sum_kernel(ScanBwdArgs a, int N) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)a.T * a.G * N) return;
@@ -1226,10 +1257,10 @@ __global__ void ssm_bwd_group_sum_kernel(ScanBwdArgs a, int N) {
   const long long tg = idx / N;
   const int g = int(tg % a.G);
   const long long t = tg / a.G;
-  const int hpg = a.H / a.G;
+  const int HP = a.H / a.hpb, ppg = a.H / a.G / a.hpb;  // partials per group
   float sb = 0.f, sc = 0.f;
-  for (int hh = 0; hh < hpg; ++hh) {
-    const size_t off = ((size_t)t * a.H + g * hpg + hh) * N + n;
+  for (int q = 0; q < ppg; ++q) {
+    const size_t off = ((size_t)t * HP + g * ppg + q) * N + n;
     sb += a.dB_part[off];
     sc += a.dC_part[off];
   }
@@ -1256,7 +1287,8 @@ hipError_t launch_ssm_bwd(const ScanBwdArgs& a, hipStream_t s) {
   const LocalArgs la{a.dy, a.C, a.dt, a.A, a.unit_start, a.unit_len, a.H, a.G, a.in, a.decay};
   hipLaunchKernelGGL((ssm_unit_local_kernel<N, true>), grid, dim3(kFwdThreads), 0, s, la);
   hipLaunchKernelGGL((ssm_bwd_propagate_kernel<N>), dim3(unsigned(a.H) * 4), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((ssm_bwd_grad_kernel<N>), grid, dim3(kBwdThreads), 0, s, a);
+  hipLaunchKernelGGL((ssm_bwd_grad_kernel<N>), dim3(unsigned(a.U) * unsigned(a.H / a.hpb)), dim3(kBwdThreads), 0,
+                     s, a);
   const long long n = (long long)a.T * a.G * N;
   hipLaunchKernelGGL(ssm_bwd_group_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, a, N);
   hipLaunchKernelGGL(ssm_bwd_unit_sum_kernel, dim3(unsigned((a.H + 63) / 64)), dim3(64), 0, s, a);
@@ -1264,6 +1296,12 @@ hipError_t launch_ssm_bwd(const ScanBwdArgs& a, hipStream_t s) {
 }
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// heads per block of the gradient pass: 4, 2 or 1, whichever divides the heads of a group
+int grad_heads_per_block(const tree_attn_ssm_shape* shape) {
+  const int hpg = shape->num_heads / shape->num_groups;
+  return hpg % 4 == 0 ? 4 : hpg % 2 == 0 ? 2 : 1;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -1474,9 +1512,12 @@ size_t tree_attn_ssm_workspace_bytes(tree_attn_mamba_plan_t plan, const tree_att
 }
 
 size_t tree_attn_ssm_bwd_workspace_bytes(tree_attn_mamba_plan_t plan, const tree_attn_ssm_shape* shape) {
-  if (!plan || !shape || shape->num_heads < 1 || shape->head_dim < 1 || shape->state_dim < 1) return 0;
+  if (!plan || !shape || shape->num_heads < 1 || shape->num_groups < 1 || shape->head_dim < 1 ||
+      shape->state_dim < 1)
+    return 0;
   const size_t st = align256(state_floats(plan, shape) * 4);
-  const size_t part = align256(size_t(plan->T) * shape->num_heads * shape->state_dim * 4);
+  const size_t part = align256(size_t(plan->T) * (shape->num_heads / grad_heads_per_block(shape)) *
+                               shape->state_dim * 4);
   const size_t uh = align256(size_t(plan->U) * shape->num_heads * 4);
   return 2 * st + 2 * part + 3 * uh;
 }
@@ -1507,8 +1548,9 @@ int tree_attn_ssm_bwd(const float* x, const float* dt, const float* A, const flo
   a.usucc_ptr = plan->d_usucc_ptr, a.usucc = plan->d_usucc, a.uchain = plan->d_uchain;
   a.H = shape->num_heads, a.G = shape->num_groups, a.U = plan->U, a.T = plan->T;
   char* w = static_cast<char*>(workspace);
+  a.hpb = grad_heads_per_block(shape);
   const size_t st = align256(state_floats(plan, shape) * 4);
-  const size_t part = align256(size_t(plan->T) * shape->num_heads * shape->state_dim * 4);
+  const size_t part = align256(size_t(plan->T) * (shape->num_heads / a.hpb) * shape->state_dim * 4);
   const size_t uh = align256(size_t(plan->U) * shape->num_heads * 4);
   a.in = reinterpret_cast<float*>(w);
   a.gout = reinterpret_cast<float*>(w + st);
