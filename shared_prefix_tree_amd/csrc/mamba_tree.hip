@@ -850,7 +850,8 @@ hipError_t launch_ssm_fwd(const ScanArgs& a, hipStream_t s) {
 //    Every exponent is <= 0.  The chunk's start states come from one
 //    forward sweep over the unit from the saved start(u); G from out(u),
 //    moved back one chunk at a time.  dB and dC are summed over the heads
-//    of a group, and dA, dD over units, by separate fixed-order passes.
+//    of a group (in place over the heads a block takes in turn, then over
+//    those blocks), and dA, dD over units, all in fixed orders.
 
 struct ScanBwdArgs {
   const float *x, *dt, *A, *B, *C, *D, *dy, *states;
