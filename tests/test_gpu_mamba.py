@@ -103,10 +103,12 @@ def test_ssm_forward_matches_oracle(name, N, H, G):
 
 
 @pytest.mark.parametrize("name", ["tiny_tree", "forest_long_segments", "forest_short_segments"])
-@pytest.mark.parametrize("N,H,G", [(128, 4, 2), (64, 6, 3)])
+@pytest.mark.parametrize("N,H,G", [(128, 4, 2), (64, 6, 3), (64, 3, 1), (64, 8, 1)])
 def test_ssm_backward_matches_oracle(name, N, H, G):
     """Every gradient against the oracle; a branch point's state gets the sum
-    of its branches (the forests have forks inside and at the end of units)."""
+    of its branches (the forests have forks inside and at the end of units).
+    The shapes give the gradient pass 2, 2, 1 and 4 heads per block (the
+    largest of 4, 2, 1 that divides the heads of a group)."""
     import shared_prefix_tree_amd as sp
 
     topo = forests()[name]
