@@ -52,6 +52,22 @@ def measured_traffic(workload, kernel):
     return k.get("bytes_per_launch") if k else None
 
 
+def mamba_scan_traffic():
+    """HBM bytes of the Mamba scan kernels per step (one forward, one backward)
+    from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE record, or None when it
+    was taken on a different mamba_tree.hip."""
+    import hashlib
+
+    try:
+        rec = json.load(open(PROFILE_TRAFFIC)).get("mamba_agent_tree_65536", {})
+        src = open(os.path.join(ROOT, "shared_prefix_tree_amd", "csrc", "mamba_tree.hip"), "rb").read()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != hashlib.sha256(src).hexdigest()[:16]:
+        return None
+    return rec.get("scan_bytes_per_step")
+
+
 def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
@@ -274,8 +290,8 @@ def edge_loss(args):
                    "saved_logits_gb": round(edges.saved_bytes() / 1e9, 3)},
         "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
         "fwd_tflops": round(fwd_f / (f_ms * 1e-3) / 1e12, 2), "bwd_tflops": round(bwd_f / (b_ms * 1e-3) / 1e12, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": round(tf / 2500.0, 4), "traffic": None},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
         "mean_loss": round(mean_loss, 5),
     }), flush=True)
 
@@ -359,7 +375,7 @@ def mamba(args):
         "ssm_fwd_tflops": round(f_fwd / (sf * 1e-3) / 1e12, 3), "ssm_bwd_tflops": round(f_bwd / (sbw * 1e-3) / 1e12, 3),
         "conv_fwd_gbs": round(conv_gbs[0], 1), "conv_bwd_gbs": round(conv_gbs[1], 1),
         "roofline": {"bound": "alu", "achieved": round(scan_tf, 3), "peak": 157.3, "unit": "TFLOP/s",
-                     "frac": round(scan_tf / 157.3, 4), "traffic": None},
+                     "frac": round(scan_tf / 157.3, 4), "traffic": mamba_scan_traffic()},
     }), flush=True)
 
 
