@@ -28,7 +28,7 @@
  * float32 accumulation (bf16 inputs feed bf16 matrix-core products; the
  * softmax probabilities are rounded to bf16 before the P*V product).
  * Query head h uses key/value head h / (Hq / Hkv).  softmax_scale <= 0 means
- * 1/sqrt(D).
+ * 1/sqrt(D); a NaN or infinite softmax_scale is INVALID_ARGUMENT.
  *
  * Ownership: the caller owns every tensor (device memory) and the
  * workspace; the library owns a plan (host + device copies of the
@@ -72,7 +72,7 @@ typedef struct {
   int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0 */
   int32_t head_dim;     /* D: 64 or 128 for bf16, 64 for fp32 */
   int32_t dtype;        /* TREE_ATTN_BF16 or TREE_ATTN_FP32 */
-  float softmax_scale;  /* <= 0: 1/sqrt(D) */
+  float softmax_scale;  /* finite; <= 0: 1/sqrt(D) */
 } tree_attn_shape;
 
 typedef struct {
@@ -149,8 +149,8 @@ int tree_attn_plan_info(tree_attn_plan_t plan, tree_attn_plan_info_t* info);
 /*
  * Bounded fragment planning with ancestor repetition (host only; issue
  * "Shared-prefix training with context parallelism for exact agent
- * trajectories": the trainer bounds fragments and may repeat ancestors
- * across fragments to honour the memory bound).  Splits a DFS segment forest
+ * trajectories", section "Describe the solution you'd like": fragments are
+ * size-bounded, and ancestor segments may be duplicated in several of them).  Splits a DFS segment forest
  * (as for tree_attn_plan) into fragments of at most max_tokens tokens, each
  * a DFS forest of its own (segments contiguous from token 0) in which every
  * token sees exactly the tokens it sees in the source forest: a fragment
@@ -192,10 +192,11 @@ int tree_attn_fragments_export(tree_attn_fragments_t fragments, int32_t which, i
                                int64_t* count);
 
 /*
- * Sampled-edge projection and loss (draft "feat(hybrid): add opt-in
- * shared-prefix attention and Mamba execution", section "Summary": select
- * edge-source hidden states before the vocabulary projection, one loss owner
- * per sampled action).  An edge e is a sampled token tgt[e] (a vocabulary
+ * Sampled-edge projection and loss (Megatron-LM pull request 7387, section
+ * "Summary": edge-source hidden states are picked out before the vocabulary
+ * projection; issue "Shared-prefix training with context parallelism for
+ * exact agent trajectories", section "Describe the solution you'd like": a
+ * single loss owner per sampled action).  An edge e is a sampled token tgt[e] (a vocabulary
  * index) predicted from the hidden state of token src[e]; only those states
  * go through the vocabulary head W [V, d]:
  *   logits[e] = W h[src[e]],  lse[e] = log sum_v exp(logits[e, v]),
@@ -275,6 +276,7 @@ typedef struct {
   int32_t num_tokens, num_segments, num_units, unit_tokens, max_depth, max_conv_width;
 } tree_attn_mamba_plan_info_t;
 typedef struct {
+  int32_t num_tokens; /* T: rows of x, dt, B, C, y; must equal the plan's token count */
   int32_t num_heads, head_dim, num_groups, state_dim;
 } tree_attn_ssm_shape;
 int tree_attn_mamba_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
@@ -291,14 +293,16 @@ int tree_attn_mamba_plan_info(tree_attn_mamba_plan_t plan, tree_attn_mamba_plan_
 #define TREE_ATTN_MAMBA_UNIT_PRED 3
 int tree_attn_mamba_plan_export(tree_attn_mamba_plan_t plan, int32_t which, int32_t* buf, int64_t cap,
                                 int64_t* count);
-/* Convolution forward: writes y. */
-int tree_attn_conv_fwd(const float* x, const float* weight, const float* bias, int32_t channels, int32_t width,
-                       tree_attn_mamba_plan_t plan, float* y, void* stream);
+/* Convolution forward: writes y.  num_tokens (the rows of x and y) must
+ * equal the plan's token count, else INVALID_ARGUMENT before any launch. */
+int tree_attn_conv_fwd(const float* x, const float* weight, const float* bias, int32_t num_tokens,
+                       int32_t channels, int32_t width, tree_attn_mamba_plan_t plan, float* y, void* stream);
 size_t tree_attn_conv_bwd_workspace_bytes(tree_attn_mamba_plan_t plan, int32_t channels, int32_t width);
-/* Convolution backward of sum <dy, y>: overwrites dx, dweight, dbias. */
-int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int32_t channels, int32_t width,
-                       tree_attn_mamba_plan_t plan, float* dx, float* dweight, float* dbias, void* workspace,
-                       size_t workspace_bytes, void* stream);
+/* Convolution backward of sum <dy, y>: overwrites dx, dweight, dbias.
+ * num_tokens (rows of x, dy, dx) must equal the plan's token count. */
+int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int32_t num_tokens, int32_t channels,
+                       int32_t width, tree_attn_mamba_plan_t plan, float* dx, float* dweight, float* dbias,
+                       void* workspace, size_t workspace_bytes, void* stream);
 /* Bytes of the saved states (the state before every 32-token chunk of every
  * scan unit, written by the forward for the backward) and of the forward's
  * workspace. */

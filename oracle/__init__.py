@@ -24,8 +24,6 @@ from .tree_attention import (  # noqa: F401
     backward_keys,
     masked_dense_forward,
     masked_dense_backward,
-    as_f64,
-    rel_l2,
 )
 from .fragments import fragment  # noqa: F401
 from .edge_loss import edge_logits, edge_loss_forward, edge_loss_backward  # noqa: F401

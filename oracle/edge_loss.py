@@ -1,12 +1,12 @@
 """Oracle for the sampled-edge projection and loss (test infrastructure
 only: tests, the smoke check and the benchmark's CPU leg).
 
-The draft "feat(hybrid): add opt-in shared-prefix attention and Mamba
-execution" (section "Summary") selects the hidden states that are the source
-of a sampled edge before the vocabulary projection; the issue "Shared-prefix
-training with context parallelism for exact agent trajectories" (section
-"Describe the solution you'd like") gives every sampled action one loss
-owner.  The pages name the loss no further; the reading taken here is the
+Megatron-LM pull request 7387 (section "Summary") picks out the hidden
+states that are the source of a sampled edge before the vocabulary
+projection; the issue "Shared-prefix training with context parallelism for
+exact agent trajectories" (section "Describe the solution you'd like") sends
+only those states through the vocabulary head and gives every sampled action
+a single loss owner.  The pages name the loss no further; the reading taken here is the
 plain next-token cross-entropy of each edge:
 
   logits[e] = W h[src[e]],   loss[e] = log sum_v exp(logits[e, v]) - logits[e, tgt[e]]

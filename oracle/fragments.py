@@ -2,9 +2,9 @@
 infrastructure only: tests, the smoke check and the benchmark's CPU leg).
 
 Issue "Shared-prefix training with context parallelism for exact agent
-trajectories", section "Describe the solution you'd like": the trainer
-bounds fragments and may repeat ancestors across fragments so that the
-memory bound holds.  The pages give the goal, not the steps; the reading
+trajectories", section "Describe the solution you'd like": fragments are
+size-bounded, and ancestor segments may be duplicated in several of them
+for that bound to hold.  The pages give the goal, not the steps; the reading
 taken here (and by the library) is the plainest one that keeps attention
 exact:
 

@@ -56,6 +56,12 @@ Parity status (pins live in ``tests/test_oracle.py``):
   owner per token, sibling-permutation and fragment-copy invariance.
 * ``pairs`` -- pinned: the tiny tree's count worked out by hand, and brute
   force (sum of |V(i)|).
+* ``ancestors`` / ``subtree_end`` / ``segment_pairs`` /
+  ``position_in_sequence`` -- pinned: root-to-segment paths, last emitted
+  tokens and per-segment pair counts derived from children lists and
+  reconstructed root-to-leaf sequences.
+
+Every public function has a pin; none is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -149,27 +155,6 @@ def segment_pairs(topo):
 def pairs(topo):
     """Number of (query, key) pairs on ancestor paths, per head: sum_i |V(i)|."""
     return int(sum(segment_pairs(topo)))
-
-
-# ---------------------------------------------------------------------------
-# dtype helpers
-
-
-def as_f64(x, dtype="bf16"):
-    """bf16 bit patterns (uint16) or float arrays -> float64."""
-    x = np.asarray(x)
-    if dtype == "bf16" or x.dtype == np.uint16:
-        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    return x.astype(np.float64)
-
-
-def rel_l2(x, ref):
-    """||x - ref||_2 / ||ref||_2 over all elements, in float64."""
-    x = np.asarray(x, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    den = np.linalg.norm(ref.ravel())
-    num = np.linalg.norm((x - ref).ravel())
-    return float(num / den) if den > 0 else float(num)
 
 
 # ---------------------------------------------------------------------------

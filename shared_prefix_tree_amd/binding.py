@@ -146,6 +146,7 @@ class MambaPlanInfo(ctypes.Structure):
 
 class SsmShape(ctypes.Structure):
     _fields_ = [
+        ("num_tokens", ctypes.c_int32),
         ("num_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("num_groups", ctypes.c_int32),
@@ -213,10 +214,10 @@ def library():
     lib.tree_attn_mamba_plan_info.argtypes = [vp, ctypes.POINTER(MambaPlanInfo)]
     lib.tree_attn_mamba_plan_export.argtypes = [vp, ctypes.c_int32, i32p, ctypes.c_int64,
                                                 ctypes.POINTER(ctypes.c_int64)]
-    lib.tree_attn_conv_fwd.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+    lib.tree_attn_conv_fwd.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
     lib.tree_attn_conv_bwd_workspace_bytes.argtypes = [vp, ctypes.c_int32, ctypes.c_int32]
     lib.tree_attn_conv_bwd_workspace_bytes.restype = ctypes.c_size_t
-    lib.tree_attn_conv_bwd.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp,
+    lib.tree_attn_conv_bwd.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp,
                                        ctypes.c_size_t, vp]
     for name in ("tree_attn_ssm_states_bytes", "tree_attn_ssm_workspace_bytes"):
         getattr(lib, name).argtypes = [vp, ctypes.POINTER(SsmShape)]
@@ -480,6 +481,7 @@ class MambaPlan:
         _check(fn(pp, sp, np_, ctypes.c_int32(len(p)), ctypes.byref(h)))
         self._handle = h
         self.device = device
+        self.num_tokens = int(self.info()["num_tokens"])
 
     @classmethod
     def from_topology(cls, topo, device=True):
@@ -526,6 +528,11 @@ def _f32(name, t, shape=None):
     return t
 
 
+def _plan_rows(name, t, plan):
+    if t.shape[0] != plan.num_tokens:
+        raise ValueError(f"{name} has {t.shape[0]} rows, the plan has {plan.num_tokens} tokens")
+
+
 def _stream_of(t, stream):
     import torch
 
@@ -541,10 +548,11 @@ def conv_fwd(x, weight, bias, plan: MambaPlan, out=None, stream=None):
     T, C = x.shape
     W = weight.shape[1]
     _f32("x", x), _f32("weight", weight, (C, W)), _f32("bias", bias, (C,))
+    _plan_rows("x", x, plan)
     y = out if out is not None else torch.empty_like(x)
     _f32("out", y, (T, C))
     with torch.cuda.device(x.device):
-        _check(library().tree_attn_conv_fwd(x.data_ptr(), weight.data_ptr(), bias.data_ptr(), C, W, plan.handle,
+        _check(library().tree_attn_conv_fwd(x.data_ptr(), weight.data_ptr(), bias.data_ptr(), T, C, W, plan.handle,
                                             y.data_ptr(), _stream_of(x, stream)))
     return y
 
@@ -556,13 +564,14 @@ def conv_bwd(x, weight, dy, plan: MambaPlan, workspace=None, stream=None):
     T, C = x.shape
     W = weight.shape[1]
     _f32("x", x), _f32("weight", weight, (C, W)), _f32("dy", dy, (T, C))
+    _plan_rows("x", x, plan)
     dx, dw, db = torch.empty_like(x), torch.empty_like(weight), torch.empty(C, dtype=torch.float32, device=x.device)
     lib = library()
     if workspace is None:
         workspace = torch.empty(max(256, lib.tree_attn_conv_bwd_workspace_bytes(plan.handle, C, W)),
                                 dtype=torch.uint8, device=x.device)
     with torch.cuda.device(x.device):
-        _check(lib.tree_attn_conv_bwd(x.data_ptr(), weight.data_ptr(), dy.data_ptr(), C, W, plan.handle,
+        _check(lib.tree_attn_conv_bwd(x.data_ptr(), weight.data_ptr(), dy.data_ptr(), T, C, W, plan.handle,
                                       dx.data_ptr(), dw.data_ptr(), db.data_ptr(), workspace.data_ptr(),
                                       workspace.numel(), _stream_of(x, stream)))
     return dx, dw, db
@@ -571,11 +580,11 @@ def conv_bwd(x, weight, dy, plan: MambaPlan, workspace=None, stream=None):
 def _ssm_shape(x, B):
     T, H, P = x.shape
     _, G, N = B.shape
-    return SsmShape(H, P, G, N)
+    return SsmShape(T, H, P, G, N)
 
 
 def ssm_states_bytes(plan: MambaPlan, num_heads, head_dim, num_groups, state_dim):
-    sh = SsmShape(num_heads, head_dim, num_groups, state_dim)
+    sh = SsmShape(plan.info()["num_tokens"], num_heads, head_dim, num_groups, state_dim)
     return int(library().tree_attn_ssm_states_bytes(plan.handle, ctypes.byref(sh)))
 
 
@@ -590,6 +599,7 @@ def ssm_fwd(x, dt, A, B, C, D, plan: MambaPlan, out=None, states=None, workspace
     for name, t, shp in (("x", x, None), ("dt", dt, (T, H)), ("A", A, (H,)), ("B", B, (T, G, N)),
                          ("C", C, (T, G, N)), ("D", D, (H,))):
         _f32(name, t, shp)
+    _plan_rows("x", x, plan)
     sh = _ssm_shape(x, B)
     lib = library()
     y = out if out is not None else torch.empty_like(x)
@@ -618,6 +628,7 @@ def ssm_bwd(x, dt, A, B, C, D, dy, plan: MambaPlan, states, workspace=None, stre
     for name, t, shp in (("x", x, None), ("dt", dt, (T, H)), ("A", A, (H,)), ("B", B, (T, G, N)),
                          ("C", C, (T, G, N)), ("D", D, (H,)), ("dy", dy, (T, H, P))):
         _f32(name, t, shp)
+    _plan_rows("x", x, plan)
     sh = _ssm_shape(x, B)
     lib = library()
     if workspace is None:

@@ -213,9 +213,10 @@ int check_call(const char* fn, tree_attn_plan_t plan, const tree_attn_shape* sha
   const int64_t grid_k = int64_t(plan->host.ktiles.size()) * shape->num_kv_heads;  // >= the wide list's
   if (grid_q >= (int64_t(1) << 31) || grid_k >= (int64_t(1) << 31))
     return fail(TREE_ATTN_UNSUPPORTED, f + ": launch grid too large");
+  // NaN and infinities are rejected; zero or a negative value asks for the default
   float s = shape->softmax_scale;
-  if (!(s > 0.f)) s = 1.f / std::sqrt(float(shape->head_dim));
   if (!std::isfinite(s)) return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": softmax_scale is not finite");
+  if (s <= 0.f) s = 1.f / std::sqrt(float(shape->head_dim));
   *scale_out = s;
   return TREE_ATTN_OK;
 }

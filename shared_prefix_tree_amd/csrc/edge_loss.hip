@@ -1,11 +1,11 @@
 // Sampled-edge projection and loss: only the hidden states that are the
 // source of a sampled token go through the vocabulary head, each sampled
-// token (edge) owning its loss once (draft "feat(hybrid): add opt-in
-// shared-prefix attention and Mamba execution", section "Summary": select
-// edge-source hidden states before the vocabulary projection; issue
-// "Shared-prefix training with context parallelism for exact agent
-// trajectories", section "Describe the solution you'd like": project only
-// sampled-edge source states, one loss owner per sampled action).
+// token (edge) owning its loss once (Megatron-LM pull request 7387, section
+// "Summary": the edge-source hidden states are picked out before the
+// vocabulary projection; issue "Shared-prefix training with context
+// parallelism for exact agent trajectories", section "Describe the solution
+// you'd like": only sampled-edge sources go through the vocabulary head, and
+// each sampled action has a single loss owner).
 //
 // For edge e with source token src[e] and sampled token tgt[e]:
 //   logits[e] = W h[src[e]]       (W: [V, d], h: [T, d], bf16)

@@ -1,9 +1,9 @@
 // Bounded fragment planning with ancestor repetition (host only).
 //
 // Issue "Shared-prefix training with context parallelism for exact agent
-// trajectories" (section "Describe the solution you'd like") has the trainer
-// bound fragments and repeat ancestors across fragments to honour a memory
-// bound; its measured token counts (the issue's own numbers: 3,744,651 tree
+// trajectories" (section "Describe the solution you'd like"): fragments are
+// size-bounded, and ancestor segments may be duplicated in several of them;
+// its measured token counts (the issue's own numbers: 3,744,651 tree
 // tokens, 3,919,929 after fragmentation) are this step's metric.
 #pragma once
 

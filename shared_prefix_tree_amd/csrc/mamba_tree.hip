@@ -1316,9 +1316,18 @@ int check_plan(const char* fn, tree_attn_mamba_plan_t plan) {
   return TREE_ATTN_OK;
 }
 
-int check_ssm_shape(const char* fn, const tree_attn_ssm_shape* sh) {
+// the caller's token count must be the plan's: every kernel walks plan->T rows
+int check_tokens(const char* fn, const tree_attn_mamba_plan_s* p, int32_t num_tokens) {
+  if (num_tokens != p->T)
+    return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": num_tokens " + std::to_string(num_tokens) +
+                                                        " != plan tokens " + std::to_string(p->T));
+  return TREE_ATTN_OK;
+}
+
+int check_ssm_shape(const char* fn, const tree_attn_mamba_plan_s* p, const tree_attn_ssm_shape* sh) {
   const std::string f(fn);
   if (!sh) return report_error(TREE_ATTN_INVALID_ARGUMENT, f + ": shape is NULL");
+  if (int rc = check_tokens(fn, p, sh->num_tokens)) return rc;
   if (sh->num_heads < 1 || sh->num_groups < 1 || sh->num_heads % sh->num_groups != 0)
     return report_error(TREE_ATTN_UNSUPPORTED, f + ": num_heads must be a positive multiple of num_groups");
   if (sh->head_dim != kHeadDim)
@@ -1420,10 +1429,11 @@ int tree_attn_mamba_plan_export(tree_attn_mamba_plan_t plan, int32_t which, int3
   return TREE_ATTN_OK;
 }
 
-int tree_attn_conv_fwd(const float* x, const float* weight, const float* bias, int32_t channels, int32_t width,
-                       tree_attn_mamba_plan_t plan, float* y, void* stream) {
+int tree_attn_conv_fwd(const float* x, const float* weight, const float* bias, int32_t num_tokens,
+                       int32_t channels, int32_t width, tree_attn_mamba_plan_t plan, float* y, void* stream) {
   const char* fn = "tree_attn_conv_fwd";
   if (int rc = check_plan(fn, plan)) return rc;
+  if (int rc = check_tokens(fn, plan, num_tokens)) return rc;
   if (!x || !weight || !bias || !y) return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL pointer");
   if (channels < 4 || channels % 4 != 0)
     return report_error(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": channels must be a positive multiple of 4");
@@ -1457,11 +1467,12 @@ size_t tree_attn_conv_bwd_workspace_bytes(tree_attn_mamba_plan_t plan, int32_t c
   return align256(nblk * size_t(channels) * (kConvMaxWidth + 1) * 4);
 }
 
-int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int32_t channels, int32_t width,
-                       tree_attn_mamba_plan_t plan, float* dx, float* dweight, float* dbias, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+int tree_attn_conv_bwd(const float* x, const float* weight, const float* dy, int32_t num_tokens, int32_t channels,
+                       int32_t width, tree_attn_mamba_plan_t plan, float* dx, float* dweight, float* dbias,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "tree_attn_conv_bwd";
   if (int rc = check_plan(fn, plan)) return rc;
+  if (int rc = check_tokens(fn, plan, num_tokens)) return rc;
   if (!x || !weight || !dy || !dx || !dweight || !dbias || !workspace)
     return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL pointer");
   if (channels < 4 || channels % 4 != 0)
@@ -1529,7 +1540,7 @@ int tree_attn_ssm_bwd(const float* x, const float* dt, const float* A, const flo
                       float* dC, float* dD, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "tree_attn_ssm_bwd";
   if (int rc = check_plan(fn, plan)) return rc;
-  if (int rc = check_ssm_shape(fn, shape)) return rc;
+  if (int rc = check_ssm_shape(fn, plan, shape)) return rc;
   if (!x || !dt || !A || !B || !C || !D || !dy || !states || !dx || !ddt || !dA || !dB || !dC || !dD || !workspace)
     return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL pointer");
   if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(B) || !aligned16(C) || !aligned16(states) ||
@@ -1572,7 +1583,7 @@ int tree_attn_ssm_fwd(const float* x, const float* dt, const float* A, const flo
                       float* states, size_t states_bytes, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "tree_attn_ssm_fwd";
   if (int rc = check_plan(fn, plan)) return rc;
-  if (int rc = check_ssm_shape(fn, shape)) return rc;
+  if (int rc = check_ssm_shape(fn, plan, shape)) return rc;
   if (!x || !dt || !A || !B || !C || !D || !y || !states || !workspace)
     return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": NULL pointer");
   if (!aligned16(x) || !aligned16(y) || !aligned16(B) || !aligned16(C) || !aligned16(states) ||

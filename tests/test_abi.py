@@ -236,6 +236,6 @@ def test_product_package_never_imports_the_oracle():
 def test_mamba_calls_reject_a_host_only_plan_without_a_device():
     plan = sp.MambaPlan([-1, 0], [0, 4], [4, 4], device=False)
     lib = sp.library()
-    rc = lib.tree_attn_conv_fwd(None, None, None, 4, 4, plan.handle, None, None)
+    rc = lib.tree_attn_conv_fwd(None, None, None, 8, 4, 4, plan.handle, None, None)
     assert rc == b.INVALID_ARGUMENT
     assert "host-only" in lib.tree_attn_last_error().decode()

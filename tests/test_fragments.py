@@ -1,8 +1,9 @@
 """Bounded fragment planning with ancestor repetition (host only).
 
 Issue "Shared-prefix training with context parallelism for exact agent
-trajectories", section "Describe the solution you'd like": the trainer
-bounds fragments and may repeat ancestors across fragments.  The oracle
+trajectories", section "Describe the solution you'd like": fragments are
+size-bounded, and ancestor segments may be duplicated in several of them.
+The oracle
 (``oracle.fragment``) is pinned by a hand-worked case and by the property
 that makes the repetition exact -- every owned token sees, mapped back to
 source tokens, exactly its visible set in the source forest; the library's

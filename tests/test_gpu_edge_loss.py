@@ -1,10 +1,10 @@
 """GPU: sampled-edge projection and loss against the float64 oracle.
 
 Only the hidden states that are the source of a sampled edge go through the
-vocabulary head, each sampled action owning its loss once (draft
-"feat(hybrid): add opt-in shared-prefix attention and Mamba execution",
-section "Summary"; issue "Shared-prefix training with context parallelism
-for exact agent trajectories", section "Describe the solution you'd like").
+vocabulary head, each sampled action owning its loss once (Megatron-LM pull
+request 7387, section "Summary"; issue "Shared-prefix training with context
+parallelism for exact agent trajectories", section "Describe the solution
+you'd like").
 
 Bounds: inputs are bf16, logits and row statistics fp32, so loss and lse
 are held to the lse bound of the attention path for bf16 inputs (max-abs

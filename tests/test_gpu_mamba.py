@@ -152,6 +152,64 @@ def test_ssm_rejects_unsupported_shapes():
         sp.conv_fwd(z(T, 6), z(6, 4), z(6), plan)
 
 
+def test_token_count_must_match_the_plan():
+    """A tensor with fewer or more rows than the plan is rejected before any
+    launch: by the binding (ValueError) and by the C ABI (INVALID_ARGUMENT,
+    outputs untouched)."""
+    import ctypes
+
+    import shared_prefix_tree_amd as sp
+    from shared_prefix_tree_amd import binding as b
+
+    dev = "cuda:0"
+    topo = tiny_tree()
+    T = topo.total_tokens
+    with torch.cuda.device(dev):
+        plan = sp.MambaPlan.from_topology(topo)
+    assert plan.num_tokens == T
+    z = lambda *s: torch.zeros(*s, dtype=torch.float32, device=dev)  # noqa: E731
+    for rows in (T - 1, T + 5):
+        with pytest.raises(ValueError, match="rows"):
+            sp.conv_fwd(z(rows, 8), z(8, 4), z(8), plan)
+        with pytest.raises(ValueError, match="rows"):
+            sp.conv_bwd(z(rows, 8), z(8, 4), z(rows, 8), plan)
+        with pytest.raises(ValueError, match="rows"):
+            sp.ssm_fwd(z(rows, 2, 64), z(rows, 2), z(2), z(rows, 1, 64), z(rows, 1, 64), z(2), plan)
+        with pytest.raises(ValueError, match="rows"):
+            sp.ssm_bwd(z(rows, 2, 64), z(rows, 2), z(2), z(rows, 1, 64), z(rows, 1, 64), z(2), z(rows, 2, 64),
+                       plan, z(64))
+    lib = sp.library()
+    x, w, bias = z(T, 8), z(8, 4), z(8)
+    y = torch.full((T, 8), 7.0, device=dev)
+    ws = torch.zeros(max(256, lib.tree_attn_conv_bwd_workspace_bytes(plan.handle, 8, 4)), dtype=torch.uint8,
+                     device=dev)
+    dx, dw, db = torch.full((T, 8), 7.0, device=dev), torch.full((8, 4), 7.0, device=dev), torch.full((8,), 7.0, device=dev)
+    for rows in (T - 1, T + 1, 0):
+        assert lib.tree_attn_conv_fwd(x.data_ptr(), w.data_ptr(), bias.data_ptr(), rows, 8, 4, plan.handle,
+                                      y.data_ptr(), None) == b.INVALID_ARGUMENT
+        assert "num_tokens" in lib.tree_attn_last_error().decode()
+        assert lib.tree_attn_conv_bwd(x.data_ptr(), w.data_ptr(), x.data_ptr(), rows, 8, 4, plan.handle,
+                                      dx.data_ptr(), dw.data_ptr(), db.data_ptr(), ws.data_ptr(), ws.numel(),
+                                      None) == b.INVALID_ARGUMENT
+    H, P, G, N = 2, 64, 1, 64
+    xs, dts, As, Bs, Ds = z(T, H, P), z(T, H), z(H), z(T, G, N), z(H)
+    ys = torch.full((T, H, P), 7.0, device=dev)
+    good = b.SsmShape(T, H, P, G, N)
+    st = torch.zeros(max(256, lib.tree_attn_ssm_states_bytes(plan.handle, ctypes.byref(good))), dtype=torch.uint8,
+                     device=dev)
+    wsf = torch.zeros(max(256, lib.tree_attn_ssm_workspace_bytes(plan.handle, ctypes.byref(good))),
+                      dtype=torch.uint8, device=dev)
+    for rows in (T - 1, T + 1):
+        bad = b.SsmShape(rows, H, P, G, N)
+        assert lib.tree_attn_ssm_fwd(xs.data_ptr(), dts.data_ptr(), As.data_ptr(), Bs.data_ptr(), Bs.data_ptr(),
+                                     Ds.data_ptr(), plan.handle, ctypes.byref(bad), ys.data_ptr(), st.data_ptr(),
+                                     st.numel(), wsf.data_ptr(), wsf.numel(), None) == b.INVALID_ARGUMENT
+        assert "num_tokens" in lib.tree_attn_last_error().decode()
+    torch.cuda.synchronize()
+    for t in (y, dx, dw, db, ys):
+        assert torch.all(t == 7.0)
+
+
 def test_ssm_at_the_benchmark_shape_on_two_groups():
     """The benchmark's mixer shape (128 heads x 64, 8 groups, state 128) on a
     ~1,000-token forest.  A group's heads read only that group's B and C, so

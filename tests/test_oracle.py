@@ -215,6 +215,34 @@ def test_visible_sets_match_reconstructed_sequences():
             assert oracle.position_in_sequence(topo, i) == len(vis[i]) - 1
 
 
+def test_ancestors_subtree_end_and_segment_pairs_from_children_lists():
+    # expectations from the children lists alone: the root-to-segment path of a
+    # DFS walk, the last token the walk emits under a segment, and the pairs of
+    # a segment's tokens counted from their reconstructed prefixes
+    for topo in small_forests(25, seed=12, max_tokens=70) + [tiny_tree(8, 4, 3)]:
+        roots, ch = children_lists(topo)
+        path_of, last_of = {}, {}
+
+        def walk(s, path):
+            path_of[s] = list(path)
+            last = int(topo.seg_start[s] + topo.seg_len[s])
+            for c in ch[s]:
+                last = max(last, walk(c, path + [s]))
+            last_of[s] = last
+            return last
+
+        for r in roots:
+            walk(r, [])
+        vis = visible_from_sequences(topo)
+        per_seg = oracle.segment_pairs(topo)
+        end = oracle.subtree_end(topo)
+        for s in range(topo.num_segments):
+            assert list(oracle.ancestors(np.asarray(topo.parent), s)) == path_of[s]
+            assert int(end[s]) == last_of[s]
+            toks = range(int(topo.seg_start[s]), int(topo.seg_start[s] + topo.seg_len[s]))
+            assert per_seg[s] == sum(len(vis[t]) for t in toks)
+
+
 def test_mask_form_subtree_interval():
     # j visible from i  <=>  j <= i and i < subtree_end(seg(j)), because a DFS
     # pre-order keeps every subtree contiguous.
