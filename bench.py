@@ -72,12 +72,28 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, topo, arrs, kv_heads=1, pair_fraction=1.0):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, topo, arrs, kv_heads=1, pair_fraction=0.5, reps=3):
     """Time the float64 oracle (unchanged) on a bounded sample of the same
     workload: the first ``kv_heads`` key/value heads (with their query
     heads) and the query segments, in index order, that hold about
-    ``pair_fraction`` of the pairs.  Credited with the sample's algorithmic
-    FLOPs (14 * D * heads * sampled pairs)."""
+    ``pair_fraction`` of the pairs.  The forward and the backward call are
+    timed separately, median of ``reps`` runs each; the oracle's backward
+    call recomputes the forward it needs, so the backward time is the
+    difference of the two medians.  Credited with the sample's algorithmic
+    FLOPs (4 D and 10 D per pair and query head)."""
+    import numpy as np
+
     import oracle
     from workloads import bf16_to_f32
 
@@ -91,26 +107,41 @@ def cpu_baseline(w, topo, arrs, kv_heads=1, pair_fraction=1.0):
             break
         segs.append(u)
         got += p
-    t0 = time.perf_counter()
-    oracle.backward(x["q"], x["k"], x["v"], x["dout"], topo, kv_heads=list(range(kv_heads)), segments=segs)
-    dt = time.perf_counter() - t0
-    flops = 14.0 * w.head_dim * G * kv_heads * got
+    heads = [h for g in range(kv_heads) for h in range(g * G, (g + 1) * G)]
+    t_fwd, t_call = [], []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.forward(x["q"], x["k"], x["v"], topo, heads=heads, segments=segs)
+        t_fwd.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        oracle.backward(x["q"], x["k"], x["v"], x["dout"], topo, kv_heads=list(range(kv_heads)), segments=segs)
+        t_call.append(time.perf_counter() - t0)
+    f_s, c_s = float(np.median(t_fwd)), float(np.median(t_call))
+    b_s = max(c_s - f_s, 1e-9)
+    unit = w.head_dim * G * kv_heads * got
     try:
         import torch
 
-        cores = torch.get_num_threads()
+        threads = torch.get_num_threads()
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        threads = len(os.sched_getaffinity(0))
     return {
-        "value": flops / dt / 1e12,
+        "value": 14.0 * unit / c_s / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(cores),
+        "cores": int(threads),
         "kind": "oracle",
-        "sample": f"float64 oracle forward+backward, key/value heads 0..{kv_heads - 1} "
-        f"({kv_heads * G} of {w.num_q_heads} query heads), query segments 0..{len(segs) - 1} "
-        f"of {topo.num_segments} ({got} of {total} pairs): {flops / 1e12:.3f} algorithmic TFLOP "
-        f"in {dt:.2f} s",
-        "seconds": round(dt, 3),
+        "sample": f"float64 oracle, key/value heads 0..{kv_heads - 1} ({kv_heads * G} of {w.num_q_heads} query "
+        f"heads), query segments 0..{len(segs) - 1} of {topo.num_segments} ({got} of {total} pairs); forward "
+        f"and backward call timed separately, median of {reps}; value = 14 D pairs / backward call (which "
+        f"recomputes the forward)",
+        "fwd_s": round(f_s, 3),
+        "bwd_s": round(b_s, 3),
+        "fwd_tflops": round(4.0 * unit / f_s / 1e12, 5),
+        "bwd_tflops": round(10.0 * unit / b_s / 1e12, 5),
+        "dtype": "f64",
+        "cpu_model": _cpu_model(),
+        "os_cpu_count": os.cpu_count(),
+        "torch_threads": int(threads),
     }
 
 
@@ -469,9 +500,12 @@ def main():
         query_run_shares(args, sp, w, topo, t, out, lse, dq, dk, dv, ws, pairs)
         return
 
+    stream = torch.cuda.current_stream()
+
     def step(events=None):
+        # the plan's tables are uploaded by a copy ordered on the step's stream
         t0 = time.perf_counter()
-        plan = sp.Plan.from_topology(topo)
+        plan = sp.Plan.from_topology(topo, stream=stream)
         plan_host_s.append(time.perf_counter() - t0)
         if events:
             events[0].record()
@@ -490,9 +524,9 @@ def main():
         sp.Plan.from_topology(topo, device=False)
         build_s.append(time.perf_counter() - t0)
     log(f"T={T} S={topo.num_segments} Hq={Hq} Hkv={Hkv} D={D} pairs={pairs}; warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
+    warm = [step() for _ in range(args.warmup)]
     torch.cuda.synchronize()
+    warm.clear()  # (plans are destroyed only once their kernels are done)
     plan_host_s.clear()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     keep = []
@@ -554,9 +588,9 @@ def main():
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
         "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2) if w.backward else None,
         "kernel_tflops_fwd_bwd": round(total / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2),
-        # the plan's host build alone, and the whole plan call inside a step: its
-        # upload is a synchronous copy, so the call also waits for the previous
-        # step's kernels (the GPU is idle only for the copy itself)
+        # the plan's host build alone, and the whole plan call inside a step
+        # (build, pinned staging, device allocation, and a copy queued on the
+        # step's stream: the host does not wait for the previous step's kernels)
         "plan_build_ms": round(1e3 * float(np.median(build_s)), 4),
         "plan_call_ms": round(1e3 * float(np.mean(plan_host_s)), 4),
         "kernels": kernels,

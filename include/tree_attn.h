@@ -111,6 +111,18 @@ int tree_attn_plan(const int32_t* parent, const int32_t* seg_start, const int32_
                    int32_t num_segments, tree_attn_plan_t* out);
 
 /*
+ * tree_attn_plan with a stream-ordered upload: the tables are staged in
+ * pinned host memory (kept by the plan until tree_attn_plan_destroy) and
+ * copied with one asynchronous copy on `stream` (a hipStream_t, NULL = the
+ * default stream), so the call never waits for kernels already queued on
+ * the device.  Kernels on `stream` may use the plan right away; work on
+ * another stream must first be ordered after the copy (an event).  Same
+ * validation, ownership and errors as tree_attn_plan.
+ */
+int tree_attn_plan_async(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                         int32_t num_segments, void* stream, tree_attn_plan_t* out);
+
+/*
  * A plan for one query run: the queries are the tokens [q_begin, q_end)
  * (0 <= q_begin < q_end <= T), the keys and values still every token.  This
  * is one context-parallel rank's share when the run is the rank's local
@@ -376,16 +388,17 @@ int tree_attn_bwd(const void* q, const void* k, const void* v, const void* out, 
  * be called on its own (for example to time it).  They share the workspace:
  *   tree_attn_bwd_rowstat  -delta[h,i] = -sum_d dout[i,h,d] * out[i,h,d] and
  *                          -lse[h,i] * log2(e) into the workspace (two float32
- *                          [Hq, T] arrays, stored negated), and zeroes its
- *                          work-item counters (the other two stages leave
- *                          them zeroed when they finish, so they may be
- *                          repeated; a new workspace needs this stage first);
+ *                          [Hq, T] arrays, stored negated), and zeroes the
+ *                          work-item counters of the other two stages;
  *   tree_attn_bwd_dkdv     dk, dv: for each key, the contributions of every
  *                          query that sees it, i.e. of every branch below a
  *                          shared prefix (draft "feat(hybrid): add opt-in
  *                          shared-prefix attention and Mamba execution",
  *                          intro); needs the rowstat workspace;
  *   tree_attn_bwd_dq       dq; needs the rowstat workspace.
+ * Called on its own, tree_attn_bwd_dkdv or _dq first zeroes its own
+ * work-item counters with a one-workgroup launch, so it needs nothing from
+ * the workspace but the row statistics.
  * Arguments, checks and errors are those of tree_attn_bwd.
  */
 int tree_attn_bwd_rowstat(const void* out, const float* lse, const void* dout, tree_attn_plan_t plan,

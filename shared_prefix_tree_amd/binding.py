@@ -37,6 +37,7 @@ SYMBOLS = (
     "tree_attn_plan_query_run",
     "tree_attn_plan_query_run_host",
     "tree_attn_plan_host",
+    "tree_attn_plan_async",
     "tree_attn_plan_destroy",
     "tree_attn_plan_info",
     "tree_attn_plan_export",
@@ -177,6 +178,7 @@ def library():
         getattr(lib, name).argtypes = [i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.POINTER(vp)]
     lib.tree_attn_plan_host.argtypes = [i32p, i32p, i32p, ctypes.c_int32, ctypes.POINTER(vp)]
+    lib.tree_attn_plan_async.argtypes = [i32p, i32p, i32p, ctypes.c_int32, vp, ctypes.POINTER(vp)]
     lib.tree_attn_plan_destroy.argtypes = [vp]
     lib.tree_attn_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     lib.tree_attn_plan_export.argtypes = [vp, ctypes.c_int32, i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
@@ -259,9 +261,12 @@ class Plan:
     ``torch.cuda.device(...)`` to choose it); ``device=False`` builds a
     host-only plan for inspection.  ``query_run=(q_begin, q_end)`` restricts
     the queries to those tokens (``tree_attn_plan_query_run[_host]``).
+    ``stream`` (a torch stream, whole-token plans only): upload the tables
+    with a copy ordered on that stream (``tree_attn_plan_async``) instead of
+    a synchronous one.
     """
 
-    def __init__(self, parent, seg_start, seg_len, device=True, query_run=None):
+    def __init__(self, parent, seg_start, seg_len, device=True, query_run=None, stream=None):
         lib = library()
         self._handle = None
         p, pp = _i32(parent)
@@ -274,6 +279,9 @@ class Plan:
             qb, qe = (int(x) for x in query_run)
             fn = lib.tree_attn_plan_query_run if device else lib.tree_attn_plan_query_run_host
             _check(fn(pp, sp, np_, ctypes.c_int32(len(p)), ctypes.c_int32(qb), ctypes.c_int32(qe), ctypes.byref(h)))
+        elif stream is not None and device:
+            _check(lib.tree_attn_plan_async(pp, sp, np_, ctypes.c_int32(len(p)), ctypes.c_void_p(stream.cuda_stream),
+                                            ctypes.byref(h)))
         else:
             fn = lib.tree_attn_plan if device else lib.tree_attn_plan_host
             _check(fn(pp, sp, np_, ctypes.c_int32(len(p)), ctypes.byref(h)))
@@ -285,8 +293,8 @@ class Plan:
             self.device_index = torch.cuda.current_device()
 
     @classmethod
-    def from_topology(cls, topo, device=True, query_run=None):
-        return cls(topo.parent, topo.seg_start, topo.seg_len, device=device, query_run=query_run)
+    def from_topology(cls, topo, device=True, query_run=None, stream=None):
+        return cls(topo.parent, topo.seg_start, topo.seg_len, device=device, query_run=query_run, stream=stream)
 
     @property
     def handle(self):

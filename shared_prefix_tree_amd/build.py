@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "lib", "libtree_attn.so")
-SOURCES = ["plan.cpp", "fragments.cpp", "api.cpp", "fwd.hip", "bwd.hip", "edge_loss.hip", "mamba_tree.hip"]
+SOURCES = ["plan.cpp", "fragments.cpp", "mamba_plan.cpp", "edge_plan.cpp", "api.cpp", "fwd.hip", "bwd.hip", "edge_loss.hip", "mamba_tree.hip"]
 LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -28,6 +28,7 @@ template <typename T, int D>
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D, int HG>
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_reset_counters(ItemCounters* c, int n, hipStream_t stream);
 
 namespace {
 
@@ -63,7 +64,8 @@ int guard_host(const char* fn, const std::function<int()>& body) noexcept {
 
 struct DevicePlan {
   int device = -1;
-  void* block = nullptr;  // one allocation holding every table below
+  void* block = nullptr;   // one allocation holding every table below
+  void* staged = nullptr;  // pinned host copy of `block` (stream-ordered uploads only)
   int32_t* span_ptr = nullptr;
   Span* spans = nullptr;
   QTile* qtiles[kNumQTileSizes] = {};
@@ -93,6 +95,7 @@ void free_device(DevicePlan& d) {
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(d.device);
   (void)hipFree(d.block);
+  if (d.staged) (void)hipHostFree(d.staged);
   if (prev >= 0) (void)hipSetDevice(prev);
   d = DevicePlan{};
 }
@@ -100,8 +103,10 @@ void free_device(DevicePlan& d) {
 size_t align16(size_t n) { return (n + 15) & ~size_t(15); }
 
 // Packs every table into one host staging buffer and uploads it with one
-// allocation and one synchronous copy.
-hipError_t upload_plan(const HostPlan& h, DevicePlan& d) {
+// allocation and one copy: synchronous (pageable staging) when `stream` is
+// nullptr, otherwise ordered on *stream from pinned staging that the plan
+// keeps until it is destroyed, so the host never waits for the device.
+hipError_t upload_plan(const HostPlan& h, DevicePlan& d, const hipStream_t* stream) {
   struct Part {
     const void* src;
     size_t bytes;
@@ -117,15 +122,26 @@ hipError_t upload_plan(const HostPlan& h, DevicePlan& d) {
     parts[4 + t] = {h.qtiles[t].data(), h.qtiles[t].size() * sizeof(QTile), reinterpret_cast<void**>(&d.qtiles[t])};
   size_t total = 0;
   for (const Part& p : parts) total += align16(p.bytes);
-  std::vector<unsigned char> stage(total, 0);
+  std::vector<unsigned char> pageable;
+  unsigned char* stage = nullptr;
+  if (stream) {
+    hipError_t e = hipHostMalloc(&d.staged, std::max<size_t>(total, 16), hipHostMallocDefault);
+    if (e != hipSuccess) return e;
+    stage = static_cast<unsigned char*>(d.staged);
+  } else {
+    pageable.resize(total);
+    stage = pageable.data();
+  }
+  std::memset(stage, 0, total);
   size_t off = 0;
   for (const Part& p : parts) {
-    if (p.bytes) std::memcpy(stage.data() + off, p.src, p.bytes);
+    if (p.bytes) std::memcpy(stage + off, p.src, p.bytes);
     off += align16(p.bytes);
   }
   hipError_t e = hipMalloc(&d.block, std::max<size_t>(total, 16));
   if (e != hipSuccess) return e;
-  e = hipMemcpy(d.block, stage.data(), total, hipMemcpyHostToDevice);
+  e = stream ? hipMemcpyAsync(d.block, stage, total, hipMemcpyHostToDevice, *stream)
+             : hipMemcpy(d.block, stage, total, hipMemcpyHostToDevice);
   off = 0;
   for (const Part& p : parts) {
     *p.dst = static_cast<unsigned char*>(d.block) + off;
@@ -135,7 +151,8 @@ hipError_t upload_plan(const HostPlan& h, DevicePlan& d) {
 }
 
 int make_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len, int32_t num_segments,
-              int32_t q_begin, int32_t q_end, tree_attn_plan_t* out, bool device) {
+              int32_t q_begin, int32_t q_end, tree_attn_plan_t* out, bool device,
+              const hipStream_t* stream = nullptr) {
   if (!out) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan: out is NULL");
   *out = nullptr;
   return guard_host("tree_attn_plan", [&]() -> int {
@@ -145,7 +162,7 @@ int make_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* se
       return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan: " + err);
     if (device) {
       hipError_t e = hipGetDevice(&p->dev.device);
-      if (e == hipSuccess) e = upload_plan(p->host, p->dev);
+      if (e == hipSuccess) e = upload_plan(p->host, p->dev, stream);
       if (e != hipSuccess) {
         free_device(p->dev);
         return hip_fail("tree_attn_plan: device upload", e);
@@ -230,6 +247,12 @@ extern "C" {
 int tree_attn_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len, int32_t num_segments,
                    tree_attn_plan_t* out) {
   return make_plan(parent, seg_start, seg_len, num_segments, 0, -1, out, true);
+}
+
+int tree_attn_plan_async(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                         int32_t num_segments, void* stream, tree_attn_plan_t* out) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return make_plan(parent, seg_start, seg_len, num_segments, 0, -1, out, true, &s);
 }
 
 int tree_attn_plan_query_run(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
@@ -481,7 +504,11 @@ int prep_bwd(const char* fn, const void* q, const void* k, const void* v, const 
 template <typename T, int D>
 hipError_t launch_bwd_stages(const BwdArgs& a, int hg, int stages, hipStream_t s) {
   hipError_t e = hipSuccess;
-  if (stages & kRowStat) e = launch_bwd_rowstat<T, D>(a, s);
+  // the row-statistics stage zeroes both stages' counters; without it, a
+  // stage zeroes its own first (a fresh workspace holds arbitrary bytes)
+  if (!(stages & kRowStat) && (stages & kDkDv)) e = launch_reset_counters(&a.counters[0], 1, s);
+  if (e == hipSuccess && !(stages & kRowStat) && (stages & kDq)) e = launch_reset_counters(&a.counters[1], 1, s);
+  if (e == hipSuccess && (stages & kRowStat)) e = launch_bwd_rowstat<T, D>(a, s);
   if (e == hipSuccess && (stages & kDkDv)) e = launch_bwd_dkdv<T, D>(a, s);
   if (e == hipSuccess && (stages & kDq))
     e = hg == 4 ? launch_bwd_dq<T, D, 4>(a, s) : hg == 2 ? launch_bwd_dq<T, D, 2>(a, s) : launch_bwd_dq<T, D, 1>(a, s);

@@ -937,6 +937,19 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // launchers (one per stage; tree_attn_bwd runs all three in order)
 
+// Zeroes n consecutive work-item counter blocks: a dK/dV or dQ stage called
+// on its own (without the row-statistics stage right before it) starts from
+// zeroed counters whatever the workspace held.
+__global__ __launch_bounds__(64) void tree_attn_reset_counters_kernel(ItemCounters* __restrict__ c, int n) {
+  const int words = n * int(sizeof(ItemCounters) / 4);
+  for (int i = threadIdx.x; i < words; i += 64) reinterpret_cast<unsigned*>(c)[i] = 0u;
+}
+
+hipError_t launch_reset_counters(ItemCounters* c, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(tree_attn_reset_counters_kernel, dim3(1), dim3(64), 0, stream, c, n);
+  return hipGetLastError();
+}
+
 // one 512-thread workgroup fits a CU (LDS), so the item-taking kernels run
 // as many workgroups as the device has CUs (fewer for fewer items)
 static unsigned persistent_grid(unsigned n_items) {

@@ -38,6 +38,7 @@
 #include <vector>
 
 #include "../../include/tree_attn.h"
+#include "edge_plan.hpp"
 
 namespace tree_attn {
 int report_error(int code, const std::string& msg);
@@ -387,25 +388,14 @@ int tree_attn_edges(const int32_t* edge_src, const int32_t* edge_tgt, int32_t nu
                     int32_t vocab, tree_attn_edges_t* out) {
   if (!out) return report_error(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_edges: out is NULL");
   *out = nullptr;
-  if (num_edges < 1 || num_tokens < 1 || vocab < 1 || !edge_src || !edge_tgt)
-    return report_error(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_edges: need >= 1 edge, token and vocabulary row");
-  for (int32_t e = 0; e < num_edges; ++e) {
-    if (edge_src[e] < 0 || edge_src[e] >= num_tokens || edge_tgt[e] < 0 || edge_tgt[e] >= vocab)
-      return report_error(TREE_ATTN_INVALID_ARGUMENT,
-                          "tree_attn_edges: edge " + std::to_string(e) + " has source " +
-                              std::to_string(edge_src[e]) + " / sampled token " + std::to_string(edge_tgt[e]) +
-                              " outside [0, " + std::to_string(num_tokens) + ") / [0, " + std::to_string(vocab) +
-                              ")");
-  }
   if (int64_t(num_edges) * kVocabChunk >= (int64_t(1) << 31))
     return report_error(TREE_ATTN_UNSUPPORTED, "tree_attn_edges: more than 262,143 edges");
   return tree_attn::guard_host("tree_attn_edges", [&]() -> int {
     // CSR by source token, edges ascending within a token
-    std::vector<int32_t> row_ptr(size_t(num_tokens) + 1, 0), ids(num_edges);
-    for (int32_t e = 0; e < num_edges; ++e) ++row_ptr[size_t(edge_src[e]) + 1];
-    for (int32_t t = 0; t < num_tokens; ++t) row_ptr[t + 1] += row_ptr[t];
-    std::vector<int32_t> fill(row_ptr.begin(), row_ptr.end() - 1);
-    for (int32_t e = 0; e < num_edges; ++e) ids[fill[edge_src[e]]++] = e;
+    std::vector<int32_t> row_ptr, ids;
+    std::string err;
+    if (!tree_attn::build_edge_csr(edge_src, edge_tgt, num_edges, num_tokens, vocab, row_ptr, ids, err))
+      return report_error(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_edges: " + err);
 
     auto r = std::make_unique<tree_attn_edges_s>();
     r->E = num_edges;

@@ -43,6 +43,7 @@
 #include <vector>
 
 #include "../../include/tree_attn.h"
+#include "mamba_plan.hpp"
 #include "plan.hpp"
 
 namespace tree_attn {
@@ -54,22 +55,15 @@ using tree_attn::report_error;
 
 namespace {
 
-constexpr int kUnit = 128;         // tokens per scan unit
-constexpr int kConvMaxWidth = 4;   // convolution widths 1..4
-constexpr int kHalo = kConvMaxWidth - 1;
+constexpr int kUnit = tree_attn::kMambaUnit;  // tokens per scan unit
+constexpr int kConvMaxWidth = tree_attn::kConvMaxWidth;
+constexpr int kHalo = tree_attn::kConvHalo;
 constexpr int kHeadDim = 64;       // P
 
 }  // namespace
 
-struct tree_attn_mamba_plan_s {
+struct tree_attn_mamba_plan_s : tree_attn::MambaTables {
   int device = -1;  // -1: host-only plan
-  int32_t T = 0, S = 0, U = 0, max_depth = 0;
-  std::vector<int32_t> prev;                    // [T]
-  std::vector<int32_t> halo;                    // [T][kHalo]: prev^1 .. prev^kHalo (-1: none)
-  std::vector<int32_t> csucc_ptr, csucc;        // token j -> entries 4 i + k with prev^k(i) = j, i != j + k, k = 1..kHalo
-  std::vector<int32_t> unit_start, unit_len, unit_pred;  // [U]
-  std::vector<int32_t> usucc_ptr, usucc;        // unit u -> units v with pred(v) = u, ascending
-  std::vector<int32_t> uchain;                  // 1: u's only successor is u + 1
   void* block = nullptr;
   const int32_t *d_halo = nullptr, *d_csucc_ptr = nullptr, *d_csucc = nullptr;
   const int32_t *d_unit_start = nullptr, *d_unit_len = nullptr, *d_unit_pred = nullptr;
@@ -77,64 +71,6 @@ struct tree_attn_mamba_plan_s {
 };
 
 namespace {
-
-bool build_mamba_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len, int32_t S,
-                      tree_attn_mamba_plan_s& m, std::string& err) {
-  tree_attn::HostPlan hp;  // validation of the DFS forest (same rules as the attention plan)
-  if (!tree_attn::build_host_plan(parent, seg_start, seg_len, S, 0, -1, hp, err)) return false;
-  const int32_t T = hp.T;
-  m.T = T;
-  m.S = S;
-  m.max_depth = hp.max_depth;
-  m.prev.resize(T);
-  for (int32_t i = 0; i < T; ++i) m.prev[i] = i - 1;
-  for (int32_t s = 0; s < S; ++s)
-    m.prev[seg_start[s]] = parent[s] < 0 ? -1 : seg_start[parent[s]] + seg_len[parent[s]] - 1;
-  m.halo.assign(size_t(T) * kHalo, -1);
-  std::vector<int32_t> count(size_t(T) + 1, 0);
-  for (int32_t i = 0; i < T; ++i) {
-    int32_t j = i;
-    for (int k = 1; k <= kHalo; ++k) {
-      j = j < 0 ? -1 : m.prev[j];
-      m.halo[size_t(i) * kHalo + k - 1] = j;
-      if (j >= 0 && j != i - k) ++count[size_t(j) + 1];  // (successors k tokens ahead are read from the halo)
-    }
-  }
-  for (int32_t t = 0; t < T; ++t) count[t + 1] += count[t];
-  m.csucc_ptr = count;
-  m.csucc.resize(count[T]);
-  std::vector<int32_t> fill(count.begin(), count.end() - 1);
-  // entries of a token in (k, i) order: for each k, successors ascending
-  for (int k = 1; k <= kHalo; ++k)
-    for (int32_t i = 0; i < T; ++i) {
-      const int32_t j = m.halo[size_t(i) * kHalo + k - 1];
-      if (j >= 0 && j != i - k) m.csucc[fill[j]++] = 4 * i + k;
-    }
-  // units
-  std::vector<int32_t> last_unit(S, -1);
-  for (int32_t s = 0; s < S; ++s) {
-    for (int32_t off = 0; off < seg_len[s]; off += kUnit) {
-      const int32_t u = int32_t(m.unit_start.size());
-      m.unit_start.push_back(seg_start[s] + off);
-      m.unit_len.push_back(std::min(kUnit, seg_len[s] - off));
-      m.unit_pred.push_back(off > 0 ? u - 1 : parent[s] < 0 ? -1 : last_unit[parent[s]]);
-      last_unit[s] = u;
-    }
-  }
-  m.U = int32_t(m.unit_start.size());
-  m.usucc_ptr.assign(size_t(m.U) + 1, 0);
-  for (int32_t u = 0; u < m.U; ++u)
-    if (m.unit_pred[u] >= 0) ++m.usucc_ptr[size_t(m.unit_pred[u]) + 1];
-  for (int32_t u = 0; u < m.U; ++u) m.usucc_ptr[u + 1] += m.usucc_ptr[u];
-  m.usucc.resize(m.usucc_ptr[m.U]);
-  std::vector<int32_t> uf(m.usucc_ptr.begin(), m.usucc_ptr.end() - 1);
-  for (int32_t u = 0; u < m.U; ++u)
-    if (m.unit_pred[u] >= 0) m.usucc[uf[m.unit_pred[u]]++] = u;
-  m.uchain.assign(m.U, 0);
-  for (int32_t u = 0; u < m.U; ++u)
-    m.uchain[u] = (m.usucc_ptr[u + 1] - m.usucc_ptr[u] == 1 && m.usucc[m.usucc_ptr[u]] == u + 1) ? 1 : 0;
-  return true;
-}
 
 hipError_t upload_mamba_plan(tree_attn_mamba_plan_s& m) {
   const std::vector<int32_t>* parts[] = {&m.halo,     &m.csucc_ptr, &m.csucc,     &m.unit_start, &m.unit_len,
@@ -1362,7 +1298,7 @@ static int mamba_plan_impl(const int32_t* parent, const int32_t* seg_start, cons
   return tree_attn::guard_host(fn, [&]() -> int {
     auto m = std::make_unique<tree_attn_mamba_plan_s>();
     std::string err;
-    if (!build_mamba_plan(parent, seg_start, seg_len, num_segments, *m, err))
+    if (!tree_attn::build_mamba_tables(parent, seg_start, seg_len, num_segments, *m, err))
       return report_error(TREE_ATTN_INVALID_ARGUMENT, std::string(fn) + ": " + err);
     if (upload) {
       if (hipError_t e = upload_mamba_plan(*m); e != hipSuccess) {

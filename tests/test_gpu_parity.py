@@ -22,7 +22,7 @@ import pytest
 
 import oracle
 from tests.parity_util import TOL, log, oracle_inputs, rel_l2, tensor_error, to_host, to_torch
-from workloads import WORKLOADS, Topology, f32_to_bf16, random_forest, tiny_tree
+from workloads import WORKLOADS, Topology, comb, f32_to_bf16, long_chain, random_forest, tiny_tree
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -122,6 +122,70 @@ EDGE = [
 def test_edge_topologies(label, topo, dtype, D):
     rng = np.random.default_rng(sum(map(ord, label)))
     compare_full(topo, make_inputs(rng, topo.total_tokens, 4, 1, D, dtype), dtype, label=f"{label}/{dtype}/D{D}")
+
+
+COMBS = [
+    # a 64-key step crosses 32 two-token spans; the deepest path has 100 spans
+    ("comb_2_1_x100", comb(100, spine_len=2, leaf_len=1, tail_len=70)),
+    # spans of 3 tokens separated by 5-token leaves, a 200-token last segment
+    ("comb_3_5_x60", comb(60, spine_len=3, leaf_len=5, tail_len=200)),
+    # exactly the 256-span limit: 255 one-token spine segments and a tail
+    ("comb_1_1_x255_tail", comb(255, spine_len=1, leaf_len=1, tail_len=40)),
+]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("label,topo", COMBS, ids=[c[0] for c in COMBS])
+def test_comb_topologies(label, topo, dtype, D):
+    """Ancestor paths that split into dozens to 256 separate short spans: the
+    forward and dQ walks look up most rows of a step span by span."""
+    sp = lib()
+    plan = sp.Plan.from_topology(topo, device=False)
+    spans = plan.export(sp.binding.EXPORT_SPAN_PTR)
+    log(f"{label}: most spans on one path {int(np.diff(spans).max())}")
+    assert int(np.diff(spans).max()) <= 256
+    rng = np.random.default_rng(sum(map(ord, label)))
+    compare_full(topo, make_inputs(rng, topo.total_tokens, 4, 2, D, dtype), dtype, label=f"{label}/{dtype}")
+
+
+def test_257_spans_are_rejected_before_any_launch():
+    """One span past the limit: UNSUPPORTED from the forward and backward
+    entry points, nothing written."""
+    import ctypes
+
+    import shared_prefix_tree_amd.binding as b
+
+    sp = lib()
+    topo = comb(256, spine_len=1, leaf_len=1, tail_len=8)  # deepest path: 257 spans
+    plan = sp.Plan.from_topology(topo)
+    assert int(np.diff(plan.export(b.EXPORT_SPAN_PTR)).max()) == 257
+    T = topo.total_tokens
+    q = torch.randn(T, 4, 128, device="cuda").bfloat16()
+    k = torch.randn(T, 2, 128, device="cuda").bfloat16()
+    out = torch.full((T, 4, 128), 7.0, device="cuda").bfloat16()
+    lse = torch.full((4, T), 7.0, device="cuda")
+    lib_ = sp.library()
+    shape = b.Shape(T, 4, 2, 128, b.BF16, 0.0)
+    assert lib_.tree_attn_fwd(q.data_ptr(), k.data_ptr(), k.data_ptr(), plan.handle, ctypes.byref(shape),
+                              out.data_ptr(), lse.data_ptr(), None) == b.UNSUPPORTED
+    assert "257" in lib_.tree_attn_last_error().decode()
+    ws = torch.zeros(max(256, sp.bwd_workspace_bytes(plan, q, k)), dtype=torch.uint8, device="cuda")
+    with pytest.raises(sp.TreeAttnError) as e:
+        sp.tree_attn_bwd(q, k, k, out, lse, q, plan, workspace=ws)
+    assert e.value.code == b.UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 7.0) and torch.all(lse == 7.0)
+
+
+def test_long_chain_structure_full_tensors():
+    """The long-chain workload's structure (40 trunk segments, a side leaf
+    after every 5th) scaled to 16,384 tokens: every element of dk and dv,
+    including the trunk root's keys, whose query ranges run to the end of
+    the chain (16k queries), against the oracle."""
+    topo = long_chain(np.random.default_rng([1003, 0]), total=16384, side_lo=64, side_hi=256)
+    rng = np.random.default_rng(1003)
+    compare_full(topo, make_inputs(rng, topo.total_tokens, 8, 2, 128, "bf16", std=0.5), "bf16",
+                 label="long_chain_16384")
 
 
 def test_large_scores_stay_finite():
@@ -340,4 +404,75 @@ def test_repeated_stages_reuse_their_work_counters():
                                      ws.data_ptr(), wsb, stream) == b.OK
         torch.cuda.synchronize()
         for a, b_ in zip(ref, (dq, dk, dv)):
+            assert torch.equal(a, b_)
+
+
+def test_stages_on_a_fresh_workspace_start_from_zeroed_counters():
+    """tree_attn_bwd_dkdv and _dq called on a workspace whose counter bytes
+    were never zeroed (only the row statistics copied in) still compute every
+    tile: each stage zeroes its own counters before it starts."""
+    import ctypes
+
+    import shared_prefix_tree_amd.binding as b
+
+    sp = lib()
+    rng = np.random.default_rng(43)
+    topo = random_forest(rng, max_tokens=900, max_len=200, max_depth=4)
+    arrs = make_inputs(rng, topo.total_tokens, 8, 2, 128, "bf16")
+    t = {k: to_torch(v, "bf16", "cuda:0") for k, v in arrs.items()}
+    plan = sp.Plan.from_topology(topo)
+    out, lse = sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan)
+    ref = sp.tree_attn_bwd(t["q"], t["k"], t["v"], out, lse, t["dout"], plan)
+    nbytes = sp.bwd_workspace_bytes(plan, t["q"], t["k"])
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    lib_ = b.library()
+    shape = b._shape(t["q"], t["k"], 0.0)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    wsb = ctypes.c_size_t(nbytes)
+    assert lib_.tree_attn_bwd_rowstat(out.data_ptr(), lse.data_ptr(), t["dout"].data_ptr(), plan.handle,
+                                      ctypes.byref(shape), ws.data_ptr(), wsb, stream) == b.OK
+    counters = 2 * 64  # two blocks of 16 unsigned counters at the end of the workspace
+    for fill in (0x5A, 0xFF, 0x01):
+        fresh = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda:0")
+        fresh[: nbytes - counters].copy_(ws[: nbytes - counters])
+        dq, dk, dv = (torch.full_like(t[n], 7.0) for n in ("q", "k", "v"))
+        assert lib_.tree_attn_bwd_dkdv(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), lse.data_ptr(),
+                                       t["dout"].data_ptr(), plan.handle, ctypes.byref(shape), dk.data_ptr(),
+                                       dv.data_ptr(), fresh.data_ptr(), wsb, stream) == b.OK
+        assert lib_.tree_attn_bwd_dq(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), lse.data_ptr(),
+                                     t["dout"].data_ptr(), plan.handle, ctypes.byref(shape), dq.data_ptr(),
+                                     fresh.data_ptr(), wsb, stream) == b.OK
+        torch.cuda.synchronize()
+        log(f"fresh workspace filled with {fill:#x}: stage-only dK/dV and dQ")
+        for a, b_ in zip(ref, (dq, dk, dv)):
+            assert torch.equal(a, b_)
+
+
+def test_stream_ordered_plan_upload_matches_the_synchronous_one():
+    """tree_attn_plan_async uploads the tables with a copy on the caller's
+    stream; kernels queued behind it on that stream give bitwise the results
+    of a plan uploaded synchronously, also when the stream is busy."""
+    sp = lib()
+    rng = np.random.default_rng(44)
+    topo = random_forest(rng, max_tokens=1500, max_len=300, max_depth=5)
+    arrs = make_inputs(rng, topo.total_tokens, 8, 2, 128, "bf16")
+    t = {k: to_torch(v, "bf16", "cuda:0") for k, v in arrs.items()}
+    ref_plan = sp.Plan.from_topology(topo)
+    out0, lse0 = sp.tree_attn_fwd(t["q"], t["k"], t["v"], ref_plan)
+    g0 = sp.tree_attn_bwd(t["q"], t["k"], t["v"], out0, lse0, t["dout"], ref_plan)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        busy = torch.randn(2048, 2048, device="cuda:0")
+        for _ in range(4):
+            busy = busy @ busy.T * 1e-3  # queue work ahead of the upload
+        plans = [sp.Plan.from_topology(topo, stream=s) for _ in range(3)]
+        results = []
+        for p in plans:
+            out, lse = sp.tree_attn_fwd(t["q"], t["k"], t["v"], p)
+            results.append((out, lse, *sp.tree_attn_bwd(t["q"], t["k"], t["v"], out, lse, t["dout"], p)))
+    torch.cuda.synchronize()
+    assert plans[0].info()["pairs"] == ref_plan.info()["pairs"]
+    for r in results:
+        for a, b_ in zip((out0, lse0, *g0), r):
             assert torch.equal(a, b_)

@@ -258,6 +258,25 @@ def fragment_forest(rng, fragments=4, capacity=32768, **kw) -> Topology:
     return topo
 
 
+def comb(teeth, spine_len=2, leaf_len=1, tail_len=0) -> Topology:
+    """A spine of ``teeth`` segments, each spine segment's first child a leaf
+    of ``leaf_len`` tokens and its second the next spine segment.  In DFS
+    order every spine segment is separated from its parent by that leaf, so
+    the deepest spine segment's ancestor path splits into ``teeth`` separate
+    token spans (``tail_len`` > 0 adds a last spine segment of that length,
+    one more span)."""
+    nodes = []
+    parent = -1
+    for _ in range(teeth):
+        me = len(nodes)
+        nodes.append((parent, spine_len))
+        nodes.append((me, leaf_len))
+        parent = me
+    if tail_len:
+        nodes.append((parent, tail_len))
+    return _from_dfs_list(nodes)
+
+
 def random_forest(rng, max_tokens=64, max_len=9, max_depth=4, p_new_root=0.15) -> Topology:
     """Small random DFS forest for brute-force tests: segment lengths
     uniform{1..max_len}, node depth <= max_depth, total <= max_tokens."""
