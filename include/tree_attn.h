@@ -410,6 +410,21 @@ int tree_attn_bwd_dq(const void* q, const void* k, const void* v, const float* l
                      tree_attn_plan_t plan, const tree_attn_shape* shape, void* dq, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * tree_attn_bwd without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The workspace is a fixed array
+ * of 64 MiB + 256 bytes that the library holds on each GPU it runs on until
+ * the process ends, so shapes with num_q_heads * total_tokens above
+ * 8,388,608 are UNSUPPORTED (before any launch).  The call allocates
+ * nothing.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * ordered by the caller.  Outputs, checks and determinism as tree_attn_bwd.
+ */
+int tree_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                          const void* dout, tree_attn_plan_t plan, const tree_attn_shape* shape, void* dq, void* dk,
+                          void* dv, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* tree_attn_last_error(void);
 

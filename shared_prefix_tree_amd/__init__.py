@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     ssm_fwd,
     ssm_states_bytes,
     tree_attn_bwd,
+    tree_attn_bwd_noalloc,
     tree_attn_bwd_stages,
     tree_attn_fwd,
 )

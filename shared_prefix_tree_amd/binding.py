@@ -47,6 +47,7 @@ SYMBOLS = (
     "tree_attn_bwd_rowstat",
     "tree_attn_bwd_dkdv",
     "tree_attn_bwd_dq",
+    "tree_attn_bwd_noalloc",
     "tree_attn_last_error",
     "tree_attn_fragment",
     "tree_attn_fragments_destroy",
@@ -189,6 +190,7 @@ def library():
     lib.tree_attn_bwd_rowstat.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), vp, ctypes.c_size_t, vp]
     lib.tree_attn_bwd_dkdv.argtypes = [vp] * 6 + [ctypes.POINTER(Shape), vp, vp, vp, ctypes.c_size_t, vp]
     lib.tree_attn_bwd_dq.argtypes = [vp] * 6 + [ctypes.POINTER(Shape), vp, vp, ctypes.c_size_t, vp]
+    lib.tree_attn_bwd_noalloc.argtypes = [vp] * 6 + [vp, ctypes.POINTER(Shape)] + [vp] * 4
     lib.tree_attn_last_error.restype = ctypes.c_char_p
     lib.tree_attn_fragment.argtypes = [i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(vp)]
     lib.tree_attn_fragments_destroy.argtypes = [vp]
@@ -747,6 +749,28 @@ def tree_attn_bwd(q, k, v, out, lse, dout, plan: Plan, softmax_scale=0.0, dq=Non
                 _stream_ptr(dev, stream),
             )
         )
+    return dq, dk, dv
+
+
+def tree_attn_bwd_noalloc(q, k, v, out, lse, dout, plan: Plan, dq, dk, dv, softmax_scale=0.0, stream=None):
+    """Backward pass into caller-given dq, dk, dv with the library's fixed
+    device scratch as workspace (``tree_attn_bwd_noalloc``): no device memory
+    is allocated.  Calls that overlap on one GPU race."""
+    import torch
+
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    for name, t, shp in (("q", q, (T, Hq, D)), ("k", k, (T, Hkv, D)), ("v", v, (T, Hkv, D)),
+                         ("out", out, (T, Hq, D)), ("dout", dout, (T, Hq, D)), ("dq", dq, (T, Hq, D)),
+                         ("dk", dk, (T, Hkv, D)), ("dv", dv, (T, Hkv, D))):
+        _check_tensor(name, t, q.dtype, shp, dev)
+    _check_tensor("lse", lse, torch.float32, (Hq, T), dev)
+    shape = _shape(q, k, softmax_scale)
+    with torch.cuda.device(dev):
+        _check(library().tree_attn_bwd_noalloc(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+            plan.handle, ctypes.byref(shape), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream_ptr(dev, stream)))
     return dq, dk, dv
 
 

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <functional>
 #include <memory>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -573,6 +574,70 @@ int tree_attn_bwd_dq(const void* q, const void* k, const void* v, const float* l
                         workspace, workspace_bytes, kDq, a, hg))
     return rc;
   return run_bwd("tree_attn_bwd_dq", a, shape, hg, kDq, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward: the workspace lives in a fixed device array of
+// this library.  Each GPU the library runs on holds its own copy of the
+// array (its own address) until the process ends; host code reaches it only
+// through the per-device address that hipGetSymbolAddress returns, never by
+// the array's name (a host-side stand-in).
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t(64) << 20) + 256;  // row statistics of Hq * T <= 2^23 rows + counters
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_fail(fn, e);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": device index " + std::to_string(dev) + " >= 64");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess || !p)
+      return hip_fail((std::string(fn) + ": hipGetSymbolAddress(scratch)").c_str(),
+                      e != hipSuccess ? e : hipErrorInvalidSymbol);
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return TREE_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tree_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                          const void* dout, tree_attn_plan_t plan, const tree_attn_shape* shape, void* dq, void* dk,
+                          void* dv, void* stream) {
+  const char* fn = "tree_attn_bwd_noalloc";
+  if (plan && shape && shape->total_tokens >= 1 && shape->num_q_heads >= 1) {
+    const size_t need = tree_attn_bwd_workspace_bytes(plan, shape);
+    if (need > kScratchBytes)
+      return fail(TREE_ATTN_UNSUPPORTED, std::string(fn) + ": the backward needs " + std::to_string(need) +
+                                             " bytes of scratch (2 * Hq * T floats + counters), above the fixed " +
+                                             std::to_string(kScratchBytes) + " (Hq * T <= 8,388,608)");
+  }
+  void* ws = nullptr;
+  if (int rc = scratch_address(fn, &ws)) return rc;
+  BwdArgs a;
+  int hg = 1;
+  // the row-statistics stage writes every statistic the later stages read
+  // and zeroes their work counters, so nothing left by an earlier call is used
+  if (int rc = prep_bwd(fn, q, k, v, out, lse, dout, plan, shape, dq, dk, dv, ws, kScratchBytes, kAll, a, hg))
+    return rc;
+  return run_bwd(fn, a, shape, hg, kAll, stream);
 }
 
 const char* tree_attn_last_error(void) { return g_last_error.c_str(); }
