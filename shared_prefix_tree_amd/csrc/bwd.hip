@@ -213,10 +213,13 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
   const unsigned s_lds = wave == 4 || wave == 5 ? s_ring + (wave - 4) * BM * 4 : lds_addr(junk);
   const unsigned s_step = wave == 4 || wave == 5 ? STATS : 0;
   const int crow = crow0 + lane / (RB / 16);
-  unsigned cchunk[NC];
-#pragma unroll
-  for (int r = 0; r < NC; ++r) cchunk[r] = (((lane % (RB / 16)) ^ swz<RB>(crow + RPC * r)) * 16);
   const unsigned row_bytes = (unsigned)a.Hq * RB;
+  unsigned cchunk[NC], coff[NC];  // swizzled chunk; whole-step offset (row crow + RPC r)
+#pragma unroll
+  for (int r = 0; r < NC; ++r) {
+    cchunk[r] = (((lane % (RB / 16)) ^ swz<RB>(crow + RPC * r)) * 16);
+    coff[r] = unsigned(crow + RPC * r) * row_bytes + cchunk[r];
+  }
   // Step `step` goes to slot step % kRing.  The copy stream advances one
   // step per call: (cp_h, cp_i0) is the head and first query of the next
   // step to copy, kept incrementally (no division); past the end it stays
@@ -228,14 +231,25 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
   auto issue = [&](int slot) {
     const int lim = last - cp_i0;
     const size_t row0 = ((size_t)cp_i0 * a.Hq + cp_h) * D;
+    if (lim >= BM - 1) {  // the whole step in range: fixed per-lane offsets
 #pragma unroll
-    for (int r = 0; r < NC; ++r) {
-      const unsigned voff = (unsigned)min(crow + RPC * r, lim) * row_bytes + cchunk[r];
-      const unsigned lofs = crow0 * RB + (unsigned)slot * TILE + RPC * r * RB;
-      copy16_async(static_cast<const T*>(a.q) + row0, voff, q_ring + lofs);
-      copy16_async(static_cast<const T*>(a.dout) + row0, voff, o_ring + lofs);
+      for (int r = 0; r < NC; ++r) {
+        const unsigned lofs = crow0 * RB + (unsigned)slot * TILE + RPC * r * RB;
+        copy16_async(static_cast<const T*>(a.q) + row0, coff[r], q_ring + lofs);
+        copy16_async(static_cast<const T*>(a.dout) + row0, coff[r], o_ring + lofs);
+      }
+      copy4_async(ssrc + (size_t)cp_h * a.T + cp_i0, (unsigned)lane * 4u, s_lds + (unsigned)slot * s_step);
+    } else {
+#pragma unroll
+      for (int r = 0; r < NC; ++r) {
+        const unsigned voff = (unsigned)min(crow + RPC * r, lim) * row_bytes + cchunk[r];
+        const unsigned lofs = crow0 * RB + (unsigned)slot * TILE + RPC * r * RB;
+        copy16_async(static_cast<const T*>(a.q) + row0, voff, q_ring + lofs);
+        copy16_async(static_cast<const T*>(a.dout) + row0, voff, o_ring + lofs);
+      }
+      copy4_async(ssrc + (size_t)cp_h * a.T + cp_i0, (unsigned)min(lane, lim) * 4u,
+                  s_lds + (unsigned)slot * s_step);
     }
-    copy4_async(ssrc + (size_t)cp_h * a.T + cp_i0, (unsigned)min(lane, lim) * 4u, s_lds + (unsigned)slot * s_step);
     if (++cp_step < n_steps) {
       cp_i0 += BM;
       if (cp_i0 > last) {
@@ -530,22 +544,36 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
   const unsigned s_lds = wave == 4 || wave == 5 ? s_ring + (wave - 4) * BM * 4 : lds_addr(junk);
   const unsigned s_step = wave == 4 || wave == 5 ? STATS : 0;
   const int crow = crow0 + lane / (RB / 16);
-  unsigned cchunk[NC];
-#pragma unroll
-  for (int r = 0; r < NC; ++r) cchunk[r] = (((lane % (RB / 16)) ^ swz<RB>(crow + RPC * r)) * 16);
   const unsigned row_bytes = (unsigned)a.Hq * RB;
+  unsigned cchunk[NC], coff[NC];  // swizzled chunk; whole-step offset (row crow + RPC r)
+#pragma unroll
+  for (int r = 0; r < NC; ++r) {
+    cchunk[r] = (((lane % (RB / 16)) ^ swz<RB>(crow + RPC * r)) * 16);
+    coff[r] = unsigned(crow + RPC * r) * row_bytes + cchunk[r];
+  }
   int cp_step = 0, cp_h = g * a.G, cp_i0 = qbeg;
   auto issue = [&](int slot) {
     const int lim = last - cp_i0;
     const size_t row0 = ((size_t)cp_i0 * a.Hq + cp_h) * D;
+    if (lim >= BM - 1) {  // the whole step in range: fixed per-lane offsets
 #pragma unroll
-    for (int r = 0; r < NC; ++r) {
-      const unsigned voff = (unsigned)min(crow + RPC * r, lim) * row_bytes + cchunk[r];
-      const unsigned lofs = crow0 * RB + (unsigned)slot * TILE + RPC * r * RB;
-      copy16_async(static_cast<const T*>(a.q) + row0, voff, q_ring + lofs);
-      copy16_async(static_cast<const T*>(a.dout) + row0, voff, o_ring + lofs);
+      for (int r = 0; r < NC; ++r) {
+        const unsigned lofs = crow0 * RB + (unsigned)slot * TILE + RPC * r * RB;
+        copy16_async(static_cast<const T*>(a.q) + row0, coff[r], q_ring + lofs);
+        copy16_async(static_cast<const T*>(a.dout) + row0, coff[r], o_ring + lofs);
+      }
+      copy4_async(ssrc + (size_t)cp_h * a.T + cp_i0, (unsigned)lane * 4u, s_lds + (unsigned)slot * s_step);
+    } else {
+#pragma unroll
+      for (int r = 0; r < NC; ++r) {
+        const unsigned voff = (unsigned)min(crow + RPC * r, lim) * row_bytes + cchunk[r];
+        const unsigned lofs = crow0 * RB + (unsigned)slot * TILE + RPC * r * RB;
+        copy16_async(static_cast<const T*>(a.q) + row0, voff, q_ring + lofs);
+        copy16_async(static_cast<const T*>(a.dout) + row0, voff, o_ring + lofs);
+      }
+      copy4_async(ssrc + (size_t)cp_h * a.T + cp_i0, (unsigned)min(lane, lim) * 4u,
+                  s_lds + (unsigned)slot * s_step);
     }
-    copy4_async(ssrc + (size_t)cp_h * a.T + cp_i0, (unsigned)min(lane, lim) * 4u, s_lds + (unsigned)slot * s_step);
     if (++cp_step < n_steps) {
       cp_i0 += BM;
       if (cp_i0 > last) {
@@ -842,8 +870,9 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, int item) {
 
   stage_spans(sSpans, a.span_ptr, a.spans, tile.seg);
   __syncthreads();
-  PathCopier<T, RB> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring),
-                       lds_addr(ring + kDqRing * TILE), sSpans, kv_len, wave, lane);
+  // (per-lane copy offsets: this walk has no vector registers to spare)
+  PathCopier<T, RB, false> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv,
+                                  lds_addr(ring), lds_addr(ring + kDqRing * TILE), sSpans, kv_len, wave, lane);
   auto issue = [&](int step) {
     copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kDqRing) * TILE);
   };

@@ -26,9 +26,11 @@
 //     transposing LDS load).  A lane owns one query column, so the row max
 //     and row sum are in-lane reductions plus one lane swap with lane l ^ 32;
 //   * the softmax works in base 2 with the scale folded into one FMA per
-//     score; the running max is only moved (and O rescaled) when a row's
-//     maximum grows by more than 2^8, which keeps the result exact (numerator
-//     and denominator share the same reference) and skips most rescales;
+//     score, against a reference that is only moved (and O rescaled) when a
+//     probability would exceed 2^16; the exponentials are taken against the
+//     current reference first and their sum decides whether a step needs the
+//     row maximum at all, so most steps compute no maximum.  Numerator and
+//     denominator share the reference, so the result is exact;
 //   * the own-segment causal rule is "virtual key position <= query
 //     position", applied only on the last steps of the walk.
 #include <type_traits>
@@ -37,7 +39,8 @@
 
 namespace tree_attn {
 
-constexpr float kRescaleSlack = 8.0f;  // log2 units: P values stay <= 256
+// a lane's sum of 32 probabilities above this (2^16) moves the reference
+constexpr float kLazyMax = 65536.0f;
 constexpr int kFwdRing = 4;
 
 template <int N>
@@ -124,35 +127,53 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
         for (int i = 0; i < 16; ++i)
           if (v0 + kb * 32 + c_row(i, half) > qpos) s[kb][i] = -INFINITY;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = max_halves(mx) * c;
-    const bool grow = mx > m + kRescaleSlack;
-    const float mnew = grow ? mx : m;
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    if (__any(grow)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    }
-    l *= alpha;
-    m = mnew;
-
-    // the denominator sums the fp32 probabilities; only the P*V operand is
-    // rounded to the input type
-    frag pf[2][2];
+    // Probabilities against the current reference m, without a row maximum:
+    // a lane whose sum exceeds kLazyMax (a score far above m), or is not a
+    // number (the first step, m = -inf), sends the wavefront through the
+    // slow path, which moves m to the row maximum, rescales l (O follows
+    // right before the P V products) and recomputes.  Every probability of
+    // the fast path is at most kLazyMax, so O and l stay far from overflow,
+    // and numerator and denominator always share one reference.
+    float p[2][16];
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -m));
-        rs += p;
-        pf[kb][i >> 3][i & 7] = to_elem<T>(p);
+        p[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -m));
+        rs += p[kb][i];
       }
+    if (__any(!(rs <= kLazyMax))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      mx = max_halves(mx) * c;
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      l *= alpha;
+      m = mnew;
+      rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -m));
+          rs += p[kb][i];
+        }
+    }
     l += rs;
+
+    // the denominator sums the fp32 probabilities; only the P*V operand is
+    // rounded to the input type
+    frag pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pf[kb][i >> 3][i & 7] = to_elem<T>(p[kb][i]);
 
 #pragma unroll
     for (int db = 0; db < DB; ++db)

@@ -145,13 +145,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 // orders them with wait_copies_barrier<N>().  Lane l reads
 // sbase + voff(l) (sbase wave-uniform) and writes LDS byte address
 // lds + size * l (lds wave-uniform).  Nothing else in such a kernel may
-// rely on M0 (no dynamic register indexing, no builtin LDS copies).
+// rely on M0 (no dynamic register indexing, no builtin LDS copies).  (The
+// LDS address goes through readfirstlane: the compiler may hold a uniform
+// value in a vector register, which the scalar operand cannot take.)
 __device__ inline void copy16_async(const void* sbase, unsigned voff, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m)
                : "memory");
 }
 __device__ inline void copy4_async(const void* sbase, unsigned voff, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m)
                : "memory");
 }
 
@@ -435,10 +439,13 @@ __device__ inline void stage_spans(Span* lds_spans, const int32_t* span_ptr, con
 // from one base; otherwise each lane looks its rows up with a per-lane span
 // cursor.  Positions past the path read the last valid row (the caller
 // masks them).  Byte offsets of rows must fit in 32 bits (checked by the
-// host).
+// host).  With SCALAR_BASE, in the one-span case the step's first row goes
+// into the wave-uniform base address (scalar arithmetic) and each lane adds
+// a fixed offset computed once, so the copies cost no vector instructions
+// (four more vector registers held for the offsets).
 __host__ __device__ constexpr int path_copies(int RB) { return 16 * RB / 1024; }
 
-template <typename T, int RB>
+template <typename T, int RB, bool SCALAR_BASE = true>
 struct PathCopier {
   static constexpr int NC = path_copies(RB);  // copies per wave per step
   static constexpr int RPC = 1024 / RB;       // rows per copy
@@ -447,6 +454,7 @@ struct PathCopier {
   unsigned row_bytes;  // bytes between consecutive tokens
   unsigned lds;        // this wave's first row in slot 0 of its ring
   unsigned chunk[NC];  // this lane's swizzled byte offset in its row, per copy
+  unsigned lane_off[NC];  // (row + RPC r) * row_bytes + chunk[r]: the one-span case's per-lane offset
   int row;             // this lane's row of copy 0 (copy r: row + RPC r)
   const Span* spans;   // the segment's spans, in LDS
   int ucur, lcur;      // wave-uniform and per-lane span cursors
@@ -461,7 +469,10 @@ struct PathCopier {
     lds = (wave < 4 ? k_ring : v_ring) + r0 * RB;
     row = r0 + lane / LPR;
 #pragma unroll
-    for (int r = 0; r < NC; ++r) chunk[r] = unsigned(((lane % LPR) ^ swz<RB>(row + RPC * r)) * 16);
+    for (int r = 0; r < NC; ++r) {
+      chunk[r] = unsigned(((lane % LPR) ^ swz<RB>(row + RPC * r)) * 16);
+      if constexpr (SCALAR_BASE) lane_off[r] = unsigned(row + RPC * r) * row_bytes + chunk[r];
+    }
     spans = sp;
     ucur = 0;
     lcur = 0;
@@ -481,21 +492,28 @@ struct PathCopier {
       clen = __builtin_amdgcn_readfirstlane(spans[ucur].len);
       cvirt = __builtin_amdgcn_readfirstlane(spans[ucur].virt);
     }
-    int phys[NC];
-    if (v0 + 64 <= cvirt + clen && v0 + 64 <= kv_len) {
+    const bool one_span = v0 + 64 <= cvirt + clen && v0 + 64 <= kv_len;
+    if (SCALAR_BASE && one_span) {
+      const char* sb = reinterpret_cast<const char*>(base) + size_t(unsigned(cphys + (v0 - cvirt))) * row_bytes;
 #pragma unroll
-      for (int r = 0; r < NC; ++r) phys[r] = cphys + (v0 - cvirt) + row + RPC * r;
+      for (int r = 0; r < NC; ++r) copy16_async(sb, lane_off[r], lds + slot + RPC * r * RB);
     } else {
+      int phys[NC];
+      if (one_span) {
 #pragma unroll
-      for (int r = 0; r < NC; ++r) {
-        const int v = min(v0 + row + RPC * r, kv_len - 1);
-        while (v >= spans[lcur].virt + spans[lcur].len) ++lcur;
-        phys[r] = spans[lcur].phys + (v - spans[lcur].virt);
+        for (int r = 0; r < NC; ++r) phys[r] = cphys + (v0 - cvirt) + row + RPC * r;
+      } else {
+#pragma unroll
+        for (int r = 0; r < NC; ++r) {
+          const int v = min(v0 + row + RPC * r, kv_len - 1);
+          while (v >= spans[lcur].virt + spans[lcur].len) ++lcur;
+          phys[r] = spans[lcur].phys + (v - spans[lcur].virt);
+        }
       }
-    }
 #pragma unroll
-    for (int r = 0; r < NC; ++r)
-      copy16_async(base, (unsigned)phys[r] * row_bytes + chunk[r], lds + slot + RPC * r * RB);
+      for (int r = 0; r < NC; ++r)
+        copy16_async(base, (unsigned)phys[r] * row_bytes + chunk[r], lds + slot + RPC * r * RB);
+    }
   }
 };
 
