@@ -358,8 +358,8 @@ int tree_attn_plan_export(tree_attn_plan_t plan, int32_t which, int32_t* buf, in
  * and lse.  stream: a hipStream_t (NULL = default).  Asynchronous.
  * Errors: INVALID_ARGUMENT (null pointer, shape mismatch, host-only plan,
  * plan built on another device), UNSUPPORTED (dtype/head_dim, more than
- * 2^31 elements in a tensor, or a segment whose ancestor path splits into
- * more than 256 separate token spans), HIP_ERROR.
+ * 2^31 elements in a tensor, or K/V of 2^32 bytes or more), HIP_ERROR.
+ * A segment's ancestor path may split into any number of token spans.
  */
 int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t plan,
                   const tree_attn_shape* shape, void* out, float* lse, void* stream);

@@ -216,10 +216,6 @@ int check_call(const char* fn, tree_attn_plan_t plan, const tree_attn_shape* sha
   const int64_t rows = int64_t(shape->total_tokens) * shape->num_q_heads;
   if (rows * shape->head_dim >= (int64_t(1) << 31))
     return fail(TREE_ATTN_UNSUPPORTED, f + ": tensors are limited to 2^31 elements");
-  if (plan->host.max_spans > kMaxSpans)
-    return fail(TREE_ATTN_UNSUPPORTED, f + ": a segment's ancestor path has " +
-                                           std::to_string(plan->host.max_spans) + " separate spans (limit " +
-                                           std::to_string(kMaxSpans) + ")");
   // the query-major kernels gather K/V rows with 32-bit byte offsets
   const int64_t elem = shape->dtype == TREE_ATTN_BF16 ? 2 : 4;
   if (int64_t(shape->total_tokens) * shape->num_kv_heads * shape->head_dim * elem >= (int64_t(1) << 32))

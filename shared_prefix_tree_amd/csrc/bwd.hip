@@ -819,7 +819,6 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, int item) {
 
   // K ring then V ring (each 64 KB, so a slot offset fits an LDS immediate)
   __shared__ __attribute__((aligned(16))) char ring[2 * kDqRing * TILE];
-  __shared__ Span sSpans[kMaxSpans];
 
   int tile_rank, group;
   decode_item(item, a.Hq / HG, tile_rank, group);
@@ -854,25 +853,16 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, int item) {
   }
   const float nlse2 = a.delta[(size_t)a.Hq * a.T + (size_t)h * a.T + qtok];
   const float ndlt = a.delta[(size_t)h * a.T + qtok];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    settle(qf[ks]);
-    settle(of[ks]);
-  }
-  asm volatile("" ::"v"(nlse2), "v"(ndlt));
-  f32x16 ndlt16;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) ndlt16[i] = ndlt;
 
   f32x16 dq[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+  f32x16 ndlt16;  // -delta of this lane's query in all 16 entries (set once the loads are in)
 
-  stage_spans(sSpans, a.span_ptr, a.spans, tile.seg);
-  __syncthreads();
   // (per-lane copy offsets: this walk has no vector registers to spare)
   PathCopier<T, RB, false> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv,
-                                  lds_addr(ring), lds_addr(ring + kDqRing * TILE), sSpans, kv_len, wave, lane);
+                                  lds_addr(ring), lds_addr(ring + kDqRing * TILE),
+                                  a.spans + a.span_ptr[tile.seg], kv_len, wave, lane);
   auto issue = [&](int step) {
     copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kDqRing) * TILE);
   };
@@ -927,6 +917,15 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, int item) {
 
 #pragma unroll
   for (int st = 0; st < kAhead; ++st) issue(st);
+  // the row loads are waited for only now, after the first copies are issued
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    settle(qf[ks]);
+    settle(of[ks]);
+  }
+  asm volatile("" ::"v"(nlse2), "v"(ndlt));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndlt16[i] = ndlt;
   // unrolled over the ring slots so every LDS offset is a constant
   for (int step = 0;; step += kDqRing) {
     body(step, Slot<0>{});

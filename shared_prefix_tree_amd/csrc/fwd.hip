@@ -63,7 +63,6 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
 
   // K ring then V ring (each 64 KB, so a slot offset fits an LDS immediate)
   __shared__ __attribute__((aligned(16))) char ring[2 * kFwdRing * TILE];
-  __shared__ Span sSpans[kMaxSpans];
 
   int tile_rank, group;
   decode_item(blockIdx.x, a.Hq / HG, tile_rank, group);
@@ -83,24 +82,23 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
   const int n_steps = (kv_len + BN - 1) / BN;
   const float c = a.scale * kLog2e;
 
+  // Q is loaded first; its wait comes after the first copies are issued, so
+  // both latencies overlap
   frag qf[KS];
   {
     const T* p = static_cast<const T*>(a.q) + ((size_t)qtok * a.Hq + h) * D + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = load_frag<T>(p + ks * 16);
   }
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
 
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  stage_spans(sSpans, a.span_ptr, a.spans, tile.seg);
-  __syncthreads();
   PathCopier<T, RB> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring),
-                       lds_addr(ring + kFwdRing * TILE), sSpans, kv_len, wave, lane);
+                           lds_addr(ring + kFwdRing * TILE), a.spans + a.span_ptr[tile.seg], kv_len, wave,
+                           lane);
   // step `step` goes to slot step % kFwdRing; steps past the end re-copy
   // the last step into their (idle) slot so every wave issues the same
   // number of copies per step
@@ -194,6 +192,8 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
 
 #pragma unroll
   for (int st = 0; st < kAhead; ++st) issue(st);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
   // unrolled over the ring slots so every LDS offset is a constant
   for (int step = 0;; step += kFwdRing) {
     body(step, Slot<0>{});

@@ -416,16 +416,15 @@ __device__ inline void finish_block(ItemCounters* ctr) {
   }
 }
 
-// A segment's merged spans are staged in LDS once per workgroup, so span
-// lookups use the LDS counter and never wait behind in-flight global->LDS
-// copies.  A segment may have at most kMaxSpans spans (checked by the host).
-constexpr int kMaxSpans = 256;
-
-// Copies the spans of segment `seg` to LDS (every thread takes part; the
-// caller synchronises before use).
-__device__ inline void stage_spans(Span* lds_spans, const int32_t* span_ptr, const Span* spans, int seg) {
-  const int first = span_ptr[seg], n = span_ptr[seg + 1] - first;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) lds_spans[i] = spans[first + i];
+// One span record through the scalar data cache: the address is
+// wave-uniform, the result lands in scalar registers, and the load is waited
+// for inside the same asm block (lgkmcnt counts scalar loads and LDS
+// operations, not the global->LDS copies, so it never waits behind those).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ inline Span load_span(const Span* p) {
+  i32x4 r;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+  return Span{r[0], r[1], r[2], r[3]};
 }
 
 // Copies of a segment's ancestor path, as one virtual key sequence, into
@@ -434,10 +433,13 @@ __device__ inline void stage_spans(Span* lds_spans, const int32_t* span_ptr, con
 // tile of the K ring and its V rows to the same slot of the V ring
 // (row-major, swizzled).  Waves 0-3 copy K rows, waves 4-7 V rows, 16 rows
 // each; one copy instruction moves 1 KB = 1024 / RB rows, so every wave
-// issues exactly path_copies(RB) copies per step.  A step inside one span
-// (the common case: spans are usually much longer than 64) takes its rows
-// from one base; otherwise each lane looks its rows up with a per-lane span
-// cursor.  Positions past the path read the last valid row (the caller
+// issues exactly path_copies(RB) copies per step.  The span records are read
+// from the plan in global memory with scalar loads, one at a time, so a
+// path may have any number of spans and nothing is staged before the walk.
+// A step inside one span (the common case: spans are usually much longer
+// than 64) takes its rows from one base; otherwise the wave visits the spans
+// the step overlaps in order and each lane takes its row from the one that
+// holds it.  Positions past the path read the last valid row (the caller
 // masks them).  Byte offsets of rows must fit in 32 bits (checked by the
 // host).  With SCALAR_BASE, in the one-span case the step's first row goes
 // into the wave-uniform base address (scalar arithmetic) and each lane adds
@@ -456,9 +458,9 @@ struct PathCopier {
   unsigned chunk[NC];  // this lane's swizzled byte offset in its row, per copy
   unsigned lane_off[NC];  // (row + RPC r) * row_bytes + chunk[r]: the one-span case's per-lane offset
   int row;             // this lane's row of copy 0 (copy r: row + RPC r)
-  const Span* spans;   // the segment's spans, in LDS
-  int ucur, lcur;      // wave-uniform and per-lane span cursors
-  int cphys, clen, cvirt;  // spans[ucur], kept in registers
+  const Span* spans;   // the segment's spans (global memory)
+  int ucur;            // wave-uniform span cursor
+  int cphys, clen, cvirt;  // spans[ucur], kept in scalar registers
   int kv_len;          // positions on the path
 
   __device__ PathCopier(const T* k, const T* v, int g, int Hkv, unsigned k_ring, unsigned v_ring, const Span* sp,
@@ -475,22 +477,22 @@ struct PathCopier {
     }
     spans = sp;
     ucur = 0;
-    lcur = 0;
     kv_len = len;
-    cphys = __builtin_amdgcn_readfirstlane(sp[0].phys);
-    clen = __builtin_amdgcn_readfirstlane(sp[0].len);
-    cvirt = __builtin_amdgcn_readfirstlane(sp[0].virt);
+    const Span s0 = load_span(sp);
+    cphys = s0.phys;
+    clen = s0.len;
+    cvirt = s0.virt;
   }
 
   // positions [v0, v0 + 64) into the ring slot at byte offset `slot`
   __device__ inline void issue(int v0, unsigned slot) {
-    // the current span stays in registers: a step inside it (the common
-    // case) reads no LDS, so the copies are not held up behind LDS traffic
+    // the current span stays in scalar registers: a step inside it (the
+    // common case) loads nothing
     while (v0 >= cvirt + clen) {
-      ++ucur;
-      cphys = __builtin_amdgcn_readfirstlane(spans[ucur].phys);
-      clen = __builtin_amdgcn_readfirstlane(spans[ucur].len);
-      cvirt = __builtin_amdgcn_readfirstlane(spans[ucur].virt);
+      const Span sp = load_span(spans + (++ucur));
+      cphys = sp.phys;
+      clen = sp.len;
+      cvirt = sp.virt;
     }
     const bool one_span = v0 + 64 <= cvirt + clen && v0 + 64 <= kv_len;
     if (SCALAR_BASE && one_span) {
@@ -503,11 +505,24 @@ struct PathCopier {
 #pragma unroll
         for (int r = 0; r < NC; ++r) phys[r] = cphys + (v0 - cvirt) + row + RPC * r;
       } else {
+        // the spans the step overlaps, from the current one (which holds v0)
+        int v[NC];
 #pragma unroll
         for (int r = 0; r < NC; ++r) {
-          const int v = min(v0 + row + RPC * r, kv_len - 1);
-          while (v >= spans[lcur].virt + spans[lcur].len) ++lcur;
-          phys[r] = spans[lcur].phys + (v - spans[lcur].virt);
+          v[r] = min(v0 + row + RPC * r, kv_len - 1);
+          phys[r] = 0;
+        }
+        const int hi = min(v0 + 63, kv_len - 1);  // the last position of the step
+        int k = ucur, sphys = cphys, slen = clen, svirt = cvirt;
+        for (;;) {
+#pragma unroll
+          for (int r = 0; r < NC; ++r)
+            if (v[r] >= svirt && v[r] < svirt + slen) phys[r] = sphys + (v[r] - svirt);
+          if (svirt + slen > hi) break;
+          const Span sp = load_span(spans + (++k));
+          sphys = sp.phys;
+          slen = sp.len;
+          svirt = sp.virt;
         }
       }
 #pragma unroll

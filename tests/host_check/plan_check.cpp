@@ -7,8 +7,7 @@
 // of sampled edges, and checks that every index a kernel derives from those
 // tables stays inside the tensors it addresses:
 //   * ancestor spans: rows phys .. phys + len - 1 inside [0, T), virtual
-//     positions contiguous from 0 up to the segment's path length, at most
-//     256 spans per segment for the walks that stage them in LDS, and the
+//     positions contiguous from 0 up to the segment's path length, and the
 //     32-bit byte offsets of K/V row gathers (row * Hkv * row bytes + row
 //     bytes) below 2^32 for the shapes the library accepts;
 //   * query tiles of every size: inside one segment and the query run,

@@ -4,7 +4,7 @@ bounds checker of every plan table the kernels read.
 ``tests/host_check/plan_check.cpp`` is built with g++ (no device code)
 together with the library's host-only sources -- the attention plan
 builder, the fragment planner, the Mamba table builder and the edge CSR --
-and run over random forests, comb topologies (paths of up to 257 separate
+and run over random forests, comb topologies (paths of up to 301 separate
 spans), and the topologies of every synthetic workload.  It checks that each
 span row, query tile, key tile, query end, 32-bit byte offset, fragment
 table, Mamba predecessor / halo / successor / unit entry and edge CSR entry
@@ -38,7 +38,7 @@ def _forests():
     out += [
         ("comb_2_1_x100", comb(100, spine_len=2, leaf_len=1, tail_len=70)),
         ("comb_1_1_x255", comb(255, spine_len=1, leaf_len=1, tail_len=40)),
-        ("comb_1_1_x256", comb(256, spine_len=1, leaf_len=1, tail_len=8)),
+        ("comb_1_1_x300", comb(300, spine_len=1, leaf_len=1, tail_len=8)),
         ("comb_7_3_x40", comb(40, spine_len=7, leaf_len=3)),
     ]
     for w in WORKLOADS:
