@@ -417,6 +417,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="agent_tree_65536_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fwd-entry", choices=("ws", "plain"), default="ws",
+                    help="forward entry point timed: tree_attn_fwd_ws (work-item counters in a workspace, the "
+                         "default) or tree_attn_fwd (one workgroup per query tile); the results are bitwise equal")
     ap.add_argument("--cpu-kv-heads", type=int, default=1)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes, --steps times (scales HBM counters)")
@@ -492,6 +495,7 @@ def main():
     info = probe.info()
     pairs = info["pairs"]
     ws = torch.empty(max(256, sp.bwd_workspace_bytes(probe, t["q"], t["k"])), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(256, sp.fwd_workspace_bytes(probe, t["q"], t["k"])), dtype=torch.uint8, device=dev)
     del probe
 
     stages = ["fwd", "rowstat", "dkdv", "dq"] if w.backward else ["fwd"]
@@ -509,7 +513,8 @@ def main():
         plan_host_s.append(time.perf_counter() - t0)
         if events:
             events[0].record()
-        sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan, out=out, lse=lse)
+        sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan, out=out, lse=lse,
+                         workspace=fws if args.fwd_entry == "ws" else None)
         if w.backward:
             sp.tree_attn_bwd_stages(t["q"], t["k"], t["v"], out, lse, t["dout"], plan, dq, dk, dv, ws,
                                     events=events[1:] if events else None)

@@ -364,6 +364,27 @@ int tree_attn_plan_export(tree_attn_plan_t plan, int32_t which, int32_t* buf, in
 int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t plan,
                   const tree_attn_shape* shape, void* out, float* lse, void* stream);
 
+/* Bytes of device workspace tree_attn_fwd_ws needs (work-item counters;
+ * 256); 0 on invalid input. */
+size_t tree_attn_fwd_workspace_bytes(tree_attn_plan_t plan, const tree_attn_shape* shape);
+
+/*
+ * tree_attn_fwd with a caller workspace of at least
+ * tree_attn_fwd_workspace_bytes() (device memory, 16-byte aligned, any
+ * contents).  The same results, bitwise: each output row is still computed
+ * by one workgroup in a fixed order; the workspace only holds the counters
+ * through which one workgroup per compute unit takes query tiles until none
+ * is left (first from its own XCD's share, then from the others'), so the
+ * eight XCDs' clock differences do not leave the slowest one finishing
+ * alone.  The counters are zeroed by a one-workgroup launch at the start of
+ * every call.  Calls that overlap on one workspace race.
+ * Errors: as tree_attn_fwd, plus INVALID_ARGUMENT for a NULL, misaligned or
+ * small workspace.
+ */
+int tree_attn_fwd_ws(const void* q, const void* k, const void* v, tree_attn_plan_t plan,
+                     const tree_attn_shape* shape, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* Bytes of device workspace tree_attn_bwd needs for this plan and shape
  * (two float32 [Hq, T] row-statistic arrays, 256-byte aligned, then 128
  * bytes of work-item counters); 0 on invalid input. */

@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     edge_loss_bwd,
     edge_loss_fwd,
     fragment,
+    fwd_workspace_bytes,
     library,
     ssm_bwd,
     ssm_fwd,

@@ -42,6 +42,8 @@ SYMBOLS = (
     "tree_attn_plan_info",
     "tree_attn_plan_export",
     "tree_attn_fwd",
+    "tree_attn_fwd_workspace_bytes",
+    "tree_attn_fwd_ws",
     "tree_attn_bwd_workspace_bytes",
     "tree_attn_bwd",
     "tree_attn_bwd_rowstat",
@@ -184,6 +186,9 @@ def library():
     lib.tree_attn_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     lib.tree_attn_plan_export.argtypes = [vp, ctypes.c_int32, i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
     lib.tree_attn_fwd.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), vp, vp, vp]
+    lib.tree_attn_fwd_workspace_bytes.argtypes = [vp, ctypes.POINTER(Shape)]
+    lib.tree_attn_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.tree_attn_fwd_ws.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), vp, vp, vp, ctypes.c_size_t, vp]
     lib.tree_attn_bwd_workspace_bytes.argtypes = [vp, ctypes.POINTER(Shape)]
     lib.tree_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.tree_attn_bwd.argtypes = [vp] * 6 + [vp, ctypes.POINTER(Shape)] + [vp] * 4 + [ctypes.c_size_t, vp]
@@ -686,9 +691,12 @@ def _stream_ptr(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def tree_attn_fwd(q, k, v, plan: Plan, softmax_scale=0.0, out=None, lse=None, stream=None):
+def tree_attn_fwd(q, k, v, plan: Plan, softmax_scale=0.0, out=None, lse=None, stream=None, workspace=None):
     """Forward pass.  q [T,Hq,D], k/v [T,Hkv,D] (bf16 or fp32, contiguous, on
-    one GPU).  Returns (out [T,Hq,D], lse [Hq,T] float32)."""
+    one GPU).  Returns (out [T,Hq,D], lse [Hq,T] float32).  With a device
+    ``workspace`` (uint8, at least ``fwd_workspace_bytes``) the call is
+    ``tree_attn_fwd_ws``: the same results, query tiles handed out through
+    work-item counters."""
     import torch
 
     T, Hq, D = q.shape
@@ -705,13 +713,22 @@ def tree_attn_fwd(q, k, v, plan: Plan, softmax_scale=0.0, out=None, lse=None, st
     _check_tensor("lse", lse, torch.float32, (Hq, T), dev)
     shape = _shape(q, k, softmax_scale)
     with torch.cuda.device(dev):
-        _check(
-            library().tree_attn_fwd(
-                q.data_ptr(), k.data_ptr(), v.data_ptr(), plan.handle, ctypes.byref(shape),
-                out.data_ptr(), lse.data_ptr(), _stream_ptr(dev, stream),
-            )
-        )
+        if workspace is None:
+            _check(library().tree_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), plan.handle,
+                                           ctypes.byref(shape), out.data_ptr(), lse.data_ptr(),
+                                           _stream_ptr(dev, stream)))
+        else:
+            _check(library().tree_attn_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), plan.handle,
+                                              ctypes.byref(shape), out.data_ptr(), lse.data_ptr(),
+                                              workspace.data_ptr(),
+                                              ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                              _stream_ptr(dev, stream)))
     return out, lse
+
+
+def fwd_workspace_bytes(plan: Plan, q, k, softmax_scale=0.0) -> int:
+    shape = _shape(q, k, softmax_scale)
+    return int(library().tree_attn_fwd_workspace_bytes(plan.handle, ctypes.byref(shape)))
 
 
 def bwd_workspace_bytes(plan: Plan, q, k, softmax_scale=0.0) -> int:

@@ -30,6 +30,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 template <typename T, int D, int HG>
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_reset_counters(ItemCounters* c, int n, hipStream_t stream);
+unsigned persistent_grid(unsigned n_items);
 
 namespace {
 
@@ -387,17 +388,26 @@ int tree_attn_plan_export(tree_attn_plan_t plan, int32_t which, int32_t* buf, in
   return TREE_ATTN_OK;
 }
 
-int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t plan, const tree_attn_shape* shape,
-                  void* out, float* lse, void* stream) {
+static int run_fwd(const char* fn, const void* q, const void* k, const void* v, tree_attn_plan_t plan,
+                   const tree_attn_shape* shape, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  const std::string f(fn);
   float scale = 0.f;
-  if (!q || !k || !v || !out || !lse) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fwd: NULL tensor pointer");
+  if (!q || !k || !v || !out || !lse) return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": NULL tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fwd: tensors must be 16-byte aligned");
-  if (int rc = check_call("tree_attn_fwd", plan, shape, &scale)) return rc;
+    return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": tensors must be 16-byte aligned");
+  if (int rc = check_call(fn, plan, shape, &scale)) return rc;
+  if (workspace) {
+    if (!aligned16(workspace)) return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": workspace must be 16-byte aligned");
+    if (workspace_bytes < sizeof(ItemCounters))
+      return fail(TREE_ATTN_INVALID_ARGUMENT, f + ": workspace " + std::to_string(workspace_bytes) +
+                                                  " bytes < required " + std::to_string(sizeof(ItemCounters)));
+  }
   const int G = shape->num_q_heads / shape->num_kv_heads;
   const int hg = gcd(G, 4);
   const int ti = qtile_index(fwd_query_tile(hg));
   FwdArgs a;
+  a.counters = static_cast<ItemCounters*>(workspace);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -413,19 +423,39 @@ int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t 
   a.G = G;
   a.scale = scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (shape->dtype == TREE_ATTN_BF16 && shape->head_dim == 128) {
-    e = hg == 4 ? launch_fwd<__bf16, 128, 4>(a, s) : hg == 2 ? launch_fwd<__bf16, 128, 2>(a, s)
-                                                           : launch_fwd<__bf16, 128, 1>(a, s);
-  } else if (shape->dtype == TREE_ATTN_BF16) {
-    e = hg == 4 ? launch_fwd<__bf16, 64, 4>(a, s) : hg == 2 ? launch_fwd<__bf16, 64, 2>(a, s)
-                                                          : launch_fwd<__bf16, 64, 1>(a, s);
-  } else {
-    e = hg == 4 ? launch_fwd<float, 64, 4>(a, s) : hg == 2 ? launch_fwd<float, 64, 2>(a, s)
-                                                         : launch_fwd<float, 64, 1>(a, s);
+  hipError_t e = hipSuccess;
+  // the work-item counters start from zero whatever the workspace held
+  if (a.counters) e = launch_reset_counters(a.counters, 1, s);
+  if (e == hipSuccess) {
+    if (shape->dtype == TREE_ATTN_BF16 && shape->head_dim == 128) {
+      e = hg == 4 ? launch_fwd<__bf16, 128, 4>(a, s) : hg == 2 ? launch_fwd<__bf16, 128, 2>(a, s)
+                                                             : launch_fwd<__bf16, 128, 1>(a, s);
+    } else if (shape->dtype == TREE_ATTN_BF16) {
+      e = hg == 4 ? launch_fwd<__bf16, 64, 4>(a, s) : hg == 2 ? launch_fwd<__bf16, 64, 2>(a, s)
+                                                            : launch_fwd<__bf16, 64, 1>(a, s);
+    } else {
+      e = hg == 4 ? launch_fwd<float, 64, 4>(a, s) : hg == 2 ? launch_fwd<float, 64, 2>(a, s)
+                                                           : launch_fwd<float, 64, 1>(a, s);
+    }
   }
-  if (e != hipSuccess) return hip_fail("tree_attn_fwd: launch", e);
+  if (e != hipSuccess) return hip_fail((f + ": launch").c_str(), e);
   return TREE_ATTN_OK;
+}
+
+int tree_attn_fwd(const void* q, const void* k, const void* v, tree_attn_plan_t plan, const tree_attn_shape* shape,
+                  void* out, float* lse, void* stream) {
+  return run_fwd("tree_attn_fwd", q, k, v, plan, shape, out, lse, nullptr, 0, stream);
+}
+
+size_t tree_attn_fwd_workspace_bytes(tree_attn_plan_t plan, const tree_attn_shape* shape) {
+  if (!plan || !shape) return 0;
+  return 256;
+}
+
+int tree_attn_fwd_ws(const void* q, const void* k, const void* v, tree_attn_plan_t plan, const tree_attn_shape* shape,
+                     void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_fwd_ws: workspace is NULL");
+  return run_fwd("tree_attn_fwd_ws", q, k, v, plan, shape, out, lse, workspace, workspace_bytes, stream);
 }
 
 // workspace: -delta and -lse2 ([Hq, T] float32 each), then the work-item

@@ -27,6 +27,7 @@
 //   3. dq (query-major): the forward's walk over the ancestor path,
 //        S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - delta),
 //        dQ^T += K^T dS^T   (K^T from the transposing LDS load).
+#include <atomic>
 #include <type_traits>
 
 #include "kernel_common.hpp"
@@ -980,17 +981,17 @@ hipError_t launch_reset_counters(ItemCounters* c, int n, hipStream_t stream) {
 
 // one 512-thread workgroup fits a CU (LDS), so the item-taking kernels run
 // as many workgroups as the device has CUs (fewer for fewer items)
-static unsigned persistent_grid(unsigned n_items) {
-  static int cus[64] = {};
+unsigned persistent_grid(unsigned n_items) {
+  static std::atomic<int> cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return n_items;
-  if (cus[dev] <= 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       return n_items;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return n_items < unsigned(cus[dev]) ? n_items : unsigned(cus[dev]);
+  return n_items < unsigned(n) ? n_items : unsigned(n);
 }
 
 template <typename T, int D>

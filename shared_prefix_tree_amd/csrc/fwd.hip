@@ -46,8 +46,14 @@ constexpr int kFwdRing = 4;
 template <int N>
 using Slot = std::integral_constant<int, N>;
 
+template <typename T, int D>
+constexpr int fwd_ring_bytes() {
+  return 2 * kFwdRing * 64 * D * int(sizeof(T));
+}
+
+// One work item: query tile `tile_rank` of the plan's list, head group `group`.
 template <typename T, int D, int HG>
-__global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   using quad = typename M::quad;
@@ -61,14 +67,17 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
   static_assert(8 % HG == 0, "eight wavefronts per workgroup");
   static_assert(kFwdRing == 4, "the walk is unrolled over four ring slots");
 
-  // K ring then V ring (each 64 KB, so a slot offset fits an LDS immediate)
-  __shared__ __attribute__((aligned(16))) char ring[2 * kFwdRing * TILE];
-
+  // `ring`: the K ring then the V ring (each 64 KB, so a slot offset fits an
+  // LDS immediate)
   int tile_rank, group;
-  decode_item(blockIdx.x, a.Hq / HG, tile_rank, group);
+  decode_item(item, a.Hq / HG, tile_rank, group);
   const QTile tile = a.tiles[tile_rank];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  // (opaque per item, so nothing derived from the thread index is hoisted
+  // out of the item loop to stay live across items)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 31, half = lane >> 5;
   const int ts = wave / HG;
@@ -224,11 +233,34 @@ __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// One workgroup per item (work in the plan's longest-first order, spread
+// over the XCDs by the dispatcher), or -- with work-item counters from the
+// caller's workspace -- one workgroup per CU taking items until none is left
+// (the hand-out of the backward walks: XCD-local lists first, then the
+// other XCDs' remaining items), which absorbs the XCDs' clock differences.
+template <typename T, int D, int HG, bool DYN>
+__global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char ring[fwd_ring_bytes<T, D>()];
+  if constexpr (DYN) {
+    __shared__ int s_item;
+    const int n_items = a.n_tiles * (a.Hq / HG);
+    for (int item; (item = take_item(a.counters, n_items, &s_item)) >= 0;) fwd_item<T, D, HG>(a, item, ring);
+    finish_block(a.counters);
+  } else {
+    fwd_item<T, D, HG>(a, blockIdx.x, ring);
+  }
+}
+
+unsigned persistent_grid(unsigned n_items);
+
 template <typename T, int D, int HG>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  const int groups = a.Hq / HG;
-  const dim3 grid((unsigned)a.n_tiles * (unsigned)groups);
-  hipLaunchKernelGGL((tree_attn_fwd_kernel<T, D, HG>), grid, dim3(512), 0, stream, a);
+  const unsigned n_items = (unsigned)a.n_tiles * (unsigned)(a.Hq / HG);
+  if (a.counters)
+    hipLaunchKernelGGL((tree_attn_fwd_kernel<T, D, HG, true>), dim3(persistent_grid(n_items)), dim3(512), 0, stream,
+                       a);
+  else
+    hipLaunchKernelGGL((tree_attn_fwd_kernel<T, D, HG, false>), dim3(n_items), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -533,6 +533,7 @@ struct PathCopier {
 };
 
 struct FwdArgs {
+  ItemCounters* counters;  // work-item hand-out (caller workspace), or null: one workgroup per item
   const void* q;
   const void* k;
   const void* v;

@@ -447,3 +447,29 @@ def test_stream_ordered_plan_upload_matches_the_synchronous_one():
     for r in results:
         for a, b_ in zip((out0, lse0, *g0), r):
             assert torch.equal(a, b_)
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", [("bf16", 128, 8, 2), ("bf16", 64, 4, 4), ("fp32", 64, 8, 1)])
+def test_workspace_forward_is_bitwise_the_plain_forward(dtype, D, Hq, Hkv):
+    """tree_attn_fwd_ws (query tiles handed out through counters in a caller
+    workspace) writes bitwise what tree_attn_fwd writes, on a fresh workspace
+    of arbitrary bytes and on repeated calls with it."""
+    sp = lib()
+    rng = np.random.default_rng(45)
+    for n, topo in enumerate([random_forest(rng, max_tokens=2500, max_len=500, max_depth=5, p_new_root=0.05),
+                              comb(80, spine_len=2, leaf_len=3, tail_len=300), tiny_tree()]):
+        arrs = make_inputs(rng, topo.total_tokens, Hq, Hkv, D, dtype)
+        t = {k: to_torch(v, dtype, "cuda:0") for k, v in arrs.items()}
+        plan = sp.Plan.from_topology(topo)
+        ref = sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan)
+        nbytes = sp.fwd_workspace_bytes(plan, t["q"], t["k"])
+        ws = torch.full((nbytes,), 0xA5 if n % 2 else 0xFF, dtype=torch.uint8, device="cuda:0")
+        for _ in range(3):
+            got = sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+        log(f"workspace forward, case {n}: T={topo.total_tokens} {dtype} D={D} bitwise equal")
+    small = torch.zeros(8, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(sp.TreeAttnError) as e:
+        sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan, workspace=small)
+    assert e.value.code == sp.binding.INVALID_ARGUMENT
