@@ -780,9 +780,10 @@ __global__ __launch_bounds__(512, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
                            ? dkdv_wide_lds_bytes<T, D>()
                            : dkdv_lds_bytes<T, D>();
   __shared__ __attribute__((aligned(16))) char lds[kLds];
-  __shared__ int s_item;
+  __shared__ int s_item[2];
+  int turn = 0;
   const int n_items = a.n_ktiles * a.Hkv;
-  for (int item; (item = take_item(&a.counters[0], n_items, &s_item)) >= 0;) {
+  for (int item; (item = take_item(&a.counters[0], n_items, s_item, turn)) >= 0;) {
     int tile_rank, g;
     decode_item(item, a.Hkv, tile_rank, g);
     const KTile tile = a.ktiles[tile_rank];
@@ -957,9 +958,10 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, int item) {
 // one workgroup per CU, taking items until none is left
 template <typename T, int D, int HG>
 __global__ __launch_bounds__(512, 1) void tree_attn_dq_kernel(BwdArgs a) {
-  __shared__ int s_item;
+  __shared__ int s_item[2];
+  int turn = 0;
   const int n_items = a.n_qtiles * (a.Hq / HG);
-  for (int item; (item = take_item(&a.counters[1], n_items, &s_item)) >= 0;) dq_item<T, D, HG>(a, item);
+  for (int item; (item = take_item(&a.counters[1], n_items, s_item, turn)) >= 0;) dq_item<T, D, HG>(a, item);
   finish_block(&a.counters[1]);
 }
 

@@ -242,9 +242,10 @@ template <typename T, int D, int HG, bool DYN>
 __global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char ring[fwd_ring_bytes<T, D>()];
   if constexpr (DYN) {
-    __shared__ int s_item;
+    __shared__ int s_item[2];
+    int turn = 0;
     const int n_items = a.n_tiles * (a.Hq / HG);
-    for (int item; (item = take_item(a.counters, n_items, &s_item)) >= 0;) fwd_item<T, D, HG>(a, item, ring);
+    for (int item; (item = take_item(a.counters, n_items, s_item, turn)) >= 0;) fwd_item<T, D, HG>(a, item, ring);
     finish_block(a.counters);
   } else {
     fwd_item<T, D, HG>(a, blockIdx.x, ring);

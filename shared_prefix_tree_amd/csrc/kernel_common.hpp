@@ -388,8 +388,13 @@ struct ItemCounters {
 };
 
 // the next item for this workgroup, or -1 when none is left (ends with a
-// barrier: the previous item is finished by every wave)
-__device__ inline int take_item(ItemCounters* ctr, int n_items, int* s_item) {
+// barrier: the previous item is finished by every wave).  The item is passed
+// through one of two LDS words, alternating between calls (`turn` is the
+// caller's, flipped here): a wave may still be reading one call's word while
+// thread 0 writes the next call's, and the word comes round again only after
+// a barrier that every wave reaches once it has read it.
+__device__ inline int take_item(ItemCounters* ctr, int n_items, int (&s_item)[2], int& turn) {
+  turn ^= 1;
   if (threadIdx.x == 0) {
     unsigned xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
@@ -402,10 +407,10 @@ __device__ inline int take_item(ItemCounters* ctr, int n_items, int* s_item) {
         break;
       }
     }
-    *s_item = item;
+    s_item[turn] = item;
   }
   __syncthreads();
-  return *s_item;
+  return s_item[turn];
 }
 
 __device__ inline void finish_block(ItemCounters* ctr) {
