@@ -406,7 +406,10 @@ def mamba(args):
         "ssm_fwd_tflops": round(f_fwd / (sf * 1e-3) / 1e12, 3), "ssm_bwd_tflops": round(f_bwd / (sbw * 1e-3) / 1e12, 3),
         "conv_fwd_gbs": round(conv_gbs[0], 1), "conv_bwd_gbs": round(conv_gbs[1], 1),
         "roofline": {"bound": "alu", "achieved": round(scan_tf, 3), "peak": 157.3, "unit": "TFLOP/s",
-                     "frac": round(scan_tf / 157.3, 4), "traffic": mamba_scan_traffic()},
+                     "frac": round(scan_tf / 157.3, 4), "traffic": mamba_scan_traffic(),
+                     "peak_basis": "published fp32 rate (matrix cores, and vector units with packed fp32); "
+                                   "the scan's vector passes are built without packed fp32 instructions, which "
+                                   "caps them at 78.6 = 256 CU x 4 SIMD x 16 lanes x 2 flops x 2.4 GHz"},
     }), flush=True)
 
 
