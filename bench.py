@@ -52,6 +52,20 @@ def measured_traffic(workload, kernel):
     return k.get("bytes_per_launch") if k else None
 
 
+def measured_sclk(workload, kernel):
+    """Shader clock (GHz) the kernel ran at in the committed rocprofv3 counter
+    run (GRBM_GUI_ACTIVE per XCD over the dispatch time), or None when it was
+    taken on different kernel sources."""
+    try:
+        rec = json.load(open(PROFILE_TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    k = rec.get("workloads", {}).get(workload, {}).get(kernel)
+    return k.get("observed_sclk_ghz") if k else None
+
+
 def mamba_scan_traffic():
     """HBM bytes of the Mamba scan kernels per step (one forward, one backward)
     from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE record, or None when it
@@ -612,6 +626,12 @@ def main():
             "traffic": traffic,
         },
     }
+    sclk = measured_sclk(w.name, dom)
+    if sclk:
+        # the published peak assumes 2.4 GHz; the same fraction against the
+        # clock rocprofv3 observed for this kernel
+        result["roofline"]["observed_sclk_ghz"] = sclk
+        result["roofline"]["frac_at_observed_sclk"] = round(achieved / (peak * sclk / 2.4), 4)
     if not args.no_cpu_baseline and w.backward:
         log("cpu baseline (float64 oracle, bounded sample)")
         result["cpu_baseline"] = cpu_baseline(w, topo, arrs, args.cpu_kv_heads)
