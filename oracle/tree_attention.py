@@ -54,6 +54,10 @@ Parity status (pins live in ``tests/test_oracle.py``):
   ``masked_dense_backward`` -- pinned: golden rational gradients, central
   finite differences, torch autograd on reconstructed sequences with one loss
   owner per token, sibling-permutation and fragment-copy invariance.
+  ``backward(..., out_dtype="bf16")`` (the row statistic taken from the
+  output as a bfloat16 caller stores it) -- pinned: a hand-worked three-token
+  gradient whose output 1/3 rounds to 171/512, and equality with the exact
+  mode wherever the output is representable.
 * ``pairs`` -- pinned: the tiny tree's count worked out by hand, and brute
   force (sum of |V(i)|).
 * ``ancestors`` / ``subtree_end`` / ``segment_pairs`` /
@@ -236,7 +240,14 @@ def forward(q, k, v, topo, scale=None, heads=None, segments=None):
     return out, lse
 
 
-def backward(q, k, v, dout, topo, scale=None, kv_heads=None, segments=None):
+def _round_bf16(x):
+    """x rounded to bfloat16 (through float32, to nearest even), as float64."""
+    b = np.ascontiguousarray(np.asarray(x, np.float64).astype(np.float32)).view(np.uint32)
+    b = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return b.view(np.float32).astype(np.float64)
+
+
+def backward(q, k, v, dout, topo, scale=None, kv_heads=None, segments=None, out_dtype=None):
     """Exact gradients (dq, dk, dv) of L = sum <dout, out>, float64.
 
     Each segment's contribution to its ancestors' dk/dv is added onto the
@@ -244,6 +255,14 @@ def backward(q, k, v, dout, topo, scale=None, kv_heads=None, segments=None):
     ``kv_heads`` restricts the work to those key/value heads (and their
     query heads); ``segments`` to the contributions of those query segments
     (a bounded sample); other entries stay 0.
+
+    The row statistic delta_i = sum_d dout[i,d] out[i,d] of the flash-style
+    backward equals sum_j P_ij dP_ij for the exact output.  A backward that
+    is handed the output as the caller stores it computes delta from that
+    stored value; ``out_dtype="bf16"`` reproduces this by rounding the
+    output to bfloat16 before delta (everything else stays exact).  Where
+    the softmax is nearly one-hot, dS = P (dP - delta) cancels and dq is
+    sensitive to that rounding.
     """
     parent, st, ln = _arrays(topo)
     T, Hq, D = q.shape
@@ -254,6 +273,10 @@ def backward(q, k, v, dout, topo, scale=None, kv_heads=None, segments=None):
     segments = range(len(parent)) if segments is None else segments
     heads = [h for g in kv_heads for h in range(g * G, (g + 1) * G)]
     out, lse = forward(q, k, v, topo, scale, heads=heads, segments=segments)
+    if out_dtype == "bf16":
+        out = _round_bf16(out)
+    elif out_dtype is not None:
+        raise ValueError(f"out_dtype {out_dtype!r}: None or 'bf16'")
     dq = np.zeros(q.shape)
     dk = np.zeros(k.shape)
     dv = np.zeros(v.shape)

@@ -297,6 +297,43 @@ def test_constant_values_give_constant_output():
     np.testing.assert_allclose(out, np.broadcast_to(v[:, :1], out.shape), atol=1e-13)
 
 
+def test_stored_bf16_output_gradient_by_hand():
+    # One segment of three tokens, D = 1, q = 0 (so every visible key has the
+    # same score), k = (1, 2, 4), v = (0, 0, 1), dout = (0, 0, 1).  Token 2
+    # sees all three keys with P = 1/3: out_2 = 1/3, dP_2j = v_j, and
+    #   dq_2 = sum_j P (v_j - delta) k_j = (4 - 7 delta) / 3.
+    # Exact delta = 1/3 gives 5/9; the bfloat16-stored output rounds 1/3 to
+    # 171/512 (0.0101010101... to 8 significant bits, to nearest), so
+    # delta = 171/512 and dq_2 = (4 - 1197/512) / 3 = 851/1536.
+    topo = Topology([-1], [0], [3])
+    q = np.zeros((3, 1, 1))
+    k = np.array([1.0, 2.0, 4.0]).reshape(3, 1, 1)
+    v = np.array([0.0, 0.0, 1.0]).reshape(3, 1, 1)
+    dout = np.array([0.0, 0.0, 1.0]).reshape(3, 1, 1)
+    dq, dk, dv = oracle.backward(q, k, v, dout, topo)
+    assert dq[2, 0, 0] == pytest.approx(5 / 9, abs=1e-15)
+    dq_b, dk_b, dv_b = oracle.backward(q, k, v, dout, topo, out_dtype="bf16")
+    assert dq_b[2, 0, 0] == pytest.approx(851 / 1536, abs=1e-15)
+    # dv does not use the row statistic; dk_j = sum_i dS_ij q_i = 0 (q = 0)
+    np.testing.assert_array_equal(dv_b, dv)
+    np.testing.assert_array_equal(dk_b, dk)
+
+
+def test_stored_bf16_output_is_exact_where_representable():
+    # Constant values that bfloat16 holds exactly make every output exact,
+    # so the stored-output mode must return the exact gradients bit for bit.
+    topo = small_forests(1, seed=8, max_tokens=40)[0]
+    T = topo.total_tokens
+    rng = np.random.default_rng(4)
+    q, k = rng.standard_normal((T, 2, 4)), rng.standard_normal((T, 1, 4))
+    v = np.broadcast_to(np.array([1.5, -2.0, 0.25, 3.0]), (T, 1, 4)).copy()
+    dout = rng.standard_normal((T, 2, 4))
+    exact = oracle.backward(q, k, v, dout, topo)
+    stored = oracle.backward(q, k, v, dout, topo, out_dtype="bf16")
+    for a, b in zip(exact, stored):
+        np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # reconstructed sequences vs torch SDPA (forward and one-owner backward)
 
