@@ -130,6 +130,17 @@ struct DkdvRing {
   static constexpr int value = sizeof(T) == 2 ? 4 : 3;  // fits P and the rings in LDS
 };
 
+// Wave priorities of the two dK/dV roles.  Both wavefronts of a SIMD (one
+// per role) are ready to issue most of the time; issue goes to the oldest
+// ready wavefront, which is the dV wave, so its dense vector work (the
+// exponentials of P) would hold back the dK wave's products.  Measured per
+// phase, the best order is: the dV wave's products first, then the dK
+// wave, then the dV wave's vector work, so the dK products run under the dV
+// wave's exponentials.
+constexpr int kPrioDvProducts = 2;
+constexpr int kPrioDk = 1;
+constexpr int kPrioDvVector = 0;
+
 template <typename T, int D>
 __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, int g, char* lds) {
   using M = Mfma<T>;
@@ -301,6 +312,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
   int dv_i0 = qbeg;  // first query of the dV waves' current step
   auto dv_iter = [&](int step, auto J) {
     constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
+    __builtin_amdgcn_s_setprio(kPrioDvProducts);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -310,6 +322,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) M::mma(t, ta.row(ks, j * TILE), kv[ks]);
     sched_pipeline<kLdsAhead, 2 * DB + KS, frag_reads<T>(true)>();
+    __builtin_amdgcn_s_setprio(kPrioDvVector);
     float x[16];
     row_stats(j * STATS, x);
     const int i0 = dv_i0;
@@ -336,6 +349,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
   for (int i = 0; i < 16; ++i) xd[i] = 0.f;
   auto dk_iter = [&](int step, auto J) {
     constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
+    __builtin_amdgcn_s_setprio(kPrioDk);
     const frag* pshr = &pshare[(step + 1) & 1][wblk * PBLK];
     const frag pf[2] = {pshr[lane], pshr[64 + lane]};
     // (the P reads go ahead of the software-pipelined fragment reads)
@@ -417,6 +431,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
     walk(std::true_type{});
   else
     walk(std::false_type{});
+  __builtin_amdgcn_s_setprio(0);
   wait_copies_barrier<0>();  // no copy in flight; the rings are free
 
   // fixed-order reduction of the two query halves, then one store per key:
@@ -611,6 +626,7 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
   int dv_i0 = qbeg;  // first query of the dV waves' current step
   auto dv_iter = [&](int step, auto J) {
     constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
+    __builtin_amdgcn_s_setprio(kPrioDvProducts);
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
@@ -624,6 +640,7 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) M::mma(t[qh], ta.row(ks, j * TILE + qh * 32 * RB), kv[ks]);
     sched_pipeline<kLdsAhead, 4 * DB + 2 * KS, frag_reads<T>(true)>();
+    __builtin_amdgcn_s_setprio(kPrioDvVector);
     const int i0 = dv_i0;
     dv_i0 = dv_i0 + BM > last ? qbeg : dv_i0 + BM;
 #pragma unroll
@@ -655,6 +672,7 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
     for (int i = 0; i < 16; ++i) xd[qh][i] = 0.f;
   auto dk_iter = [&](int step, auto J) {
     constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
+    __builtin_amdgcn_s_setprio(kPrioDk);
     frag pf[2][2];
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
@@ -747,6 +765,7 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
     walk(std::true_type{});
   else
     walk(std::false_type{});
+  __builtin_amdgcn_s_setprio(0);
   wait_copies_barrier<0>();  // no copy in flight when the workgroup ends
 
   if (key_valid) {
