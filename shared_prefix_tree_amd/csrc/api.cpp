@@ -185,9 +185,13 @@ int gcd(int a, int b) {
   return a;
 }
 
-// Query tile of the forward and dQ kernels (8 wavefronts): 32 query rows
-// per wavefront, HG heads of a key/value group side by side.
-int fwd_query_tile(int hg) { return 32 * (8 / hg); }
+// Query tile of the forward and dQ kernels: 32 query rows per wavefront,
+// HG heads of a key/value group side by side; 8 wavefronts per workgroup,
+// 12 in the forward for bf16 rows of 128 with head groups of 4.
+int fwd_query_tile(int hg, const tree_attn_shape* shape) {
+  const bool twelve = hg == 4 && shape->dtype == TREE_ATTN_BF16 && shape->head_dim == 128;
+  return 32 * ((twelve ? 12 : 8) / hg);
+}
 int dq_query_tile(int hg) { return 32 * (8 / hg); }
 
 // Shared argument checks of fwd/bwd.  Returns 0 or an error code.
@@ -223,7 +227,7 @@ int check_call(const char* fn, tree_attn_plan_t plan, const tree_attn_shape* sha
     return fail(TREE_ATTN_UNSUPPORTED, f + ": k and v are limited to 2^32 bytes");
   const int hg = gcd(shape->num_q_heads / shape->num_kv_heads, 4);
   int64_t grid_q = 0;
-  for (int tq : {fwd_query_tile(hg), dq_query_tile(hg)})
+  for (int tq : {fwd_query_tile(hg, shape), dq_query_tile(hg)})
     grid_q = std::max(grid_q, int64_t(plan->host.qtiles[qtile_index(tq)].size()) * (shape->num_q_heads / hg));
   const int64_t grid_k = int64_t(plan->host.ktiles.size()) * shape->num_kv_heads;  // >= the wide list's
   if (grid_q >= (int64_t(1) << 31) || grid_k >= (int64_t(1) << 31))
@@ -405,7 +409,7 @@ static int run_fwd(const char* fn, const void* q, const void* k, const void* v, 
   }
   const int G = shape->num_q_heads / shape->num_kv_heads;
   const int hg = gcd(G, 4);
-  const int ti = qtile_index(fwd_query_tile(hg));
+  const int ti = qtile_index(fwd_query_tile(hg, shape));
   FwdArgs a;
   a.counters = static_cast<ItemCounters*>(workspace);
   a.q = q;

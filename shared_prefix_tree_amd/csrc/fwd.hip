@@ -9,9 +9,10 @@
 // trajectories", section "Describe the solution you'd like": attention for
 // each query run against only its ancestor path).
 //
-// Work decomposition (one workgroup = 8 wavefronts, one per compute unit):
+// Work decomposition (one workgroup of W wavefronts per compute unit; W = 8,
+// or 12 for bf16 rows of 128 with head groups of 4, see below):
 //   * a workgroup owns a query tile of 32*NT tokens (inside one segment) and
-//     HG query heads of one key/value head (NT*HG = 8);
+//     HG query heads of one key/value head (NT*HG = W);
 //   * wave w holds 32 query rows (token sub-tile w / HG, head w % HG) with Q
 //     in registers;
 //   * the workgroup walks the segment's ancestor path as one virtual key
@@ -32,7 +33,13 @@
 //     row maximum at all, so most steps compute no maximum.  Numerator and
 //     denominator share the reference, so the result is exact;
 //   * the own-segment causal rule is "virtual key position <= query
-//     position", applied only on the last steps of the walk.
+//     position", applied only on the last steps of the walk;
+//   * with W = 12 (three wavefronts per SIMD instead of two, so a SIMD has a
+//     third instruction stream to issue from while the others wait), each
+//     step is taken as two 32-key halves (S, softmax and P V of one half,
+//     then of the other), which keeps a wavefront within the 168 registers
+//     that three per SIMD leave; waves 0-7 issue the copies, waves 8-11
+//     only compute.
 #include <type_traits>
 
 #include "kernel_common.hpp"
@@ -52,7 +59,7 @@ constexpr int fwd_ring_bytes() {
 }
 
 // One work item: query tile `tile_rank` of the plan's list, head group `group`.
-template <typename T, int D, int HG>
+template <typename T, int D, int HG, int W>
 __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring) {
   using M = Mfma<T>;
   using frag = typename M::frag;
@@ -64,7 +71,9 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
   constexpr int TILE = BN * RB;           // bytes of one 64-row tile
   constexpr int kAhead = kFwdRing - 1;
   static_assert(RB == 128 || RB == 256, "128- or 256-byte rows");
-  static_assert(8 % HG == 0, "eight wavefronts per workgroup");
+  static_assert(W == 8 || W == 12, "8 or 12 wavefronts per workgroup");
+  static_assert(W % HG == 0, "whole head groups per workgroup");
+  constexpr bool kCopier8 = W == 8;  // (else only waves 0-7 issue copies)
   static_assert(kFwdRing == 4, "the walk is unrolled over four ring slots");
 
   // `ring`: the K ring then the V ring (each 64 KB, so a slot offset fits an
@@ -112,7 +121,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
   // the last step into their (idle) slot so every wave issues the same
   // number of copies per step
   auto issue = [&](int step) {
-    copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kFwdRing) * TILE);
+    if (kCopier8 || wave < 8) copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kFwdRing) * TILE);
   };
   TileAddr<T, D> ka, va;  // per-lane read addresses in slot 0 of each ring
   ka.init(lds_addr(ring), lane);
@@ -190,13 +199,70 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
         for (int hh = 0; hh < 2; ++hh) M::mma(o[db], va.tr(db, off + (kb * 32 + 16 * hh) * RB), pf[kb][hh]);
     sched_pipeline<kLdsAhead, 4 * DB, frag_reads<T>(true)>();
   };
+  // W = 12: the same step as two 32-key halves (fewer live registers)
+  auto compute_halves = [&](int v0, auto B) {
+    constexpr int off = decltype(B)::value * TILE;
+    const bool diag = v0 + BN - 1 > wave_pos0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) M::mma(s, ka.row(ks, off + kb * 32 * RB), qf[ks]);
+      sched_pipeline<kLdsAhead, KS, frag_reads<T>(false)>();
+      if (diag) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (v0 + kb * 32 + c_row(i, half) > qpos) s[i] = -INFINITY;
+      }
+      float p[16];
+      float rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m));
+        rs += p[i];
+      }
+      if (__any(!(rs <= kLazyMax))) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+        mx = max_halves(mx) * c;
+        const float mnew = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        l *= alpha;
+        m = mnew;
+        rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m));
+          rs += p[i];
+        }
+      }
+      l += rs;
+      frag pf[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = to_elem<T>(p[i]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) M::mma(o[db], va.tr(db, off + (kb * 32 + 16 * hh) * RB), pf[hh]);
+      sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
+    }
+  };
   auto body = [&](int step, auto B) {
     // this wave's copies of `step` are done once only the kAhead - 1 newer
     // steps' copies may be in flight; after the barrier every wave's are,
     // and nobody reads the slot refilled next (last read at step - 1)
-    wait_copies_barrier<(kAhead - 1) * path_copies(RB)>();
+    if (kCopier8 || wave < 8)
+      wait_copies_barrier<(kAhead - 1) * path_copies(RB)>();
+    else
+      wait_copies_barrier<0>();
     issue(step + kAhead);
-    compute(step * BN, B);
+    if constexpr (W == 12)
+      compute_halves(step * BN, B);
+    else
+      compute(step * BN, B);
   };
 
 #pragma unroll
@@ -238,30 +304,38 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
 // caller's workspace -- one workgroup per CU taking items until none is left
 // (the hand-out of the backward walks: XCD-local lists first, then the
 // other XCDs' remaining items), which absorbs the XCDs' clock differences.
-template <typename T, int D, int HG, bool DYN>
-__global__ __launch_bounds__(512, 1) void tree_attn_fwd_kernel(FwdArgs a) {
+template <typename T, int D, int HG, bool DYN, int W>
+__global__ __launch_bounds__(64 * W, 1) void tree_attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char ring[fwd_ring_bytes<T, D>()];
   if constexpr (DYN) {
     __shared__ int s_item[2];
     int turn = 0;
     const int n_items = a.n_tiles * (a.Hq / HG);
-    for (int item; (item = take_item(a.counters, n_items, s_item, turn)) >= 0;) fwd_item<T, D, HG>(a, item, ring);
+    for (int item; (item = take_item(a.counters, n_items, s_item, turn)) >= 0;) fwd_item<T, D, HG, W>(a, item, ring);
     finish_block(a.counters);
   } else {
-    fwd_item<T, D, HG>(a, blockIdx.x, ring);
+    fwd_item<T, D, HG, W>(a, blockIdx.x, ring);
   }
 }
 
 unsigned persistent_grid(unsigned n_items);
 
+// wavefronts per workgroup: 12 for bf16 rows of 128 with head groups of 4
+// (96-query tiles), else 8
+template <typename T, int D, int HG>
+constexpr int fwd_waves() {
+  return sizeof(T) == 2 && D == 128 && HG == 4 ? 12 : 8;
+}
+
 template <typename T, int D, int HG>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  constexpr int W = fwd_waves<T, D, HG>();
   const unsigned n_items = (unsigned)a.n_tiles * (unsigned)(a.Hq / HG);
   if (a.counters)
-    hipLaunchKernelGGL((tree_attn_fwd_kernel<T, D, HG, true>), dim3(persistent_grid(n_items)), dim3(512), 0, stream,
-                       a);
+    hipLaunchKernelGGL((tree_attn_fwd_kernel<T, D, HG, true, W>), dim3(persistent_grid(n_items)), dim3(64 * W), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((tree_attn_fwd_kernel<T, D, HG, false>), dim3(n_items), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((tree_attn_fwd_kernel<T, D, HG, false, W>), dim3(n_items), dim3(64 * W), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@
 //     [virt, virt + len) of the segment's reconstructed root-to-leaf
 //     sequence, so the own-segment causal rule becomes "virtual key
 //     position <= query position";
-//   * query tiles (32/64/128/256 tokens, never crossing a segment) with the
+//   * query tiles (32/64/128/256/96 tokens, never crossing a segment) with the
 //     position of their first token in that sequence;
 //   * key tiles (64 tokens, never crossing a segment) with the end of the
 //     contiguous range of queries that see them.  In a DFS pre-order every
@@ -46,12 +46,14 @@ struct Span {
   int32_t pad;
 };
 
-constexpr int kNumQTileSizes = 4;
-constexpr int kQTileSizes[kNumQTileSizes] = {32, 64, 128, 256};
+constexpr int kNumQTileSizes = 5;
+constexpr int kQTileSizes[kNumQTileSizes] = {32, 64, 128, 256, 96};
 constexpr int kKTile = 64;       // key tiles of the fp32 dK/dV pass
 constexpr int kKTileWide = 128;  // key tiles of the bf16 dK/dV pass
 
-inline int qtile_index(int tq) { return tq == 32 ? 0 : tq == 64 ? 1 : tq == 128 ? 2 : tq == 256 ? 3 : -1; }
+inline int qtile_index(int tq) {
+  return tq == 32 ? 0 : tq == 64 ? 1 : tq == 128 ? 2 : tq == 256 ? 3 : tq == 96 ? 4 : -1;
+}
 
 struct HostPlan {
   int32_t T = 0, S = 0, num_roots = 0, max_depth = 0, max_spans = 0;
