@@ -306,6 +306,11 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
 // other XCDs' remaining items), which absorbs the XCDs' clock differences.
 template <typename T, int D, int HG, bool DYN, int W>
 __global__ __launch_bounds__(64 * W, 1) void tree_attn_fwd_kernel(FwdArgs a) {
+  // With three wavefronts per SIMD, issue ties go to the oldest, and the
+  // youngest third (waves 8-11, which issue no copies) finished each step
+  // last while the oldest waited at the barrier; a higher priority for it
+  // evens the three out (agent tree -1.4 %).
+  if (W == 12 && __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= 8) __builtin_amdgcn_s_setprio(1);
   __shared__ __attribute__((aligned(16))) char ring[fwd_ring_bytes<T, D>()];
   if constexpr (DYN) {
     __shared__ int s_item[2];
