@@ -22,7 +22,7 @@ import pytest
 
 import oracle
 from tests.parity_util import TOL, log, oracle_inputs, rel_l2, tensor_error, to_host, to_torch
-from workloads import WORKLOADS, Topology, comb, f32_to_bf16, long_chain, random_forest, tiny_tree
+from workloads import WORKLOADS, Topology, agent_tree, comb, f32_to_bf16, long_chain, random_forest, tiny_tree
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -497,6 +497,30 @@ def test_stream_ordered_plan_upload_matches_the_synchronous_one():
     for r in results:
         for a, b_ in zip((out0, lse0, *g0), r):
             assert torch.equal(a, b_)
+
+
+def test_workspace_forward_many_items_per_workgroup():
+    """The workspace forward with many work items per workgroup (each
+    persistent workgroup takes item after item through the counters): bitwise
+    the plain forward (one workgroup per item) on a forest of short paths (one-
+    to five-step items) and on a 32,768-token agent tree (about 3,000 items of
+    1 to 150 steps over 256 workgroups)."""
+    sp = lib()
+    rng = np.random.default_rng(46)
+    topos = [random_forest(rng, max_tokens=24000, max_len=120, max_depth=2, p_new_root=0.5),
+             agent_tree(rng, total=32768)]
+    for n, topo in enumerate(topos):
+        arrs = make_inputs(rng, topo.total_tokens, 32, 8, 128, "bf16")
+        t = {k: to_torch(v, "bf16", "cuda:0") for k, v in arrs.items()}
+        plan = sp.Plan.from_topology(topo)
+        ref = sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan)
+        ws = torch.full((sp.fwd_workspace_bytes(plan, t["q"], t["k"]),), 0x5A, dtype=torch.uint8, device="cuda:0")
+        for _ in range(2):
+            got = sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+        log(f"workspace forward, many items, case {n}: T={topo.total_tokens} "
+            f"segments={len(topo.seg_len)} bitwise equal")
 
 
 @pytest.mark.parametrize("dtype,D,Hq,Hkv", [("bf16", 128, 8, 2), ("bf16", 64, 4, 4), ("fp32", 64, 8, 1)])
