@@ -768,9 +768,18 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
   __builtin_amdgcn_s_setprio(0);
   wait_copies_barrier<0>();  // no copy in flight when the workgroup ends
 
-  if (key_valid) {
+  const float mul = dk_role ? a.scale : 1.f;
+  if constexpr (RB == 256) {
+    // whole-row stores of the wavefront's 32 keys through its 32-row block
+    // of the (now idle) rings
+    store_block_rows<T, D>(acc, mul, lds_addr(lds) + unsigned(wave) * 32 * RB, [&](int r) {
+      const int jk = tile.k0 + kq * 32 + r;
+      return jk < tile.k0 + tile.nk
+                 ? reinterpret_cast<char*>(dk_role ? a.dk : a.dv) + ((size_t)jk * a.Hkv + g) * RB
+                 : nullptr;
+    });
+  } else if (key_valid) {
     T* op = static_cast<T*>(dk_role ? a.dk : a.dv) + ((size_t)jkey * a.Hkv + g) * D;
-    const float mul = dk_role ? a.scale : 1.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -960,7 +969,15 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, int item) {
   }
   wait_copies_barrier<0>();  // no copy in flight when the workgroup ends
 
-  if (qrow < tile.nq) {
+  if constexpr (RB == 256) {
+    // whole-row stores through this wavefront's 32-row block of the (now
+    // idle) ring
+    store_block_rows<T, D>(dq, a.scale, lds_addr(ring) + unsigned(wave) * 32 * RB, [&](int r) {
+      return ts * 32 + r < tile.nq
+                 ? reinterpret_cast<char*>(a.dq) + ((size_t)(tile.q0 + ts * 32 + r) * a.Hq + h) * RB
+                 : nullptr;
+    });
+  } else if (qrow < tile.nq) {
     T* dqp = static_cast<T*>(a.dq) + ((size_t)(tile.q0 + qrow) * a.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)

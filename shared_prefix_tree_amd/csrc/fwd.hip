@@ -284,45 +284,15 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
 
   l = sum_halves(l);
   if constexpr (RB == 256) {
-    // The output rows go through this wavefront's 32-row block of the
-    // (now idle) ring, so each store writes whole rows: written straight
-    // from the C layout, every store instruction would put 16 bytes into
-    // each of 32 rows a head-row apart (32 partial cache lines).  Rows are
-    // swizzled like the tiles (two-way bank conflicts on the writes, none
-    // on the row reads).
-    const float inv = 1.f / l;
-    const unsigned blk = lds_addr(ring) + unsigned(wave) * 32 * RB;
-    // (lane values taken afresh here, so none of this is computed ahead of
-    // the walk and held in registers through it)
-    int ln;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-    const int col = ln & 31, half = ln >> 5;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        // 16 bytes per lane of (db, grp): 4 elements (bf16) or their
-        // halves (fp32 writes the pair of 8-byte pieces)
-        quad t4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t4[e] = to_elem<T>(o[db][grp * 4 + e] * inv);
-        constexpr int EB = 4 * int(sizeof(T));  // bytes of one lane's piece
-        const int byte = (db * 32 + grp * 8 + half * 4) * int(sizeof(T));
-        const unsigned at = blk + col * RB + (((byte >> 4) ^ swz<RB>(col)) << 4) + (byte & 15);
-        *reinterpret_cast<__attribute__((address_space(3))) quad*>((size_t)at) = t4;
-        static_assert(EB == 8 || EB == 16, "8- or 16-byte pieces");
-      }
-    const int r16 = ln >> 4, ch = ln & 15;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = 4 * j + r16;
-      const u32x4 v4 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          (size_t)(blk + row * RB + ((ch ^ swz<RB>(row)) << 4)));
-      if (ts * 32 + row < tile.nq)
-        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.out) +
-                                  (((size_t)(tile.q0 + ts * 32 + row) * a.Hq + h) * RB) + ch * 16) = v4;
-    }
-    if (ts * 32 + col < tile.nq && half == 0)
+    // whole-row stores through this wavefront's 32-row block of the (now
+    // idle) ring
+    store_block_rows<T, D>(o, 1.f / l, lds_addr(ring) + unsigned(wave) * 32 * RB, [&](int r) {
+      return ts * 32 + r < tile.nq
+                 ? reinterpret_cast<char*>(a.out) + ((size_t)(tile.q0 + ts * 32 + r) * a.Hq + h) * RB
+                 : nullptr;
+    });
+    const int ln = lane_now(), col = ln & 31;
+    if (ts * 32 + col < tile.nq && ln < 32)
       a.lse[(size_t)h * a.T + tile.q0 + ts * 32 + col] = m * kLn2 + __logf(l);
   } else if (qrow < tile.nq) {
     const float inv = 1.f / l;

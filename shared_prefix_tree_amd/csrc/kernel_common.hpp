@@ -353,6 +353,54 @@ __device__ inline T to_elem(float x) {
   return T(x);
 }
 
+// This lane's index in its wavefront, computed where it is used: an opaque
+// instruction pair, so values derived from it are not computed ahead of a
+// loop and held in registers through it.
+__device__ inline int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// Writes a wavefront's 32 x D block, held in the C layout (lane l: block row
+// l % 32; acc[db][i]: column 32 db + c_row(i, l / 32)), times `mul`, to 32
+// global rows of RB = 256 bytes, through a 32-row LDS block `blk` (byte
+// address; free, and read by no other wavefront), so that every store
+// writes whole rows.  Straight from the C layout each store instruction
+// would put 8 or 16 bytes into each of 32 rows a head-row apart: 32 partial
+// cache lines.  The block is swizzled like the tiles (two-way bank
+// conflicts on the writes, none on the row reads).  `row_ptr(r)` is the
+// global address of block row r; rows with row_ptr(r) == nullptr are
+// skipped.
+template <typename T, int D, class RowPtr>
+__device__ inline void store_block_rows(const f32x16 (&acc)[D / 32], float mul, unsigned blk, RowPtr row_ptr) {
+  constexpr int RB = D * int(sizeof(T));
+  static_assert(RB == 256, "256-byte rows");
+  using quad = typename Mfma<T>::quad;
+  const int ln = lane_now();
+  const int col = ln & 31, half = ln >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      quad t4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t4[e] = to_elem<T>(acc[db][grp * 4 + e] * mul);
+      const int byte = (db * 32 + grp * 8 + half * 4) * int(sizeof(T));
+      const unsigned at = blk + col * RB + (((byte >> 4) ^ swz<RB>(col)) << 4) + (byte & 15);
+      *reinterpret_cast<__attribute__((address_space(3))) quad*>((size_t)at) = t4;
+    }
+  const int r16 = ln >> 4, ch = ln & 15;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 4 * j + r16;
+    const u32x4 v4 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+        (size_t)(blk + row * RB + ((ch ^ swz<RB>(row)) << 4)));
+    char* p = reinterpret_cast<char*>(row_ptr(row));
+    if (p) *reinterpret_cast<u32x4*>(p + ch * 16) = v4;
+  }
+}
+
 // Work-item decode.  Workgroups are dispatched round-robin over the 8 XCDs
 // (each with its own L2), so block b runs on XCD b % 8.  When the head
 // groups split evenly over the XCDs, each XCD gets a contiguous range of
