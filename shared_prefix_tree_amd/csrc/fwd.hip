@@ -151,13 +151,14 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
     // the fast path is at most kLazyMax, so O and l stay far from overflow,
     // and numerator and denominator always share one reference.
     float p[2][16];
-    float rs = 0.f;
+    // (the sum starts from the first term, not from an addition to 0)
+    float rs;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         p[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -m));
-        rs += p[kb][i];
+        rs = kb == 0 && i == 0 ? p[0][0] : rs + p[kb][i];
       }
     if (__any(!(rs <= kLazyMax))) {
       float mx = -INFINITY;
@@ -172,13 +173,12 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       l *= alpha;
       m = mnew;
-      rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           p[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -m));
-          rs += p[kb][i];
+          rs = kb == 0 && i == 0 ? p[0][0] : rs + p[kb][i];
         }
     }
     l += rs;
@@ -215,11 +215,12 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
           if (v0 + kb * 32 + c_row(i, half) > qpos) s[i] = -INFINITY;
       }
       float p[16];
-      float rs = 0.f;
+      // (the sum starts from the first term, not from an addition to 0)
+      float rs;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m));
-        rs += p[i];
+        rs = i == 0 ? p[0] : rs + p[i];
       }
       if (__any(!(rs <= kLazyMax))) {
         float mx = -INFINITY;
@@ -232,11 +233,10 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
         l *= alpha;
         m = mnew;
-        rs = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m));
-          rs += p[i];
+          rs = i == 0 ? p[0] : rs + p[i];
         }
       }
       l += rs;
