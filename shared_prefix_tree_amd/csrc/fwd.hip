@@ -100,10 +100,26 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
   const int n_steps = (kv_len + BN - 1) / BN;
   const float c = a.scale * kLog2e;
 
-  // Q is loaded first; its wait comes after the first copies are issued, so
-  // both latencies overlap
+  // Q: with 12 wavefronts, copied whole-row into ring slots 1-3 (idle until
+  // the first steps' copies; K ring for waves 0-5, V ring for waves 6-11)
+  // and read from there; else loaded first, its wait coming after the first
+  // copies are issued, so both latencies overlap
+  constexpr bool kStageQ = W == 12 && RB == 256;
   frag qf[KS];
-  {
+  unsigned qblk = 0;
+  if constexpr (kStageQ) {
+    qblk = wave < 6 ? lds_addr(ring) + TILE + unsigned(wave) * 32 * RB
+                    : lds_addr(ring + kFwdRing * TILE) + TILE + unsigned(wave - 6) * 32 * RB;
+    const char* qb = static_cast<const char*>(a.q) + ((size_t)tile.q0 * a.Hq + h) * RB;
+    const unsigned rstride = unsigned(a.Hq) * RB;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = 4 * r + (lane >> 4);
+      const unsigned voff = unsigned(min(ts * 32 + row, tile.nq - 1)) * rstride +
+                            unsigned(((lane & 15) ^ swz<RB>(row)) * 16);
+      copy16_async(qb, voff, qblk + r * 1024);
+    }
+  } else {
     const T* p = static_cast<const T*>(a.q) + ((size_t)qtok * a.Hq + h) * D + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = load_frag<T>(p + ks * 16);
@@ -265,10 +281,26 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
       compute(step * BN, B);
   };
 
+  if constexpr (kStageQ) {
+    // step 0's copies with the Q rows; Q into registers; then steps 1-2
+    // into the slots the Q rows leave
+    issue(0);
+    wait_copies_barrier<0>();
 #pragma unroll
-  for (int st = 0; st < kAhead; ++st) issue(st);
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = *reinterpret_cast<const __attribute__((address_space(3))) frag*>(
+          (size_t)(qblk + col * RB + (((2 * ks + half) ^ swz<RB>(col)) << 4)));
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
+    for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
+    wait_copies_barrier<0>();
+    issue(1);
+    issue(2);
+  } else {
+#pragma unroll
+    for (int st = 0; st < kAhead; ++st) issue(st);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
+  }
   // unrolled over the ring slots so every LDS offset is a constant
   for (int step = 0;; step += kFwdRing) {
     body(step, Slot<0>{});
