@@ -68,7 +68,6 @@ struct DevicePlan {
   int device = -1;
   void* block = nullptr;   // one allocation holding every table below
   void* staged = nullptr;  // pinned host copy of `block` (stream-ordered uploads only)
-  int32_t* span_ptr = nullptr;
   Span* spans = nullptr;
   QTile* qtiles[kNumQTileSizes] = {};
   KTile* ktiles = nullptr;
@@ -114,14 +113,13 @@ hipError_t upload_plan(const HostPlan& h, DevicePlan& d, const hipStream_t* stre
     size_t bytes;
     void** dst;
   };
-  Part parts[4 + kNumQTileSizes] = {
-      {h.span_ptr.data(), h.span_ptr.size() * sizeof(int32_t), reinterpret_cast<void**>(&d.span_ptr)},
+  Part parts[3 + kNumQTileSizes] = {
       {h.spans.data(), h.spans.size() * sizeof(Span), reinterpret_cast<void**>(&d.spans)},
       {h.ktiles.data(), h.ktiles.size() * sizeof(KTile), reinterpret_cast<void**>(&d.ktiles)},
       {h.ktiles_wide.data(), h.ktiles_wide.size() * sizeof(KTile), reinterpret_cast<void**>(&d.ktiles_wide)},
   };
   for (int t = 0; t < kNumQTileSizes; ++t)
-    parts[4 + t] = {h.qtiles[t].data(), h.qtiles[t].size() * sizeof(QTile), reinterpret_cast<void**>(&d.qtiles[t])};
+    parts[3 + t] = {h.qtiles[t].data(), h.qtiles[t].size() * sizeof(QTile), reinterpret_cast<void**>(&d.qtiles[t])};
   size_t total = 0;
   for (const Part& p : parts) total += align16(p.bytes);
   std::vector<unsigned char> pageable;
@@ -361,10 +359,20 @@ int tree_attn_plan_export(tree_attn_plan_t plan, int32_t which, int32_t* buf, in
       src = reinterpret_cast<const int32_t*>(h.spans.data());
       n = int64_t(h.spans.size()) * 4;
       break;
-    case TREE_ATTN_EXPORT_Q_TILES:
-      src = reinterpret_cast<const int32_t*>(h.qtiles[0].data());
+    case TREE_ATTN_EXPORT_Q_TILES: {
+      // the first four fields of each record (the rest repeat the spans)
       n = int64_t(h.qtiles[0].size()) * 4;
-      break;
+      *count = n;
+      if (buf) {
+        if (cap < n) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan_export: buffer too small");
+        for (size_t i = 0; i < h.qtiles[0].size(); ++i) {
+          const QTile& t = h.qtiles[0][i];
+          const int32_t rec[4] = {t.q0, t.nq, t.seg, t.pos0};
+          std::memcpy(buf + 4 * i, rec, sizeof(rec));
+        }
+      }
+      return TREE_ATTN_OK;
+    }
     case TREE_ATTN_EXPORT_KV_TILES:
       src = reinterpret_cast<const int32_t*>(h.ktiles.data());
       n = int64_t(h.ktiles.size()) * 4;
@@ -418,7 +426,6 @@ static int run_fwd(const char* fn, const void* q, const void* k, const void* v, 
   a.out = out;
   a.lse = lse;
   a.tiles = plan->dev.qtiles[ti];
-  a.span_ptr = plan->dev.span_ptr;
   a.spans = plan->dev.spans;
   a.n_tiles = int32_t(plan->host.qtiles[ti].size());
   a.T = shape->total_tokens;
@@ -518,7 +525,6 @@ int prep_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   // as large, so wider tiles would not fit LDS)
   const bool wide = shape->dtype == TREE_ATTN_BF16;
   a.ktiles = wide ? plan->dev.ktiles_wide : plan->dev.ktiles;
-  a.span_ptr = plan->dev.span_ptr;
   a.spans = plan->dev.spans;
   a.n_qtiles = int32_t(plan->host.qtiles[ti].size());
   a.n_ktiles = int32_t(wide ? plan->host.ktiles_wide.size() : plan->host.ktiles.size());

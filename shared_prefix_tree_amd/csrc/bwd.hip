@@ -892,7 +892,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, int item) {
   // (per-lane copy offsets: this walk has no vector registers to spare)
   PathCopier<T, RB, false> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv,
                                   lds_addr(ring), lds_addr(ring + kDqRing * TILE),
-                                  a.spans + a.span_ptr[tile.seg], kv_len, wave, lane);
+                                  a.spans, tile, kv_len, wave, lane);
   auto issue = [&](int step) {
     copier.issue(min(step, n_steps - 1) * BN, (unsigned)(step % kDqRing) * TILE);
   };

@@ -131,7 +131,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
   float m = -INFINITY, l = 0.f;
 
   PathCopier<T, RB> copier(static_cast<const T*>(a.k), static_cast<const T*>(a.v), g, a.Hkv, lds_addr(ring),
-                           lds_addr(ring + kFwdRing * TILE), a.spans + a.span_ptr[tile.seg], kv_len, wave,
+                           lds_addr(ring + kFwdRing * TILE), a.spans, tile, kv_len, wave,
                            lane);
   // step `step` goes to slot step % kFwdRing; steps past the end re-copy
   // the last step into their (idle) slot so every wave issues the same

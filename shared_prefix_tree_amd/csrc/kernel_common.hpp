@@ -486,9 +486,10 @@ __device__ inline Span load_span(const Span* p) {
 // tile of the K ring and its V rows to the same slot of the V ring
 // (row-major, swizzled).  Waves 0-3 copy K rows, waves 4-7 V rows, 16 rows
 // each; one copy instruction moves 1 KB = 1024 / RB rows, so every wave
-// issues exactly path_copies(RB) copies per step.  The span records are read
-// from the plan in global memory with scalar loads, one at a time, so a
-// path may have any number of spans and nothing is staged before the walk.
+// issues exactly path_copies(RB) copies per step.  The first span record
+// comes with the query tile's record; later ones are read from the plan in
+// global memory with scalar loads, one at a time, so a path may have any
+// number of spans and nothing is staged before the walk.
 // A step inside one span (the common case: spans are usually much longer
 // than 64) takes its rows from one base; otherwise the wave visits the spans
 // the step overlaps in order and each lane takes its row from the one that
@@ -516,8 +517,10 @@ struct PathCopier {
   int cphys, clen, cvirt;  // spans[ucur], kept in scalar registers
   int kv_len;          // positions on the path
 
-  __device__ PathCopier(const T* k, const T* v, int g, int Hkv, unsigned k_ring, unsigned v_ring, const Span* sp,
-                        int len, int wave, int lane) {
+  // spans: the plan's span list; tile: the query tile whose ancestor path
+  // is walked (it names the path's first span and holds a copy of it)
+  __device__ PathCopier(const T* k, const T* v, int g, int Hkv, unsigned k_ring, unsigned v_ring,
+                        const Span* all_spans, const QTile& tile, int len, int wave, int lane) {
     base = (wave < 4 ? k : v) + (size_t)g * RB / sizeof(T);
     row_bytes = (unsigned)Hkv * RB;
     const int r0 = (wave & 3) * 16;
@@ -528,13 +531,12 @@ struct PathCopier {
       chunk[r] = unsigned(((lane % LPR) ^ swz<RB>(row + RPC * r)) * 16);
       if constexpr (SCALAR_BASE) lane_off[r] = unsigned(row + RPC * r) * row_bytes + chunk[r];
     }
-    spans = sp;
+    spans = all_spans + tile.span0;
     ucur = 0;
     kv_len = len;
-    const Span s0 = load_span(sp);
-    cphys = s0.phys;
-    clen = s0.len;
-    cvirt = s0.virt;
+    cphys = tile.phys0;
+    clen = tile.len0;
+    cvirt = tile.virt0;
   }
 
   // positions [v0, v0 + 64) into the ring slot at byte offset `slot`
@@ -593,7 +595,6 @@ struct FwdArgs {
   void* out;
   float* lse;
   const QTile* tiles;
-  const int32_t* span_ptr;
   const Span* spans;
   int32_t n_tiles;
   int32_t T, Hq, Hkv, G;
@@ -614,7 +615,6 @@ struct BwdArgs {
   ItemCounters* counters;  // [0]: dK/dV pass, [1]: dQ pass (in the workspace)
   const QTile* qtiles;
   const KTile* ktiles;
-  const int32_t* span_ptr;
   const Span* spans;
   int32_t n_qtiles, n_ktiles;
   int32_t T, Hq, Hkv, G;

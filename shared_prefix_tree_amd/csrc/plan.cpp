@@ -134,7 +134,11 @@ bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int3
       // the run's tokens of this segment, [o0, o1) from its start
       const int32_t o0 = std::max(0, q_begin - seg_start[s]), o1 = std::min(seg_len[s], q_end - seg_start[s]);
       for (int32_t o = o0; o < o1; o += tq)
-        tiles.push_back(QTile{seg_start[s] + o, std::min(tq, o1 - o), s, p.prefix[s] + o});
+        {
+        const Span& f = p.spans[p.span_ptr[s]];
+        tiles.push_back(QTile{seg_start[s] + o, std::min(tq, o1 - o), s, p.prefix[s] + o, p.span_ptr[s], f.phys, f.len,
+                              f.virt});
+      }
     }
     std::stable_sort(tiles.begin(), tiles.end(), [](const QTile& a, const QTile& b) {
       return int64_t(a.pos0) + a.nq > int64_t(b.pos0) + b.nq;

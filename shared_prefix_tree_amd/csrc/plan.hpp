@@ -30,7 +30,12 @@ struct QTile {
   int32_t nq;    // tokens in the tile (<= tile size)
   int32_t seg;   // segment of every token in the tile
   int32_t pos0;  // position of q0 in its reconstructed sequence
+  // the segment's first span (its index in the span list, then a copy of
+  // phys, len, virt), so a walk starts from this one record
+  int32_t span0;
+  int32_t phys0, len0, virt0;
 };
+static_assert(sizeof(QTile) == 32, "one 32-byte record per query tile");
 
 struct KTile {
   int32_t k0;    // first key token
