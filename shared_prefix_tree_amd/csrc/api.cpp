@@ -240,6 +240,20 @@ int check_call(const char* fn, tree_attn_plan_t plan, const tree_attn_shape* sha
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// the first four int32 fields of each 32-byte tile record (the rest hold
+// what the kernels need with the tile: a first span, a segment end)
+template <class Tile>
+int export_heads(const std::vector<Tile>& tiles, int32_t* buf, int64_t cap, int64_t* count) {
+  static_assert(sizeof(Tile) == 8 * sizeof(int32_t), "32-byte tile records");
+  const int64_t n = int64_t(tiles.size()) * 4;
+  *count = n;
+  if (buf) {
+    if (cap < n) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan_export: buffer too small");
+    for (size_t i = 0; i < tiles.size(); ++i) std::memcpy(buf + 4 * i, &tiles[i], 4 * sizeof(int32_t));
+  }
+  return TREE_ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -359,24 +373,10 @@ int tree_attn_plan_export(tree_attn_plan_t plan, int32_t which, int32_t* buf, in
       src = reinterpret_cast<const int32_t*>(h.spans.data());
       n = int64_t(h.spans.size()) * 4;
       break;
-    case TREE_ATTN_EXPORT_Q_TILES: {
-      // the first four fields of each record (the rest repeat the spans)
-      n = int64_t(h.qtiles[0].size()) * 4;
-      *count = n;
-      if (buf) {
-        if (cap < n) return fail(TREE_ATTN_INVALID_ARGUMENT, "tree_attn_plan_export: buffer too small");
-        for (size_t i = 0; i < h.qtiles[0].size(); ++i) {
-          const QTile& t = h.qtiles[0][i];
-          const int32_t rec[4] = {t.q0, t.nq, t.seg, t.pos0};
-          std::memcpy(buf + 4 * i, rec, sizeof(rec));
-        }
-      }
-      return TREE_ATTN_OK;
-    }
+    case TREE_ATTN_EXPORT_Q_TILES:  // the first four fields of each record
+      return export_heads(h.qtiles[0], buf, cap, count);
     case TREE_ATTN_EXPORT_KV_TILES:
-      src = reinterpret_cast<const int32_t*>(h.ktiles.data());
-      n = int64_t(h.ktiles.size()) * 4;
-      break;
+      return export_heads(h.ktiles, buf, cap, count);
     case TREE_ATTN_EXPORT_SEG_DEPTH:
       src = h.depth.data();
       n = h.S;

@@ -534,11 +534,20 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) settle(kv[ks]);
 
-  // the queries walked: those of the run that see the tile
-  const int qbeg = max(tile.k0, a.q_begin), qend = min(tile.qend, a.q_end);
-  const int nblk = qend > qbeg ? (qend - qbeg + BM - 1) / BM : 0;
-  const int n_steps = a.G * nblk;
-  const int last = qend - 1;
+  // The queries walked: those of the run that see the tile, in two ranges,
+  // each for every head of the group in turn.  First the segment's
+  // descendants [send, qend): the same range for every tile of the segment,
+  // so tiles of one segment walked at the same time on one XCD stay on the
+  // same rows, which its L2 then serves once.  Then the tile's own segment
+  // [qbeg, send), whose length differs from tile to tile.  An empty first
+  // range is dropped.  (qend is clamped to qbeg when no query of the run
+  // sees the tile, so neither range has a negative length.)
+  const int qbeg = max(tile.k0, a.q_begin), qend = max(min(tile.qend, a.q_end), qbeg);
+  const int split = min(max(tile.send, qbeg), qend);
+  const bool first_empty = split >= qend;
+  const int lo0 = first_empty ? qbeg : split, hi0 = qend;
+  const int lo1 = first_empty ? qend : qbeg, hi1 = first_empty ? qend : split;
+  const int n_steps = a.G * ((hi0 - lo0 + BM - 1) / BM + (hi1 - lo1 + BM - 1) / BM);
   if (n_steps == 0) {  // no query of the run sees the tile: zero gradients
     if (key_valid) {
       T* op = static_cast<T*>(dk_role ? a.dk : a.dv) + ((size_t)jkey * a.Hkv + g) * D;
@@ -567,9 +576,9 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
     cchunk[r] = (((lane % (RB / 16)) ^ swz<RB>(crow + RPC * r)) * 16);
     coff[r] = unsigned(crow + RPC * r) * row_bytes + cchunk[r];
   }
-  int cp_step = 0, cp_h = g * a.G, cp_i0 = qbeg;
+  int cp_step = 0, cp_h = g * a.G, cp_i0 = lo0, cp_lo = lo0, cp_hi = hi0;
   auto issue = [&](int slot) {
-    const int lim = last - cp_i0;
+    const int lim = cp_hi - 1 - cp_i0;
     const size_t row0 = ((size_t)cp_i0 * a.Hq + cp_h) * D;
     if (lim >= BM - 1) {  // the whole step in range: fixed per-lane offsets
 #pragma unroll
@@ -592,9 +601,13 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
     }
     if (++cp_step < n_steps) {
       cp_i0 += BM;
-      if (cp_i0 > last) {
-        cp_i0 = qbeg;
-        ++cp_h;
+      if (cp_i0 >= cp_hi) {
+        cp_i0 = cp_lo;
+        if (++cp_h == (g + 1) * a.G) {  // on to the second range
+          cp_h = g * a.G;
+          cp_i0 = cp_lo = lo1;
+          cp_hi = hi1;
+        }
       }
     }
   };
@@ -623,7 +636,8 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
   //   dV waves: dV^T += dO^T P of step - 1, then S and P of `step`;
   //   dK waves: dP - delta, dS, dK^T += Q^T dS of step - 1.
   frag pprev[2][2];
-  int dv_i0 = qbeg;  // first query of the dV waves' current step
+  // first query, range and head count of the dV waves' current step
+  int dv_i0 = lo0, dv_lo = lo0, dv_hi = hi0, dv_hc = 0;
   auto dv_iter = [&](int step, auto J) {
     constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
     __builtin_amdgcn_s_setprio(kPrioDvProducts);
@@ -641,8 +655,16 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
       for (int ks = 0; ks < KS; ++ks) M::mma(t[qh], ta.row(ks, j * TILE + qh * 32 * RB), kv[ks]);
     sched_pipeline<kLdsAhead, 4 * DB + 2 * KS, frag_reads<T>(true)>();
     __builtin_amdgcn_s_setprio(kPrioDvVector);
-    const int i0 = dv_i0;
-    dv_i0 = dv_i0 + BM > last ? qbeg : dv_i0 + BM;
+    const int i0 = dv_i0, ihi = dv_hi;
+    dv_i0 += BM;
+    if (dv_i0 >= dv_hi) {
+      dv_i0 = dv_lo;
+      if (++dv_hc == a.G) {
+        dv_hc = 0;
+        dv_i0 = dv_lo = lo1;
+        dv_hi = hi1;
+      }
+    }
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
       float x[16];
@@ -651,11 +673,11 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
 #pragma unroll
       for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(t[qh][i], c, x[i]));
       if (__builtin_amdgcn_readfirstlane(int(i0 + qh * 32 < tile.k0 + kq * 32 + 31 ||
-                                             i0 + qh * 32 + 31 >= qend))) {
+                                             i0 + qh * 32 + 31 >= ihi))) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qi = i0 + qh * 32 + c_row(i, half);
-          if (qi < jkey || qi >= qend) p[i] = 0.f;
+          if (qi < jkey || qi >= ihi) p[i] = 0.f;
         }
       }
 #pragma unroll

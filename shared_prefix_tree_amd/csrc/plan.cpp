@@ -154,7 +154,8 @@ bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int3
   p.ktiles.clear();
   for (int32_t s = 0; s < S; ++s)
     for (int32_t o = 0; o < seg_len[s]; o += kKTile)
-      p.ktiles.push_back(KTile{seg_start[s] + o, std::min(kKTile, seg_len[s] - o), s, p.end[s]});
+      p.ktiles.push_back(
+          KTile{seg_start[s] + o, std::min(kKTile, seg_len[s] - o), s, p.end[s], seg_start[s] + seg_len[s], {}});
   std::stable_sort(p.ktiles.begin(), p.ktiles.end(), [&](const KTile& a, const KTile& b) { return walk(a) > walk(b); });
   // 128-key tiles; a segment's remainder of at most 64 keys is a 64-key tile
   // (walked at half the cost per step), so no tile is more than half empty.
@@ -162,7 +163,8 @@ bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int3
   p.ktiles_wide.clear();
   for (int32_t s = 0; s < S; ++s)
     for (int32_t o = 0; o < seg_len[s]; o += kKTileWide)
-      p.ktiles_wide.push_back(KTile{seg_start[s] + o, std::min(kKTileWide, seg_len[s] - o), s, p.end[s]});
+      p.ktiles_wide.push_back(
+          KTile{seg_start[s] + o, std::min(kKTileWide, seg_len[s] - o), s, p.end[s], seg_start[s] + seg_len[s], {}});
   auto cost = [&](const KTile& t) { return (walk(t) + kKTile - 1) / kKTile * (t.nk > kKTile ? 15 : 8); };
   std::stable_sort(p.ktiles_wide.begin(), p.ktiles_wide.end(),
                    [&](const KTile& a, const KTile& b) { return cost(a) > cost(b); });

@@ -42,7 +42,10 @@ struct KTile {
   int32_t nk;    // tokens in the tile (<= 64)
   int32_t seg;   // segment of every key in the tile
   int32_t qend;  // queries that see the tile: [k0, qend)
+  int32_t send;  // one past the segment's last token: [send, qend) are its descendants
+  int32_t pad[3];
 };
+static_assert(sizeof(KTile) == 32, "one 32-byte record per key tile");
 
 struct Span {
   int32_t phys;  // first physical token
