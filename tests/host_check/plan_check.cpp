@@ -14,7 +14,10 @@
 //     position of the first token equal to its offset on the path, every run
 //     token in exactly one tile;
 //   * key tiles (64 and 128 keys): inside one segment, query end equal to the
-//     end of the segment's subtree, every key in exactly one tile;
+//     end of the segment's subtree, every key in exactly one tile, and the
+//     two query ranges of the 128-key walk non-negative and covering exactly
+//     the run's queries that see the tile;
+//   * the first span copied into each query tile record;
 //   * fragments, Mamba predecessors / halo / successors / units, edge CSR.
 // Malformed forests must be rejected with an error, never read out of range.
 //
@@ -124,6 +127,11 @@ void check_attention_plan(const Forest& f, int32_t qb, int32_t qe) {
       CHECK(q.pos0 == prefix[s] + (q.q0 - f.start[s]), "%s: tile position", f.name.c_str());
       // the walk covers virtual positions [0, pos0 + nq): all on the path
       CHECK(int64_t(q.pos0) + q.nq <= int64_t(prefix[s]) + f.len[s], "%s: walk length", f.name.c_str());
+      // the first span, carried in the tile record, is the segment's first
+      CHECK(q.span0 == p.span_ptr[s], "%s: tile first span index", f.name.c_str());
+      const Span& sp0 = p.spans[size_t(q.span0)];
+      CHECK(q.phys0 == sp0.phys && q.len0 == sp0.len && q.virt0 == sp0.virt && q.virt0 == 0,
+            "%s: tile first span copy", f.name.c_str());
       for (int32_t i = q.q0; i < q.q0 + q.nq; ++i) ++seen[i];
     }
     for (int32_t i = 0; i < T; ++i)
@@ -142,6 +150,29 @@ void check_attention_plan(const Forest& f, int32_t qb, int32_t qe) {
             f.name.c_str());
       CHECK(k.qend == end[k.seg] && k.qend <= T && k.qend >= k.k0 + k.nk, "%s: key tile query end",
             f.name.c_str());
+      CHECK(k.send == f.start[k.seg] + f.len[k.seg], "%s: key tile segment end", f.name.c_str());
+      // The 128-key walk's two query ranges, derived as the kernel derives
+      // them: the segment's descendants, then its own queries.  Neither may
+      // have a negative length (the copies clamp rows to range end - 1 as an
+      // unsigned offset), both lie in [0, T), and together they are exactly
+      // the run's queries that see the tile.
+      {
+        const int32_t qbeg = std::max(k.k0, qb), qend = std::max(std::min(k.qend, qe), qbeg);
+        const int32_t split = std::min(std::max(k.send, qbeg), qend);
+        const bool first_empty = split >= qend;
+        const int32_t lo0 = first_empty ? qbeg : split, hi0 = qend;
+        const int32_t lo1 = first_empty ? qend : qbeg, hi1 = first_empty ? qend : split;
+        CHECK(lo0 <= hi0 && lo1 <= hi1, "%s: walk range lengths", f.name.c_str());
+        CHECK(lo0 >= 0 && hi0 <= T && lo1 >= 0 && hi1 <= T, "%s: walk ranges inside [0, T)", f.name.c_str());
+        const int32_t want_lo = std::max(k.k0, qb), want_hi = std::min(k.qend, qe);
+        const int64_t want = std::max(0, want_hi - want_lo);
+        CHECK(int64_t(hi0 - lo0) + (hi1 - lo1) == want, "%s: walk ranges cover the visible run queries",
+              f.name.c_str());
+        // [lo1, hi1) then directly [lo0, hi0) when both are non-empty
+        if (want > 0)
+          CHECK(hi0 == want_hi && (hi1 == lo1 ? lo0 == want_lo : lo1 == want_lo && hi1 == lo0),
+                "%s: walk ranges adjacent", f.name.c_str());
+      }
       for (int32_t j = k.k0; j < k.k0 + k.nk; ++j) ++seen[j];
     }
     for (int32_t j = 0; j < T; ++j) CHECK(seen[j] == 1, "%s: key %d in %d tiles", f.name.c_str(), j, seen[j]);

@@ -143,3 +143,42 @@ def test_query_run_of_one_token_in_a_leaf():
         h = to_host(g)
         assert np.all(h[~seen] == 0.0)
         assert np.any(h[seen] != 0.0)
+
+
+def test_query_runs_before_and_inside_descendants():
+    """Runs whose ends cut the 128-key dK/dV walk's two query ranges (a
+    segment's descendants, then its own queries) in the degenerate ways: a run
+    that ends hundreds of tokens before most key tiles (no query of the run
+    sees them: exactly zero gradients), and runs that lie only among a
+    segment's descendants or only in its own queries.  dk / dv against the
+    float64 oracle with dout zeroed outside the run."""
+    import shared_prefix_tree_amd as sp
+    from workloads import long_chain
+
+    rng = np.random.default_rng(5)
+    # trunk segments 0, 1, 3, 4 with side leaves 2 and 5 (1,400 tokens)
+    topo = long_chain(rng, total=1400, trunk=4, every=2, side_lo=100, side_hi=200)
+    T = topo.total_tokens
+    arrs = make_inputs(rng, T, 8, 2, 128, "bf16")
+    dev = "cuda:0"
+    t = {k: to_torch(v, "bf16", dev) for k, v in arrs.items()}
+    x = oracle_inputs(arrs, "bf16")
+    for qb, qe in ((0, 100), (600, 700), (1000, 1010), (270, 530)):
+        with torch.cuda.device(dev):
+            plan = sp.Plan.from_topology(topo, query_run=(qb, qe))
+        log(f"run [{qb}, {qe}) of T={T}")
+        out, lse = sp.tree_attn_fwd(t["q"], t["k"], t["v"], plan)
+        _, dk, dv = sp.tree_attn_bwd(t["q"], t["k"], t["v"], out, lse, t["dout"], plan)
+        torch.cuda.synchronize()
+        dout_run = np.zeros_like(x["dout"])
+        dout_run[qb:qe] = x["dout"][qb:qe]
+        _, dk_ref, dv_ref = oracle.backward(x["q"], x["k"], x["v"], dout_run, topo)
+        seen = np.zeros(T, bool)
+        for i in range(qb, qe):
+            seen[oracle.visible_tokens(topo, i)] = True
+        for name, got, ref in (("dk", dk, dk_ref), ("dv", dv, dv_ref)):
+            h = to_host(got)
+            err, bound = tensor_error(name, h, ref, "bf16")
+            log(f"  {name} error {err:.3g} (<= {bound:.0e}); unseen keys {int((~seen).sum())}")
+            assert err <= bound, (qb, qe, name, err)
+            assert np.all(h[~seen] == 0.0), (qb, qe, name)
