@@ -141,6 +141,48 @@ constexpr int kPrioDvProducts = 2;
 constexpr int kPrioDk = 1;
 constexpr int kPrioDvVector = 0;
 
+// The queries a key tile's walk visits: those of the run that see the tile,
+// in two ranges, each walked for every head of the group in turn.  First
+// the segment's descendants [send, qend): the same range for every tile of
+// the segment, so the tiles of one segment walked at the same time on one
+// XCD stay on the same rows, which its L2 then serves once.  Then the
+// tile's own segment [qbeg, send), whose length differs from tile to tile.
+// An empty first range is dropped; qend is clamped to qbeg when no query of
+// the run sees the tile, so neither range has a negative length (the copies
+// clamp rows to the range's last row as an unsigned offset).
+struct QueryRanges {
+  int lo0, hi0, lo1, hi1;
+};
+__device__ inline QueryRanges query_ranges(const KTile& t, int q_begin, int q_end) {
+  const int qbeg = max(t.k0, q_begin), qend = max(min(t.qend, q_end), qbeg);
+  const int split = min(max(t.send, qbeg), qend);
+  if (split >= qend) return QueryRanges{qbeg, qend, qend, qend};
+  return QueryRanges{split, qend, qbeg, split};
+}
+// steps of `bm` queries per head
+__device__ inline int range_blocks(const QueryRanges& r, int bm) {
+  return (r.hi0 - r.lo0 + bm - 1) / bm + (r.hi1 - r.lo1 + bm - 1) / bm;
+}
+
+// A walk's position: the step's first query, the range [lo, hi) it is in,
+// and its head within the group (0 .. G - 1).  Kept incrementally (no
+// division).
+struct WalkCursor {
+  int i0, lo, hi, h;
+  __device__ explicit WalkCursor(const QueryRanges& r) : i0(r.lo0), lo(r.lo0), hi(r.hi0), h(0) {}
+  __device__ inline void advance(const QueryRanges& r, int G, int bm) {
+    i0 += bm;
+    if (i0 >= hi) {
+      i0 = lo;
+      if (++h == G) {  // on to the second range
+        h = 0;
+        i0 = lo = r.lo1;
+        hi = r.hi1;
+      }
+    }
+  }
+};
+
 template <typename T, int D>
 __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, int g, char* lds) {
   using M = Mfma<T>;
@@ -195,11 +237,8 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) settle(kv[ks]);
 
-  // the queries walked: those of the run that see the tile
-  const int qbeg = max(tile.k0, a.q_begin), qend = min(tile.qend, a.q_end);
-  const int nblk = qend > qbeg ? (qend - qbeg + BM - 1) / BM : 0;
-  const int n_steps = a.G * nblk;
-  const int last = qend - 1;
+  const QueryRanges rg = query_ranges(tile, a.q_begin, a.q_end);
+  const int n_steps = a.G * range_blocks(rg, BM);
   if (n_steps == 0) {  // no query of the run sees the tile: zero gradients
     if (qh == 0 && key_valid) {
       T* op = static_cast<T*>(dk_role ? a.dk : a.dv) + ((size_t)jkey * a.Hkv + g) * D;
@@ -233,15 +272,16 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
     coff[r] = unsigned(crow + RPC * r) * row_bytes + cchunk[r];
   }
   // Step `step` goes to slot step % kRing.  The copy stream advances one
-  // step per call: (cp_h, cp_i0) is the head and first query of the next
-  // step to copy, kept incrementally (no division); past the end it stays
-  // on the last step, re-copying its rows into the (idle) slot, so a dK wave
-  // always issues kCopiesK copies.  Rows past the range read the last row
-  // (masked to P = 0).  Each copy reads from a wave-uniform row base plus a
-  // small per-lane offset.
-  int cp_step = 0, cp_h = g * a.G, cp_i0 = qbeg;
+  // step per call: `cp` is the next step to copy; past the end it stays on
+  // the last step, re-copying its rows into the (idle) slot, so a dK wave
+  // always issues kCopiesK copies.  Rows past the range read the range's
+  // last row (masked to P = 0).  Each copy reads from a wave-uniform row
+  // base plus a small per-lane offset.
+  int cp_step = 0;
+  WalkCursor cp(rg);
   auto issue = [&](int slot) {
-    const int lim = last - cp_i0;
+    const int cp_i0 = cp.i0, cp_h = g * a.G + cp.h;
+    const int lim = cp.hi - 1 - cp_i0;
     const size_t row0 = ((size_t)cp_i0 * a.Hq + cp_h) * D;
     if (lim >= BM - 1) {  // the whole step in range: fixed per-lane offsets
 #pragma unroll
@@ -262,13 +302,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
       copy4_async(ssrc + (size_t)cp_h * a.T + cp_i0, (unsigned)min(lane, lim) * 4u,
                   s_lds + (unsigned)slot * s_step);
     }
-    if (++cp_step < n_steps) {
-      cp_i0 += BM;
-      if (cp_i0 > last) {
-        cp_i0 = qbeg;
-        ++cp_h;
-      }
-    }
+    if (++cp_step < n_steps) cp.advance(rg, a.G, BM);
   };
 
   // Per-lane read addresses in slot 0: A rows (Q for the dV role, dO for
@@ -309,7 +343,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
   // 0 reads a zero-filled slot (kRing - 1) and P buffer, so it adds zero;
   // the S, P of iteration n_steps are never used.
   frag pprev[2];
-  int dv_i0 = qbeg;  // first query of the dV waves' current step
+  WalkCursor dvc(rg);  // the dV waves' current step
   auto dv_iter = [&](int step, auto J) {
     constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
     __builtin_amdgcn_s_setprio(kPrioDvProducts);
@@ -325,17 +359,17 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
     __builtin_amdgcn_s_setprio(kPrioDvVector);
     float x[16];
     row_stats(j * STATS, x);
-    const int i0 = dv_i0;
-    dv_i0 = dv_i0 + BM > last ? qbeg : dv_i0 + BM;
+    const int i0 = dvc.i0, ihi = dvc.hi;
+    dvc.advance(rg, a.G, BM);
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(t[i], c, x[i]));
     if (__builtin_amdgcn_readfirstlane(int(i0 + qh * 32 < tile.k0 + kb * 32 + 31 ||
-                                           i0 + qh * 32 + 31 >= qend))) {
+                                           i0 + qh * 32 + 31 >= ihi))) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int qi = i0 + qh * 32 + c_row(i, half);
-        if (qi < jkey || qi >= qend) p[i] = 0.f;
+        if (qi < jkey || qi >= ihi) p[i] = 0.f;
       }
     }
 #pragma unroll
@@ -534,20 +568,8 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) settle(kv[ks]);
 
-  // The queries walked: those of the run that see the tile, in two ranges,
-  // each for every head of the group in turn.  First the segment's
-  // descendants [send, qend): the same range for every tile of the segment,
-  // so tiles of one segment walked at the same time on one XCD stay on the
-  // same rows, which its L2 then serves once.  Then the tile's own segment
-  // [qbeg, send), whose length differs from tile to tile.  An empty first
-  // range is dropped.  (qend is clamped to qbeg when no query of the run
-  // sees the tile, so neither range has a negative length.)
-  const int qbeg = max(tile.k0, a.q_begin), qend = max(min(tile.qend, a.q_end), qbeg);
-  const int split = min(max(tile.send, qbeg), qend);
-  const bool first_empty = split >= qend;
-  const int lo0 = first_empty ? qbeg : split, hi0 = qend;
-  const int lo1 = first_empty ? qend : qbeg, hi1 = first_empty ? qend : split;
-  const int n_steps = a.G * ((hi0 - lo0 + BM - 1) / BM + (hi1 - lo1 + BM - 1) / BM);
+  const QueryRanges rg = query_ranges(tile, a.q_begin, a.q_end);
+  const int n_steps = a.G * range_blocks(rg, BM);
   if (n_steps == 0) {  // no query of the run sees the tile: zero gradients
     if (key_valid) {
       T* op = static_cast<T*>(dk_role ? a.dk : a.dv) + ((size_t)jkey * a.Hkv + g) * D;
@@ -576,9 +598,11 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
     cchunk[r] = (((lane % (RB / 16)) ^ swz<RB>(crow + RPC * r)) * 16);
     coff[r] = unsigned(crow + RPC * r) * row_bytes + cchunk[r];
   }
-  int cp_step = 0, cp_h = g * a.G, cp_i0 = lo0, cp_lo = lo0, cp_hi = hi0;
+  int cp_step = 0;
+  WalkCursor cp(rg);
   auto issue = [&](int slot) {
-    const int lim = cp_hi - 1 - cp_i0;
+    const int cp_i0 = cp.i0, cp_h = g * a.G + cp.h;
+    const int lim = cp.hi - 1 - cp_i0;
     const size_t row0 = ((size_t)cp_i0 * a.Hq + cp_h) * D;
     if (lim >= BM - 1) {  // the whole step in range: fixed per-lane offsets
 #pragma unroll
@@ -599,17 +623,7 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
       copy4_async(ssrc + (size_t)cp_h * a.T + cp_i0, (unsigned)min(lane, lim) * 4u,
                   s_lds + (unsigned)slot * s_step);
     }
-    if (++cp_step < n_steps) {
-      cp_i0 += BM;
-      if (cp_i0 >= cp_hi) {
-        cp_i0 = cp_lo;
-        if (++cp_h == (g + 1) * a.G) {  // on to the second range
-          cp_h = g * a.G;
-          cp_i0 = cp_lo = lo1;
-          cp_hi = hi1;
-        }
-      }
-    }
+    if (++cp_step < n_steps) cp.advance(rg, a.G, BM);
   };
 
   // per-lane read addresses in slot 0 (the query half is a constant offset)
@@ -636,8 +650,7 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
   //   dV waves: dV^T += dO^T P of step - 1, then S and P of `step`;
   //   dK waves: dP - delta, dS, dK^T += Q^T dS of step - 1.
   frag pprev[2][2];
-  // first query, range and head count of the dV waves' current step
-  int dv_i0 = lo0, dv_lo = lo0, dv_hi = hi0, dv_hc = 0;
+  WalkCursor dvc(rg);  // the dV waves' current step
   auto dv_iter = [&](int step, auto J) {
     constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
     __builtin_amdgcn_s_setprio(kPrioDvProducts);
@@ -655,16 +668,8 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
       for (int ks = 0; ks < KS; ++ks) M::mma(t[qh], ta.row(ks, j * TILE + qh * 32 * RB), kv[ks]);
     sched_pipeline<kLdsAhead, 4 * DB + 2 * KS, frag_reads<T>(true)>();
     __builtin_amdgcn_s_setprio(kPrioDvVector);
-    const int i0 = dv_i0, ihi = dv_hi;
-    dv_i0 += BM;
-    if (dv_i0 >= dv_hi) {
-      dv_i0 = dv_lo;
-      if (++dv_hc == a.G) {
-        dv_hc = 0;
-        dv_i0 = dv_lo = lo1;
-        dv_hi = hi1;
-      }
-    }
+    const int i0 = dvc.i0, ihi = dvc.hi;
+    dvc.advance(rg, a.G, BM);
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
       float x[16];
