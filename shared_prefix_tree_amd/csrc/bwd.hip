@@ -928,22 +928,27 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, int item) {
   ka.init(lds_addr(ring), lane);
   va.init(lds_addr(ring + kDqRing * TILE), lane);
 
-  // the two 32-key halves one after the other: only one half's S and dP
-  // are live at a time
+  // The two 32-key halves one after the other (only one half's S and dP
+  // are live at a time), with half 0's dQ products issued after half 1's S
+  // and dP products: half 1's vector work (P, dS) then issues between
+  // those independent products while the matrix core works through them.
+  // Every accumulator sums in the same order as half by half.
   auto compute = [&](int v0, auto B) {
     constexpr int off = decltype(B)::value * TILE;
     const bool need_mask = v0 + BN - 1 > wave_pos0;  // wave-uniform
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // dP - delta: the products accumulate onto -delta (this lane's
-      // query is the same in all 16 entries)
-      f32x16 s = f32x16{}, dp = ndlt16;
+    // S and dP - delta of half kb (the dP products accumulate onto -delta:
+    // this lane's query is the same in all 16 entries)
+    auto products = [&](int kb, f32x16& s, f32x16& dp) {
+      s = f32x16{};
+      dp = ndlt16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         M::mma(s, ka.row(ks, off + kb * 32 * RB), qf[ks]);
         M::mma(dp, va.row(ks, off + kb * 32 * RB), of[ks]);
       }
-      sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
+    };
+    // dS = P (dP - delta) of half kb, P = exp2(S c - lse2)
+    auto vector_work = [&](int kb, const f32x16& s, const f32x16& dp, frag (&dsf)[2]) {
       float p[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, nlse2));
@@ -952,16 +957,32 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, int item) {
         for (int i = 0; i < 16; ++i)
           if (v0 + kb * 32 + c_row(i, half) > qpos) p[i] = 0.f;
       }
-      frag dsf[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) dsf[i >> 3][i & 7] = to_elem<T>(p[i] * dp[i]);
+    };
+    auto dq_products = [&](int kb, const frag (&dsf)[2]) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          M::mma(dq[db], ka.tr(db, off + (kb * 32 + 16 * hh) * RB), dsf[hh]);
-      sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
+        for (int hh = 0; hh < 2; ++hh) M::mma(dq[db], ka.tr(db, off + (kb * 32 + 16 * hh) * RB), dsf[hh]);
+    };
+    frag ds0[2], ds1[2];
+    {
+      f32x16 s, dp;
+      products(0, s, dp);
+      sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
+      vector_work(0, s, dp, ds0);
     }
+    {
+      f32x16 s, dp;
+      products(1, s, dp);
+      dq_products(0, ds0);
+      vector_work(1, s, dp, ds1);
+      if constexpr (frag_reads<T>(false) > 0)
+        sched_products_then_valu<kLdsAhead, 2 * KS, frag_reads<T>(false), 2 * DB, frag_reads<T>(true), 8>();
+    }
+    dq_products(1, ds1);
+    sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
   };
   auto body = [&](int step, auto B) {
     // this wave's copies of `step` are done once only the kAhead - 1 newer

@@ -317,19 +317,27 @@ struct TileAddr<float, D> {
   }
 };
 
-// As sched_pipeline, and VALU instructions after every matrix product, so
-// that independent vector work of the same wavefront runs while the matrix
-// core is busy.
+// As sched_pipeline over two groups of products in order, N1 products of
+// READS1 LDS reads each and then N2 of READS2 (the reads run AHEAD products
+// ahead across the boundary), with up to VALU vector instructions after
+// each product of the second group: vector work of the same wavefront that
+// needs only the first group's results then issues while the matrix core
+// works through the second.
 constexpr int kSchedValu = 0x0002;
 
-template <int AHEAD, int N, int READS, int VALU>
-__device__ inline void sched_pipeline_valu() {
-  if constexpr (READS > 0 && N > AHEAD) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AHEAD * READS, 0);
+template <int AHEAD, int N1, int READS1, int N2, int READS2, int VALU>
+__device__ inline void sched_products_then_valu() {
+  static_assert(READS1 > 0 && READS2 > 0 && N1 > AHEAD && N2 > AHEAD, "LDS-fed products");
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AHEAD * READS1, 0);
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
+  for (int i = 0; i < N1 + N2; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    if (READS > 0 && i < N - AHEAD) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU, 0);
+    const int next = i + AHEAD;  // the product whose operands are read now
+    if (next < N1)
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS1, 0);
+    else if (next < N1 + N2)
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS2, 0);
+    if (i >= N1) __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU, 0);
   }
 }
 
