@@ -654,18 +654,20 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
   auto dv_iter = [&](int step, auto J) {
     constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
     __builtin_amdgcn_s_setprio(kPrioDvProducts);
+    // (consecutive products go to different accumulators; each one still
+    // sums in the same order)
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int db = 0; db < DB; ++db)
           M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * RB), pprev[qh][hh]);
     f32x16 t[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) M::mma(t[qh], ta.row(ks, j * TILE + qh * 32 * RB), kv[ks]);
+      for (int qh = 0; qh < 2; ++qh) M::mma(t[qh], ta.row(ks, j * TILE + qh * 32 * RB), kv[ks]);
     sched_pipeline<kLdsAhead, 4 * DB + 2 * KS, frag_reads<T>(true)>();
     __builtin_amdgcn_s_setprio(kPrioDvVector);
     const int i0 = dvc.i0, ihi = dvc.hi;
@@ -716,9 +718,9 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
 #pragma unroll
       for (int i = 0; i < 16; ++i) t[qh][i] = xd[qh][i];
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) M::mma(t[qh], ta.row(ks, jp * TILE + qh * 32 * RB), kv[ks]);
+      for (int qh = 0; qh < 2; ++qh) M::mma(t[qh], ta.row(ks, jp * TILE + qh * 32 * RB), kv[ks]);
     sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
     frag xf[2][2];
 #pragma unroll
@@ -729,9 +731,9 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int db = 0; db < DB; ++db)
           M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * RB), xf[qh][hh]);
     sched_pipeline<kLdsAhead, 4 * DB, frag_reads<T>(true)>();
     __builtin_amdgcn_sched_barrier(0);
