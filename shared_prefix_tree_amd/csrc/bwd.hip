@@ -347,10 +347,12 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
   auto dv_iter = [&](int step, auto J) {
     constexpr int j = decltype(J)::value, jp = (j + kRing - 1) % kRing;
     __builtin_amdgcn_s_setprio(kPrioDvProducts);
+    // (consecutive products to different accumulators; each sums in the
+    // same order)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int db = 0; db < DB; ++db)
         M::mma(acc[db], tc.tr(db, jp * TILE + 16 * hh * RB), pprev[hh]);
     f32x16 t = f32x16{};
 #pragma unroll
@@ -399,9 +401,9 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
 #pragma unroll
     for (int i = 0; i < 16; ++i) xf[i >> 3][i & 7] = to_elem<T>(PHandoff<T>::times(pf[i >> 3], i & 7, t[i]));
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int db = 0; db < DB; ++db)
         M::mma(acc[db], tc.tr(db, jp * TILE + 16 * hh * RB), xf[hh]);
     sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
     __builtin_amdgcn_sched_barrier(0);
@@ -964,9 +966,9 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, int item) {
     };
     auto dq_products = [&](int kb, const frag (&dsf)[2]) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) M::mma(dq[db], ka.tr(db, off + (kb * 32 + 16 * hh) * RB), dsf[hh]);
+        for (int db = 0; db < DB; ++db) M::mma(dq[db], ka.tr(db, off + (kb * 32 + 16 * hh) * RB), dsf[hh]);
     };
     frag ds0[2], ds1[2];
     {

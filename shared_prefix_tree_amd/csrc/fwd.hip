@@ -146,10 +146,12 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
   auto compute = [&](int v0, auto B) {
     constexpr int off = decltype(B)::value * TILE;
     f32x16 s[2] = {f32x16{}, f32x16{}};
+    // (consecutive products to different accumulators; each sums in the
+    // same order)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) M::mma(s[kb], ka.row(ks, off + kb * 32 * RB), qf[ks]);
+      for (int kb = 0; kb < 2; ++kb) M::mma(s[kb], ka.row(ks, off + kb * 32 * RB), qf[ks]);
     sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
 
     if (v0 + BN - 1 > wave_pos0) {
@@ -208,11 +210,11 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
       for (int i = 0; i < 16; ++i) pf[kb][i >> 3][i & 7] = to_elem<T>(p[kb][i]);
 
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) M::mma(o[db], va.tr(db, off + (kb * 32 + 16 * hh) * RB), pf[kb][hh]);
+        for (int db = 0; db < DB; ++db) M::mma(o[db], va.tr(db, off + (kb * 32 + 16 * hh) * RB), pf[kb][hh]);
     sched_pipeline<kLdsAhead, 4 * DB, frag_reads<T>(true)>();
   };
   // W = 12: the same step as two 32-key halves (fewer live registers)
@@ -259,10 +261,12 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
       frag pf[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = to_elem<T>(p[i]);
+      // (consecutive products to different accumulators; each sums in the
+      // same order)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) M::mma(o[db], va.tr(db, off + (kb * 32 + 16 * hh) * RB), pf[hh]);
+        for (int db = 0; db < DB; ++db) M::mma(o[db], va.tr(db, off + (kb * 32 + 16 * hh) * RB), pf[hh]);
       sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
     }
   };
