@@ -719,25 +719,34 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
     for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
       for (int i = 0; i < 16; ++i) t[qh][i] = xd[qh][i];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int qh = 0; qh < 2; ++qh) M::mma(t[qh], ta.row(ks, jp * TILE + qh * 32 * RB), kv[ks]);
-    sched_pipeline<kLdsAhead, 2 * KS, frag_reads<T>(false)>();
+    // dP of half 0, then dP of half 1 with half 0's dS between its
+    // products, then dK of half 0 with half 1's dS between its products,
+    // then dK of half 1: each half's vector work issues while the matrix
+    // core works through independent products (same sums, same order)
     frag xf[2][2];
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh)
+    auto ds = [&](int qh) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         xf[qh][i >> 3][i & 7] = to_elem<T>(PHandoff<T>::times(pf[qh][i >> 3], i & 7, t[qh][i]));
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh)
+    };
+    auto dk = [&](int qh) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           M::mma(acc[db], tc.tr(db, jp * TILE + (qh * 32 + 16 * hh) * RB), xf[qh][hh]);
-    sched_pipeline<kLdsAhead, 4 * DB, frag_reads<T>(true)>();
+    };
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) M::mma(t[qh], ta.row(ks, jp * TILE + qh * 32 * RB), kv[ks]);
+    ds(0);
+    sched_products_then_valu<kLdsAhead, KS, frag_reads<T>(false), KS, frag_reads<T>(false), 3>();
+    __builtin_amdgcn_sched_barrier(0);
+    dk(0);
+    ds(1);
+    dk(1);
+    sched_products_then_valu<kLdsAhead, 2 * DB, frag_reads<T>(true), 2 * DB, frag_reads<T>(true), 0, 3>();
     __builtin_amdgcn_sched_barrier(0);
     // -delta of `step` (in LDS since this iteration's barrier; its slot is
     // refilled only kRing - kAhead steps later)

@@ -320,12 +320,12 @@ struct TileAddr<float, D> {
 // As sched_pipeline over two groups of products in order, N1 products of
 // READS1 LDS reads each and then N2 of READS2 (the reads run AHEAD products
 // ahead across the boundary), with up to VALU vector instructions after
-// each product of the second group: vector work of the same wavefront that
-// needs only the first group's results then issues while the matrix core
-// works through the second.
+// each product of the second group (and VALU1 after each of the first):
+// vector work of the same wavefront that needs only earlier results then
+// issues while the matrix core works through the products.
 constexpr int kSchedValu = 0x0002;
 
-template <int AHEAD, int N1, int READS1, int N2, int READS2, int VALU>
+template <int AHEAD, int N1, int READS1, int N2, int READS2, int VALU, int VALU1 = 0>
 __device__ inline void sched_products_then_valu() {
   static_assert(READS1 > 0 && READS2 > 0 && N1 > AHEAD && N2 > AHEAD, "LDS-fed products");
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AHEAD * READS1, 0);
@@ -337,7 +337,10 @@ __device__ inline void sched_products_then_valu() {
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS1, 0);
     else if (next < N1 + N2)
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS2, 0);
-    if (i >= N1) __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU, 0);
+    if (i >= N1)
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU, 0);
+    else if (VALU1 > 0)
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU1, 0);
   }
 }
 
