@@ -670,7 +670,8 @@ __device__ __forceinline__ void dkdv_wide_item(const BwdArgs& a, const KTile& ti
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int qh = 0; qh < 2; ++qh) M::mma(t[qh], ta.row(ks, j * TILE + qh * 32 * RB), kv[ks]);
-    sched_pipeline<kLdsAhead, 4 * DB + 2 * KS, frag_reads<T>(true)>();
+    // (the dV products take two LDS reads each, the S products one)
+    sched_products_then_valu<kLdsAhead, 4 * DB, frag_reads<T>(true), 2 * KS, frag_reads<T>(false), 0>();
     __builtin_amdgcn_s_setprio(kPrioDvVector);
     const int i0 = dvc.i0, ihi = dvc.hi;
     dvc.advance(rg, a.G, BM);
