@@ -357,7 +357,9 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, const KTile& tile, i
     f32x16 t = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) M::mma(t, ta.row(ks, j * TILE), kv[ks]);
-    sched_pipeline<kLdsAhead, 2 * DB + KS, frag_reads<T>(true)>();
+    // (the dV products take two LDS reads each, the S products one)
+    if constexpr (frag_reads<T>(false) > 0)
+      sched_products_then_valu<kLdsAhead, 2 * DB, frag_reads<T>(true), KS, frag_reads<T>(false), 0>();
     __builtin_amdgcn_s_setprio(kPrioDvVector);
     float x[16];
     row_stats(j * STATS, x);
