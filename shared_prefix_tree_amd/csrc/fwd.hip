@@ -270,6 +270,11 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
       sched_pipeline<kLdsAhead, 2 * DB, frag_reads<T>(true)>();
     }
   };
+  // A wavefront whose 32 query rows all lie past the tile's end (in the
+  // last tile of a segment) copies and waits like the others but computes
+  // and stores nothing, so the wavefronts with rows have their SIMD's
+  // matrix core to themselves.
+  const bool rows_valid = ts * 32 < tile.nq;  // wave-uniform
   auto body = [&](int step, auto B) {
     // this wave's copies of `step` are done once only the kAhead - 1 newer
     // steps' copies may be in flight; after the barrier every wave's are,
@@ -279,10 +284,12 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
     else
       wait_copies_barrier<0>();
     issue(step + kAhead);
-    if constexpr (W == 12)
-      compute_halves(step * BN, B);
-    else
-      compute(step * BN, B);
+    if (rows_valid) {
+      if constexpr (W == 12)
+        compute_halves(step * BN, B);
+      else
+        compute(step * BN, B);
+    }
   };
 
   if constexpr (kStageQ) {
@@ -317,6 +324,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, char* ring)
     if (step + 4 >= n_steps) break;
   }
   wait_copies_barrier<0>();  // no copy in flight when the workgroup ends
+  if (!rows_valid) return;
 
   l = sum_halves(l);
   if constexpr (RB == 256) {
