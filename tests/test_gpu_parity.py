@@ -124,6 +124,18 @@ def test_edge_topologies(label, topo, dtype, D):
     compare_full(topo, make_inputs(rng, topo.total_tokens, 4, 1, D, dtype), dtype, label=f"{label}/{dtype}/D{D}")
 
 
+def test_forward_tail_tiles_of_every_row_count():
+    """96-query forward tiles (12 wavefronts: three 32-row blocks of four
+    query heads) whose last tile holds 1, 32, 33, 64, 65 or 95 rows.  A
+    wavefront whose rows all lie past the tile's end skips its products and
+    stores; every existing row must still match the float64 oracle."""
+    lens = [97, 32, 33, 64, 65, 95, 128, 160]
+    starts = np.cumsum([0] + lens[:-1]).tolist()
+    topo = Topology([-1] + [0] * (len(lens) - 1), starts, lens)
+    rng = np.random.default_rng(4242)
+    compare_full(topo, make_inputs(rng, topo.total_tokens, 8, 2, 128, "bf16"), "bf16", label="tail_tiles")
+
+
 COMBS = [
     # a 64-key step crosses 32 two-token spans; the deepest path has 100 spans
     ("comb_2_1_x100", comb(100, spine_len=2, leaf_len=1, tail_len=70)),
