@@ -131,13 +131,15 @@ bool build_host_plan(const int32_t* parent, const int32_t* seg_start, const int3
     auto& tiles = p.qtiles[t];
     tiles.clear();
     for (int32_t s = 0; s < S; ++s) {
-      // the run's tokens of this segment, [o0, o1) from its start
+      // the run's tokens of this segment, [o0, o1) from its start; a short
+      // tile goes first, where its walk of the ancestor path is shortest
+      // (fewer of its rows exist, so fewer wavefronts share the work)
       const int32_t o0 = std::max(0, q_begin - seg_start[s]), o1 = std::min(seg_len[s], q_end - seg_start[s]);
-      for (int32_t o = o0; o < o1; o += tq)
-        {
-        const Span& f = p.spans[p.span_ptr[s]];
-        tiles.push_back(QTile{seg_start[s] + o, std::min(tq, o1 - o), s, p.prefix[s] + o, p.span_ptr[s], f.phys, f.len,
-                              f.virt});
+      const Span& f = p.spans[p.span_ptr[s]];
+      for (int32_t o = o0; o < o1;) {
+        const int32_t n = o == o0 && (o1 - o0) % tq ? (o1 - o0) % tq : tq;
+        tiles.push_back(QTile{seg_start[s] + o, n, s, p.prefix[s] + o, p.span_ptr[s], f.phys, f.len, f.virt});
+        o += n;
       }
     }
     std::stable_sort(tiles.begin(), tiles.end(), [](const QTile& a, const QTile& b) {
